@@ -1,0 +1,337 @@
+/*
+ * CPU oracle for the in-model embedding cache — TEST INFRASTRUCTURE ONLY.
+ *
+ * Plain, single-threaded, deliberately slow C.  Only the tests, the smoke
+ * check and the benchmark's CPU-baseline leg may load this library; the
+ * product path (libhlr.so) never does and shares no code with it.
+ *
+ * Build: gcc -O2 -std=c11 -ffp-contract=off -fno-fast-math -shared -fPIC
+ * (no FMA contraction: every float operation below rounds on its own, in the
+ * order written).
+ *
+ * Sources (cited by page title and section; no line numbers):
+ *  [ML]   "Memory Layer: Train the In-Model Cache for Recommendation Models",
+ *         sec. 2 (method): MPZCH identity tensor maps raw IDs to rows with no
+ *         collisions, 512-d rows, metadata shares the row index, bounded
+ *         capacity with LRU eviction; Writeback gradient g = M[i] - e_i applied
+ *         by exact SGD at learning rate 1 so M[i] becomes e_i; duplicate IDs of
+ *         a batch are deduplicated so each row receives one exact write; a
+ *         cache miss zeroes the cached branch.  Sec. 5 (limitations): serving
+ *         reads int8-quantised rows.
+ *  [CS3]  "CS3: Efficient Online Capability Synergy for Two-Tower
+ *         Recommendation", sec. 2 (method): CTS keeps c <- a*c + (1-a)*v,
+ *         updated only on positive interactions; CMS keeps s <- b*s + (1-b)*h
+ *         for every interaction.
+ *  [DLRM] "DLRMv4: MLPerf recommendation training goes sequential", feature
+ *         expansion paragraph: native sparse tables plus cross-product hashed
+ *         tables, 512-d fp32 rows, per-token (unpooled) lookups.
+ *  [SM64] SplitMix64 (Steele, Lea, Flood, "Fast splittable pseudorandom number
+ *         generators", OOPSLA 2014): 64-bit finaliser with the variant-13
+ *         shift/multiply constants.
+ *
+ * Readings of points the pages leave open (each is listed in the design doc):
+ *  - hash: SplitMix64 finaliser; bucket(x) = mix(x) mod (capacity/probes);
+ *  - probes of x are the aligned bucket slots bucket(x)*P + j, j = 0..P-1;
+ *  - identity == -1 is an empty slot, an input ID of -1 is invalid;
+ *  - a batch is applied in two phases: every ID resident at batch start is a
+ *    hit and its slot is pinned (stamp = now); then the distinct missed IDs are
+ *    inserted in order of first occurrence, each taking the first empty slot of
+ *    its bucket, else the unpinned slot (stamp < now) with the smallest stamp
+ *    (lowest probe index on ties), else it overflows (row -1, zero vector);
+ *  - an inserted row is zero-filled, evicted IDs are reported at the first
+ *    occurrence of the ID that replaced them;
+ *  - dedup keeps the last occurrence, unique keys ascending;
+ *  - Writeback arithmetic is fp32: M' = fl(M - fl(M - e));
+ *  - duplicate gradients are summed in batch order inside runs of 256
+ *    consecutive occurrences, run totals added in batch order, then
+ *    M' = fl(M - fl(lr * s));
+ *  - EMA arithmetic is fp32 per step: T' = fl(fl(a*T) + fl(b*v)), positions in
+ *    batch order;
+ *  - dequant-score is evaluated in fp64: x_d = q_d*scale + bias,
+ *    score = sum_d x_d*u_d, rounded once to fp32; a miss scores exactly 0.
+ */
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+
+#define ORC_OK 0
+#define ORC_EINVAL 1
+#define ORC_ENOMEM 2
+#define ORC_ESTAMP 3
+
+#define ORC_EMPTY (-1)
+#define ORC_SUM_RUN 256
+
+/* [SM64] finaliser. */
+uint64_t orc_mix64(uint64_t z) {
+    z = (z ^ (z >> 30)) * 0xbf58476d1ce4e5b9ULL;
+    z = (z ^ (z >> 27)) * 0x94d049bb133111ebULL;
+    return z ^ (z >> 31);
+}
+
+/* Bucket of an ID: the ID's two's-complement bits hashed, reduced modulo the bucket count. */
+int64_t orc_bucket(int64_t id, int64_t num_buckets) {
+    return (int64_t)(orc_mix64((uint64_t)id) % (uint64_t)num_buckets);
+}
+
+/* ------------------------------------------------------------ sort helpers */
+typedef struct { int64_t key; int64_t pos; } orc_pair;
+
+static int cmp_pair(const void *a, const void *b) {
+    const orc_pair *x = (const orc_pair *)a, *y = (const orc_pair *)b;
+    if (x->key != y->key) return x->key < y->key ? -1 : 1;
+    if (x->pos != y->pos) return x->pos < y->pos ? -1 : 1;
+    return 0;
+}
+
+static int cmp_pos_first(const void *a, const void *b) {
+    const orc_pair *x = (const orc_pair *)a, *y = (const orc_pair *)b;
+    if (x->pos != y->pos) return x->pos < y->pos ? -1 : 1;
+    return 0;
+}
+
+/* ----------------------------------------------------------- MPZCH step [ML] */
+/*
+ * One batch against the MPZCH table.
+ * identity[C], stamps[C]: table state, updated in place (insert mode only).
+ * values[C*dim]: may be NULL; inserted rows are zero-filled when given.
+ * Outputs per position: rows (slot or -1), hit (1 = resident at batch start),
+ * evicted (the ID an insert displaced, at that insert's first occurrence; -1
+ * elsewhere).  stats[5] = {hit positions, inserts, evictions, overflows,
+ * invalid positions}.
+ */
+int orc_mpzch_step(int64_t *identity, int64_t *stamps, float *values, int64_t capacity, int32_t probes,
+                   int64_t dim, const int64_t *ids, int64_t n, int64_t now, int32_t insert,
+                   int64_t *rows, int8_t *hit, int64_t *evicted, int64_t *stats) {
+    if (capacity <= 0 || probes <= 0 || capacity % probes != 0 || n < 0 || dim <= 0) return ORC_EINVAL;
+    const int64_t nb = capacity / probes;
+    int64_t st[5] = {0, 0, 0, 0, 0};
+    if (insert) {
+        for (int64_t s = 0; s < capacity; ++s)
+            if (stamps[s] >= now) return ORC_ESTAMP;
+    }
+    /* Phase 1: IDs resident at batch start are hits and pin their slot. */
+    for (int64_t i = 0; i < n; ++i) {
+        rows[i] = -1;
+        hit[i] = 0;
+        evicted[i] = ORC_EMPTY;
+        if (ids[i] == ORC_EMPTY) { st[4]++; continue; }
+        const int64_t base = orc_bucket(ids[i], nb) * probes;
+        for (int32_t j = 0; j < probes; ++j) {
+            if (identity[base + j] == ids[i]) {
+                rows[i] = base + j;
+                hit[i] = 1;
+                st[0]++;
+                if (insert) stamps[base + j] = now;
+                break;
+            }
+        }
+    }
+    if (insert) {
+        /* Phase 2: distinct missed IDs in order of first occurrence. */
+        int64_t m = 0;
+        for (int64_t i = 0; i < n; ++i)
+            if (!hit[i] && ids[i] != ORC_EMPTY) m++;
+        orc_pair *miss = (orc_pair *)malloc((size_t)(m ? m : 1) * sizeof(orc_pair));
+        orc_pair *first = (orc_pair *)malloc((size_t)(m ? m : 1) * sizeof(orc_pair));
+        if (!miss || !first) { free(miss); free(first); return ORC_ENOMEM; }
+        m = 0;
+        for (int64_t i = 0; i < n; ++i)
+            if (!hit[i] && ids[i] != ORC_EMPTY) { miss[m].key = ids[i]; miss[m].pos = i; m++; }
+        qsort(miss, (size_t)m, sizeof(orc_pair), cmp_pair);
+        int64_t f = 0;
+        for (int64_t k = 0; k < m; ++k)
+            if (k == 0 || miss[k].key != miss[k - 1].key) first[f++] = miss[k];
+        qsort(first, (size_t)f, sizeof(orc_pair), cmp_pos_first);
+        for (int64_t k = 0; k < f; ++k) {
+            const int64_t id = first[k].key;
+            const int64_t base = orc_bucket(id, nb) * probes;
+            int32_t best = -1;
+            for (int32_t j = 0; j < probes; ++j)
+                if (identity[base + j] == ORC_EMPTY) { best = j; break; }
+            if (best < 0) {
+                for (int32_t j = 0; j < probes; ++j)
+                    if (stamps[base + j] < now && (best < 0 || stamps[base + j] < stamps[base + best])) best = j;
+            }
+            if (best < 0) { st[3]++; continue; } /* overflow: every slot pinned by this batch */
+            const int64_t s = base + best;
+            const int64_t old = identity[s];
+            if (old != ORC_EMPTY) st[2]++;
+            st[1]++;
+            identity[s] = id;
+            stamps[s] = now;
+            if (values) memset(values + s * dim, 0, (size_t)dim * sizeof(float));
+            evicted[first[k].pos] = old;
+        }
+        /* Every missed position takes the slot its ID now occupies (or -1 on overflow). */
+        for (int64_t k = 0; k < m; ++k) {
+            const int64_t id = miss[k].key, i = miss[k].pos;
+            const int64_t base = orc_bucket(id, nb) * probes;
+            for (int32_t j = 0; j < probes; ++j)
+                if (identity[base + j] == id) { rows[i] = base + j; break; }
+        }
+        free(miss);
+        free(first);
+    }
+    if (stats) memcpy(stats, st, sizeof(st));
+    return ORC_OK;
+}
+
+/* ------------------------------------------------------------- gather [ML] */
+/* out[i] = table[rows[i]]; a row of -1 (miss or overflow) reads as the zero vector. */
+int orc_gather(const float *table, int64_t num_rows, int64_t dim, const int64_t *rows, int64_t n, float *out) {
+    for (int64_t i = 0; i < n; ++i) {
+        if (rows[i] < -1 || rows[i] >= num_rows) return ORC_EINVAL;
+        for (int64_t d = 0; d < dim; ++d) out[i * dim + d] = rows[i] < 0 ? 0.0f : table[rows[i] * dim + d];
+    }
+    return ORC_OK;
+}
+
+/* --------------------------------------------------------------- dedup [ML] */
+/*
+ * Distinct keys in ascending order, the last position of each, and for every
+ * position the index of its key.  Returns the number of distinct keys (or -1).
+ */
+int64_t orc_dedup(const int64_t *keys, int64_t n, int64_t *unique, int64_t *last_pos, int64_t *inverse) {
+    orc_pair *p = (orc_pair *)malloc((size_t)(n ? n : 1) * sizeof(orc_pair));
+    if (!p) return -1;
+    for (int64_t i = 0; i < n; ++i) { p[i].key = keys[i]; p[i].pos = i; }
+    qsort(p, (size_t)n, sizeof(orc_pair), cmp_pair);
+    int64_t u = -1;
+    for (int64_t k = 0; k < n; ++k) {
+        if (k == 0 || p[k].key != p[k - 1].key) { ++u; unique[u] = p[k].key; }
+        last_pos[u] = p[k].pos; /* positions ascend within a key: the final one is the last occurrence */
+        if (inverse) inverse[p[k].pos] = u;
+    }
+    free(p);
+    return u + 1;
+}
+
+/* Positions grouped by row (rows >= 0 only), each group in ascending position. */
+static orc_pair *group_rows(const int64_t *rows, const uint8_t *mask, int64_t n, int64_t num_rows, int64_t *m_out,
+                            int *err) {
+    int64_t m = 0;
+    *err = ORC_OK;
+    for (int64_t i = 0; i < n; ++i) {
+        if (rows[i] < -1 || rows[i] >= num_rows) { *err = ORC_EINVAL; return NULL; }
+        if (rows[i] >= 0 && (!mask || mask[i])) m++;
+    }
+    orc_pair *p = (orc_pair *)malloc((size_t)(m ? m : 1) * sizeof(orc_pair));
+    if (!p) { *err = ORC_ENOMEM; return NULL; }
+    m = 0;
+    for (int64_t i = 0; i < n; ++i)
+        if (rows[i] >= 0 && (!mask || mask[i])) { p[m].key = rows[i]; p[m].pos = i; m++; }
+    qsort(p, (size_t)m, sizeof(orc_pair), cmp_pair);
+    *m_out = m;
+    return p;
+}
+
+/* ------------------------------------------------------ Writeback [ML] sec.2 */
+/*
+ * Each distinct row r >= 0 of the batch takes one exact write from its last
+ * occurrence p: g = fl(M[r] - e[p]); M[r] = fl(M[r] - g)  (learning rate 1).
+ */
+int orc_writeback_last(float *table, int64_t num_rows, int64_t dim, const int64_t *rows, const float *e, int64_t n) {
+    int64_t m = 0;
+    int err;
+    orc_pair *p = group_rows(rows, NULL, n, num_rows, &m, &err);
+    if (!p) return err;
+    for (int64_t k = 0; k < m; ++k) {
+        if (k + 1 < m && p[k + 1].key == p[k].key) continue; /* not the last occurrence */
+        float *w = table + p[k].key * dim;
+        const float *src = e + p[k].pos * dim;
+        for (int64_t d = 0; d < dim; ++d) {
+            const float g = w[d] - src[d];
+            w[d] = w[d] - g;
+        }
+    }
+    free(p);
+    return ORC_OK;
+}
+
+/* --------------------------------------------- SGD with summed duplicates */
+/*
+ * Duplicate gradients of a row are summed, then applied once:
+ * s = (sum over the row's positions in batch order, in runs of 256 consecutive
+ * occurrences; the run totals are added in batch order), M[r] = fl(M[r] - fl(lr*s)).
+ */
+int orc_sgd_sum(float *table, int64_t num_rows, int64_t dim, const int64_t *rows, const float *g, int64_t n,
+                float lr) {
+    int64_t m = 0;
+    int err;
+    orc_pair *p = group_rows(rows, NULL, n, num_rows, &m, &err);
+    if (!p) return err;
+    int64_t k0 = 0;
+    while (k0 < m) {
+        int64_t k1 = k0;
+        while (k1 < m && p[k1].key == p[k0].key) k1++;
+        float *w = table + p[k0].key * dim;
+        for (int64_t d = 0; d < dim; ++d) {
+            float s = 0.0f;
+            for (int64_t r0 = k0; r0 < k1; r0 += ORC_SUM_RUN) {
+                const int64_t r1 = r0 + ORC_SUM_RUN < k1 ? r0 + ORC_SUM_RUN : k1;
+                float run = g[p[r0].pos * dim + d];
+                for (int64_t k = r0 + 1; k < r1; ++k) run = run + g[p[k].pos * dim + d];
+                s = (r0 == k0) ? run : s + run;
+            }
+            const float step = lr * s;
+            w[d] = w[d] - step;
+        }
+        k0 = k1;
+    }
+    free(p);
+    return ORC_OK;
+}
+
+/* --------------------------------------------------------------- EMA [CS3] */
+/*
+ * In batch order, for every position i with rows[i] >= 0 and mask[i] != 0 (mask
+ * NULL = all): T[r] = fl(fl(a*T[r]) + fl(b*v_i)), element-wise.
+ */
+int orc_ema(float *table, int64_t num_rows, int64_t dim, const int64_t *rows, const float *vals,
+            const uint8_t *mask, int64_t n, float a, float b) {
+    for (int64_t i = 0; i < n; ++i)
+        if (rows[i] < -1 || rows[i] >= num_rows) return ORC_EINVAL;
+    for (int64_t i = 0; i < n; ++i) {
+        if (rows[i] < 0 || (mask && !mask[i])) continue;
+        float *t = table + rows[i] * dim;
+        const float *v = vals + i * dim;
+        for (int64_t d = 0; d < dim; ++d) {
+            const float x = a * t[d];
+            const float y = b * v[d];
+            t[d] = x + y;
+        }
+    }
+    return ORC_OK;
+}
+
+/* -------------------------------------------- int8 dequant + dot [ML] sec.5 */
+/*
+ * scores[q][c] = sum_d (qtable[row][d]*scale[row] + bias[row]) * user[q][d]
+ * in fp64, rounded to fp32; row = rows[q*cands + c]; row -1 (miss) scores 0.
+ */
+int orc_dequant_score(const int8_t *qtable, const float *scale, const float *bias, int64_t num_rows, int64_t dim,
+                      const int64_t *rows, int64_t num_requests, int64_t cands, const float *user, float *out) {
+    for (int64_t r = 0; r < num_requests; ++r) {
+        for (int64_t c = 0; c < cands; ++c) {
+            const int64_t row = rows[r * cands + c];
+            if (row < -1 || row >= num_rows) return ORC_EINVAL;
+            if (row < 0) { out[r * cands + c] = 0.0f; continue; }
+            double acc = 0.0;
+            for (int64_t d = 0; d < dim; ++d) {
+                const double x = (double)qtable[row * dim + d] * (double)scale[row] + (double)bias[row];
+                acc += x * (double)user[r * dim + d];
+            }
+            out[r * cands + c] = (float)acc;
+        }
+    }
+    return ORC_OK;
+}
+
+/* ------------------------------------------------ hashing trick [DLRM] */
+/* rows[i] = mix(ids[i]) mod num_rows: collisions allowed, no identity tensor. */
+int orc_hashed_rows(const int64_t *ids, int64_t n, int64_t num_rows, int64_t *rows) {
+    if (num_rows <= 0) return ORC_EINVAL;
+    for (int64_t i = 0; i < n; ++i) rows[i] = (int64_t)(orc_mix64((uint64_t)ids[i]) % (uint64_t)num_rows);
+    return ORC_OK;
+}

@@ -1,0 +1,450 @@
+"""Pins of the CPU oracle to things other than itself (CPU only).
+
+Each test checks an oracle function against something the pages or the
+mathematics fix: published SplitMix64 outputs, textbook LRU caches (batch of one
+ID = set-associative LRU; one bucket = fully associative LRU), library routines
+(numpy take / unique / cumsum / matmul), exact rational arithmetic, closed forms
+and invariants stated on the pages.  A plausible mistake in the oracle (wrong
+probe index, wrong victim order, dropped term, wrong sign, transposed operand,
+first- instead of last-occurrence) fails at least one of them.
+"""
+import collections
+import os
+import struct
+from fractions import Fraction
+
+import numpy as np
+import pytest
+
+import oracle
+import synth
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+U32 = 2.0 ** -24
+
+
+def f32_from_hex(h):
+    return np.frombuffer(struct.pack("<I", int(h, 16)), dtype=np.float32)[0]
+
+
+# ----------------------------------------------------------------- hashing
+def test_mix64_matches_published_splitmix64_outputs():
+    want = [int(l.split()[0], 16) for l in open(os.path.join(GOLDEN, "splitmix64_seed0.txt")) if l.startswith("0x")]
+    state, got = 0, []
+    for _ in want:
+        state = (state + 0x9E3779B97F4A7C15) & 0xFFFFFFFFFFFFFFFF
+        got.append(oracle.mix64(state))
+    assert got == want
+
+
+def test_bucket_is_hash_mod_bucket_count_on_twos_complement_bits():
+    for x in [0, 1, -1, -2, 123456789, -(1 << 63), (1 << 63) - 1]:
+        for nb in [1, 7, 512, 524288]:
+            assert oracle.bucket(x, nb) == oracle.mix64(x & 0xFFFFFFFFFFFFFFFF) % nb
+
+
+def test_hashed_rows_is_hash_mod_rows():
+    ids = np.array([0, 5, -7, 1 << 40, -(1 << 62)], np.int64)
+    rows = oracle.hashed_rows(ids, 25_165_824)
+    assert rows.tolist() == [oracle.mix64(int(x) & 0xFFFFFFFFFFFFFFFF) % 25_165_824 for x in ids]
+
+
+# ------------------------------------------------------------ textbook LRU
+class TextbookSetAssocLRU:
+    """Classic set-associative LRU cache: per set an LRU-ordered list of (id, way)."""
+
+    def __init__(self, sets, ways, set_of):
+        self.ways, self.set_of = ways, set_of
+        self.sets = [collections.OrderedDict() for _ in range(sets)]
+
+    def access(self, x):
+        """Returns (hit, way, evicted_id or -1)."""
+        s = self.sets[self.set_of(x)]
+        if x in s:
+            s.move_to_end(x)
+            return True, s[x], -1
+        used = set(s.values())
+        if len(s) < self.ways:
+            way = min(w for w in range(self.ways) if w not in used)
+            s[x] = way
+            return False, way, -1
+        victim, way = s.popitem(last=False)
+        s[x] = way
+        return False, way, victim
+
+
+@pytest.mark.parametrize("capacity,universe,steps", [(64, 200, 3000), (4096, 10_000, 6000)])
+def test_batch_of_one_is_textbook_set_associative_lru(capacity, universe, steps):
+    P = 8
+    nb = capacity // P
+    t = oracle.MPZCHTable(capacity, P, 4)
+    g = synth.rng(77, capacity)
+    keys = synth.universe_keys(universe, 77)
+    stream = keys[synth.zipf_ranks(g, universe, 1.1, steps)]
+    ref = TextbookSetAssocLRU(nb, P, lambda x: oracle.bucket(int(x), nb))
+    for now, x in enumerate(stream, start=1):
+        rows, hit, ev, st = t.step(np.array([x]), now)
+        h, way, victim = ref.access(int(x))
+        assert bool(hit[0]) == h
+        assert rows[0] == oracle.bucket(int(x), nb) * P + way
+        assert ev[0] == victim
+    resident = {int(x) for x in t.identity if x != -1}
+    assert resident == {k for s in ref.sets for k in s}
+
+
+def test_one_bucket_is_fully_associative_lru():
+    """capacity == probes: no hashing is involved at all."""
+    P = 8
+    t = oracle.MPZCHTable(P, P, 2)
+    seq = [5, 6, 7, 5, 8, 9, 10, 11, 12, 13, 5, 14, 6, 15, 7, 5, 16]
+    lru = collections.OrderedDict()
+    for now, x in enumerate(seq, start=1):
+        rows, hit, ev, _ = t.step(np.array([x]), now)
+        if x in lru:
+            lru.move_to_end(x)
+            assert hit[0] == 1 and ev[0] == -1
+        else:
+            victim = -1
+            if len(lru) == P:
+                victim, _ = lru.popitem(last=False)
+            lru[x] = None
+            assert hit[0] == 0 and ev[0] == victim
+    assert set(t.identity.tolist()) == set(lru)
+
+
+# ------------------------------------------------- batch-level invariants
+def _bucket_members(ids, nb):
+    return [oracle.bucket(int(x), nb) for x in ids]
+
+
+def _check_batch(tab, ids, now, rows, hit, ev, st, before_id, before_st):
+    P, C = tab.probes, tab.capacity
+    nb = C // P
+    resident0 = {int(x): s for s, x in enumerate(before_id) if x != -1}
+    # zero collisions: the identity map stays injective and every ID sits in its own bucket
+    live = tab.identity[tab.identity != -1]
+    assert np.unique(live).size == live.size
+    for s in np.nonzero(tab.identity != -1)[0]:
+        assert oracle.bucket(int(tab.identity[s]), nb) == s // P
+    seen_row = {}
+    for i, x in enumerate(ids):
+        x = int(x)
+        if x == -1:
+            assert rows[i] == -1 and hit[i] == 0
+            continue
+        # hit mask = membership at batch start (plain set)
+        assert bool(hit[i]) == (x in resident0)
+        if rows[i] >= 0:
+            assert tab.identity[rows[i]] == x
+            assert tab.stamps[rows[i]] == now
+        # all positions of one ID share one row
+        assert seen_row.setdefault(x, rows[i]) == rows[i]
+    # rows of hits never move within the batch
+    for i, x in enumerate(ids):
+        if hit[i]:
+            assert rows[i] == resident0[int(x)]
+    # evicted IDs: were resident, not in this batch, and LRU among the bucket's unpinned slots
+    batch = {int(x) for x in ids}
+    evicted = [int(e) for e in ev if e != -1]
+    assert len(evicted) == st[2] and len(set(evicted)) == len(evicted)
+    for e in evicted:
+        assert e in resident0 and e not in batch
+        s = resident0[e]
+        b = s // P
+        survivors = [before_st[q] for q in range(b * P, b * P + P)
+                     if before_id[q] != -1 and tab.identity[q] == before_id[q] and tab.stamps[q] != now]
+        assert all(before_st[s] <= v for v in survivors)
+    # an eviction only happens in a bucket that had no empty slot left
+    for e in evicted:
+        b = resident0[e] // P
+        assert not np.any(tab.identity[b * P:(b + 1) * P] == -1)
+    # overflow only when every slot of the bucket is pinned by this batch
+    for i, x in enumerate(ids):
+        if x != -1 and rows[i] == -1:
+            b = oracle.bucket(int(x), nb)
+            assert np.all(tab.stamps[b * P:(b + 1) * P] == now)
+    # inserted rows are zero vectors (a new ID never reads an evicted vector)
+    if tab.values is not None:
+        for i in range(len(ids)):
+            if rows[i] >= 0 and not hit[i]:
+                assert not np.any(tab.values[rows[i]])
+    assert st[0] == int(np.sum(hit)) and st[4] == int(np.sum(np.asarray(ids) == -1))
+
+
+def test_invariants_on_tiny_config_stream():
+    cfg = synth.TINY
+    tab = oracle.MPZCHTable(cfg.capacity, cfg.probes, cfg.dim)
+    for t, ids in enumerate(synth.mpzch_stream(cfg, 30), start=1):
+        ids = ids.copy()
+        ids[::97] = -1  # sprinkle invalid IDs
+        bid, bst = tab.identity.copy(), tab.stamps.copy()
+        tab.values[:] = 1.0  # so zero-fill is observable
+        rows, hit, ev, st = tab.step(ids, t)
+        _check_batch(tab, ids, t, rows, hit, ev, st, bid, bst)
+
+
+def _ids_in_bucket(target, nb, count, start=1):
+    out, x = [], start
+    while len(out) < count:
+        if oracle.bucket(x, nb) == target:
+            out.append(x)
+        x += 1
+    return out
+
+
+def test_crafted_bucket_overflow_empty_first_lru_and_ties():
+    P, C = 8, 64
+    nb = C // P
+    ids = _ids_in_bucket(3, nb, 24)
+    t = oracle.MPZCHTable(C, P, 4)
+    # 1) 11 new IDs in one empty bucket: first 8 by first occurrence take slots 0..7 in probe order, 3 overflow
+    batch = np.array(ids[:11][::-1] + [ids[10]], np.int64)  # reversed, plus a duplicate of the first one
+    rows, hit, ev, st = t.step(batch, 10)
+    assert rows[:8].tolist() == [3 * P + j for j in range(8)]
+    assert rows[8:11].tolist() == [-1, -1, -1] and rows[11] == rows[0]
+    assert st.tolist() == [0, 8, 0, 3, 0]
+    # 2) later batch, 2 new IDs: victims are the two smallest stamps; equal stamps -> lowest probe index
+    t.stamps[3 * P:3 * P + 8] = [50, 20, 20, 40, 30, 60, 70, 80]
+    resid = t.identity[3 * P:3 * P + 8].copy()
+    rows, hit, ev, st = t.step(np.array([ids[20], ids[21]], np.int64), 100)
+    assert rows.tolist() == [3 * P + 1, 3 * P + 2]
+    assert ev.tolist() == [resid[1], resid[2]]
+    # 3) a resident hit in the batch is pinned and can't be chosen as victim
+    t.stamps[3 * P:3 * P + 8] = [5, 6, 7, 8, 9, 10, 11, 12]
+    hot = int(t.identity[3 * P])
+    rows, hit, ev, st = t.step(np.array([ids[22], hot], np.int64), 200)
+    assert hit.tolist() == [0, 1] and rows[0] == 3 * P + 1 and rows[1] == 3 * P
+
+
+def test_lookup_only_changes_nothing():
+    t = oracle.MPZCHTable(64, 8, 4)
+    t.step(np.arange(1, 40, dtype=np.int64), 1)
+    ident, stamps, vals = t.identity.copy(), t.stamps.copy(), t.values.copy()
+    ids = np.arange(20, 60, dtype=np.int64)
+    rows, hit, ev, st = t.step(ids, 2, insert=False)
+    assert np.array_equal(ident, t.identity) and np.array_equal(stamps, t.stamps) and np.array_equal(vals, t.values)
+    for i, x in enumerate(ids):
+        if hit[i]:
+            assert ident[rows[i]] == x
+        else:
+            assert rows[i] == -1 and x not in set(ident.tolist())
+
+
+def test_non_increasing_now_is_rejected():
+    t = oracle.MPZCHTable(64, 8, 4)
+    t.step(np.array([1, 2], np.int64), 5)
+    with pytest.raises(ValueError):
+        t.step(np.array([3], np.int64), 5)
+
+
+# ------------------------------------------------------------------ gather
+def test_gather_matches_numpy_take_and_zero_for_misses():
+    g = np.random.default_rng(1)
+    table = g.standard_normal((100, 12)).astype(np.float32)
+    rows = g.integers(-1, 100, size=777)
+    out = oracle.gather(table, rows)
+    ref = np.where((rows >= 0)[:, None], np.take(table, np.maximum(rows, 0), axis=0), 0.0)
+    assert np.array_equal(out, ref.astype(np.float32))
+
+
+# ------------------------------------------------------------------- dedup
+@pytest.mark.parametrize("n", [0, 1, 5, 1000, 4099])
+def test_dedup_matches_numpy_unique_and_last_occurrence(n):
+    g = np.random.default_rng(n)
+    keys = g.integers(-50, 50, size=n).astype(np.int64) * (1 << 40) + g.integers(0, 3, size=n)
+    uq, lp, inv = oracle.dedup(keys)
+    ref_u, ref_inv = np.unique(keys, return_inverse=True)
+    assert np.array_equal(uq, ref_u)
+    assert np.array_equal(inv, ref_inv.reshape(-1))
+    last = {}
+    for i, k in enumerate(keys.tolist()):
+        last[k] = i
+    assert lp.tolist() == [last[k] for k in ref_u.tolist()]
+
+
+# --------------------------------------------------------------- Writeback
+def test_writeback_golden_fp32_cases():
+    for line in open(os.path.join(GOLDEN, "writeback_fp32_cases.txt")):
+        if not line.startswith("0x"):
+            continue
+        m, e, want = [f32_from_hex(h) for h in line.split()[:3]]
+        table = np.array([[m, 7.0]], np.float32)
+        oracle.writeback_last(table, np.array([0]), np.array([[e, 7.0]], np.float32))
+        assert table[0, 0].tobytes() == np.float32(want).tobytes(), line
+
+
+def test_writeback_closed_form_bound_last_wins_untouched():
+    g = np.random.default_rng(5)
+    C, D, n = 300, 16, 2000
+    table = (g.standard_normal((C, D)) * g.choice([1e-3, 1.0, 1e3], size=(C, 1))).astype(np.float32)
+    table[:40] = 0.0  # fresh rows
+    rows = g.integers(-1, 200, size=n)
+    e = g.standard_normal((n, D)).astype(np.float32)
+    before = table.copy()
+    oracle.writeback_last(table, rows, e)
+    last = {}
+    for i, r in enumerate(rows.tolist()):
+        if r >= 0:
+            last[r] = i
+    for r in range(C):
+        if r not in last:
+            assert np.array_equal(table[r], before[r])  # untouched rows are bit-identical
+            continue
+        ev = e[last[r]]
+        for d in range(D):
+            v, ee, out = Fraction(float(before[r, d])), Fraction(float(ev[d])), Fraction(float(table[r, d]))
+            if v == 0 or (ee / 2 <= v <= 2 * ee) or (2 * ee <= v <= ee / 2):
+                assert out == ee  # exact: 0-(0-e) and Sterbenz
+            bound = Fraction(U32) * (abs(v - ee) + abs(ee)) * (1 + Fraction(U32))
+            assert abs(out - ee) <= bound
+
+
+# ------------------------------------------------------------ SGD-sum
+def _exact_update(w, gs, lr):
+    return Fraction(float(w)) - Fraction(float(lr)) * sum(Fraction(float(x)) for x in gs)
+
+
+def test_sgd_sum_short_segments_equal_sequential_cumsum():
+    g = np.random.default_rng(9)
+    C, D, n = 50, 8, 3000
+    table = g.standard_normal((C, D)).astype(np.float32)
+    rows = g.integers(-1, C, size=n)
+    grads = (g.standard_normal((n, D)) * 1e-3).astype(np.float32)
+    before = table.copy()
+    oracle.sgd_sum(table, rows, grads, 0.01)
+    for r in range(C):
+        pos = np.nonzero(rows == r)[0]
+        if pos.size == 0:
+            assert np.array_equal(table[r], before[r])
+            continue
+        assert pos.size <= oracle.SUM_RUN
+        s = np.cumsum(grads[pos], axis=0, dtype=np.float32)[-1]  # numpy cumsum: strictly sequential
+        want = before[r] - (np.float32(0.01) * s).astype(np.float32)
+        assert np.array_equal(table[r], want.astype(np.float32))
+
+
+def test_sgd_sum_long_segment_runs_of_256_and_exact_bound():
+    g = np.random.default_rng(11)
+    D, k = 4, 1000
+    rows = np.zeros(k, np.int64)
+    grads = (g.standard_normal((k, D)) * 1e-3).astype(np.float32)
+    table = np.ones((1, D), np.float32)
+    oracle.sgd_sum(table, rows, grads, 1.0)
+    runs = [np.cumsum(grads[i:i + 256], axis=0, dtype=np.float32)[-1] for i in range(0, k, 256)]
+    s = np.cumsum(np.stack(runs), axis=0, dtype=np.float32)[-1]
+    assert np.array_equal(table[0], (np.float32(1.0) - s).astype(np.float32))
+    for d in range(D):
+        exact = _exact_update(1.0, grads[:, d], 1.0)
+        err_bound = Fraction(k + 2) * Fraction(U32) * (sum(abs(Fraction(float(x))) for x in grads[:, d]) + 1)
+        assert abs(Fraction(float(table[0, d])) - exact) <= err_bound
+
+
+def test_sgd_sum_integer_gradients_are_exact():
+    g = np.random.default_rng(3)
+    rows = g.integers(0, 5, size=2000)
+    grads = g.integers(-8, 9, size=(2000, 3)).astype(np.float32)
+    table = np.zeros((5, 3), np.float32)
+    oracle.sgd_sum(table, rows, grads, 0.5)
+    for r in range(5):
+        assert np.array_equal(table[r], -0.5 * grads[rows == r].sum(axis=0))
+
+
+# -------------------------------------------------------------------- EMA
+def test_ema_special_cases():
+    g = np.random.default_rng(2)
+    C, D, n = 20, 5, 400
+    rows = g.integers(-1, C, size=n)
+    vals = g.standard_normal((n, D)).astype(np.float32)
+    mask = (g.random(n) < 0.3).astype(np.uint8)
+    t0 = g.standard_normal((C, D)).astype(np.float32)
+    # a=0, b=1: the row ends as the last masked value exactly
+    t = t0.copy()
+    oracle.ema(t, rows, vals, mask, 0.0, 1.0)
+    for r in range(C):
+        pos = [i for i in range(n) if rows[i] == r and mask[i]]
+        assert np.array_equal(t[r], vals[pos[-1]] if pos else t0[r])
+    # a=1, b=0: unchanged; empty mask: unchanged
+    t = t0.copy()
+    oracle.ema(t, rows, vals, None, 1.0, 0.0)
+    assert np.array_equal(t, t0)
+    t = t0.copy()
+    oracle.ema(t, rows, vals, np.zeros(n, np.uint8), 0.99, 0.01)
+    assert np.array_equal(t, t0)
+
+
+def test_ema_dyadic_values_are_exact_rationals():
+    """Small dyadic inputs with a=1/2, b=1/4: no rounding occurs, result = exact recurrence."""
+    g = np.random.default_rng(4)
+    C, D, n = 6, 3, 40
+    rows = g.integers(0, C, size=n)
+    vals = g.integers(-16, 17, size=(n, D)).astype(np.float32)
+    t = g.integers(-16, 17, size=(C, D)).astype(np.float32)
+    exact = [[Fraction(float(x)) for x in row] for row in t]
+    oracle.ema(t, rows, vals, None, 0.5, 0.25)
+    for i in range(n):
+        r = rows[i]
+        exact[r] = [Fraction(1, 2) * exact[r][d] + Fraction(1, 4) * Fraction(float(vals[i, d])) for d in range(D)]
+    for r in range(C):
+        assert [Fraction(float(x)) for x in t[r]] == exact[r]
+
+
+def test_ema_within_fp64_closed_form():
+    g = np.random.default_rng(6)
+    D, k = 16, 3000
+    vals = g.standard_normal((k, D)).astype(np.float32)
+    t0 = g.standard_normal((1, D)).astype(np.float32)
+    for a, b in [(0.99, 0.01), (0.95, 0.05)]:
+        t = t0.copy()
+        oracle.ema(t, np.zeros(k, np.int64), vals, None, a, b)
+        af, bf = float(np.float32(a)), float(np.float32(b))
+        w = af ** np.arange(k - 1, -1, -1, dtype=np.float64)
+        closed = af ** k * t0[0].astype(np.float64) + bf * (w[:, None] * vals.astype(np.float64)).sum(axis=0)
+        m = af ** k * np.abs(t0[0]) + bf * (w[:, None] * np.abs(vals)).sum(axis=0)
+        # sequential fp32 rounding: at most ~2 roundings per step, damped by a
+        assert np.all(np.abs(t[0] - closed) <= 2.5 * U32 / (1 - af) * m + 1e-30)
+
+
+# ---------------------------------------------------------- dequant-score
+def test_dequant_score_special_cases_and_library_matmul():
+    g = np.random.default_rng(8)
+    C, D, R, K = 50, 32, 4, 20
+    q = g.integers(-128, 128, size=(C, D)).astype(np.int8)
+    scale = (g.random(C) * 0.01 + 1e-3).astype(np.float32)
+    bias = (g.standard_normal(C) * 0.01).astype(np.float32)
+    rows = g.integers(-1, C, size=R * K)
+    user = g.standard_normal((R, D)).astype(np.float32)
+    out = oracle.dequant_score(q, scale, bias, rows, user, K)
+    x = q.astype(np.float64) * scale[:, None].astype(np.float64) + bias[:, None].astype(np.float64)
+    ref = np.einsum("rkd,rd->rk", x[np.maximum(rows, 0)].reshape(R, K, D), user.astype(np.float64))
+    ref[rows.reshape(R, K) < 0] = 0.0
+    scale_ = np.einsum("rkd,rd->rk", np.abs(x[np.maximum(rows, 0)].reshape(R, K, D)), np.abs(user.astype(np.float64)))
+    assert np.all(np.abs(out - ref) <= 1e-7 * scale_ + 1e-30)
+    assert np.all(out[rows.reshape(R, K) < 0] == 0.0)
+    # one-hot user vector picks x_d; all-zero codes give bias * sum(u)
+    onehot = np.zeros((1, D), np.float32)
+    onehot[0, 5] = 1.0
+    r1 = np.arange(C, dtype=np.int64)
+    s1 = oracle.dequant_score(q, scale, bias, r1, onehot, C)
+    assert np.array_equal(s1[0], x[:, 5].astype(np.float32))
+    s0 = oracle.dequant_score(np.zeros_like(q), scale, bias, r1, user[:1], C)
+    assert np.allclose(s0[0], bias.astype(np.float64) * user[0].astype(np.float64).sum(), rtol=1e-6, atol=0)
+
+
+# -------------------------------------------------------------- generators
+def test_zipf_sampler_matches_pmf_chi2():
+    g = synth.rng(123, 0)
+    n_univ, s, draws = 1000, 1.1, 200_000
+    r = synth.zipf_ranks(g, n_univ, s, draws)
+    p = synth.zipf_pmf(n_univ, s)
+    obs = np.bincount(r, minlength=n_univ)[:50].astype(np.float64)
+    exp = p[:50] * draws
+    chi2 = float(np.sum((obs - exp) ** 2 / exp))
+    assert chi2 < 100.0  # 49 dof: p(chi2 > 100) ~ 2e-5
+
+
+def test_tiny_config_distinct_count_near_expectation():
+    cfg = synth.TINY
+    e_u = synth.expected_distinct(cfg.universe, cfg.zipf_s, cfg.batch)
+    assert 380 < e_u < 440
+    us = [np.unique(ids).size for ids in synth.mpzch_stream(cfg, 20)]
+    assert abs(np.mean(us) - e_u) < 15
