@@ -1,0 +1,228 @@
+"""MI355X-native hot path of an in-model embedding cache (MPZCH + Writeback).
+
+Thin ctypes binding over libhlr.so (include/hlr.h).  Every step runs in the
+library's HIP kernels; this module only marshals torch tensors (device memory
+and the current HIP stream) into the C ABI and turns status codes into
+exceptions.  There is no CPU fallback: if the library is missing, or a tensor
+is not on a GPU, the call raises.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import threading
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libhlr.so")
+
+HLR_OK = 0
+STATUS = {0: "ok", 1: "invalid argument", 2: "unsupported dim", 3: "misaligned pointer", 4: "workspace too small",
+          5: "HIP launch error"}
+WB_LAST_WINS = 0
+WB_SGD_SUM = 1
+SGD_SUM_RUN = 256
+EMPTY_ID = -1
+
+_lib = None
+_lock = threading.Lock()
+_ws = {}
+
+
+class HLRError(RuntimeError):
+    pass
+
+
+def load_library():
+    """Loads libhlr.so (raises if it has not been built)."""
+    global _lib
+    with _lock:
+        if _lib is not None:
+            return _lib
+        if not os.path.exists(LIB_PATH):
+            raise HLRError(f"{LIB_PATH} is missing: build it with `python -m hashed_lookup_row_amd.build` "
+                           "(or __graft_entry__.build())")
+        lib = ctypes.CDLL(LIB_PATH)
+        i64, i32, p, sz, f32 = ctypes.c_int64, ctypes.c_int32, ctypes.c_void_p, ctypes.c_size_t, ctypes.c_float
+        sig = {
+            "hlr_status_string": (ctypes.c_char_p, [i32]),
+            "hlr_version": (i32, []),
+            "mpzch_lookup_or_insert_workspace_size": (sz, [i64, i32]),
+            "mpzch_lookup_or_insert": (i32, [p, p, p, i64, i32, i64, p, i64, i64, i32, p, p, p, p, p, sz, p]),
+            "gather_rows": (i32, [p, i64, i64, p, i64, p, p]),
+            "dedup_ids_workspace_size": (sz, [i64]),
+            "dedup_ids": (i32, [p, i64, p, p, p, p, p, sz, p]),
+            "writeback_rows_workspace_size": (sz, [i64, i64, i64, i32]),
+            "writeback_rows": (i32, [p, i64, i64, p, p, i64, i32, f32, p, sz, p]),
+            "ema_update_rows_workspace_size": (sz, [i64, i64, i64]),
+            "ema_update_rows": (i32, [p, i64, i64, p, p, p, i64, f32, f32, p, sz, p]),
+            "gather_dequant_score": (i32, [p, p, p, i64, i64, p, i64, i64, p, p, p]),
+            "hashed_rows": (i32, [p, i64, i64, p, p]),
+        }
+        for name, (res, args) in sig.items():
+            f = getattr(lib, name)
+            f.restype = res
+            f.argtypes = args
+        _lib = lib
+        return lib
+
+
+def exported_symbols():
+    return ["hlr_status_string", "hlr_version", "mpzch_lookup_or_insert_workspace_size", "mpzch_lookup_or_insert",
+            "gather_rows", "dedup_ids_workspace_size", "dedup_ids", "writeback_rows_workspace_size",
+            "writeback_rows", "ema_update_rows_workspace_size", "ema_update_rows", "gather_dequant_score",
+            "hashed_rows"]
+
+
+def _check(rc: int, what: str):
+    if rc != HLR_OK:
+        raise HLRError(f"{what}: {STATUS.get(rc, rc)} (status {rc})")
+
+
+def _dev(t: torch.Tensor, name: str, dtype=None):
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch tensor")
+    if t.device.type != "cuda":
+        raise HLRError(f"{name} must be a GPU tensor (got {t.device}); there is no CPU path")
+    if dtype is not None and t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if not t.is_contiguous():
+        raise HLRError(f"{name} must be contiguous")
+    return t
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(device):
+    return ctypes.c_void_p(torch.cuda.current_stream(device).cuda_stream)
+
+
+def workspace(device, nbytes: int) -> torch.Tensor:
+    """Grow-only scratch buffer per device (calls on one stream may share it)."""
+    if nbytes <= 0:
+        return None
+    key = torch.device(device).index
+    buf = _ws.get(key)
+    if buf is None or buf.numel() < nbytes:
+        buf = torch.empty(int(nbytes * 1.25) + 4096, dtype=torch.uint8, device=device)
+        _ws[key] = buf
+    return buf
+
+
+def _ws_args(device, nbytes):
+    buf = workspace(device, nbytes)
+    if buf is None:
+        return None, 0
+    base = buf.data_ptr()
+    aligned = (base + 255) // 256 * 256
+    return ctypes.c_void_p(aligned), buf.numel() - (aligned - base)
+
+
+# ----------------------------------------------------------------- entry points
+def mpzch_lookup_or_insert(identity, stamps, values, probes, ids, now, insert=True, out_rows=None, out_hit=None,
+                           out_evicted=None, out_stats=None):
+    """MPZCH lookup (insert=False) or lookup-or-insert with LRU eviction.
+
+    Returns (rows int64[n], hit int8[n], evicted int64[n] or None, stats int64[6] or None)."""
+    lib = load_library()
+    _dev(identity, "identity", torch.int64)
+    if stamps is not None:
+        _dev(stamps, "stamps", torch.int64)
+    if values is not None:
+        _dev(values, "values", torch.float32)
+    _dev(ids, "ids", torch.int64)
+    dev = identity.device
+    n = ids.numel()
+    dim = values.shape[1] if values is not None else 0
+    rows = out_rows if out_rows is not None else torch.empty(n, dtype=torch.int64, device=dev)
+    hit = out_hit if out_hit is not None else torch.empty(n, dtype=torch.int8, device=dev)
+    need = lib.mpzch_lookup_or_insert_workspace_size(n, 1 if insert else 0)
+    ws, wsb = _ws_args(dev, need)
+    rc = lib.mpzch_lookup_or_insert(_ptr(identity), _ptr(stamps), _ptr(values), identity.numel(), int(probes), dim,
+                                    _ptr(ids), n, int(now), 1 if insert else 0, _ptr(rows), _ptr(hit),
+                                    _ptr(out_evicted), _ptr(out_stats), ws, wsb, _stream(dev))
+    _check(rc, "mpzch_lookup_or_insert")
+    return rows, hit, out_evicted, out_stats
+
+
+def gather_rows(table, rows, out=None):
+    lib = load_library()
+    _dev(table, "table", torch.float32)
+    _dev(rows, "rows", torch.int64)
+    n, dim = rows.numel(), table.shape[1]
+    out = out if out is not None else torch.empty((n, dim), dtype=torch.float32, device=table.device)
+    _check(lib.gather_rows(_ptr(table), table.shape[0], dim, _ptr(rows), n, _ptr(out), _stream(table.device)),
+           "gather_rows")
+    return out
+
+
+def dedup_ids(keys, out_unique=None, out_last_pos=None, out_inverse=None, out_num_unique=None, inverse=True):
+    """Returns (unique[n], last_pos[n], inverse[n] or None, num_unique int64[1]); first u entries valid."""
+    lib = load_library()
+    _dev(keys, "keys", torch.int64)
+    dev, n = keys.device, keys.numel()
+    uq = out_unique if out_unique is not None else torch.empty(n, dtype=torch.int64, device=dev)
+    lp = out_last_pos if out_last_pos is not None else torch.empty(n, dtype=torch.int64, device=dev)
+    inv = out_inverse if out_inverse is not None else (torch.empty(n, dtype=torch.int64, device=dev)
+                                                       if inverse else None)
+    nu = out_num_unique if out_num_unique is not None else torch.empty(1, dtype=torch.int64, device=dev)
+    ws, wsb = _ws_args(dev, lib.dedup_ids_workspace_size(n))
+    _check(lib.dedup_ids(_ptr(keys), n, _ptr(uq), _ptr(lp), _ptr(inv), _ptr(nu), ws, wsb, _stream(dev)),
+           "dedup_ids")
+    return uq, lp, inv, nu
+
+
+def writeback_rows(table, rows, src, mode=WB_LAST_WINS, lr=1.0):
+    lib = load_library()
+    _dev(table, "table", torch.float32)
+    _dev(rows, "rows", torch.int64)
+    _dev(src, "src", torch.float32)
+    n, dim = rows.numel(), table.shape[1]
+    if src.numel() != n * dim:
+        raise HLRError("src must be [n, dim]")
+    ws, wsb = _ws_args(table.device, lib.writeback_rows_workspace_size(table.shape[0], dim, n, int(mode)))
+    _check(lib.writeback_rows(_ptr(table), table.shape[0], dim, _ptr(rows), _ptr(src), n, int(mode), float(lr), ws,
+                              wsb, _stream(table.device)), "writeback_rows")
+    return table
+
+
+def ema_update_rows(table, rows, vals, mask, a, b):
+    lib = load_library()
+    _dev(table, "table", torch.float32)
+    _dev(rows, "rows", torch.int64)
+    _dev(vals, "vals", torch.float32)
+    if mask is not None:
+        _dev(mask, "mask", torch.uint8)
+    n, dim = rows.numel(), table.shape[1]
+    if vals.numel() != n * dim:
+        raise HLRError("vals must be [n, dim]")
+    ws, wsb = _ws_args(table.device, lib.ema_update_rows_workspace_size(table.shape[0], dim, n))
+    _check(lib.ema_update_rows(_ptr(table), table.shape[0], dim, _ptr(rows), _ptr(vals), _ptr(mask), n, float(a),
+                               float(b), ws, wsb, _stream(table.device)), "ema_update_rows")
+    return table
+
+
+def gather_dequant_score(qtable, scale, bias, rows, user, cands, out=None):
+    lib = load_library()
+    _dev(qtable, "qtable", torch.int8)
+    _dev(scale, "scale", torch.float32)
+    _dev(bias, "bias", torch.float32)
+    _dev(rows, "rows", torch.int64)
+    _dev(user, "user", torch.float32)
+    nreq, dim = user.shape[0], qtable.shape[1]
+    out = out if out is not None else torch.empty((nreq, cands), dtype=torch.float32, device=qtable.device)
+    _check(lib.gather_dequant_score(_ptr(qtable), _ptr(scale), _ptr(bias), qtable.shape[0], dim, _ptr(rows), nreq,
+                                    int(cands), _ptr(user), _ptr(out), _stream(qtable.device)),
+           "gather_dequant_score")
+    return out
+
+
+def hashed_rows(ids, num_rows, out=None):
+    lib = load_library()
+    _dev(ids, "ids", torch.int64)
+    out = out if out is not None else torch.empty(ids.numel(), dtype=torch.int64, device=ids.device)
+    _check(lib.hashed_rows(_ptr(ids), ids.numel(), int(num_rows), _ptr(out), _stream(ids.device)), "hashed_rows")
+    return out

@@ -1,0 +1,375 @@
+// MPZCH lookup / insert with LRU eviction.
+//
+// "Memory Layer: Train the In-Model Cache for Recommendation Models", sec. 2:
+// an identity tensor maps raw item IDs to rows with no collisions (one ID per
+// row), capacity is bounded, rows are recycled least-recently-used, and the
+// LRU metadata shares the row index.
+//
+// A batch is applied in two phases.  Phase 1 (probe): every ID resident at
+// batch start hits and pins its slot (stamp = now).  Phase 2: the distinct
+// missed IDs of each bucket, in order of first occurrence, take the bucket's
+// slots in preference order — empty slots by probe index, then unpinned slots
+// by (stamp, probe index) — one per ID; the rest overflow.  Taking the k-th
+// preferred slot for the k-th new ID is exactly the serial
+// first-empty-else-LRU rule, because every insert pins the slot it takes.
+//
+// GPU plan (all on one stream, no host sync):
+//   mz_init    clear the transient miss table / bucket table and stats
+//   mz_probe   one lane per position: bucket probe, hit + pin, or register
+//              the miss (hash table keyed by ID, atomicMin of first position);
+//              the lane that creates an ID's entry links it into its bucket's
+//              list (hash table keyed by bucket, atomicExch list push)
+//   mz_assign  one lane per bucket with pending IDs: picks the IDs with the
+//              smallest first positions, commits them with atomic CAS on the
+//              identity slot (a failed CAS would mean a broken invariant and
+//              is counted), stamps them, records the displaced ID
+//   mz_resolve one lane per missed position: row of its ID; the first
+//              occurrence reports the eviction and the wave zero-fills the
+//              new row cooperatively (16-byte stores)
+#include "hlr_common.hpp"
+
+namespace {
+using namespace hlr;
+
+constexpr int kMaxProbes = 32;
+constexpr int kThreads = 256;
+
+struct MZWork {
+  int64_t *mkey;   // miss table: ID (-1 = free)
+  int32_t *mfpos;  // first occurrence of the ID in the batch
+  int32_t *mnext;  // next entry of the same bucket (-1 = end)
+  int64_t *mslot;  // slot given to the ID (-1 = overflow)
+  int64_t *mevict; // ID displaced by the insert (-1 = slot was empty)
+  int64_t *bkey;   // bucket table: bucket index (-1 = free)
+  int32_t *bhead;  // first miss-table entry of the bucket's list
+  int32_t *pent;   // per position: miss-table entry, -1 = hit / invalid
+  unsigned long long *stats;  // [6] used when the caller passes no stats array
+  uint32_t cap;    // entries of each hash table (power of two)
+};
+
+size_t mz_layout(int64_t n, MZWork *w, void *base) {
+  Carver c(base);
+  const uint64_t cap = next_pow2(static_cast<uint64_t>(n > 32 ? 2 * n : 64));
+  w->mkey = c.take<int64_t>(cap);
+  w->mfpos = c.take<int32_t>(cap);
+  w->mnext = c.take<int32_t>(cap);
+  w->mslot = c.take<int64_t>(cap);
+  w->mevict = c.take<int64_t>(cap);
+  w->bkey = c.take<int64_t>(cap);
+  w->bhead = c.take<int32_t>(cap);
+  w->pent = c.take<int32_t>(static_cast<size_t>(n > 0 ? n : 1));
+  w->stats = c.take<unsigned long long>(8);
+  w->cap = static_cast<uint32_t>(cap);
+  return c.off;
+}
+
+__device__ __forceinline__ int64_t ld_relaxed(const int64_t *p) {
+  return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+__device__ __forceinline__ uint64_t bucket_of(uint64_t h, uint64_t nb, bool pow2) {
+  return pow2 ? (h & (nb - 1)) : (h % nb);
+}
+
+__global__ void __launch_bounds__(kThreads) mz_init(MZWork w, unsigned long long *stats) {
+  const uint32_t stride = kThreads * gridDim.x;
+  for (uint32_t i = blockIdx.x * kThreads + threadIdx.x; i < w.cap; i += stride) {
+    w.mkey[i] = -1;
+    w.mfpos[i] = 0x7fffffff;
+    w.mslot[i] = -1;
+    w.bkey[i] = -1;
+    w.bhead[i] = -1;
+  }
+  if (stats && blockIdx.x == 0 && threadIdx.x < 6) stats[threadIdx.x] = 0ull;
+}
+
+__global__ void mz_zero_stats(unsigned long long *stats) {
+  if (threadIdx.x < 6) stats[threadIdx.x] = 0ull;
+}
+
+template <int P>
+__global__ void __launch_bounds__(kThreads)
+    mz_probe(const int64_t *__restrict__ ids, int64_t n, const int64_t *__restrict__ identity, int64_t *stamps,
+             uint64_t nb, bool nb_pow2, int probes_rt, int64_t now, int insert, int64_t *__restrict__ rows,
+             int8_t *__restrict__ hit, int64_t *__restrict__ evicted, MZWork w, unsigned long long *stats) {
+  const int probes = P > 0 ? P : probes_rt;
+  const int64_t i = static_cast<int64_t>(blockIdx.x) * kThreads + threadIdx.x;
+  const bool valid = i < n;
+  const int64_t id = valid ? ids[i] : HLR_EMPTY_ID;
+  const bool invalid = valid && id == HLR_EMPTY_ID;
+  int64_t row = -1;
+  uint64_t h = 0, b = 0;
+  if (valid && !invalid) {
+    h = mix64(static_cast<uint64_t>(id));
+    b = bucket_of(h, nb, nb_pow2);
+    const int64_t base = static_cast<int64_t>(b) * probes;
+    if (P == 8) {
+      const longlong2 *q = reinterpret_cast<const longlong2 *>(identity + base);
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const longlong2 v = q[j];
+        if (v.x == id) row = base + 2 * j;
+        if (v.y == id) row = base + 2 * j + 1;
+      }
+    } else {
+      for (int j = 0; j < probes; ++j)
+        if (identity[base + j] == id) row = base + j;
+    }
+  }
+  const bool is_hit = row >= 0;
+  const bool is_miss = valid && !invalid && !is_hit;
+  if (valid) {
+    rows[i] = row;
+    hit[i] = is_hit ? 1 : 0;
+    if (evicted) evicted[i] = HLR_EMPTY_ID;
+    if (insert) {
+      if (is_hit) stamps[row] = now;
+      w.pent[i] = -1;
+    }
+  }
+  if (stats) {
+    wave_count(&stats[0], is_hit);
+    wave_count(&stats[4], invalid);
+  }
+  if (!(insert && is_miss)) return;
+  // Register the missed ID in the transient miss table (keyed by ID).
+  const uint32_t mmask = w.cap - 1;
+  uint32_t s = static_cast<uint32_t>(h >> 32) & mmask;
+  bool created = false;
+  for (;;) {
+    const int64_t k = ld_relaxed(&w.mkey[s]);
+    if (k == id) break;
+    if (k == -1) {
+      const int64_t prev = atomic_cas_i64(&w.mkey[s], -1, id);
+      if (prev == -1) {
+        created = true;
+        break;
+      }
+      if (prev == id) break;
+    }
+    s = (s + 1) & mmask;
+  }
+  atomicMin(&w.mfpos[s], static_cast<int32_t>(i));
+  w.pent[i] = static_cast<int32_t>(s);
+  if (!created) return;
+  // Push the new entry onto its bucket's list (bucket table keyed by bucket index).
+  uint32_t t = static_cast<uint32_t>(mix64(b ^ 0x5851f42d4c957f2dULL) >> 32) & mmask;
+  const int64_t bk = static_cast<int64_t>(b);
+  for (;;) {
+    const int64_t k = ld_relaxed(&w.bkey[t]);
+    if (k == bk) break;
+    if (k == -1) {
+      const int64_t prev = atomic_cas_i64(&w.bkey[t], -1, bk);
+      if (prev == -1 || prev == bk) break;
+    }
+    t = (t + 1) & mmask;
+  }
+  w.mnext[s] = atomicExch(&w.bhead[t], static_cast<int32_t>(s));
+}
+
+// One lane per bucket-table entry: the serial insert rule of one bucket.
+template <int P>
+__global__ void __launch_bounds__(kThreads)
+    mz_assign(int64_t *identity, int64_t *stamps, int probes_rt, int64_t now, MZWork w,
+              unsigned long long *stats) {
+  constexpr int PM = P > 0 ? P : kMaxProbes;
+  const int probes = P > 0 ? P : probes_rt;
+  const uint32_t t = blockIdx.x * kThreads + threadIdx.x;
+  int ins = 0, evs = 0, ovf = 0, bad = 0;
+  const int64_t bk = t < w.cap ? w.bkey[t] : -1;
+  if (bk >= 0) {
+    const int64_t base = bk * probes;
+    int64_t idv[PM], stv[PM];
+    int rank[PM];
+#pragma unroll
+    for (int j = 0; j < PM; ++j) {
+      if (j < probes) {
+        idv[j] = identity[base + j];
+        stv[j] = stamps[base + j];
+      }
+    }
+    int nempty = 0, nfree = 0;
+#pragma unroll
+    for (int j = 0; j < PM; ++j) {
+      if (j < probes) {
+        if (idv[j] == HLR_EMPTY_ID) ++nempty;
+        else if (stv[j] < now) ++nfree;
+      }
+    }
+    const int avail = nempty + nfree;
+    // Preference rank of every slot: empties by probe index, then unpinned by (stamp, index).
+#pragma unroll
+    for (int j = 0; j < PM; ++j) {
+      if (j >= probes) continue;
+      int r = PM + 1;
+      if (idv[j] == HLR_EMPTY_ID) {
+        r = 0;
+#pragma unroll
+        for (int k = 0; k < PM; ++k)
+          if (k < j && idv[k] == HLR_EMPTY_ID) ++r;
+      } else if (stv[j] < now) {
+        r = nempty;
+#pragma unroll
+        for (int k = 0; k < PM; ++k) {
+          if (k < probes && idv[k] != HLR_EMPTY_ID && stv[k] < now &&
+              (stv[k] < stv[j] || (stv[k] == stv[j] && k < j)))
+            ++r;
+        }
+      }
+      rank[j] = r;
+    }
+    // Walk the bucket's pending IDs, keeping the `avail` smallest first positions (sorted).
+    int32_t sf[PM], se[PM];
+    int cnt = 0, L = 0;
+    int32_t lastf = 0;  // largest kept first position (valid once cnt == avail)
+    for (int32_t e = w.bhead[t]; e != -1; e = w.mnext[e]) {
+      const int32_t f = w.mfpos[e];
+      ++L;
+      int pos;
+      if (cnt < avail) pos = cnt++;
+      else if (cnt > 0 && f < lastf) pos = cnt - 1;
+      else continue;
+#pragma unroll
+      for (int k = 0; k < PM; ++k)
+        if (k == pos) {
+          sf[k] = f;
+          se[k] = e;
+        }
+#pragma unroll
+      for (int k = PM - 1; k > 0; --k) {
+        if (k <= pos && sf[k] < sf[k - 1]) {
+          const int32_t tf = sf[k], te = se[k];
+          sf[k] = sf[k - 1];
+          se[k] = se[k - 1];
+          sf[k - 1] = tf;
+          se[k - 1] = te;
+        }
+      }
+#pragma unroll
+      for (int k = 0; k < PM; ++k)
+        if (k == cnt - 1) lastf = sf[k];
+    }
+#pragma unroll
+    for (int k = 0; k < PM; ++k) {
+      if (k >= cnt) continue;
+      int j = -1;
+#pragma unroll
+      for (int q = 0; q < PM; ++q)
+        if (q < probes && rank[q] == k) j = q;
+      const int64_t slot = base + j;
+      const int64_t old = idv[j];
+      const int64_t id = w.mkey[se[k]];
+      const int64_t prev = atomic_cas_i64(&identity[slot], old, id);
+      if (prev != old) ++bad;
+      stamps[slot] = now;
+      w.mslot[se[k]] = slot;
+      w.mevict[se[k]] = old;
+      ++ins;
+      if (old != HLR_EMPTY_ID) ++evs;
+    }
+    ovf = L - cnt;
+  }
+  if (stats) {
+    if (ins) atomicAdd(&stats[1], (unsigned long long)ins);
+    if (evs) atomicAdd(&stats[2], (unsigned long long)evs);
+    if (ovf) atomicAdd(&stats[3], (unsigned long long)ovf);
+    if (bad) atomicAdd(&stats[5], (unsigned long long)bad);
+  }
+}
+
+__global__ void __launch_bounds__(kThreads)
+    mz_resolve(int64_t n, float *values, int64_t dim, MZWork w, int64_t *__restrict__ rows,
+               int64_t *__restrict__ evicted) {
+  const int64_t i = static_cast<int64_t>(blockIdx.x) * kThreads + threadIdx.x;
+  const int32_t e = i < n ? w.pent[i] : -1;
+  int64_t slot = -1;
+  bool zero_fill = false;
+  if (e >= 0) {
+    slot = w.mslot[e];
+    rows[i] = slot;
+    const bool first = w.mfpos[e] == static_cast<int32_t>(i);
+    if (first && slot >= 0) {
+      if (evicted) evicted[i] = w.mevict[e];
+      zero_fill = values != nullptr;
+    }
+  }
+  // The whole wave zero-fills each new row: 16-byte stores, lanes along the row.
+  uint64_t m = ballot(zero_fill);
+  const int64_t v4 = dim >> 2;
+  const float4 z = make_float4(0.f, 0.f, 0.f, 0.f);
+  while (m) {
+    const int l = __builtin_ctzll(m);
+    m &= m - 1;
+    const int64_t s = readlane_i64(slot, l);
+    float4 *dst = reinterpret_cast<float4 *>(values) + s * v4;
+    for (int64_t c = lane_id(); c < v4; c += kWave) dst[c] = z;
+  }
+}
+
+template <int P>
+void mz_launch(int64_t *identity, int64_t *stamps, float *values, int64_t capacity, int probes, int64_t dim,
+               const int64_t *ids, int64_t n, int64_t now, int insert, int64_t *rows, int8_t *hit,
+               int64_t *evicted, unsigned long long *stats, MZWork &w, hipStream_t s) {
+  const uint64_t nb = static_cast<uint64_t>(capacity / probes);
+  const bool pow2 = (nb & (nb - 1)) == 0;
+  const int gpos = grid_for(n, kThreads);
+  if (insert) {
+    int gi = grid_for(w.cap, kThreads * 4);
+    if (gi > 2048) gi = 2048;
+    mz_init<<<gi, kThreads, 0, s>>>(w, stats);
+  } else if (stats) {
+    mz_zero_stats<<<1, 64, 0, s>>>(stats);
+  }
+  mz_probe<P><<<gpos, kThreads, 0, s>>>(ids, n, identity, stamps, nb, pow2, probes, now, insert, rows, hit, evicted,
+                                         w, stats);
+  if (!insert) return;
+  mz_assign<P><<<grid_for(w.cap, kThreads), kThreads, 0, s>>>(identity, stamps, probes, now, w, stats);
+  mz_resolve<<<gpos, kThreads, 0, s>>>(n, values, dim, w, rows, evicted);
+}
+
+}  // namespace
+
+extern "C" size_t mpzch_lookup_or_insert_workspace_size(int64_t n, int32_t insert) {
+  if (!insert || n < 0) return 0;
+  MZWork w;
+  return mz_layout(n, &w, nullptr);
+}
+
+extern "C" hlr_status mpzch_lookup_or_insert(int64_t *identity, int64_t *stamps, float *values, int64_t capacity,
+                                             int32_t probes, int64_t dim, const int64_t *ids, int64_t n,
+                                             int64_t now, int32_t insert, int64_t *out_rows, int8_t *out_hit,
+                                             int64_t *out_evicted, int64_t *out_stats, void *ws, size_t ws_bytes,
+                                             hipStream_t stream) {
+  if (n < 0 || n > kMaxN || capacity <= 0 || probes < 1 || probes > kMaxProbes || capacity % probes != 0)
+    return HLR_INVALID_ARG;
+  if (insert != 0 && insert != 1) return HLR_INVALID_ARG;
+  if (!identity || (insert && !stamps)) return HLR_INVALID_ARG;
+  if (n > 0 && (!ids || !out_rows || !out_hit)) return HLR_INVALID_ARG;
+  if (values && (dim <= 0 || dim % 4 != 0)) return HLR_UNSUPPORTED_DIM;
+  if (!aligned(identity, 8) || (stamps && !aligned(stamps, 8)) || (ids && !aligned(ids, 8)) ||
+      (out_rows && !aligned(out_rows, 8)) || (out_evicted && !aligned(out_evicted, 8)) ||
+      (out_stats && !aligned(out_stats, 8)) || (values && !aligned(values, 16)))
+    return HLR_MISALIGNED;
+  // the aligned-bucket fast path reads a bucket as 16-byte pairs
+  if (probes == 8 && !aligned(identity, 16)) return HLR_MISALIGNED;
+  MZWork w{};
+  if (insert) {
+    const size_t need = mz_layout(n, &w, nullptr);
+    if (!ws || ws_bytes < need) return HLR_WORKSPACE_TOO_SMALL;
+    if (!aligned(ws, 256)) return HLR_MISALIGNED;
+    mz_layout(n, &w, ws);
+  }
+  unsigned long long *stats = out_stats ? reinterpret_cast<unsigned long long *>(out_stats)
+                                        : (insert ? w.stats : nullptr);
+  if (n == 0) {
+    if (out_stats) mz_zero_stats<<<1, 64, 0, stream>>>(stats);
+    return launch_status();
+  }
+  if (probes == 8)
+    mz_launch<8>(identity, stamps, values, capacity, probes, dim, ids, n, now, insert, out_rows, out_hit, out_evicted,
+                 stats, w, stream);
+  else
+    mz_launch<0>(identity, stamps, values, capacity, probes, dim, ids, n, now, insert, out_rows, out_hit,
+                 out_evicted, stats, w, stream);
+  return launch_status();
+}

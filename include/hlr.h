@@ -1,0 +1,192 @@
+/*
+ * hlr.h — C ABI of libhlr.so, the MI355X (gfx950) hot path of an in-model
+ * embedding cache for recommendation models.
+ *
+ * The operations follow these pages (cited by title and section):
+ *  [ML]   "Memory Layer: Train the In-Model Cache for Recommendation Models",
+ *         sec. 2 (method) and sec. 5 (limitations);
+ *  [CS3]  "CS3: Efficient Online Capability Synergy for Two-Tower
+ *         Recommendation", sec. 2 (method: CTS and CMS);
+ *  [DLRM] "DLRMv4: MLPerf recommendation training goes sequential", feature
+ *         expansion paragraph (hashed tables, 512-d fp32 rows, per-token
+ *         unpooled lookups).
+ *
+ * Conventions shared by every entry point
+ *  - Array arguments are DEVICE pointers on the current HIP device, owned by
+ *    the caller.  The library allocates nothing and keeps no state between
+ *    calls; every launch is enqueued on `stream` and no call synchronises.
+ *  - Rows are int64 indices into a table of `num_rows` rows of `dim` values,
+ *    row-major; -1 means "no row" (a miss or an overflow) and reads as the
+ *    zero vector.  Rows outside [-1, num_rows) are a caller error: kernels skip
+ *    them (treat them like -1) so memory stays safe; results for them are
+ *    unspecified.
+ *  - float tables, value and output arrays must be 16-byte aligned and
+ *    `dim % 4 == 0` (rows are moved as 16-byte vectors); int64 arrays must be
+ *    8-byte aligned.  n counts positions; 0 <= n < 2^31.
+ *  - Scratch: entry points that need device scratch take (ws, ws_bytes);
+ *    `*_workspace_size(...)` gives the byte count for a given problem.  ws
+ *    must be 256-byte aligned and may be NULL only when that size is 0.  The
+ *    workspace is scratch only: its contents on entry do not matter and calls
+ *    that share one workspace must be ordered on one stream.
+ *  - Every entry point returns an hlr_status.  Host-checkable faults return
+ *    an error before anything is enqueued.  Device-side data faults are never
+ *    thrown; mpzch_lookup_or_insert counts them in out_stats.
+ *  - Floating point: no contraction into FMA; each fp32 operation named
+ *    below rounds on its own (IEEE round-to-nearest-even, denormals kept).
+ */
+#ifndef HLR_H
+#define HLR_H
+
+#include <stddef.h>
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef int32_t hlr_status;
+#define HLR_OK 0
+#define HLR_INVALID_ARG 1        /* bad size, NULL where not allowed, bad mode */
+#define HLR_UNSUPPORTED_DIM 2    /* dim % 4 != 0 (dim % 16 != 0 for int8 rows) or dim <= 0 */
+#define HLR_MISALIGNED 3         /* pointer not aligned as required */
+#define HLR_WORKSPACE_TOO_SMALL 4
+#define HLR_HIP_ERROR 5          /* a launch failed (hipGetLastError) */
+
+#define HLR_EMPTY_ID (-1)        /* identity value of an empty slot; also an invalid input ID */
+
+/* Human-readable name of a status code (static string, never NULL). */
+const char *hlr_status_string(hlr_status status);
+
+/* Library ABI version (major*100 + minor). */
+int32_t hlr_version(void);
+
+/* ------------------------------------------------------------------------
+ * MPZCH lookup / insert with LRU eviction   [ML] sec. 2
+ *
+ * The identity tensor maps raw int64 item IDs to table rows with no
+ * collisions (one ID per row).  Capacity is bounded and rows are recycled
+ * least-recently-used; metadata (the LRU stamp) shares the row index.
+ *
+ *  identity[capacity]  int64, -1 = empty slot.  In/out (insert mode).
+ *  stamps[capacity]    int64 LRU stamps (last batch that touched the slot;
+ *                      -1 for never).  In/out (insert mode).
+ *  values[capacity*dim] fp32 rows, nullable: when given, rows that receive a
+ *                      new ID are zero-filled (a new ID never reads an
+ *                      evicted ID's vector; a miss reads zero, [ML] sec. 2).
+ *  capacity % probes == 0; probes in [1, 32].  Bucket of x =
+ *  SplitMix64-finaliser(x) mod (capacity/probes); x probes the `probes`
+ *  consecutive slots of its bucket in order.
+ *  ids[n]              int64 item IDs; -1 is invalid (row -1, counted).
+ *  now                 int64 step counter, strictly greater than every stamp
+ *                      already stored (insert mode); not checked on device.
+ *  insert              1 = training batch (lookup, pin, insert, evict);
+ *                      0 = serving lookup (reads only, changes nothing).
+ *  Semantics (two phases): every ID resident at batch start is a hit and its
+ *  slot's stamp becomes `now` (pinned).  Then the distinct missed IDs, in
+ *  order of first occurrence in `ids`, are inserted: each takes the first
+ *  empty slot of its bucket, else the unpinned slot (stamp < now) with the
+ *  smallest stamp (lowest probe index on ties), else it overflows (row -1).
+ *  out_rows[n]         slot of each position's ID, or -1.
+ *  out_hit[n]          int8, 1 iff the ID was resident at batch start.
+ *  out_evicted[n]      nullable; the ID displaced by an insert, written at that
+ *                      ID's first occurrence; -1 elsewhere.
+ *  out_stats[6]        nullable, device int64: {hit positions, inserts,
+ *                      evictions, overflows (distinct IDs), invalid positions,
+ *                      internal consistency failures (always 0)}.
+ *  Workspace: mpzch_lookup_or_insert_workspace_size(n, insert) bytes
+ *  (0 in lookup-only mode).
+ * --------------------------------------------------------------------- */
+size_t mpzch_lookup_or_insert_workspace_size(int64_t n, int32_t insert);
+hlr_status mpzch_lookup_or_insert(int64_t *identity, int64_t *stamps, float *values, int64_t capacity,
+                                  int32_t probes, int64_t dim, const int64_t *ids, int64_t n, int64_t now,
+                                  int32_t insert, int64_t *out_rows, int8_t *out_hit, int64_t *out_evicted,
+                                  int64_t *out_stats, void *ws, size_t ws_bytes, hipStream_t stream);
+
+/* ------------------------------------------------------------------------
+ * Row gather   [ML] sec. 2 (the model reads the cached row M[i])
+ *  out[i][:] = table[rows[i]][:] for rows[i] >= 0, zeros for rows[i] == -1.
+ *  table[num_rows*dim], out[n*dim] fp32, 16-byte aligned, dim % 4 == 0.
+ * --------------------------------------------------------------------- */
+hlr_status gather_rows(const float *table, int64_t num_rows, int64_t dim, const int64_t *rows, int64_t n,
+                       float *out, hipStream_t stream);
+
+/* ------------------------------------------------------------------------
+ * In-batch deduplication   [ML] sec. 2 (duplicate IDs of a batch are
+ * deduplicated so each row gets one exact write)
+ *  keys[n]             int64 keys (IDs or rows).
+ *  out_unique[n]       distinct keys in ascending signed order (first u used).
+ *  out_last_pos[n]     position of the LAST occurrence of each distinct key.
+ *  out_inverse[n]      nullable; index into out_unique of each position's key.
+ *  out_num_unique      device int64 scalar: u.
+ *  Workspace: dedup_ids_workspace_size(n) bytes.
+ * --------------------------------------------------------------------- */
+size_t dedup_ids_workspace_size(int64_t n);
+hlr_status dedup_ids(const int64_t *keys, int64_t n, int64_t *out_unique, int64_t *out_last_pos,
+                     int64_t *out_inverse, int64_t *out_num_unique, void *ws, size_t ws_bytes,
+                     hipStream_t stream);
+
+/* ------------------------------------------------------------------------
+ * Row updates from a batch   [ML] sec. 2 (Writeback); [DLRM] (per-row SGD)
+ *  table[num_rows*dim] fp32 in place; rows[n]; src[n*dim] fp32.
+ *  mode HLR_WB_LAST_WINS: src holds the item-tower vectors e_i.  Every
+ *    distinct row r >= 0 takes one exact write from its LAST occurrence p:
+ *    g = fl(M[r] - e_p), M[r] = fl(M[r] - g)   (exact SGD at learning rate 1,
+ *    so M[r] becomes e_p up to these two roundings).  lr must be 1.
+ *  mode HLR_WB_SGD_SUM: src holds gradients g_i.  The gradients of each row
+ *    are summed in batch order within runs of 256 consecutive occurrences,
+ *    run totals added in batch order (s), then M[r] = fl(M[r] - fl(lr*s)).
+ *  Rows not in the batch are untouched.
+ *  Workspace: writeback_rows_workspace_size(num_rows, dim, n, mode) bytes.
+ * --------------------------------------------------------------------- */
+#define HLR_WB_LAST_WINS 0
+#define HLR_WB_SGD_SUM 1
+#define HLR_SGD_SUM_RUN 256
+size_t writeback_rows_workspace_size(int64_t num_rows, int64_t dim, int64_t n, int32_t mode);
+hlr_status writeback_rows(float *table, int64_t num_rows, int64_t dim, const int64_t *rows, const float *src,
+                          int64_t n, int32_t mode, float lr, void *ws, size_t ws_bytes, hipStream_t stream);
+
+/* ------------------------------------------------------------------------
+ * EMA row updates   [CS3] sec. 2 (CTS: c <- a*c + (1-a)*v on positive
+ * interactions; CMS: s <- b*s + (1-b)*h on every interaction)
+ *  For every position i in batch order with rows[i] >= 0 and mask[i] != 0
+ *  (mask NULL = every position): T[r] = fl(fl(a*T[r]) + fl(b*vals[i])),
+ *  element-wise; duplicates of a row are applied in batch order, so the
+ *  result equals the sequential loop bit for bit.  a and b are passed
+ *  separately (b is not recomputed as 1-a).
+ *  table[num_rows*dim] fp32 in place; vals[n*dim] fp32; mask[n] uint8.
+ *  Workspace: ema_update_rows_workspace_size(num_rows, dim, n) bytes.
+ * --------------------------------------------------------------------- */
+size_t ema_update_rows_workspace_size(int64_t num_rows, int64_t dim, int64_t n);
+hlr_status ema_update_rows(float *table, int64_t num_rows, int64_t dim, const int64_t *rows, const float *vals,
+                           const uint8_t *mask, int64_t n, float a, float b, void *ws, size_t ws_bytes,
+                           hipStream_t stream);
+
+/* ------------------------------------------------------------------------
+ * Serving score: int8 row dequantisation fused with a dot product
+ *   [ML] sec. 1 (O(1K) candidates scored per request) and sec. 5 (serving
+ *   reads int8 rows); miss -> zero vector [ML] sec. 2.
+ *  qtable[num_rows*dim] int8 (16-byte aligned, dim % 16 == 0);
+ *  scale[num_rows], bias[num_rows] fp32: x_d = q_d*scale + bias.
+ *  rows[num_requests*cands_per_request] (from a lookup-only MPZCH call);
+ *  user_vecs[num_requests*dim] fp32.
+ *  out_scores[r*cands + c] = sum_d x_d * user[r][d], dequantisation and sum
+ *  evaluated in fp64 and rounded once to fp32; a row of -1 scores 0.0f.
+ * --------------------------------------------------------------------- */
+hlr_status gather_dequant_score(const int8_t *qtable, const float *scale, const float *bias, int64_t num_rows,
+                                int64_t dim, const int64_t *rows, int64_t num_requests,
+                                int64_t cands_per_request, const float *user_vecs, float *out_scores,
+                                hipStream_t stream);
+
+/* ------------------------------------------------------------------------
+ * Hashed-table row mapping   [DLRM] feature expansion (hashed tables)
+ *  out_rows[i] = SplitMix64-finaliser(ids[i]) mod num_rows (collisions
+ *  allowed; no identity tensor).  num_rows >= 1.
+ * --------------------------------------------------------------------- */
+hlr_status hashed_rows(const int64_t *ids, int64_t n, int64_t num_rows, int64_t *out_rows, hipStream_t stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* HLR_H */

@@ -1,0 +1,119 @@
+"""Host-side checks of the C ABI (CPU only: no kernel is launched).
+
+The library must load, export every entry point include/hlr.h declares, and
+reject host-checkable faults with the documented status before enqueueing
+anything.
+"""
+import ctypes
+import os
+import re
+
+import pytest
+
+import hashed_lookup_row_amd as hlr
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "hlr.h")
+
+OK, INVALID, DIM, MISALIGNED, WS_SMALL = 0, 1, 2, 3, 4
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(hlr.LIB_PATH):
+        pytest.fail("libhlr.so is not built (run __graft_entry__.build())")
+    return hlr.load_library()
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?\w[\w\s\*]*?\b(\w+)\s*\(", text, flags=re.M)) - {"defined"})
+
+
+def test_every_declared_function_is_exported(lib):
+    names = declared_functions()
+    assert len(names) >= 13, names
+    for name in names:
+        assert hasattr(lib, name), name
+    assert set(names) == set(hlr.exported_symbols())
+
+
+def test_status_strings_and_version(lib):
+    for code, s in hlr.STATUS.items():
+        assert lib.hlr_status_string(code).decode() == s
+    assert lib.hlr_status_string(99).decode() == "unknown status"
+    assert lib.hlr_version() >= 100
+
+
+def test_workspace_sizes_are_host_only_and_monotone(lib):
+    assert lib.mpzch_lookup_or_insert_workspace_size(1000, 0) == 0
+    a = lib.mpzch_lookup_or_insert_workspace_size(1000, 1)
+    b = lib.mpzch_lookup_or_insert_workspace_size(65536, 1)
+    assert 0 < a < b and b % 256 == 0
+    assert lib.dedup_ids_workspace_size(65536) > lib.dedup_ids_workspace_size(100) > 0
+    assert lib.writeback_rows_workspace_size(1 << 22, 512, 65536, 0) > 0
+    assert lib.writeback_rows_workspace_size(1 << 22, 512, 65536, 1) > 0
+    assert lib.ema_update_rows_workspace_size(1 << 20, 128, 262144) > 0
+
+
+P16 = ctypes.c_void_p(1 << 20)       # 16-byte aligned stand-in address (never dereferenced)
+P_ODD = ctypes.c_void_p((1 << 20) + 4)
+
+
+def test_gather_argument_errors(lib):
+    s = None
+    assert lib.gather_rows(P16, 10, 3, P16, 5, P16, s) == DIM
+    assert lib.gather_rows(P16, 10, 0, P16, 5, P16, s) == DIM
+    assert lib.gather_rows(P16, 10, 8, P16, -1, P16, s) == INVALID
+    assert lib.gather_rows(P16, 10, 8, None, 5, P16, s) == INVALID
+    assert lib.gather_rows(P_ODD, 10, 8, P16, 5, P16, s) == MISALIGNED
+    assert lib.gather_rows(P16, 10, 8, P16, 0, P16, s) == OK  # n == 0: nothing to do
+
+
+def test_mpzch_argument_errors(lib):
+    s = None
+    args = lambda cap, probes, n, ins, ws, wsb: lib.mpzch_lookup_or_insert(
+        P16, P16, None, cap, probes, 0, P16, n, 5, ins, P16, P16, None, None, ws, wsb, s)
+    assert args(100, 8, 10, 1, None, 0) == INVALID  # capacity % probes != 0
+    assert args(64, 0, 10, 1, None, 0) == INVALID
+    assert args(64, 33, 10, 1, None, 0) == INVALID
+    assert args(64, 8, -3, 1, None, 0) == INVALID
+    assert args(64, 8, 10, 2, None, 0) == INVALID
+    assert args(64, 8, 10, 1, None, 0) == WS_SMALL
+    need = lib.mpzch_lookup_or_insert_workspace_size(10, 1)
+    assert args(64, 8, 10, 1, P16, need - 1) == WS_SMALL
+    assert args(64, 8, 10, 1, ctypes.c_void_p((1 << 20) + 16), need) == MISALIGNED
+    # values given with a dim that is not a multiple of 4
+    assert lib.mpzch_lookup_or_insert(P16, P16, P16, 64, 8, 6, P16, 10, 5, 1, P16, P16, None, None, P16, need,
+                                      s) == DIM
+
+
+def test_writeback_and_ema_argument_errors(lib):
+    s = None
+    need = lib.writeback_rows_workspace_size(100, 8, 10, 0)
+    assert lib.writeback_rows(P16, 100, 8, P16, P16, 10, 0, 0.5, P16, need, s) == INVALID  # last-wins needs lr=1
+    assert lib.writeback_rows(P16, 100, 8, P16, P16, 10, 7, 1.0, P16, need, s) == INVALID  # unknown mode
+    assert lib.writeback_rows(P16, 100, 6, P16, P16, 10, 0, 1.0, P16, need, s) == DIM
+    assert lib.writeback_rows(P16, 100, 8, P16, P16, 10, 0, 1.0, None, 0, s) == WS_SMALL
+    assert lib.writeback_rows(P16, 100, 8, P16, P_ODD, 10, 1, 0.1, P16, 1 << 30, s) == MISALIGNED
+    assert lib.ema_update_rows(P16, 100, 2048, P16, P16, None, 10, 0.9, 0.1, P16, 1 << 30, s) == DIM
+    assert lib.ema_update_rows(P16, 100, 8, P16, P16, None, 10, 0.9, 0.1, None, 0, s) == WS_SMALL
+
+
+def test_score_dedup_hashed_argument_errors(lib):
+    s = None
+    assert lib.gather_dequant_score(P16, P16, P16, 10, 520, P16, 2, 3, P16, P16, s) == DIM
+    assert lib.gather_dequant_score(P_ODD, P16, P16, 10, 512, P16, 2, 3, P16, P16, s) == MISALIGNED
+    assert lib.gather_dequant_score(P16, P16, P16, 10, 512, P16, -1, 3, P16, P16, s) == INVALID
+    assert lib.dedup_ids(P16, 10, P16, P16, None, None, P16, 1 << 30, s) == INVALID  # count pointer required
+    assert lib.dedup_ids(P16, 10, P16, P16, None, P16, None, 0, s) == WS_SMALL
+    assert lib.hashed_rows(P16, 10, 0, P16, s) == INVALID
+    assert lib.hashed_rows(P_ODD, 10, 5, P16, s) == MISALIGNED
+
+
+def test_binding_refuses_cpu_tensors():
+    import torch
+    t = torch.zeros((4, 4))
+    with pytest.raises(hlr.HLRError):
+        hlr.gather_rows(t, torch.zeros(2, dtype=torch.int64))
