@@ -14,7 +14,7 @@
 // first-empty-else-LRU rule, because every insert pins the slot it takes.
 //
 // GPU plan (all on one stream, no host sync):
-//   mz_init    clear the transient miss table / bucket table and stats
+//   mz_init    clear the transient miss table and bucket table
 //   mz_probe   one lane per position: bucket probe, hit + pin, or register
 //              the miss (hash table keyed by ID, atomicMin of first position);
 //              the lane that creates an ID's entry links it into its bucket's
@@ -25,7 +25,10 @@
 //              is counted), stamps them, records the displaced ID
 //   mz_resolve one lane per missed position: row of its ID; the first
 //              occurrence reports the eviction and the wave zero-fills the
-//              new row cooperatively (16-byte stores)
+//              new row cooperatively (16-byte stores); an extra block folds the
+//              per-block partial counts of probe and assign into the stats
+// Counts are kept per block and folded once, never with same-address global
+// atomics (those serialise at the memory side).
 #include "hlr_common.hpp"
 
 namespace {
@@ -43,9 +46,12 @@ struct MZWork {
   int64_t *bkey;   // bucket table: bucket index (-1 = free)
   int32_t *bhead;  // first miss-table entry of the bucket's list
   int32_t *pent;   // per position: miss-table entry, -1 = hit / invalid
-  unsigned long long *stats;  // [6] used when the caller passes no stats array
+  uint32_t *part;  // per-block partial counts: probe blocks x 2, then assign blocks x 4
   uint32_t cap;    // entries of each hash table (power of two)
+  uint32_t probe_blocks;
 };
+
+constexpr int kAssignMaxBlocks = 1024;
 
 size_t mz_layout(int64_t n, MZWork *w, void *base) {
   Carver c(base);
@@ -58,7 +64,8 @@ size_t mz_layout(int64_t n, MZWork *w, void *base) {
   w->bkey = c.take<int64_t>(cap);
   w->bhead = c.take<int32_t>(cap);
   w->pent = c.take<int32_t>(static_cast<size_t>(n > 0 ? n : 1));
-  w->stats = c.take<unsigned long long>(8);
+  w->probe_blocks = static_cast<uint32_t>((n + kThreads - 1) / kThreads);
+  w->part = c.take<uint32_t>(2 * static_cast<size_t>(w->probe_blocks) + 4 * kAssignMaxBlocks);
   w->cap = static_cast<uint32_t>(cap);
   return c.off;
 }
@@ -71,16 +78,23 @@ __device__ __forceinline__ uint64_t bucket_of(uint64_t h, uint64_t nb, bool pow2
   return pow2 ? (h & (nb - 1)) : (h % nb);
 }
 
-__global__ void __launch_bounds__(kThreads) mz_init(MZWork w, unsigned long long *stats) {
+__global__ void __launch_bounds__(kThreads) mz_init(MZWork w) {
   const uint32_t stride = kThreads * gridDim.x;
   for (uint32_t i = blockIdx.x * kThreads + threadIdx.x; i < w.cap; i += stride) {
     w.mkey[i] = -1;
     w.mfpos[i] = 0x7fffffff;
-    w.mslot[i] = -1;
     w.bkey[i] = -1;
     w.bhead[i] = -1;
   }
-  if (stats && blockIdx.x == 0 && threadIdx.x < 6) stats[threadIdx.x] = 0ull;
+}
+
+// Sum of one small count per thread over the block (LDS), visible to thread 0.
+__device__ __forceinline__ uint32_t block_sum(uint32_t x, uint32_t *sh) {
+  if (threadIdx.x == 0) *sh = 0u;
+  __syncthreads();
+  if (x) atomicAdd(sh, x);
+  __syncthreads();
+  return *sh;
 }
 
 __global__ void mz_zero_stats(unsigned long long *stats) {
@@ -128,8 +142,18 @@ __global__ void __launch_bounds__(kThreads)
     }
   }
   if (stats) {
-    wave_count(&stats[0], is_hit);
-    wave_count(&stats[4], invalid);
+    __shared__ uint32_t sh_hit, sh_inv;
+    const uint32_t h_blk = block_sum(is_hit ? 1u : 0u, &sh_hit);
+    const uint32_t i_blk = block_sum(invalid ? 1u : 0u, &sh_inv);
+    if (threadIdx.x == 0) {
+      if (insert) {
+        w.part[2 * blockIdx.x] = h_blk;
+        w.part[2 * blockIdx.x + 1] = i_blk;
+      } else {
+        if (h_blk) atomicAdd(&stats[0], (unsigned long long)h_blk);
+        if (i_blk) atomicAdd(&stats[4], (unsigned long long)i_blk);
+      }
+    }
   }
   if (!(insert && is_miss)) return;
   // Register the missed ID in the transient miss table (keyed by ID).
@@ -174,9 +198,9 @@ __global__ void __launch_bounds__(kThreads)
               unsigned long long *stats) {
   constexpr int PM = P > 0 ? P : kMaxProbes;
   const int probes = P > 0 ? P : probes_rt;
-  const uint32_t t = blockIdx.x * kThreads + threadIdx.x;
-  int ins = 0, evs = 0, ovf = 0, bad = 0;
-  const int64_t bk = t < w.cap ? w.bkey[t] : -1;
+  uint32_t ins = 0, evs = 0, ovf = 0, bad = 0;
+  for (uint32_t t = blockIdx.x * kThreads + threadIdx.x; t < w.cap; t += kThreads * gridDim.x) {
+  const int64_t bk = w.bkey[t];
   if (bk >= 0) {
     const int64_t base = bk * probes;
     int64_t idv[PM], stv[PM];
@@ -224,6 +248,7 @@ __global__ void __launch_bounds__(kThreads)
     int32_t lastf = 0;  // largest kept first position (valid once cnt == avail)
     for (int32_t e = w.bhead[t]; e != -1; e = w.mnext[e]) {
       const int32_t f = w.mfpos[e];
+      w.mslot[e] = -1;  // overflow unless selected below
       ++L;
       int pos;
       if (cnt < avail) pos = cnt++;
@@ -267,19 +292,54 @@ __global__ void __launch_bounds__(kThreads)
       ++ins;
       if (old != HLR_EMPTY_ID) ++evs;
     }
-    ovf = L - cnt;
+    ovf += L - cnt;
+  }
   }
   if (stats) {
-    if (ins) atomicAdd(&stats[1], (unsigned long long)ins);
-    if (evs) atomicAdd(&stats[2], (unsigned long long)evs);
-    if (ovf) atomicAdd(&stats[3], (unsigned long long)ovf);
-    if (bad) atomicAdd(&stats[5], (unsigned long long)bad);
+    __shared__ uint32_t sh[4];
+    const uint32_t a = block_sum(ins, &sh[0]);
+    const uint32_t b = block_sum(evs, &sh[1]);
+    const uint32_t c = block_sum(ovf, &sh[2]);
+    const uint32_t d = block_sum(bad, &sh[3]);
+    if (threadIdx.x == 0) {
+      uint32_t *p = w.part + 2 * w.probe_blocks + 4 * blockIdx.x;
+      p[0] = a;
+      p[1] = b;
+      p[2] = c;
+      p[3] = d;
+    }
   }
 }
 
 __global__ void __launch_bounds__(kThreads)
     mz_resolve(int64_t n, float *values, int64_t dim, MZWork w, int64_t *__restrict__ rows,
-               int64_t *__restrict__ evicted) {
+               int64_t *__restrict__ evicted, unsigned long long *stats, uint32_t assign_blocks) {
+  if (blockIdx.x == gridDim.x - 1) {
+    // The extra last block folds the per-block partial counts of mz_probe and
+    // mz_assign into the stats (no global atomics); it has no positions.
+    if (!stats) return;
+    // Final stats from the per-block partials of mz_probe and mz_assign (no global atomics).
+    __shared__ unsigned long long acc[6];
+    if (threadIdx.x < 6) acc[threadIdx.x] = 0ull;
+    __syncthreads();
+    unsigned long long loc[6] = {0, 0, 0, 0, 0, 0};
+    for (uint32_t b = threadIdx.x; b < w.probe_blocks; b += kThreads) {
+      loc[0] += w.part[2 * b];
+      loc[4] += w.part[2 * b + 1];
+    }
+    for (uint32_t b = threadIdx.x; b < assign_blocks; b += kThreads) {
+      const uint32_t *p = w.part + 2 * w.probe_blocks + 4 * b;
+      loc[1] += p[0];
+      loc[2] += p[1];
+      loc[3] += p[2];
+      loc[5] += p[3];
+    }
+    for (int k = 0; k < 6; ++k)
+      if (loc[k]) atomicAdd(&acc[k], loc[k]);
+    __syncthreads();
+    if (threadIdx.x < 6) stats[threadIdx.x] = acc[threadIdx.x];
+    return;
+  }
   const int64_t i = static_cast<int64_t>(blockIdx.x) * kThreads + threadIdx.x;
   const int32_t e = i < n ? w.pent[i] : -1;
   int64_t slot = -1;
@@ -314,17 +374,19 @@ void mz_launch(int64_t *identity, int64_t *stamps, float *values, int64_t capaci
   const bool pow2 = (nb & (nb - 1)) == 0;
   const int gpos = grid_for(n, kThreads);
   if (insert) {
-    int gi = grid_for(w.cap, kThreads * 4);
-    if (gi > 2048) gi = 2048;
-    mz_init<<<gi, kThreads, 0, s>>>(w, stats);
+    int gi = grid_for(w.cap, kThreads);
+    if (gi > 4096) gi = 4096;
+    mz_init<<<gi, kThreads, 0, s>>>(w);
   } else if (stats) {
     mz_zero_stats<<<1, 64, 0, s>>>(stats);
   }
   mz_probe<P><<<gpos, kThreads, 0, s>>>(ids, n, identity, stamps, nb, pow2, probes, now, insert, rows, hit, evicted,
                                          w, stats);
   if (!insert) return;
-  mz_assign<P><<<grid_for(w.cap, kThreads), kThreads, 0, s>>>(identity, stamps, probes, now, w, stats);
-  mz_resolve<<<gpos, kThreads, 0, s>>>(n, values, dim, w, rows, evicted);
+  int ga = grid_for(w.cap, kThreads);
+  if (ga > kAssignMaxBlocks) ga = kAssignMaxBlocks;
+  mz_assign<P><<<ga, kThreads, 0, s>>>(identity, stamps, probes, now, w, stats);
+  mz_resolve<<<gpos + 1, kThreads, 0, s>>>(n, values, dim, w, rows, evicted, stats, static_cast<uint32_t>(ga));
 }
 
 }  // namespace
@@ -359,8 +421,7 @@ extern "C" hlr_status mpzch_lookup_or_insert(int64_t *identity, int64_t *stamps,
     if (!aligned(ws, 256)) return HLR_MISALIGNED;
     mz_layout(n, &w, ws);
   }
-  unsigned long long *stats = out_stats ? reinterpret_cast<unsigned long long *>(out_stats)
-                                        : (insert ? w.stats : nullptr);
+  unsigned long long *stats = reinterpret_cast<unsigned long long *>(out_stats);
   if (n == 0) {
     if (out_stats) mz_zero_stats<<<1, 64, 0, stream>>>(stats);
     return launch_status();

@@ -6,11 +6,11 @@
 // batch are deduplicated first so each row receives one exact write.  The
 // last occurrence of a row wins.
 //   lw_init   clear a transient hash table keyed by row (2n slots)
-//   lw_last   per wave, lanes holding the same row are grouped (ballot peel)
-//             and only the group's highest lane does the atomicMax of its
-//             position, so a hot Zipf row costs one atomic per wave
-//   lw_apply  flat 16-byte units (position, column): the winner position of
-//             each row reads M and e, writes fl(M - fl(M - e))
+//   lw_last   a block folds its positions in LDS (row -> last position),
+//             then one global atomicMax per distinct row of the block; new
+//             global slots go to a compact list
+//   lw_apply  one wave per distinct row: reads M and e at the last
+//             occurrence, writes fl(M - fl(M - e)) with 16-byte accesses
 //
 // SGD_SUM — per-row SGD with duplicate gradients summed and applied once (the
 // same sparse-table update pattern at a learning rate other than 1, as in the
@@ -28,9 +28,10 @@ constexpr int kThreads = 256;
 constexpr int kUnroll = 4;
 
 struct LWWork {
-  int64_t *hkey;   // row held by the slot (-1 = free)
-  int32_t *hlast;  // last position of that row
-  int32_t *pent;   // per position: its slot, -1 = row skipped
+  int64_t *hkey;    // row held by the slot (-1 = free)
+  int32_t *hlast;   // last position of that row
+  int32_t *list;    // slots in use, compacted (first *count entries)
+  uint32_t *count;  // [1]
   uint32_t cap;
 };
 
@@ -39,7 +40,8 @@ size_t lw_layout(int64_t n, LWWork *w, void *base) {
   const uint64_t cap = next_pow2(static_cast<uint64_t>(n > 32 ? 2 * n : 64));
   w->hkey = c.take<int64_t>(cap);
   w->hlast = c.take<int32_t>(cap);
-  w->pent = c.take<int32_t>(static_cast<size_t>(n > 0 ? n : 1));
+  w->list = c.take<int32_t>(cap);
+  w->count = c.take<uint32_t>(1);
   w->cap = static_cast<uint32_t>(cap);
   return c.off;
 }
@@ -50,83 +52,123 @@ __global__ void __launch_bounds__(kThreads) lw_init(LWWork w) {
     w.hkey[i] = -1;
     w.hlast[i] = -1;
   }
+  if (blockIdx.x == 0 && threadIdx.x == 0) *w.count = 0u;
 }
 
-__device__ __forceinline__ int32_t lw_slot(LWWork w, int64_t r) {
-  const uint32_t mask = w.cap - 1;
-  uint32_t s = static_cast<uint32_t>(mix64(static_cast<uint64_t>(r)) >> 32) & mask;
-  for (;;) {
-    const int64_t k = __hip_atomic_load(&w.hkey[s], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    if (k == r) return static_cast<int32_t>(s);
-    if (k == -1) {
-      const int64_t prev = atomic_cas_i64(&w.hkey[s], -1, r);
-      if (prev == -1 || prev == r) return static_cast<int32_t>(s);
-    }
-    s = (s + 1) & mask;
-  }
-}
+// Last occurrence of every row.  A block first folds its 512 positions in an
+// LDS hash table (row -> largest position, LDS atomics), then publishes one
+// global atomicMax per distinct row of the block: a hot Zipf row costs one
+// global atomic per block, not one per position.  Each thread issues the CAS
+// of all its LDS entries before waiting on any, so the global round trips
+// overlap.  Newly claimed global slots are appended to a compact list (one
+// global atomicAdd per block).
+constexpr int kLwItems = 2;
+constexpr int kLwTile = kThreads * kLwItems;  // positions per block
+constexpr int kLwLds = 2 * kLwTile;           // LDS hash entries
+constexpr int kLwPer = kLwLds / kThreads;     // LDS entries scanned per thread
 
 __global__ void __launch_bounds__(kThreads)
     lw_last(const int64_t *__restrict__ rows, int64_t n, int64_t num_rows, LWWork w) {
-  const int64_t i = static_cast<int64_t>(blockIdx.x) * kThreads + threadIdx.x;
-  const bool valid = i < n;
-  const int64_t r = valid ? rows[i] : -1;
-  const bool ok = valid && r >= 0 && r < num_rows;
-  if (valid && !ok) w.pent[i] = -1;
-  const int64_t i0 = i - lane_id();
-  uint64_t todo = ballot(ok);
-  while (todo) {
-    const int leader = __builtin_ctzll(todo);
-    const int64_t rl = readlane_i64(r, leader);
-    const uint64_t grp = ballot(ok && r == rl);
-    const int last = 63 - __builtin_clzll(grp);
-    int32_t s = 0;
-    if (lane_id() == leader) {
-      s = lw_slot(w, rl);
-      atomicMax(&w.hlast[s], static_cast<int32_t>(i0 + last));
-    }
-    s = readlane_i32(s, leader);
-    if ((grp >> lane_id()) & 1ull) w.pent[i] = s;
-    todo &= ~grp;
+  __shared__ unsigned long long lkey[kLwLds];
+  __shared__ int32_t lpos[kLwLds];
+  __shared__ int32_t lnew_slots[kLwLds];
+  __shared__ uint32_t lnew, lbase;
+  for (int e = threadIdx.x; e < kLwLds; e += kThreads) {
+    lkey[e] = ~0ull;
+    lpos[e] = -1;
   }
+  if (threadIdx.x == 0) lnew = 0u;
+  __syncthreads();
+  const int64_t base = static_cast<int64_t>(blockIdx.x) * kLwTile;
+#pragma unroll
+  for (int k = 0; k < kLwItems; ++k) {
+    const int64_t i = base + k * kThreads + threadIdx.x;
+    if (i >= n) continue;
+    const int64_t r = rows[i];
+    if (r < 0 || r >= num_rows) continue;
+    uint32_t e = static_cast<uint32_t>(mix64(static_cast<uint64_t>(r)) >> 40) & (kLwLds - 1);
+    for (;;) {
+      const unsigned long long prev = atomicCAS(&lkey[e], ~0ull, static_cast<unsigned long long>(r));
+      if (prev == ~0ull || prev == static_cast<unsigned long long>(r)) break;
+      e = (e + 1) & (kLwLds - 1);
+    }
+    atomicMax(&lpos[e], static_cast<int32_t>(i));
+  }
+  __syncthreads();
+  const uint32_t mask = w.cap - 1;
+  int64_t key[kLwPer];
+  int32_t pos[kLwPer];
+  uint32_t gs[kLwPer];
+  int64_t prev[kLwPer];
+#pragma unroll
+  for (int j = 0; j < kLwPer; ++j) {
+    const int e = threadIdx.x + j * kThreads;
+    const unsigned long long k = lkey[e];
+    key[j] = k == ~0ull ? -1 : static_cast<int64_t>(k);
+    pos[j] = lpos[e];
+    gs[j] = static_cast<uint32_t>(mix64(static_cast<uint64_t>(key[j])) >> 32) & mask;
+  }
+  // all first-probe CAS in flight together
+#pragma unroll
+  for (int j = 0; j < kLwPer; ++j) prev[j] = key[j] >= 0 ? atomic_cas_i64(&w.hkey[gs[j]], -1, key[j]) : key[j];
+#pragma unroll
+  for (int j = 0; j < kLwPer; ++j) {
+    if (key[j] < 0) continue;
+    bool created = prev[j] == -1;
+    while (!created && prev[j] != key[j]) {  // collision: linear probing
+      gs[j] = (gs[j] + 1) & mask;
+      prev[j] = atomic_cas_i64(&w.hkey[gs[j]], -1, key[j]);
+      created = prev[j] == -1;
+    }
+    atomicMax(&w.hlast[gs[j]], pos[j]);
+    if (created) lnew_slots[atomicAdd(&lnew, 1u)] = static_cast<int32_t>(gs[j]);
+  }
+  __syncthreads();
+  if (threadIdx.x == 0) lbase = lnew ? atomicAdd(w.count, lnew) : 0u;
+  __syncthreads();
+  for (uint32_t j = threadIdx.x; j < lnew; j += kThreads) w.list[lbase + j] = lnew_slots[j];
 }
 
-template <int V4>
+// One wave per winner row (two rows in flight per wave): g = fl(M - e), M' = fl(M - g).
+template <int NC>
 __global__ void __launch_bounds__(kThreads)
-    lw_apply(float4 *table, const float4 *__restrict__ src, const int64_t *__restrict__ rows, int64_t n,
-             LWWork w, int64_t v4_rt) {
-  const int64_t v4 = V4 > 0 ? V4 : v4_rt;
-  const int64_t total = n * v4;
-  const int64_t base = static_cast<int64_t>(blockIdx.x) * (kThreads * kUnroll) + threadIdx.x;
-  int64_t dst[kUnroll], from[kUnroll];
+    lw_apply(float4 *table, const float4 *__restrict__ src, LWWork w, int64_t v4) {
+  constexpr int RPW = 2;
+  const uint32_t count = *w.count;
+  const int lane = lane_id();
+  const uint32_t waves = gridDim.x * (kThreads / kWave);
+  for (uint32_t j0 = ((blockIdx.x * kThreads + threadIdx.x) / kWave) * RPW; j0 < count; j0 += waves * RPW) {
+    int64_t mrow[RPW], erow[RPW];
 #pragma unroll
-  for (int k = 0; k < kUnroll; ++k) {
-    const int64_t u = base + k * kThreads;
-    dst[k] = -1;
-    if (u < total) {
-      const int64_t i = u / v4;
-      const int32_t s = w.pent[i];
-      if (s >= 0 && w.hlast[s] == static_cast<int32_t>(i)) {
-        const int64_t c = u - i * v4;
-        dst[k] = rows[i] * v4 + c;
-        from[k] = u;
+    for (int q = 0; q < RPW; ++q) {
+      mrow[q] = -1;
+      if (j0 + q < count) {
+        const int32_t s = w.list[j0 + q];
+        mrow[q] = w.hkey[s] * v4;
+        erow[q] = static_cast<int64_t>(w.hlast[s]) * v4;
       }
     }
-  }
-  float4 m[kUnroll], e[kUnroll];
+    float4 m[RPW][NC], e[RPW][NC];
 #pragma unroll
-  for (int k = 0; k < kUnroll; ++k) {
-    if (dst[k] >= 0) {
-      m[k] = table[dst[k]];
-      e[k] = src[from[k]];
-    }
-  }
+    for (int q = 0; q < RPW; ++q)
 #pragma unroll
-  for (int k = 0; k < kUnroll; ++k) {
-    if (dst[k] >= 0) {
-      const float4 g = f4_sub(m[k], e[k]);  // g = fl(M - e)
-      table[dst[k]] = f4_sub(m[k], g);      // M' = fl(M - g)
-    }
+      for (int c = 0; c < NC; ++c) {
+        const int64_t col = lane + c * kWave;
+        if (mrow[q] >= 0 && col < v4) {
+          m[q][c] = table[mrow[q] + col];
+          e[q][c] = src[erow[q] + col];
+        }
+      }
+#pragma unroll
+    for (int q = 0; q < RPW; ++q)
+#pragma unroll
+      for (int c = 0; c < NC; ++c) {
+        const int64_t col = lane + c * kWave;
+        if (mrow[q] >= 0 && col < v4) {
+          const float4 g = f4_sub(m[q][c], e[q][c]);  // g = fl(M - e)
+          table[mrow[q] + col] = f4_sub(m[q][c], g);  // M' = fl(M - g)
+        }
+      }
   }
 }
 
@@ -238,17 +280,17 @@ extern "C" hlr_status writeback_rows(float *table, int64_t num_rows, int64_t dim
   if (mode == HLR_WB_LAST_WINS) {
     LWWork w;
     lw_layout(n, &w, ws);
-    int gi = grid_for(w.cap, kThreads * 4);
-    if (gi > 2048) gi = 2048;
+    int gi = grid_for(w.cap, kThreads);
+    if (gi > 4096) gi = 4096;
     lw_init<<<gi, kThreads, 0, stream>>>(w);
-    lw_last<<<grid_for(n, kThreads), kThreads, 0, stream>>>(rows, n, num_rows, w);
-    const int ga = grid_for(n * v4, kThreads * kUnroll);
-    switch (v4) {
-      case 16: lw_apply<16><<<ga, kThreads, 0, stream>>>(t4, s4, rows, n, w, v4); break;
-      case 32: lw_apply<32><<<ga, kThreads, 0, stream>>>(t4, s4, rows, n, w, v4); break;
-      case 128: lw_apply<128><<<ga, kThreads, 0, stream>>>(t4, s4, rows, n, w, v4); break;
-      default: lw_apply<0><<<ga, kThreads, 0, stream>>>(t4, s4, rows, n, w, v4); break;
-    }
+    lw_last<<<grid_for(n, kLwTile), kThreads, 0, stream>>>(rows, n, num_rows, w);
+    int ga = grid_for(n, 8);
+    if (ga > 2048) ga = 2048;
+    const int64_t nc = (v4 + kWave - 1) / kWave;
+    if (nc == 1) lw_apply<1><<<ga, kThreads, 0, stream>>>(t4, s4, w, v4);
+    else if (nc == 2) lw_apply<2><<<ga, kThreads, 0, stream>>>(t4, s4, w, v4);
+    else if (nc <= 4) lw_apply<4><<<ga, kThreads, 0, stream>>>(t4, s4, w, v4);
+    else return HLR_UNSUPPORTED_DIM;
     return launch_status();
   }
   SegWork<uint32_t> w;
