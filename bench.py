@@ -31,6 +31,38 @@ HBM_PEAK_GBS = 8000.0
 PMC_FILE = os.path.join(ROOT, "profiles", "gather_memory_layer_pmc.json")
 
 
+class HipTimer:
+    """HIP events created with hipEventDisableSystemFence (timing only: no cache writeback/invalidate on
+    record), recorded on the stream the kernels are launched on."""
+
+    DISABLE_SYSTEM_FENCE = 0x20000000
+
+    def __init__(self):
+        import ctypes
+        self.ct = ctypes
+        self.hip = ctypes.CDLL("libamdhip64.so")
+        self.pairs = []
+
+    def event(self):
+        e = self.ct.c_void_p()
+        rc = self.hip.hipEventCreateWithFlags(self.ct.byref(e), self.ct.c_uint(self.DISABLE_SYSTEM_FENCE))
+        if rc != 0:
+            raise RuntimeError(f"hipEventCreateWithFlags failed ({rc})")
+        return e
+
+    def record(self, e, stream):
+        rc = self.hip.hipEventRecord(e, self.ct.c_void_p(stream))
+        if rc != 0:
+            raise RuntimeError(f"hipEventRecord failed ({rc})")
+
+    def elapsed_s(self, a, b):
+        ms = self.ct.c_float()
+        rc = self.hip.hipEventElapsedTime(self.ct.byref(ms), a, b)
+        if rc != 0:
+            raise RuntimeError(f"hipEventElapsedTime failed ({rc})")
+        return ms.value * 1e-3
+
+
 def src_sha(path):
     return hashlib.sha256(open(path, "rb").read()).hexdigest()[:16]
 
@@ -46,6 +78,9 @@ def parse():
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain 1 GiB device copy (reference for HBM counters)")
     ap.add_argument("--scale", type=float, default=1.0, help="shrink capacity/universe/batch (testing only)")
+    ap.add_argument("--workload", default="memory-layer",
+                    choices=["memory-layer", "serving", "dlrm", "cs3", "dedup"],
+                    help="memory-layer (default, the headline) or one of the other rows' workloads")
     ap.add_argument("--op-events", action="store_true",
                     help="also time lookup and writeback separately (events between every call)")
     return ap.parse_args()
@@ -82,6 +117,9 @@ def main():
         copy_calibration(torch)
         return
     sys.path.insert(0, ROOT)
+    if args.workload != "memory-layer":
+        {"serving": run_serving, "dlrm": run_dlrm, "cs3": run_cs3, "dedup": run_dedup}[args.workload](args)
+        return
     import hashed_lookup_row_amd as hlr
     import synth
 
@@ -100,7 +138,7 @@ def main():
     t0 = time.time()
     prefill = synth.prefill_batches(cfg)
     stream, fc = [], 0
-    for t in range(1, W + K + 1):
+    for t in range(1, W + K + 2):
         ids, fc = synth.mpzch_step_ids(cfg, t, fc)
         stream.append(ids)
     print(f"[bench] generated inputs in {time.time() - t0:.1f}s", file=sys.stderr, flush=True)
@@ -124,45 +162,51 @@ def main():
     print(f"[bench] prefilled {len(prefill)} batches; load {(identity >= 0).float().mean().item():.4f}",
           file=sys.stderr, flush=True)
 
-    def step(t, rows, evs=None):
-        if evs and args.op_events:
-            evs[0].record()
+    timer = HipTimer()
+    cur = torch.cuda.current_stream(dev).cuda_stream
+
+    def step(t, rows, evs=None, stats_out=None):
+        if evs is not None and args.op_events:
+            timer.record(evs[0], cur)
         hlr.mpzch_lookup_or_insert(identity, stamps, values, P, ids_dev[t], base_now + 1 + t, insert=True,
-                                   out_rows=rows, out_hit=hit_buf, out_stats=stats)
-        if evs:
-            evs[1].record()
+                                   out_rows=rows, out_hit=hit_buf, out_stats=stats_out)
+        if evs is not None:
+            timer.record(evs[1], cur)
         hlr.gather_rows(values, rows, out=out)
-        if evs:
-            evs[2].record()
+        if evs is not None:
+            timer.record(evs[2], cur)
         hlr.writeback_rows(values, rows, e_pool[t % npool])
-        if evs and args.op_events:
-            evs[3].record()
+        if evs is not None and args.op_events:
+            timer.record(evs[3], cur)
 
     for t in range(W):
         step(t, rows_buf[0])
     torch.cuda.synchronize()
 
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(K)]
-    start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    # gather timed with HIP events on every `sample`-th timed step (events add a little time to a step)
+    sample = 1 if args.op_events else 4
+    evs = {k: [timer.event() for _ in range(4)] for k in range(0, K, sample)}
+    start, stop = timer.event(), timer.event()
     torch.cuda.synchronize()
     wall0 = time.perf_counter()
-    start.record()
+    timer.record(start, cur)
     for k in range(K):
-        step(W + k, rows_buf[k], evs[k])
-    stop.record()
+        step(W + k, rows_buf[k], evs.get(k))
+    timer.record(stop, cur)
     torch.cuda.synchronize()
     wall = time.perf_counter() - wall0
-    total_s = start.elapsed_time(stop) * 1e-3
-    if args.op_events:
-        per_op = np.array([[e[i].elapsed_time(e[i + 1]) * 1e-3 for i in range(3)] for e in evs])  # s
-    else:
-        per_op = np.array([[np.nan, e[1].elapsed_time(e[2]) * 1e-3, np.nan] for e in evs])
-
+    total_s = timer.elapsed_s(start, stop)
+    per_op = np.array([[timer.elapsed_s(e[i], e[i + 1]) if (args.op_events or i == 1) else np.nan
+                        for i in range(3)] for e in evs.values()])  # s
+    gather_steps = np.array(sorted(evs.keys()))
+    # one more step after the timed region reports the optional MPZCH stats (hit rate, inserts, ...)
+    step(W + K, torch.empty(n, dtype=torch.int64, device=dev), None, stats)
+    torch.cuda.synchronize()
     # distinct rows per step (for algorithmic bytes)
     us = np.array([torch.unique(r[r >= 0]).numel() for r in rows_buf], dtype=np.float64)
     dup = 1.0 - us.mean() / n
     gather_bytes = n * R + us * R + n * 8  # write out, read distinct rows, read row indices
-    gather_gbs = float(gather_bytes.sum() / per_op[:, 1].sum() / 1e9)
+    gather_gbs = float(gather_bytes[gather_steps].sum() / per_op[:, 1].sum() / 1e9)
     wb_bytes = 3 * us * R + n * 8
     step_bytes = n * R + 4 * us * R + 8 * n
     ms_per_step = total_s / K * 1e3
@@ -197,25 +241,27 @@ def main():
             "bound": "hbm", "kernel": "gather_kernel<128>",
             "achieved": gather_gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": gather_gbs / HBM_PEAK_GBS,
             "traffic": traffic,
-            "algorithmic_bytes_per_launch": float(gather_bytes.mean()),
+            "algorithmic_bytes_per_launch": float(gather_bytes[gather_steps].mean()),
             "avg_launch_us": float(per_op[:, 1].mean() * 1e6),
+            "timed_launches": int(len(gather_steps)),
         },
         "step_hbm": {
             "algorithmic_bytes_per_step": float(step_bytes.mean()),
             "achieved_gbs": float(step_bytes.sum() / total_s / 1e9),
             "frac": float(step_bytes.sum() / total_s / 1e9 / HBM_PEAK_GBS),
-            "writeback_gbs": float(wb_bytes.sum() / per_op[:, 2].sum() / 1e9) if args.op_events else None,
+            "writeback_gbs": float(wb_bytes[gather_steps].sum() / per_op[:, 2].sum() / 1e9) if args.op_events
+            else None,
         },
         "ops_us": ({"lookup_or_insert": float(per_op[:, 0].mean() * 1e6), "gather": float(per_op[:, 1].mean() * 1e6),
                     "writeback": float(per_op[:, 2].mean() * 1e6)} if args.op_events else None),
         "distinct_rows_per_step": float(us.mean()),
         "dup_frac": float(dup),
-        "hit_rate_last_step": None,
+        "hit_rate_after": None,
         "wall_s": wall,
     }
     st = stats.cpu().numpy()
-    line["hit_rate_last_step"] = float(st[0] / n)
-    line["last_step_stats"] = {"hits": int(st[0]), "inserts": int(st[1]), "evictions": int(st[2]),
+    line["hit_rate_after"] = float(st[0] / n)
+    line["stats_after"] = {"hits": int(st[0]), "inserts": int(st[1]), "evictions": int(st[2]),
                                "overflows": int(st[3]), "invalid": int(st[4]), "consistency_failures": int(st[5])}
 
     if not args.no_cpu_baseline:
@@ -255,6 +301,239 @@ def cpu_baseline(cfg, prefill, stream, e_pool, npool, base_now, budget_s, W):
             "sample": f"{steps} steps (steps {W + 1}..{W + steps} of the same stream, {n} IDs each) after an "
                       f"untimed oracle prefill ({setup:.1f}s); single-threaded C oracle, lookup+gather+writeback",
             "seconds": spent, "host_nproc": os.cpu_count()}
+
+
+# ----------------------------------------------------------------------------------------------
+# Other rows of the path, measured on their own workloads (one JSON line each; not the headline).
+def _line(metric, value, unit, K, W, ms, config, roof, extra):
+    d = {"metric": metric, "value": value, "unit": unit, "n_gpus": 1, "steps": K, "warmup": W, "ms_per_step": ms,
+         "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "data": "synthetic", "config": config,
+         "roofline": roof}
+    d.update(extra)
+    print(json.dumps(d), flush=True)
+
+
+def _roof(name, nbytes, seconds, bound="hbm"):
+    gbs = nbytes / seconds / 1e9
+    return {"bound": bound, "kernel": name, "achieved": gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+            "frac": gbs / HBM_PEAK_GBS, "traffic": None, "algorithmic_bytes_per_launch": nbytes,
+            "avg_launch_us": seconds * 1e6}
+
+
+def _timed(timer, cur, fn, K):
+    """Runs fn(k) for k < K with an event pair around each call; returns per-call seconds."""
+    import numpy as np
+    evs = [(timer.event(), timer.event()) for _ in range(K)]
+    for k in range(K):
+        timer.record(evs[k][0], cur)
+        fn(k)
+        timer.record(evs[k][1], cur)
+    import torch
+    torch.cuda.synchronize()
+    return np.array([timer.elapsed_s(a, b) for a, b in evs])
+
+
+def run_serving(args):
+    """Serving read path: lookup-only MPZCH + int8 dequant + dot, 256 requests x 1024 candidates."""
+    import numpy as np
+    import torch
+    import hashed_lookup_row_amd as hlr
+    import synth
+    dev = torch.device("cuda:0")
+    cfg, sv = synth.MEMORY_LAYER, synth.SERVING
+    C, P, D = sv.capacity, cfg.probes, sv.dim
+    identity = torch.full((C,), -1, dtype=torch.int64, device=dev)
+    stamps = torch.full((C,), -1, dtype=torch.int64, device=dev)
+    for k, b in enumerate(synth.prefill_batches(cfg), start=1):
+        hlr.mpzch_lookup_or_insert(identity, stamps, None, P, torch.from_numpy(b).to(dev), k)
+    keys = synth.universe_keys(cfg.universe, cfg.config)
+    ident = identity.cpu().numpy()
+    cands = synth.serving_candidates(keys[np.isin(keys, ident[ident >= 0])], sv.requests, sv.cands, sv.zipf_s,
+                                     sv.miss_frac)
+    q, scale, bias = synth.int8_table(C, D, device=dev)
+    user = synth.normal_rows(sv.requests, D, 1.0, 3, 0, device=dev)
+    ids = torch.from_numpy(cands).to(dev)
+    rows = torch.empty(ids.numel(), dtype=torch.int64, device=dev)
+    hit = torch.empty(ids.numel(), dtype=torch.int8, device=dev)
+    scores = torch.empty((sv.requests, sv.cands), dtype=torch.float32, device=dev)
+    timer, cur = HipTimer(), torch.cuda.current_stream(dev).cuda_stream
+    K, W = args.steps, args.warmup
+    for _ in range(W):
+        hlr.mpzch_lookup_or_insert(identity, None, None, P, ids, 0, insert=False, out_rows=rows, out_hit=hit)
+        hlr.gather_dequant_score(q, scale, bias, rows, user, sv.cands, out=scores)
+    t_look = _timed(timer, cur, lambda k: hlr.mpzch_lookup_or_insert(identity, None, None, P, ids, 0, insert=False,
+                                                                     out_rows=rows, out_hit=hit), K)
+    t_score = _timed(timer, cur, lambda k: hlr.gather_dequant_score(q, scale, bias, rows, user, sv.cands,
+                                                                    out=scores), K)
+    r = rows.cpu().numpy()
+    u = np.unique(r[r >= 0]).size
+    n = r.size
+    score_bytes = u * (D + 8) + 8 * n + 4 * n + sv.requests * D * 4
+    look_bytes = 8 * n + u * 64 + 9 * n
+    step_s = float(np.median(t_look) + np.median(t_score))
+    _line("candidate scores/s (lookup-only MPZCH + int8 dequant + dot)", n / step_s, "scores/s", K, W,
+          step_s * 1e3, {"workload": sv.name, "requests": sv.requests, "cands": sv.cands, "dim": D, "capacity": C},
+          _roof("score_kernel<2>", score_bytes, float(np.median(t_score))),
+          {"dtype": "int8->fp64", "distinct_rows": int(u), "hit_rate": float((r >= 0).mean()),
+           "ops_us": {"lookup_only": float(np.median(t_look) * 1e6), "score": float(np.median(t_score) * 1e6)},
+           "lookup_roofline": _roof("mz_probe<8>", look_bytes, float(np.median(t_look))),
+           "score_fp64_ops_per_s": float(3 * n * D / np.median(t_score))})
+
+
+def run_dlrm(args):
+    """DLRMv4-like: 8 hashed tables (120 GiB), per table hashed rows + gather + duplicate-summed SGD."""
+    import numpy as np
+    import torch
+    import hashed_lookup_row_amd as hlr
+    import synth
+    dev = torch.device("cuda:0")
+    cfg = synth.DLRM
+    D, n = cfg.dim, cfg.per_table
+    R = D * 4
+    tables = []
+    for t, nr in enumerate(cfg.table_rows):
+        x = torch.empty((nr, D), dtype=torch.float32, device=dev)
+        synth.dlrm_fill_table(t, nr, D, x)
+        tables.append(x)
+    K, W = args.steps, args.warmup
+    keys = [[torch.from_numpy(synth.dlrm_keys(cfg, t, s + 1)).to(dev) for t in range(8)] for s in range(2)]
+    grads = [[synth.normal_rows(n, D, cfg.g_std, 4, 100 * s + t, device=dev) for t in range(8)] for s in range(2)]
+    rows = [torch.empty(n, dtype=torch.int64, device=dev) for _ in range(8)]
+    out = torch.empty((n, D), dtype=torch.float32, device=dev)
+    timer, cur = HipTimer(), torch.cuda.current_stream(dev).cuda_stream
+    ev = {}
+
+    def step(s, rec):
+        for t in range(8):
+            if rec:
+                ev.setdefault(t, []).append([timer.event() for _ in range(4)])
+                e = ev[t][-1]
+                timer.record(e[0], cur)
+            hlr.hashed_rows(keys[s % 2][t], cfg.table_rows[t], out=rows[t])
+            if rec:
+                timer.record(e[1], cur)
+            hlr.gather_rows(tables[t], rows[t], out=out)
+            if rec:
+                timer.record(e[2], cur)
+            hlr.writeback_rows(tables[t], rows[t], grads[s % 2][t], mode=hlr.WB_SGD_SUM, lr=cfg.lr)
+            if rec:
+                timer.record(e[3], cur)
+
+    for s in range(W):
+        step(s, False)
+    torch.cuda.synchronize()
+    a, b = timer.event(), timer.event()
+    timer.record(a, cur)
+    for s in range(K):
+        step(W + s, True)
+    timer.record(b, cur)
+    torch.cuda.synchronize()
+    total = timer.elapsed_s(a, b)
+    per = {t: np.array([[timer.elapsed_s(e[i], e[i + 1]) for i in range(3)] for e in ev[t]]) for t in range(8)}
+    us = [np.unique(rows[t].cpu().numpy()).size for t in range(8)]
+    g_bytes = sum(n * R + u * R + 8 * n for u in us)          # gather: write n rows, read u rows, indices
+    s_bytes = sum(n * R + 2 * u * R + 8 * n for u in us)      # SGD: read n gradients, read+write u rows
+    g_time = sum(per[t][:, 1].mean() for t in range(8))
+    s_time = sum(per[t][:, 2].mean() for t in range(8))
+    step_s = total / K
+    _line("per-token rows/s (8 hashed tables: gather + duplicate-summed SGD)", 8 * n / step_s, "rows/s", K, W,
+          step_s * 1e3, {"workload": cfg.name, "tables": 8, "rows_per_table": list(cfg.table_rows), "dim": D,
+                         "keys_per_table": n, "zipf_s": cfg.zipf_s, "lr": cfg.lr},
+          _roof("sgd_apply (writeback_rows SGD_SUM, all kernels)", s_bytes / 8, s_time / 8),
+          {"dtype": "fp32", "distinct_rows_per_table": us,
+           "gather_roofline": _roof("gather_kernel<128>", g_bytes / 8, g_time / 8),
+           "step_hbm_gbs": (g_bytes + s_bytes) / step_s / 1e9,
+           "ops_us_per_table": {"hashed_rows": float(sum(per[t][:, 0].mean() for t in range(8)) / 8 * 1e6),
+                                "gather": float(g_time / 8 * 1e6), "sgd_sum": float(s_time / 8 * 1e6)}})
+
+
+def run_cs3(args):
+    """CS3 EMA caches: CTS on positives (c_user, c_item) and CMS on all pairs (s_user, s_item)."""
+    import numpy as np
+    import torch
+    import hashed_lookup_row_amd as hlr
+    import synth
+    dev = torch.device("cuda:0")
+    cfg = synth.CS3
+    D, n = cfg.dim, cfg.batch
+    R = D * 4
+    tabs = {k: torch.zeros((m, D), dtype=torch.float32, device=dev)
+            for k, m in {"c_user": cfg.users, "s_user": cfg.users, "c_item": cfg.items, "s_item": cfg.items}.items()}
+    K, W = args.steps, args.warmup
+    inp = []
+    for s in range(2):
+        ur, ir, y = synth.cs3_step(cfg, s + 1)
+        inp.append([torch.from_numpy(x).to(dev) for x in (ur, ir, y)] +
+                   [synth.normal_rows(n, D, 1.0, 5, s + 1, stream=k, device=dev) for k in (1, 2, 3)])
+    timer, cur = HipTimer(), torch.cuda.current_stream(dev).cuda_stream
+    calls = [("c_user", 0, 3, True, cfg.cts_a, cfg.cts_b), ("c_item", 1, 4, True, cfg.cts_a, cfg.cts_b),
+             ("s_user", 0, 5, False, cfg.cms_a, cfg.cms_b), ("s_item", 1, 5, False, cfg.cms_a, cfg.cms_b)]
+    ev = []
+
+    def step(s, rec):
+        x = inp[s % 2]
+        for name, ri, vi, masked, a, b in calls:
+            if rec:
+                ev.append((name, timer.event(), timer.event()))
+                timer.record(ev[-1][1], cur)
+            hlr.ema_update_rows(tabs[name], x[ri], x[vi], x[2] if masked else None, a, b)
+            if rec:
+                timer.record(ev[-1][2], cur)
+
+    for s in range(W):
+        step(s, False)
+    torch.cuda.synchronize()
+    a, b = timer.event(), timer.event()
+    timer.record(a, cur)
+    for s in range(K):
+        step(W + s, True)
+    timer.record(b, cur)
+    torch.cuda.synchronize()
+    total = timer.elapsed_s(a, b)
+    per = {}
+    for name, e0, e1 in ev:
+        per.setdefault(name, []).append(timer.elapsed_s(e0, e1))
+    x = inp[0]
+    ur, ir, y = (t.cpu().numpy() for t in x[:3])
+    m = int(y.sum())
+    nb = {"c_user": m * R + 2 * np.unique(ur[y > 0]).size * R, "c_item": m * R + 2 * np.unique(ir[y > 0]).size * R,
+          "s_user": n * R + 2 * np.unique(ur).size * R, "s_item": n * R + 2 * np.unique(ir).size * R}
+    tot_bytes = sum(nb.values()) + 4 * 9 * n
+    step_s = total / K
+    worst = max(per, key=lambda k: np.mean(per[k]))
+    _line("interaction pairs/s (CTS + CMS EMA row updates)", n / step_s, "pairs/s", K, W, step_s * 1e3,
+          {"workload": cfg.name, "users": cfg.users, "items": cfg.items, "dim": D, "pairs": n},
+          _roof(f"ema_update_rows ({worst})", nb[worst], float(np.mean(per[worst]))),
+          {"dtype": "fp32", "step_hbm_gbs": tot_bytes / step_s / 1e9,
+           "ops_us": {k: float(np.mean(v) * 1e6) for k, v in per.items()},
+           "top_user_occurrences": int(np.bincount(ur).max())})
+
+
+def run_dedup(args):
+    """Standalone dedup_ids on the Memory-Layer ID stream (65,536 int64 IDs per call)."""
+    import numpy as np
+    import torch
+    import hashed_lookup_row_amd as hlr
+    import synth
+    dev = torch.device("cuda:0")
+    cfg = synth.MEMORY_LAYER
+    K, W = args.steps, args.warmup
+    ids = [torch.from_numpy(synth.mpzch_step_ids(cfg, t + 1, 0)[0]).to(dev) for t in range(8)]
+    n = cfg.batch
+    uq = torch.empty(n, dtype=torch.int64, device=dev)
+    lp = torch.empty(n, dtype=torch.int64, device=dev)
+    inv = torch.empty(n, dtype=torch.int64, device=dev)
+    nu = torch.empty(1, dtype=torch.int64, device=dev)
+    timer, cur = HipTimer(), torch.cuda.current_stream(dev).cuda_stream
+    for k in range(W):
+        hlr.dedup_ids(ids[k % 8], uq, lp, inv, nu)
+    t = _timed(timer, cur, lambda k: hlr.dedup_ids(ids[k % 8], uq, lp, inv, nu), K)
+    u = int(nu.item())
+    nbytes = 8 * n + 16 * u + 8 * n  # keys in; unique + last position out; inverse out
+    _line("IDs deduplicated/s (dedup_ids, last occurrence wins)", n / float(np.median(t)), "ids/s", K, W,
+          float(np.median(t)) * 1e3, {"workload": "memory-layer ID stream", "ids": n},
+          _roof("dedup_ids (radix sort + segments, all kernels)", nbytes, float(np.median(t))),
+          {"dtype": "int64", "distinct": u})
 
 
 if __name__ == "__main__":

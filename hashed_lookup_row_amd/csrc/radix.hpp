@@ -2,11 +2,12 @@
 // sorted keys.  Used to group a batch's positions by key (dedup) or by row
 // (duplicate-summed SGD, EMA), positions ascending inside every group.
 //
-// Per pass: hist_kernel (per-tile digit histograms; the last tile to finish
-// turns the digit-major count matrix into exclusive offsets) and
-// scatter_kernel (stable ranks inside the tile from wave ballots + per-wave
-// LDS counters).  Digits are 8..11 bits, chosen so the key width is covered in
-// ceil(bits/11) passes.
+// Per pass: hist_kernel (per-tile digit histograms) and scatter_kernel (each
+// tile derives its output offsets from all tiles' histograms, then stable
+// ranks inside the tile from wave ballots + per-wave LDS counters).  No kernel
+// waits on another block: cross-block data only crosses kernel boundaries (an
+// agent-scope fence inside a kernel writes back the XCD's L2 and is avoided).  Digits are up to 8 bits, chosen so the key width is covered in
+// ceil(bits/8) passes.
 #pragma once
 
 #include "hlr_common.hpp"
@@ -14,10 +15,16 @@
 namespace {
 
 constexpr int kSortThreads = 256;
-constexpr int kSortItems = 16;
-constexpr int kSortTile = kSortThreads * kSortItems;  // 4096 elements per tile
-constexpr int kMaxDigitBits = 11;
-constexpr int kMaxBins = 1 << kMaxDigitBits;
+constexpr int kMaxSortItems = 16;                      // elements per thread, at most
+constexpr int kMaxDigitBits = 8;
+constexpr int kMaxBins = 1 << kMaxDigitBits;           // one digit per thread in the offset scan
+
+// Elements per thread: tiles of 1024..4096 so that a sort runs about 64 tiles.
+inline int sort_items(int64_t n) {
+  if (n <= 64 * 1024) return 4;
+  if (n <= 64 * 2048) return 8;
+  return 16;
+}
 
 struct SortPlan {
   int passes = 0;
@@ -60,14 +67,19 @@ struct SegWork {
   int32_t *seg_start;  // [n]
   int32_t *seg_end;    // [n]
   int64_t *nseg;       // [1]
+  int2 *hlist;         // heavy work units (segment, run), built by the light kernel
+  int32_t *clist;      // segments with more than one run (combined after the heavy kernel)
   int64_t n;
   int nblocks;
+  int items;  // elements per thread (tile = 256 * items)
 };
 
 template <typename K>
 inline size_t segwork_layout(int64_t n, SegWork<K> *w, void *base) {
   hlr::Carver c(base);
-  const int nb = static_cast<int>((n + kSortTile - 1) / kSortTile);
+  const int items = sort_items(n);
+  const int64_t tile = static_cast<int64_t>(kSortThreads) * items;
+  const int nb = static_cast<int>((n + tile - 1) / tile);
   const size_t nn = static_cast<size_t>(n > 0 ? n : 1);
   w->k[0] = c.take<K>(nn);
   w->k[1] = c.take<K>(nn);
@@ -80,8 +92,11 @@ inline size_t segwork_layout(int64_t n, SegWork<K> *w, void *base) {
   w->seg_start = c.take<int32_t>(nn);
   w->seg_end = c.take<int32_t>(nn);
   w->nseg = c.take<int64_t>(1);
+  w->hlist = c.take<int2>(nn / 32 + 64);
+  w->clist = c.take<int32_t>(nn / 256 + 64);
   w->n = n;
   w->nblocks = nb;
+  w->items = items;
   return c.off;
 }
 
@@ -104,85 +119,64 @@ __device__ __forceinline__ uint32_t block_exclusive_scan(uint32_t x, uint32_t *s
   return incl - x;
 }
 
-template <typename K>
+template <typename K, int ITEMS>
 __global__ void __launch_bounds__(kSortThreads)
-    hist_kernel(const K *__restrict__ keys, int64_t n, int shift, int bits, uint32_t *counts, int nblocks,
-                uint32_t *ticket) {
+    hist_kernel(const K *__restrict__ keys, int64_t n, int shift, int bits, uint32_t *counts) {
+  constexpr int TILE = kSortThreads * ITEMS;
   __shared__ uint32_t h[kMaxBins];
-  __shared__ uint32_t sh[kSortThreads];
-  __shared__ int is_last;
   const int bins = 1 << bits;
   const uint32_t mask = static_cast<uint32_t>(bins - 1);
-  for (int d = threadIdx.x; d < bins; d += kSortThreads) h[d] = 0;
+  h[threadIdx.x] = 0;
   __syncthreads();
-  const int64_t base = static_cast<int64_t>(blockIdx.x) * kSortTile;
+  const int64_t base = static_cast<int64_t>(blockIdx.x) * TILE;
 #pragma unroll
-  for (int k = 0; k < kSortItems; ++k) {
+  for (int k = 0; k < ITEMS; ++k) {
     const int64_t idx = base + k * kSortThreads + threadIdx.x;
     if (idx < n) atomicAdd(&h[static_cast<uint32_t>(keys[idx] >> shift) & mask], 1u);
   }
   __syncthreads();
-  for (int d = threadIdx.x; d < bins; d += kSortThreads) counts[static_cast<int64_t>(d) * nblocks + blockIdx.x] = h[d];
-  __threadfence();
-  __syncthreads();
-  if (threadIdx.x == 0) is_last = (atomicAdd(ticket, 1u) == static_cast<uint32_t>(nblocks - 1));
-  __syncthreads();
-  if (!is_last) return;
-  __threadfence();
-  // Digit totals, then an exclusive scan over digits, then per-(digit, tile) offsets.
-  for (int d = threadIdx.x; d < bins; d += kSortThreads) {
-    uint32_t s = 0;
-    for (int b = 0; b < nblocks; ++b) s += counts[static_cast<int64_t>(d) * nblocks + b];
-    h[d] = s;
-  }
-  __syncthreads();
-  const int per = (bins + kSortThreads - 1) / kSortThreads;
-  uint32_t local = 0;
-  for (int i = 0; i < per; ++i) {
-    const int d = threadIdx.x * per + i;
-    if (d < bins) local += h[d];
-  }
-  uint32_t tot;
-  uint32_t run = block_exclusive_scan(local, sh, &tot);
-  for (int i = 0; i < per; ++i) {
-    const int d = threadIdx.x * per + i;
-    if (d < bins) {
-      const uint32_t c = h[d];
-      h[d] = run;
-      run += c;
-    }
-  }
-  __syncthreads();
-  for (int d = threadIdx.x; d < bins; d += kSortThreads) {
-    uint32_t r = h[d];
-    for (int b = 0; b < nblocks; ++b) {
-      const int64_t at = static_cast<int64_t>(d) * nblocks + b;
-      const uint32_t c = counts[at];
-      counts[at] = r;
-      r += c;
-    }
-  }
-  if (threadIdx.x == 0) *ticket = 0u;
+  counts[static_cast<int64_t>(blockIdx.x) * kMaxBins + threadIdx.x] = threadIdx.x < bins ? h[threadIdx.x] : 0u;
 }
 
-template <typename K>
+template <typename K, int ITEMS>
 __global__ void __launch_bounds__(kSortThreads)
     scatter_kernel(const K *__restrict__ kin, const uint32_t *__restrict__ vin, K *__restrict__ kout,
-                   uint32_t *__restrict__ vout, int64_t n, int shift, int bits, const uint32_t *__restrict__ offsets,
+                   uint32_t *__restrict__ vout, int64_t n, int shift, int bits, const uint32_t *__restrict__ counts,
                    int nblocks) {
+  constexpr int TILE = kSortThreads * ITEMS;
   __shared__ uint32_t cnt[4][kMaxBins];
+  __shared__ uint32_t sh[kSortThreads];
+  __shared__ uint32_t offs[kMaxBins];
   const int bins = 1 << bits;
   const uint32_t mask = static_cast<uint32_t>(bins - 1);
   const int w = threadIdx.x >> 6;
+  // This tile's output offset of every digit: (keys with smaller digits) + (same digit, earlier tiles).
+  // Thread d reads digit d of every tile's histogram (rows of 256 counts, coalesced across the block).
+  {
+    const int d = threadIdx.x;
+    uint32_t before = 0, total = 0;
+    for (int b0 = 0; b0 < nblocks; b0 += 16) {
+      uint32_t v[16];
+#pragma unroll
+      for (int u = 0; u < 16; ++u) v[u] = b0 + u < nblocks ? counts[static_cast<int64_t>(b0 + u) * kMaxBins + d] : 0u;
+#pragma unroll
+      for (int u = 0; u < 16; ++u) {
+        if (b0 + u < static_cast<int>(blockIdx.x)) before += v[u];
+        total += v[u];
+      }
+    }
+    uint32_t all;
+    offs[d] = block_exclusive_scan(total, sh, &all) + before;
+  }
   for (int x = threadIdx.x; x < 4 * bins; x += kSortThreads) cnt[x / bins][x % bins] = 0;
   __syncthreads();
-  const int64_t base = static_cast<int64_t>(blockIdx.x) * kSortTile + w * (kSortTile / 4);
+  const int64_t base = static_cast<int64_t>(blockIdx.x) * TILE + w * (TILE / 4);
   const uint64_t lt = hlr::lanemask_lt();
-  K kk[kSortItems];
-  uint32_t vv[kSortItems];
-  uint32_t rk[kSortItems];
+  K kk[ITEMS];
+  uint32_t vv[ITEMS];
+  uint32_t rk[ITEMS];
 #pragma unroll
-  for (int r = 0; r < kSortItems; ++r) {
+  for (int r = 0; r < ITEMS; ++r) {
     const int64_t idx = base + r * hlr::kWave + hlr::lane_id();
     const bool valid = idx < n;
     const K k = valid ? kin[idx] : K(0);
@@ -202,7 +196,7 @@ __global__ void __launch_bounds__(kSortThreads)
   }
   __syncthreads();
   for (int d = threadIdx.x; d < bins; d += kSortThreads) {
-    uint32_t run = offsets[static_cast<int64_t>(d) * nblocks + blockIdx.x];
+    uint32_t run = offs[d];
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
       const uint32_t c = cnt[q][d];
@@ -212,7 +206,7 @@ __global__ void __launch_bounds__(kSortThreads)
   }
   __syncthreads();
 #pragma unroll
-  for (int r = 0; r < kSortItems; ++r) {
+  for (int r = 0; r < ITEMS; ++r) {
     const int64_t idx = base + r * hlr::kWave + hlr::lane_id();
     if (idx < n) {
       const uint32_t d = static_cast<uint32_t>(kk[r] >> shift) & mask;
@@ -223,18 +217,16 @@ __global__ void __launch_bounds__(kSortThreads)
   }
 }
 
-// Segment pass 1: number of segment heads per tile; the last tile turns the
-// counts into exclusive tile offsets (bcount[nblocks + b]) and the total.
-// Elements whose key equals `excluded` belong to no segment.
+// Segment pass 1: number of segment heads per tile.  Elements whose key equals
+// `excluded` belong to no segment.
 template <typename K>
 __global__ void __launch_bounds__(kSortThreads)
     seg_count_kernel(const K *__restrict__ keys, int64_t n, K excluded, bool use_excluded, uint32_t *bcount,
-                     int nblocks, uint32_t *ticket, int64_t *nseg) {
+                     int items) {
   __shared__ uint32_t sh[kSortThreads];
-  __shared__ int is_last;
-  const int64_t base = static_cast<int64_t>(blockIdx.x) * kSortTile + threadIdx.x * kSortItems;
+  const int64_t base = static_cast<int64_t>(blockIdx.x) * kSortThreads * items + threadIdx.x * items;
   uint32_t c = 0;
-  for (int i = 0; i < kSortItems; ++i) {
+  for (int i = 0; i < items; ++i) {
     const int64_t j = base + i;
     if (j < n) {
       const K k = keys[j];
@@ -246,22 +238,6 @@ __global__ void __launch_bounds__(kSortThreads)
   uint32_t tot;
   block_exclusive_scan(c, sh, &tot);
   if (threadIdx.x == 0) bcount[blockIdx.x] = tot;
-  __threadfence();
-  __syncthreads();
-  if (threadIdx.x == 0) is_last = (atomicAdd(ticket, 1u) == static_cast<uint32_t>(nblocks - 1));
-  __syncthreads();
-  if (!is_last) return;
-  __threadfence();
-  if (threadIdx.x == 0) {
-    uint32_t run = 0;
-    for (int b = 0; b < nblocks; ++b) {
-      const uint32_t x = bcount[b];
-      bcount[nblocks + b] = run;
-      run += x;
-    }
-    *nseg = run;
-    *ticket = 0u;
-  }
 }
 
 // Segment pass 2: per sorted element its segment index; heads and tails record
@@ -271,11 +247,29 @@ template <typename K, typename Emit>
 __global__ void __launch_bounds__(kSortThreads)
     seg_index_kernel(const K *__restrict__ keys, const uint32_t *__restrict__ vals, int64_t n, K excluded,
                      bool use_excluded, const uint32_t *__restrict__ bcount, int nblocks, int32_t *segidx,
-                     int32_t *seg_start, int32_t *seg_end, Emit emit) {
+                     int32_t *seg_start, int32_t *seg_end, int64_t *nseg, Emit emit, int items) {
   __shared__ uint32_t sh[kSortThreads];
-  const int64_t base = static_cast<int64_t>(blockIdx.x) * kSortTile + threadIdx.x * kSortItems;
+  __shared__ uint32_t blk_off;
+  // This tile's first segment index = heads in earlier tiles; tile 0 also publishes the total.
+  {
+    uint32_t before = 0, total = 0;
+    for (int b = threadIdx.x; b < nblocks; b += kSortThreads) {
+      const uint32_t v = bcount[b];
+      if (b < static_cast<int>(blockIdx.x)) before += v;
+      total += v;
+    }
+    uint32_t all;
+    const uint32_t bsum = block_exclusive_scan(before, sh, &all);
+    (void)bsum;
+    if (threadIdx.x == 0) blk_off = all;
+    uint32_t tall;
+    block_exclusive_scan(total, sh, &tall);
+    if (blockIdx.x == 0 && threadIdx.x == 0) *nseg = tall;
+    __syncthreads();
+  }
+  const int64_t base = static_cast<int64_t>(blockIdx.x) * kSortThreads * items + threadIdx.x * items;
   uint32_t c = 0;
-  for (int i = 0; i < kSortItems; ++i) {
+  for (int i = 0; i < items; ++i) {
     const int64_t j = base + i;
     if (j < n) {
       const K k = keys[j];
@@ -284,8 +278,8 @@ __global__ void __launch_bounds__(kSortThreads)
     }
   }
   uint32_t tot;
-  uint32_t run = block_exclusive_scan(c, sh, &tot) + bcount[nblocks + blockIdx.x];
-  for (int i = 0; i < kSortItems; ++i) {
+  uint32_t run = block_exclusive_scan(c, sh, &tot) + blk_off;
+  for (int i = 0; i < items; ++i) {
     const int64_t j = base + i;
     if (j >= n) break;
     const K k = keys[j];
@@ -311,27 +305,34 @@ struct NoEmit {
 };
 
 // Runs every radix pass; returns the index (0/1) of the buffer holding the result.
-template <typename K>
-inline int radix_sort_pairs(SegWork<K> &w, int total_bits, hipStream_t s) {
+template <typename K, int ITEMS>
+inline int radix_sort_pairs_t(SegWork<K> &w, int total_bits, hipStream_t s) {
   const SortPlan plan = make_plan(total_bits);
   int cur = 0;
   for (int p = 0; p < plan.passes; ++p) {
-    hist_kernel<K><<<w.nblocks, kSortThreads, 0, s>>>(w.k[cur], w.n, plan.shift[p], plan.bits[p], w.counts,
-                                                       w.nblocks, w.ticket);
-    scatter_kernel<K><<<w.nblocks, kSortThreads, 0, s>>>(w.k[cur], w.v[cur], w.k[cur ^ 1], w.v[cur ^ 1], w.n,
-                                                          plan.shift[p], plan.bits[p], w.counts, w.nblocks);
+    hist_kernel<K, ITEMS><<<w.nblocks, kSortThreads, 0, s>>>(w.k[cur], w.n, plan.shift[p], plan.bits[p],
+                                                              w.counts);
+    scatter_kernel<K, ITEMS><<<w.nblocks, kSortThreads, 0, s>>>(w.k[cur], w.v[cur], w.k[cur ^ 1], w.v[cur ^ 1],
+                                                                 w.n, plan.shift[p], plan.bits[p], w.counts,
+                                                                 w.nblocks);
     cur ^= 1;
   }
   return cur;
 }
 
+template <typename K>
+inline int radix_sort_pairs(SegWork<K> &w, int total_bits, hipStream_t s) {
+  if (w.items == 4) return radix_sort_pairs_t<K, 4>(w, total_bits, s);
+  if (w.items == 8) return radix_sort_pairs_t<K, 8>(w, total_bits, s);
+  return radix_sort_pairs_t<K, 16>(w, total_bits, s);
+}
+
 template <typename K, typename Emit>
 inline void segment_sorted(SegWork<K> &w, int cur, K excluded, bool use_excluded, Emit emit, hipStream_t s) {
-  seg_count_kernel<K><<<w.nblocks, kSortThreads, 0, s>>>(w.k[cur], w.n, excluded, use_excluded, w.bcount,
-                                                          w.nblocks, w.ticket, w.nseg);
+  seg_count_kernel<K><<<w.nblocks, kSortThreads, 0, s>>>(w.k[cur], w.n, excluded, use_excluded, w.bcount, w.items);
   seg_index_kernel<K, Emit><<<w.nblocks, kSortThreads, 0, s>>>(w.k[cur], w.v[cur], w.n, excluded, use_excluded,
                                                                 w.bcount, w.nblocks, w.segidx, w.seg_start,
-                                                                w.seg_end, emit);
+                                                                w.seg_end, w.nseg, emit, w.items);
 }
 
 }  // namespace
@@ -365,5 +366,99 @@ inline int group_by_row(SegWork<uint32_t> &w, const int64_t *rows, const uint8_t
   segment_sorted<uint32_t>(w, cur, static_cast<uint32_t>(num_rows), true, NoEmit{}, s);
   return cur;
 }
+
+}  // namespace
+
+namespace {
+
+// Partial results of the runs (runs of B consecutive occurrences of a row) of
+// rows longer than B.  At most one such row starts inside any sorted window
+// [x*B, (x+1)*B) and at most one non-first run starts inside it, so
+// slot = 2*window + (first run ? 1 : 0) is unique per call and < 2*ceil(n/B) + 2.
+__device__ __forceinline__ int64_t run_slot(int32_t j0, int32_t m, int B) {
+  return 2 * static_cast<int64_t>(j0 / B) + (m == 0 ? 1 : 0);
+}
+
+}  // namespace
+
+namespace {
+
+// Block-cooperative streaming of rows through LDS for an in-order consumer.
+// Rows row_of(j) (D floats, 16-byte aligned) for j in [j0, j1) are loaded in
+// stages of kStageFloats floats (64 KiB: 32 rows at D = 512, 128 rows at D = 128)
+// with every thread keeping 16 float4 loads in flight, written to one of two LDS
+// buffers, and consumed in order while the next stage's loads are in flight.
+// Thread t owns elements e = t + 256*q (q < EPT) of every row and calls
+// f(j, q, value) for each position j in order.  All threads of the block must
+// call it (it synchronises).  Requires dynamic LDS of 2 * kStageFloats floats.
+constexpr int kStageFloats = 16384;
+constexpr int kStageLoads = 16;  // float4 per thread per stage (256 threads x 16 x 16 B = 64 KiB)
+constexpr int kHeavyLds = 2 * kStageFloats * 4;  // bytes
+
+template <int EPT, typename RowOf, typename F>
+__device__ __forceinline__ void block_stream(RowOf row_of, int32_t j0, int32_t j1, int64_t D, float *lds, F f) {
+  const int64_t v4 = D / 4;
+  const int sp = static_cast<int>(kStageFloats / D);  // rows per stage
+  const int units = static_cast<int>(sp * v4);
+  const int nst = (j1 - j0 + sp - 1) / sp;
+  const int tid = threadIdx.x;
+  float4 reg[kStageLoads];
+  auto load = [&](int st) {
+    const int32_t base = j0 + st * sp;
+#pragma unroll
+    for (int k = 0; k < kStageLoads; ++k) {
+      const int u = tid + 256 * k;
+      reg[k] = make_float4(0.f, 0.f, 0.f, 0.f);
+      if (u < units) {
+        const int p = static_cast<int>(u / v4);
+        const int32_t j = base + p;
+        if (j < j1) reg[k] = row_of(j)[u - p * v4];
+      }
+    }
+  };
+  auto store = [&](int buf) {
+    float4 *L = reinterpret_cast<float4 *>(lds + buf * kStageFloats);
+#pragma unroll
+    for (int k = 0; k < kStageLoads; ++k) {
+      const int u = tid + 256 * k;
+      if (u < units) L[u] = reg[k];
+    }
+  };
+  if (nst <= 0) return;
+  load(0);
+  store(0);
+  __syncthreads();
+  for (int st = 0; st < nst; ++st) {
+    if (st + 1 < nst) load(st + 1);
+    const float *L = lds + (st & 1) * kStageFloats;
+    const int32_t base = j0 + st * sp;
+    const int cnt = j1 - base < sp ? j1 - base : sp;
+    for (int p = 0; p < cnt; ++p) {
+#pragma unroll
+      for (int q = 0; q < EPT; ++q) {
+        const int64_t e = tid + 256 * q;
+        if (e < D) f(base + p, q, L[p * D + e]);
+      }
+    }
+    if (st + 1 < nst) store((st + 1) & 1);
+    __syncthreads();
+  }
+}
+
+// Registers a long segment (>= kHeavyMin occurrences, cut into runs of B) as
+// work for the block kernels: one entry (segment, run) per run, and the
+// segment in the combine list when it has more than one run.  Called by one
+// lane; counters[0] / counters[1] count the two lists (zeroed by rowkey_init).
+// Capacity: runs <= n/kHeavyMin + n/B <= n/32 for B >= 64.
+__device__ __forceinline__ void push_heavy(int32_t k, int32_t len, int B, uint32_t *counters, int2 *hlist,
+                                           int32_t *clist) {
+  const int32_t nr = (len + B - 1) / B;
+  const uint32_t base = atomicAdd(&counters[0], static_cast<uint32_t>(nr));
+  for (int32_t m = 0; m < nr; ++m) hlist[base + m] = make_int2(k, m);
+  if (nr > 1) clist[atomicAdd(&counters[1], 1u)] = k;
+}
+
+constexpr int kHeavyMin = 64;  // segments with at least this many occurrences go to the block kernels
+constexpr int kHeavyBlocks = 256;  // block kernels: one 128 KiB-LDS block per CU
 
 }  // namespace

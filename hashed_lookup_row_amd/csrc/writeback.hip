@@ -15,10 +15,13 @@
 // SGD_SUM — per-row SGD with duplicate gradients summed and applied once (the
 // same sparse-table update pattern at a learning rate other than 1, as in the
 // hashed tables of "DLRMv4: MLPerf recommendation training goes sequential").
-// Positions are grouped by row with a stable radix sort (radix.hpp); one wave
-// owns a row: it sums the row's gradients in batch order in runs of 256
-// occurrences (run totals added in batch order) and writes
-// fl(M - fl(lr * s)).
+// Positions are grouped by row with a stable radix sort (radix.hpp).  Rows with
+// few occurrences are summed by one wave each (sgd_light), which also lists the
+// runs of longer rows.  Every run of 256 consecutive occurrences of a longer
+// row is summed in batch order by its own block, which streams the gradient
+// rows through LDS (sgd_heavy), so a Zipf-hot row (tens of thousands of
+// duplicates) spreads over the whole GPU; sgd_combine then adds each row's run
+// totals in batch order and writes fl(M - fl(lr * s)).
 #include "radix.hpp"
 
 namespace {
@@ -172,79 +175,175 @@ __global__ void __launch_bounds__(kThreads)
   }
 }
 
-// One wave per row segment; lanes own 16-byte column units (NC per lane).
+// Duplicate-summed SGD helpers: a wave sums a run of a row's gradients in batch
+// order with the next U rows' loads in flight (lanes own 16-byte column units).
+constexpr int kRun = HLR_SGD_SUM_RUN;
+constexpr int kPrefetch = 8;
+
 template <int NC>
-__global__ void __launch_bounds__(kThreads)
-    sgd_apply(float4 *table, const float4 *__restrict__ g, const uint32_t *__restrict__ skey,
-              const uint32_t *__restrict__ spos, const int32_t *__restrict__ seg_start,
-              const int32_t *__restrict__ seg_end, const int64_t *__restrict__ nseg, float lr, int64_t v4) {
-  const int64_t nsegs = *nseg;
-  const int64_t waves = static_cast<int64_t>(gridDim.x) * (kThreads / kWave);
-  const int lane = lane_id();
-  for (int64_t k = (static_cast<int64_t>(blockIdx.x) * kThreads + threadIdx.x) / kWave; k < nsegs; k += waves) {
-    const int32_t s = seg_start[k], e = seg_end[k];
-    const int64_t r = skey[s];
-    float4 tot[NC], run[NC];
-    for (int32_t rs = s; rs < e; rs += HLR_SGD_SUM_RUN) {
-      const int32_t re = rs + HLR_SGD_SUM_RUN < e ? rs + HLR_SGD_SUM_RUN : e;
-      {
-        const int64_t p = spos[rs];
+__device__ __forceinline__ void add4(float4 (&acc)[NC], const float4 (&x)[NC]) {
 #pragma unroll
-        for (int q = 0; q < NC; ++q) {
-          const int64_t c = lane + q * kWave;
-          run[q] = c < v4 ? g[p * v4 + c] : make_float4(0.f, 0.f, 0.f, 0.f);
-        }
+  for (int q = 0; q < NC; ++q)
+    acc[q] = make_float4(acc[q].x + x[q].x, acc[q].y + x[q].y, acc[q].z + x[q].z, acc[q].w + x[q].w);
+}
+
+// acc = g[spos[j0]]; then acc += g[spos[j]] for j in (j0, j1), in order.
+template <int NC>
+__device__ __forceinline__ void sum_run(const float4 *__restrict__ g, const uint32_t *__restrict__ spos, int32_t j0,
+                                        int32_t j1, int64_t v4, int lane, float4 (&acc)[NC]) {
+#pragma unroll
+  for (int q = 0; q < NC; ++q) {
+    const int64_t c = lane + q * kWave;
+    acc[q] = c < v4 ? g[static_cast<int64_t>(spos[j0]) * v4 + c] : make_float4(0.f, 0.f, 0.f, 0.f);
+  }
+  int32_t j = j0 + 1;
+  for (; j + kPrefetch <= j1; j += kPrefetch) {
+    float4 x[kPrefetch][NC];
+#pragma unroll
+    for (int u = 0; u < kPrefetch; ++u) {
+      const int64_t p = spos[j + u];
+#pragma unroll
+      for (int q = 0; q < NC; ++q) {
+        const int64_t c = lane + q * kWave;
+        x[u][q] = c < v4 ? g[p * v4 + c] : make_float4(0.f, 0.f, 0.f, 0.f);
       }
-      int32_t j = rs + 1;
-      for (; j + 4 <= re; j += 4) {
-        float4 x[4][NC];
-#pragma unroll
-        for (int u = 0; u < 4; ++u) {
-          const int64_t p = spos[j + u];
-#pragma unroll
-          for (int q = 0; q < NC; ++q) {
-            const int64_t c = lane + q * kWave;
-            x[u][q] = c < v4 ? g[p * v4 + c] : make_float4(0.f, 0.f, 0.f, 0.f);
-          }
-        }
-#pragma unroll
-        for (int u = 0; u < 4; ++u)
-#pragma unroll
-          for (int q = 0; q < NC; ++q) run[q] = make_float4(run[q].x + x[u][q].x, run[q].y + x[u][q].y,
-                                                            run[q].z + x[u][q].z, run[q].w + x[u][q].w);
-      }
-      for (; j < re; ++j) {
-        const int64_t p = spos[j];
-#pragma unroll
-        for (int q = 0; q < NC; ++q) {
-          const int64_t c = lane + q * kWave;
-          const float4 x = c < v4 ? g[p * v4 + c] : make_float4(0.f, 0.f, 0.f, 0.f);
-          run[q] = make_float4(run[q].x + x.x, run[q].y + x.y, run[q].z + x.z, run[q].w + x.w);
-        }
-      }
-#pragma unroll
-      for (int q = 0; q < NC; ++q)
-        tot[q] = rs == s ? run[q]
-                         : make_float4(tot[q].x + run[q].x, tot[q].y + run[q].y, tot[q].z + run[q].z,
-                                       tot[q].w + run[q].w);
     }
+#pragma unroll
+    for (int u = 0; u < kPrefetch; ++u) add4<NC>(acc, x[u]);
+  }
+  for (; j < j1; ++j) {
+    float4 x[NC];
+    const int64_t p = spos[j];
 #pragma unroll
     for (int q = 0; q < NC; ++q) {
       const int64_t c = lane + q * kWave;
-      if (c < v4) {
-        const float4 wv = table[r * v4 + c];
-        const float4 st = make_float4(lr * tot[q].x, lr * tot[q].y, lr * tot[q].z, lr * tot[q].w);
-        table[r * v4 + c] = f4_sub(wv, st);
-      }
+      x[q] = c < v4 ? g[p * v4 + c] : make_float4(0.f, 0.f, 0.f, 0.f);
     }
+    add4<NC>(acc, x);
   }
 }
 
 template <int NC>
-void sgd_launch(float4 *t4, const float4 *g4, SegWork<uint32_t> &w, int cur, float lr, int64_t v4, hipStream_t s) {
-  int grid = grid_for(w.n, 4 * 8);  // ~8 segments per wave at most, 4 waves per block
-  if (grid > 2048) grid = 2048;
-  sgd_apply<NC><<<grid, kThreads, 0, s>>>(t4, g4, w.k[cur], w.v[cur], w.seg_start, w.seg_end, w.nseg, lr, v4);
+__device__ __forceinline__ void sgd_update(float4 *table, int64_t r, const float4 (&tot)[NC], float lr, int64_t v4,
+                                           int lane) {
+#pragma unroll
+  for (int q = 0; q < NC; ++q) {
+    const int64_t c = lane + q * kWave;
+    if (c < v4) {
+      const float4 wv = table[r * v4 + c];
+      const float4 st = make_float4(lr * tot[q].x, lr * tot[q].y, lr * tot[q].z, lr * tot[q].w);
+      table[r * v4 + c] = f4_sub(wv, st);  // fl(M - fl(lr * s))
+    }
+  }
+}
+
+// Light rows (fewer than kHeavyMin occurrences, hence one run): one wave per
+// row.  Longer rows are registered for the block kernels.
+template <int NC>
+__global__ void __launch_bounds__(kThreads)
+    sgd_light(float4 *table, const float4 *__restrict__ g, const uint32_t *__restrict__ skey,
+              const uint32_t *__restrict__ spos, const int32_t *__restrict__ seg_start,
+              const int32_t *__restrict__ seg_end, const int64_t *__restrict__ nseg_p, float lr, int64_t v4,
+              uint32_t *counters, int2 *hlist, int32_t *clist) {
+  const int64_t nseg = *nseg_p;
+  const int64_t waves = static_cast<int64_t>(gridDim.x) * (kThreads / kWave);
+  const int lane = lane_id();
+  for (int64_t k = (static_cast<int64_t>(blockIdx.x) * kThreads + threadIdx.x) / kWave; k < nseg; k += waves) {
+    const int32_t s = seg_start[k], e = seg_end[k];
+    if (e - s >= kHeavyMin) {
+      if (lane == 0) push_heavy(static_cast<int32_t>(k), e - s, kRun, counters, hlist, clist);
+      continue;
+    }
+    float4 run[NC];
+    sum_run<NC>(g, spos, s, e, v4, lane, run);
+    sgd_update<NC>(table, skey[s], run, lr, v4, lane);
+  }
+}
+
+template <int EPT>
+__device__ __forceinline__ void sgd_write(float *table, int64_t r, const float (&acc)[EPT], float lr, int64_t D) {
+#pragma unroll
+  for (int q = 0; q < EPT; ++q) {
+    const int64_t e = threadIdx.x + 256 * q;
+    if (e < D) {
+      const float step = lr * acc[q];
+      table[r * D + e] = table[r * D + e] - step;  // fl(M - fl(lr * s))
+    }
+  }
+}
+
+// Heavy rows: one block per run of <= 256 occurrences, the gradient rows
+// streamed through LDS (block_stream).  A row with one run is updated at once;
+// otherwise the run total goes to `partial` for sgd_combine.
+template <int EPT>
+__global__ void __launch_bounds__(kThreads)
+    sgd_heavy(float *table, const float *__restrict__ g, const uint32_t *__restrict__ skey,
+              const uint32_t *__restrict__ spos, const int32_t *__restrict__ seg_start,
+              const int32_t *__restrict__ seg_end, const uint32_t *__restrict__ counters,
+              const int2 *__restrict__ hlist, float lr, int64_t D, float *partial) {
+  __shared__ float lds[2 * kStageFloats];
+  const uint32_t count = counters[0];
+  const int64_t v4 = D / 4;
+  const float4 *g4 = reinterpret_cast<const float4 *>(g);
+  for (uint32_t i = blockIdx.x; i < count; i += gridDim.x) {
+    const int2 km = hlist[i];
+    const int32_t s = seg_start[km.x], e = seg_end[km.x];
+    const int32_t j0 = s + km.y * kRun;
+    const int32_t j1 = j0 + kRun < e ? j0 + kRun : e;
+    float acc[EPT];
+    block_stream<EPT>([&](int32_t j) { return g4 + static_cast<int64_t>(spos[j]) * v4; }, j0, j1, D, lds,
+                      [&](int32_t j, int q, float v) { acc[q] = j == j0 ? v : acc[q] + v; });
+    if (e - s <= kRun) {
+      sgd_write<EPT>(table, skey[s], acc, lr, D);
+      continue;
+    }
+    const int64_t slot = run_slot(j0, km.y, kRun);
+#pragma unroll
+    for (int q = 0; q < EPT; ++q) {
+      const int64_t el = threadIdx.x + 256 * q;
+      if (el < D) partial[slot * D + el] = acc[q];
+    }
+  }
+}
+
+// Rows with several runs: the run totals are added in batch order (streamed
+// through LDS), then the row is updated once.
+template <int EPT>
+__global__ void __launch_bounds__(kThreads)
+    sgd_combine(float *table, const uint32_t *__restrict__ skey, const int32_t *__restrict__ seg_start,
+                const int32_t *__restrict__ seg_end, const uint32_t *__restrict__ counters,
+                const int32_t *__restrict__ clist, float lr, int64_t D, const float *__restrict__ partial) {
+  __shared__ float lds[2 * kStageFloats];
+  const uint32_t count = counters[1];
+  for (uint32_t i = blockIdx.x; i < count; i += gridDim.x) {
+    const int32_t k = clist[i];
+    const int32_t s = seg_start[k], e = seg_end[k];
+    const int32_t nruns = (e - s + kRun - 1) / kRun;
+    float acc[EPT];
+    block_stream<EPT>(
+        [&](int32_t m) { return reinterpret_cast<const float4 *>(partial + run_slot(s + m * kRun, m, kRun) * D); }, 0,
+        nruns, D, lds, [&](int32_t m, int q, float v) { acc[q] = m == 0 ? v : acc[q] + v; });
+    sgd_write<EPT>(table, skey[s], acc, lr, D);
+  }
+}
+
+inline size_t sgd_partial_elems(int64_t n, int64_t dim) {
+  return static_cast<size_t>(2 * ((n + kRun - 1) / kRun) + 2) * static_cast<size_t>(dim / 4);
+}
+
+template <int NC, int EPT>
+void sgd_launch(float *table, const float *g, SegWork<uint32_t> &w, int cur, float lr, int64_t dim, float *partial,
+                hipStream_t s) {
+  const int64_t v4 = dim / 4;
+  int grid = grid_for(w.n, 4 * 4);
+  if (grid > 4096) grid = 4096;
+  sgd_light<NC><<<grid, kThreads, 0, s>>>(reinterpret_cast<float4 *>(table), reinterpret_cast<const float4 *>(g),
+                                          w.k[cur], w.v[cur], w.seg_start, w.seg_end, w.nseg, lr, v4, w.ticket,
+                                          w.hlist, w.clist);
+  sgd_heavy<EPT><<<kHeavyBlocks, kThreads, 0, s>>>(table, g, w.k[cur], w.v[cur], w.seg_start, w.seg_end, w.ticket,
+                                                    w.hlist, lr, dim, partial);
+  sgd_combine<EPT><<<kHeavyBlocks, kThreads, 0, s>>>(table, w.k[cur], w.seg_start, w.seg_end, w.ticket, w.clist, lr,
+                                                      dim, partial);
 }
 
 }  // namespace
@@ -258,7 +357,10 @@ extern "C" size_t writeback_rows_workspace_size(int64_t num_rows, int64_t dim, i
     return lw_layout(n, &w, nullptr);
   }
   SegWork<uint32_t> w;
-  return segwork_layout<uint32_t>(n, &w, nullptr);
+  Carver c(nullptr);
+  c.off = segwork_layout<uint32_t>(n, &w, nullptr);
+  c.take<float4>(sgd_partial_elems(n, dim > 0 ? dim : 4));
+  return c.off;
 }
 
 extern "C" hlr_status writeback_rows(float *table, int64_t num_rows, int64_t dim, const int64_t *rows,
@@ -293,13 +395,15 @@ extern "C" hlr_status writeback_rows(float *table, int64_t num_rows, int64_t dim
     else return HLR_UNSUPPORTED_DIM;
     return launch_status();
   }
-  SegWork<uint32_t> w;
-  segwork_layout<uint32_t>(n, &w, ws);
-  const int cur = group_by_row(w, rows, nullptr, num_rows, stream);
   const int64_t nc = (v4 + kWave - 1) / kWave;
-  if (nc == 1) sgd_launch<1>(t4, s4, w, cur, lr, v4, stream);
-  else if (nc == 2) sgd_launch<2>(t4, s4, w, cur, lr, v4, stream);
-  else if (nc <= 4) sgd_launch<4>(t4, s4, w, cur, lr, v4, stream);
-  else return HLR_UNSUPPORTED_DIM;  // dim > 1024
+  if (nc > 4) return HLR_UNSUPPORTED_DIM;  // dim > 1024
+  SegWork<uint32_t> w;
+  Carver c(ws);
+  c.off = segwork_layout<uint32_t>(n, &w, ws);
+  float *partial = reinterpret_cast<float *>(c.take<float4>(sgd_partial_elems(n, dim)));
+  const int cur = group_by_row(w, rows, nullptr, num_rows, stream);
+  if (nc == 1) sgd_launch<1, 1>(table, src, w, cur, lr, dim, partial, stream);
+  else if (nc == 2) sgd_launch<2, 2>(table, src, w, cur, lr, dim, partial, stream);
+  else sgd_launch<4, 4>(table, src, w, cur, lr, dim, partial, stream);
   return launch_status();
 }

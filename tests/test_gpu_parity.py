@@ -302,3 +302,47 @@ def test_repeat_runs_are_bit_identical(dev):
         hlr.writeback_rows(t, rows, vals)
         outs.append(to_np(t))
     assert bits_equal(outs[0], outs[1])
+
+
+def test_ema_long_row_many_chunks(dev):
+    """One row with 40,000 occurrences (a = 0.95): dozens of speculative chunks, bit-exact."""
+    g = np.random.default_rng(40)
+    n, D = 40_000, 128
+    rows = np.zeros(n, np.int64)
+    rows[g.random(n) < 0.1] = 1
+    vals = g.standard_normal((n, D)).astype(np.float32)
+    table = g.standard_normal((2, D)).astype(np.float32)
+    t = torch.from_numpy(table).to(dev)
+    hlr.ema_update_rows(t, torch.from_numpy(rows).to(dev), torch.from_numpy(vals).to(dev), None, 0.95, 0.05)
+    oracle.ema(table, rows, vals, None, 0.95, 0.05)
+    assert bits_equal(to_np(t), table)
+
+
+@pytest.mark.parametrize("spike_at", [900, 1990, 3000])
+def test_ema_speculation_fallback_is_exact(dev, spike_at):
+    """Huge values just before a chunk's warm-up window make its speculative start wrong; the
+    chunk must be recomputed from the exact state (a = 0.5: warm-up 47, chunks of 1024)."""
+    g = np.random.default_rng(spike_at)
+    n, D = 4500, 8
+    rows = np.zeros(n, np.int64)
+    vals = g.standard_normal((n, D)).astype(np.float32)
+    vals[spike_at:spike_at + 60] = 1e30
+    table = np.zeros((1, D), np.float32)
+    t = torch.from_numpy(table).to(dev)
+    hlr.ema_update_rows(t, torch.from_numpy(rows).to(dev), torch.from_numpy(vals).to(dev), None, 0.5, 0.5)
+    oracle.ema(table, rows, vals, None, 0.5, 0.5)
+    assert bits_equal(to_np(t), table)
+
+
+def test_sgd_sum_single_row_many_runs(dev):
+    """One row with 30,000 duplicate gradients: 118 runs summed in parallel, combined in order."""
+    g = np.random.default_rng(30)
+    n, D = 30_000, 512
+    rows = np.where(g.random(n) < 0.8, 7, g.integers(0, 10, size=n)).astype(np.int64)
+    grads = (g.standard_normal((n, D)) * 1e-3).astype(np.float32)
+    table = (g.standard_normal((10, D)) * 0.01).astype(np.float32)
+    t = torch.from_numpy(table).to(dev)
+    hlr.writeback_rows(t, torch.from_numpy(rows).to(dev), torch.from_numpy(grads).to(dev), mode=hlr.WB_SGD_SUM,
+                       lr=0.01)
+    oracle.sgd_sum(table, rows, grads, 0.01)
+    assert bits_equal(to_np(t), table)
