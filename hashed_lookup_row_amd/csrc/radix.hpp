@@ -383,70 +383,107 @@ __device__ __forceinline__ int64_t run_slot(int32_t j0, int32_t m, int B) {
 
 namespace {
 
-// Block-cooperative streaming of rows through LDS for an in-order consumer.
-// Rows row_of(j) (D floats, 16-byte aligned) for j in [j0, j1) are loaded in
-// stages of kStageFloats floats (64 KiB: 32 rows at D = 512, 128 rows at D = 128)
-// with every thread keeping 16 float4 loads in flight, written to one of two LDS
-// buffers, and consumed in order while the next stage's loads are in flight.
-// Thread t owns elements e = t + 256*q (q < EPT) of every row and calls
-// f(j, q, value) for each position j in order.  All threads of the block must
-// call it (it synchronises).  Requires dynamic LDS of 2 * kStageFloats floats.
-constexpr int kStageFloats = 16384;
-constexpr int kStageLoads = 16;  // float4 per thread per stage (256 threads x 16 x 16 B = 64 KiB)
-constexpr int kHeavyLds = 2 * kStageFloats * 4;  // bytes
+// Heavy rows are processed as independent wave work items, one per (run, slice):
+// a slice is 128 consecutive elements of the row (lanes own 2 each, float2), so a
+// row of D elements has ceil(D / 128) slices and every slice of every run is
+// its own wave.  slice_run() applies f(j, x) to positions j in [j0, j1) in order.
+// Loads go out kSlicePrefetch positions at a time, all issued before any is
+// used: the position indices first (wave-uniform, so scalar loads), then the
+// rows, with no per-lane condition on either (lanes past the end of the row
+// read element 0 and their results are dropped by the caller; positions past
+// j1 in the last batch re-read position j1 - 1 and are not applied).
+constexpr int kSliceElems = 128;
+constexpr int kSlicePrefetch = 32;
 
-template <int EPT, typename RowOf, typename F>
-__device__ __forceinline__ void block_stream(RowOf row_of, int32_t j0, int32_t j1, int64_t D, float *lds, F f) {
-  const int64_t v4 = D / 4;
-  const int sp = static_cast<int>(kStageFloats / D);  // rows per stage
-  const int units = static_cast<int>(sp * v4);
-  const int nst = (j1 - j0 + sp - 1) / sp;
-  const int tid = threadIdx.x;
-  float4 reg[kStageLoads];
-  auto load = [&](int st) {
-    const int32_t base = j0 + st * sp;
+__host__ __device__ __forceinline__ int64_t num_slices(int64_t D) { return (D + kSliceElems - 1) / kSliceElems; }
+
+template <typename F>
+__device__ __forceinline__ void slice_run(const float *__restrict__ src, const uint32_t *__restrict__ spos, int32_t j0,
+                                          int32_t j1, int64_t D, int64_t e, F f) {
+  const int64_t ec = e < D ? e : 0;
+  j0 = __builtin_amdgcn_readfirstlane(j0);
+  j1 = __builtin_amdgcn_readfirstlane(j1);
+  if (j0 >= j1) return;
+  // the indices of the next batch load while this batch's rows are in flight
+  uint32_t pn[kSlicePrefetch];
 #pragma unroll
-    for (int k = 0; k < kStageLoads; ++k) {
-      const int u = tid + 256 * k;
-      reg[k] = make_float4(0.f, 0.f, 0.f, 0.f);
-      if (u < units) {
-        const int p = static_cast<int>(u / v4);
-        const int32_t j = base + p;
-        if (j < j1) reg[k] = row_of(j)[u - p * v4];
-      }
-    }
-  };
-  auto store = [&](int buf) {
-    float4 *L = reinterpret_cast<float4 *>(lds + buf * kStageFloats);
+  for (int u = 0; u < kSlicePrefetch; ++u) pn[u] = spos[j0 + u < j1 ? j0 + u : j1 - 1];
+  for (int32_t j = j0; j < j1; j += kSlicePrefetch) {
+    float2 x[kSlicePrefetch];
 #pragma unroll
-    for (int k = 0; k < kStageLoads; ++k) {
-      const int u = tid + 256 * k;
-      if (u < units) L[u] = reg[k];
-    }
-  };
-  if (nst <= 0) return;
-  load(0);
-  store(0);
-  __syncthreads();
-  for (int st = 0; st < nst; ++st) {
-    if (st + 1 < nst) load(st + 1);
-    const float *L = lds + (st & 1) * kStageFloats;
-    const int32_t base = j0 + st * sp;
-    const int cnt = j1 - base < sp ? j1 - base : sp;
-    for (int p = 0; p < cnt; ++p) {
+    for (int u = 0; u < kSlicePrefetch; ++u)
+      x[u] = *reinterpret_cast<const float2 *>(src + static_cast<int64_t>(pn[u]) * D + ec);
+    const int32_t jn = j + kSlicePrefetch;
+    if (jn < j1) {
 #pragma unroll
-      for (int q = 0; q < EPT; ++q) {
-        const int64_t e = tid + 256 * q;
-        if (e < D) f(base + p, q, L[p * D + e]);
-      }
+      for (int u = 0; u < kSlicePrefetch; ++u) pn[u] = spos[jn + u < j1 ? jn + u : j1 - 1];
     }
-    if (st + 1 < nst) store((st + 1) & 1);
-    __syncthreads();
+#pragma unroll
+    for (int u = 0; u < kSlicePrefetch; ++u)
+      if (j + u < j1) f(j + u, x[u]);
+  }
+}
+
+// Same, over rows given by an index function (partial results).
+template <typename RowOf, typename F>
+__device__ __forceinline__ void slice_run_rows(RowOf row_of, int32_t j0, int32_t j1, int64_t D, int64_t e, F f) {
+  const int64_t ec = e < D ? e : 0;
+  j0 = __builtin_amdgcn_readfirstlane(j0);
+  j1 = __builtin_amdgcn_readfirstlane(j1);
+  for (int32_t j = j0; j < j1; j += kSlicePrefetch) {
+    float2 x[kSlicePrefetch];
+#pragma unroll
+    for (int u = 0; u < kSlicePrefetch; ++u)
+      x[u] = *reinterpret_cast<const float2 *>(row_of(j + u < j1 ? j + u : j1 - 1) + ec);
+#pragma unroll
+    for (int u = 0; u < kSlicePrefetch; ++u)
+      if (j + u < j1) f(j + u, x[u]);
+  }
+}
+
+// Light rows: one wave per row, lanes own 16-byte units (columns lane + 64 q).
+// rows_run() applies f(j, x) to positions j in [j0, j1) in order, loading P
+// positions at a time with every load issued before any is used and no
+// per-lane condition on a load (lanes past the row end read unit 0; their
+// results are dropped by the caller).  Short tails go 4 at a time.
+template <int P, int NC, typename F>
+__device__ __forceinline__ void rows_run(const float4 *__restrict__ src, const uint32_t *__restrict__ spos,
+                                         int32_t j0, int32_t j1, int64_t v4, int lane, F f) {
+  int64_t col[NC];
+#pragma unroll
+  for (int q = 0; q < NC; ++q) col[q] = lane + q * hlr::kWave < v4 ? lane + q * hlr::kWave : 0;
+  j0 = __builtin_amdgcn_readfirstlane(j0);
+  j1 = __builtin_amdgcn_readfirstlane(j1);
+  int32_t j = j0;
+  for (; j + P <= j1; j += P) {
+    int64_t p[P];
+#pragma unroll
+    for (int u = 0; u < P; ++u) p[u] = static_cast<int64_t>(spos[j + u]) * v4;
+    float4 x[P][NC];
+#pragma unroll
+    for (int u = 0; u < P; ++u)
+#pragma unroll
+      for (int q = 0; q < NC; ++q) x[u][q] = src[p[u] + col[q]];
+#pragma unroll
+    for (int u = 0; u < P; ++u) f(j + u, x[u]);
+  }
+  for (; j < j1; j += 4) {
+    int64_t p[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) p[u] = static_cast<int64_t>(spos[j + u < j1 ? j + u : j1 - 1]) * v4;
+    float4 x[4][NC];
+#pragma unroll
+    for (int u = 0; u < 4; ++u)
+#pragma unroll
+      for (int q = 0; q < NC; ++q) x[u][q] = src[p[u] + col[q]];
+#pragma unroll
+    for (int u = 0; u < 4; ++u)
+      if (j + u < j1) f(j + u, x[u]);
   }
 }
 
 // Registers a long segment (>= kHeavyMin occurrences, cut into runs of B) as
-// work for the block kernels: one entry (segment, run) per run, and the
+// work for the slice kernels: one entry (segment, run) per run, and the
 // segment in the combine list when it has more than one run.  Called by one
 // lane; counters[0] / counters[1] count the two lists (zeroed by rowkey_init).
 // Capacity: runs <= n/kHeavyMin + n/B <= n/32 for B >= 64.
@@ -458,7 +495,6 @@ __device__ __forceinline__ void push_heavy(int32_t k, int32_t len, int B, uint32
   if (nr > 1) clist[atomicAdd(&counters[1], 1u)] = k;
 }
 
-constexpr int kHeavyMin = 64;  // segments with at least this many occurrences go to the block kernels
-constexpr int kHeavyBlocks = 256;  // block kernels: one 128 KiB-LDS block per CU
+constexpr int kHeavyMin = 64;  // segments with at least this many occurrences go to the slice kernels
 
 }  // namespace

@@ -17,18 +17,17 @@
 // hashed tables of "DLRMv4: MLPerf recommendation training goes sequential").
 // Positions are grouped by row with a stable radix sort (radix.hpp).  Rows with
 // few occurrences are summed by one wave each (sgd_light), which also lists the
-// runs of longer rows.  Every run of 256 consecutive occurrences of a longer
-// row is summed in batch order by its own block, which streams the gradient
-// rows through LDS (sgd_heavy), so a Zipf-hot row (tens of thousands of
-// duplicates) spreads over the whole GPU; sgd_combine then adds each row's run
-// totals in batch order and writes fl(M - fl(lr * s)).
+// runs of longer rows.  Every (run of 256 consecutive occurrences, 128-element
+// slice) of a longer row is summed in batch order by its own wave (sgd_heavy),
+// so a Zipf-hot row (tens of thousands of duplicates) spreads over the whole
+// GPU; sgd_combine then adds each row's run totals in batch order and writes
+// fl(M - fl(lr * s)).
 #include "radix.hpp"
 
 namespace {
 using namespace hlr;
 
 constexpr int kThreads = 256;
-constexpr int kUnroll = 4;
 
 struct LWWork {
   int64_t *hkey;    // row held by the slot (-1 = free)
@@ -175,52 +174,21 @@ __global__ void __launch_bounds__(kThreads)
   }
 }
 
-// Duplicate-summed SGD helpers: a wave sums a run of a row's gradients in batch
-// order with the next U rows' loads in flight (lanes own 16-byte column units).
+// Duplicate-summed SGD: a wave sums a run of a row's gradients in batch order
+// (lanes own 16-byte column units), acc = g[spos[j0]], then acc += g[spos[j]].
 constexpr int kRun = HLR_SGD_SUM_RUN;
-constexpr int kPrefetch = 8;
 
 template <int NC>
-__device__ __forceinline__ void add4(float4 (&acc)[NC], const float4 (&x)[NC]) {
-#pragma unroll
-  for (int q = 0; q < NC; ++q)
-    acc[q] = make_float4(acc[q].x + x[q].x, acc[q].y + x[q].y, acc[q].z + x[q].z, acc[q].w + x[q].w);
-}
+constexpr int light_batch() { return NC == 1 ? 16 : (NC == 2 ? 8 : 4); }
 
-// acc = g[spos[j0]]; then acc += g[spos[j]] for j in (j0, j1), in order.
 template <int NC>
 __device__ __forceinline__ void sum_run(const float4 *__restrict__ g, const uint32_t *__restrict__ spos, int32_t j0,
                                         int32_t j1, int64_t v4, int lane, float4 (&acc)[NC]) {
+  rows_run<light_batch<NC>(), NC>(g, spos, j0, j1, v4, lane, [&](int32_t j, const float4(&x)[NC]) {
 #pragma unroll
-  for (int q = 0; q < NC; ++q) {
-    const int64_t c = lane + q * kWave;
-    acc[q] = c < v4 ? g[static_cast<int64_t>(spos[j0]) * v4 + c] : make_float4(0.f, 0.f, 0.f, 0.f);
-  }
-  int32_t j = j0 + 1;
-  for (; j + kPrefetch <= j1; j += kPrefetch) {
-    float4 x[kPrefetch][NC];
-#pragma unroll
-    for (int u = 0; u < kPrefetch; ++u) {
-      const int64_t p = spos[j + u];
-#pragma unroll
-      for (int q = 0; q < NC; ++q) {
-        const int64_t c = lane + q * kWave;
-        x[u][q] = c < v4 ? g[p * v4 + c] : make_float4(0.f, 0.f, 0.f, 0.f);
-      }
-    }
-#pragma unroll
-    for (int u = 0; u < kPrefetch; ++u) add4<NC>(acc, x[u]);
-  }
-  for (; j < j1; ++j) {
-    float4 x[NC];
-    const int64_t p = spos[j];
-#pragma unroll
-    for (int q = 0; q < NC; ++q) {
-      const int64_t c = lane + q * kWave;
-      x[q] = c < v4 ? g[p * v4 + c] : make_float4(0.f, 0.f, 0.f, 0.f);
-    }
-    add4<NC>(acc, x);
-  }
+    for (int q = 0; q < NC; ++q)
+      acc[q] = j == j0 ? x[q] : make_float4(acc[q].x + x[q].x, acc[q].y + x[q].y, acc[q].z + x[q].z, acc[q].w + x[q].w);
+  });
 }
 
 template <int NC>
@@ -260,70 +228,62 @@ __global__ void __launch_bounds__(kThreads)
   }
 }
 
-template <int EPT>
-__device__ __forceinline__ void sgd_write(float *table, int64_t r, const float (&acc)[EPT], float lr, int64_t D) {
-#pragma unroll
-  for (int q = 0; q < EPT; ++q) {
-    const int64_t e = threadIdx.x + 256 * q;
-    if (e < D) {
-      const float step = lr * acc[q];
-      table[r * D + e] = table[r * D + e] - step;  // fl(M - fl(lr * s))
-    }
+__device__ __forceinline__ void sgd_write2(float *table, int64_t r, float2 acc, float lr, int64_t D, int64_t e) {
+  if (e < D) {
+    float2 *w = reinterpret_cast<float2 *>(table + r * D + e);
+    const float2 m = *w;
+    const float s0 = lr * acc.x, s1 = lr * acc.y;
+    *w = make_float2(m.x - s0, m.y - s1);  // fl(M - fl(lr * s))
   }
 }
 
-// Heavy rows: one block per run of <= 256 occurrences, the gradient rows
-// streamed through LDS (block_stream).  A row with one run is updated at once;
-// otherwise the run total goes to `partial` for sgd_combine.
-template <int EPT>
+// Heavy rows: one wave per (run of <= 256 occurrences, 128-element slice).  A
+// row with one run is updated at once; otherwise the run total goes to
+// `partial` for sgd_combine.
 __global__ void __launch_bounds__(kThreads)
     sgd_heavy(float *table, const float *__restrict__ g, const uint32_t *__restrict__ skey,
               const uint32_t *__restrict__ spos, const int32_t *__restrict__ seg_start,
               const int32_t *__restrict__ seg_end, const uint32_t *__restrict__ counters,
               const int2 *__restrict__ hlist, float lr, int64_t D, float *partial) {
-  __shared__ float lds[2 * kStageFloats];
-  const uint32_t count = counters[0];
-  const int64_t v4 = D / 4;
-  const float4 *g4 = reinterpret_cast<const float4 *>(g);
-  for (uint32_t i = blockIdx.x; i < count; i += gridDim.x) {
-    const int2 km = hlist[i];
-    const int32_t s = seg_start[km.x], e = seg_end[km.x];
+  const int64_t S = num_slices(D);
+  const int64_t items = static_cast<int64_t>(counters[0]) * S;
+  const int64_t waves = static_cast<int64_t>(gridDim.x) * (kThreads / kWave);
+  for (int64_t it = (static_cast<int64_t>(blockIdx.x) * kThreads + threadIdx.x) / kWave; it < items; it += waves) {
+    const int2 km = hlist[it / S];
+    const int64_t e = (it % S) * kSliceElems + 2 * lane_id();
+    const int32_t s = seg_start[km.x], end = seg_end[km.x];
     const int32_t j0 = s + km.y * kRun;
-    const int32_t j1 = j0 + kRun < e ? j0 + kRun : e;
-    float acc[EPT];
-    block_stream<EPT>([&](int32_t j) { return g4 + static_cast<int64_t>(spos[j]) * v4; }, j0, j1, D, lds,
-                      [&](int32_t j, int q, float v) { acc[q] = j == j0 ? v : acc[q] + v; });
-    if (e - s <= kRun) {
-      sgd_write<EPT>(table, skey[s], acc, lr, D);
-      continue;
-    }
-    const int64_t slot = run_slot(j0, km.y, kRun);
-#pragma unroll
-    for (int q = 0; q < EPT; ++q) {
-      const int64_t el = threadIdx.x + 256 * q;
-      if (el < D) partial[slot * D + el] = acc[q];
+    const int32_t j1 = j0 + kRun < end ? j0 + kRun : end;
+    float2 acc = make_float2(0.f, 0.f);
+    slice_run(g, spos, j0, j1, D, e, [&](int32_t j, float2 x) {
+      acc = j == j0 ? x : make_float2(acc.x + x.x, acc.y + x.y);
+    });
+    if (end - s <= kRun) {
+      sgd_write2(table, skey[s], acc, lr, D, e);
+    } else if (e < D) {
+      *reinterpret_cast<float2 *>(partial + run_slot(j0, km.y, kRun) * D + e) = acc;
     }
   }
 }
 
-// Rows with several runs: the run totals are added in batch order (streamed
-// through LDS), then the row is updated once.
-template <int EPT>
+// Rows with several runs: one wave per (row, slice) adds the run totals in
+// batch order, then updates the row once.
 __global__ void __launch_bounds__(kThreads)
     sgd_combine(float *table, const uint32_t *__restrict__ skey, const int32_t *__restrict__ seg_start,
                 const int32_t *__restrict__ seg_end, const uint32_t *__restrict__ counters,
                 const int32_t *__restrict__ clist, float lr, int64_t D, const float *__restrict__ partial) {
-  __shared__ float lds[2 * kStageFloats];
-  const uint32_t count = counters[1];
-  for (uint32_t i = blockIdx.x; i < count; i += gridDim.x) {
-    const int32_t k = clist[i];
-    const int32_t s = seg_start[k], e = seg_end[k];
-    const int32_t nruns = (e - s + kRun - 1) / kRun;
-    float acc[EPT];
-    block_stream<EPT>(
-        [&](int32_t m) { return reinterpret_cast<const float4 *>(partial + run_slot(s + m * kRun, m, kRun) * D); }, 0,
-        nruns, D, lds, [&](int32_t m, int q, float v) { acc[q] = m == 0 ? v : acc[q] + v; });
-    sgd_write<EPT>(table, skey[s], acc, lr, D);
+  const int64_t S = num_slices(D);
+  const int64_t items = static_cast<int64_t>(counters[1]) * S;
+  const int64_t waves = static_cast<int64_t>(gridDim.x) * (kThreads / kWave);
+  for (int64_t it = (static_cast<int64_t>(blockIdx.x) * kThreads + threadIdx.x) / kWave; it < items; it += waves) {
+    const int32_t k = clist[it / S];
+    const int64_t e = (it % S) * kSliceElems + 2 * lane_id();
+    const int32_t s = seg_start[k], end = seg_end[k];
+    const int32_t nruns = (end - s + kRun - 1) / kRun;
+    float2 acc = make_float2(0.f, 0.f);
+    slice_run_rows([&](int32_t m) { return partial + run_slot(s + m * kRun, m, kRun) * D; }, 0, nruns, D, e,
+                   [&](int32_t m, float2 x) { acc = m == 0 ? x : make_float2(acc.x + x.x, acc.y + x.y); });
+    sgd_write2(table, skey[s], acc, lr, D, e);
   }
 }
 
@@ -331,7 +291,7 @@ inline size_t sgd_partial_elems(int64_t n, int64_t dim) {
   return static_cast<size_t>(2 * ((n + kRun - 1) / kRun) + 2) * static_cast<size_t>(dim / 4);
 }
 
-template <int NC, int EPT>
+template <int NC>
 void sgd_launch(float *table, const float *g, SegWork<uint32_t> &w, int cur, float lr, int64_t dim, float *partial,
                 hipStream_t s) {
   const int64_t v4 = dim / 4;
@@ -340,10 +300,13 @@ void sgd_launch(float *table, const float *g, SegWork<uint32_t> &w, int cur, flo
   sgd_light<NC><<<grid, kThreads, 0, s>>>(reinterpret_cast<float4 *>(table), reinterpret_cast<const float4 *>(g),
                                           w.k[cur], w.v[cur], w.seg_start, w.seg_end, w.nseg, lr, v4, w.ticket,
                                           w.hlist, w.clist);
-  sgd_heavy<EPT><<<kHeavyBlocks, kThreads, 0, s>>>(table, g, w.k[cur], w.v[cur], w.seg_start, w.seg_end, w.ticket,
-                                                    w.hlist, lr, dim, partial);
-  sgd_combine<EPT><<<kHeavyBlocks, kThreads, 0, s>>>(table, w.k[cur], w.seg_start, w.seg_end, w.ticket, w.clist, lr,
-                                                      dim, partial);
+  int gh = grid_for(w.n / 32 * num_slices(dim), 4);
+  if (gh > 2048) gh = 2048;
+  sgd_heavy<<<gh, kThreads, 0, s>>>(table, g, w.k[cur], w.v[cur], w.seg_start, w.seg_end, w.ticket, w.hlist, lr,
+                                    dim, partial);
+  int gc = grid_for(w.n / 256 * num_slices(dim), 4);
+  if (gc > 1024) gc = 1024;
+  sgd_combine<<<gc, kThreads, 0, s>>>(table, w.k[cur], w.seg_start, w.seg_end, w.ticket, w.clist, lr, dim, partial);
 }
 
 }  // namespace
@@ -402,8 +365,8 @@ extern "C" hlr_status writeback_rows(float *table, int64_t num_rows, int64_t dim
   c.off = segwork_layout<uint32_t>(n, &w, ws);
   float *partial = reinterpret_cast<float *>(c.take<float4>(sgd_partial_elems(n, dim)));
   const int cur = group_by_row(w, rows, nullptr, num_rows, stream);
-  if (nc == 1) sgd_launch<1, 1>(table, src, w, cur, lr, dim, partial, stream);
-  else if (nc == 2) sgd_launch<2, 2>(table, src, w, cur, lr, dim, partial, stream);
-  else sgd_launch<4, 4>(table, src, w, cur, lr, dim, partial, stream);
+  if (nc == 1) sgd_launch<1>(table, src, w, cur, lr, dim, partial, stream);
+  else if (nc == 2) sgd_launch<2>(table, src, w, cur, lr, dim, partial, stream);
+  else sgd_launch<4>(table, src, w, cur, lr, dim, partial, stream);
   return launch_status();
 }
