@@ -164,16 +164,18 @@ __global__ void __launch_bounds__(kThreads)
   }
 }
 
-// Chunking: a warm-up of W = ceil(24 / -ln a) steps shrinks a start error by
-// e^-24 (three orders below fp32 resolution), leaving the rest of the warm-up
-// for the two trajectories to round onto the same value.  A chunk's wave walks
-// W + L positions, so chunks are short (L = 256) to keep that chain short; the
-// redundant warm-up work is cheap next to the latency it removes.  Without
-// contraction (a outside (0, 1)) rows run whole.
+// Chunking: a warm-up of W = ceil(28 / -ln a) steps shrinks a start error by
+// e^-28, about 2^-40: far below fp32 resolution, with the remaining steps
+// spent while the two trajectories' roundings fall onto the same value (for
+// a = 0.95 and 0.99 about one 128-element slice in a thousand still differs
+// after W steps; a slice that differs is recomputed by ema_combine).  A chunk's
+// wave walks W + L positions, so chunks are short (L = 256) to keep that chain
+// short; the redundant warm-up work is cheap next to the latency it removes.
+// Without contraction (a outside (0, 1)) rows run whole.
 inline void ema_plan(float a, int64_t n, int *L, int *W) {
   constexpr int kChunk = 256;
   if (a > 0.f && a < 1.f) {
-    const double w = std::ceil(24.0 / -std::log(static_cast<double>(a)));
+    const double w = std::ceil(28.0 / -std::log(static_cast<double>(a)));
     *W = static_cast<int>(w < 1048576.0 ? w : 1048576.0);
     *L = kChunk;
   } else {

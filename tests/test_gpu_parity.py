@@ -321,7 +321,7 @@ def test_ema_long_row_many_chunks(dev):
 @pytest.mark.parametrize("spike_at", [900, 1990, 3000])
 def test_ema_speculation_fallback_is_exact(dev, spike_at):
     """Huge values just before a chunk's warm-up window make its speculative start wrong; the
-    chunk must be recomputed from the exact state (a = 0.5: warm-up 35, chunks of 256)."""
+    chunk must be recomputed from the exact state (a = 0.5: warm-up 41, chunks of 256)."""
     g = np.random.default_rng(spike_at)
     n, D = 4500, 8
     rows = np.zeros(n, np.int64)
