@@ -59,6 +59,11 @@ def load_library():
             "ema_update_rows": (i32, [p, i64, i64, p, p, p, i64, f32, f32, p, sz, p]),
             "gather_dequant_score": (i32, [p, p, p, i64, i64, p, i64, i64, p, p, p]),
             "hashed_rows": (i32, [p, i64, i64, p, p]),
+            "mpzch_zero_inserted": (i32, [p, i64, i64, p, p, i64, p]),
+            "writeback_plan": (i32, [i64, p, i64, i32, p, sz, p]),
+            "writeback_apply": (i32, [p, i64, i64, p, i64, i32, f32, p, sz, p]),
+            "ema_update_plan": (i32, [i64, p, p, i64, p, sz, p]),
+            "ema_update_apply": (i32, [p, i64, i64, p, i64, f32, f32, p, sz, p]),
         }
         for name, (res, args) in sig.items():
             f = getattr(lib, name)
@@ -72,7 +77,8 @@ def exported_symbols():
     return ["hlr_status_string", "hlr_version", "mpzch_lookup_or_insert_workspace_size", "mpzch_lookup_or_insert",
             "gather_rows", "dedup_ids_workspace_size", "dedup_ids", "writeback_rows_workspace_size",
             "writeback_rows", "ema_update_rows_workspace_size", "ema_update_rows", "gather_dequant_score",
-            "hashed_rows"]
+            "hashed_rows", "mpzch_zero_inserted", "writeback_plan", "writeback_apply", "ema_update_plan",
+            "ema_update_apply"]
 
 
 def _check(rc: int, what: str):
@@ -96,7 +102,15 @@ def _ptr(t):
     return None if t is None else ctypes.c_void_p(t.data_ptr())
 
 
-def _stream(device):
+_raw_stream = getattr(torch._C, "_cuda_getCurrentRawStream", None)
+
+
+def _stream(device, stream=None):
+    """HIP stream handle: `stream` (a torch stream or a raw handle) or the device's current stream."""
+    if stream is not None:
+        return ctypes.c_void_p(stream if isinstance(stream, int) else stream.cuda_stream)
+    if _raw_stream is not None:
+        return ctypes.c_void_p(_raw_stream(device.index if device.index is not None else torch.cuda.current_device()))
     return ctypes.c_void_p(torch.cuda.current_stream(device).cuda_stream)
 
 
@@ -122,10 +136,16 @@ def _ws_args(device, nbytes):
 
 
 # ----------------------------------------------------------------- entry points
+def mpzch_workspace_size(n, insert=True) -> int:
+    return int(load_library().mpzch_lookup_or_insert_workspace_size(int(n), 1 if insert else 0))
+
+
 def mpzch_lookup_or_insert(identity, stamps, values, probes, ids, now, insert=True, out_rows=None, out_hit=None,
-                           out_evicted=None, out_stats=None):
+                           out_evicted=None, out_stats=None, ws=None, stream=None):
     """MPZCH lookup (insert=False) or lookup-or-insert with LRU eviction.
 
+    ws: optional caller workspace (uint8 GPU tensor, new_workspace()); default: the
+    per-device shared buffer (calls that share it must be ordered on one stream).
     Returns (rows int64[n], hit int8[n], evicted int64[n] or None, stats int64[6] or None)."""
     lib = load_library()
     _dev(identity, "identity", torch.int64)
@@ -140,26 +160,29 @@ def mpzch_lookup_or_insert(identity, stamps, values, probes, ids, now, insert=Tr
     rows = out_rows if out_rows is not None else torch.empty(n, dtype=torch.int64, device=dev)
     hit = out_hit if out_hit is not None else torch.empty(n, dtype=torch.int8, device=dev)
     need = lib.mpzch_lookup_or_insert_workspace_size(n, 1 if insert else 0)
-    ws, wsb = _ws_args(dev, need)
+    if ws is not None and need > 0:
+        ws, wsb = _own_ws(ws, need)
+    else:
+        ws, wsb = _ws_args(dev, need)
     rc = lib.mpzch_lookup_or_insert(_ptr(identity), _ptr(stamps), _ptr(values), identity.numel(), int(probes), dim,
                                     _ptr(ids), n, int(now), 1 if insert else 0, _ptr(rows), _ptr(hit),
-                                    _ptr(out_evicted), _ptr(out_stats), ws, wsb, _stream(dev))
+                                    _ptr(out_evicted), _ptr(out_stats), ws, wsb, _stream(dev, stream))
     _check(rc, "mpzch_lookup_or_insert")
     return rows, hit, out_evicted, out_stats
 
 
-def gather_rows(table, rows, out=None):
+def gather_rows(table, rows, out=None, stream=None):
     lib = load_library()
     _dev(table, "table", torch.float32)
     _dev(rows, "rows", torch.int64)
     n, dim = rows.numel(), table.shape[1]
     out = out if out is not None else torch.empty((n, dim), dtype=torch.float32, device=table.device)
-    _check(lib.gather_rows(_ptr(table), table.shape[0], dim, _ptr(rows), n, _ptr(out), _stream(table.device)),
+    _check(lib.gather_rows(_ptr(table), table.shape[0], dim, _ptr(rows), n, _ptr(out), _stream(table.device, stream)),
            "gather_rows")
     return out
 
 
-def dedup_ids(keys, out_unique=None, out_last_pos=None, out_inverse=None, out_num_unique=None, inverse=True):
+def dedup_ids(keys, out_unique=None, out_last_pos=None, out_inverse=None, out_num_unique=None, inverse=True, stream=None):
     """Returns (unique[n], last_pos[n], inverse[n] or None, num_unique int64[1]); first u entries valid."""
     lib = load_library()
     _dev(keys, "keys", torch.int64)
@@ -170,12 +193,12 @@ def dedup_ids(keys, out_unique=None, out_last_pos=None, out_inverse=None, out_nu
                                                        if inverse else None)
     nu = out_num_unique if out_num_unique is not None else torch.empty(1, dtype=torch.int64, device=dev)
     ws, wsb = _ws_args(dev, lib.dedup_ids_workspace_size(n))
-    _check(lib.dedup_ids(_ptr(keys), n, _ptr(uq), _ptr(lp), _ptr(inv), _ptr(nu), ws, wsb, _stream(dev)),
+    _check(lib.dedup_ids(_ptr(keys), n, _ptr(uq), _ptr(lp), _ptr(inv), _ptr(nu), ws, wsb, _stream(dev, stream)),
            "dedup_ids")
     return uq, lp, inv, nu
 
 
-def writeback_rows(table, rows, src, mode=WB_LAST_WINS, lr=1.0):
+def writeback_rows(table, rows, src, mode=WB_LAST_WINS, lr=1.0, stream=None):
     lib = load_library()
     _dev(table, "table", torch.float32)
     _dev(rows, "rows", torch.int64)
@@ -185,11 +208,11 @@ def writeback_rows(table, rows, src, mode=WB_LAST_WINS, lr=1.0):
         raise HLRError("src must be [n, dim]")
     ws, wsb = _ws_args(table.device, lib.writeback_rows_workspace_size(table.shape[0], dim, n, int(mode)))
     _check(lib.writeback_rows(_ptr(table), table.shape[0], dim, _ptr(rows), _ptr(src), n, int(mode), float(lr), ws,
-                              wsb, _stream(table.device)), "writeback_rows")
+                              wsb, _stream(table.device, stream)), "writeback_rows")
     return table
 
 
-def ema_update_rows(table, rows, vals, mask, a, b):
+def ema_update_rows(table, rows, vals, mask, a, b, stream=None):
     lib = load_library()
     _dev(table, "table", torch.float32)
     _dev(rows, "rows", torch.int64)
@@ -201,11 +224,11 @@ def ema_update_rows(table, rows, vals, mask, a, b):
         raise HLRError("vals must be [n, dim]")
     ws, wsb = _ws_args(table.device, lib.ema_update_rows_workspace_size(table.shape[0], dim, n))
     _check(lib.ema_update_rows(_ptr(table), table.shape[0], dim, _ptr(rows), _ptr(vals), _ptr(mask), n, float(a),
-                               float(b), ws, wsb, _stream(table.device)), "ema_update_rows")
+                               float(b), ws, wsb, _stream(table.device, stream)), "ema_update_rows")
     return table
 
 
-def gather_dequant_score(qtable, scale, bias, rows, user, cands, out=None):
+def gather_dequant_score(qtable, scale, bias, rows, user, cands, out=None, stream=None):
     lib = load_library()
     _dev(qtable, "qtable", torch.int8)
     _dev(scale, "scale", torch.float32)
@@ -215,14 +238,92 @@ def gather_dequant_score(qtable, scale, bias, rows, user, cands, out=None):
     nreq, dim = user.shape[0], qtable.shape[1]
     out = out if out is not None else torch.empty((nreq, cands), dtype=torch.float32, device=qtable.device)
     _check(lib.gather_dequant_score(_ptr(qtable), _ptr(scale), _ptr(bias), qtable.shape[0], dim, _ptr(rows), nreq,
-                                    int(cands), _ptr(user), _ptr(out), _stream(qtable.device)),
+                                    int(cands), _ptr(user), _ptr(out), _stream(qtable.device, stream)),
            "gather_dequant_score")
     return out
 
 
-def hashed_rows(ids, num_rows, out=None):
+def hashed_rows(ids, num_rows, out=None, stream=None):
     lib = load_library()
     _dev(ids, "ids", torch.int64)
     out = out if out is not None else torch.empty(ids.numel(), dtype=torch.int64, device=ids.device)
-    _check(lib.hashed_rows(_ptr(ids), ids.numel(), int(num_rows), _ptr(out), _stream(ids.device)), "hashed_rows")
+    _check(lib.hashed_rows(_ptr(ids), ids.numel(), int(num_rows), _ptr(out), _stream(ids.device, stream)), "hashed_rows")
     return out
+
+
+# ------------------------------------------------- split (plan / apply) forms
+def new_workspace(device, nbytes: int) -> torch.Tensor:
+    """A caller-owned scratch buffer for the plan/apply entry points (one per plan in flight)."""
+    return torch.empty(max(int(nbytes), 1) + 256, dtype=torch.uint8, device=device)
+
+
+def _own_ws(ws: torch.Tensor, need: int):
+    _dev(ws, "ws", torch.uint8)
+    base = ws.data_ptr()
+    aligned = (base + 255) // 256 * 256
+    avail = ws.numel() - (aligned - base)
+    if avail < need:
+        raise HLRError(f"workspace too small: {avail} bytes, need {need}")
+    return ctypes.c_void_p(aligned), avail
+
+
+def writeback_workspace_size(num_rows, dim, n, mode=WB_LAST_WINS) -> int:
+    return int(load_library().writeback_rows_workspace_size(int(num_rows), int(dim), int(n), int(mode)))
+
+
+def ema_workspace_size(num_rows, dim, n) -> int:
+    return int(load_library().ema_update_rows_workspace_size(int(num_rows), int(dim), int(n)))
+
+
+def mpzch_zero_inserted(values, rows, hit, stream=None):
+    """Zero the rows a lookup (run with values=None) inserted: rows[i] for hit[i] == 0."""
+    lib = load_library()
+    _dev(values, "values", torch.float32)
+    _dev(rows, "rows", torch.int64)
+    _dev(hit, "hit", torch.int8)
+    _check(lib.mpzch_zero_inserted(_ptr(values), values.shape[0], values.shape[1], _ptr(rows), _ptr(hit),
+                                   rows.numel(), _stream(values.device, stream)), "mpzch_zero_inserted")
+
+
+def writeback_plan(num_rows, rows, ws, mode=WB_LAST_WINS, stream=None):
+    lib = load_library()
+    _dev(rows, "rows", torch.int64)
+    n = rows.numel()
+    w, wb = _own_ws(ws, lib.writeback_rows_workspace_size(int(num_rows), 4, n, int(mode)))
+    _check(lib.writeback_plan(int(num_rows), _ptr(rows), n, int(mode), w, wb, _stream(rows.device, stream)),
+           "writeback_plan")
+
+
+def writeback_apply(table, src, ws, mode=WB_LAST_WINS, lr=1.0, stream=None):
+    lib = load_library()
+    _dev(table, "table", torch.float32)
+    _dev(src, "src", torch.float32)
+    dim = table.shape[1]
+    n = src.numel() // dim
+    w, wb = _own_ws(ws, lib.writeback_rows_workspace_size(table.shape[0], dim, n, int(mode)))
+    _check(lib.writeback_apply(_ptr(table), table.shape[0], dim, _ptr(src), n, int(mode), float(lr), w, wb,
+                               _stream(table.device, stream)), "writeback_apply")
+    return table
+
+
+def ema_update_plan(num_rows, rows, mask, ws, stream=None):
+    lib = load_library()
+    _dev(rows, "rows", torch.int64)
+    if mask is not None:
+        _dev(mask, "mask", torch.uint8)
+    n = rows.numel()
+    w, wb = _own_ws(ws, lib.ema_update_rows_workspace_size(int(num_rows), 4, n))
+    _check(lib.ema_update_plan(int(num_rows), _ptr(rows), _ptr(mask), n, w, wb, _stream(rows.device, stream)),
+           "ema_update_plan")
+
+
+def ema_update_apply(table, vals, a, b, ws, stream=None):
+    lib = load_library()
+    _dev(table, "table", torch.float32)
+    _dev(vals, "vals", torch.float32)
+    dim = table.shape[1]
+    n = vals.numel() // dim
+    w, wb = _own_ws(ws, lib.ema_update_rows_workspace_size(table.shape[0], dim, n))
+    _check(lib.ema_update_apply(_ptr(table), table.shape[0], dim, _ptr(vals), n, float(a), float(b), w, wb,
+                                _stream(table.device, stream)), "ema_update_apply")
+    return table

@@ -1,0 +1,57 @@
+"""Raw HIP events and stream waits (ctypes over libamdhip64), for ordering work between streams.
+
+Events are created without timing and without the system-scope fence: they order work between
+streams of one GPU, for which the device-scope release and acquire of the packets suffice, and a
+system-scope fence would write back the L2 caches at every record.  Timing events keep timing on.
+"""
+from __future__ import annotations
+
+import ctypes
+
+_DISABLE_TIMING = 0x2
+_DISABLE_SYSTEM_FENCE = 0x20000000
+
+
+class _Hip:
+    def __init__(self):
+        self.lib = ctypes.CDLL("libamdhip64.so")
+        self.lib.hipEventCreateWithFlags.argtypes = [ctypes.POINTER(ctypes.c_void_p), ctypes.c_uint]
+        self.lib.hipEventRecord.argtypes = [ctypes.c_void_p, ctypes.c_void_p]
+        self.lib.hipStreamWaitEvent.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_uint]
+        self.lib.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p, ctypes.c_void_p]
+        self.lib.hipEventDestroy.argtypes = [ctypes.c_void_p]
+
+    def event(self, timing: bool = False) -> ctypes.c_void_p:
+        e = ctypes.c_void_p()
+        flags = _DISABLE_SYSTEM_FENCE | (0 if timing else _DISABLE_TIMING)
+        rc = self.lib.hipEventCreateWithFlags(ctypes.byref(e), flags)
+        if rc != 0:
+            raise RuntimeError(f"hipEventCreateWithFlags failed ({rc})")
+        return e
+
+    def record(self, e, stream: int):
+        rc = self.lib.hipEventRecord(e, ctypes.c_void_p(stream))
+        if rc != 0:
+            raise RuntimeError(f"hipEventRecord failed ({rc})")
+
+    def wait(self, stream: int, e):
+        rc = self.lib.hipStreamWaitEvent(ctypes.c_void_p(stream), e, 0)
+        if rc != 0:
+            raise RuntimeError(f"hipStreamWaitEvent failed ({rc})")
+
+    def elapsed_s(self, a, b) -> float:
+        ms = ctypes.c_float()
+        rc = self.lib.hipEventElapsedTime(ctypes.byref(ms), a, b)
+        if rc != 0:
+            raise RuntimeError(f"hipEventElapsedTime failed ({rc})")
+        return ms.value * 1e-3
+
+
+_hip = None
+
+
+def hip() -> _Hip:
+    global _hip
+    if _hip is None:
+        _hip = _Hip()
+    return _hip

@@ -223,25 +223,74 @@ extern "C" size_t ema_update_rows_workspace_size(int64_t num_rows, int64_t dim, 
   return c.off;
 }
 
-extern "C" hlr_status ema_update_rows(float *table, int64_t num_rows, int64_t dim, const int64_t *rows,
-                                      const float *vals, const uint8_t *mask, int64_t n, float a, float b, void *ws,
-                                      size_t ws_bytes, hipStream_t stream) {
+namespace {
+
+hlr_status ema_args(int64_t num_rows, int64_t n) {
   if (n < 0 || n > kMaxN || num_rows < 0 || num_rows >= 0x7fffffff) return HLR_INVALID_ARG;
-  if (dim <= 0 || dim % 4 != 0 || dim > 1024) return HLR_UNSUPPORTED_DIM;
-  if (n == 0 || num_rows == 0) return HLR_OK;
-  if (!table || !rows || !vals) return HLR_INVALID_ARG;
-  if (!aligned(table, 16) || !aligned(vals, 16) || !aligned(rows, 8)) return HLR_MISALIGNED;
-  const size_t need = ema_update_rows_workspace_size(num_rows, dim, n);
+  return HLR_OK;
+}
+
+hlr_status ema_ws(void *ws, size_t ws_bytes, size_t need) {
   if (!ws || ws_bytes < need) return HLR_WORKSPACE_TOO_SMALL;
   if (!aligned(ws, 256)) return HLR_MISALIGNED;
+  return HLR_OK;
+}
+
+void ema_apply(float *table, int64_t num_rows, int64_t dim, const float *vals, int64_t n, float a, float b, void *ws,
+               hipStream_t stream) {
   SegWork<uint32_t> w;
   Carver c(ws);
   c.off = segwork_layout<uint32_t>(n, &w, ws);
   float *partial = reinterpret_cast<float *>(c.take<float4>(ema_partial_elems(n, dim)));
-  const int cur = group_by_row(w, rows, mask, num_rows, stream);
+  const int cur = sorted_buffer(num_rows);
   const int64_t nc = (dim / 4 + kWave - 1) / kWave;
   if (nc == 1) ema_launch<1>(table, vals, w, cur, a, b, dim, partial, stream);
   else if (nc == 2) ema_launch<2>(table, vals, w, cur, a, b, dim, partial, stream);
   else ema_launch<4>(table, vals, w, cur, a, b, dim, partial, stream);
+}
+
+}  // namespace
+
+extern "C" hlr_status ema_update_rows(float *table, int64_t num_rows, int64_t dim, const int64_t *rows,
+                                      const float *vals, const uint8_t *mask, int64_t n, float a, float b, void *ws,
+                                      size_t ws_bytes, hipStream_t stream) {
+  hlr_status st = ema_args(num_rows, n);
+  if (st != HLR_OK) return st;
+  if (dim <= 0 || dim % 4 != 0 || dim > 1024) return HLR_UNSUPPORTED_DIM;
+  if (n == 0 || num_rows == 0) return HLR_OK;
+  if (!table || !rows || !vals) return HLR_INVALID_ARG;
+  if (!aligned(table, 16) || !aligned(vals, 16) || !aligned(rows, 8)) return HLR_MISALIGNED;
+  if ((st = ema_ws(ws, ws_bytes, ema_update_rows_workspace_size(num_rows, dim, n))) != HLR_OK) return st;
+  SegWork<uint32_t> w;
+  segwork_layout<uint32_t>(n, &w, ws);
+  group_by_row(w, rows, mask, num_rows, stream);
+  ema_apply(table, num_rows, dim, vals, n, a, b, ws, stream);
+  return launch_status();
+}
+
+extern "C" hlr_status ema_update_plan(int64_t num_rows, const int64_t *rows, const uint8_t *mask, int64_t n,
+                                      void *ws, size_t ws_bytes, hipStream_t stream) {
+  hlr_status st = ema_args(num_rows, n);
+  if (st != HLR_OK) return st;
+  if (n == 0 || num_rows == 0) return HLR_OK;
+  if (!rows) return HLR_INVALID_ARG;
+  if (!aligned(rows, 8)) return HLR_MISALIGNED;
+  if ((st = ema_ws(ws, ws_bytes, ema_update_rows_workspace_size(num_rows, 4, n))) != HLR_OK) return st;
+  SegWork<uint32_t> w;
+  segwork_layout<uint32_t>(n, &w, ws);
+  group_by_row(w, rows, mask, num_rows, stream);
+  return launch_status();
+}
+
+extern "C" hlr_status ema_update_apply(float *table, int64_t num_rows, int64_t dim, const float *vals, int64_t n,
+                                       float a, float b, void *ws, size_t ws_bytes, hipStream_t stream) {
+  hlr_status st = ema_args(num_rows, n);
+  if (st != HLR_OK) return st;
+  if (dim <= 0 || dim % 4 != 0 || dim > 1024) return HLR_UNSUPPORTED_DIM;
+  if (n == 0 || num_rows == 0) return HLR_OK;
+  if (!table || !vals) return HLR_INVALID_ARG;
+  if (!aligned(table, 16) || !aligned(vals, 16)) return HLR_MISALIGNED;
+  if ((st = ema_ws(ws, ws_bytes, ema_update_rows_workspace_size(num_rows, dim, n))) != HLR_OK) return st;
+  ema_apply(table, num_rows, dim, vals, n, a, b, ws, stream);
   return launch_status();
 }

@@ -366,6 +366,29 @@ __global__ void __launch_bounds__(kThreads)
   }
 }
 
+// Zero-fill of the rows a batch inserted (positions with hit 0 and a row),
+// for callers that run the lookup without `values` on another stream and
+// clear the new rows on the stream that reads and writes them.  One wave per
+// 64 positions; the whole wave clears each selected row with 16-byte stores.
+__global__ void __launch_bounds__(kThreads)
+    mz_zero_inserted(float4 *values, int64_t num_rows, int64_t v4, const int64_t *__restrict__ rows,
+                     const int8_t *__restrict__ hit, int64_t n) {
+  const int64_t i = static_cast<int64_t>(blockIdx.x) * kThreads + threadIdx.x;
+  int64_t r = -1;
+  if (i < n && hit[i] == 0) {
+    r = rows[i];
+    if (r >= num_rows) r = -1;
+  }
+  uint64_t m = ballot(r >= 0);
+  const float4 z = make_float4(0.f, 0.f, 0.f, 0.f);
+  while (m) {
+    const int l = __builtin_ctzll(m);
+    m &= m - 1;
+    float4 *dst = values + readlane_i64(r, l) * v4;
+    for (int64_t c = lane_id(); c < v4; c += kWave) dst[c] = z;
+  }
+}
+
 template <int P>
 void mz_launch(int64_t *identity, int64_t *stamps, float *values, int64_t capacity, int probes, int64_t dim,
                const int64_t *ids, int64_t n, int64_t now, int insert, int64_t *rows, int8_t *hit,
@@ -432,5 +455,17 @@ extern "C" hlr_status mpzch_lookup_or_insert(int64_t *identity, int64_t *stamps,
   else
     mz_launch<0>(identity, stamps, values, capacity, probes, dim, ids, n, now, insert, out_rows, out_hit,
                  out_evicted, stats, w, stream);
+  return launch_status();
+}
+
+extern "C" hlr_status mpzch_zero_inserted(float *values, int64_t capacity, int64_t dim, const int64_t *rows,
+                                          const int8_t *hit, int64_t n, hipStream_t stream) {
+  if (n < 0 || n > kMaxN || capacity <= 0) return HLR_INVALID_ARG;
+  if (dim <= 0 || dim % 4 != 0) return HLR_UNSUPPORTED_DIM;
+  if (n == 0) return HLR_OK;
+  if (!values || !rows || !hit) return HLR_INVALID_ARG;
+  if (!aligned(values, 16) || !aligned(rows, 8)) return HLR_MISALIGNED;
+  mz_zero_inserted<<<grid_for(n, kThreads), kThreads, 0, stream>>>(reinterpret_cast<float4 *>(values), capacity,
+                                                                   dim / 4, rows, hit, n);
   return launch_status();
 }

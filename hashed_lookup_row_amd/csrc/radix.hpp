@@ -358,6 +358,11 @@ __global__ void __launch_bounds__(256)
 // Groups positions by row: returns the buffer index holding (row, position)
 // sorted by row, positions ascending within a row, with the segment table
 // (seg_start, seg_end, nseg) built.
+// Index (0/1) of the buffer that holds the sorted result for a table of num_rows rows.
+inline int sorted_buffer(int64_t num_rows) {
+  return make_plan(bit_width_u64(static_cast<uint64_t>(num_rows))).passes & 1;
+}
+
 inline int group_by_row(SegWork<uint32_t> &w, const int64_t *rows, const uint8_t *mask, int64_t num_rows,
                         hipStream_t s) {
   rowkey_init<<<hlr::grid_for(w.n, 256), 256, 0, s>>>(rows, mask, w.n, num_rows, w.k[0], w.v[0], w.ticket);

@@ -326,22 +326,23 @@ extern "C" size_t writeback_rows_workspace_size(int64_t num_rows, int64_t dim, i
   return c.off;
 }
 
-extern "C" hlr_status writeback_rows(float *table, int64_t num_rows, int64_t dim, const int64_t *rows,
-                                     const float *src, int64_t n, int32_t mode, float lr, void *ws, size_t ws_bytes,
-                                     hipStream_t stream) {
+namespace {
+
+hlr_status wb_args(int64_t num_rows, int64_t n, int32_t mode) {
   if (n < 0 || n > kMaxN || num_rows < 0 || num_rows >= 0x7fffffff) return HLR_INVALID_ARG;
   if (mode != HLR_WB_LAST_WINS && mode != HLR_WB_SGD_SUM) return HLR_INVALID_ARG;
-  if (mode == HLR_WB_LAST_WINS && lr != 1.0f) return HLR_INVALID_ARG;
-  if (dim <= 0 || dim % 4 != 0) return HLR_UNSUPPORTED_DIM;
-  if (n == 0 || num_rows == 0) return HLR_OK;
-  if (!table || !rows || !src) return HLR_INVALID_ARG;
-  if (!aligned(table, 16) || !aligned(src, 16) || !aligned(rows, 8)) return HLR_MISALIGNED;
-  const size_t need = writeback_rows_workspace_size(num_rows, dim, n, mode);
+  return HLR_OK;
+}
+
+hlr_status ws_check(void *ws, size_t ws_bytes, size_t need) {
   if (!ws || ws_bytes < need) return HLR_WORKSPACE_TOO_SMALL;
   if (!aligned(ws, 256)) return HLR_MISALIGNED;
-  const int64_t v4 = dim / 4;
-  float4 *t4 = reinterpret_cast<float4 *>(table);
-  const float4 *s4 = reinterpret_cast<const float4 *>(src);
+  return HLR_OK;
+}
+
+// Plan: depends on rows only.  LAST_WINS: the row -> last position table and
+// its compact list; SGD_SUM: positions grouped by row (sort + segments).
+void wb_plan(int64_t num_rows, const int64_t *rows, int64_t n, int32_t mode, void *ws, hipStream_t stream) {
   if (mode == HLR_WB_LAST_WINS) {
     LWWork w;
     lw_layout(n, &w, ws);
@@ -349,24 +350,80 @@ extern "C" hlr_status writeback_rows(float *table, int64_t num_rows, int64_t dim
     if (gi > 4096) gi = 4096;
     lw_init<<<gi, kThreads, 0, stream>>>(w);
     lw_last<<<grid_for(n, kLwTile), kThreads, 0, stream>>>(rows, n, num_rows, w);
+    return;
+  }
+  SegWork<uint32_t> w;
+  segwork_layout<uint32_t>(n, &w, ws);
+  group_by_row(w, rows, nullptr, num_rows, stream);
+}
+
+// Apply: reads the plan left in the workspace by wb_plan.
+void wb_apply(float *table, int64_t num_rows, int64_t dim, const float *src, int64_t n, int32_t mode, float lr,
+              void *ws, hipStream_t stream) {
+  const int64_t v4 = dim / 4;
+  const int64_t nc = (v4 + kWave - 1) / kWave;
+  if (mode == HLR_WB_LAST_WINS) {
+    LWWork w;
+    lw_layout(n, &w, ws);
     int ga = grid_for(n, 8);
     if (ga > 2048) ga = 2048;
-    const int64_t nc = (v4 + kWave - 1) / kWave;
+    float4 *t4 = reinterpret_cast<float4 *>(table);
+    const float4 *s4 = reinterpret_cast<const float4 *>(src);
     if (nc == 1) lw_apply<1><<<ga, kThreads, 0, stream>>>(t4, s4, w, v4);
     else if (nc == 2) lw_apply<2><<<ga, kThreads, 0, stream>>>(t4, s4, w, v4);
-    else if (nc <= 4) lw_apply<4><<<ga, kThreads, 0, stream>>>(t4, s4, w, v4);
-    else return HLR_UNSUPPORTED_DIM;
-    return launch_status();
+    else lw_apply<4><<<ga, kThreads, 0, stream>>>(t4, s4, w, v4);
+    return;
   }
-  const int64_t nc = (v4 + kWave - 1) / kWave;
-  if (nc > 4) return HLR_UNSUPPORTED_DIM;  // dim > 1024
   SegWork<uint32_t> w;
   Carver c(ws);
   c.off = segwork_layout<uint32_t>(n, &w, ws);
   float *partial = reinterpret_cast<float *>(c.take<float4>(sgd_partial_elems(n, dim)));
-  const int cur = group_by_row(w, rows, nullptr, num_rows, stream);
+  const int cur = sorted_buffer(num_rows);
   if (nc == 1) sgd_launch<1>(table, src, w, cur, lr, dim, partial, stream);
   else if (nc == 2) sgd_launch<2>(table, src, w, cur, lr, dim, partial, stream);
   else sgd_launch<4>(table, src, w, cur, lr, dim, partial, stream);
+}
+
+}  // namespace
+
+extern "C" hlr_status writeback_rows(float *table, int64_t num_rows, int64_t dim, const int64_t *rows,
+                                     const float *src, int64_t n, int32_t mode, float lr, void *ws, size_t ws_bytes,
+                                     hipStream_t stream) {
+  hlr_status st = wb_args(num_rows, n, mode);
+  if (st != HLR_OK) return st;
+  if (mode == HLR_WB_LAST_WINS && lr != 1.0f) return HLR_INVALID_ARG;
+  if (dim <= 0 || dim % 4 != 0 || dim > 1024) return HLR_UNSUPPORTED_DIM;
+  if (n == 0 || num_rows == 0) return HLR_OK;
+  if (!table || !rows || !src) return HLR_INVALID_ARG;
+  if (!aligned(table, 16) || !aligned(src, 16) || !aligned(rows, 8)) return HLR_MISALIGNED;
+  if ((st = ws_check(ws, ws_bytes, writeback_rows_workspace_size(num_rows, dim, n, mode))) != HLR_OK) return st;
+  wb_plan(num_rows, rows, n, mode, ws, stream);
+  wb_apply(table, num_rows, dim, src, n, mode, lr, ws, stream);
+  return launch_status();
+}
+
+extern "C" hlr_status writeback_plan(int64_t num_rows, const int64_t *rows, int64_t n, int32_t mode, void *ws,
+                                     size_t ws_bytes, hipStream_t stream) {
+  hlr_status st = wb_args(num_rows, n, mode);
+  if (st != HLR_OK) return st;
+  if (n == 0 || num_rows == 0) return HLR_OK;
+  if (!rows) return HLR_INVALID_ARG;
+  if (!aligned(rows, 8)) return HLR_MISALIGNED;
+  if ((st = ws_check(ws, ws_bytes, writeback_rows_workspace_size(num_rows, 4, n, mode))) != HLR_OK) return st;
+  wb_plan(num_rows, rows, n, mode, ws, stream);
+  return launch_status();
+}
+
+extern "C" hlr_status writeback_apply(float *table, int64_t num_rows, int64_t dim, const float *src, int64_t n,
+                                      int32_t mode, float lr, void *ws, size_t ws_bytes, hipStream_t stream) {
+  hlr_status st = wb_args(num_rows, n, mode);
+  if (st != HLR_OK) return st;
+  if (mode == HLR_WB_LAST_WINS && lr != 1.0f) return HLR_INVALID_ARG;
+  if (dim <= 0 || dim % 4 != 0 || dim > 1024) return HLR_UNSUPPORTED_DIM;
+  if (n == 0 || num_rows == 0) return HLR_OK;
+  if (!table || !src) return HLR_INVALID_ARG;
+  if (!aligned(table, 16) || !aligned(src, 16)) return HLR_MISALIGNED;
+  if ((st = ws_check(ws, ws_bytes, writeback_rows_workspace_size(num_rows, dim, n, mode))) != HLR_OK) return st;
+  wb_apply(table, num_rows, dim, src, n, mode, lr, ws, stream);
   return launch_status();
 }

@@ -1,0 +1,232 @@
+"""Two-stream schedules of the cache's per-batch work.
+
+The work of a batch splits into a part that needs only IDs and rows (MPZCH
+lookup/insert, hashed-row mapping, the grouping half of Writeback / SGD-sum /
+EMA) and a part that moves row data (zero-filling new rows, gather, applying
+updates).  The first part is latency-bound and light on HBM, the second is
+HBM-bound, so they overlap well: the ID-side work of batch t runs on a lookup
+stream while the row traffic of batch t-1 runs on the compute stream, the
+overlap of the dispatch (embedding lookup) and compute streams in "MTGR:
+Industrial-Scale Generative Recommendation Framework in Meituan", sec. 3.5.
+
+Only kernels of libhlr.so run; this module enqueues them on two torch streams
+and orders them with events.  Every schedule gives the same results as the
+same calls made one after another on one stream (the tests check this against
+the oracle).
+
+Ordering, per batch t (ring of `depth` buffer sets, k = t mod depth):
+  lookup stream:  wait compute(t - depth) done  ->  ID-side calls of t into set k, an event after each
+  compute stream: wait for the event each row-side call needs  ->  row-side calls of t  ->  record done(t)
+A lookup without `values` leaves the rows it inserts untouched; the compute
+stream zero-fills them (mpzch_zero_inserted) after batch t-1's Writeback has
+written them and before batch t gathers them, which is the order a single
+stream would give.
+
+The compute stream is the caller's current stream when the pipeline is built.
+Inputs handed to step() (IDs, keys, rows, masks) must already be written when
+step() is called (for example uploaded and synchronised ahead of time): the
+lookup stream does not wait for the compute stream.
+"""
+from __future__ import annotations
+
+import torch
+
+from ._hip import hip
+from . import (WB_LAST_WINS, WB_SGD_SUM, ema_update_apply, ema_update_plan, ema_workspace_size, gather_rows,
+               hashed_rows, mpzch_lookup_or_insert, mpzch_workspace_size, mpzch_zero_inserted, new_workspace,
+               writeback_apply, writeback_plan, writeback_workspace_size)
+
+
+class _Ring:
+    """Ring of `depth` buffer sets shared by a lookup stream and the compute stream.
+
+    Events marks[k][j] are recorded on the lookup stream at the j-th point the compute
+    stream has to wait for; done[k] is recorded on the compute stream when set k is free.
+    Raw HIP events and stream handles keep the host cost of a step low."""
+
+    def __init__(self, device, depth, points=1, lookup=None):
+        self.device = torch.device(device)
+        self.depth = depth
+        self.lookup = lookup if lookup is not None else torch.cuda.Stream(self.device)  # default priority
+        self.compute = torch.cuda.current_stream(self.device)
+        self.ls, self.cs = self.lookup.cuda_stream, self.compute.cuda_stream
+        self.hip = hip()
+        self.marks = [[self.hip.event() for _ in range(points)] for _ in range(depth)]
+        self.done = [self.hip.event() for _ in range(depth)]
+        self.fork = self.hip.event()
+        self.t = 0
+
+    def restart(self):
+        """Orders the lookup stream after everything enqueued on the compute stream so far and
+        starts a fresh ring (no waits on earlier ring events).  Needed to begin a graph capture
+        on the compute stream: the lookup stream then joins the capture from this point."""
+        self.hip.record(self.fork, self.cs)
+        self.hip.wait(self.ls, self.fork)
+        self.t = 0
+
+    def begin_lookup(self):
+        k = self.t % self.depth
+        if self.t >= self.depth:
+            self.hip.wait(self.ls, self.done[k])
+        return k
+
+    def mark(self, k, j):
+        self.hip.record(self.marks[k][j], self.ls)
+
+    def wait(self, k, j):
+        self.hip.wait(self.cs, self.marks[k][j])
+
+    def end_compute(self, k):
+        self.hip.record(self.done[k], self.cs)
+        self.t += 1
+
+
+def _on(stream, *tensors):
+    """Tells torch's allocator that `stream` uses these caller tensors."""
+    for x in tensors:
+        if x is not None:
+            x.record_stream(stream)
+
+
+class MemoryLayerPipeline:
+    """MPZCH lookup/insert + gather + Writeback (last occurrence wins, lr = 1) per batch.
+
+    lookup stream:  mpzch_lookup_or_insert(values=None) -> writeback_plan(LAST_WINS)
+    compute stream: mpzch_zero_inserted -> gather_rows -> writeback_apply(LAST_WINS)
+    step() returns the gathered rows (on the compute stream) and leaves rows/hit of
+    the batch in ring slot k (`rows(k)`, `hit(k)`)."""
+
+    def __init__(self, identity, stamps, values, probes, n, depth=2):
+        self.identity, self.stamps, self.values, self.probes, self.n = identity, stamps, values, probes, n
+        dev = values.device
+        self.ring = _Ring(dev, depth, points=2)
+        C, D = values.shape
+        wsb = writeback_workspace_size(C, D, n, WB_LAST_WINS)
+        self._rows = [torch.empty(n, dtype=torch.int64, device=dev) for _ in range(depth)]
+        self._hit = [torch.empty(n, dtype=torch.int8, device=dev) for _ in range(depth)]
+        self._ws = [new_workspace(dev, wsb) for _ in range(depth)]
+        self._mz_ws = new_workspace(dev, mpzch_workspace_size(n))
+
+    def restart(self):
+        self.ring.restart()
+
+    def rows(self, k):
+        return self._rows[k]
+
+    def hit(self, k):
+        return self._hit[k]
+
+    def step(self, ids, now, e, out=None, evicted=None, stats=None, mark=None):
+        """mark: optional callable, called with 0 just before and 1 just after the gather is
+        enqueued on the compute stream (e.g. to record timing events there)."""
+        r = self.ring
+        k = r.begin_lookup()
+        _on(r.lookup, ids, evicted, stats)
+        mpzch_lookup_or_insert(self.identity, self.stamps, None, self.probes, ids, now, True,
+                               out_rows=self._rows[k], out_hit=self._hit[k], out_evicted=evicted, out_stats=stats,
+                               ws=self._mz_ws, stream=r.ls)
+        r.mark(k, 0)
+        writeback_plan(self.values.shape[0], self._rows[k], self._ws[k], WB_LAST_WINS, stream=r.ls)
+        r.mark(k, 1)
+        r.wait(k, 0)
+        mpzch_zero_inserted(self.values, self._rows[k], self._hit[k], stream=r.cs)
+        if mark is not None:
+            mark(0)
+        out = gather_rows(self.values, self._rows[k], out, stream=r.cs)
+        if mark is not None:
+            mark(1)
+        r.wait(k, 1)
+        writeback_apply(self.values, e, self._ws[k], WB_LAST_WINS, 1.0, stream=r.cs)
+        r.end_compute(k)
+        return out, k
+
+
+class HashedTablesPipeline:
+    """Hashed tables (row = mix(key) mod rows): gather + duplicate-summed SGD per table.
+
+    lookup stream:  hashed_rows -> writeback_plan(SGD_SUM), table by table
+    compute stream: gather_rows -> writeback_apply(SGD_SUM, lr), table by table
+    One ring per table, so a table's next batch may plan while other tables apply."""
+
+    def __init__(self, tables, n, depth=2):
+        self.tables, self.n = tables, n
+        dev = tables[0].device
+        first = _Ring(dev, depth, points=2)
+        self.rings = [first] + [_Ring(dev, depth, points=2, lookup=first.lookup) for _ in tables[1:]]
+        self._rows = [[torch.empty(n, dtype=torch.int64, device=dev) for _ in range(depth)] for _ in tables]
+        self._ws = [[new_workspace(dev, writeback_workspace_size(t.shape[0], t.shape[1], n, WB_SGD_SUM))
+                     for _ in range(depth)] for t in tables]
+
+    def restart(self):
+        for r in self.rings:
+            r.restart()
+
+    def rows(self, table, k):
+        return self._rows[table][k]
+
+    def step(self, keys, grads, lr, outs=None, mark=None):
+        """keys[i], grads[i]: table i's keys (int64[n]) and gradients ([n, dim]); returns the gathered rows.
+        mark: optional callable, called on the compute stream with ("gather" | "apply", table, 0 | 1)
+        just before (0) and after (1) each gather and apply is enqueued."""
+        mark = mark if mark is not None else (lambda tag: None)
+        ks = []
+        for i, t in enumerate(self.tables):
+            r = self.rings[i]
+            k = r.begin_lookup()
+            _on(r.lookup, keys[i])
+            hashed_rows(keys[i], t.shape[0], out=self._rows[i][k], stream=r.ls)
+            r.mark(k, 0)
+            writeback_plan(t.shape[0], self._rows[i][k], self._ws[i][k], WB_SGD_SUM, stream=r.ls)
+            r.mark(k, 1)
+            ks.append(k)
+        res = []
+        for i, t in enumerate(self.tables):
+            r, k = self.rings[i], ks[i]
+            r.wait(k, 0)
+            mark(("gather", i, 0))
+            res.append(gather_rows(t, self._rows[i][k], None if outs is None else outs[i], stream=r.cs))
+            mark(("gather", i, 1))
+            r.wait(k, 1)
+            mark(("apply", i, 0))
+            writeback_apply(t, grads[i], self._ws[i][k], WB_SGD_SUM, lr, stream=r.cs)
+            mark(("apply", i, 1))
+            r.end_compute(k)
+        return res
+
+
+class EMAPipeline:
+    """EMA row updates of several tables per batch (CS3: CTS on positives, CMS on all).
+
+    lookup stream:  ema_update_plan for every update of the batch
+    compute stream: ema_update_apply for every update, in the order given
+    `updates` fixes, per update, the table and its row count; step() takes the
+    rows, masks and values of each update."""
+
+    def __init__(self, tables, n, depth=2):
+        self.tables, self.n = tables, n
+        dev = tables[0].device
+        self.ring = _Ring(dev, depth, points=len(tables))
+        self._ws = [[new_workspace(dev, ema_workspace_size(t.shape[0], t.shape[1], n)) for t in tables]
+                    for _ in range(depth)]
+
+    def restart(self):
+        self.ring.restart()
+
+    def step(self, rows, masks, vals, coeffs, mark=None):
+        """rows[i], masks[i] (or None), vals[i], coeffs[i] = (a, b) for update i of tables[i].
+        mark: optional callable, called on the compute stream with ("apply", i, 0 | 1) just
+        before and after each apply is enqueued."""
+        mark = mark if mark is not None else (lambda tag: None)
+        r = self.ring
+        k = r.begin_lookup()
+        _on(r.lookup, *rows, *masks)
+        for i, t in enumerate(self.tables):
+            ema_update_plan(t.shape[0], rows[i], masks[i], self._ws[k][i], stream=r.ls)
+            r.mark(k, i)
+        for i, t in enumerate(self.tables):
+            a, b = coeffs[i]
+            r.wait(k, i)
+            mark(("apply", i, 0))
+            ema_update_apply(t, vals[i], a, b, self._ws[k][i], stream=r.cs)
+            mark(("apply", i, 1))
+        r.end_compute(k)

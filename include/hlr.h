@@ -103,6 +103,17 @@ hlr_status mpzch_lookup_or_insert(int64_t *identity, int64_t *stamps, float *val
                                   int32_t insert, int64_t *out_rows, int8_t *out_hit, int64_t *out_evicted,
                                   int64_t *out_stats, void *ws, size_t ws_bytes, hipStream_t stream);
 
+/* Zero-fill of the rows a batch inserted, split from the lookup: a lookup
+ * run with values == NULL (for instance on its own stream, so it can overlap
+ * the previous batch's row traffic) leaves the new rows as they were; this
+ * call then writes zeros to rows[i] for every position with hit[i] == 0 and
+ * rows[i] >= 0, which is exactly the set of slots the lookup inserted into.
+ * Enqueue it after every earlier write to those rows and before any read
+ * of them for this batch.  values[capacity*dim] fp32 (16-byte aligned,
+ * dim % 4 == 0); rows[n], hit[n] from mpzch_lookup_or_insert. */
+hlr_status mpzch_zero_inserted(float *values, int64_t capacity, int64_t dim, const int64_t *rows,
+                               const int8_t *hit, int64_t n, hipStream_t stream);
+
 /* ------------------------------------------------------------------------
  * Row gather   [ML] sec. 2 (the model reads the cached row M[i])
  *  out[i][:] = table[rows[i]][:] for rows[i] >= 0, zeros for rows[i] == -1.
@@ -147,6 +158,27 @@ hlr_status writeback_rows(float *table, int64_t num_rows, int64_t dim, const int
                           int64_t n, int32_t mode, float lr, void *ws, size_t ws_bytes, hipStream_t stream);
 
 /* ------------------------------------------------------------------------
+ * writeback_rows in two halves, so the half that needs only `rows` can run on
+ * another stream ahead of the values (the lookup/dispatch stream beside the
+ * compute stream of "MTGR: Industrial-Scale Generative Recommendation
+ * Framework in Meituan", sec. 3.5).  writeback_plan followed by
+ * writeback_apply with the same workspace, n, num_rows and mode equals
+ * writeback_rows bit for bit.
+ *  writeback_plan: groups the positions of rows[n] by row (LAST_WINS: the
+ *    last position of every distinct row; SGD_SUM: positions in batch order
+ *    per row) into ws.  `rows` is not read after the plan.
+ *  writeback_apply: applies src[n*dim] to table through the plan in ws.
+ *  ws: writeback_rows_workspace_size(num_rows, dim, n, mode) bytes, sized for
+ *    the apply's dim.  It holds the plan between the two calls: each plan
+ *    serves exactly one apply, and nothing else may use ws in between (order
+ *    the two calls with an event when they run on different streams).
+ * --------------------------------------------------------------------- */
+hlr_status writeback_plan(int64_t num_rows, const int64_t *rows, int64_t n, int32_t mode, void *ws,
+                          size_t ws_bytes, hipStream_t stream);
+hlr_status writeback_apply(float *table, int64_t num_rows, int64_t dim, const float *src, int64_t n,
+                           int32_t mode, float lr, void *ws, size_t ws_bytes, hipStream_t stream);
+
+/* ------------------------------------------------------------------------
  * EMA row updates   [CS3] sec. 2 (CTS: c <- a*c + (1-a)*v on positive
  * interactions; CMS: s <- b*s + (1-b)*h on every interaction)
  *  For every position i in batch order with rows[i] >= 0 and mask[i] != 0
@@ -161,6 +193,17 @@ size_t ema_update_rows_workspace_size(int64_t num_rows, int64_t dim, int64_t n);
 hlr_status ema_update_rows(float *table, int64_t num_rows, int64_t dim, const int64_t *rows, const float *vals,
                            const uint8_t *mask, int64_t n, float a, float b, void *ws, size_t ws_bytes,
                            hipStream_t stream);
+
+/* ema_update_rows in two halves, as writeback_plan / writeback_apply:
+ * ema_update_plan groups the positions (rows[n], mask[n] or NULL) by row into
+ * ws; ema_update_apply applies vals[n*dim] with (a, b) through that plan.
+ * Together they equal ema_update_rows bit for bit.  ws:
+ * ema_update_rows_workspace_size(num_rows, dim, n) bytes, sized for the
+ * apply's dim; each plan serves exactly one apply. */
+hlr_status ema_update_plan(int64_t num_rows, const int64_t *rows, const uint8_t *mask, int64_t n, void *ws,
+                           size_t ws_bytes, hipStream_t stream);
+hlr_status ema_update_apply(float *table, int64_t num_rows, int64_t dim, const float *vals, int64_t n, float a,
+                            float b, void *ws, size_t ws_bytes, hipStream_t stream);
 
 /* ------------------------------------------------------------------------
  * Serving score: int8 row dequantisation fused with a dot product

@@ -101,6 +101,30 @@ def test_writeback_and_ema_argument_errors(lib):
     assert lib.ema_update_rows(P16, 100, 8, P16, P16, None, 10, 0.9, 0.1, None, 0, s) == WS_SMALL
 
 
+def test_split_entry_point_argument_errors(lib):
+    s = None
+    need = lib.writeback_rows_workspace_size(100, 8, 10, 1)
+    assert lib.writeback_plan(100, P16, 10, 7, P16, need, s) == INVALID  # unknown mode
+    assert lib.writeback_plan(100, P16, -1, 0, P16, need, s) == INVALID
+    assert lib.writeback_plan(100, None, 10, 1, P16, need, s) == INVALID
+    assert lib.writeback_plan(100, P16, 10, 1, None, 0, s) == WS_SMALL
+    assert lib.writeback_plan(100, P16, 0, 1, None, 0, s) == OK  # nothing to plan
+    assert lib.writeback_apply(P16, 100, 8, P16, 10, 0, 0.5, P16, need, s) == INVALID  # last-wins needs lr=1
+    assert lib.writeback_apply(P16, 100, 6, P16, 10, 1, 0.1, P16, need, s) == DIM
+    assert lib.writeback_apply(P16, 100, 8, P_ODD, 10, 1, 0.1, P16, need, s) == MISALIGNED
+    assert lib.writeback_apply(P16, 100, 8, P16, 10, 1, 0.1, P16, need - 1, s) == WS_SMALL
+    eneed = lib.ema_update_rows_workspace_size(100, 8, 10)
+    assert lib.ema_update_plan(100, P16, None, -5, P16, eneed, s) == INVALID
+    assert lib.ema_update_plan(100, P_ODD, None, 10, P16, eneed, s) == MISALIGNED
+    assert lib.ema_update_plan(100, P16, None, 10, ctypes.c_void_p((1 << 20) + 16), eneed, s) == MISALIGNED
+    assert lib.ema_update_apply(P16, 100, 2048, P16, 10, 0.9, 0.1, P16, eneed, s) == DIM
+    assert lib.ema_update_apply(P16, 100, 8, P16, 10, 0.9, 0.1, None, 0, s) == WS_SMALL
+    assert lib.mpzch_zero_inserted(P16, 64, 6, P16, P16, 10, s) == DIM
+    assert lib.mpzch_zero_inserted(P16, 0, 8, P16, P16, 10, s) == INVALID
+    assert lib.mpzch_zero_inserted(P16, 64, 8, None, P16, 10, s) == INVALID
+    assert lib.mpzch_zero_inserted(P_ODD, 64, 8, P16, P16, 10, s) == MISALIGNED
+
+
 def test_score_dedup_hashed_argument_errors(lib):
     s = None
     assert lib.gather_dequant_score(P16, P16, P16, 10, 520, P16, 2, 3, P16, P16, s) == DIM

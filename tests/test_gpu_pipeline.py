@@ -1,0 +1,195 @@
+"""GPU parity of the split entry points (plan / apply, lookup without values + zero-fill) and of
+the two-stream schedules in hashed_lookup_row_amd.pipeline, against the oracle.
+
+The schedules are run for several batches without synchronising in between, so the lookup
+stream really runs ahead of the compute stream; every output of every batch and the final
+state must equal the oracle's sequential result bit for bit.
+"""
+import numpy as np
+import pytest
+import torch
+
+import hashed_lookup_row_amd as hlr
+import oracle
+import synth
+from hashed_lookup_row_amd import pipeline
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def dev():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    hlr.load_library()
+    return torch.device("cuda:0")
+
+
+def to_np(t):
+    torch.cuda.synchronize()
+    return t.detach().cpu().numpy()
+
+
+def bits_equal(a, b):
+    return a.shape == b.shape and np.ascontiguousarray(a).tobytes() == np.ascontiguousarray(b).tobytes()
+
+
+def side_stream_plan(dev, plan):
+    """Runs plan() on another stream and makes the current stream wait for it."""
+    s = torch.cuda.Stream(dev)
+    s.wait_stream(torch.cuda.current_stream(dev))
+    with torch.cuda.stream(s):
+        plan()
+    torch.cuda.current_stream(dev).wait_stream(s)
+
+
+@pytest.mark.parametrize("mode,lr", [(hlr.WB_LAST_WINS, 1.0), (hlr.WB_SGD_SUM, 0.01)])
+@pytest.mark.parametrize("num_rows,n,D", [(50, 3000, 64), (5000, 20_000, 512), (7, 1, 4)])
+def test_writeback_plan_apply(dev, mode, lr, num_rows, n, D):
+    g = np.random.default_rng(num_rows + n + mode)
+    rows = g.integers(-1, num_rows, size=n).astype(np.int64)
+    rows[g.random(n) < 0.3] = 3 % num_rows  # a hot row
+    src = g.standard_normal((n, D)).astype(np.float32)
+    table = g.standard_normal((num_rows, D)).astype(np.float32)
+    t = torch.from_numpy(table).to(dev)
+    r = torch.from_numpy(rows).to(dev)
+    ws = hlr.new_workspace(dev, hlr.writeback_workspace_size(num_rows, D, n, mode))
+    side_stream_plan(dev, lambda: hlr.writeback_plan(num_rows, r, ws, mode))
+    hlr.writeback_apply(t, torch.from_numpy(src).to(dev), ws, mode, lr)
+    if mode == hlr.WB_LAST_WINS:
+        oracle.writeback_last(table, rows, src)
+    else:
+        oracle.sgd_sum(table, rows, src, lr)
+    assert bits_equal(to_np(t), table)
+
+
+@pytest.mark.parametrize("masked", [False, True])
+def test_ema_plan_apply(dev, masked):
+    g = np.random.default_rng(7 + masked)
+    num_rows, n, D = 300, 30_000, 128
+    rows = np.minimum(synth.zipf_ranks(g, num_rows, 1.1, n), num_rows - 1).astype(np.int64)
+    vals = g.standard_normal((n, D)).astype(np.float32)
+    mask = (g.random(n) < 0.5).astype(np.uint8) if masked else None
+    table = g.standard_normal((num_rows, D)).astype(np.float32)
+    t = torch.from_numpy(table).to(dev)
+    r = torch.from_numpy(rows).to(dev)
+    m = torch.from_numpy(mask).to(dev) if masked else None
+    ws = hlr.new_workspace(dev, hlr.ema_workspace_size(num_rows, D, n))
+    side_stream_plan(dev, lambda: hlr.ema_update_plan(num_rows, r, m, ws))
+    hlr.ema_update_apply(t, torch.from_numpy(vals).to(dev), 0.95, 0.05, ws)
+    oracle.ema(table, rows, vals, mask, 0.95, 0.05)
+    assert bits_equal(to_np(t), table)
+
+
+def prefilled_pair(dev, cfg):
+    C, P, D = cfg.capacity, cfg.probes, cfg.dim
+    identity = torch.full((C,), -1, dtype=torch.int64, device=dev)
+    stamps = torch.full((C,), -1, dtype=torch.int64, device=dev)
+    o = oracle.MPZCHTable(C, P, D, with_values=False)
+    batches = synth.prefill_batches(cfg)
+    for k, b in enumerate(batches, start=1):
+        hlr.mpzch_lookup_or_insert(identity, stamps, None, P, torch.from_numpy(b).to(dev), k)
+        o.step(b, k)
+    o.values = np.zeros((C, D), np.float32)
+    return identity, stamps, o, len(batches)
+
+
+def test_lookup_without_values_then_zero_inserted(dev):
+    cfg = synth.scaled_memory_layer(capacity=8_192, universe=60_000, batch=4_096, steps=4, dim=64)
+    C, P, D = cfg.capacity, cfg.probes, cfg.dim
+    identity, stamps, o, base = prefilled_pair(dev, cfg)
+    g = np.random.default_rng(3)
+    values_np = g.standard_normal((C, D)).astype(np.float32)  # stale rows that inserts must clear
+    o.values = values_np.copy()
+    values = torch.from_numpy(values_np).to(dev)
+    for t, ids_np in enumerate(synth.mpzch_stream(cfg, cfg.steps), start=1):
+        ids = torch.from_numpy(ids_np).to(dev)
+        rows, hit, _, _ = hlr.mpzch_lookup_or_insert(identity, stamps, None, P, ids, base + t)
+        hlr.mpzch_zero_inserted(values, rows, hit)
+        orows, ohit, _, _ = o.step(ids_np, base + t)
+        assert np.array_equal(to_np(rows), orows) and np.array_equal(to_np(hit), ohit)
+        assert bits_equal(to_np(values), o.values), f"step {t}"
+
+
+@pytest.mark.parametrize("depth", [2, 3])
+def test_memory_layer_pipeline(dev, depth):
+    cfg = synth.scaled_memory_layer(capacity=16_384, universe=120_000, batch=8_192, steps=8)
+    C, P, D, n = cfg.capacity, cfg.probes, cfg.dim, cfg.batch
+    identity, stamps, o, base = prefilled_pair(dev, cfg)
+    values = torch.zeros((C, D), dtype=torch.float32, device=dev)
+    ids_np = synth.mpzch_stream(cfg, cfg.steps)
+    e_np = [synth.normal_rows_np(n, D, cfg.e_std, 2, t) for t in range(1, cfg.steps + 1)]
+    ids = [torch.from_numpy(x).to(dev) for x in ids_np]
+    es = [torch.from_numpy(x).to(dev) for x in e_np]
+    outs = [torch.empty((n, D), dtype=torch.float32, device=dev) for _ in ids]
+    evs = [torch.empty(n, dtype=torch.int64, device=dev) for _ in ids]
+    sts = [torch.zeros(6, dtype=torch.int64, device=dev) for _ in ids]
+    torch.cuda.synchronize()
+    pipe = pipeline.MemoryLayerPipeline(identity, stamps, values, P, n, depth=depth)
+    for t in range(cfg.steps):  # no synchronisation between batches
+        pipe.step(ids[t], base + t + 1, es[t], out=outs[t], evicted=evs[t], stats=sts[t])
+    last_rows = [to_np(pipe.rows(k)).copy() for k in range(depth)]
+    for t in range(cfg.steps):
+        orows, ohit, oev, ost = o.step(ids_np[t], base + t + 1)
+        assert bits_equal(to_np(outs[t]), o.gather(orows)), f"gather step {t}"
+        o.writeback(orows, e_np[t])
+        assert np.array_equal(to_np(evs[t]), oev), f"evicted step {t}"
+        assert np.array_equal(to_np(sts[t])[:5], ost), f"stats step {t}"
+        if t >= cfg.steps - depth:
+            assert np.array_equal(last_rows[t % depth], orows)
+    assert np.array_equal(to_np(identity), o.identity)
+    assert np.array_equal(to_np(stamps), o.stamps)
+    assert bits_equal(to_np(values), o.values)
+
+
+def test_hashed_tables_pipeline(dev):
+    g = np.random.default_rng(11)
+    sizes, n, D, lr, steps = [5000, 700, 3000], 6000, 128, 0.01, 4
+    tables_np = [(g.standard_normal((m, D)) * 0.01).astype(np.float32) for m in sizes]
+    tables = [torch.from_numpy(x).to(dev) for x in tables_np]
+    keys_np = [[(g.zipf(1.3, size=n) * 2654435761 % (1 << 40)).astype(np.int64) for _ in sizes]
+               for _ in range(steps)]
+    grads_np = [[(g.standard_normal((n, D)) * 1e-3).astype(np.float32) for _ in sizes] for _ in range(steps)]
+    keys = [[torch.from_numpy(k).to(dev) for k in ks] for ks in keys_np]
+    grads = [[torch.from_numpy(x).to(dev) for x in gs] for gs in grads_np]
+    torch.cuda.synchronize()
+    pipe = pipeline.HashedTablesPipeline(tables, n)
+    outs = [pipe.step(keys[s], grads[s], lr) for s in range(steps)]
+    for s in range(steps):
+        for i, m in enumerate(sizes):
+            rows = oracle.hashed_rows(keys_np[s][i], m)
+            assert bits_equal(to_np(outs[s][i]), oracle.gather(tables_np[i], rows)), (s, i)
+            oracle.sgd_sum(tables_np[i], rows, grads_np[s][i], lr)
+    for i in range(len(sizes)):
+        assert bits_equal(to_np(tables[i]), tables_np[i]), i
+
+
+def test_ema_pipeline(dev):
+    cfg = synth.CS3
+    users, items, D, n = 4096, 8192, 128, 20_000
+    g = np.random.default_rng(5)
+    names = ["c_user", "c_item", "s_user", "s_item"]
+    shapes = [users, items, users, items]
+    cpu = [np.zeros((m, D), np.float32) for m in shapes]
+    gpu = [torch.zeros((m, D), dtype=torch.float32, device=dev) for m in shapes]
+    batches = []
+    for step in range(3):
+        u = np.minimum(synth.zipf_ranks(g, users, 1.1, n), users - 1).astype(np.int64)
+        it = np.minimum(synth.zipf_ranks(g, items, 1.05, n), items - 1).astype(np.int64)
+        y = (g.random(n) < 0.05).astype(np.uint8)
+        v = [g.standard_normal((n, D)).astype(np.float32) for _ in range(3)]
+        batches.append((u, it, y, v))
+    dev_b = [tuple(torch.from_numpy(x).to(dev) for x in (u, it, y)) + ([torch.from_numpy(x).to(dev) for x in v],)
+             for (u, it, y, v) in batches]
+    torch.cuda.synchronize()
+    pipe = pipeline.EMAPipeline(gpu, n)
+    coeffs = [(cfg.cts_a, cfg.cts_b), (cfg.cts_a, cfg.cts_b), (cfg.cms_a, cfg.cms_b), (cfg.cms_a, cfg.cms_b)]
+    for (ur, ir, yy, vv) in dev_b:
+        pipe.step([ur, ir, ur, ir], [yy, yy, None, None], [vv[0], vv[1], vv[2], vv[2]], coeffs)
+    for (u, it, y, v) in batches:
+        oracle.ema(cpu[0], u, v[0], y, cfg.cts_a, cfg.cts_b)
+        oracle.ema(cpu[1], it, v[1], y, cfg.cts_a, cfg.cts_b)
+        oracle.ema(cpu[2], u, v[2], None, cfg.cms_a, cfg.cms_b)
+        oracle.ema(cpu[3], it, v[2], None, cfg.cms_a, cfg.cms_b)
+    for k, name in enumerate(names):
+        assert bits_equal(to_np(gpu[k]), cpu[k]), name
