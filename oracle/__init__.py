@@ -61,6 +61,8 @@ def _load():
             lib.orc_writeback_last.argtypes = [p, i64, i64, p, p, i64]
             lib.orc_sgd_sum.restype = ctypes.c_int
             lib.orc_sgd_sum.argtypes = [p, i64, i64, p, p, i64, ctypes.c_float]
+            lib.orc_l2_align.restype = ctypes.c_int
+            lib.orc_l2_align.argtypes = [p, i64, i64, p, p, i64, ctypes.c_float]
             lib.orc_ema.restype = ctypes.c_int
             lib.orc_ema.argtypes = [p, i64, i64, p, p, p, i64, ctypes.c_float, ctypes.c_float]
             lib.orc_dequant_score.restype = ctypes.c_int
@@ -177,6 +179,15 @@ def sgd_sum(table, rows, g, lr):
     g = _c(g, np.float32)
     _check(_load().orc_sgd_sum(_ptr(table), table.shape[0], table.shape[1], _ptr(rows), _ptr(g), rows.size,
                                ctypes.c_float(lr)), "sgd_sum")
+
+
+def l2_align(table, rows, e, lr):
+    """SGD on ||M[r] - e_i||^2: per occurrence g = 2 (M - e_i), summed per row as in sgd_sum."""
+    assert table.dtype == np.float32 and table.flags.c_contiguous
+    rows = _c(rows, np.int64)
+    e = _c(e, np.float32)
+    _check(_load().orc_l2_align(_ptr(table), table.shape[0], table.shape[1], _ptr(rows), _ptr(e), rows.size,
+                                ctypes.c_float(lr)), "l2_align")
 
 
 def ema(table, rows, vals, mask, a, b):

@@ -283,6 +283,49 @@ int orc_sgd_sum(float *table, int64_t num_rows, int64_t dim, const int64_t *rows
     return ORC_OK;
 }
 
+/* ------------------------------------------------ L2 alignment [ML] sec. 2 */
+/*
+ * The plain alternative to Writeback that [ML] sec. 2 and sec. 3 compare with
+ * it: learn the cache row by SGD on the squared distance ||M[r] - sg(e_i)||^2.
+ * Each occurrence i of row r contributes the gradient 2 (M[r] - e_i), taken at
+ * the row's value before the batch: g_i = fl(2 * fl(M[r] - e_i)) (the doubling
+ * is exact).  A row's gradients are summed as in orc_sgd_sum (runs of
+ * ORC_SUM_RUN consecutive occurrences in batch order, run totals in order) and
+ * applied once: M[r] = fl(M[r] - fl(lr * s)).
+ */
+int orc_l2_align(float *table, int64_t num_rows, int64_t dim, const int64_t *rows, const float *e, int64_t n,
+                 float lr) {
+    int64_t m = 0;
+    int err;
+    orc_pair *p = group_rows(rows, NULL, n, num_rows, &m, &err);
+    if (!p) return err;
+    int64_t k0 = 0;
+    while (k0 < m) {
+        int64_t k1 = k0;
+        while (k1 < m && p[k1].key == p[k0].key) k1++;
+        float *w = table + p[k0].key * dim;
+        for (int64_t d = 0; d < dim; ++d) {
+            const float before = w[d];
+            float s = 0.0f;
+            for (int64_t r0 = k0; r0 < k1; r0 += ORC_SUM_RUN) {
+                const int64_t r1 = r0 + ORC_SUM_RUN < k1 ? r0 + ORC_SUM_RUN : k1;
+                float diff = before - e[p[r0].pos * dim + d];
+                float run = 2.0f * diff;
+                for (int64_t k = r0 + 1; k < r1; ++k) {
+                    diff = before - e[p[k].pos * dim + d];
+                    run = run + 2.0f * diff;
+                }
+                s = (r0 == k0) ? run : s + run;
+            }
+            const float step = lr * s;
+            w[d] = before - step;
+        }
+        k0 = k1;
+    }
+    free(p);
+    return ORC_OK;
+}
+
 /* --------------------------------------------------------------- EMA [CS3] */
 /*
  * In batch order, for every position i with rows[i] >= 0 and mask[i] != 0 (mask

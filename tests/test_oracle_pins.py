@@ -349,6 +349,52 @@ def test_sgd_sum_integer_gradients_are_exact():
         assert np.array_equal(table[r], -0.5 * grads[rows == r].sum(axis=0))
 
 
+# ------------------------------------------------------------ L2 alignment
+def test_l2_align_single_occurrence_half_rate_is_writeback():
+    """lr = 0.5, one occurrence per row: M - 0.5 * 2 (M - e) is the Writeback assignment
+    fl(M - fl(M - e)) exactly (the doubling and the halving are exact)."""
+    g = np.random.default_rng(21)
+    C, D = 40, 16
+    rows = g.permutation(C)[:25].astype(np.int64)
+    e = g.standard_normal((25, D)).astype(np.float32)
+    table = g.standard_normal((C, D)).astype(np.float32)
+    before = table.copy()
+    oracle.l2_align(table, rows, e, 0.5)
+    want = before.copy()
+    want[rows] = before[rows] - (before[rows] - e)  # numpy float32: each operation rounded
+    assert np.array_equal(table, want)
+
+
+def test_l2_align_duplicates_exact_on_short_dyadics():
+    """Values on a coarse dyadic grid make every partial sum exact, so the result must be the exact
+    M - lr * sum_i 2 (M - e_i) with M the row before the batch (catches a dropped factor 2, a
+    flipped sign, or a gradient taken at the partly updated row)."""
+    g = np.random.default_rng(22)
+    C, D, n = 6, 4, 900
+    rows = g.integers(-1, C, size=n).astype(np.int64)
+    rows[:300] = 2  # one row with 300+ occurrences: more than one run of 256
+    e = (g.integers(-64, 65, size=(n, D)) / 16.0).astype(np.float32)
+    table = (g.integers(-64, 65, size=(C, D)) / 16.0).astype(np.float32)
+    before = table.copy()
+    lr = 2.0 ** -12
+    oracle.l2_align(table, rows, e, lr)
+    for r in range(C):
+        pos = np.nonzero(rows == r)[0]
+        for d in range(D):
+            m = Fraction(float(before[r, d]))
+            exact = m - Fraction(lr) * sum(2 * (m - Fraction(float(e[i, d]))) for i in pos)
+            assert Fraction(float(table[r, d])) == exact, (r, d)
+
+
+def test_l2_align_duplicates_at_matching_rate_assign_e():
+    """k copies of the same target with lr = 1 / (2k) move the row onto the target exactly."""
+    for k in (1, 2, 8, 64):
+        e = np.array([[1.5, -0.25, 3.0, 0.0]], np.float32)
+        table = np.array([[0.5, 2.0, -1.0, 7.0], [9.0, 9.0, 9.0, 9.0]], np.float32)
+        oracle.l2_align(table, np.zeros(k, np.int64), np.repeat(e, k, axis=0), 1.0 / (2 * k))
+        assert np.array_equal(table[0], e[0]) and np.array_equal(table[1], np.full(4, 9.0, np.float32))
+
+
 # -------------------------------------------------------------------- EMA
 def test_ema_special_cases():
     g = np.random.default_rng(2)
