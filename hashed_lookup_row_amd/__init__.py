@@ -22,6 +22,7 @@ STATUS = {0: "ok", 1: "invalid argument", 2: "unsupported dim", 3: "misaligned p
           5: "HIP launch error"}
 WB_LAST_WINS = 0
 WB_SGD_SUM = 1
+WB_L2_ALIGN = 2
 SGD_SUM_RUN = 256
 EMPTY_ID = -1
 

@@ -22,6 +22,11 @@
 // so a Zipf-hot row (tens of thousands of duplicates) spreads over the whole
 // GPU; sgd_combine then adds each row's run totals in batch order and writes
 // fl(M - fl(lr * s)).
+//
+// L2_ALIGN — the alternative to Writeback that the same Memory Layer section
+// compares: SGD on ||M[r] - sg(e_i)||^2, i.e. the gradient 2 (M[r] - e_i) per
+// occurrence at the row's value before the batch, summed and applied as in
+// SGD_SUM (same kernels, the gradient formed on the fly from M and e).
 #include "radix.hpp"
 
 namespace {
@@ -176,38 +181,39 @@ __global__ void __launch_bounds__(kThreads)
 
 // Duplicate-summed SGD: a wave sums a run of a row's gradients in batch order
 // (lanes own 16-byte column units), acc = g[spos[j0]], then acc += g[spos[j]].
+// L2 = true is the L2-alignment update: the source holds targets e_i and each
+// occurrence's gradient is fl(2 * fl(M - e_i)) with M the row before the batch
+// (the doubling is exact); everything else is as for SGD_SUM.
 constexpr int kRun = HLR_SGD_SUM_RUN;
 
 template <int NC>
 constexpr int light_batch() { return NC == 1 ? 16 : (NC == 2 ? 8 : 4); }
 
-template <int NC>
+__device__ __forceinline__ float4 l2_grad(float4 m, float4 e) {
+  const float4 d = f4_sub(m, e);
+  return make_float4(2.f * d.x, 2.f * d.y, 2.f * d.z, 2.f * d.w);
+}
+
+__device__ __forceinline__ float2 l2_grad(float2 m, float2 e) {
+  return make_float2(2.f * (m.x - e.x), 2.f * (m.y - e.y));
+}
+
+template <int NC, bool L2>
 __device__ __forceinline__ void sum_run(const float4 *__restrict__ g, const uint32_t *__restrict__ spos, int32_t j0,
-                                        int32_t j1, int64_t v4, int lane, float4 (&acc)[NC]) {
+                                        int32_t j1, int64_t v4, int lane, const float4 (&m)[NC], float4 (&acc)[NC]) {
   rows_run<light_batch<NC>(), NC>(g, spos, j0, j1, v4, lane, [&](int32_t j, const float4(&x)[NC]) {
 #pragma unroll
-    for (int q = 0; q < NC; ++q)
-      acc[q] = j == j0 ? x[q] : make_float4(acc[q].x + x[q].x, acc[q].y + x[q].y, acc[q].z + x[q].z, acc[q].w + x[q].w);
+    for (int q = 0; q < NC; ++q) {
+      const float4 y = L2 ? l2_grad(m[q], x[q]) : x[q];
+      acc[q] = j == j0 ? y : make_float4(acc[q].x + y.x, acc[q].y + y.y, acc[q].z + y.z, acc[q].w + y.w);
+    }
   });
 }
 
-template <int NC>
-__device__ __forceinline__ void sgd_update(float4 *table, int64_t r, const float4 (&tot)[NC], float lr, int64_t v4,
-                                           int lane) {
-#pragma unroll
-  for (int q = 0; q < NC; ++q) {
-    const int64_t c = lane + q * kWave;
-    if (c < v4) {
-      const float4 wv = table[r * v4 + c];
-      const float4 st = make_float4(lr * tot[q].x, lr * tot[q].y, lr * tot[q].z, lr * tot[q].w);
-      table[r * v4 + c] = f4_sub(wv, st);  // fl(M - fl(lr * s))
-    }
-  }
-}
-
 // Light rows (fewer than kHeavyMin occurrences, hence one run): one wave per
-// row.  Longer rows are registered for the block kernels.
-template <int NC>
+// row; the row is read once, before its gradients, and written once:
+// fl(M - fl(lr * s)).  Longer rows are registered for the slice kernels.
+template <int NC, bool L2>
 __global__ void __launch_bounds__(kThreads)
     sgd_light(float4 *table, const float4 *__restrict__ g, const uint32_t *__restrict__ skey,
               const uint32_t *__restrict__ spos, const int32_t *__restrict__ seg_start,
@@ -222,9 +228,20 @@ __global__ void __launch_bounds__(kThreads)
       if (lane == 0) push_heavy(static_cast<int32_t>(k), e - s, kRun, counters, hlist, clist);
       continue;
     }
-    float4 run[NC];
-    sum_run<NC>(g, spos, s, e, v4, lane, run);
-    sgd_update<NC>(table, skey[s], run, lr, v4, lane);
+    const int64_t r = skey[s];
+    float4 m[NC], run[NC];
+#pragma unroll
+    for (int q = 0; q < NC; ++q) {
+      const int64_t c = lane + q * kWave;
+      m[q] = table[r * v4 + (c < v4 ? c : 0)];
+    }
+    sum_run<NC, L2>(g, spos, s, e, v4, lane, m, run);
+#pragma unroll
+    for (int q = 0; q < NC; ++q) {
+      const int64_t c = lane + q * kWave;
+      const float4 st = make_float4(lr * run[q].x, lr * run[q].y, lr * run[q].z, lr * run[q].w);
+      if (c < v4) table[r * v4 + c] = f4_sub(m[q], st);  // fl(M - fl(lr * s))
+    }
   }
 }
 
@@ -239,7 +256,9 @@ __device__ __forceinline__ void sgd_write2(float *table, int64_t r, float2 acc, 
 
 // Heavy rows: one wave per (run of <= 256 occurrences, 128-element slice).  A
 // row with one run is updated at once; otherwise the run total goes to
-// `partial` for sgd_combine.
+// `partial` for sgd_combine.  No wave writes a multi-run row before the
+// combine, so the L2 gradients all see the row as it was before the batch.
+template <bool L2>
 __global__ void __launch_bounds__(kThreads)
     sgd_heavy(float *table, const float *__restrict__ g, const uint32_t *__restrict__ skey,
               const uint32_t *__restrict__ spos, const int32_t *__restrict__ seg_start,
@@ -254,9 +273,12 @@ __global__ void __launch_bounds__(kThreads)
     const int32_t s = seg_start[km.x], end = seg_end[km.x];
     const int32_t j0 = s + km.y * kRun;
     const int32_t j1 = j0 + kRun < end ? j0 + kRun : end;
+    float2 mv = make_float2(0.f, 0.f);
+    if (L2) mv = *reinterpret_cast<const float2 *>(table + static_cast<int64_t>(skey[s]) * D + (e < D ? e : 0));
     float2 acc = make_float2(0.f, 0.f);
     slice_run(g, spos, j0, j1, D, e, [&](int32_t j, float2 x) {
-      acc = j == j0 ? x : make_float2(acc.x + x.x, acc.y + x.y);
+      const float2 y = L2 ? l2_grad(mv, x) : x;
+      acc = j == j0 ? y : make_float2(acc.x + y.x, acc.y + y.y);
     });
     if (end - s <= kRun) {
       sgd_write2(table, skey[s], acc, lr, D, e);
@@ -291,22 +313,31 @@ inline size_t sgd_partial_elems(int64_t n, int64_t dim) {
   return static_cast<size_t>(2 * ((n + kRun - 1) / kRun) + 2) * static_cast<size_t>(dim / 4);
 }
 
-template <int NC>
+template <int NC, bool L2>
 void sgd_launch(float *table, const float *g, SegWork<uint32_t> &w, int cur, float lr, int64_t dim, float *partial,
                 hipStream_t s) {
   const int64_t v4 = dim / 4;
   int grid = grid_for(w.n, 4 * 4);
   if (grid > 4096) grid = 4096;
-  sgd_light<NC><<<grid, kThreads, 0, s>>>(reinterpret_cast<float4 *>(table), reinterpret_cast<const float4 *>(g),
-                                          w.k[cur], w.v[cur], w.seg_start, w.seg_end, w.nseg, lr, v4, w.ticket,
-                                          w.hlist, w.clist);
+  sgd_light<NC, L2><<<grid, kThreads, 0, s>>>(reinterpret_cast<float4 *>(table), reinterpret_cast<const float4 *>(g),
+                                              w.k[cur], w.v[cur], w.seg_start, w.seg_end, w.nseg, lr, v4, w.ticket,
+                                              w.hlist, w.clist);
   int gh = grid_for(w.n / 32 * num_slices(dim), 4);
   if (gh > 2048) gh = 2048;
-  sgd_heavy<<<gh, kThreads, 0, s>>>(table, g, w.k[cur], w.v[cur], w.seg_start, w.seg_end, w.ticket, w.hlist, lr,
-                                    dim, partial);
+  sgd_heavy<L2><<<gh, kThreads, 0, s>>>(table, g, w.k[cur], w.v[cur], w.seg_start, w.seg_end, w.ticket, w.hlist, lr,
+                                        dim, partial);
   int gc = grid_for(w.n / 256 * num_slices(dim), 4);
   if (gc > 1024) gc = 1024;
   sgd_combine<<<gc, kThreads, 0, s>>>(table, w.k[cur], w.seg_start, w.seg_end, w.ticket, w.clist, lr, dim, partial);
+}
+
+template <bool L2>
+void sgd_dispatch(float *table, const float *g, SegWork<uint32_t> &w, int cur, float lr, int64_t dim, float *partial,
+                  hipStream_t s) {
+  const int64_t nc = (dim / 4 + kWave - 1) / kWave;
+  if (nc == 1) sgd_launch<1, L2>(table, g, w, cur, lr, dim, partial, s);
+  else if (nc == 2) sgd_launch<2, L2>(table, g, w, cur, lr, dim, partial, s);
+  else sgd_launch<4, L2>(table, g, w, cur, lr, dim, partial, s);
 }
 
 }  // namespace
@@ -330,7 +361,7 @@ namespace {
 
 hlr_status wb_args(int64_t num_rows, int64_t n, int32_t mode) {
   if (n < 0 || n > kMaxN || num_rows < 0 || num_rows >= 0x7fffffff) return HLR_INVALID_ARG;
-  if (mode != HLR_WB_LAST_WINS && mode != HLR_WB_SGD_SUM) return HLR_INVALID_ARG;
+  if (mode != HLR_WB_LAST_WINS && mode != HLR_WB_SGD_SUM && mode != HLR_WB_L2_ALIGN) return HLR_INVALID_ARG;
   return HLR_OK;
 }
 
@@ -379,9 +410,8 @@ void wb_apply(float *table, int64_t num_rows, int64_t dim, const float *src, int
   c.off = segwork_layout<uint32_t>(n, &w, ws);
   float *partial = reinterpret_cast<float *>(c.take<float4>(sgd_partial_elems(n, dim)));
   const int cur = sorted_buffer(num_rows);
-  if (nc == 1) sgd_launch<1>(table, src, w, cur, lr, dim, partial, stream);
-  else if (nc == 2) sgd_launch<2>(table, src, w, cur, lr, dim, partial, stream);
-  else sgd_launch<4>(table, src, w, cur, lr, dim, partial, stream);
+  if (mode == HLR_WB_L2_ALIGN) sgd_dispatch<true>(table, src, w, cur, lr, dim, partial, stream);
+  else sgd_dispatch<false>(table, src, w, cur, lr, dim, partial, stream);
 }
 
 }  // namespace

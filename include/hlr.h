@@ -147,11 +147,16 @@ hlr_status dedup_ids(const int64_t *keys, int64_t n, int64_t *out_unique, int64_
  *  mode HLR_WB_SGD_SUM: src holds gradients g_i.  The gradients of each row
  *    are summed in batch order within runs of 256 consecutive occurrences,
  *    run totals added in batch order (s), then M[r] = fl(M[r] - fl(lr*s)).
+ *  mode HLR_WB_L2_ALIGN: src holds targets e_i; the row is learned by SGD on
+ *    ||M[r] - e_i||^2, the alternative to Writeback in [ML] sec. 2 and 3:
+ *    each occurrence's gradient is fl(2*fl(M[r] - e_i)) with M[r] the row
+ *    before the batch, summed and applied exactly as in HLR_WB_SGD_SUM.
  *  Rows not in the batch are untouched.
  *  Workspace: writeback_rows_workspace_size(num_rows, dim, n, mode) bytes.
  * --------------------------------------------------------------------- */
 #define HLR_WB_LAST_WINS 0
 #define HLR_WB_SGD_SUM 1
+#define HLR_WB_L2_ALIGN 2
 #define HLR_SGD_SUM_RUN 256
 size_t writeback_rows_workspace_size(int64_t num_rows, int64_t dim, int64_t n, int32_t mode);
 hlr_status writeback_rows(float *table, int64_t num_rows, int64_t dim, const int64_t *rows, const float *src,
@@ -165,8 +170,8 @@ hlr_status writeback_rows(float *table, int64_t num_rows, int64_t dim, const int
  * writeback_apply with the same workspace, n, num_rows and mode equals
  * writeback_rows bit for bit.
  *  writeback_plan: groups the positions of rows[n] by row (LAST_WINS: the
- *    last position of every distinct row; SGD_SUM: positions in batch order
- *    per row) into ws.  `rows` is not read after the plan.
+ *    last position of every distinct row; SGD_SUM and L2_ALIGN: positions in
+ *    batch order per row) into ws.  `rows` is not read after the plan.
  *  writeback_apply: applies src[n*dim] to table through the plan in ws.
  *  ws: writeback_rows_workspace_size(num_rows, dim, n, mode) bytes, sized for
  *    the apply's dim.  It holds the plan between the two calls: each plan

@@ -246,6 +246,22 @@ def test_sgd_sum_matches_oracle(dev, n, C, D, s):
     assert np.bincount(rows[rows >= 0]).max() > 256 or n < 5000  # a multi-run segment is exercised
 
 
+@pytest.mark.parametrize("n,C,D,s,lr", [(20_000, 3000, 512, 1.2, 0.05), (3000, 2, 64, 1.0, 0.5),
+                                        (65_536, 30_000, 512, 1.05, 0.01), (777, 50, 4, 1.1, 0.25),
+                                        (30_000, 12, 128, 2.0, 0.001)])
+def test_l2_align_matches_oracle(dev, n, C, D, s, lr):
+    """Writeback's L2 alternative: per-occurrence gradient 2 (M - e_i) at the pre-batch row, summed per row."""
+    g = np.random.default_rng(n + D + 1)
+    table = g.standard_normal((C, D)).astype(np.float32)
+    rows = _zipf_rows(g, n, C, s)
+    rows[g.random(n) < 0.01] = -1
+    e = g.standard_normal((n, D)).astype(np.float32)
+    t = torch.from_numpy(table).to(dev)
+    hlr.writeback_rows(t, torch.from_numpy(rows).to(dev), torch.from_numpy(e).to(dev), mode=hlr.WB_L2_ALIGN, lr=lr)
+    oracle.l2_align(table, rows, e, lr)
+    assert bits_equal(to_np(t), table)
+
+
 @pytest.mark.parametrize("n,C,D,masked,a,b", [(20_000, 3000, 128, True, 0.99, 0.01),
                                               (50_000, 1000, 128, False, 0.95, 0.05),
                                               (4097, 7, 4, False, 0.5, 0.5), (3000, 100, 512, True, 0.9, 0.1)])

@@ -43,7 +43,7 @@ def side_stream_plan(dev, plan):
     torch.cuda.current_stream(dev).wait_stream(s)
 
 
-@pytest.mark.parametrize("mode,lr", [(hlr.WB_LAST_WINS, 1.0), (hlr.WB_SGD_SUM, 0.01)])
+@pytest.mark.parametrize("mode,lr", [(hlr.WB_LAST_WINS, 1.0), (hlr.WB_SGD_SUM, 0.01), (hlr.WB_L2_ALIGN, 0.1)])
 @pytest.mark.parametrize("num_rows,n,D", [(50, 3000, 64), (5000, 20_000, 512), (7, 1, 4)])
 def test_writeback_plan_apply(dev, mode, lr, num_rows, n, D):
     g = np.random.default_rng(num_rows + n + mode)
@@ -58,8 +58,10 @@ def test_writeback_plan_apply(dev, mode, lr, num_rows, n, D):
     hlr.writeback_apply(t, torch.from_numpy(src).to(dev), ws, mode, lr)
     if mode == hlr.WB_LAST_WINS:
         oracle.writeback_last(table, rows, src)
-    else:
+    elif mode == hlr.WB_SGD_SUM:
         oracle.sgd_sum(table, rows, src, lr)
+    else:
+        oracle.l2_align(table, rows, src, lr)
     assert bits_equal(to_np(t), table)
 
 
