@@ -65,6 +65,6 @@ extern "C" hlr_status dedup_ids(const int64_t *keys, int64_t n, int64_t *out_uni
   w.nseg = out_num_unique;
   dedup_init<<<grid_for(n, 256), 256, 0, stream>>>(keys, n, w.k[0], w.v[0], w.ticket);
   const int cur = radix_sort_pairs<uint64_t>(w, 64, stream);
-  segment_sorted<uint64_t>(w, cur, 0ull, false, DedupEmit{out_unique, out_last_pos, out_inverse}, stream);
+  segment_sorted<uint64_t>(w, cur, 0ull, false, nullptr, DedupEmit{out_unique, out_last_pos, out_inverse}, stream);
   return launch_status();
 }

@@ -25,49 +25,60 @@ __device__ __forceinline__ float4 ema_step(float4 t, float4 v, float a, float b)
 
 // Row loads in flight per wave in the light kernel.
 template <int NC>
-constexpr int light_batch() { return NC == 1 ? 16 : (NC == 2 ? 8 : 4); }
+constexpr int light_batch() { return NC == 4 ? 4 : 8; }
 
 // Light rows (fewer than kHeavyMin occurrences): one wave per row, exact.
-// Longer rows are registered (in chunks of L) for the block kernels.
+// Longer rows are registered (in chunks of L) for the slice kernels.  A wave
+// walks rows k, k + waves, ...; the next row's (start, end, row) is loaded
+// while the current row is processed (wave-uniform, so scalar loads).
 template <int NC>
 __global__ void __launch_bounds__(kThreads)
-    ema_light(float4 *table, const float4 *__restrict__ vals, const uint32_t *__restrict__ skey,
+    ema_light(float4 *table, const float4 *__restrict__ vals, const uint32_t *__restrict__ seg_key,
               const uint32_t *__restrict__ spos, const int32_t *__restrict__ seg_start,
               const int32_t *__restrict__ seg_end, const int64_t *__restrict__ nseg_p, float a, float b, int64_t v4,
               int L, uint32_t *counters, int2 *hlist, int32_t *clist) {
   const int64_t nseg = *nseg_p;
   const int64_t waves = static_cast<int64_t>(gridDim.x) * (kThreads / kWave);
   const int lane = lane_id();
-  for (int64_t k = (static_cast<int64_t>(blockIdx.x) * kThreads + threadIdx.x) / kWave; k < nseg; k += waves) {
-    const int32_t s = seg_start[k], e = seg_end[k];
+  int64_t k = __builtin_amdgcn_readfirstlane(static_cast<int>((blockIdx.x * kThreads + threadIdx.x) / kWave));
+  if (k >= nseg) return;
+  int32_t s = seg_start[k], e = seg_end[k];
+  int64_t r = seg_key[k];
+  for (;;) {
+    const int64_t kn = k + waves;
+    const int64_t kc = kn < nseg ? kn : nseg - 1;
+    const int32_t sn = seg_start[kc], en = seg_end[kc];
+    const int64_t rn = seg_key[kc];
     if (e - s >= kHeavyMin) {
       if (lane == 0) push_heavy(static_cast<int32_t>(k), e - s, L, counters, hlist, clist);
-      continue;
-    }
-    const int64_t r = skey[s];
-    float4 st[NC];
+    } else {
+      float4 st[NC];
 #pragma unroll
-    for (int q = 0; q < NC; ++q) {
-      const int64_t c = lane + q * kWave;
-      st[q] = c < v4 ? table[r * v4 + c] : make_float4(0.f, 0.f, 0.f, 0.f);
-    }
-    rows_run<light_batch<NC>(), NC>(vals, spos, s, e, v4, lane, [&](int32_t, const float4(&x)[NC]) {
+      for (int q = 0; q < NC; ++q) {
+        const int64_t c = lane + q * kWave;
+        st[q] = table[r * v4 + (c < v4 ? c : 0)];
+      }
+      rows_run<light_batch<NC>(), NC>(vals, spos, s, e, v4, lane, [&](int32_t, const float4(&x)[NC]) {
 #pragma unroll
-      for (int q = 0; q < NC; ++q) st[q] = ema_step(st[q], x[q], a, b);
-    });
+        for (int q = 0; q < NC; ++q) st[q] = ema_step(st[q], x[q], a, b);
+      });
 #pragma unroll
-    for (int q = 0; q < NC; ++q) {
-      const int64_t c = lane + q * kWave;
-      if (c < v4) table[r * v4 + c] = st[q];
+      for (int q = 0; q < NC; ++q) {
+        const int64_t c = lane + q * kWave;
+        if (c < v4) table[r * v4 + c] = st[q];
+      }
     }
+    if (kn >= nseg) break;
+    k = kn;
+    s = sn;
+    e = en;
+    r = rn;
   }
 }
 
-__device__ __forceinline__ float2 ema2(float2 t, float2 v, float a, float b) {
-  return make_float2(a * t.x + b * v.x, a * t.y + b * v.y);
-}
+__device__ __forceinline__ float ema1(float t, float v, float a, float b) { return a * t + b * v; }
 
-// Heavy rows: one wave per (chunk of <= L occurrences, 128-element slice).  A
+// Heavy rows: one wave per (chunk of <= L occurrences, 64-element slice).  A
 // row with one chunk is applied exactly from its stored value.  For a longer
 // row, chunk 0 runs exactly; chunk m > 0 starts W occurrences early from a zero
 // state (the recurrence contracts by a per step, so after W steps the state no
@@ -83,7 +94,7 @@ __global__ void __launch_bounds__(kThreads)
   const int64_t waves = static_cast<int64_t>(gridDim.x) * (kThreads / kWave);
   for (int64_t it = (static_cast<int64_t>(blockIdx.x) * kThreads + threadIdx.x) / kWave; it < items; it += waves) {
     const int2 km = hlist[it / S];
-    const int64_t e = (it % S) * kSliceElems + 2 * lane_id();
+    const int64_t e = (it % S) * kSliceElems + lane_id();
     const bool act = e < D;
     const int32_t s = seg_start[km.x], end = seg_end[km.x];
     const int64_t r = skey[s];
@@ -91,21 +102,21 @@ __global__ void __launch_bounds__(kThreads)
     const int32_t j1 = j0 + L < end ? j0 + L : end;
     const bool exact_start = km.y == 0 || j0 - W <= s;
     const int32_t from = exact_start ? s : j0 - W;
-    float2 st = (exact_start && act) ? *reinterpret_cast<const float2 *>(table + r * D + e) : make_float2(0.f, 0.f);
+    float st = (exact_start && act) ? table[r * D + e] : 0.f;
     if (end - s <= L) {  // the whole row in one chunk
-      slice_run(vals, spos, s, end, D, e, [&](int32_t, float2 x) { st = ema2(st, x, a, b); });
-      if (act) *reinterpret_cast<float2 *>(table + r * D + e) = st;
+      slice_run(vals, spos, s, end, D, e, [&](int32_t, float x) { st = ema1(st, x, a, b); });
+      if (act) table[r * D + e] = st;
       continue;
     }
-    float2 sig = st;
-    slice_run(vals, spos, from, j1, D, e, [&](int32_t j, float2 x) {
+    float sig = st;
+    slice_run(vals, spos, from, j1, D, e, [&](int32_t j, float x) {
       if (j == j0) sig = st;
-      st = ema2(st, x, a, b);
+      st = ema1(st, x, a, b);
     });
     if (act) {
       const int64_t slot = run_slot(j0, km.y, L);
-      *reinterpret_cast<float2 *>(partial + (2 * slot) * D + e) = sig;
-      *reinterpret_cast<float2 *>(partial + (2 * slot + 1) * D + e) = st;
+      partial[(2 * slot) * D + e] = sig;
+      partial[(2 * slot + 1) * D + e] = st;
     }
   }
 }
@@ -129,38 +140,44 @@ __global__ void __launch_bounds__(kThreads)
   const int64_t waves = static_cast<int64_t>(gridDim.x) * (kThreads / kWave);
   for (int64_t it = (static_cast<int64_t>(blockIdx.x) * kThreads + threadIdx.x) / kWave; it < items; it += waves) {
     const int32_t k = clist[it / S];
-    const int64_t e = (it % S) * kSliceElems + 2 * lane_id();
+    const int64_t e = (it % S) * kSliceElems + lane_id();
     const bool act = e < D;
     const int64_t ec = act ? e : 0;
     const int32_t s = seg_start[k], end = seg_end[k];
     const int32_t nch = (end - s + L - 1) / L;
     auto slot2 = [&](int32_t m) { return partial + 2 * run_slot(s + m * L, m, L) * D; };
-    float2 cur = *reinterpret_cast<const float2 *>(slot2(0) + D + ec);
-    for (int32_t m0 = 1; m0 < nch; m0 += kCombineBatch) {
-      float2 sg[kCombineBatch], tau[kCombineBatch];
+    float cur = slot2(0)[D + ec];
+    int32_t m = 1;
+    while (m < nch) {
+      float sg[kCombineBatch], tau[kCombineBatch];
 #pragma unroll
       for (int u = 0; u < kCombineBatch; ++u) {
-        const float *q = slot2(m0 + u < nch ? m0 + u : nch - 1);
-        sg[u] = *reinterpret_cast<const float2 *>(q + ec);
-        tau[u] = *reinterpret_cast<const float2 *>(q + D + ec);
+        const float *q = slot2(m + u < nch ? m + u : nch - 1);
+        sg[u] = q[ec];
+        tau[u] = q[D + ec];
       }
+      // walk the batch in registers up to the first chunk whose sigma differs anywhere in the slice
+      int bad = kCombineBatch;
 #pragma unroll
       for (int u = 0; u < kCombineBatch; ++u) {
-        const int32_t m = m0 + u;
-        if (m >= nch) break;
-        const bool ok = !act || (__float_as_uint(sg[u].x) == __float_as_uint(cur.x) &&
-                                 __float_as_uint(sg[u].y) == __float_as_uint(cur.y));
-        if (__ballot(!ok) == 0ull) {
-          cur = tau[u];
-          continue;
+        const bool eq = !act || __float_as_uint(sg[u]) == __float_as_uint(cur);
+        const bool all = __ballot(!eq) == 0ull;
+        if (bad == kCombineBatch && m + u < nch) {
+          if (all) cur = tau[u];
+          else bad = u;
         }
-        // a speculative start differs in this slice: recompute the chunk from the exact state
-        const int32_t c0 = s + m * L;
-        const int32_t c1 = c0 + L < end ? c0 + L : end;
-        slice_run(vals, spos, c0, c1, D, e, [&](int32_t, float2 x) { cur = ema2(cur, x, a, b); });
       }
+      if (bad == kCombineBatch) {
+        m += kCombineBatch;
+        continue;
+      }
+      // chunk m + bad started from a wrong state in this slice: recompute it from the exact state
+      const int32_t c0 = s + (m + bad) * L;
+      const int32_t c1 = c0 + L < end ? c0 + L : end;
+      slice_run(vals, spos, c0, c1, D, e, [&](int32_t, float x) { cur = ema1(cur, x, a, b); });
+      m += bad + 1;
     }
-    if (act) *reinterpret_cast<float2 *>(table + skey[s] * D + e) = cur;
+    if (act) table[skey[s] * D + e] = cur;
   }
 }
 
@@ -198,7 +215,7 @@ void ema_launch(float *table, const float *vals, SegWork<uint32_t> &w, int cur, 
   int grid = grid_for(w.n, 4 * 4);
   if (grid > 4096) grid = 4096;
   ema_light<NC><<<grid, kThreads, 0, s>>>(reinterpret_cast<float4 *>(table), reinterpret_cast<const float4 *>(vals),
-                                          w.k[cur], w.v[cur], w.seg_start, w.seg_end, w.nseg, a, b, v4, L, w.ticket,
+                                          w.seg_key, w.v[cur], w.seg_start, w.seg_end, w.nseg, a, b, v4, L, w.ticket,
                                           w.hlist, w.clist);
   int gh = grid_for(w.n / 32 * num_slices(dim), 4);
   if (gh > 2048) gh = 2048;

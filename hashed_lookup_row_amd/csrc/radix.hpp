@@ -17,6 +17,7 @@ namespace {
 constexpr int kSortThreads = 256;
 constexpr int kMaxSortItems = 16;                      // elements per thread, at most
 constexpr int kMaxDigitBits = 8;
+constexpr int kPosPad = 128;  // slack after the position buffers: batched reads may run past n
 constexpr int kMaxBins = 1 << kMaxDigitBits;           // one digit per thread in the offset scan
 
 // Elements per thread: tiles of 1024..4096 so that a sort runs about 64 tiles.
@@ -66,6 +67,7 @@ struct SegWork {
   int32_t *segidx;   // [n]   segment of each sorted element (-1: excluded)
   int32_t *seg_start;  // [n]
   int32_t *seg_end;    // [n]
+  K *seg_key;          // [n]   key of each segment (row grouping only)
   int64_t *nseg;       // [1]
   int2 *hlist;         // heavy work units (segment, run), built by the light kernel
   int32_t *clist;      // segments with more than one run (combined after the heavy kernel)
@@ -83,14 +85,15 @@ inline size_t segwork_layout(int64_t n, SegWork<K> *w, void *base) {
   const size_t nn = static_cast<size_t>(n > 0 ? n : 1);
   w->k[0] = c.take<K>(nn);
   w->k[1] = c.take<K>(nn);
-  w->v[0] = c.take<uint32_t>(nn);
-  w->v[1] = c.take<uint32_t>(nn);
+  w->v[0] = c.take<uint32_t>(nn + kPosPad);
+  w->v[1] = c.take<uint32_t>(nn + kPosPad);
   w->counts = c.take<uint32_t>(static_cast<size_t>(kMaxBins) * (nb > 0 ? nb : 1));
   w->ticket = c.take<uint32_t>(4);
   w->bcount = c.take<uint32_t>(2 * static_cast<size_t>(nb > 0 ? nb : 1));
   w->segidx = c.take<int32_t>(nn);
   w->seg_start = c.take<int32_t>(nn);
   w->seg_end = c.take<int32_t>(nn);
+  w->seg_key = c.take<K>(nn);
   w->nseg = c.take<int64_t>(1);
   w->hlist = c.take<int2>(nn / 32 + 64);
   w->clist = c.take<int32_t>(nn / 256 + 64);
@@ -217,38 +220,68 @@ __global__ void __launch_bounds__(kSortThreads)
   }
 }
 
-// Segment pass 1: number of segment heads per tile.  Elements whose key equals
+// Segment passes.  A tile of 256 * ITEMS sorted elements is read as ITEMS
+// chunks of 256 consecutive elements (thread t takes element t of each chunk),
+// so every load is coalesced; heads (an element whose key differs from its
+// predecessor's) are counted with wave ballots.  Elements whose key equals
 // `excluded` belong to no segment.
-template <typename K>
-__global__ void __launch_bounds__(kSortThreads)
-    seg_count_kernel(const K *__restrict__ keys, int64_t n, K excluded, bool use_excluded, uint32_t *bcount,
-                     int items) {
-  __shared__ uint32_t sh[kSortThreads];
-  const int64_t base = static_cast<int64_t>(blockIdx.x) * kSortThreads * items + threadIdx.x * items;
-  uint32_t c = 0;
-  for (int i = 0; i < items; ++i) {
-    const int64_t j = base + i;
-    if (j < n) {
-      const K k = keys[j];
-      const bool ok = !(use_excluded && k == excluded);
-      const bool head = ok && (j == 0 || keys[j - 1] != k);
-      c += head ? 1u : 0u;
-    }
+template <typename K, int ITEMS>
+__device__ __forceinline__ void seg_heads(const K *__restrict__ keys, int64_t n, K excluded, bool use_excluded,
+                                          K (&kk)[ITEMS], bool (&head)[ITEMS], bool (&tail)[ITEMS],
+                                          bool (&ok)[ITEMS]) {
+  const int64_t base = static_cast<int64_t>(blockIdx.x) * kSortThreads * ITEMS + threadIdx.x;
+  K prev[ITEMS], next[ITEMS];
+#pragma unroll
+  for (int i = 0; i < ITEMS; ++i) {
+    const int64_t j = base + i * kSortThreads;
+    kk[i] = j < n ? keys[j] : K(0);
+    prev[i] = (j > 0 && j < n) ? keys[j - 1] : K(0);
+    next[i] = j + 1 < n ? keys[j + 1] : K(0);
   }
-  uint32_t tot;
-  block_exclusive_scan(c, sh, &tot);
-  if (threadIdx.x == 0) bcount[blockIdx.x] = tot;
+#pragma unroll
+  for (int i = 0; i < ITEMS; ++i) {
+    const int64_t j = base + i * kSortThreads;
+    ok[i] = j < n && !(use_excluded && kk[i] == excluded);
+    head[i] = ok[i] && (j == 0 || prev[i] != kk[i]);
+    tail[i] = ok[i] && (j == n - 1 || next[i] != kk[i]);
+  }
+}
+
+// Segment pass 1: number of segment heads per tile.
+template <typename K, int ITEMS>
+__global__ void __launch_bounds__(kSortThreads)
+    seg_count_kernel(const K *__restrict__ keys, int64_t n, K excluded, bool use_excluded, uint32_t *bcount) {
+  __shared__ uint32_t wsum[kSortThreads / hlr::kWave];
+  K kk[ITEMS];
+  bool head[ITEMS], tail[ITEMS], ok[ITEMS];
+  seg_heads<K, ITEMS>(keys, n, excluded, use_excluded, kk, head, tail, ok);
+  uint32_t c = 0;
+#pragma unroll
+  for (int i = 0; i < ITEMS; ++i) c += static_cast<uint32_t>(__popcll(hlr::ballot(head[i])));
+  const int w = threadIdx.x / hlr::kWave;
+  if (hlr::lane_id() == 0) wsum[w] = c;
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    uint32_t t = 0;
+    for (int q = 0; q < kSortThreads / hlr::kWave; ++q) t += wsum[q];
+    bcount[blockIdx.x] = t;
+  }
 }
 
 // Segment pass 2: per sorted element its segment index; heads and tails record
-// the segment bounds.  The functor `emit(j, seg, head, tail, key, val)` adds
-// mode-specific outputs (dedup: unique keys, last positions, inverse).
-template <typename K, typename Emit>
+// the segment bounds (and, when seg_key is given, the segment's key).  The
+// functor `emit(j, seg, head, tail, key, val)` adds mode-specific outputs
+// (dedup: unique keys, last positions, inverse).  A head's segment index is
+// the number of heads before it: earlier tiles (from bcount), earlier chunks
+// and waves of this tile (per-wave ballot counts in LDS), earlier lanes.
+template <typename K, typename Emit, int ITEMS>
 __global__ void __launch_bounds__(kSortThreads)
     seg_index_kernel(const K *__restrict__ keys, const uint32_t *__restrict__ vals, int64_t n, K excluded,
                      bool use_excluded, const uint32_t *__restrict__ bcount, int nblocks, int32_t *segidx,
-                     int32_t *seg_start, int32_t *seg_end, int64_t *nseg, Emit emit, int items) {
+                     int32_t *seg_start, int32_t *seg_end, K *seg_key, int64_t *nseg, Emit emit) {
+  constexpr int NW = kSortThreads / hlr::kWave;
   __shared__ uint32_t sh[kSortThreads];
+  __shared__ uint32_t wcnt[ITEMS][NW];
   __shared__ uint32_t blk_off;
   // This tile's first segment index = heads in earlier tiles; tile 0 also publishes the total.
   {
@@ -259,43 +292,53 @@ __global__ void __launch_bounds__(kSortThreads)
       total += v;
     }
     uint32_t all;
-    const uint32_t bsum = block_exclusive_scan(before, sh, &all);
-    (void)bsum;
+    block_exclusive_scan(before, sh, &all);
     if (threadIdx.x == 0) blk_off = all;
     uint32_t tall;
     block_exclusive_scan(total, sh, &tall);
     if (blockIdx.x == 0 && threadIdx.x == 0) *nseg = tall;
-    __syncthreads();
   }
-  const int64_t base = static_cast<int64_t>(blockIdx.x) * kSortThreads * items + threadIdx.x * items;
-  uint32_t c = 0;
-  for (int i = 0; i < items; ++i) {
-    const int64_t j = base + i;
+  K kk[ITEMS];
+  bool head[ITEMS], tail[ITEMS], ok[ITEMS];
+  seg_heads<K, ITEMS>(keys, n, excluded, use_excluded, kk, head, tail, ok);
+  const int w = threadIdx.x / hlr::kWave;
+  const uint64_t lt = hlr::lanemask_lt();
+  uint32_t rank[ITEMS];  // heads before this element within its wave's 64 elements, this one included
+#pragma unroll
+  for (int i = 0; i < ITEMS; ++i) {
+    const uint64_t m = hlr::ballot(head[i]);
+    rank[i] = static_cast<uint32_t>(__popcll(m & lt)) + (head[i] ? 1u : 0u);
+    if (hlr::lane_id() == 0) wcnt[i][w] = static_cast<uint32_t>(__popcll(m));
+  }
+  __syncthreads();
+  uint32_t run = blk_off;  // heads before chunk i
+  const int64_t base = static_cast<int64_t>(blockIdx.x) * kSortThreads * ITEMS + threadIdx.x;
+#pragma unroll
+  for (int i = 0; i < ITEMS; ++i) {
+    uint32_t before_w = 0, chunk = 0;
+#pragma unroll
+    for (int q = 0; q < NW; ++q) {
+      const uint32_t c = wcnt[i][q];
+      before_w += q < w ? c : 0u;
+      chunk += c;
+    }
+    const int64_t j = base + i * kSortThreads;
     if (j < n) {
-      const K k = keys[j];
-      const bool ok = !(use_excluded && k == excluded);
-      c += (ok && (j == 0 || keys[j - 1] != k)) ? 1u : 0u;
+      if (!ok[i]) {
+        segidx[j] = -1;
+      } else {
+        // the segment this element belongs to: heads up to and including it, minus one
+        const int32_t seg = static_cast<int32_t>(run + before_w + rank[i]) - 1;
+        segidx[j] = seg;
+        if (head[i]) {
+          seg_start[seg] = static_cast<int32_t>(j);
+          if (seg_key) seg_key[seg] = kk[i];
+        }
+        if (tail[i]) seg_end[seg] = static_cast<int32_t>(j + 1);
+        emit(j, seg, head[i], tail[i], kk[i], vals[j]);
+      }
     }
-  }
-  uint32_t tot;
-  uint32_t run = block_exclusive_scan(c, sh, &tot) + blk_off;
-  for (int i = 0; i < items; ++i) {
-    const int64_t j = base + i;
-    if (j >= n) break;
-    const K k = keys[j];
-    const bool ok = !(use_excluded && k == excluded);
-    if (!ok) {
-      segidx[j] = -1;
-      continue;
-    }
-    const bool head = (j == 0 || keys[j - 1] != k);
-    const bool tail = (j == n - 1 || keys[j + 1] != k);
-    if (head) ++run;
-    const int32_t seg = static_cast<int32_t>(run) - 1;
-    segidx[j] = seg;
-    if (head) seg_start[seg] = static_cast<int32_t>(j);
-    if (tail) seg_end[seg] = static_cast<int32_t>(j + 1);
-    emit(j, seg, head, tail, k, vals[j]);
+    run += chunk;
   }
 }
 
@@ -327,12 +370,21 @@ inline int radix_sort_pairs(SegWork<K> &w, int total_bits, hipStream_t s) {
   return radix_sort_pairs_t<K, 16>(w, total_bits, s);
 }
 
+template <typename K, typename Emit, int ITEMS>
+inline void segment_sorted_t(SegWork<K> &w, int cur, K excluded, bool use_excluded, K *seg_key, Emit emit,
+                             hipStream_t s) {
+  seg_count_kernel<K, ITEMS><<<w.nblocks, kSortThreads, 0, s>>>(w.k[cur], w.n, excluded, use_excluded, w.bcount);
+  seg_index_kernel<K, Emit, ITEMS><<<w.nblocks, kSortThreads, 0, s>>>(
+      w.k[cur], w.v[cur], w.n, excluded, use_excluded, w.bcount, w.nblocks, w.segidx, w.seg_start, w.seg_end,
+      seg_key, w.nseg, emit);
+}
+
 template <typename K, typename Emit>
-inline void segment_sorted(SegWork<K> &w, int cur, K excluded, bool use_excluded, Emit emit, hipStream_t s) {
-  seg_count_kernel<K><<<w.nblocks, kSortThreads, 0, s>>>(w.k[cur], w.n, excluded, use_excluded, w.bcount, w.items);
-  seg_index_kernel<K, Emit><<<w.nblocks, kSortThreads, 0, s>>>(w.k[cur], w.v[cur], w.n, excluded, use_excluded,
-                                                                w.bcount, w.nblocks, w.segidx, w.seg_start,
-                                                                w.seg_end, w.nseg, emit, w.items);
+inline void segment_sorted(SegWork<K> &w, int cur, K excluded, bool use_excluded, K *seg_key, Emit emit,
+                           hipStream_t s) {
+  if (w.items == 4) segment_sorted_t<K, Emit, 4>(w, cur, excluded, use_excluded, seg_key, emit, s);
+  else if (w.items == 8) segment_sorted_t<K, Emit, 8>(w, cur, excluded, use_excluded, seg_key, emit, s);
+  else segment_sorted_t<K, Emit, 16>(w, cur, excluded, use_excluded, seg_key, emit, s);
 }
 
 }  // namespace
@@ -368,7 +420,7 @@ inline int group_by_row(SegWork<uint32_t> &w, const int64_t *rows, const uint8_t
   rowkey_init<<<hlr::grid_for(w.n, 256), 256, 0, s>>>(rows, mask, w.n, num_rows, w.k[0], w.v[0], w.ticket);
   const int bits = bit_width_u64(static_cast<uint64_t>(num_rows));
   const int cur = radix_sort_pairs<uint32_t>(w, bits, s);
-  segment_sorted<uint32_t>(w, cur, static_cast<uint32_t>(num_rows), true, NoEmit{}, s);
+  segment_sorted<uint32_t>(w, cur, static_cast<uint32_t>(num_rows), true, w.seg_key, NoEmit{}, s);
   return cur;
 }
 
@@ -389,42 +441,52 @@ __device__ __forceinline__ int64_t run_slot(int32_t j0, int32_t m, int B) {
 namespace {
 
 // Heavy rows are processed as independent wave work items, one per (run, slice):
-// a slice is 128 consecutive elements of the row (lanes own 2 each, float2), so a
-// row of D elements has ceil(D / 128) slices and every slice of every run is
-// its own wave.  slice_run() applies f(j, x) to positions j in [j0, j1) in order.
-// Loads go out kSlicePrefetch positions at a time, all issued before any is
-// used: the position indices first (wave-uniform, so scalar loads), then the
-// rows, with no per-lane condition on either (lanes past the end of the row
+// a slice is kSliceElems consecutive elements of the row (lanes own one each),
+// so a row of D elements has ceil(D / kSliceElems) slices and every slice of
+// every run is its own wave.  slice_run() applies f(j, x) to positions j in
+// [j0, j1) in order.  Positions go in batches of kSlicePrefetch: the rows of a
+// batch are requested together (one 256-byte access per position), then the
+// position indices of the next batch, so they arrive while this batch is
+// consumed.  Indices are read with one vector load (lane u takes position
+// j + u) and broadcast with readlane, which costs no memory round trip of its
+// own.  No row load has a per-lane condition: lanes past the end of the row
 // read element 0 and their results are dropped by the caller; positions past
-// j1 in the last batch re-read position j1 - 1 and are not applied).
-constexpr int kSliceElems = 128;
-constexpr int kSlicePrefetch = 32;
+// j1 in the last batch re-read position j1 - 1 and are not applied.
+using SliceV = float;
+constexpr int kSliceElems = 64;
+constexpr int kSlicePrefetch = 48;
+static_assert(kSlicePrefetch <= 64, "one index per lane");
 
 __host__ __device__ __forceinline__ int64_t num_slices(int64_t D) { return (D + kSliceElems - 1) / kSliceElems; }
+
+// This lane's index of the batch at j (lanes >= P repeat the last of the batch).
+template <int P>
+__device__ __forceinline__ uint32_t slice_idx(const uint32_t *__restrict__ spos, int32_t j, int32_t j1) {
+  const int l = hlr::lane_id();
+  const int32_t jj = j + (l < P ? l : P - 1);
+  return spos[jj < j1 ? jj : j1 - 1];
+}
 
 template <typename F>
 __device__ __forceinline__ void slice_run(const float *__restrict__ src, const uint32_t *__restrict__ spos, int32_t j0,
                                           int32_t j1, int64_t D, int64_t e, F f) {
+  constexpr int P = kSlicePrefetch;
   const int64_t ec = e < D ? e : 0;
   j0 = __builtin_amdgcn_readfirstlane(j0);
   j1 = __builtin_amdgcn_readfirstlane(j1);
   if (j0 >= j1) return;
-  // the indices of the next batch load while this batch's rows are in flight
-  uint32_t pn[kSlicePrefetch];
+  uint32_t pv = slice_idx<P>(spos, j0, j1);
+  for (int32_t j = j0; j < j1; j += P) {
+    SliceV x[P];
 #pragma unroll
-  for (int u = 0; u < kSlicePrefetch; ++u) pn[u] = spos[j0 + u < j1 ? j0 + u : j1 - 1];
-  for (int32_t j = j0; j < j1; j += kSlicePrefetch) {
-    float2 x[kSlicePrefetch];
-#pragma unroll
-    for (int u = 0; u < kSlicePrefetch; ++u)
-      x[u] = *reinterpret_cast<const float2 *>(src + static_cast<int64_t>(pn[u]) * D + ec);
-    const int32_t jn = j + kSlicePrefetch;
-    if (jn < j1) {
-#pragma unroll
-      for (int u = 0; u < kSlicePrefetch; ++u) pn[u] = spos[jn + u < j1 ? jn + u : j1 - 1];
+    for (int u = 0; u < P; ++u) {
+      const uint32_t p = __builtin_amdgcn_readlane(pv, u);
+      x[u] = src[static_cast<int64_t>(p) * D + ec];
     }
+    pv = slice_idx<P>(spos, j + P, j1);  // next batch's indices, behind this batch's rows
+    __builtin_amdgcn_sched_barrier(0);     // keep both requests ahead of the consumption below
 #pragma unroll
-    for (int u = 0; u < kSlicePrefetch; ++u)
+    for (int u = 0; u < P; ++u)
       if (j + u < j1) f(j + u, x[u]);
   }
 }
@@ -432,16 +494,16 @@ __device__ __forceinline__ void slice_run(const float *__restrict__ src, const u
 // Same, over rows given by an index function (partial results).
 template <typename RowOf, typename F>
 __device__ __forceinline__ void slice_run_rows(RowOf row_of, int32_t j0, int32_t j1, int64_t D, int64_t e, F f) {
+  constexpr int P = 32;
   const int64_t ec = e < D ? e : 0;
   j0 = __builtin_amdgcn_readfirstlane(j0);
   j1 = __builtin_amdgcn_readfirstlane(j1);
-  for (int32_t j = j0; j < j1; j += kSlicePrefetch) {
-    float2 x[kSlicePrefetch];
+  for (int32_t j = j0; j < j1; j += P) {
+    SliceV x[P];
 #pragma unroll
-    for (int u = 0; u < kSlicePrefetch; ++u)
-      x[u] = *reinterpret_cast<const float2 *>(row_of(j + u < j1 ? j + u : j1 - 1) + ec);
+    for (int u = 0; u < P; ++u) x[u] = row_of(j + u < j1 ? j + u : j1 - 1)[ec];
 #pragma unroll
-    for (int u = 0; u < kSlicePrefetch; ++u)
+    for (int u = 0; u < P; ++u)
       if (j + u < j1) f(j + u, x[u]);
   }
 }
@@ -472,10 +534,13 @@ __device__ __forceinline__ void rows_run(const float4 *__restrict__ src, const u
 #pragma unroll
     for (int u = 0; u < P; ++u) f(j + u, x[u]);
   }
+  const uint32_t last = j < j1 ? spos[j1 - 1] : 0u;
   for (; j < j1; j += 4) {
     int64_t p[4];
 #pragma unroll
-    for (int u = 0; u < 4; ++u) p[u] = static_cast<int64_t>(spos[j + u < j1 ? j + u : j1 - 1]) * v4;
+    for (int u = 0; u < 4; ++u) p[u] = spos[j + u];  // within the buffer's slack past n
+#pragma unroll
+    for (int u = 0; u < 4; ++u) p[u] = static_cast<int64_t>(j + u < j1 ? static_cast<uint32_t>(p[u]) : last) * v4;
     float4 x[4][NC];
 #pragma unroll
     for (int u = 0; u < 4; ++u)

@@ -187,16 +187,14 @@ __global__ void __launch_bounds__(kThreads)
 constexpr int kRun = HLR_SGD_SUM_RUN;
 
 template <int NC>
-constexpr int light_batch() { return NC == 1 ? 16 : (NC == 2 ? 8 : 4); }
+constexpr int light_batch() { return NC == 4 ? 4 : 8; }
 
 __device__ __forceinline__ float4 l2_grad(float4 m, float4 e) {
   const float4 d = f4_sub(m, e);
   return make_float4(2.f * d.x, 2.f * d.y, 2.f * d.z, 2.f * d.w);
 }
 
-__device__ __forceinline__ float2 l2_grad(float2 m, float2 e) {
-  return make_float2(2.f * (m.x - e.x), 2.f * (m.y - e.y));
-}
+__device__ __forceinline__ float l2_grad(float m, float e) { return 2.f * (m - e); }
 
 template <int NC, bool L2>
 __device__ __forceinline__ void sum_run(const float4 *__restrict__ g, const uint32_t *__restrict__ spos, int32_t j0,
@@ -212,49 +210,60 @@ __device__ __forceinline__ void sum_run(const float4 *__restrict__ g, const uint
 
 // Light rows (fewer than kHeavyMin occurrences, hence one run): one wave per
 // row; the row is read once, before its gradients, and written once:
-// fl(M - fl(lr * s)).  Longer rows are registered for the slice kernels.
+// fl(M - fl(lr * s)).  Longer rows are registered for the slice kernels.  A
+// wave walks rows k, k + waves, ...; the next row's (start, end, row) is
+// loaded while the current row is processed (wave-uniform, so scalar loads).
 template <int NC, bool L2>
 __global__ void __launch_bounds__(kThreads)
-    sgd_light(float4 *table, const float4 *__restrict__ g, const uint32_t *__restrict__ skey,
+    sgd_light(float4 *table, const float4 *__restrict__ g, const uint32_t *__restrict__ seg_key,
               const uint32_t *__restrict__ spos, const int32_t *__restrict__ seg_start,
               const int32_t *__restrict__ seg_end, const int64_t *__restrict__ nseg_p, float lr, int64_t v4,
               uint32_t *counters, int2 *hlist, int32_t *clist) {
   const int64_t nseg = *nseg_p;
   const int64_t waves = static_cast<int64_t>(gridDim.x) * (kThreads / kWave);
   const int lane = lane_id();
-  for (int64_t k = (static_cast<int64_t>(blockIdx.x) * kThreads + threadIdx.x) / kWave; k < nseg; k += waves) {
-    const int32_t s = seg_start[k], e = seg_end[k];
+  int64_t k = __builtin_amdgcn_readfirstlane(static_cast<int>((blockIdx.x * kThreads + threadIdx.x) / kWave));
+  if (k >= nseg) return;
+  int32_t s = seg_start[k], e = seg_end[k];
+  int64_t r = seg_key[k];
+  for (;;) {
+    const int64_t kn = k + waves;
+    const int64_t kc = kn < nseg ? kn : nseg - 1;
+    const int32_t sn = seg_start[kc], en = seg_end[kc];
+    const int64_t rn = seg_key[kc];
     if (e - s >= kHeavyMin) {
       if (lane == 0) push_heavy(static_cast<int32_t>(k), e - s, kRun, counters, hlist, clist);
-      continue;
-    }
-    const int64_t r = skey[s];
-    float4 m[NC], run[NC];
+    } else {
+      float4 m[NC], run[NC];
 #pragma unroll
-    for (int q = 0; q < NC; ++q) {
-      const int64_t c = lane + q * kWave;
-      m[q] = table[r * v4 + (c < v4 ? c : 0)];
-    }
-    sum_run<NC, L2>(g, spos, s, e, v4, lane, m, run);
+      for (int q = 0; q < NC; ++q) {
+        const int64_t c = lane + q * kWave;
+        m[q] = table[r * v4 + (c < v4 ? c : 0)];
+      }
+      sum_run<NC, L2>(g, spos, s, e, v4, lane, m, run);
 #pragma unroll
-    for (int q = 0; q < NC; ++q) {
-      const int64_t c = lane + q * kWave;
-      const float4 st = make_float4(lr * run[q].x, lr * run[q].y, lr * run[q].z, lr * run[q].w);
-      if (c < v4) table[r * v4 + c] = f4_sub(m[q], st);  // fl(M - fl(lr * s))
+      for (int q = 0; q < NC; ++q) {
+        const int64_t c = lane + q * kWave;
+        const float4 st = make_float4(lr * run[q].x, lr * run[q].y, lr * run[q].z, lr * run[q].w);
+        if (c < v4) table[r * v4 + c] = f4_sub(m[q], st);  // fl(M - fl(lr * s))
+      }
     }
+    if (kn >= nseg) break;
+    k = kn;
+    s = sn;
+    e = en;
+    r = rn;
   }
 }
 
-__device__ __forceinline__ void sgd_write2(float *table, int64_t r, float2 acc, float lr, int64_t D, int64_t e) {
+__device__ __forceinline__ void sgd_write1(float *table, int64_t r, float acc, float lr, int64_t D, int64_t e) {
   if (e < D) {
-    float2 *w = reinterpret_cast<float2 *>(table + r * D + e);
-    const float2 m = *w;
-    const float s0 = lr * acc.x, s1 = lr * acc.y;
-    *w = make_float2(m.x - s0, m.y - s1);  // fl(M - fl(lr * s))
+    const float st = lr * acc;
+    table[r * D + e] = table[r * D + e] - st;  // fl(M - fl(lr * s))
   }
 }
 
-// Heavy rows: one wave per (run of <= 256 occurrences, 128-element slice).  A
+// Heavy rows: one wave per (run of <= 256 occurrences, 64-element slice).  A
 // row with one run is updated at once; otherwise the run total goes to
 // `partial` for sgd_combine.  No wave writes a multi-run row before the
 // combine, so the L2 gradients all see the row as it was before the batch.
@@ -269,21 +278,21 @@ __global__ void __launch_bounds__(kThreads)
   const int64_t waves = static_cast<int64_t>(gridDim.x) * (kThreads / kWave);
   for (int64_t it = (static_cast<int64_t>(blockIdx.x) * kThreads + threadIdx.x) / kWave; it < items; it += waves) {
     const int2 km = hlist[it / S];
-    const int64_t e = (it % S) * kSliceElems + 2 * lane_id();
+    const int64_t e = (it % S) * kSliceElems + lane_id();
     const int32_t s = seg_start[km.x], end = seg_end[km.x];
     const int32_t j0 = s + km.y * kRun;
     const int32_t j1 = j0 + kRun < end ? j0 + kRun : end;
-    float2 mv = make_float2(0.f, 0.f);
-    if (L2) mv = *reinterpret_cast<const float2 *>(table + static_cast<int64_t>(skey[s]) * D + (e < D ? e : 0));
-    float2 acc = make_float2(0.f, 0.f);
-    slice_run(g, spos, j0, j1, D, e, [&](int32_t j, float2 x) {
-      const float2 y = L2 ? l2_grad(mv, x) : x;
-      acc = j == j0 ? y : make_float2(acc.x + y.x, acc.y + y.y);
+    float mv = 0.f;
+    if (L2) mv = table[static_cast<int64_t>(skey[s]) * D + (e < D ? e : 0)];
+    float acc = 0.f;
+    slice_run(g, spos, j0, j1, D, e, [&](int32_t j, float x) {
+      const float y = L2 ? l2_grad(mv, x) : x;
+      acc = j == j0 ? y : acc + y;
     });
     if (end - s <= kRun) {
-      sgd_write2(table, skey[s], acc, lr, D, e);
+      sgd_write1(table, skey[s], acc, lr, D, e);
     } else if (e < D) {
-      *reinterpret_cast<float2 *>(partial + run_slot(j0, km.y, kRun) * D + e) = acc;
+      partial[run_slot(j0, km.y, kRun) * D + e] = acc;
     }
   }
 }
@@ -299,13 +308,13 @@ __global__ void __launch_bounds__(kThreads)
   const int64_t waves = static_cast<int64_t>(gridDim.x) * (kThreads / kWave);
   for (int64_t it = (static_cast<int64_t>(blockIdx.x) * kThreads + threadIdx.x) / kWave; it < items; it += waves) {
     const int32_t k = clist[it / S];
-    const int64_t e = (it % S) * kSliceElems + 2 * lane_id();
+    const int64_t e = (it % S) * kSliceElems + lane_id();
     const int32_t s = seg_start[k], end = seg_end[k];
     const int32_t nruns = (end - s + kRun - 1) / kRun;
-    float2 acc = make_float2(0.f, 0.f);
+    float acc = 0.f;
     slice_run_rows([&](int32_t m) { return partial + run_slot(s + m * kRun, m, kRun) * D; }, 0, nruns, D, e,
-                   [&](int32_t m, float2 x) { acc = m == 0 ? x : make_float2(acc.x + x.x, acc.y + x.y); });
-    sgd_write2(table, skey[s], acc, lr, D, e);
+                   [&](int32_t m, float x) { acc = m == 0 ? x : acc + x; });
+    sgd_write1(table, skey[s], acc, lr, D, e);
   }
 }
 
@@ -320,7 +329,7 @@ void sgd_launch(float *table, const float *g, SegWork<uint32_t> &w, int cur, flo
   int grid = grid_for(w.n, 4 * 4);
   if (grid > 4096) grid = 4096;
   sgd_light<NC, L2><<<grid, kThreads, 0, s>>>(reinterpret_cast<float4 *>(table), reinterpret_cast<const float4 *>(g),
-                                              w.k[cur], w.v[cur], w.seg_start, w.seg_end, w.nseg, lr, v4, w.ticket,
+                                              w.seg_key, w.v[cur], w.seg_start, w.seg_end, w.nseg, lr, v4, w.ticket,
                                               w.hlist, w.clist);
   int gh = grid_for(w.n / 32 * num_slices(dim), 4);
   if (gh > 2048) gh = 2048;
