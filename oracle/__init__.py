@@ -34,7 +34,7 @@ def build(force: bool = True) -> str:
     """Compile oracle.c into liboracle.so with gcc (no FMA contraction, no fast-math)."""
     if force or not os.path.exists(_LIB) or os.path.getmtime(_LIB) < os.path.getmtime(_SRC):
         tmp = _LIB + ".tmp%d" % os.getpid()
-        cmd = ["gcc", "-O2", "-std=c11", "-ffp-contract=off", "-fno-fast-math", "-fPIC", "-shared", _SRC, "-o", tmp]
+        cmd = ["gcc", "-O2", "-std=c11", "-ffp-contract=off", "-fno-fast-math", "-fPIC", "-shared", _SRC, "-o", tmp, "-lm"]
         subprocess.check_call(cmd)
         os.replace(tmp, _LIB)
     return _LIB
@@ -63,6 +63,8 @@ def _load():
             lib.orc_sgd_sum.argtypes = [p, i64, i64, p, p, i64, ctypes.c_float]
             lib.orc_l2_align.restype = ctypes.c_int
             lib.orc_l2_align.argtypes = [p, i64, i64, p, p, i64, ctypes.c_float]
+            lib.orc_quantize_rows.restype = ctypes.c_int
+            lib.orc_quantize_rows.argtypes = [p, i64, i64, p, i64, i64, i32, p, p, p]
             lib.orc_ema.restype = ctypes.c_int
             lib.orc_ema.argtypes = [p, i64, i64, p, p, p, i64, ctypes.c_float, ctypes.c_float]
             lib.orc_dequant_score.restype = ctypes.c_int
@@ -188,6 +190,21 @@ def l2_align(table, rows, e, lr):
     e = _c(e, np.float32)
     _check(_load().orc_l2_align(_ptr(table), table.shape[0], table.shape[1], _ptr(rows), _ptr(e), rows.size,
                                 ctypes.c_float(lr)), "l2_align")
+
+
+def quantize_rows(table, rows, count=-1, scatter=False, out=None):
+    """int8 per-row min-max quantisation of table[rows[i]].  Returns (q, scale, bias):
+    compact (index i) or, with scatter=True, written at index rows[i] of `out` = (q, scale, bias)."""
+    assert table.dtype == np.float32 and table.flags.c_contiguous
+    rows = _c(rows, np.int64)
+    dim = table.shape[1]
+    if out is None:
+        m = table.shape[0] if scatter else rows.size
+        out = (np.zeros((m, dim), np.int8), np.zeros(m, np.float32), np.zeros(m, np.float32))
+    q, sc, bi = out
+    _check(_load().orc_quantize_rows(_ptr(table), table.shape[0], dim, _ptr(rows), rows.size, int(count),
+                                     1 if scatter else 0, _ptr(q), _ptr(sc), _ptr(bi)), "quantize_rows")
+    return q, sc, bi
 
 
 def ema(table, rows, vals, mask, a, b):

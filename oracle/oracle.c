@@ -50,6 +50,7 @@
  *  - dequant-score is evaluated in fp64: x_d = q_d*scale + bias,
  *    score = sum_d x_d*u_d, rounded once to fp32; a miss scores exactly 0.
  */
+#include <math.h>
 #include <stdint.h>
 #include <stdlib.h>
 #include <string.h>
@@ -344,6 +345,58 @@ int orc_ema(float *table, int64_t num_rows, int64_t dim, const int64_t *rows, co
             const float y = b * v[d];
             t[d] = x + y;
         }
+    }
+    return ORC_OK;
+}
+
+/* ------------------------------------- int8 row quantisation [ML] sec. 2, 5 */
+/*
+ * Raw Embedding Streaming quantises the rows a step touched before they are
+ * published to serving, and serving reads int8 rows ([ML] sec. 2 and sec. 5).
+ * Per row, asymmetric min-max over the row's fp32 values, each operation
+ * rounded in fp32:
+ *   scale = fl(fl(max - min) / 255), or 1 when max == min;
+ *   bias  = fl(min + fl(128 * scale));
+ *   q_d   = clamp(rne(fl(fl(x_d - bias) / scale)), -128, 127),
+ * so q_d * scale + bias dequantises back to within about scale / 2.
+ * Output i receives row rows[i] (scatter == 0: out index i; scatter == 1: out
+ * index rows[i]).  rows[i] == -1 writes q = 0, scale = 0, bias = 0 in the
+ * compact form and nothing in the scatter form.  Only the first min(n, count)
+ * entries are used (count < 0: n).
+ */
+int orc_quantize_rows(const float *table, int64_t num_rows, int64_t dim, const int64_t *rows, int64_t n,
+                      int64_t count, int32_t scatter, int8_t *out_q, float *out_scale, float *out_bias) {
+    const int64_t m = (count >= 0 && count < n) ? count : n;
+    for (int64_t i = 0; i < m; ++i)
+        if (rows[i] < -1 || rows[i] >= num_rows) return ORC_EINVAL;
+    for (int64_t i = 0; i < m; ++i) {
+        const int64_t r = rows[i];
+        if (r < 0) {
+            if (!scatter) {
+                memset(out_q + i * dim, 0, (size_t)dim);
+                out_scale[i] = 0.0f;
+                out_bias[i] = 0.0f;
+            }
+            continue;
+        }
+        const int64_t o = scatter ? r : i;
+        const float *x = table + r * dim;
+        float lo = x[0], hi = x[0];
+        for (int64_t d = 1; d < dim; ++d) {
+            if (x[d] < lo) lo = x[d];
+            if (x[d] > hi) hi = x[d];
+        }
+        const float range = hi - lo;
+        const float scale = (range == 0.0f) ? 1.0f : range / 255.0f;
+        const float offset = 128.0f * scale;
+        const float bias = lo + offset;
+        for (int64_t d = 0; d < dim; ++d) {
+            const float centred = x[d] - bias;
+            const float v = rintf(centred / scale);
+            out_q[o * dim + d] = (int8_t)(v < -128.0f ? -128.0f : (v > 127.0f ? 127.0f : v));
+        }
+        out_scale[o] = scale;
+        out_bias[o] = bias;
     }
     return ORC_OK;
 }

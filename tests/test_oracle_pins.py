@@ -395,6 +395,55 @@ def test_l2_align_duplicates_at_matching_rate_assign_e():
         assert np.array_equal(table[0], e[0]) and np.array_equal(table[1], np.full(4, 9.0, np.float32))
 
 
+# ------------------------------------------------------- int8 quantisation
+def test_quantize_integer_grid_is_exact():
+    """min 0 and max 255 give scale 1 and bias 128, so integer values map to x - 128 exactly; scaling
+    the row by a power of two scales scale and bias by it and leaves the codes unchanged."""
+    g = np.random.default_rng(31)
+    vals = g.integers(0, 256, size=(3, 40)).astype(np.float32)
+    vals[:, 0], vals[:, 1] = 0.0, 255.0
+    for k in (0, 3, -5):
+        t = (vals * np.float32(2.0 ** k)).astype(np.float32)
+        q, sc, bi = oracle.quantize_rows(t, np.arange(3))
+        assert np.array_equal(q.astype(np.int64), vals.astype(np.int64) - 128)
+        assert np.all(sc == np.float32(2.0 ** k)) and np.all(bi == np.float32(128 * 2.0 ** k))
+
+
+def test_quantize_constant_row_and_ties_to_even():
+    t = np.full((1, 8), -3.25, np.float32)
+    q, sc, bi = oracle.quantize_rows(t, np.array([0]))
+    assert sc[0] == 1.0 and bi[0] == np.float32(-3.25 + 128) and np.all(q == -128)
+    assert q[0, 0] * sc[0] + bi[0] == np.float32(-3.25)  # dequantises exactly
+    # scale 1, bias 128: x = 3.5 -> -124.5 -> -124 (even); 4.5 -> -123.5 -> -124; 5.5 -> -122.5 -> -122
+    row = np.array([[0.0, 255.0, 3.5, 4.5, 5.5, 6.5]], np.float32)
+    q, _, _ = oracle.quantize_rows(row, np.array([0]))
+    assert q[0].tolist() == [-128, 127, -124, -124, -122, -122]
+
+
+def test_quantize_round_trip_bound_and_layouts():
+    """|q*scale + bias - x| <= scale/2 up to a few ulps for every value; codes span [-128, 127]; the
+    scatter form writes row r's codes at index r; rows of -1 and the count limit are honoured."""
+    g = np.random.default_rng(32)
+    t = (g.standard_normal((50, 64)) * g.uniform(0.01, 10, size=(50, 1))).astype(np.float32)
+    rows = np.array([7, 3, -1, 49, 7, 0], np.int64)
+    q, sc, bi = oracle.quantize_rows(t, rows)
+    for i, r in enumerate(rows):
+        if r < 0:
+            assert not q[i].any() and sc[i] == 0 and bi[i] == 0
+            continue
+        deq = q[i].astype(np.float64) * sc[i] + bi[i]
+        assert np.all(np.abs(deq - t[r]) <= 0.5 * sc[i] * (1 + 1e-5) + 4 * np.spacing(np.abs(t[r]).max()))
+        assert q[i].min() == -128 and q[i].max() == 127
+    out = (np.zeros((50, 64), np.int8), np.zeros(50, np.float32), np.zeros(50, np.float32))
+    oracle.quantize_rows(t, rows, scatter=True, out=out)
+    for i, r in enumerate(rows):
+        if r >= 0:
+            assert np.array_equal(out[0][r], q[i]) and out[1][r] == sc[i] and out[2][r] == bi[i]
+    assert not out[0][1].any()  # untouched rows stay as they were
+    q2, _, _ = oracle.quantize_rows(t, rows, count=2)
+    assert np.array_equal(q2[:2], q[:2]) and not q2[2:].any()
+
+
 # -------------------------------------------------------------------- EMA
 def test_ema_special_cases():
     g = np.random.default_rng(2)
