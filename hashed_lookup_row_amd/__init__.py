@@ -65,6 +65,10 @@ def load_library():
             "writeback_apply": (i32, [p, i64, i64, p, i64, i32, f32, p, sz, p]),
             "ema_update_plan": (i32, [i64, p, p, i64, p, sz, p]),
             "ema_update_apply": (i32, [p, i64, i64, p, i64, f32, f32, p, sz, p]),
+            "writeback_plan_rows": (i32, [i64, i64, p, sz, p, p, p]),
+            "quantize_rows_int8": (i32, [p, i64, i64, p, i64, p, i32, p, p, p, p]),
+            "mark_rows": (i32, [p, i64, p, i64, p, p, p, p]),
+            "clear_marks": (i32, [p, p, i64, p, p]),
         }
         for name, (res, args) in sig.items():
             f = getattr(lib, name)
@@ -79,7 +83,7 @@ def exported_symbols():
             "gather_rows", "dedup_ids_workspace_size", "dedup_ids", "writeback_rows_workspace_size",
             "writeback_rows", "ema_update_rows_workspace_size", "ema_update_rows", "gather_dequant_score",
             "hashed_rows", "mpzch_zero_inserted", "writeback_plan", "writeback_apply", "ema_update_plan",
-            "ema_update_apply"]
+            "ema_update_apply", "writeback_plan_rows", "quantize_rows_int8", "mark_rows", "clear_marks"]
 
 
 def _check(rc: int, what: str):
@@ -328,3 +332,57 @@ def ema_update_apply(table, vals, a, b, ws, stream=None):
     _check(lib.ema_update_apply(_ptr(table), table.shape[0], dim, _ptr(vals), n, float(a), float(b), w, wb,
                                 _stream(table.device, stream)), "ema_update_apply")
     return table
+
+
+def writeback_plan_rows(num_rows, n, ws, out_rows=None, out_count=None, stream=None):
+    """Distinct rows of a LAST_WINS plan in `ws` (unspecified order): (rows int64[n], count int64[1])."""
+    lib = load_library()
+    dev = ws.device
+    rows = out_rows if out_rows is not None else torch.empty(max(int(n), 1), dtype=torch.int64, device=dev)
+    cnt = out_count if out_count is not None else torch.empty(1, dtype=torch.int64, device=dev)
+    w, wb = _own_ws(ws, lib.writeback_rows_workspace_size(int(num_rows), 4, int(n), WB_LAST_WINS))
+    _check(lib.writeback_plan_rows(int(num_rows), int(n), w, wb, _ptr(rows), _ptr(cnt), _stream(dev, stream)),
+           "writeback_plan_rows")
+    return rows, cnt
+
+
+def quantize_rows_int8(table, rows, count=None, scatter=False, out=None, stream=None):
+    """int8 per-row min-max quantisation of table[rows[i]] (first min(n, *count) entries).
+    Returns (q int8, scale fp32, bias fp32): compact [n] rows, or with scatter=True written at index
+    rows[i] of `out` (arrays of table.shape[0] rows; allocated zeroed if not given)."""
+    lib = load_library()
+    _dev(table, "table", torch.float32)
+    _dev(rows, "rows", torch.int64)
+    if count is not None:
+        _dev(count, "count", torch.int64)
+    dev, n, dim = table.device, rows.numel(), table.shape[1]
+    if out is None:
+        m = table.shape[0] if scatter else n
+        out = (torch.zeros((m, dim), dtype=torch.int8, device=dev), torch.zeros(m, dtype=torch.float32, device=dev),
+               torch.zeros(m, dtype=torch.float32, device=dev))
+    q, sc, bi = out
+    _check(lib.quantize_rows_int8(_ptr(table), table.shape[0], dim, _ptr(rows), n, _ptr(count), 1 if scatter else 0,
+                                  _ptr(q), _ptr(sc), _ptr(bi), _stream(dev, stream)), "quantize_rows_int8")
+    return q, sc, bi
+
+
+def mark_rows(rows, num_rows, flags, lst, list_count, count=None, stream=None):
+    """Appends the rows not yet flagged to `lst` (flags uint32[num_rows], lst int64[num_rows], list_count int64[1])."""
+    lib = load_library()
+    _dev(rows, "rows", torch.int64)
+    _dev(flags, "flags", torch.int32)
+    _dev(lst, "list", torch.int64)
+    _dev(list_count, "list_count", torch.int64)
+    if count is not None:
+        _dev(count, "count", torch.int64)
+    _check(lib.mark_rows(_ptr(rows), rows.numel(), _ptr(count), int(num_rows), _ptr(flags), _ptr(lst),
+                         _ptr(list_count), _stream(rows.device, stream)), "mark_rows")
+
+
+def clear_marks(lst, list_count, num_rows, flags, stream=None):
+    lib = load_library()
+    _dev(lst, "list", torch.int64)
+    _dev(list_count, "list_count", torch.int64)
+    _dev(flags, "flags", torch.int32)
+    _check(lib.clear_marks(_ptr(lst), _ptr(list_count), int(num_rows), _ptr(flags), _stream(lst.device, stream)),
+           "clear_marks")

@@ -20,6 +20,7 @@ class _Hip:
         self.lib.hipStreamWaitEvent.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_uint]
         self.lib.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p, ctypes.c_void_p]
         self.lib.hipEventDestroy.argtypes = [ctypes.c_void_p]
+        self.lib.hipEventSynchronize.argtypes = [ctypes.c_void_p]
 
     def event(self, timing: bool = False) -> ctypes.c_void_p:
         e = ctypes.c_void_p()
@@ -38,6 +39,11 @@ class _Hip:
         rc = self.lib.hipStreamWaitEvent(ctypes.c_void_p(stream), e, 0)
         if rc != 0:
             raise RuntimeError(f"hipStreamWaitEvent failed ({rc})")
+
+    def synchronize(self, e):
+        rc = self.lib.hipEventSynchronize(e)
+        if rc != 0:
+            raise RuntimeError(f"hipEventSynchronize failed ({rc})")
 
     def elapsed_s(self, a, b) -> float:
         ms = ctypes.c_float()

@@ -136,6 +136,16 @@ __global__ void __launch_bounds__(kThreads)
   for (uint32_t j = threadIdx.x; j < lnew; j += kThreads) w.list[lbase + j] = lnew_slots[j];
 }
 
+// Distinct rows of a LAST_WINS plan (list order), for callers that publish
+// the rows a batch wrote.
+__global__ void __launch_bounds__(kThreads)
+    lw_rows(LWWork w, int64_t n, int64_t *__restrict__ out_rows, int64_t *__restrict__ out_count) {
+  const uint32_t count = *w.count;
+  const int64_t i = static_cast<int64_t>(blockIdx.x) * kThreads + threadIdx.x;
+  if (i < count && i < n) out_rows[i] = w.hkey[w.list[i]];
+  if (i == 0) *out_count = count;
+}
+
 // One wave per winner row (two rows in flight per wave): g = fl(M - e), M' = fl(M - g).
 template <int NC>
 __global__ void __launch_bounds__(kThreads)
@@ -464,5 +474,25 @@ extern "C" hlr_status writeback_apply(float *table, int64_t num_rows, int64_t di
   if (!aligned(table, 16) || !aligned(src, 16)) return HLR_MISALIGNED;
   if ((st = ws_check(ws, ws_bytes, writeback_rows_workspace_size(num_rows, dim, n, mode))) != HLR_OK) return st;
   wb_apply(table, num_rows, dim, src, n, mode, lr, ws, stream);
+  return launch_status();
+}
+
+extern "C" hlr_status writeback_plan_rows(int64_t num_rows, int64_t n, const void *ws, size_t ws_bytes,
+                                          int64_t *out_rows, int64_t *out_count, hipStream_t stream) {
+  hlr_status st = wb_args(num_rows, n, HLR_WB_LAST_WINS);
+  if (st != HLR_OK) return st;
+  if (!out_count) return HLR_INVALID_ARG;
+  if (n > 0 && !out_rows) return HLR_INVALID_ARG;
+  if ((out_rows && !aligned(out_rows, 8)) || !aligned(out_count, 8)) return HLR_MISALIGNED;
+  if (n == 0 || num_rows == 0) {
+    hlr_fill(out_count, 1, int64_t(0), stream);
+    return launch_status();
+  }
+  if ((st = ws_check(const_cast<void *>(ws), ws_bytes, writeback_rows_workspace_size(num_rows, 4, n,
+                                                                                     HLR_WB_LAST_WINS))) != HLR_OK)
+    return st;
+  LWWork w;
+  lw_layout(n, &w, const_cast<void *>(ws));
+  lw_rows<<<grid_for(n, kThreads), kThreads, 0, stream>>>(w, n, out_rows, out_count);
   return launch_status();
 }

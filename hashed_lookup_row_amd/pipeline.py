@@ -32,9 +32,10 @@ from __future__ import annotations
 import torch
 
 from ._hip import hip
-from . import (WB_LAST_WINS, WB_SGD_SUM, ema_update_apply, ema_update_plan, ema_workspace_size, gather_rows,
-               hashed_rows, mpzch_lookup_or_insert, mpzch_workspace_size, mpzch_zero_inserted, new_workspace,
-               writeback_apply, writeback_plan, writeback_workspace_size)
+from . import (WB_LAST_WINS, WB_SGD_SUM, clear_marks, ema_update_apply, ema_update_plan, ema_workspace_size,
+               gather_rows, hashed_rows, mark_rows, mpzch_lookup_or_insert, mpzch_workspace_size,
+               mpzch_zero_inserted, new_workspace, quantize_rows_int8, writeback_apply, writeback_plan,
+               writeback_plan_rows, writeback_workspace_size)
 
 
 class _Ring:
@@ -116,9 +117,11 @@ class MemoryLayerPipeline:
     def hit(self, k):
         return self._hit[k]
 
-    def step(self, ids, now, e, out=None, evicted=None, stats=None, mark=None):
+    def step(self, ids, now, e, out=None, evicted=None, stats=None, mark=None, publisher=None):
         """mark: optional callable, called with 0 just before and 1 just after the gather is
-        enqueued on the compute stream (e.g. to record timing events there)."""
+        enqueued on the compute stream (e.g. to record timing events there).
+        publisher: optional RESPublisher; it collects the rows this batch wrote and publishes
+        them at its own cadence."""
         r = self.ring
         k = r.begin_lookup()
         _on(r.lookup, ids, evicted, stats)
@@ -128,6 +131,8 @@ class MemoryLayerPipeline:
         r.mark(k, 0)
         writeback_plan(self.values.shape[0], self._rows[k], self._ws[k], WB_LAST_WINS, stream=r.ls)
         r.mark(k, 1)
+        if publisher is not None:
+            publisher.after_lookup(self)
         r.wait(k, 0)
         mpzch_zero_inserted(self.values, self._rows[k], self._hit[k], stream=r.cs)
         if mark is not None:
@@ -137,6 +142,8 @@ class MemoryLayerPipeline:
             mark(1)
         r.wait(k, 1)
         writeback_apply(self.values, e, self._ws[k], WB_LAST_WINS, 1.0, stream=r.cs)
+        if publisher is not None:
+            publisher.after_apply(self, self._ws[k])
         r.end_compute(k)
         return out, k
 
@@ -230,3 +237,139 @@ class EMAPipeline:
             ema_update_apply(t, vals[i], a, b, self._ws[k][i], stream=r.cs)
             mark(("apply", i, 1))
         r.end_compute(k)
+
+
+class RESPublisher:
+    """Raw Embedding Streaming, GPU side ("Memory Layer: Train the In-Model Cache for Recommendation
+    Models", sec. 2): training's fresh rows are copied out while they are in HBM, deduplicated,
+    quantised and pushed to serving together with the ID map and its metadata at intervals.
+
+    Per batch (compute stream, after the Writeback apply): the rows the batch wrote are added once
+    each to a written-row set (writeback_plan_rows + mark_rows).  Every `every` batches a publish:
+      compute stream: quantise the set's rows to int8 (quantize_rows_int8, per-row min-max) into a
+                      device staging slot, keep the row list and count beside it, clear the set;
+      lookup stream:  at that batch's boundary (after its MPZCH step, before the next one) copy
+                      identity and stamps into a device snapshot slot (a consistent, step-aligned
+                      snapshot);
+      copy stream:    copy the snapshot and the row count to pinned host memory; the staged rows of a
+                      publish are copied once its count has reached the host, at the next publish (or
+                      at flush()), so no GPU stream ever waits for the host.
+    Two slots alternate; each is reused only after its copies finished.  on_publish(packet), if given,
+    receives each publish as host numpy arrays once complete (the host then waits for that copy)."""
+
+    def __init__(self, pipe, every, on_publish=None):
+        dev = pipe.values.device
+        C, D = pipe.values.shape
+        self.C, self.D, self.every, self.on_publish = C, D, int(every), on_publish
+        cap = min(C, self.every * pipe.n)  # a batch writes at most n rows
+        self.cap = cap
+        self.copy = torch.cuda.Stream(dev)
+        self.cps = self.copy.cuda_stream
+        self.hip = hip()
+        i64 = dict(dtype=torch.int64, device=dev)
+        self.flags = torch.zeros(C, dtype=torch.int32, device=dev)
+        self.lst = torch.empty(C, **i64)
+        self.lst_count = torch.zeros(1, **i64)
+        self.plan_rows = torch.empty(pipe.n, **i64)
+        self.plan_count = torch.zeros(1, **i64)
+        self.st_q = [torch.empty((cap, D), dtype=torch.int8, device=dev) for _ in range(2)]
+        self.st_sc = [torch.empty(cap, dtype=torch.float32, device=dev) for _ in range(2)]
+        self.st_bi = [torch.empty(cap, dtype=torch.float32, device=dev) for _ in range(2)]
+        self.st_rows = [torch.empty(cap, **i64) for _ in range(2)]
+        self.st_cnt = [torch.zeros(1, **i64) for _ in range(2)]
+        self.snap = [(torch.empty_like(pipe.identity), torch.empty_like(pipe.stamps)) for _ in range(2)]
+        pin = dict(pin_memory=True)
+        self.h_cnt = [torch.zeros(1, dtype=torch.int64, **pin) for _ in range(2)]
+        self.h_snap = [(torch.empty(C, dtype=torch.int64, **pin), torch.empty(C, dtype=torch.int64, **pin))
+                       for _ in range(2)]
+        self.h_q = [torch.empty((cap, D), dtype=torch.int8, **pin) for _ in range(2)]
+        self.h_sc = [torch.empty(cap, dtype=torch.float32, **pin) for _ in range(2)]
+        self.h_bi = [torch.empty(cap, dtype=torch.float32, **pin) for _ in range(2)]
+        self.h_rows = [torch.empty(cap, dtype=torch.int64, **pin) for _ in range(2)]
+        ev = self.hip.event
+        self.ev_staged = [ev() for _ in range(2)]      # compute: slot staged
+        self.ev_snapped = [ev() for _ in range(2)]     # lookup: snapshot taken
+        self.ev_snap_out = [ev() for _ in range(2)]    # copy: snapshot and count on the host
+        self.ev_rows_out = [ev() for _ in range(2)]    # copy: staged rows on the host
+        self.t = 0          # batches seen
+        self.p = 0          # publishes started
+        self.pending = None  # (slot, step) whose rows still have to be copied out
+        self.steps = [None, None]
+
+    def _publishing(self):
+        return (self.t + 1) % self.every == 0
+
+    def after_lookup(self, pipe):
+        """Lookup stream, after this batch's MPZCH step: snapshot identity and stamps on publishing batches."""
+        if not self._publishing():
+            return
+        s, ls = self.p % 2, pipe.ring.ls
+        if self.p >= 2:
+            self.hip.wait(ls, self.ev_snap_out[s])
+        ident, stamps = self.snap[s]
+        with torch.cuda.stream(pipe.ring.lookup):
+            ident.copy_(pipe.identity)
+            stamps.copy_(pipe.stamps)
+        self.hip.record(self.ev_snapped[s], ls)
+
+    def after_apply(self, pipe, plan_ws):
+        """Compute stream, after this batch's Writeback apply."""
+        cs = pipe.ring.cs
+        writeback_plan_rows(self.C, pipe.n, plan_ws, out_rows=self.plan_rows, out_count=self.plan_count, stream=cs)
+        mark_rows(self.plan_rows, self.C, self.flags, self.lst, self.lst_count, count=self.plan_count, stream=cs)
+        if self._publishing():
+            self._publish(pipe)
+        self.t += 1
+
+    def _publish(self, pipe):
+        s, cs = self.p % 2, pipe.ring.cs
+        if self.p >= 2:
+            self.hip.wait(cs, self.ev_rows_out[s])
+        with torch.cuda.stream(pipe.ring.compute):
+            quantize_rows_int8(pipe.values, self.lst[:self.cap], count=self.lst_count,
+                               out=(self.st_q[s], self.st_sc[s], self.st_bi[s]), stream=cs)
+            self.st_rows[s].copy_(self.lst[:self.cap])
+            self.st_cnt[s].copy_(self.lst_count)
+        clear_marks(self.lst, self.lst_count, self.C, self.flags, stream=cs)
+        self.hip.record(self.ev_staged[s], cs)
+        self.hip.wait(self.cps, self.ev_staged[s])
+        self.hip.wait(self.cps, self.ev_snapped[s])
+        with torch.cuda.stream(self.copy):
+            self.h_cnt[s].copy_(self.st_cnt[s], non_blocking=True)
+            self.h_snap[s][0].copy_(self.snap[s][0], non_blocking=True)
+            self.h_snap[s][1].copy_(self.snap[s][1], non_blocking=True)
+        self.hip.record(self.ev_snap_out[s], self.cps)
+        self.steps[s] = self.t
+        if self.pending is not None:
+            self._copy_rows(*self.pending)
+        self.pending = (s, self.t)
+        self.p += 1
+
+    def _copy_rows(self, s, step):
+        """Copies publish slot s's staged rows to the host (its count is already there)."""
+        # the count was copied at that publish; wait for that copy (long done in steady state)
+        self._host_wait(self.ev_snap_out[s])
+        c = min(int(self.h_cnt[s][0]), self.cap)
+        with torch.cuda.stream(self.copy):
+            if c > 0:
+                self.h_q[s][:c].copy_(self.st_q[s][:c], non_blocking=True)
+                self.h_sc[s][:c].copy_(self.st_sc[s][:c], non_blocking=True)
+                self.h_bi[s][:c].copy_(self.st_bi[s][:c], non_blocking=True)
+                self.h_rows[s][:c].copy_(self.st_rows[s][:c], non_blocking=True)
+        self.hip.record(self.ev_rows_out[s], self.cps)
+        if self.on_publish is not None:
+            self._host_wait(self.ev_rows_out[s])
+            self.on_publish({"step": step, "rows": self.h_rows[s][:c].numpy().copy(),
+                             "q": self.h_q[s][:c].numpy().copy(), "scale": self.h_sc[s][:c].numpy().copy(),
+                             "bias": self.h_bi[s][:c].numpy().copy(),
+                             "identity": self.h_snap[s][0].numpy().copy(),
+                             "stamps": self.h_snap[s][1].numpy().copy()})
+
+    def _host_wait(self, e):
+        self.hip.synchronize(e)
+
+    def flush(self):
+        """Completes the last publish's row copy (call after the last batch)."""
+        if self.pending is not None:
+            self._copy_rows(*self.pending)
+            self.pending = None

@@ -183,6 +183,15 @@ hlr_status writeback_plan(int64_t num_rows, const int64_t *rows, int64_t n, int3
 hlr_status writeback_apply(float *table, int64_t num_rows, int64_t dim, const float *src, int64_t n,
                            int32_t mode, float lr, void *ws, size_t ws_bytes, hipStream_t stream);
 
+/* The distinct rows a LAST_WINS plan covers (the rows the batch writes), for
+ * publishing them after the apply (Raw Embedding Streaming, [ML] sec. 2).
+ *  ws: a workspace holding a writeback_plan(..., HLR_WB_LAST_WINS) for the
+ *  same num_rows and n, not yet reused.  out_rows[n] receives the distinct
+ *  rows in an unspecified order (the first *out_count entries);
+ *  out_count: device int64 scalar. */
+hlr_status writeback_plan_rows(int64_t num_rows, int64_t n, const void *ws, size_t ws_bytes, int64_t *out_rows,
+                               int64_t *out_count, hipStream_t stream);
+
 /* ------------------------------------------------------------------------
  * EMA row updates   [CS3] sec. 2 (CTS: c <- a*c + (1-a)*v on positive
  * interactions; CMS: s <- b*s + (1-b)*h on every interaction)
@@ -225,6 +234,43 @@ hlr_status gather_dequant_score(const int8_t *qtable, const float *scale, const 
                                 int64_t dim, const int64_t *rows, int64_t num_requests,
                                 int64_t cands_per_request, const float *user_vecs, float *out_scores,
                                 hipStream_t stream);
+
+/* ------------------------------------------------------------------------
+ * int8 row quantisation for publishing   [ML] sec. 2 (Raw Embedding
+ * Streaming quantises the rows a step touched before pushing them to
+ * serving) and sec. 5 (serving reads int8 rows)
+ *  For each i < m, m = min(n, *count) (count NULL: m = n), row r = rows[i]:
+ *    scale = fl(fl(max - min) / 255), or 1 when max == min;
+ *    bias  = fl(min + fl(128 * scale));
+ *    q_d   = clamp(rne(fl(fl(x_d - bias) / scale)), -128, 127)
+ *  over the row's fp32 values x (min, max over the row; fp32 throughout).
+ *  scatter 0: written at index i (out_q[m*dim], out_scale[m], out_bias[m]);
+ *    a row of -1 gives q = 0, scale = 0, bias = 0.
+ *  scatter 1: written at index r (arrays of num_rows entries, for example
+ *    the serving table of gather_dequant_score); rows of -1 are skipped.
+ *  table fp32 (16-byte aligned, dim % 4 == 0, dim <= 1024); out_q 4-byte
+ *  aligned.  q*scale + bias dequantises to within about scale/2.
+ * --------------------------------------------------------------------- */
+hlr_status quantize_rows_int8(const float *table, int64_t num_rows, int64_t dim, const int64_t *rows, int64_t n,
+                              const int64_t *count, int32_t scatter, int8_t *out_q, float *out_scale,
+                              float *out_bias, hipStream_t stream);
+
+/* ------------------------------------------------------------------------
+ * Written-row set between publishes   [ML] sec. 2 (Raw Embedding Streaming
+ * deduplicates the rows training wrote and pushes them at intervals)
+ *  mark_rows: for i < min(n, *count) (count NULL: n) with 0 <= rows[i] <
+ *    num_rows, the row is appended to list[] (and *list_count incremented)
+ *    unless flags[row] is already set; then flags[row] is set.  Duplicates
+ *    across calls are listed once; list order is unspecified.
+ *    flags[num_rows] uint32 (zero before first use); list[num_rows] int64;
+ *    list_count device int64 scalar (zero before first use).
+ *  clear_marks: unflags the first *list_count rows of list and sets
+ *    *list_count = 0, leaving flags all zero again.
+ * --------------------------------------------------------------------- */
+hlr_status mark_rows(const int64_t *rows, int64_t n, const int64_t *count, int64_t num_rows, uint32_t *flags,
+                     int64_t *list, int64_t *list_count, hipStream_t stream);
+hlr_status clear_marks(const int64_t *list, int64_t *list_count, int64_t num_rows, uint32_t *flags,
+                       hipStream_t stream);
 
 /* ------------------------------------------------------------------------
  * Hashed-table row mapping   [DLRM] feature expansion (hashed tables)

@@ -125,6 +125,26 @@ def test_split_entry_point_argument_errors(lib):
     assert lib.mpzch_zero_inserted(P_ODD, 64, 8, P16, P16, 10, s) == MISALIGNED
 
 
+def test_publishing_entry_point_argument_errors(lib):
+    s = None
+    assert lib.quantize_rows_int8(P16, 10, 6, P16, 5, None, 0, P16, P16, P16, s) == DIM
+    assert lib.quantize_rows_int8(P16, 10, 2048, P16, 5, None, 0, P16, P16, P16, s) == DIM
+    assert lib.quantize_rows_int8(P16, 10, 8, P16, 5, None, 2, P16, P16, P16, s) == INVALID  # scatter flag
+    assert lib.quantize_rows_int8(P16, 10, 8, P16, -5, None, 0, P16, P16, P16, s) == INVALID
+    assert lib.quantize_rows_int8(P16, 10, 8, None, 5, None, 0, P16, P16, P16, s) == INVALID
+    assert lib.quantize_rows_int8(P_ODD, 10, 8, P16, 5, None, 0, P16, P16, P16, s) == MISALIGNED
+    assert lib.quantize_rows_int8(P16, 10, 8, P16, 0, None, 0, P16, P16, P16, s) == OK
+    assert lib.mark_rows(P16, -1, None, 10, P16, P16, P16, s) == INVALID
+    assert lib.mark_rows(P16, 5, None, 10, None, P16, P16, s) == INVALID
+    assert lib.mark_rows(P_ODD, 5, None, 10, P16, P16, P16, s) == MISALIGNED
+    assert lib.clear_marks(P16, None, 10, P16, s) == INVALID
+    assert lib.clear_marks(P16, P16, -1, P16, s) == INVALID
+    need = lib.writeback_rows_workspace_size(100, 4, 10, 0)
+    assert lib.writeback_plan_rows(100, 10, P16, need, P16, None, s) == INVALID
+    assert lib.writeback_plan_rows(100, 10, P16, need - 1, P16, P16, s) == WS_SMALL
+    assert lib.writeback_plan_rows(100, -2, P16, need, P16, P16, s) == INVALID
+
+
 def test_score_dedup_hashed_argument_errors(lib):
     s = None
     assert lib.gather_dequant_score(P16, P16, P16, 10, 520, P16, 2, 3, P16, P16, s) == DIM
