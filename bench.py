@@ -79,7 +79,7 @@ def parse():
                     help="only run a plain 1 GiB device copy (reference for HBM counters)")
     ap.add_argument("--scale", type=float, default=1.0, help="shrink capacity/universe/batch (testing only)")
     ap.add_argument("--workload", default="memory-layer",
-                    choices=["memory-layer", "serving", "dlrm", "cs3", "dedup"],
+                    choices=["memory-layer", "serving", "dlrm", "cs3", "dedup", "res"],
                     help="memory-layer (default, the headline) or one of the other rows' workloads")
     ap.add_argument("--op-events", action="store_true",
                     help="also time lookup and writeback separately (events between every call)")
@@ -118,7 +118,8 @@ def main():
         return
     sys.path.insert(0, ROOT)
     if args.workload != "memory-layer":
-        {"serving": run_serving, "dlrm": run_dlrm, "cs3": run_cs3, "dedup": run_dedup}[args.workload](args)
+        {"serving": run_serving, "dlrm": run_dlrm, "cs3": run_cs3, "dedup": run_dedup,
+         "res": run_res}[args.workload](args)
         return
     import hashed_lookup_row_amd as hlr
     import synth
@@ -561,6 +562,79 @@ def run_cs3(args):
            "apply_us": {k: v * 1e6 for k, v in per.items()},
            "one_stream": {"ms_per_step": serial / K * 1e3, "pairs_per_s": n * K / serial},
            "top_user_occurrences": int(np.bincount(ur).max())})
+
+
+def run_res(args):
+    """Memory-Layer step with the Raw Embedding Streaming bookkeeping (each batch's written rows added to
+    the publish set), then one publish of everything written in the timed batches: quantise to int8,
+    snapshot identity/stamps at the batch boundary, copy both to pinned host memory."""
+    import numpy as np
+    import torch
+    import hashed_lookup_row_amd as hlr
+    import synth
+    from hashed_lookup_row_amd.pipeline import MemoryLayerPipeline, RESPublisher
+    from hashed_lookup_row_amd._hip import hip
+    dev = torch.device("cuda:0")
+    cfg = synth.MEMORY_LAYER
+    C, P, D, n = cfg.capacity, cfg.probes, cfg.dim, cfg.batch
+    # at most 50 timed batches between the two publishes: about 0.55M distinct rows are written in them
+    K, W = min(args.steps, 50), args.warmup
+    stream, fc = [], 0
+    for t in range(1, W + K + 1):
+        ids, fc = synth.mpzch_step_ids(cfg, t, fc)
+        stream.append(ids)
+    identity = torch.full((C,), -1, dtype=torch.int64, device=dev)
+    stamps = torch.full((C,), -1, dtype=torch.int64, device=dev)
+    values = torch.zeros((C, D), dtype=torch.float32, device=dev)
+    prefill = synth.prefill_batches(cfg)
+    for k, b in enumerate(prefill, start=1):
+        hlr.mpzch_lookup_or_insert(identity, stamps, None, P, torch.from_numpy(b).to(dev), k)
+    base = len(prefill)
+    ids_dev = [torch.from_numpy(x).to(dev) for x in stream]
+    e_pool = [synth.normal_rows(n, D, cfg.e_std, cfg.config, t + 1, device=dev) for t in range(8)]
+    out = torch.empty((n, D), dtype=torch.float32, device=dev)
+    torch.cuda.synchronize()
+    timer, cur = HipTimer(), torch.cuda.current_stream(dev).cuda_stream
+    pipe = MemoryLayerPipeline(identity, stamps, values, P, n)
+    pub = RESPublisher(pipe, 0, max_rows=1 << 20)
+    for t in range(W):
+        pipe.step(ids_dev[t], base + 1 + t, e_pool[t % 8], out=out, publisher=pub)
+    pub.publish_now(pipe)  # clears the warm-up's rows (and warms the host copy path)
+    pub.flush()
+    torch.cuda.synchronize()
+    pub.copy.synchronize()
+    a, b = timer.event(), timer.event()
+    timer.record(a, cur)
+    for k in range(K):
+        t = W + k
+        pipe.step(ids_dev[t], base + 1 + t, e_pool[t % 8], out=out, publisher=pub)
+    timer.record(b, cur)
+    torch.cuda.synchronize()
+    total = timer.elapsed_s(a, b)
+    # one publish of the rows the K timed batches wrote; quantiser timed on the compute stream and the
+    # host copies (snapshot + count, then the rows) on the copy stream
+    h = hip()
+    qa, qb, ca, cb = h.event(True), h.event(True), h.event(True), h.event(True)
+    h.record(qa, cur)
+    pub.publish_now(pipe)
+    h.record(qb, cur)
+    h.record(ca, pub.cps)
+    pub.flush()
+    h.record(cb, pub.cps)
+    torch.cuda.synchronize()
+    pub.copy.synchronize()
+    u = int(pub.h_cnt[(pub.p - 1) % 2][0])
+    pub_s = h.elapsed_s(qa, qb)
+    copy_s = h.elapsed_s(qa, cb)
+    qbytes = u * (D * 4 + D + 8 + 8) + u * 8 * 2
+    host_bytes = u * (D + 16) + 16 * C + 8
+    step_s = total / K
+    _line("rows/s of the Memory-Layer step with RES bookkeeping (written-row set per batch)", n / step_s, "rows/s",
+          K, W, step_s * 1e3, {"workload": cfg.name + "+res", "capacity": C, "dim": D, "ids_per_step": n},
+          _roof("publish on the compute stream (quantize_rows_int8 + staging copies)", qbytes, pub_s),
+          {"dtype": "fp32->int8", "published_rows": u, "publish_gpu_us": pub_s * 1e6,
+           "host_copy": {"bytes": host_bytes, "ms_from_publish_start": copy_s * 1e3,
+                         "GBps": host_bytes / copy_s / 1e9}})
 
 
 def run_dedup(args):

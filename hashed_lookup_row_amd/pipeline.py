@@ -255,14 +255,18 @@ class RESPublisher:
                       publish are copied once its count has reached the host, at the next publish (or
                       at flush()), so no GPU stream ever waits for the host.
     Two slots alternate; each is reused only after its copies finished.  on_publish(packet), if given,
-    receives each publish as host numpy arrays once complete (the host then waits for that copy)."""
+    receives each publish as host numpy arrays once complete (the host then waits for that copy).
+    every = 0 publishes only on publish_now()."""
 
-    def __init__(self, pipe, every, on_publish=None):
+    def __init__(self, pipe, every, on_publish=None, max_rows=None):
         dev = pipe.values.device
         C, D = pipe.values.shape
         self.C, self.D, self.every, self.on_publish = C, D, int(every), on_publish
-        cap = min(C, self.every * pipe.n)  # a batch writes at most n rows
-        self.cap = cap
+        # staging rows per publish: a batch writes at most n rows; with publish_now() only, max_rows
+        # bounds the rows written between two publishes (a publish with more raises at the host)
+        cap = min(C, self.every * pipe.n) if self.every > 0 else C
+        self.cap = cap if max_rows is None else min(cap, int(max_rows))
+        cap = self.cap
         self.copy = torch.cuda.Stream(dev)
         self.cps = self.copy.cuda_stream
         self.hip = hip()
@@ -297,7 +301,21 @@ class RESPublisher:
         self.steps = [None, None]
 
     def _publishing(self):
-        return (self.t + 1) % self.every == 0
+        return self.every > 0 and (self.t + 1) % self.every == 0
+
+    def publish_now(self, pipe):
+        """Publishes the rows written so far at the current batch boundary (between steps)."""
+        s = self.p % 2
+        if self.p >= 2:
+            self.hip.wait(pipe.ring.ls, self.ev_snap_out[s])
+        with torch.cuda.stream(pipe.ring.lookup):
+            self.snap[s][0].copy_(pipe.identity)
+            self.snap[s][1].copy_(pipe.stamps)
+        self.hip.record(self.ev_snapped[s], pipe.ring.ls)
+        self.hip.wait(pipe.ring.cs, self.ev_snapped[s])  # the batch boundary on both streams
+        self.t -= 1
+        self._publish(pipe)
+        self.t += 1
 
     def after_lookup(self, pipe):
         """Lookup stream, after this batch's MPZCH step: snapshot identity and stamps on publishing batches."""
@@ -349,7 +367,10 @@ class RESPublisher:
         """Copies publish slot s's staged rows to the host (its count is already there)."""
         # the count was copied at that publish; wait for that copy (long done in steady state)
         self._host_wait(self.ev_snap_out[s])
-        c = min(int(self.h_cnt[s][0]), self.cap)
+        c = int(self.h_cnt[s][0])
+        if c > self.cap:
+            raise RuntimeError(f"publish of {c} rows exceeds the staging capacity {self.cap}: raise max_rows "
+                               "or publish more often")
         with torch.cuda.stream(self.copy):
             if c > 0:
                 self.h_q[s][:c].copy_(self.st_q[s][:c], non_blocking=True)

@@ -121,15 +121,16 @@ def test_res_publisher_schedule(dev):
     pub = pipeline.RESPublisher(pipe, every=3, on_publish=packets.append)
     for t in range(cfg.steps):
         pipe.step(ids[t], base + t + 1, es[t], publisher=pub)
+    pub.publish_now(pipe)  # the rows of batch 9, written after the last periodic publish
     pub.flush()
     torch.cuda.synchronize()
-    assert [p["step"] for p in packets] == [2, 5, 8]
+    assert [p["step"] for p in packets] == [2, 5, 8, 9]
     written, states = set(), {}
     for t in range(cfg.steps):
         orows, _, _, _ = o.step(ids_np[t], base + t + 1)
         o.writeback(orows, e_np[t])
         written |= set(orows[orows >= 0].tolist())
-        if (t + 1) % 3 == 0:
+        if (t + 1) % 3 == 0 or t == cfg.steps - 1:
             states[t] = (written, o.values.copy(), o.identity.copy(), o.stamps.copy())
             written = set()
     for p in packets:
