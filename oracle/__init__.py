@@ -61,6 +61,8 @@ def _load():
             lib.orc_writeback_last.argtypes = [p, i64, i64, p, p, i64]
             lib.orc_sgd_sum.restype = ctypes.c_int
             lib.orc_sgd_sum.argtypes = [p, i64, i64, p, p, i64, ctypes.c_float]
+            lib.orc_dks_step.restype = ctypes.c_int
+            lib.orc_dks_step.argtypes = [p, p, i64, p, p, i64, i64, p, p, i64, i64, i32, p, p, p]
             lib.orc_l2_align.restype = ctypes.c_int
             lib.orc_l2_align.argtypes = [p, i64, i64, p, p, i64, ctypes.c_float]
             lib.orc_quantize_rows.restype = ctypes.c_int
@@ -181,6 +183,34 @@ def sgd_sum(table, rows, g, lr):
     g = _c(g, np.float32)
     _check(_load().orc_sgd_sum(_ptr(table), table.shape[0], table.shape[1], _ptr(rows), _ptr(g), rows.size,
                                ctypes.c_float(lr)), "sgd_sum")
+
+
+class KeyStore:
+    """Decoupled key store (open addressing, linear probing) + value store (rows handed out in order)."""
+
+    def __init__(self, key_cap: int, max_rows: int, dim: int, with_values: bool = True):
+        self.key_cap, self.max_rows, self.dim = int(key_cap), int(max_rows), int(dim)
+        self.keys = np.full(self.key_cap, -1, np.int64)
+        self.krows = np.full(self.key_cap, -1, np.int64)
+        self.stamps = np.full(self.max_rows, -1, np.int64)
+        self.values = np.zeros((self.max_rows, self.dim), np.float32) if with_values else None
+        self.next_row = np.zeros(1, np.int64)
+
+    def step(self, ids, now: int, insert: bool = True):
+        ids = _c(ids, np.int64)
+        n = ids.size
+        rows = np.empty(n, np.int64)
+        hit = np.empty(n, np.int8)
+        stats = np.zeros(4, np.int64)
+        _check(_load().orc_dks_step(_ptr(self.keys), _ptr(self.krows), self.key_cap, _ptr(self.stamps),
+                                    _ptr(self.values), self.dim, self.max_rows, _ptr(self.next_row), _ptr(ids), n,
+                                    int(now), 1 if insert else 0, _ptr(rows), _ptr(hit), _ptr(stats)), "dks_step")
+        return rows, hit, stats
+
+    def mapping(self):
+        """{key: row} of the stored keys."""
+        m = self.keys >= 0
+        return dict(zip(self.keys[m].tolist(), self.krows[m].tolist()))
 
 
 def l2_align(table, rows, e, lr):

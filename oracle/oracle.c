@@ -284,6 +284,78 @@ int orc_sgd_sum(float *table, int64_t num_rows, int64_t dim, const int64_t *rows
     return ORC_OK;
 }
 
+/* ------------------------------ decoupled, growable key store [MTGR] sec. 3.2 */
+/*
+ * Key store and value store are separate ([MTGR] sec. 3.2): the key store maps
+ * a raw key to a row of the value store; the value store holds the rows and
+ * their metadata (here the last batch that touched the row); growing the key
+ * store copies keys only.  Readings: the key store is an open-addressing table
+ * of `key_cap` slots (keys[], krows[]; key -1 = empty), linear probing from
+ * mix(key) mod key_cap; the value store hands out rows in order (next_row, at
+ * most max_rows).  One batch, two phases as for MPZCH: keys already stored are
+ * hits (row, stamp = now); then the distinct missed keys, in order of first
+ * occurrence, take rows next_row, next_row + 1, ... (zero-filled when values
+ * is given, stamp = now) until max_rows, after which they overflow (row -1,
+ * nothing stored).  insert == 0 only looks up.  The table must keep at least
+ * one empty slot.  stats: {hit positions, inserted keys, overflowed keys,
+ * invalid positions}.
+ */
+static int64_t orc_dks_find(const int64_t *keys, int64_t key_cap, int64_t key, int64_t *slot) {
+    int64_t s = (int64_t)(orc_mix64((uint64_t)key) % (uint64_t)key_cap);
+    for (int64_t j = 0; j < key_cap; ++j) {
+        if (keys[s] == key) { *slot = s; return 1; }
+        if (keys[s] == ORC_EMPTY) { *slot = s; return 0; }
+        s = (s + 1) % key_cap;
+    }
+    *slot = -1;
+    return 0;
+}
+
+int orc_dks_step(int64_t *keys, int64_t *krows, int64_t key_cap, int64_t *stamps, float *values, int64_t dim,
+                 int64_t max_rows, int64_t *next_row, const int64_t *ids, int64_t n, int64_t now, int32_t insert,
+                 int64_t *rows, int8_t *hit, int64_t *stats) {
+    if (key_cap <= 0 || n < 0 || max_rows < 0 || *next_row < 0 || *next_row > max_rows) return ORC_EINVAL;
+    int64_t st[4] = {0, 0, 0, 0};
+    /* Phase 1: keys already stored. */
+    for (int64_t i = 0; i < n; ++i) {
+        rows[i] = -1;
+        hit[i] = 0;
+        if (ids[i] == ORC_EMPTY) { st[3]++; continue; }
+        int64_t slot;
+        if (orc_dks_find(keys, key_cap, ids[i], &slot)) {
+            rows[i] = krows[slot];
+            hit[i] = 1;
+            st[0]++;
+            if (insert) stamps[rows[i]] = now;
+        }
+    }
+    if (insert) {
+        /* Phase 2: distinct missed keys in order of first occurrence take the next rows. */
+        for (int64_t i = 0; i < n; ++i) {
+            if (ids[i] == ORC_EMPTY || hit[i]) continue;
+            int64_t slot;
+            if (orc_dks_find(keys, key_cap, ids[i], &slot)) {  /* inserted earlier in this batch */
+                rows[i] = krows[slot];
+                continue;
+            }
+            int64_t first = 1;
+            for (int64_t k = 0; k < i && first; ++k)
+                if (ids[k] == ids[i]) first = 0;
+            if (!first) continue;  /* an earlier occurrence overflowed */
+            if (*next_row >= max_rows || slot < 0) { st[2]++; continue; }
+            const int64_t r = (*next_row)++;
+            keys[slot] = ids[i];
+            krows[slot] = r;
+            stamps[r] = now;
+            if (values) memset(values + r * dim, 0, (size_t)dim * sizeof(float));
+            rows[i] = r;
+            st[1]++;
+        }
+    }
+    for (int k = 0; k < 4; ++k) stats[k] = st[k];
+    return ORC_OK;
+}
+
 /* ------------------------------------------------ L2 alignment [ML] sec. 2 */
 /*
  * The plain alternative to Writeback that [ML] sec. 2 and sec. 3 compare with

@@ -349,6 +349,67 @@ def test_sgd_sum_integer_gradients_are_exact():
         assert np.array_equal(table[r], -0.5 * grads[rows == r].sum(axis=0))
 
 
+# ------------------------------------------------ decoupled key store (MTGR)
+def _dict_store(stream, max_rows):
+    """Reference key -> row map: a Python dict, rows handed out in order of first appearance."""
+    d, out = {}, []
+    for ids in stream:
+        rows, hit = [], []
+        pending = {}
+        for k in ids.tolist():
+            if k == -1:
+                rows.append(-1), hit.append(0)
+            elif k in d:
+                rows.append(d[k]), hit.append(1)
+            else:
+                rows.append(None), hit.append(0)
+        for i, k in enumerate(ids.tolist()):  # misses in order of first occurrence
+            if rows[i] is None:
+                if k not in pending:
+                    pending[k] = len(d) + len(pending) if len(d) + len(pending) < max_rows else -1
+                rows[i] = pending[k]
+        for k, r in pending.items():
+            if r >= 0:
+                d[k] = r
+        out.append((np.array(rows), np.array(hit, np.int8)))
+    return d, out
+
+
+def test_key_store_matches_dict_reference_and_table_invariants():
+    g = np.random.default_rng(41)
+    stream = [np.where(g.random(300) < 0.02, -1, g.zipf(1.3, size=300) * 7919 - 50).astype(np.int64)
+              for _ in range(12)]
+    for key_cap, max_rows in [(1024, 700), (512, 200), (256, 255)]:
+        ks = oracle.KeyStore(key_cap, max_rows, 4)
+        ks.values[:] = 1.0
+        d, ref = _dict_store(stream, max_rows)
+        for t, ids in enumerate(stream):
+            rows, hit, st = ks.step(ids, t + 1)
+            assert np.array_equal(rows, ref[t][0]) and np.array_equal(hit, ref[t][1]), (key_cap, t)
+            assert st[3] == np.count_nonzero(ids == -1) and st[0] == hit.sum()
+        assert ks.mapping() == d and ks.next_row[0] == len(d)
+        used = ks.keys >= 0
+        for s in np.nonzero(used)[0]:  # every key reachable from its home slot without crossing an empty slot
+            home = oracle.mix64(int(ks.keys[s])) % key_cap
+            j = home
+            while j != s:
+                assert ks.keys[j] >= 0
+                j = (j + 1) % key_cap
+        new_rows = np.arange(len(d))
+        assert np.all(ks.values[new_rows] == 0) and np.all(ks.values[len(d):] == 1)  # only new rows zeroed
+
+
+def test_key_store_lookup_only_changes_nothing_and_stamps():
+    ks = oracle.KeyStore(64, 32, 2)
+    ks.step(np.array([3, 4, 3, 5], np.int64), 1)
+    before = (ks.keys.copy(), ks.krows.copy(), ks.stamps.copy(), ks.next_row.copy())
+    rows, hit, st = ks.step(np.array([4, 9, 3], np.int64), 2, insert=False)
+    assert rows.tolist() == [1, -1, 0] and hit.tolist() == [1, 0, 1] and st[1] == 0
+    assert all(np.array_equal(a, b) for a, b in zip(before, (ks.keys, ks.krows, ks.stamps, ks.next_row)))
+    ks.step(np.array([5, 6], np.int64), 3)
+    assert ks.stamps[:4].tolist() == [1, 1, 3, 3]  # rows of 3, 4 last touched in batch 1; 5 and new 6 in batch 3
+
+
 # ------------------------------------------------------------ L2 alignment
 def test_l2_align_single_occurrence_half_rate_is_writeback():
     """lr = 0.5, one occurrence per row: M - 0.5 * 2 (M - e) is the Writeback assignment
