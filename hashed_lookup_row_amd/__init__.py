@@ -69,6 +69,9 @@ def load_library():
             "quantize_rows_int8": (i32, [p, i64, i64, p, i64, p, i32, p, p, p, p]),
             "mark_rows": (i32, [p, i64, p, i64, p, p, p, p]),
             "clear_marks": (i32, [p, p, i64, p, p]),
+            "dks_workspace_size": (sz, [i64]),
+            "dks_lookup_or_insert": (i32, [p, p, i64, p, p, i64, i64, p, p, i64, i64, i32, p, p, p, p, sz, p]),
+            "dks_rehash": (i32, [p, p, i64, p, p, i64, p]),
         }
         for name, (res, args) in sig.items():
             f = getattr(lib, name)
@@ -83,7 +86,8 @@ def exported_symbols():
             "gather_rows", "dedup_ids_workspace_size", "dedup_ids", "writeback_rows_workspace_size",
             "writeback_rows", "ema_update_rows_workspace_size", "ema_update_rows", "gather_dequant_score",
             "hashed_rows", "mpzch_zero_inserted", "writeback_plan", "writeback_apply", "ema_update_plan",
-            "ema_update_apply", "writeback_plan_rows", "quantize_rows_int8", "mark_rows", "clear_marks"]
+            "ema_update_apply", "writeback_plan_rows", "quantize_rows_int8", "mark_rows", "clear_marks",
+            "dks_workspace_size", "dks_lookup_or_insert", "dks_rehash"]
 
 
 def _check(rc: int, what: str):
@@ -386,3 +390,44 @@ def clear_marks(lst, list_count, num_rows, flags, stream=None):
     _dev(flags, "flags", torch.int32)
     _check(lib.clear_marks(_ptr(lst), _ptr(list_count), int(num_rows), _ptr(flags), _stream(lst.device, stream)),
            "clear_marks")
+
+
+def dks_lookup_or_insert(keys, krows, stamps, values, max_rows, next_row, ids, now, insert=True, out_rows=None,
+                         out_hit=None, out_stats=None, ws=None, stream=None):
+    """Decoupled key store lookup (insert=False) or lookup-or-insert.  Returns (rows, hit, stats or None)."""
+    lib = load_library()
+    _dev(keys, "keys", torch.int64)
+    _dev(krows, "krows", torch.int64)
+    _dev(ids, "ids", torch.int64)
+    if stamps is not None:
+        _dev(stamps, "stamps", torch.int64)
+    if values is not None:
+        _dev(values, "values", torch.float32)
+    if next_row is not None:
+        _dev(next_row, "next_row", torch.int64)
+    dev, n = keys.device, ids.numel()
+    dim = values.shape[1] if values is not None else 0
+    rows = out_rows if out_rows is not None else torch.empty(n, dtype=torch.int64, device=dev)
+    hit = out_hit if out_hit is not None else torch.empty(n, dtype=torch.int8, device=dev)
+    need = lib.dks_workspace_size(n) if insert else 0
+    if ws is not None and need > 0:
+        w, wb = _own_ws(ws, need)
+    else:
+        w, wb = _ws_args(dev, need)
+    _check(lib.dks_lookup_or_insert(_ptr(keys), _ptr(krows), keys.numel(), _ptr(stamps), _ptr(values), dim,
+                                    int(max_rows), _ptr(next_row), _ptr(ids), n, int(now), 1 if insert else 0,
+                                    _ptr(rows), _ptr(hit), _ptr(out_stats), w, wb, _stream(dev, stream)),
+           "dks_lookup_or_insert")
+    return rows, hit, out_stats
+
+
+def dks_rehash(keys, krows, new_cap, stream=None):
+    """New (keys, krows) of new_cap slots holding the same key -> row map."""
+    lib = load_library()
+    _dev(keys, "keys", torch.int64)
+    _dev(krows, "krows", torch.int64)
+    nk = torch.empty(int(new_cap), dtype=torch.int64, device=keys.device)
+    nr = torch.empty(int(new_cap), dtype=torch.int64, device=keys.device)
+    _check(lib.dks_rehash(_ptr(keys), _ptr(krows), keys.numel(), _ptr(nk), _ptr(nr), int(new_cap),
+                          _stream(keys.device, stream)), "dks_rehash")
+    return nk, nr

@@ -273,6 +273,38 @@ hlr_status clear_marks(const int64_t *list, int64_t *list_count, int64_t num_row
                        hipStream_t stream);
 
 /* ------------------------------------------------------------------------
+ * Decoupled, growable key store   "MTGR: Industrial-Scale Generative
+ * Recommendation Framework in Meituan", sec. 3.2 (key store maps a key to a
+ * row of a separate value store holding the rows and their eviction
+ * metadata; growing copies the light key store only)
+ *  keys[key_cap], krows[key_cap] int64: the key store, open addressing with
+ *    linear probing from SplitMix64-finaliser(key) mod key_cap; key_cap a
+ *    power of two; key -1 = empty slot.  Keep at least n empty slots before a
+ *    batch (grow with dks_rehash); otherwise results are unspecified.
+ *  Value store: values[max_rows*dim] fp32 (nullable: new rows are then not
+ *    zero-filled), stamps[max_rows] int64 (last batch that touched the row),
+ *    next_row: device int64, rows in use (in/out).
+ *  Semantics (insert 1): keys already stored are hits (row, stamps[row] =
+ *    now); then the distinct missed keys, in order of first occurrence in ids,
+ *    take rows next_row, next_row + 1, ... (zero-filled, stamped) while rows
+ *    remain; later ones overflow (row -1, not stored).  insert 0 only looks
+ *    up and changes nothing.  ids of -1 are invalid (row -1, counted).
+ *  out_rows[n], out_hit[n] int8; out_stats[4] nullable, device int64:
+ *    {hit positions, inserted keys, overflowed keys, invalid positions}.
+ *  Workspace: dks_workspace_size(n) bytes (insert mode only).
+ * dks_rehash: copies every stored key with its row into an empty key store of
+ *  new_cap >= key_cap slots (filled with -1 by the call); rows and values are
+ *  not touched.
+ * --------------------------------------------------------------------- */
+size_t dks_workspace_size(int64_t n);
+hlr_status dks_lookup_or_insert(int64_t *keys, int64_t *krows, int64_t key_cap, int64_t *stamps, float *values,
+                                int64_t dim, int64_t max_rows, int64_t *next_row, const int64_t *ids, int64_t n,
+                                int64_t now, int32_t insert, int64_t *out_rows, int8_t *out_hit,
+                                int64_t *out_stats, void *ws, size_t ws_bytes, hipStream_t stream);
+hlr_status dks_rehash(const int64_t *keys, const int64_t *krows, int64_t key_cap, int64_t *new_keys,
+                      int64_t *new_krows, int64_t new_cap, hipStream_t stream);
+
+/* ------------------------------------------------------------------------
  * Hashed-table row mapping   [DLRM] feature expansion (hashed tables)
  *  out_rows[i] = SplitMix64-finaliser(ids[i]) mod num_rows (collisions
  *  allowed; no identity tensor).  num_rows >= 1.

@@ -145,6 +145,25 @@ def test_publishing_entry_point_argument_errors(lib):
     assert lib.writeback_plan_rows(100, -2, P16, need, P16, P16, s) == INVALID
 
 
+def test_key_store_argument_errors(lib):
+    s = None
+    need = lib.dks_workspace_size(10)
+    call = lambda cap, ins, ws, wsb, dim=0, values=None, n=10: lib.dks_lookup_or_insert(
+        P16, P16, cap, P16, values, dim, 100, P16, P16, n, 3, ins, P16, P16, None, ws, wsb, s)
+    assert call(1000, 1, P16, need) == INVALID      # key capacity not a power of two
+    assert call(1024, 2, P16, need) == INVALID      # insert flag
+    assert call(1024, 1, None, 0) == WS_SMALL
+    assert call(1024, 1, P16, need - 1) == WS_SMALL
+    assert call(1024, 1, ctypes.c_void_p((1 << 20) + 16), need) == MISALIGNED
+    assert call(1024, 1, P16, need, dim=6, values=P16) == DIM
+    assert call(1024, 1, P16, need, n=-1) == INVALID
+    assert lib.dks_lookup_or_insert(P16, P16, 1024, None, None, 0, 100, None, P16, 10, 3, 1, P16, P16, None, P16,
+                                    need, s) == INVALID  # insert needs stamps and next_row
+    assert lib.dks_rehash(P16, P16, 1024, P16, P16, 512, s) == INVALID  # smaller table
+    assert lib.dks_rehash(P16, P16, 1024, P16, P16, 3000, s) == INVALID
+    assert lib.dks_rehash(P_ODD, P16, 1024, P16, P16, 2048, s) == MISALIGNED
+
+
 def test_score_dedup_hashed_argument_errors(lib):
     s = None
     assert lib.gather_dequant_score(P16, P16, P16, 10, 520, P16, 2, 3, P16, P16, s) == DIM
