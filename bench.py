@@ -79,7 +79,7 @@ def parse():
                     help="only run a plain 1 GiB device copy (reference for HBM counters)")
     ap.add_argument("--scale", type=float, default=1.0, help="shrink capacity/universe/batch (testing only)")
     ap.add_argument("--workload", default="memory-layer",
-                    choices=["memory-layer", "serving", "dlrm", "cs3", "dedup", "res"],
+                    choices=["memory-layer", "serving", "dlrm", "cs3", "dedup", "res", "keystore"],
                     help="memory-layer (default, the headline) or one of the other rows' workloads")
     ap.add_argument("--op-events", action="store_true",
                     help="also time lookup and writeback separately (events between every call)")
@@ -119,7 +119,7 @@ def main():
     sys.path.insert(0, ROOT)
     if args.workload != "memory-layer":
         {"serving": run_serving, "dlrm": run_dlrm, "cs3": run_cs3, "dedup": run_dedup,
-         "res": run_res}[args.workload](args)
+         "res": run_res, "keystore": run_keystore}[args.workload](args)
         return
     import hashed_lookup_row_amd as hlr
     import synth
@@ -635,6 +635,65 @@ def run_res(args):
           {"dtype": "fp32->int8", "published_rows": u, "publish_gpu_us": pub_s * 1e6,
            "host_copy": {"bytes": host_bytes, "ms_from_publish_start": copy_s * 1e3,
                          "GBps": host_bytes / copy_s / 1e9}})
+
+
+def run_keystore(args):
+    """The Memory-Layer ID stream (65,536 IDs per batch, Zipf(1.05) over 20M keys + 0.5% fresh) through
+    the decoupled key store: key store from 2^20 slots, grown by rehash (keys only) whenever it could
+    pass half full; value store of 4Mi rows x 512 fp32 (new rows zero-filled), as in the Memory Layer."""
+    import numpy as np
+    import torch
+    import hashed_lookup_row_amd as hlr
+    import synth
+    from hashed_lookup_row_amd.keystore import DynamicKeyStore
+    dev = torch.device("cuda:0")
+    cfg = synth.MEMORY_LAYER
+    C, D, n = cfg.capacity, cfg.dim, cfg.batch
+    K, W = args.steps, args.warmup
+    stream, fc = [], 0
+    for t in range(1, W + K + 1):
+        ids, fc = synth.mpzch_step_ids(cfg, t, fc)
+        stream.append(ids)
+    ids_dev = [torch.from_numpy(x).to(dev) for x in stream]
+    values = torch.zeros((C, D), dtype=torch.float32, device=dev)
+    store = DynamicKeyStore(values, C, key_cap=1 << 20)
+    rows = torch.empty(n, dtype=torch.int64, device=dev)
+    hit = torch.empty(n, dtype=torch.int8, device=dev)
+    stats = torch.zeros(4, dtype=torch.int64, device=dev)
+    for t in range(W):
+        store.step(ids_dev[t], t + 1, out_rows=rows, out_hit=hit)
+    torch.cuda.synchronize()
+    timer, cur = HipTimer(), torch.cuda.current_stream(dev).cuda_stream
+    r0 = store.rehashes
+    a, b = timer.event(), timer.event()
+    timer.record(a, cur)
+    for k in range(K):
+        t = W + k
+        store.step(ids_dev[t], t + 1, out_rows=rows, out_hit=hit, out_stats=stats if k == K - 1 else None)
+    timer.record(b, cur)
+    torch.cuda.synchronize()
+    total = timer.elapsed_s(a, b)
+    st = stats.cpu().numpy()
+    used = int(store.next_row.cpu()[0])
+    # one rehash of the final key store into one twice as large (keys and row indices only), timed alone
+    ra, rb = timer.event(), timer.event()
+    timer.record(ra, cur)
+    hlr.dks_rehash(store.keys, store.krows, 2 * store.keys.numel())
+    timer.record(rb, cur)
+    torch.cuda.synchronize()
+    rehash_s = timer.elapsed_s(ra, rb)
+    cap = store.keys.numel()
+    step_s = total / K
+    probe_bytes = n * (8 + 64 + 8 + 8 + 1 + 8)  # id, key line, row index, out row, hit, stamp per position
+    _line("IDs/s through the decoupled key store (lookup-or-insert, growth by rehash)", n / step_s, "ids/s", K, W,
+          step_s * 1e3, {"workload": "memory-layer ID stream, decoupled key store", "value_rows": C, "dim": D,
+                         "ids_per_step": n, "key_slots_final": cap},
+          _roof("dks_lookup_or_insert (all kernels)", probe_bytes, step_s),
+          {"dtype": "int64", "rows_in_use": used, "rehashes_timed": store.rehashes - r0,
+           "last_step_stats": {"hits": int(st[0]), "inserts": int(st[1]), "overflows": int(st[2]),
+                               "invalid": int(st[3])},
+           "rehash": {"from_slots": cap, "to_slots": 2 * cap, "us": rehash_s * 1e6,
+                      "bytes_moved": cap * 16 + 2 * cap * 16}})
 
 
 def run_dedup(args):

@@ -392,6 +392,10 @@ def clear_marks(lst, list_count, num_rows, flags, stream=None):
            "clear_marks")
 
 
+def dks_workspace_size(n) -> int:
+    return int(load_library().dks_workspace_size(int(n)))
+
+
 def dks_lookup_or_insert(keys, krows, stamps, values, max_rows, next_row, ids, now, insert=True, out_rows=None,
                          out_hit=None, out_stats=None, ws=None, stream=None):
     """Decoupled key store lookup (insert=False) or lookup-or-insert.  Returns (rows, hit, stats or None)."""

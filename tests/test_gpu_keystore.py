@@ -131,3 +131,27 @@ def test_rehash_keeps_the_map(dev):
         kk, rr = to_np(k), to_np(r)
         sel = kk >= 0
         assert dict(zip(kk[sel].tolist(), rr[sel].tolist())) == m
+
+
+def test_dynamic_key_store_grows_without_waiting(dev):
+    """DynamicKeyStore: batches enqueued back to back (no synchronisation), growth decided from
+    completed copies of the row count; every batch's rows equal the oracle's."""
+    from hashed_lookup_row_amd.keystore import DynamicKeyStore
+    g = np.random.default_rng(12)
+    dim, max_rows, n = 32, 60_000, 3000
+    values = torch.zeros((max_rows, dim), dtype=torch.float32, device=dev)
+    store = DynamicKeyStore(values, max_rows, key_cap=1024)
+    ora = oracle.KeyStore(1 << 18, max_rows, dim)
+    batches = [zipf_keys(g, n, 1.1, 500_000) for _ in range(15)]
+    dev_b = [torch.from_numpy(b).to(dev) for b in batches]
+    outs = [torch.empty(n, dtype=torch.int64, device=dev) for _ in batches]
+    torch.cuda.synchronize()
+    for t, b in enumerate(dev_b):
+        store.step(b, t + 1, out_rows=outs[t])
+    for t, b in enumerate(batches):
+        orows, _, _ = ora.step(b, t + 1)
+        assert np.array_equal(to_np(outs[t]), orows), t
+    assert store.rehashes >= 3
+    k, r = to_np(store.keys), to_np(store.krows)
+    assert dict(zip(k[k >= 0].tolist(), r[k >= 0].tolist())) == ora.mapping()
+    assert (k >= 0).sum() <= store.keys.numel() // 2
