@@ -399,11 +399,11 @@ def run_serving(args):
     step_s = float(np.median(t_look) + np.median(t_score))
     _line("candidate scores/s (lookup-only MPZCH + int8 dequant + dot)", n / step_s, "scores/s", K, W,
           step_s * 1e3, {"workload": sv.name, "requests": sv.requests, "cands": sv.cands, "dim": D, "capacity": C},
-          _roof("score_kernel<2>", score_bytes, float(np.median(t_score))),
+          _roof("score_kernel<2,2>", score_bytes, float(np.median(t_score))),
           {"dtype": "int8->fp64", "distinct_rows": int(u), "hit_rate": float((r >= 0).mean()),
            "ops_us": {"lookup_only": float(np.median(t_look) * 1e6), "score": float(np.median(t_score) * 1e6)},
            "lookup_roofline": _roof("mz_probe<8>", look_bytes, float(np.median(t_look))),
-           "score_fp64_ops_per_s": float(3 * n * D / np.median(t_score))})
+           "score_valu_ops_per_s": float(3 * n * D / np.median(t_score))})
 
 
 def _marker(timer, cur, store):

@@ -227,8 +227,10 @@ hlr_status ema_update_apply(float *table, int64_t num_rows, int64_t dim, const f
  *  scale[num_rows], bias[num_rows] fp32: x_d = q_d*scale + bias.
  *  rows[num_requests*cands_per_request] (from a lookup-only MPZCH call);
  *  user_vecs[num_requests*dim] fp32.
- *  out_scores[r*cands + c] = sum_d x_d * user[r][d], dequantisation and sum
- *  evaluated in fp64 and rounded once to fp32; a row of -1 scores 0.0f.
+ *  out_scores[r*cands + c] = sum_d x_d * user[r][d], evaluated in fp64 as
+ *  scale*sum_d q_d*u_d + bias*sum_d u_d (the same sum up to fp64 rounding
+ *  order) and rounded once to fp32; a row of -1, or any row outside
+ *  [0, num_rows), scores 0.0f and is not read.  num_rows = 0: all 0.0f.
  * --------------------------------------------------------------------- */
 hlr_status gather_dequant_score(const int8_t *qtable, const float *scale, const float *bias, int64_t num_rows,
                                 int64_t dim, const int64_t *rows, int64_t num_requests,

@@ -297,6 +297,34 @@ def test_dequant_score(dev, R, K, D):
     assert np.all(got[rows.reshape(R, K) < 0] == 0.0)
 
 
+def test_dequant_score_edge_cases(dev):
+    """An empty table scores every candidate 0; a ragged last block of candidates (K % 64 != 0)
+    and rows at both ends of the table match the oracle."""
+    R, K, D = 2, 5, 256
+    user = torch.ones((R, D), dtype=torch.float32, device=dev)
+    rows = torch.full((R * K,), -1, dtype=torch.int64, device=dev)
+    empty_q = torch.empty((0, D), dtype=torch.int8, device=dev)
+    empty_f = torch.empty(0, dtype=torch.float32, device=dev)
+    out = hlr.gather_dequant_score(empty_q, empty_f, empty_f, rows, user, K)
+    assert np.array_equal(to_np(out), np.zeros(R * K, np.float32).reshape(out.shape))
+    g = np.random.default_rng(77)
+    C, K = 130, 129
+    q = g.integers(-128, 128, size=(C, D)).astype(np.int8)
+    scale = (g.random(C) * 0.01 + 1e-4).astype(np.float32)
+    bias = (g.standard_normal(C) * 0.1).astype(np.float32)
+    rows = g.integers(0, C, size=R * K).astype(np.int64)
+    rows[:4] = [0, C - 1, C, -5]
+    user = g.standard_normal((R, D)).astype(np.float32)
+    out = hlr.gather_dequant_score(*(torch.from_numpy(x).to(dev) for x in (q, scale, bias, rows, user)), K)
+    ref = oracle.dequant_score(q, scale, bias, np.where((rows >= 0) & (rows < C), rows, -1), user, K)
+    x = q.astype(np.float64) * scale[:, None] + bias[:, None]
+    cond = np.einsum("rkd,rd->rk", np.abs(x[np.clip(rows, 0, C - 1)].reshape(R, K, D)),
+                     np.abs(user.astype(np.float64)))
+    got = to_np(out)
+    assert np.all(np.abs(got.astype(np.float64) - ref) <= 1e-6 * cond)
+    assert got.reshape(-1)[2] == 0.0 and got.reshape(-1)[3] == 0.0
+
+
 def test_hashed_rows(dev):
     ids = np.concatenate([np.arange(-50, 50), synth.dlrm_keys(synth.DLRM, 1, 1)[:5000]]).astype(np.int64)
     for nr in [1, 7, 4 * synth.MI, 24 * synth.MI]:
