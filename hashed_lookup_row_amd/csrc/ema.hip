@@ -78,6 +78,13 @@ __global__ void __launch_bounds__(kThreads)
 
 __device__ __forceinline__ float ema1(float t, float v, float a, float b) { return a * t + b * v; }
 
+// A heavy chunk is one dependent chain per element, so its speed is set by how
+// many of its positions are requested ahead: its waves walk 16-element slices,
+// four positions per load instruction, 56 instructions (224 positions) a batch.
+constexpr int kHeavyG = 4;
+constexpr int kHeavyP = 56;
+using HeavySlices = Narrow<kHeavyG>;
+
 // Heavy rows: one wave per (chunk of <= L occurrences, 64-element slice).  A
 // row with one chunk is applied exactly from its stored value.  For a longer
 // row, chunk 0 runs exactly; chunk m > 0 starts W occurrences early from a zero
@@ -89,13 +96,14 @@ __global__ void __launch_bounds__(kThreads)
               const uint32_t *__restrict__ spos, const int32_t *__restrict__ seg_start,
               const int32_t *__restrict__ seg_end, const uint32_t *__restrict__ counters,
               const int2 *__restrict__ hlist, float a, float b, int64_t D, int L, int W, float *partial) {
-  const int64_t S = num_slices(D);
+  const int64_t S = HeavySlices::slices(D);
   const int64_t items = static_cast<int64_t>(counters[0]) * S;
   const int64_t waves = static_cast<int64_t>(gridDim.x) * (kThreads / kWave);
   for (int64_t it = (static_cast<int64_t>(blockIdx.x) * kThreads + threadIdx.x) / kWave; it < items; it += waves) {
     const int2 km = hlist[it / S];
-    const int64_t e = (it % S) * kSliceElems + lane_id();
-    const bool act = e < D;
+    const int lane = lane_id();
+    const int64_t e = (it % S) * HeavySlices::kWidth + (lane % HeavySlices::kWidth);
+    const bool act = lane < HeavySlices::kWidth && e < D;  // lane group 0 holds the chain
     const int32_t s = seg_start[km.x], end = seg_end[km.x];
     const int64_t r = skey[s];
     const int32_t j0 = s + km.y * L;
@@ -103,16 +111,24 @@ __global__ void __launch_bounds__(kThreads)
     const bool exact_start = km.y == 0 || j0 - W <= s;
     const int32_t from = exact_start ? s : j0 - W;
     float st = (exact_start && act) ? table[r * D + e] : 0.f;
-    if (end - s <= L) {  // the whole row in one chunk
-      slice_run(vals, spos, s, end, D, e, [&](int32_t, float x) { st = ema1(st, x, a, b); });
+    // A row in one chunk is walked whole.  Otherwise the warm-up (or the exact
+    // prefix) is walked first and the chunk second; sigma is the state between
+    // them.  (One call site for both walks keeps the kernel's code small.)
+    const bool whole = end - s <= L;
+    int32_t w0 = whole ? s : from, w1 = whole ? end : j0;
+    float sig = st;
+    for (int k = 0; k < 2; ++k) {
+      slice_run_narrow<kHeavyG, kHeavyP>(vals, spos, w0, w1, D, e, [&](int32_t, float x) { st = ema1(st, x, a, b); });
+      if (k == 0) {
+        sig = st;
+        w0 = w1;
+        w1 = whole ? w1 : j1;
+      }
+    }
+    if (whole) {
       if (act) table[r * D + e] = st;
       continue;
     }
-    float sig = st;
-    slice_run(vals, spos, from, j1, D, e, [&](int32_t j, float x) {
-      if (j == j0) sig = st;
-      st = ema1(st, x, a, b);
-    });
     if (act) {
       const int64_t slot = run_slot(j0, km.y, L);
       partial[(2 * slot) * D + e] = sig;
@@ -186,15 +202,16 @@ __global__ void __launch_bounds__(kThreads)
 // spent while the two trajectories' roundings fall onto the same value (for
 // a = 0.95 and 0.99 about one 128-element slice in a thousand still differs
 // after W steps; a slice that differs is recomputed by ema_combine).  A chunk's
-// wave walks W + L positions, so chunks are short (L = 256) to keep that chain
-// short; the redundant warm-up work is cheap next to the latency it removes.
-// Without contraction (a outside (0, 1)) rows run whole.
+// wave walks W + L positions and reads a value row for each, so L = max(256,
+// 2W) keeps the redundant warm-up reads at most half of a chunk's; a row of at
+// most L occurrences runs whole, as one exact chain.  Without contraction (a
+// outside (0, 1)) rows run whole.
 inline void ema_plan(float a, int64_t n, int *L, int *W) {
   constexpr int kChunk = 256;
   if (a > 0.f && a < 1.f) {
     const double w = std::ceil(28.0 / -std::log(static_cast<double>(a)));
     *W = static_cast<int>(w < 1048576.0 ? w : 1048576.0);
-    *L = kChunk;
+    *L = 2 * *W > kChunk ? 2 * *W : kChunk;
   } else {
     *W = 0;
     *L = static_cast<int>(n > kChunk ? (n < 0x7fffffff ? n : 0x7fffffff) : kChunk);
@@ -217,7 +234,7 @@ void ema_launch(float *table, const float *vals, SegWork<uint32_t> &w, int cur, 
   ema_light<NC><<<grid, kThreads, 0, s>>>(reinterpret_cast<float4 *>(table), reinterpret_cast<const float4 *>(vals),
                                           w.seg_key, w.v[cur], w.seg_start, w.seg_end, w.nseg, a, b, v4, L, w.ticket,
                                           w.hlist, w.clist);
-  int gh = grid_for(w.n / 32 * num_slices(dim), 4);
+  int gh = grid_for(w.n / 32 * HeavySlices::slices(dim), 4);
   if (gh > 2048) gh = 2048;
   ema_heavy<<<gh, kThreads, 0, s>>>(table, vals, w.k[cur], w.v[cur], w.seg_start, w.seg_end, w.ticket, w.hlist, a,
                                     b, dim, L, W, partial);

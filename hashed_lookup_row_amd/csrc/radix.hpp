@@ -444,18 +444,26 @@ namespace {
 // a slice is kSliceElems consecutive elements of the row (lanes own one each),
 // so a row of D elements has ceil(D / kSliceElems) slices and every slice of
 // every run is its own wave.  slice_run() applies f(j, x) to positions j in
-// [j0, j1) in order.  Positions go in batches of kSlicePrefetch: the rows of a
-// batch are requested together (one 256-byte access per position), then the
-// position indices of the next batch, so they arrive while this batch is
-// consumed.  Indices are read with one vector load (lane u takes position
-// j + u) and broadcast with readlane, which costs no memory round trip of its
-// own.  No row load has a per-lane condition: lanes past the end of the row
-// read element 0 and their results are dropped by the caller; positions past
-// j1 in the last batch re-read position j1 - 1 and are not applied.
+// [j0, j1) in order.  Positions go in batches of P: the rows of a batch are
+// requested together (one 256-byte access per position), then the position
+// indices of the next batch, so they arrive while this batch is consumed.
+// Indices are read with one vector load (lane u takes position j + u) and
+// broadcast with readlane; a row is then read with a buffer load whose base
+// (the row's address) is built in scalar registers and whose offset is the
+// lane's byte offset, so a position costs scalar arithmetic and no per-lane
+// 64-bit address.  No row load has a per-lane condition: lanes past the end of
+// the row read element 0 and their results are dropped by the caller;
+// positions past j1 in the last batch re-read position j1 - 1 and are not
+// applied.  A batch costs one register per position; P + 1 loads in flight
+// stay within the wave's memory counter (at most 63 outstanding).
+//
+// (Keeping two batches in flight across loop iterations was tried: hipcc
+// then copies the in-flight registers at the loop head, which waits for every
+// load, so the single batch is kept.)
 using SliceV = float;
 constexpr int kSliceElems = 64;
 constexpr int kSlicePrefetch = 48;
-static_assert(kSlicePrefetch <= 64, "one index per lane");
+static_assert(kSlicePrefetch <= 62, "one index per lane, counter limit");
 
 __host__ __device__ __forceinline__ int64_t num_slices(int64_t D) { return (D + kSliceElems - 1) / kSliceElems; }
 
@@ -467,11 +475,21 @@ __device__ __forceinline__ uint32_t slice_idx(const uint32_t *__restrict__ spos,
   return spos[jj < j1 ? jj : j1 - 1];
 }
 
-template <typename F>
+// Element `eoff / 4` of row p: word 3 is the gfx9 descriptor for raw 32-bit
+// accesses; the record limit exceeds any offset used here.
+__device__ __forceinline__ SliceV slice_load(const char *base, uint32_t p, uint32_t row_bytes, uint32_t eoff) {
+  char *rp = const_cast<char *>(base) + static_cast<uint64_t>(p) * row_bytes;
+  const __amdgpu_buffer_rsrc_t r = __builtin_amdgcn_make_buffer_rsrc(rp, 0, 0x7fffffff, 0x00020000);
+  return __builtin_bit_cast(SliceV, __builtin_amdgcn_raw_buffer_load_b32(r, eoff, 0, 0));
+}
+
+template <int P = kSlicePrefetch, typename F>
 __device__ __forceinline__ void slice_run(const float *__restrict__ src, const uint32_t *__restrict__ spos, int32_t j0,
                                           int32_t j1, int64_t D, int64_t e, F f) {
-  constexpr int P = kSlicePrefetch;
-  const int64_t ec = e < D ? e : 0;
+  static_assert(P <= 62, "one index per lane, counter limit");
+  const uint32_t eoff = static_cast<uint32_t>(e < D ? e : 0) * static_cast<uint32_t>(sizeof(SliceV));
+  const uint32_t row_bytes = static_cast<uint32_t>(D * sizeof(SliceV));
+  const char *base = reinterpret_cast<const char *>(src);
   j0 = __builtin_amdgcn_readfirstlane(j0);
   j1 = __builtin_amdgcn_readfirstlane(j1);
   if (j0 >= j1) return;
@@ -479,15 +497,76 @@ __device__ __forceinline__ void slice_run(const float *__restrict__ src, const u
   for (int32_t j = j0; j < j1; j += P) {
     SliceV x[P];
 #pragma unroll
-    for (int u = 0; u < P; ++u) {
-      const uint32_t p = __builtin_amdgcn_readlane(pv, u);
-      x[u] = src[static_cast<int64_t>(p) * D + ec];
-    }
+    for (int u = 0; u < P; ++u) x[u] = slice_load(base, __builtin_amdgcn_readlane(pv, u), row_bytes, eoff);
     pv = slice_idx<P>(spos, j + P, j1);  // next batch's indices, behind this batch's rows
     __builtin_amdgcn_sched_barrier(0);     // keep both requests ahead of the consumption below
 #pragma unroll
     for (int u = 0; u < P; ++u)
       if (j + u < j1) f(j + u, x[u]);
+  }
+}
+
+// Narrow slices for long dependent chains.  A chain's speed is the number of
+// its positions in flight, and a wave has at most 63 loads outstanding, so
+// here one load instruction fetches G positions: the wave's lanes form G
+// groups of 64/G lanes, group h reading position j + G*u + h of instruction u
+// (a slice of 64/G elements, lane l holding element l % (64/G)).  Group 0 runs
+// the chain: before each position is applied its value is moved from group h
+// to group 0 with a lane permute (off the chain's dependency path).  The
+// other groups' lanes run the same arithmetic on values that are dropped: the
+// caller keeps only group 0's results.  Indices come in by vector loads of up
+// to 64 positions and reach each group by lane permute.  P instructions per
+// batch plus the index loads stay within the 63-load counter.
+template <int G>
+struct Narrow {
+  static constexpr int kWidth = 64 / G;  // slice width in elements
+  __host__ __device__ static constexpr int64_t slices(int64_t D) { return (D + kWidth - 1) / kWidth; }
+};
+
+template <int G, int P, typename F>
+__device__ __forceinline__ void slice_run_narrow(const float *__restrict__ src, const uint32_t *__restrict__ spos,
+                                                 int32_t j0, int32_t j1, int64_t D, int64_t e, F f) {
+  constexpr int W = 64 / G;
+  constexpr int NP = G * P;
+  constexpr int NI = (NP + 63) / 64;
+  static_assert(64 % G == 0 && P + NI <= 63, "counter limit");
+  const int lane = hlr::lane_id();
+  const int h = lane / W;
+  const int64_t ec = e < D ? e : 0;
+  j0 = __builtin_amdgcn_readfirstlane(j0);
+  j1 = __builtin_amdgcn_readfirstlane(j1);
+  if (j0 >= j1) return;
+  uint32_t pv[NI];
+#pragma unroll
+  for (int i = 0; i < NI; ++i) {
+    const int32_t jj = j0 + 64 * i + lane;
+    pv[i] = spos[jj < j1 ? jj : j1 - 1];
+  }
+  for (int32_t j = j0; j < j1; j += NP) {
+    SliceV x[P];
+#pragma unroll
+    for (int u = 0; u < P; ++u) {
+      const uint32_t p = static_cast<uint32_t>(__shfl(static_cast<int>(pv[(G * u) / 64]), (G * u) % 64 + h));
+      x[u] = src[static_cast<int64_t>(p) * D + ec];
+    }
+#pragma unroll
+    for (int i = 0; i < NI; ++i) {  // next batch's indices, behind this batch's rows
+      const int32_t jj = j + NP + 64 * i + lane;
+      pv[i] = spos[jj < j1 ? jj : j1 - 1];
+    }
+    __builtin_amdgcn_sched_barrier(0);
+    if (j + NP <= j1) {  // a full batch: no per-position condition
+#pragma unroll
+      for (int u = 0; u < P; ++u)
+#pragma unroll
+        for (int g = 0; g < G; ++g) f(j + G * u + g, g == 0 ? x[u] : __shfl(x[u], g * W + (lane & (W - 1))));
+    } else {
+#pragma unroll
+      for (int u = 0; u < P; ++u)
+#pragma unroll
+        for (int g = 0; g < G; ++g)
+          if (j + G * u + g < j1) f(j + G * u + g, g == 0 ? x[u] : __shfl(x[u], g * W + (lane & (W - 1))));
+    }
   }
 }
 

@@ -348,8 +348,10 @@ def test_repeat_runs_are_bit_identical(dev):
     assert bits_equal(outs[0], outs[1])
 
 
-def test_ema_long_row_many_chunks(dev):
-    """One row with 40,000 occurrences (a = 0.95): dozens of speculative chunks, bit-exact."""
+@pytest.mark.parametrize("a,b", [(0.95, 0.05), (0.99, 0.01), (0.9, 0.1)])
+def test_ema_long_row_many_chunks(dev, a, b):
+    """One row with 36,000 occurrences and one with 4,000: many speculative chunks (warm-up
+    ceil(28 / -ln a), chunks of twice that), bit-exact."""
     g = np.random.default_rng(40)
     n, D = 40_000, 128
     rows = np.zeros(n, np.int64)
@@ -357,8 +359,8 @@ def test_ema_long_row_many_chunks(dev):
     vals = g.standard_normal((n, D)).astype(np.float32)
     table = g.standard_normal((2, D)).astype(np.float32)
     t = torch.from_numpy(table).to(dev)
-    hlr.ema_update_rows(t, torch.from_numpy(rows).to(dev), torch.from_numpy(vals).to(dev), None, 0.95, 0.05)
-    oracle.ema(table, rows, vals, None, 0.95, 0.05)
+    hlr.ema_update_rows(t, torch.from_numpy(rows).to(dev), torch.from_numpy(vals).to(dev), None, a, b)
+    oracle.ema(table, rows, vals, None, a, b)
     assert bits_equal(to_np(t), table)
 
 
