@@ -170,8 +170,8 @@ def main():
     pipe = MemoryLayerPipeline(identity, stamps, values, P, n, depth=2)
 
     def piped_step(t, evs=None):
-        mark = (lambda j: timer.record(evs[j], cur)) if evs is not None else None
-        pipe.step(ids_dev[t], base_now + 1 + t, e_pool[t % npool], out=out, mark=mark)
+        # one library call per batch (memory_layer_step); evs: timing events around the gather
+        pipe.step(ids_dev[t], base_now + 1 + t, e_pool[t % npool], out=out, gather_events=evs)
 
     def serial_step(t, evs=None, stats_out=None):
         if evs is not None:

@@ -72,6 +72,8 @@ def load_library():
             "dks_workspace_size": (sz, [i64]),
             "dks_lookup_or_insert": (i32, [p, p, i64, p, p, i64, i64, p, p, i64, i64, i32, p, p, p, p, sz, p]),
             "dks_rehash": (i32, [p, p, i64, p, p, i64, p]),
+            "memory_layer_step": (i32, [p, p, p, i64, i32, i64, p, i64, i64, p, p, p, p, p, p, p, sz, p, sz,
+                                        p, p, p, p, p, p, p, p]),
         }
         for name, (res, args) in sig.items():
             f = getattr(lib, name)
@@ -87,7 +89,7 @@ def exported_symbols():
             "writeback_rows", "ema_update_rows_workspace_size", "ema_update_rows", "gather_dequant_score",
             "hashed_rows", "mpzch_zero_inserted", "writeback_plan", "writeback_apply", "ema_update_plan",
             "ema_update_apply", "writeback_plan_rows", "quantize_rows_int8", "mark_rows", "clear_marks",
-            "dks_workspace_size", "dks_lookup_or_insert", "dks_rehash"]
+            "dks_workspace_size", "dks_lookup_or_insert", "dks_rehash", "memory_layer_step"]
 
 
 def _check(rc: int, what: str):

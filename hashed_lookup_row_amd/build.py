@@ -23,7 +23,7 @@ INCLUDE = os.path.join(ROOT, "include")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(HERE, "libhlr.so")
 
-SOURCES = ["capi.hip", "mpzch.hip", "gather.hip", "dedup.hip", "writeback.hip", "ema.hip", "score.hip", "quantize.hip", "publish.hip", "keystore.hip"]
+SOURCES = ["capi.hip", "mpzch.hip", "gather.hip", "dedup.hip", "writeback.hip", "ema.hip", "score.hip", "quantize.hip", "publish.hip", "keystore.hip", "step.hip"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 FLAGS = [

@@ -32,10 +32,10 @@ from __future__ import annotations
 import torch
 
 from ._hip import hip
-from . import (WB_LAST_WINS, WB_SGD_SUM, clear_marks, ema_update_apply, ema_update_plan, ema_workspace_size,
-               gather_rows, hashed_rows, mark_rows, mpzch_lookup_or_insert, mpzch_workspace_size,
-               mpzch_zero_inserted, new_workspace, quantize_rows_int8, writeback_apply, writeback_plan,
-               writeback_plan_rows, writeback_workspace_size)
+from . import (WB_LAST_WINS, WB_SGD_SUM, HLRError, _check, _dev, _own_ws, clear_marks, ema_update_apply,
+               ema_update_plan, ema_workspace_size, gather_rows, hashed_rows, load_library, mark_rows,
+               mpzch_lookup_or_insert, mpzch_workspace_size, mpzch_zero_inserted, new_workspace, quantize_rows_int8,
+               writeback_apply, writeback_plan, writeback_plan_rows, writeback_workspace_size)
 
 
 class _Ring:
@@ -95,9 +95,13 @@ class MemoryLayerPipeline:
     lookup stream:  mpzch_lookup_or_insert(values=None) -> writeback_plan(LAST_WINS)
     compute stream: mpzch_zero_inserted -> gather_rows -> writeback_apply(LAST_WINS)
     step() returns the gathered rows (on the compute stream) and leaves rows/hit of
-    the batch in ring slot k (`rows(k)`, `hit(k)`)."""
+    the batch in ring slot k (`rows(k)`, `hit(k)`).
 
-    def __init__(self, identity, stamps, values, probes, n, depth=2):
+    With native=True (the default) a batch is enqueued by one library call
+    (memory_layer_step) whenever no per-call hook (mark, publisher) is given; the
+    schedule and the results are the same as the call-by-call path."""
+
+    def __init__(self, identity, stamps, values, probes, n, depth=2, native=True):
         self.identity, self.stamps, self.values, self.probes, self.n = identity, stamps, values, probes, n
         dev = values.device
         self.ring = _Ring(dev, depth, points=2)
@@ -107,6 +111,15 @@ class MemoryLayerPipeline:
         self._hit = [torch.empty(n, dtype=torch.int8, device=dev) for _ in range(depth)]
         self._ws = [new_workspace(dev, wsb) for _ in range(depth)]
         self._mz_ws = new_workspace(dev, mpzch_workspace_size(n))
+        self.native = native
+        if native:
+            for t, name, dt in ((identity, "identity", torch.int64), (stamps, "stamps", torch.int64),
+                                (values, "values", torch.float32)):
+                _dev(t, name, dt)
+            self._fn = load_library().memory_layer_step
+            self._mz = _own_ws(self._mz_ws, mpzch_workspace_size(n))
+            self._wb = [_own_ws(w, wsb) for w in self._ws]
+            self._const = (identity.data_ptr(), stamps.data_ptr(), values.data_ptr(), C, int(probes), D)
 
     def restart(self):
         self.ring.restart()
@@ -117,11 +130,19 @@ class MemoryLayerPipeline:
     def hit(self, k):
         return self._hit[k]
 
-    def step(self, ids, now, e, out=None, evicted=None, stats=None, mark=None, publisher=None):
+    def step(self, ids, now, e, out=None, evicted=None, stats=None, mark=None, publisher=None, gather_events=None):
         """mark: optional callable, called with 0 just before and 1 just after the gather is
         enqueued on the compute stream (e.g. to record timing events there).
+        gather_events: optional pair of HIP events recorded on the compute stream around the gather.
         publisher: optional RESPublisher; it collects the rows this batch wrote and publishes
         them at its own cadence."""
+        if self.native and mark is None and publisher is None:
+            return self._native_step(ids, now, e, out, evicted, stats, gather_events)
+        if gather_events is not None:
+            if mark is not None:
+                raise ValueError("give mark or gather_events, not both")
+            h, cs = self.ring.hip, self.ring.cs
+            mark = lambda j: h.record(gather_events[j], cs)  # noqa: E731
         r = self.ring
         k = r.begin_lookup()
         _on(r.lookup, ids, evicted, stats)
@@ -145,6 +166,34 @@ class MemoryLayerPipeline:
         if publisher is not None:
             publisher.after_apply(self, self._ws[k])
         r.end_compute(k)
+        return out, k
+
+    def _native_step(self, ids, now, e, out, evicted, stats, gather_events):
+        r = self.ring
+        C, P, D = self._const[3], self._const[4], self._const[5]
+        n = ids.numel()
+        if not (ids.is_cuda and ids.dtype == torch.int64 and ids.is_contiguous() and n <= self.n):
+            raise HLRError(f"ids must be a contiguous GPU int64 tensor of at most {self.n} elements")
+        if not (e.is_cuda and e.dtype == torch.float32 and e.is_contiguous() and e.numel() == n * D):
+            raise HLRError(f"e must be a contiguous GPU float32 tensor of {n} x {D} elements")
+        for t, name, dt, m in ((evicted, "evicted", torch.int64, n), (stats, "stats", torch.int64, 6)):
+            if t is not None and not (t.is_cuda and t.dtype == dt and t.is_contiguous() and t.numel() >= m):
+                raise HLRError(f"{name} must be a contiguous GPU {dt} tensor of at least {m} elements")
+        if out is None:
+            out = torch.empty((n, D), dtype=torch.float32, device=self.values.device)
+        elif not (out.is_cuda and out.dtype == torch.float32 and out.is_contiguous() and out.numel() == n * D):
+            raise HLRError(f"out must be a contiguous GPU float32 tensor of {n} x {D} elements")
+        k = r.t % r.depth
+        _on(r.lookup, ids, evicted, stats)
+        gb, ge = gather_events if gather_events is not None else (None, None)
+        mz, mzb = self._mz
+        wb, wbb = self._wb[k]
+        rc = self._fn(*self._const, ids.data_ptr(), n, int(now), e.data_ptr(), self._rows[k].data_ptr(),
+                      self._hit[k].data_ptr(), None if evicted is None else evicted.data_ptr(),
+                      None if stats is None else stats.data_ptr(), out.data_ptr(), mz, mzb, wb, wbb, r.ls, r.cs,
+                      r.done[k] if r.t >= r.depth else None, r.marks[k][0], r.marks[k][1], gb, ge, r.done[k])
+        _check(rc, "memory_layer_step")
+        r.t += 1
         return out, k
 
 

@@ -9,7 +9,10 @@
  *         Recommendation", sec. 2 (method: CTS and CMS);
  *  [DLRM] "DLRMv4: MLPerf recommendation training goes sequential", feature
  *         expansion paragraph (hashed tables, 512-d fp32 rows, per-token
- *         unpooled lookups).
+ *         unpooled lookups);
+ *  [MTGR] "MTGR: Industrial-Scale Generative Recommendation Framework in
+ *         Meituan", sec. 3.2 (dynamic hash table) and sec. 3.5 (dispatch and
+ *         compute streams).
  *
  * Conventions shared by every entry point
  *  - Array arguments are DEVICE pointers on the current HIP device, owned by
@@ -312,6 +315,43 @@ hlr_status dks_rehash(const int64_t *keys, const int64_t *krows, int64_t key_cap
  *  allowed; no identity tensor).  num_rows >= 1.
  * --------------------------------------------------------------------- */
 hlr_status hashed_rows(const int64_t *ids, int64_t n, int64_t num_rows, int64_t *out_rows, hipStream_t stream);
+
+/* ------------------------------------------------------------------------
+ * One Memory-Layer training batch in one host call   [ML] sec. 2 (lookup,
+ * gather, Writeback with lr = 1); two-stream overlap as the dispatch and
+ * compute streams of [MTGR] sec. 3.5.
+ *  Enqueues, in this order:
+ *   lookup stream:  wait slot_free (if given);
+ *                   mpzch_lookup_or_insert(values = NULL, insert = 1);
+ *                   record looked_up;
+ *                   writeback_plan(LAST_WINS) over out_rows into wb_ws;
+ *                   record planned.
+ *   compute stream: wait looked_up; mpzch_zero_inserted;
+ *                   record gather_begin (if given); gather_rows into out;
+ *                   record gather_end (if given); wait planned;
+ *                   writeback_apply(LAST_WINS, lr = 1) with e;
+ *                   record slot_done (if given).
+ *  The results equal those calls made one after another on one stream:
+ *  identity/stamps/values updated, out_rows/out_hit/out_evicted/out_stats as
+ *  mpzch_lookup_or_insert, out[n*dim] the gathered rows (read before the
+ *  Writeback), values[r] <- fl(M - fl(M - e[last position of r])).
+ *  Arguments as the calls above; capacity = the table's row count.  Events are
+ *  the caller's (hipEventCreateWithFlags; timing needed only for the gather
+ *  pair); looked_up and planned are required, the others nullable
+ *  (gather_begin and gather_end together).  mz_ws / wb_ws: workspaces of
+ *  mpzch_lookup_or_insert_workspace_size(n, 1) and
+ *  writeback_rows_workspace_size(capacity, dim, n, HLR_WB_LAST_WINS) bytes;
+ *  out_rows, out_hit and wb_ws stay in use until slot_done.
+ *  Host-checkable errors return before anything is enqueued; a HIP error
+ *  from a later call returns HLR_HIP_ERROR with the batch partly enqueued.
+ * --------------------------------------------------------------------- */
+hlr_status memory_layer_step(int64_t *identity, int64_t *stamps, float *values, int64_t capacity, int32_t probes,
+                             int64_t dim, const int64_t *ids, int64_t n, int64_t now, const float *e,
+                             int64_t *out_rows, int8_t *out_hit, int64_t *out_evicted, int64_t *out_stats,
+                             float *out, void *mz_ws, size_t mz_ws_bytes, void *wb_ws, size_t wb_ws_bytes,
+                             hipStream_t lookup, hipStream_t compute, hipEvent_t slot_free, hipEvent_t looked_up,
+                             hipEvent_t planned, hipEvent_t gather_begin, hipEvent_t gather_end,
+                             hipEvent_t slot_done);
 
 #ifdef __cplusplus
 }

@@ -164,6 +164,30 @@ def test_key_store_argument_errors(lib):
     assert lib.dks_rehash(P_ODD, P16, 1024, P16, P16, 2048, s) == MISALIGNED
 
 
+def test_memory_layer_step_argument_errors(lib):
+    """Every host-checkable fault returns before anything is enqueued (no stream or event is touched)."""
+    s = None
+    n, C, D, P = 1000, 4096, 64, 8
+    mzb = lib.mpzch_lookup_or_insert_workspace_size(n, 1)
+    wbb = lib.writeback_rows_workspace_size(C, D, n, 0)
+
+    def call(cap=C, probes=P, dim=D, n=n, values=P16, ids=P16, mzb=mzb, wbb=wbb, looked=P16, planned=P16,
+             gb=None, ge=None):
+        return lib.memory_layer_step(P16, P16, values, cap, probes, dim, ids, n, 5, P16, P16, P16, None, None,
+                                     P16, P16, mzb, P16, wbb, s, s, None, looked, planned, gb, ge, None)
+    assert call(cap=4095) == INVALID                 # capacity % probes
+    assert call(probes=0) == INVALID
+    assert call(n=-1) == INVALID
+    assert call(dim=6) == DIM
+    assert call(values=None) == INVALID
+    assert call(ids=None) == INVALID
+    assert call(looked=None) == INVALID              # ordering events are required
+    assert call(gb=P16) == INVALID                   # gather events come in pairs
+    assert call(values=P_ODD) == MISALIGNED
+    assert call(mzb=mzb - 1) == WS_SMALL
+    assert call(wbb=wbb - 1) == WS_SMALL
+
+
 def test_score_dedup_hashed_argument_errors(lib):
     s = None
     assert lib.gather_dequant_score(P16, P16, P16, 10, 520, P16, 2, 3, P16, P16, s) == DIM

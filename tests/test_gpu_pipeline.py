@@ -113,8 +113,9 @@ def test_lookup_without_values_then_zero_inserted(dev):
         assert bits_equal(to_np(values), o.values), f"step {t}"
 
 
-@pytest.mark.parametrize("depth", [2, 3])
-def test_memory_layer_pipeline(dev, depth):
+@pytest.mark.parametrize("depth,native", [(2, True), (3, True), (2, False)])
+def test_memory_layer_pipeline(dev, depth, native):
+    """The batch as one library call (native) and as seven, both against the oracle."""
     cfg = synth.scaled_memory_layer(capacity=16_384, universe=120_000, batch=8_192, steps=8)
     C, P, D, n = cfg.capacity, cfg.probes, cfg.dim, cfg.batch
     identity, stamps, o, base = prefilled_pair(dev, cfg)
@@ -127,7 +128,7 @@ def test_memory_layer_pipeline(dev, depth):
     evs = [torch.empty(n, dtype=torch.int64, device=dev) for _ in ids]
     sts = [torch.zeros(6, dtype=torch.int64, device=dev) for _ in ids]
     torch.cuda.synchronize()
-    pipe = pipeline.MemoryLayerPipeline(identity, stamps, values, P, n, depth=depth)
+    pipe = pipeline.MemoryLayerPipeline(identity, stamps, values, P, n, depth=depth, native=native)
     for t in range(cfg.steps):  # no synchronisation between batches
         pipe.step(ids[t], base + t + 1, es[t], out=outs[t], evicted=evs[t], stats=sts[t])
     last_rows = [to_np(pipe.rows(k)).copy() for k in range(depth)]
