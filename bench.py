@@ -71,6 +71,9 @@ def parse():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--depth", type=int, default=3, help="ring depth of the two-stream schedule")
+    ap.add_argument("--no-lookahead", dest="lookahead", action="store_false",
+                    help="enqueue each batch's lookup with its own row traffic instead of one batch ahead")
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--e-pool", type=int, default=16, help="distinct e batches cycled through")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -141,7 +144,7 @@ def main():
     t0 = time.time()
     prefill = synth.prefill_batches(cfg)
     stream, fc = [], 0
-    for t in range(1, W + 2 * K + 2):
+    for t in range(1, W + 2 * K + 3):
         ids, fc = synth.mpzch_step_ids(cfg, t, fc)
         stream.append(ids)
     print(f"[bench] generated inputs in {time.time() - t0:.1f}s", file=sys.stderr, flush=True)
@@ -167,10 +170,13 @@ def main():
 
     timer = HipTimer()
     cur = torch.cuda.current_stream(dev).cuda_stream
-    pipe = MemoryLayerPipeline(identity, stamps, values, P, n, depth=2)
+    pipe = MemoryLayerPipeline(identity, stamps, values, P, n, depth=args.depth)
 
-    def piped_step(t, evs=None):
-        # one library call per batch (memory_layer_step); evs: timing events around the gather
+    def piped_step(t, evs=None, ahead=None):
+        # one library call per half batch (memory_layer_step): the lookup half of batch `ahead` (the next
+        # one) is enqueued before the row traffic of batch t; evs: timing events around the gather
+        if ahead is not None:
+            pipe.prefetch(ids_dev[ahead], base_now + 1 + ahead)
         pipe.step(ids_dev[t], base_now + 1 + t, e_pool[t % npool], out=out, gather_events=evs)
 
     def serial_step(t, evs=None, stats_out=None):
@@ -187,8 +193,11 @@ def main():
         if evs is not None:
             timer.record(evs[3], cur)
 
+    la = args.lookahead
+    if la:
+        pipe.prefetch(ids_dev[0], base_now + 1)
     for t in range(W):
-        piped_step(t)
+        piped_step(t, ahead=t + 1 if la else None)
     torch.cuda.synchronize()
 
     # two-stream schedule (the headline): gather timed with HIP events on the compute stream on every
@@ -199,8 +208,8 @@ def main():
     torch.cuda.synchronize()
     wall0 = time.perf_counter()
     timer.record(start, cur)
-    for k in range(K):
-        piped_step(W + k, evs.get(k))
+    for k in range(K):  # with lookahead: K lookup halves (W+1 .. W+K) and K row halves (W .. W+K-1)
+        piped_step(W + k, evs.get(k), ahead=W + k + 1 if la else None)
     timer.record(stop, cur)
     enqueue = time.perf_counter() - wall0
     torch.cuda.synchronize()
@@ -209,19 +218,24 @@ def main():
     gather_s = np.array([timer.elapsed_s(e[0], e[1]) for e in evs.values()])
     gather_steps = np.array(sorted(evs.keys()))
 
+    if la:  # the row half of the batch looked up last, outside the timed region
+        piped_step(W + K)
+        torch.cuda.synchronize()
+    off = 1 if la else 0
+
     # the same step as three calls on one stream, over the next K batches (reported beside the headline)
     sevs = {k: [timer.event() for _ in range(4)] for k in range(K)} if args.op_events else {}
     s_start, s_stop = timer.event(), timer.event()
     timer.record(s_start, cur)
     for k in range(K):
-        serial_step(W + K + k, sevs.get(k))
+        serial_step(W + K + off + k, sevs.get(k))
     timer.record(s_stop, cur)
     torch.cuda.synchronize()
     serial_s = timer.elapsed_s(s_start, s_stop)
     per_op = np.array([[timer.elapsed_s(e[i], e[i + 1]) for i in range(3)] for e in sevs.values()]) \
         if args.op_events else None
     # one more step after the timed regions reports the optional MPZCH stats (hit rate, inserts, ...)
-    serial_step(W + 2 * K, None, stats)
+    serial_step(W + 2 * K + off, None, stats)
     torch.cuda.synchronize()
     # distinct rows per timed step (for algorithmic bytes): MPZCH gives every distinct valid ID its own
     # row and no two IDs share one, so u = distinct IDs minus those without a row (overflows and
@@ -259,8 +273,11 @@ def main():
             "capacity": C, "dim": D, "probes": P, "ids_per_step": n, "universe": cfg.universe,
             "zipf_s": cfg.zipf_s, "fresh_frac": cfg.fresh_frac, "prefilled": True,
             "step": "mpzch_lookup_or_insert + gather_rows + writeback_rows(last_wins, lr=1)",
-            "schedule": "two streams: lookup (MPZCH without values, Writeback plan) beside compute (zero-fill of "
-                        "new rows, gather, Writeback apply); batch t's lookup overlaps batch t-1's row traffic",
+            "schedule": ("two streams: lookup (MPZCH without values, Writeback plan) beside compute (zero-fill of "
+                         "new rows, gather, Writeback apply), one library call per half batch; "
+                         + (f"lookahead: batch t+1's lookup is enqueued before batch t's row traffic, ring depth "
+                            f"{args.depth}" if la else f"batch t's lookup with its own row traffic, ring depth "
+                                                       f"{args.depth}")),
         },
         "roofline": {
             "bound": "hbm", "kernel": "gather_kernel<128>",

@@ -73,7 +73,7 @@ def load_library():
             "dks_lookup_or_insert": (i32, [p, p, i64, p, p, i64, i64, p, p, i64, i64, i32, p, p, p, p, sz, p]),
             "dks_rehash": (i32, [p, p, i64, p, p, i64, p]),
             "memory_layer_step": (i32, [p, p, p, i64, i32, i64, p, i64, i64, p, p, p, p, p, p, p, sz, p, sz,
-                                        p, p, p, p, p, p, p, p]),
+                                        p, p, p, p, p, p, p, p, i32]),
         }
         for name, (res, args) in sig.items():
             f = getattr(lib, name)

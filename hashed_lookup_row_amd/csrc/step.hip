@@ -7,7 +7,10 @@
 // of "MTGR: Industrial-Scale Generative Recommendation Framework in Meituan",
 // sec. 3.5.  The calls are the library's own entry points, so the batch gives
 // the same results as those calls made one after another on one stream; one
-// host call instead of seven keeps the host ahead of the GPU.
+// host call instead of seven keeps the host ahead of the GPU.  The two halves
+// can also be enqueued by separate calls, so that a caller enqueues the
+// ID-side half of batch t+1 before the row traffic of batch t (lookahead): the
+// lookup kernels then find the GPU ready while the previous batch's rows move.
 #include <hip/hip_runtime.h>
 
 #include "hlr.h"
@@ -25,30 +28,37 @@ extern "C" hlr_status memory_layer_step(int64_t *identity, int64_t *stamps, floa
                                         int64_t *out_stats, float *out, void *mz_ws, size_t mz_ws_bytes,
                                         void *wb_ws, size_t wb_ws_bytes, hipStream_t lookup, hipStream_t compute,
                                         hipEvent_t slot_free, hipEvent_t looked_up, hipEvent_t planned,
-                                        hipEvent_t gather_begin, hipEvent_t gather_end, hipEvent_t slot_done) {
+                                        hipEvent_t gather_begin, hipEvent_t gather_end, hipEvent_t slot_done,
+                                        int32_t halves) {
   // everything host-checkable first, so that an error enqueues nothing
   if (n < 0 || n > hlr::kMaxN || capacity <= 0 || probes < 1 || probes > 32 || capacity % probes != 0)
     return HLR_INVALID_ARG;
   if (dim <= 0 || dim % 4 != 0) return HLR_UNSUPPORTED_DIM;
-  if (!identity || !stamps || !values || !out_rows || !out_hit || !looked_up || !planned) return HLR_INVALID_ARG;
-  if (n > 0 && (!ids || !e || !out)) return HLR_INVALID_ARG;
+  if (halves < 1 || halves > 3) return HLR_INVALID_ARG;
+  const bool lk = halves & 1, cp = halves & 2;
+  if (!values || !out_rows || !out_hit || !looked_up || !planned) return HLR_INVALID_ARG;
+  if (lk && (!identity || !stamps || (n > 0 && !ids))) return HLR_INVALID_ARG;
+  if (cp && n > 0 && (!e || !out)) return HLR_INVALID_ARG;
   if ((gather_begin == nullptr) != (gather_end == nullptr)) return HLR_INVALID_ARG;
   if (!hlr::aligned(values, 16) || (e && !hlr::aligned(e, 16)) || (out && !hlr::aligned(out, 16)) ||
-      !hlr::aligned(identity, 8) || !hlr::aligned(stamps, 8) || (ids && !hlr::aligned(ids, 8)) ||
-      !hlr::aligned(out_rows, 8))
+      (identity && !hlr::aligned(identity, 8)) || (stamps && !hlr::aligned(stamps, 8)) ||
+      (ids && !hlr::aligned(ids, 8)) || !hlr::aligned(out_rows, 8))
     return HLR_MISALIGNED;
   if (mz_ws_bytes < mpzch_lookup_or_insert_workspace_size(n, 1) ||
       wb_ws_bytes < writeback_rows_workspace_size(capacity, dim, n, HLR_WB_LAST_WINS))
     return HLR_WORKSPACE_TOO_SMALL;
   hlr_status st;
-  // lookup stream
-  if (slot_free && (st = hip_ok(hipStreamWaitEvent(lookup, slot_free, 0))) != HLR_OK) return st;
-  if ((st = mpzch_lookup_or_insert(identity, stamps, nullptr, capacity, probes, dim, ids, n, now, 1, out_rows, out_hit,
-                                   out_evicted, out_stats, mz_ws, mz_ws_bytes, lookup)) != HLR_OK)
-    return st;
-  if ((st = hip_ok(hipEventRecord(looked_up, lookup))) != HLR_OK) return st;
-  if ((st = writeback_plan(capacity, out_rows, n, HLR_WB_LAST_WINS, wb_ws, wb_ws_bytes, lookup)) != HLR_OK) return st;
-  if ((st = hip_ok(hipEventRecord(planned, lookup))) != HLR_OK) return st;
+  if (lk) {  // lookup stream
+    if (slot_free && (st = hip_ok(hipStreamWaitEvent(lookup, slot_free, 0))) != HLR_OK) return st;
+    if ((st = mpzch_lookup_or_insert(identity, stamps, nullptr, capacity, probes, dim, ids, n, now, 1, out_rows,
+                                     out_hit, out_evicted, out_stats, mz_ws, mz_ws_bytes, lookup)) != HLR_OK)
+      return st;
+    if ((st = hip_ok(hipEventRecord(looked_up, lookup))) != HLR_OK) return st;
+    if ((st = writeback_plan(capacity, out_rows, n, HLR_WB_LAST_WINS, wb_ws, wb_ws_bytes, lookup)) != HLR_OK)
+      return st;
+    if ((st = hip_ok(hipEventRecord(planned, lookup))) != HLR_OK) return st;
+  }
+  if (!cp) return HLR_OK;
   // compute stream
   if ((st = hip_ok(hipStreamWaitEvent(compute, looked_up, 0))) != HLR_OK) return st;
   if ((st = mpzch_zero_inserted(values, capacity, dim, out_rows, out_hit, n, compute)) != HLR_OK) return st;

@@ -29,6 +29,8 @@ lookup stream does not wait for the compute stream.
 """
 from __future__ import annotations
 
+from collections import deque
+
 import torch
 
 from ._hip import hip
@@ -99,7 +101,14 @@ class MemoryLayerPipeline:
 
     With native=True (the default) a batch is enqueued by one library call
     (memory_layer_step) whenever no per-call hook (mark, publisher) is given; the
-    schedule and the results are the same as the call-by-call path."""
+    schedule and the results are the same as the call-by-call path.
+
+    Lookahead (native only): prefetch(ids, now) enqueues the ID-side half of a later
+    batch right away; the step() of that batch (same ids tensor, same now) then
+    enqueues only its row traffic.  Calling prefetch(batch t+1) before step(batch t)
+    lets the lookup kernels of t+1 run beside the row traffic of t instead of after
+    it (the data loader usually has the next batch's IDs early).  At most `depth`
+    batches may be looked up and not yet stepped."""
 
     def __init__(self, identity, stamps, values, probes, n, depth=2, native=True):
         self.identity, self.stamps, self.values, self.probes, self.n = identity, stamps, values, probes, n
@@ -120,15 +129,32 @@ class MemoryLayerPipeline:
             self._mz = _own_ws(self._mz_ws, mpzch_workspace_size(n))
             self._wb = [_own_ws(w, wsb) for w in self._ws]
             self._const = (identity.data_ptr(), stamps.data_ptr(), values.data_ptr(), C, int(probes), D)
+        self._tl = 0              # lookup halves enqueued (the ring's t counts row halves)
+        self._ahead = deque()     # (ids, now, slot, evicted, stats) looked up ahead of their step()
 
     def restart(self):
+        if self._ahead:
+            raise HLRError("restart() with batches looked up ahead of step()")
         self.ring.restart()
+        self._tl = 0
 
     def rows(self, k):
         return self._rows[k]
 
     def hit(self, k):
         return self._hit[k]
+
+    def prefetch(self, ids, now, evicted=None, stats=None):
+        """Enqueues the ID-side half (lookup/insert, Writeback plan) of a later batch now."""
+        if not self.native:
+            raise HLRError("prefetch() needs native=True")
+        r = self.ring
+        if self._tl - r.t >= r.depth:  # lookup j reuses the slot of row half j - depth, which must be enqueued
+            raise HLRError(f"at most {r.depth} batches may be looked up and not yet stepped")
+        self._check_ids(ids, evicted, stats)
+        k = self._tl % r.depth
+        self._call(ids, now, None, None, evicted, stats, None, k, 1)
+        self._ahead.append((ids, int(now), k, evicted, stats))
 
     def step(self, ids, now, e, out=None, evicted=None, stats=None, mark=None, publisher=None, gather_events=None):
         """mark: optional callable, called with 0 just before and 1 just after the gather is
@@ -138,6 +164,8 @@ class MemoryLayerPipeline:
         them at its own cadence."""
         if self.native and mark is None and publisher is None:
             return self._native_step(ids, now, e, out, evicted, stats, gather_events)
+        if self._ahead:
+            raise HLRError("a step with mark or publisher cannot follow prefetch()")
         if gather_events is not None:
             if mark is not None:
                 raise ValueError("give mark or gather_events, not both")
@@ -168,31 +196,53 @@ class MemoryLayerPipeline:
         r.end_compute(k)
         return out, k
 
-    def _native_step(self, ids, now, e, out, evicted, stats, gather_events):
-        r = self.ring
-        C, P, D = self._const[3], self._const[4], self._const[5]
+    def _check_ids(self, ids, evicted, stats):
         n = ids.numel()
         if not (ids.is_cuda and ids.dtype == torch.int64 and ids.is_contiguous() and n <= self.n):
             raise HLRError(f"ids must be a contiguous GPU int64 tensor of at most {self.n} elements")
+        for t, name, m in ((evicted, "evicted", n), (stats, "stats", 6)):
+            if t is not None and not (t.is_cuda and t.dtype == torch.int64 and t.is_contiguous() and t.numel() >= m):
+                raise HLRError(f"{name} must be a contiguous GPU int64 tensor of at least {m} elements")
+
+    def _call(self, ids, now, e, out, evicted, stats, gather_events, k, halves):
+        r = self.ring
+        if halves & 1:
+            _on(r.lookup, ids, evicted, stats)
+            slot_free = r.done[k] if self._tl >= r.depth else None
+        else:
+            slot_free = None
+        gb, ge = gather_events if gather_events is not None else (None, None)
+        mz, mzb = self._mz
+        wb, wbb = self._wb[k]
+        rc = self._fn(*self._const, ids.data_ptr(), ids.numel(), int(now), None if e is None else e.data_ptr(),
+                      self._rows[k].data_ptr(), self._hit[k].data_ptr(),
+                      None if evicted is None else evicted.data_ptr(), None if stats is None else stats.data_ptr(),
+                      None if out is None else out.data_ptr(), mz, mzb, wb, wbb, r.ls, r.cs, slot_free,
+                      r.marks[k][0], r.marks[k][1], gb, ge, r.done[k], halves)
+        _check(rc, "memory_layer_step")
+        if halves & 1:
+            self._tl += 1
+
+    def _native_step(self, ids, now, e, out, evicted, stats, gather_events):
+        r = self.ring
+        D = self._const[5]
+        n = ids.numel()
         if not (e.is_cuda and e.dtype == torch.float32 and e.is_contiguous() and e.numel() == n * D):
             raise HLRError(f"e must be a contiguous GPU float32 tensor of {n} x {D} elements")
-        for t, name, dt, m in ((evicted, "evicted", torch.int64, n), (stats, "stats", torch.int64, 6)):
-            if t is not None and not (t.is_cuda and t.dtype == dt and t.is_contiguous() and t.numel() >= m):
-                raise HLRError(f"{name} must be a contiguous GPU {dt} tensor of at least {m} elements")
         if out is None:
             out = torch.empty((n, D), dtype=torch.float32, device=self.values.device)
         elif not (out.is_cuda and out.dtype == torch.float32 and out.is_contiguous() and out.numel() == n * D):
             raise HLRError(f"out must be a contiguous GPU float32 tensor of {n} x {D} elements")
-        k = r.t % r.depth
-        _on(r.lookup, ids, evicted, stats)
-        gb, ge = gather_events if gather_events is not None else (None, None)
-        mz, mzb = self._mz
-        wb, wbb = self._wb[k]
-        rc = self._fn(*self._const, ids.data_ptr(), n, int(now), e.data_ptr(), self._rows[k].data_ptr(),
-                      self._hit[k].data_ptr(), None if evicted is None else evicted.data_ptr(),
-                      None if stats is None else stats.data_ptr(), out.data_ptr(), mz, mzb, wb, wbb, r.ls, r.cs,
-                      r.done[k] if r.t >= r.depth else None, r.marks[k][0], r.marks[k][1], gb, ge, r.done[k])
-        _check(rc, "memory_layer_step")
+        if self._ahead:
+            pids, pnow, k, pev, pst = self._ahead[0]
+            if pids is not ids or pnow != int(now) or pev is not evicted or pst is not stats:
+                raise HLRError("step() must take the batches in the order prefetch() looked them up")
+            self._ahead.popleft()
+            self._call(ids, now, e, out, evicted, stats, gather_events, k, 2)
+        else:
+            self._check_ids(ids, evicted, stats)
+            k = self._tl % r.depth
+            self._call(ids, now, e, out, evicted, stats, gather_events, k, 3)
         r.t += 1
         return out, k
 

@@ -342,6 +342,16 @@ hlr_status hashed_rows(const int64_t *ids, int64_t n, int64_t num_rows, int64_t 
  *  mpzch_lookup_or_insert_workspace_size(n, 1) and
  *  writeback_rows_workspace_size(capacity, dim, n, HLR_WB_LAST_WINS) bytes;
  *  out_rows, out_hit and wb_ws stay in use until slot_done.
+ *  halves: 1 = the lookup-stream half only, 2 = the compute-stream half
+ *  only, 3 = both.  A batch's lookup half must be enqueued before its compute
+ *  half (the compute half waits on looked_up and planned as recorded by the
+ *  most recent lookup half); enqueueing the lookup half of batch t+1 before
+ *  the compute half of batch t (lookahead) is allowed and gives the same
+ *  results, since the compute stream keeps the row traffic in batch order.
+ *  Pointers a half does not use may be NULL there (the lookup half does not
+ *  read e or out, the compute half does not read identity, stamps or ids);
+ *  the buffers of a batch (out_rows, out_hit, wb_ws) and its events must be
+ *  the same in both calls.
  *  Host-checkable errors return before anything is enqueued; a HIP error
  *  from a later call returns HLR_HIP_ERROR with the batch partly enqueued.
  * --------------------------------------------------------------------- */
@@ -351,7 +361,7 @@ hlr_status memory_layer_step(int64_t *identity, int64_t *stamps, float *values, 
                              float *out, void *mz_ws, size_t mz_ws_bytes, void *wb_ws, size_t wb_ws_bytes,
                              hipStream_t lookup, hipStream_t compute, hipEvent_t slot_free, hipEvent_t looked_up,
                              hipEvent_t planned, hipEvent_t gather_begin, hipEvent_t gather_end,
-                             hipEvent_t slot_done);
+                             hipEvent_t slot_done, int32_t halves);
 
 #ifdef __cplusplus
 }

@@ -172,9 +172,9 @@ def test_memory_layer_step_argument_errors(lib):
     wbb = lib.writeback_rows_workspace_size(C, D, n, 0)
 
     def call(cap=C, probes=P, dim=D, n=n, values=P16, ids=P16, mzb=mzb, wbb=wbb, looked=P16, planned=P16,
-             gb=None, ge=None):
+             gb=None, ge=None, halves=3):
         return lib.memory_layer_step(P16, P16, values, cap, probes, dim, ids, n, 5, P16, P16, P16, None, None,
-                                     P16, P16, mzb, P16, wbb, s, s, None, looked, planned, gb, ge, None)
+                                     P16, P16, mzb, P16, wbb, s, s, None, looked, planned, gb, ge, None, halves)
     assert call(cap=4095) == INVALID                 # capacity % probes
     assert call(probes=0) == INVALID
     assert call(n=-1) == INVALID
@@ -186,6 +186,7 @@ def test_memory_layer_step_argument_errors(lib):
     assert call(values=P_ODD) == MISALIGNED
     assert call(mzb=mzb - 1) == WS_SMALL
     assert call(wbb=wbb - 1) == WS_SMALL
+    assert call(halves=0) == INVALID and call(halves=4) == INVALID
 
 
 def test_score_dedup_hashed_argument_errors(lib):

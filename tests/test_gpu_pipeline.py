@@ -113,9 +113,11 @@ def test_lookup_without_values_then_zero_inserted(dev):
         assert bits_equal(to_np(values), o.values), f"step {t}"
 
 
-@pytest.mark.parametrize("depth,native", [(2, True), (3, True), (2, False)])
-def test_memory_layer_pipeline(dev, depth, native):
-    """The batch as one library call (native) and as seven, both against the oracle."""
+@pytest.mark.parametrize("depth,native,lookahead", [(2, True, False), (3, True, False), (2, False, False),
+                                                    (2, True, True), (3, True, True)])
+def test_memory_layer_pipeline(dev, depth, native, lookahead):
+    """The batch as one library call (native) and as seven, and with the next batch looked up
+    before the current batch's row traffic (lookahead), all against the oracle."""
     cfg = synth.scaled_memory_layer(capacity=16_384, universe=120_000, batch=8_192, steps=8)
     C, P, D, n = cfg.capacity, cfg.probes, cfg.dim, cfg.batch
     identity, stamps, o, base = prefilled_pair(dev, cfg)
@@ -129,7 +131,11 @@ def test_memory_layer_pipeline(dev, depth, native):
     sts = [torch.zeros(6, dtype=torch.int64, device=dev) for _ in ids]
     torch.cuda.synchronize()
     pipe = pipeline.MemoryLayerPipeline(identity, stamps, values, P, n, depth=depth, native=native)
+    if lookahead:
+        pipe.prefetch(ids[0], base + 1, evicted=evs[0], stats=sts[0])
     for t in range(cfg.steps):  # no synchronisation between batches
+        if lookahead and t + 1 < cfg.steps:
+            pipe.prefetch(ids[t + 1], base + t + 2, evicted=evs[t + 1], stats=sts[t + 1])
         pipe.step(ids[t], base + t + 1, es[t], out=outs[t], evicted=evs[t], stats=sts[t])
     last_rows = [to_np(pipe.rows(k)).copy() for k in range(depth)]
     for t in range(cfg.steps):
@@ -143,6 +149,27 @@ def test_memory_layer_pipeline(dev, depth, native):
     assert np.array_equal(to_np(identity), o.identity)
     assert np.array_equal(to_np(stamps), o.stamps)
     assert bits_equal(to_np(values), o.values)
+
+
+def test_prefetch_limits(dev):
+    """Lookahead is bounded by the ring depth and must be consumed in order (host-side errors)."""
+    C, P, D, n = 1024, 8, 16, 64
+    identity = torch.full((C,), -1, dtype=torch.int64, device=dev)
+    stamps = torch.full((C,), -1, dtype=torch.int64, device=dev)
+    values = torch.zeros((C, D), dtype=torch.float32, device=dev)
+    pipe = pipeline.MemoryLayerPipeline(identity, stamps, values, P, n, depth=2)
+    ids = [torch.arange(i * n, (i + 1) * n, dtype=torch.int64, device=dev) for i in range(4)]
+    e = torch.zeros((n, D), dtype=torch.float32, device=dev)
+    pipe.prefetch(ids[0], 1)
+    pipe.prefetch(ids[1], 2)
+    with pytest.raises(hlr.HLRError):
+        pipe.prefetch(ids[2], 3)
+    with pytest.raises(hlr.HLRError):
+        pipe.step(ids[1], 2, e)
+    pipe.step(ids[0], 1, e)
+    pipe.step(ids[1], 2, e)
+    torch.cuda.synchronize()
+    assert int((identity >= 0).sum().item()) == 2 * n
 
 
 def test_hashed_tables_pipeline(dev):
