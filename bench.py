@@ -423,12 +423,25 @@ def run_serving(args):
            "score_valu_ops_per_s": float(3 * n * D / np.median(t_score))})
 
 
-def _marker(timer, cur, store):
-    """A pipeline mark hook recording HIP events on the compute stream into store[(op, i)]."""
+class _EventPool:
+    """Timing events created before the timed region: creating HIP events inside it has stalled the GPU
+    for tens of milliseconds now and then (the runtime growing its signal pool)."""
+
+    def __init__(self, timer, count):
+        self.free = [timer.event() for _ in range(count)]
+
+    def take(self):
+        if not self.free:
+            raise RuntimeError("event pool exhausted: size it for the timed steps")
+        return self.free.pop()
+
+
+def _marker(timer, cur, store, pool):
+    """A pipeline mark hook recording HIP events (from `pool`) on the compute stream into store[(op, i)]."""
     def mark(tag):
         op, i, edge = tag
         if edge == 0:
-            store.setdefault((op, i), []).append([timer.event(), timer.event()])
+            store.setdefault((op, i), []).append([pool.take(), pool.take()])
         timer.record(store[(op, i)][-1][edge], cur)
     return mark
 
@@ -473,9 +486,10 @@ def run_dlrm(args):
         pipe.step(keys[s % 2], grads[s % 2], cfg.lr, outs)
     torch.cuda.synchronize()
     a, b = timer.event(), timer.event()
+    pool = _EventPool(timer, K * 8 * 2 * 2)  # per step: 8 tables x (gather, apply) x 2 edges
     timer.record(a, cur)
     for s in range(K):
-        pipe.step(keys[s % 2], grads[s % 2], cfg.lr, outs, mark=_marker(timer, cur, ev))
+        pipe.step(keys[s % 2], grads[s % 2], cfg.lr, outs, mark=_marker(timer, cur, ev, pool))
     timer.record(b, cur)
     torch.cuda.synchronize()
     total = timer.elapsed_s(a, b)
@@ -548,12 +562,19 @@ def run_cs3(args):
     torch.cuda.synchronize()
     ev = {}
     a, b = timer.event(), timer.event()
+    pool = _EventPool(timer, K * 4 * 2)  # per step: 4 applies x 2 edges
+    # an event on the compute stream after every step: per-step times (median reported), and without them
+    # this schedule has stalled for about 40 ms at the start of the timed region on some runs (a runtime
+    # effect, seen as an idle GPU in kernel traces, never with these events)
+    sev = [timer.event() for _ in range(K)]
     timer.record(a, cur)
     for s in range(K):
-        piped_step(W + s, _marker(timer, cur, ev))
+        piped_step(W + s, _marker(timer, cur, ev, pool))
+        timer.record(sev[s], cur)
     timer.record(b, cur)
     torch.cuda.synchronize()
     total = timer.elapsed_s(a, b)
+    step_ms = [timer.elapsed_s(a if s == 0 else sev[s - 1], sev[s]) * 1e3 for s in range(K)]
     c, d = timer.event(), timer.event()
     timer.record(c, cur)
     for s in range(K):
@@ -577,6 +598,7 @@ def run_cs3(args):
           _roof(f"ema_update_apply ({worst}: ema_light + ema_heavy + ema_combine)", nb[worst], per[worst]),
           {"dtype": "fp32", "step_hbm_gbs": tot_bytes / step_s / 1e9,
            "apply_us": {k: v * 1e6 for k, v in per.items()},
+           "step_ms_median": float(np.median(step_ms)), "step_ms_max": float(np.max(step_ms)),
            "one_stream": {"ms_per_step": serial / K * 1e3, "pairs_per_s": n * K / serial},
            "top_user_occurrences": int(np.bincount(ur).max())})
 

@@ -24,7 +24,12 @@ class DynamicKeyStore:
         self.stamps = torch.full((self.max_rows,), -1, dtype=torch.int64, device=dev)
         self.next_row = torch.zeros(1, dtype=torch.int64, device=dev)
         self.stream = stream
-        self._pinned = deque(torch.zeros(1, dtype=torch.int64, pin_memory=True) for _ in range(8))
+        # pinned copies of next_row, each with its event (created here: creating events per batch can
+        # stall the GPU now and then while the runtime grows its signal pool)
+        self._pinned = deque((torch.zeros(1, dtype=torch.int64, pin_memory=True), torch.cuda.Event())
+                             for _ in range(8))
+        for _, ev in self._pinned:  # torch creates an event's HIP event at its first record
+            ev.record(torch.cuda.current_stream(dev))
         self._pending = deque()  # (event, pinned copy of next_row, keys offered up to that batch)
         self._offered = 0        # keys offered to the store so far (an upper bound for rows in use)
         self._known_used = 0
@@ -36,7 +41,7 @@ class DynamicKeyStore:
         while self._pending and self._pending[0][0].query():
             ev, pin, offered = self._pending.popleft()
             self._known_used, self._known_offered = int(pin[0]), offered
-            self._pinned.append(pin)
+            self._pinned.append((pin, ev))
 
     def bound(self, n):
         """Upper bound for the rows in use after a batch of n more keys."""
@@ -64,10 +69,9 @@ class DynamicKeyStore:
         self._offered += n
         if self._pinned:
             s = self.stream if self.stream is not None else torch.cuda.current_stream(ids.device)
-            pin = self._pinned.popleft()
+            pin, ev = self._pinned.popleft()
             with torch.cuda.stream(s):
                 pin.copy_(self.next_row, non_blocking=True)
-                ev = torch.cuda.Event()
                 ev.record(s)
             self._pending.append((ev, pin, self._offered))
         return rows, hit
