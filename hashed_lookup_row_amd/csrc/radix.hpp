@@ -69,6 +69,7 @@ struct SegWork {
   int32_t *seg_end;    // [n]
   K *seg_key;          // [n]   key of each segment (row grouping only)
   int64_t *nseg;       // [1]
+  uint32_t *nact;      // [1]   elements that take part (sorted first); the rest of the n slots are unused
   int2 *hlist;         // heavy work units (segment, run), built by the light kernel
   int32_t *clist;      // segments with more than one run (combined after the heavy kernel)
   int64_t n;
@@ -87,14 +88,17 @@ inline size_t segwork_layout(int64_t n, SegWork<K> *w, void *base) {
   w->k[1] = c.take<K>(nn);
   w->v[0] = c.take<uint32_t>(nn + kPosPad);
   w->v[1] = c.take<uint32_t>(nn + kPosPad);
-  w->counts = c.take<uint32_t>(static_cast<size_t>(kMaxBins) * (nb > 0 ? nb : 1));
+  // per-tile tables sized for the smallest tile (a masked grouping sorts with 4 items per thread)
+  const int64_t nb_max = (n + kSortThreads * 4 - 1) / (kSortThreads * 4);
+  w->counts = c.take<uint32_t>(static_cast<size_t>(kMaxBins) * (nb_max > 0 ? nb_max : 1));
   w->ticket = c.take<uint32_t>(4);
-  w->bcount = c.take<uint32_t>(2 * static_cast<size_t>(nb > 0 ? nb : 1));
+  w->bcount = c.take<uint32_t>(2 * static_cast<size_t>(nb_max > 0 ? nb_max : 1));
   w->segidx = c.take<int32_t>(nn);
   w->seg_start = c.take<int32_t>(nn);
   w->seg_end = c.take<int32_t>(nn);
   w->seg_key = c.take<K>(nn);
   w->nseg = c.take<int64_t>(1);
+  w->nact = c.take<uint32_t>(1);
   w->hlist = c.take<int2>(nn / 32 + 64);
   w->clist = c.take<int32_t>(nn / 256 + 64);
   w->n = n;
@@ -104,6 +108,20 @@ inline size_t segwork_layout(int64_t n, SegWork<K> *w, void *base) {
 }
 
 // ------------------------------------------------------------------ kernels
+// Elements in use: the first *nact of the n slots when a device count is
+// given (a compacted input), else all n.
+__device__ __forceinline__ int64_t active_count(int64_t n, const uint32_t *nact) {
+  if (!nact) return n;
+  const int64_t m = static_cast<int64_t>(*nact);
+  return m < n ? m : n;
+}
+
+// Tiles holding elements in use; per-tile tables are read only for these.
+__device__ __forceinline__ int used_tiles(int64_t m, int tile, int nblocks) {
+  const int64_t t = (m + tile - 1) / tile;
+  return static_cast<int>(t < nblocks ? t : nblocks);
+}
+
 // Block-wide exclusive scan of one uint32 per thread (256 threads); returns the
 // exclusive prefix and writes the block total to *total.
 __device__ __forceinline__ uint32_t block_exclusive_scan(uint32_t x, uint32_t *sh /*[256+]*/, uint32_t *total) {
@@ -124,8 +142,11 @@ __device__ __forceinline__ uint32_t block_exclusive_scan(uint32_t x, uint32_t *s
 
 template <typename K, int ITEMS>
 __global__ void __launch_bounds__(kSortThreads)
-    hist_kernel(const K *__restrict__ keys, int64_t n, int shift, int bits, uint32_t *counts) {
+    hist_kernel(const K *__restrict__ keys, int64_t n, const uint32_t *__restrict__ nact, int shift, int bits,
+                uint32_t *counts) {
   constexpr int TILE = kSortThreads * ITEMS;
+  n = active_count(n, nact);
+  if (static_cast<int64_t>(blockIdx.x) * TILE >= n) return;  // empty tiles are never read (see used_tiles)
   __shared__ uint32_t h[kMaxBins];
   const int bins = 1 << bits;
   const uint32_t mask = static_cast<uint32_t>(bins - 1);
@@ -144,9 +165,11 @@ __global__ void __launch_bounds__(kSortThreads)
 template <typename K, int ITEMS>
 __global__ void __launch_bounds__(kSortThreads)
     scatter_kernel(const K *__restrict__ kin, const uint32_t *__restrict__ vin, K *__restrict__ kout,
-                   uint32_t *__restrict__ vout, int64_t n, int shift, int bits, const uint32_t *__restrict__ counts,
-                   int nblocks) {
+                   uint32_t *__restrict__ vout, int64_t n, const uint32_t *__restrict__ nact, int shift, int bits,
+                   const uint32_t *__restrict__ counts, int nblocks) {
   constexpr int TILE = kSortThreads * ITEMS;
+  n = active_count(n, nact);
+  if (static_cast<int64_t>(blockIdx.x) * TILE >= n) return;  // an empty tile writes nothing
   __shared__ uint32_t cnt[4][kMaxBins];
   __shared__ uint32_t sh[kSortThreads];
   __shared__ uint32_t offs[kMaxBins];
@@ -155,6 +178,7 @@ __global__ void __launch_bounds__(kSortThreads)
   const int w = threadIdx.x >> 6;
   // This tile's output offset of every digit: (keys with smaller digits) + (same digit, earlier tiles).
   // Thread d reads digit d of every tile's histogram (rows of 256 counts, coalesced across the block).
+  nblocks = used_tiles(n, TILE, nblocks);
   {
     const int d = threadIdx.x;
     uint32_t before = 0, total = 0;
@@ -250,8 +274,11 @@ __device__ __forceinline__ void seg_heads(const K *__restrict__ keys, int64_t n,
 // Segment pass 1: number of segment heads per tile.
 template <typename K, int ITEMS>
 __global__ void __launch_bounds__(kSortThreads)
-    seg_count_kernel(const K *__restrict__ keys, int64_t n, K excluded, bool use_excluded, uint32_t *bcount) {
+    seg_count_kernel(const K *__restrict__ keys, int64_t n, const uint32_t *__restrict__ nact, K excluded,
+                     bool use_excluded, uint32_t *bcount) {
   __shared__ uint32_t wsum[kSortThreads / hlr::kWave];
+  n = active_count(n, nact);
+  if (static_cast<int64_t>(blockIdx.x) * kSortThreads * ITEMS >= n) return;  // never read (see used_tiles)
   K kk[ITEMS];
   bool head[ITEMS], tail[ITEMS], ok[ITEMS];
   seg_heads<K, ITEMS>(keys, n, excluded, use_excluded, kk, head, tail, ok);
@@ -276,10 +303,14 @@ __global__ void __launch_bounds__(kSortThreads)
 // and waves of this tile (per-wave ballot counts in LDS), earlier lanes.
 template <typename K, typename Emit, int ITEMS>
 __global__ void __launch_bounds__(kSortThreads)
-    seg_index_kernel(const K *__restrict__ keys, const uint32_t *__restrict__ vals, int64_t n, K excluded,
-                     bool use_excluded, const uint32_t *__restrict__ bcount, int nblocks, int32_t *segidx,
-                     int32_t *seg_start, int32_t *seg_end, K *seg_key, int64_t *nseg, Emit emit) {
+    seg_index_kernel(const K *__restrict__ keys, const uint32_t *__restrict__ vals, int64_t n,
+                     const uint32_t *__restrict__ nact, K excluded, bool use_excluded,
+                     const uint32_t *__restrict__ bcount, int nblocks, int32_t *segidx, int32_t *seg_start,
+                     int32_t *seg_end, K *seg_key, int64_t *nseg, Emit emit) {
   constexpr int NW = kSortThreads / hlr::kWave;
+  n = active_count(n, nact);
+  nblocks = used_tiles(n, kSortThreads * ITEMS, nblocks);
+  if (static_cast<int>(blockIdx.x) >= nblocks && blockIdx.x != 0) return;  // tile 0 publishes nseg even if m == 0
   __shared__ uint32_t sh[kSortThreads];
   __shared__ uint32_t wcnt[ITEMS][NW];
   __shared__ uint32_t blk_off;
@@ -349,42 +380,44 @@ struct NoEmit {
 
 // Runs every radix pass; returns the index (0/1) of the buffer holding the result.
 template <typename K, int ITEMS>
-inline int radix_sort_pairs_t(SegWork<K> &w, int total_bits, hipStream_t s) {
+inline int radix_sort_pairs_t(SegWork<K> &w, int total_bits, const uint32_t *nact, hipStream_t s) {
   const SortPlan plan = make_plan(total_bits);
   int cur = 0;
   for (int p = 0; p < plan.passes; ++p) {
-    hist_kernel<K, ITEMS><<<w.nblocks, kSortThreads, 0, s>>>(w.k[cur], w.n, plan.shift[p], plan.bits[p],
+    hist_kernel<K, ITEMS><<<w.nblocks, kSortThreads, 0, s>>>(w.k[cur], w.n, nact, plan.shift[p], plan.bits[p],
                                                               w.counts);
     scatter_kernel<K, ITEMS><<<w.nblocks, kSortThreads, 0, s>>>(w.k[cur], w.v[cur], w.k[cur ^ 1], w.v[cur ^ 1],
-                                                                 w.n, plan.shift[p], plan.bits[p], w.counts,
+                                                                 w.n, nact, plan.shift[p], plan.bits[p], w.counts,
                                                                  w.nblocks);
     cur ^= 1;
   }
   return cur;
 }
 
+// nact: device count of the elements in use (the first *nact slots), or NULL for all n.
 template <typename K>
-inline int radix_sort_pairs(SegWork<K> &w, int total_bits, hipStream_t s) {
-  if (w.items == 4) return radix_sort_pairs_t<K, 4>(w, total_bits, s);
-  if (w.items == 8) return radix_sort_pairs_t<K, 8>(w, total_bits, s);
-  return radix_sort_pairs_t<K, 16>(w, total_bits, s);
+inline int radix_sort_pairs(SegWork<K> &w, int total_bits, hipStream_t s, const uint32_t *nact = nullptr) {
+  if (w.items == 4) return radix_sort_pairs_t<K, 4>(w, total_bits, nact, s);
+  if (w.items == 8) return radix_sort_pairs_t<K, 8>(w, total_bits, nact, s);
+  return radix_sort_pairs_t<K, 16>(w, total_bits, nact, s);
 }
 
 template <typename K, typename Emit, int ITEMS>
 inline void segment_sorted_t(SegWork<K> &w, int cur, K excluded, bool use_excluded, K *seg_key, Emit emit,
-                             hipStream_t s) {
-  seg_count_kernel<K, ITEMS><<<w.nblocks, kSortThreads, 0, s>>>(w.k[cur], w.n, excluded, use_excluded, w.bcount);
+                             const uint32_t *nact, hipStream_t s) {
+  seg_count_kernel<K, ITEMS><<<w.nblocks, kSortThreads, 0, s>>>(w.k[cur], w.n, nact, excluded, use_excluded,
+                                                                 w.bcount);
   seg_index_kernel<K, Emit, ITEMS><<<w.nblocks, kSortThreads, 0, s>>>(
-      w.k[cur], w.v[cur], w.n, excluded, use_excluded, w.bcount, w.nblocks, w.segidx, w.seg_start, w.seg_end,
+      w.k[cur], w.v[cur], w.n, nact, excluded, use_excluded, w.bcount, w.nblocks, w.segidx, w.seg_start, w.seg_end,
       seg_key, w.nseg, emit);
 }
 
 template <typename K, typename Emit>
 inline void segment_sorted(SegWork<K> &w, int cur, K excluded, bool use_excluded, K *seg_key, Emit emit,
-                           hipStream_t s) {
-  if (w.items == 4) segment_sorted_t<K, Emit, 4>(w, cur, excluded, use_excluded, seg_key, emit, s);
-  else if (w.items == 8) segment_sorted_t<K, Emit, 8>(w, cur, excluded, use_excluded, seg_key, emit, s);
-  else segment_sorted_t<K, Emit, 16>(w, cur, excluded, use_excluded, seg_key, emit, s);
+                           hipStream_t s, const uint32_t *nact = nullptr) {
+  if (w.items == 4) segment_sorted_t<K, Emit, 4>(w, cur, excluded, use_excluded, seg_key, emit, nact, s);
+  else if (w.items == 8) segment_sorted_t<K, Emit, 8>(w, cur, excluded, use_excluded, seg_key, emit, nact, s);
+  else segment_sorted_t<K, Emit, 16>(w, cur, excluded, use_excluded, seg_key, emit, nact, s);
 }
 
 }  // namespace
@@ -393,10 +426,10 @@ namespace {
 
 // Sort keys for grouping a batch by row: row r for positions that take part
 // (row in range, mask set), the sentinel num_rows (sorted last, excluded from
-// every segment) for the others.
+// every segment) for the others.  All n positions are sorted (*nact = n).
 __global__ void __launch_bounds__(256)
     rowkey_init(const int64_t *__restrict__ rows, const uint8_t *__restrict__ mask, int64_t n, int64_t num_rows,
-                uint32_t *__restrict__ k, uint32_t *__restrict__ v, uint32_t *ticket) {
+                uint32_t *__restrict__ k, uint32_t *__restrict__ v, uint32_t *ticket, uint32_t *nact) {
   const int64_t i = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;
   if (i < n) {
     const int64_t r = rows[i];
@@ -405,6 +438,101 @@ __global__ void __launch_bounds__(256)
     v[i] = static_cast<uint32_t>(i);
   }
   if (i < 4) ticket[i] = 0u;
+  if (i == 0) *nact = static_cast<uint32_t>(n);
+}
+
+// With a mask, only the positions that take part are sorted: they are first
+// compacted, in position order, into the first *nact slots (a masked update
+// such as CTS's positives is a few percent of the batch, and the sort then
+// handles only those).  Tiles as in the sort (256 * ITEMS positions, chunks of
+// 256 consecutive positions); pass 1 counts each tile's positions that take
+// part, pass 2 places them: earlier tiles, then earlier chunks and waves of
+// this tile (ballot counts in LDS), then earlier lanes.
+template <int ITEMS>
+__device__ __forceinline__ bool row_takes_part(const int64_t *__restrict__ rows, const uint8_t *__restrict__ mask,
+                                               int64_t n, int64_t num_rows, int64_t i, int64_t *r) {
+  if (i >= n) return false;
+  *r = rows[i];
+  return *r >= 0 && *r < num_rows && mask[i] != 0;
+}
+
+template <int ITEMS>
+__global__ void __launch_bounds__(kSortThreads)
+    mask_count_kernel(const int64_t *__restrict__ rows, const uint8_t *__restrict__ mask, int64_t n,
+                      int64_t num_rows, uint32_t *bcount) {
+  __shared__ uint32_t wsum[kSortThreads / hlr::kWave];
+  const int64_t base = static_cast<int64_t>(blockIdx.x) * kSortThreads * ITEMS + threadIdx.x;
+  uint32_t c = 0;
+#pragma unroll
+  for (int i = 0; i < ITEMS; ++i) {
+    int64_t r;
+    c += static_cast<uint32_t>(__popcll(hlr::ballot(row_takes_part<ITEMS>(rows, mask, n, num_rows,
+                                                                           base + i * kSortThreads, &r))));
+  }
+  if (hlr::lane_id() == 0) wsum[threadIdx.x / hlr::kWave] = c;
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    uint32_t t = 0;
+    for (int q = 0; q < kSortThreads / hlr::kWave; ++q) t += wsum[q];
+    bcount[blockIdx.x] = t;
+  }
+}
+
+template <int ITEMS>
+__global__ void __launch_bounds__(kSortThreads)
+    mask_compact_kernel(const int64_t *__restrict__ rows, const uint8_t *__restrict__ mask, int64_t n,
+                        int64_t num_rows, const uint32_t *__restrict__ bcount, int nblocks, uint32_t *__restrict__ k,
+                        uint32_t *__restrict__ v, uint32_t *ticket, uint32_t *nact) {
+  constexpr int NW = kSortThreads / hlr::kWave;
+  __shared__ uint32_t sh[kSortThreads];
+  __shared__ uint32_t wcnt[ITEMS][NW];
+  __shared__ uint32_t blk_off;
+  {
+    uint32_t before = 0, total = 0;
+    for (int b = threadIdx.x; b < nblocks; b += kSortThreads) {
+      const uint32_t c = bcount[b];
+      if (b < static_cast<int>(blockIdx.x)) before += c;
+      total += c;
+    }
+    uint32_t all;
+    block_exclusive_scan(before, sh, &all);
+    if (threadIdx.x == 0) blk_off = all;
+    uint32_t tall;
+    block_exclusive_scan(total, sh, &tall);
+    if (blockIdx.x == 0 && threadIdx.x == 0) *nact = tall;
+    if (blockIdx.x == 0 && threadIdx.x < 4) ticket[threadIdx.x] = 0u;
+  }
+  const int w = threadIdx.x / hlr::kWave;
+  const uint64_t lt = hlr::lanemask_lt();
+  const int64_t base = static_cast<int64_t>(blockIdx.x) * kSortThreads * ITEMS + threadIdx.x;
+  bool ok[ITEMS];
+  int64_t r[ITEMS];
+  uint32_t rank[ITEMS];
+#pragma unroll
+  for (int i = 0; i < ITEMS; ++i) {
+    ok[i] = row_takes_part<ITEMS>(rows, mask, n, num_rows, base + i * kSortThreads, &r[i]);
+    const uint64_t m = hlr::ballot(ok[i]);
+    rank[i] = static_cast<uint32_t>(__popcll(m & lt));
+    if (hlr::lane_id() == 0) wcnt[i][w] = static_cast<uint32_t>(__popcll(m));
+  }
+  __syncthreads();
+  uint32_t run = blk_off;
+#pragma unroll
+  for (int i = 0; i < ITEMS; ++i) {
+    uint32_t before_w = 0, chunk = 0;
+#pragma unroll
+    for (int q = 0; q < NW; ++q) {
+      const uint32_t c = wcnt[i][q];
+      before_w += q < w ? c : 0u;
+      chunk += c;
+    }
+    if (ok[i]) {
+      const uint32_t dst = run + before_w + rank[i];
+      k[dst] = static_cast<uint32_t>(r[i]);
+      v[dst] = static_cast<uint32_t>(base + i * kSortThreads);
+    }
+    run += chunk;
+  }
 }
 
 // Groups positions by row: returns the buffer index holding (row, position)
@@ -415,12 +543,29 @@ inline int sorted_buffer(int64_t num_rows) {
   return make_plan(bit_width_u64(static_cast<uint64_t>(num_rows))).passes & 1;
 }
 
+template <int ITEMS>
+inline void compact_masked(SegWork<uint32_t> &w, const int64_t *rows, const uint8_t *mask, int64_t num_rows,
+                           hipStream_t s) {
+  mask_count_kernel<ITEMS><<<w.nblocks, kSortThreads, 0, s>>>(rows, mask, w.n, num_rows, w.bcount);
+  mask_compact_kernel<ITEMS><<<w.nblocks, kSortThreads, 0, s>>>(rows, mask, w.n, num_rows, w.bcount, w.nblocks,
+                                                                 w.k[0], w.v[0], w.ticket, w.nact);
+}
+
 inline int group_by_row(SegWork<uint32_t> &w, const int64_t *rows, const uint8_t *mask, int64_t num_rows,
                         hipStream_t s) {
-  rowkey_init<<<hlr::grid_for(w.n, 256), 256, 0, s>>>(rows, mask, w.n, num_rows, w.k[0], w.v[0], w.ticket);
+  if (mask) {
+    // small tiles: a masked grouping usually keeps a few percent of the batch, and tiles past
+    // the compacted count cost a launch slot only
+    w.items = 4;
+    w.nblocks = static_cast<int>((w.n + kSortThreads * 4 - 1) / (kSortThreads * 4));
+    compact_masked<4>(w, rows, mask, num_rows, s);
+  } else {
+    rowkey_init<<<hlr::grid_for(w.n, 256), 256, 0, s>>>(rows, mask, w.n, num_rows, w.k[0], w.v[0], w.ticket,
+                                                       w.nact);
+  }
   const int bits = bit_width_u64(static_cast<uint64_t>(num_rows));
-  const int cur = radix_sort_pairs<uint32_t>(w, bits, s);
-  segment_sorted<uint32_t>(w, cur, static_cast<uint32_t>(num_rows), true, w.seg_key, NoEmit{}, s);
+  const int cur = radix_sort_pairs<uint32_t>(w, bits, s, w.nact);
+  segment_sorted<uint32_t>(w, cur, static_cast<uint32_t>(num_rows), true, w.seg_key, NoEmit{}, s, w.nact);
   return cur;
 }
 
