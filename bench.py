@@ -513,7 +513,7 @@ def run_dlrm(args):
                          "keys_per_table": n, "zipf_s": cfg.zipf_s, "lr": cfg.lr,
                          "schedule": "two streams: hashed rows + SGD plan (sort) on a lookup stream beside gather + "
                                      "SGD apply on the compute stream"},
-          _roof("writeback_apply SGD_SUM (sgd_light + sgd_heavy + sgd_combine)", s_bytes / 8, s_time / 8),
+          _roof("writeback_apply SGD_SUM (sgd_apply_kernel + sgd_combine)", s_bytes / 8, s_time / 8),
           {"dtype": "fp32", "distinct_rows_per_table": us,
            "gather_roofline": _roof("gather_kernel<128>", g_bytes / 8, g_time / 8),
            "step_hbm_gbs": (g_bytes + s_bytes) / step_s / 1e9,
@@ -593,9 +593,9 @@ def run_cs3(args):
     worst = max(per, key=lambda k: per[k])
     _line("interaction pairs/s (CTS + CMS EMA row updates)", n / step_s, "pairs/s", K, W, step_s * 1e3,
           {"workload": cfg.name, "users": cfg.users, "items": cfg.items, "dim": D, "pairs": n,
-           "schedule": "two streams: the four EMA plans (sorts) on a lookup stream beside the four applies on the "
-                       "compute stream"},
-          _roof(f"ema_update_apply ({worst}: ema_light + ema_heavy + ema_combine)", nb[worst], per[worst]),
+           "schedule": "two streams: the EMA plans on a lookup stream (CMS plans sorted, CTS plans cut out of "
+                       "them by the label mask) beside the four applies on the compute stream"},
+          _roof(f"ema_update_apply ({worst}: ema_apply_kernel + ema_combine)", nb[worst], per[worst]),
           {"dtype": "fp32", "step_hbm_gbs": tot_bytes / step_s / 1e9,
            "apply_us": {k: v * 1e6 for k, v in per.items()},
            "step_ms_median": float(np.median(step_ms)), "step_ms_max": float(np.max(step_ms)),

@@ -65,6 +65,7 @@ def load_library():
             "writeback_apply": (i32, [p, i64, i64, p, i64, i32, f32, p, sz, p]),
             "ema_update_plan": (i32, [i64, p, p, i64, p, sz, p]),
             "ema_update_apply": (i32, [p, i64, i64, p, i64, f32, f32, p, sz, p]),
+            "ema_update_plan_subset": (i32, [i64, p, i64, p, sz, p, sz, p]),
             "writeback_plan_rows": (i32, [i64, i64, p, sz, p, p, p]),
             "quantize_rows_int8": (i32, [p, i64, i64, p, i64, p, i32, p, p, p, p]),
             "mark_rows": (i32, [p, i64, p, i64, p, p, p, p]),
@@ -89,7 +90,7 @@ def exported_symbols():
             "writeback_rows", "ema_update_rows_workspace_size", "ema_update_rows", "gather_dequant_score",
             "hashed_rows", "mpzch_zero_inserted", "writeback_plan", "writeback_apply", "ema_update_plan",
             "ema_update_apply", "writeback_plan_rows", "quantize_rows_int8", "mark_rows", "clear_marks",
-            "dks_workspace_size", "dks_lookup_or_insert", "dks_rehash", "memory_layer_step"]
+            "dks_workspace_size", "dks_lookup_or_insert", "dks_rehash", "memory_layer_step", "ema_update_plan_subset"]
 
 
 def _check(rc: int, what: str):
@@ -326,6 +327,18 @@ def ema_update_plan(num_rows, rows, mask, ws, stream=None):
     w, wb = _own_ws(ws, lib.ema_update_rows_workspace_size(int(num_rows), 4, n))
     _check(lib.ema_update_plan(int(num_rows), _ptr(rows), _ptr(mask), n, w, wb, _stream(rows.device, stream)),
            "ema_update_plan")
+
+
+def ema_update_plan_subset(num_rows, mask, src_ws, ws, stream=None):
+    """The plan of the positions of the plan in src_ws whose mask is set (no sort)."""
+    lib = load_library()
+    _dev(mask, "mask", torch.uint8)
+    n = mask.numel()
+    need = lib.ema_update_rows_workspace_size(int(num_rows), 4, n)
+    sw, swb = _own_ws(src_ws, need)
+    w, wb = _own_ws(ws, need)
+    _check(lib.ema_update_plan_subset(int(num_rows), _ptr(mask), n, sw, swb, w, wb, _stream(mask.device, stream)),
+           "ema_update_plan_subset")
 
 
 def ema_update_apply(table, vals, a, b, ws, stream=None):

@@ -13,4 +13,4 @@ extern "C" const char *hlr_status_string(hlr_status status) {
   }
 }
 
-extern "C" int32_t hlr_version(void) { return 102; }
+extern "C" int32_t hlr_version(void) { return 103; }

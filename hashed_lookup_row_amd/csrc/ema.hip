@@ -6,10 +6,12 @@
 // Plan: positions that take part are grouped by row with a stable radix sort
 // (radix.hpp), so each row's positions come out in batch order.  A row's
 // positions are applied in order (T = fl(fl(a*T) + fl(b*v))): short rows by
-// one wave each (ema_light), long rows by one wave per (chunk, 128-element
+// one wave each (light part), long rows by one wave per (chunk, 16-element
 // slice), the chunks of a row running in parallel from speculative warmed-up
-// states (ema_heavy) that ema_combine verifies bit for bit.  The result equals
-// the sequential loop bit for bit.
+// states (heavy part) that ema_combine verifies bit for bit.  The result equals
+// the sequential loop bit for bit.  The plan lists the long rows' runs, so one
+// launch (ema_apply_kernel) holds both parts: its first blocks start the long
+// dependent chains and the rest stream the short rows beside them.
 #include <cmath>
 
 #include "radix.hpp"
@@ -23,24 +25,27 @@ __device__ __forceinline__ float4 ema_step(float4 t, float4 v, float a, float b)
   return make_float4(a * t.x + b * v.x, a * t.y + b * v.y, a * t.z + b * v.z, a * t.w + b * v.w);
 }
 
-// Row loads in flight per wave in the light kernel.
+// Row loads in flight per wave in the light part.  The launch's register
+// budget is set by the heavy part's narrow walk (about 136 registers, three
+// waves per SIMD), so the light rows at dim <= 256 keep 16 rows in flight per
+// wave to make up for the lower occupancy.
 template <int NC>
-constexpr int light_batch() { return NC == 4 ? 4 : 8; }
+constexpr int light_batch() { return NC == 4 ? 4 : (NC == 2 ? 8 : 16); }
 
-// Light rows (fewer than kHeavyMin occurrences): one wave per row, exact.
-// Longer rows are registered (in chunks of L) for the slice kernels.  A wave
-// walks rows k, k + waves, ...; the next row's (start, end, row) is loaded
-// while the current row is processed (wave-uniform, so scalar loads).
+// Light rows (fewer than kHeavyMin occurrences): one wave per row, exact.  A
+// wave walks rows k, k + waves, ...; the next row's (start, end, row) is loaded
+// while the current row is processed (wave-uniform, so scalar loads).  Longer
+// rows belong to the heavy part.
 template <int NC>
-__global__ void __launch_bounds__(kThreads)
-    ema_light(float4 *table, const float4 *__restrict__ vals, const uint32_t *__restrict__ seg_key,
-              const uint32_t *__restrict__ spos, const int32_t *__restrict__ seg_start,
-              const int32_t *__restrict__ seg_end, const int64_t *__restrict__ nseg_p, float a, float b, int64_t v4,
-              int L, uint32_t *counters, int2 *hlist, int32_t *clist) {
+__device__ __forceinline__ void ema_light(float4 *table, const float4 *__restrict__ vals,
+                                          const uint32_t *__restrict__ seg_key, const uint32_t *__restrict__ spos,
+                                          const int32_t *__restrict__ seg_start, const int32_t *__restrict__ seg_end,
+                                          const int64_t *__restrict__ nseg_p, float a, float b, int64_t v4,
+                                          int block, int nblocks) {
   const int64_t nseg = *nseg_p;
-  const int64_t waves = static_cast<int64_t>(gridDim.x) * (kThreads / kWave);
+  const int64_t waves = static_cast<int64_t>(nblocks) * (kThreads / kWave);
   const int lane = lane_id();
-  int64_t k = __builtin_amdgcn_readfirstlane(static_cast<int>((blockIdx.x * kThreads + threadIdx.x) / kWave));
+  int64_t k = __builtin_amdgcn_readfirstlane(static_cast<int>((block * kThreads + threadIdx.x) / kWave));
   if (k >= nseg) return;
   int32_t s = seg_start[k], e = seg_end[k];
   int64_t r = seg_key[k];
@@ -49,9 +54,7 @@ __global__ void __launch_bounds__(kThreads)
     const int64_t kc = kn < nseg ? kn : nseg - 1;
     const int32_t sn = seg_start[kc], en = seg_end[kc];
     const int64_t rn = seg_key[kc];
-    if (e - s >= kHeavyMin) {
-      if (lane == 0) push_heavy(static_cast<int32_t>(k), e - s, L, counters, hlist, clist);
-    } else {
+    if (e - s < kHeavyMin) {
       float4 st[NC];
 #pragma unroll
       for (int q = 0; q < NC; ++q) {
@@ -85,30 +88,36 @@ constexpr int kHeavyG = 4;
 constexpr int kHeavyP = 56;
 using HeavySlices = Narrow<kHeavyG>;
 
-// Heavy rows: one wave per (chunk of <= L occurrences, 64-element slice).  A
+// Heavy rows: one wave per (chunk of <= L occurrences, 16-element slice).  A
 // row with one chunk is applied exactly from its stored value.  For a longer
 // row, chunk 0 runs exactly; chunk m > 0 starts W occurrences early from a zero
 // state (the recurrence contracts by a per step, so after W steps the state no
 // longer depends on where it started) and records sigma (the state entering
 // its first occurrence) and tau (the state after its last) for ema_combine.
-__global__ void __launch_bounds__(kThreads)
-    ema_heavy(float *table, const float *__restrict__ vals, const uint32_t *__restrict__ skey,
-              const uint32_t *__restrict__ spos, const int32_t *__restrict__ seg_start,
-              const int32_t *__restrict__ seg_end, const uint32_t *__restrict__ counters,
-              const int2 *__restrict__ hlist, float a, float b, int64_t D, int L, int W, float *partial) {
+// The plan lists runs of kBaseRun; a chunk is L / kBaseRun of them, and the
+// wave of a run that does not start a chunk has nothing to do.
+__device__ __forceinline__ void ema_heavy(float *table, const float *__restrict__ vals,
+                                          const uint32_t *__restrict__ skey, const uint32_t *__restrict__ spos,
+                                          const int32_t *__restrict__ seg_start, const int32_t *__restrict__ seg_end,
+                                          const uint32_t *__restrict__ counters, const int2 *__restrict__ hlist,
+                                          float a, float b, int64_t D, int L, int W, float *partial, int block,
+                                          int nblocks) {
   const int64_t S = HeavySlices::slices(D);
   const int64_t items = static_cast<int64_t>(counters[0]) * S;
-  const int64_t waves = static_cast<int64_t>(gridDim.x) * (kThreads / kWave);
-  for (int64_t it = (static_cast<int64_t>(blockIdx.x) * kThreads + threadIdx.x) / kWave; it < items; it += waves) {
+  const int64_t waves = static_cast<int64_t>(nblocks) * (kThreads / kWave);
+  const int32_t per_chunk = L / kBaseRun;
+  for (int64_t it = (static_cast<int64_t>(block) * kThreads + threadIdx.x) / kWave; it < items; it += waves) {
     const int2 km = hlist[it / S];
+    if (km.y % per_chunk != 0) continue;
+    const int32_t m = km.y / per_chunk;
     const int lane = lane_id();
     const int64_t e = (it % S) * HeavySlices::kWidth + (lane % HeavySlices::kWidth);
     const bool act = lane < HeavySlices::kWidth && e < D;  // lane group 0 holds the chain
     const int32_t s = seg_start[km.x], end = seg_end[km.x];
     const int64_t r = skey[s];
-    const int32_t j0 = s + km.y * L;
-    const int32_t j1 = j0 + L < end ? j0 + L : end;
-    const bool exact_start = km.y == 0 || j0 - W <= s;
+    const int32_t j0 = s + m * L;
+    const int32_t j1 = static_cast<int64_t>(j0) + L < end ? j0 + L : end;
+    const bool exact_start = m == 0 || j0 - W <= s;
     const int32_t from = exact_start ? s : j0 - W;
     float st = (exact_start && act) ? table[r * D + e] : 0.f;
     // A row in one chunk is walked whole.  Otherwise the warm-up (or the exact
@@ -130,11 +139,32 @@ __global__ void __launch_bounds__(kThreads)
       continue;
     }
     if (act) {
-      const int64_t slot = run_slot(j0, km.y, L);
+      const int64_t slot = run_slot(j0, m, L);
       partial[(2 * slot) * D + e] = sig;
       partial[(2 * slot + 1) * D + e] = st;
     }
   }
+}
+
+// Both parts in one launch: blocks [0, heavy_blocks) take the heavy runs (so
+// their chains start first), the others the light rows.  The parts touch
+// disjoint rows.
+template <int NC>
+__global__ void __launch_bounds__(kThreads)
+    ema_apply_kernel(float *table, const float *__restrict__ vals, const uint32_t *__restrict__ seg_key,
+                     const uint32_t *__restrict__ skey, const uint32_t *__restrict__ spos,
+                     const int32_t *__restrict__ seg_start, const int32_t *__restrict__ seg_end,
+                     const int64_t *__restrict__ nseg_p, const uint32_t *__restrict__ counters,
+                     const int2 *__restrict__ hlist, float a, float b, int64_t D, int L, int W, int heavy_blocks,
+                     float *partial) {
+  const int blk = static_cast<int>(blockIdx.x);
+  if (blk < heavy_blocks)
+    ema_heavy(table, vals, skey, spos, seg_start, seg_end, counters, hlist, a, b, D, L, W, partial, blk,
+              heavy_blocks);
+  else
+    ema_light<NC>(reinterpret_cast<float4 *>(table), reinterpret_cast<const float4 *>(vals), seg_key, spos,
+                  seg_start, seg_end, nseg_p, a, b, D / 4, blk - heavy_blocks,
+                  static_cast<int>(gridDim.x) - heavy_blocks);
 }
 
 // Rows with several chunks: one wave per (row, slice) walks the chunks in
@@ -156,11 +186,12 @@ __global__ void __launch_bounds__(kThreads)
   const int64_t waves = static_cast<int64_t>(gridDim.x) * (kThreads / kWave);
   for (int64_t it = (static_cast<int64_t>(blockIdx.x) * kThreads + threadIdx.x) / kWave; it < items; it += waves) {
     const int32_t k = clist[it / S];
+    const int32_t s = seg_start[k], end = seg_end[k];
+    if (end - s <= L) continue;  // one chunk: walked whole by the heavy part
     const int64_t e = (it % S) * kSliceElems + lane_id();
     const bool act = e < D;
     const int64_t ec = act ? e : 0;
-    const int32_t s = seg_start[k], end = seg_end[k];
-    const int32_t nch = (end - s + L - 1) / L;
+    const int32_t nch = static_cast<int32_t>((static_cast<int64_t>(end - s) + L - 1) / L);
     auto slot2 = [&](int32_t m) { return partial + 2 * run_slot(s + m * L, m, L) * D; };
     float cur = slot2(0)[D + ec];
     int32_t m = 1;
@@ -189,7 +220,7 @@ __global__ void __launch_bounds__(kThreads)
       }
       // chunk m + bad started from a wrong state in this slice: recompute it from the exact state
       const int32_t c0 = s + (m + bad) * L;
-      const int32_t c1 = c0 + L < end ? c0 + L : end;
+      const int32_t c1 = static_cast<int64_t>(c0) + L < end ? c0 + L : end;
       slice_run(vals, spos, c0, c1, D, e, [&](int32_t, float x) { cur = ema1(cur, x, a, b); });
       m += bad + 1;
     }
@@ -202,20 +233,25 @@ __global__ void __launch_bounds__(kThreads)
 // spent while the two trajectories' roundings fall onto the same value (for
 // a = 0.95 and 0.99 about one 128-element slice in a thousand still differs
 // after W steps; a slice that differs is recomputed by ema_combine).  A chunk's
-// wave walks W + L positions and reads a value row for each, so L = max(256,
-// 2W) keeps the redundant warm-up reads at most half of a chunk's; a row of at
-// most L occurrences runs whole, as one exact chain.  Without contraction (a
-// outside (0, 1)) rows run whole.
+// wave walks W + L positions and reads a value row for each, so L >= max(256,
+// 2W) keeps the redundant warm-up reads at most half of a chunk's; L is a
+// whole number of the plan's runs (kBaseRun), and a row of at most L
+// occurrences runs whole, as one exact chain.  Without contraction (a outside
+// (0, 1)) rows run whole.
 inline void ema_plan(float a, int64_t n, int *L, int *W) {
-  constexpr int kChunk = 256;
+  int64_t len;
   if (a > 0.f && a < 1.f) {
     const double w = std::ceil(28.0 / -std::log(static_cast<double>(a)));
     *W = static_cast<int>(w < 1048576.0 ? w : 1048576.0);
-    *L = 2 * *W > kChunk ? 2 * *W : kChunk;
+    len = 2 * static_cast<int64_t>(*W);
   } else {
     *W = 0;
-    *L = static_cast<int>(n > kChunk ? (n < 0x7fffffff ? n : 0x7fffffff) : kChunk);
+    len = n;
   }
+  constexpr int64_t kMaxL = 0x7fffffff / kBaseRun * kBaseRun;
+  len = len > kBaseRun ? len : kBaseRun;
+  len = (len + kBaseRun - 1) / kBaseRun * kBaseRun;
+  *L = static_cast<int>(len < kMaxL ? len : kMaxL);
 }
 
 inline size_t ema_partial_elems(int64_t n, int64_t dim) {
@@ -228,16 +264,13 @@ void ema_launch(float *table, const float *vals, SegWork<uint32_t> &w, int cur, 
                 float *partial, hipStream_t s) {
   int L, W;
   ema_plan(a, w.n, &L, &W);
-  const int64_t v4 = dim / 4;
-  int grid = grid_for(w.n, 4 * 4);
-  if (grid > 4096) grid = 4096;
-  ema_light<NC><<<grid, kThreads, 0, s>>>(reinterpret_cast<float4 *>(table), reinterpret_cast<const float4 *>(vals),
-                                          w.seg_key, w.v[cur], w.seg_start, w.seg_end, w.nseg, a, b, v4, L, w.ticket,
-                                          w.hlist, w.clist);
+  int gl = grid_for(w.n, 4 * 4);
+  if (gl > 4096) gl = 4096;
   int gh = grid_for(w.n / 32 * HeavySlices::slices(dim), 4);
   if (gh > 2048) gh = 2048;
-  ema_heavy<<<gh, kThreads, 0, s>>>(table, vals, w.k[cur], w.v[cur], w.seg_start, w.seg_end, w.ticket, w.hlist, a,
-                                    b, dim, L, W, partial);
+  ema_apply_kernel<NC><<<gh + gl, kThreads, 0, s>>>(table, vals, w.seg_key, w.k[cur], w.v[cur], w.seg_start,
+                                                    w.seg_end, w.nseg, w.ticket, w.hlist, a, b, dim, L, W, gh,
+                                                    partial);
   int gc = grid_for(w.n / 256 * num_slices(dim), 4);
   if (gc > 1024) gc = 1024;
   ema_combine<<<gc, kThreads, 0, s>>>(table, vals, w.k[cur], w.v[cur], w.seg_start, w.seg_end, w.ticket, w.clist, a,
@@ -298,6 +331,7 @@ extern "C" hlr_status ema_update_rows(float *table, int64_t num_rows, int64_t di
   SegWork<uint32_t> w;
   segwork_layout<uint32_t>(n, &w, ws);
   group_by_row(w, rows, mask, num_rows, stream);
+  list_heavy_units(w, stream);
   ema_apply(table, num_rows, dim, vals, n, a, b, ws, stream);
   return launch_status();
 }
@@ -313,6 +347,26 @@ extern "C" hlr_status ema_update_plan(int64_t num_rows, const int64_t *rows, con
   SegWork<uint32_t> w;
   segwork_layout<uint32_t>(n, &w, ws);
   group_by_row(w, rows, mask, num_rows, stream);
+  list_heavy_units(w, stream);
+  return launch_status();
+}
+
+extern "C" hlr_status ema_update_plan_subset(int64_t num_rows, const uint8_t *mask, int64_t n, const void *src_ws,
+                                             size_t src_ws_bytes, void *ws, size_t ws_bytes, hipStream_t stream) {
+  hlr_status st = ema_args(num_rows, n);
+  if (st != HLR_OK) return st;
+  if (n == 0 || num_rows == 0) return HLR_OK;
+  if (!mask) return HLR_INVALID_ARG;
+  const size_t need = ema_update_rows_workspace_size(num_rows, 4, n);
+  if ((st = ema_ws(const_cast<void *>(src_ws), src_ws_bytes, need)) != HLR_OK) return st;
+  if ((st = ema_ws(ws, ws_bytes, need)) != HLR_OK) return st;
+  const char *a0 = static_cast<const char *>(src_ws), *b0 = static_cast<const char *>(ws);
+  if (a0 < b0 + need && b0 < a0 + need) return HLR_INVALID_ARG;  // the two plans must not overlap
+  SegWork<uint32_t> src, w;
+  segwork_layout<uint32_t>(n, &src, const_cast<void *>(src_ws));
+  segwork_layout<uint32_t>(n, &w, ws);
+  subset_of_group(w, src, mask, num_rows, stream);
+  list_heavy_units(w, stream);
   return launch_status();
 }
 

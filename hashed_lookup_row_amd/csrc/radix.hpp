@@ -70,7 +70,7 @@ struct SegWork {
   K *seg_key;          // [n]   key of each segment (row grouping only)
   int64_t *nseg;       // [1]
   uint32_t *nact;      // [1]   elements that take part (sorted first); the rest of the n slots are unused
-  int2 *hlist;         // heavy work units (segment, run), built by the light kernel
+  int2 *hlist;         // heavy work units (segment, run), listed by the plan (list_heavy_units)
   int32_t *clist;      // segments with more than one run (combined after the heavy kernel)
   int64_t n;
   int nblocks;
@@ -444,45 +444,70 @@ __global__ void __launch_bounds__(256)
 // With a mask, only the positions that take part are sorted: they are first
 // compacted, in position order, into the first *nact slots (a masked update
 // such as CTS's positives is a few percent of the batch, and the sort then
-// handles only those).  Tiles as in the sort (256 * ITEMS positions, chunks of
-// 256 consecutive positions); pass 1 counts each tile's positions that take
+// handles only those).  Tiles as in the sort (256 * ITEMS elements, chunks of
+// 256 consecutive elements); pass 1 counts each tile's elements that take
 // part, pass 2 places them: earlier tiles, then earlier chunks and waves of
-// this tile (ballot counts in LDS), then earlier lanes.
-template <int ITEMS>
-__device__ __forceinline__ bool row_takes_part(const int64_t *__restrict__ rows, const uint8_t *__restrict__ mask,
-                                               int64_t n, int64_t num_rows, int64_t i, int64_t *r) {
-  if (i >= n) return false;
-  *r = rows[i];
-  return *r >= 0 && *r < num_rows && mask[i] != 0;
-}
+// this tile (ballot counts in LDS), then earlier lanes.  The compaction is
+// stable, so it also cuts a subset out of an existing plan's sorted pairs
+// without sorting again (FromPlan).
+//
+// Element i of a batch: position i, if its row is in range and its mask set.
+struct FromPositions {
+  const int64_t *rows;
+  const uint8_t *mask;
+  int64_t num_rows;
+  __device__ __forceinline__ int64_t count(int64_t n) const { return n; }
+  __device__ __forceinline__ bool get(int64_t i, int64_t m, uint32_t *key, uint32_t *pos) const {
+    if (i >= m) return false;
+    const int64_t r = rows[i];
+    *key = static_cast<uint32_t>(r);
+    *pos = static_cast<uint32_t>(i);
+    return r >= 0 && r < num_rows && mask[i] != 0;
+  }
+};
 
-template <int ITEMS>
+// Element i of a plan's sorted (row, position) pairs: kept if it belongs to a
+// row (not the sentinel) and the mask is set at its position.
+struct FromPlan {
+  const uint32_t *keys;
+  const uint32_t *spos;
+  const uint32_t *nact;
+  uint32_t sentinel;
+  const uint8_t *mask;
+  __device__ __forceinline__ int64_t count(int64_t n) const { return active_count(n, nact); }
+  __device__ __forceinline__ bool get(int64_t i, int64_t m, uint32_t *key, uint32_t *pos) const {
+    if (i >= m) return false;
+    *key = keys[i];
+    *pos = spos[i];
+    return *key != sentinel && mask[*pos] != 0;
+  }
+};
+
+template <int ITEMS, typename Src>
 __global__ void __launch_bounds__(kSortThreads)
-    mask_count_kernel(const int64_t *__restrict__ rows, const uint8_t *__restrict__ mask, int64_t n,
-                      int64_t num_rows, uint32_t *bcount) {
+    mask_count_kernel(Src src, int64_t n, uint32_t *bcount) {
   __shared__ uint32_t wsum[kSortThreads / hlr::kWave];
+  const int64_t m = src.count(n);
   const int64_t base = static_cast<int64_t>(blockIdx.x) * kSortThreads * ITEMS + threadIdx.x;
   uint32_t c = 0;
 #pragma unroll
   for (int i = 0; i < ITEMS; ++i) {
-    int64_t r;
-    c += static_cast<uint32_t>(__popcll(hlr::ballot(row_takes_part<ITEMS>(rows, mask, n, num_rows,
-                                                                           base + i * kSortThreads, &r))));
+    uint32_t key, pos;
+    c += static_cast<uint32_t>(__popcll(hlr::ballot(src.get(base + i * kSortThreads, m, &key, &pos))));
   }
   if (hlr::lane_id() == 0) wsum[threadIdx.x / hlr::kWave] = c;
   __syncthreads();
-  if (threadIdx.x == 0) {
+  if (threadIdx.x == 0) {  // every tile writes its count, empty or not
     uint32_t t = 0;
     for (int q = 0; q < kSortThreads / hlr::kWave; ++q) t += wsum[q];
     bcount[blockIdx.x] = t;
   }
 }
 
-template <int ITEMS>
+template <int ITEMS, typename Src>
 __global__ void __launch_bounds__(kSortThreads)
-    mask_compact_kernel(const int64_t *__restrict__ rows, const uint8_t *__restrict__ mask, int64_t n,
-                        int64_t num_rows, const uint32_t *__restrict__ bcount, int nblocks, uint32_t *__restrict__ k,
-                        uint32_t *__restrict__ v, uint32_t *ticket, uint32_t *nact) {
+    mask_compact_kernel(Src src, int64_t n, const uint32_t *__restrict__ bcount, int nblocks,
+                        uint32_t *__restrict__ k, uint32_t *__restrict__ v, uint32_t *ticket, uint32_t *nact) {
   constexpr int NW = kSortThreads / hlr::kWave;
   __shared__ uint32_t sh[kSortThreads];
   __shared__ uint32_t wcnt[ITEMS][NW];
@@ -502,18 +527,18 @@ __global__ void __launch_bounds__(kSortThreads)
     if (blockIdx.x == 0 && threadIdx.x == 0) *nact = tall;
     if (blockIdx.x == 0 && threadIdx.x < 4) ticket[threadIdx.x] = 0u;
   }
+  const int64_t m = src.count(n);
   const int w = threadIdx.x / hlr::kWave;
   const uint64_t lt = hlr::lanemask_lt();
   const int64_t base = static_cast<int64_t>(blockIdx.x) * kSortThreads * ITEMS + threadIdx.x;
   bool ok[ITEMS];
-  int64_t r[ITEMS];
-  uint32_t rank[ITEMS];
+  uint32_t key[ITEMS], pos[ITEMS], rank[ITEMS];
 #pragma unroll
   for (int i = 0; i < ITEMS; ++i) {
-    ok[i] = row_takes_part<ITEMS>(rows, mask, n, num_rows, base + i * kSortThreads, &r[i]);
-    const uint64_t m = hlr::ballot(ok[i]);
-    rank[i] = static_cast<uint32_t>(__popcll(m & lt));
-    if (hlr::lane_id() == 0) wcnt[i][w] = static_cast<uint32_t>(__popcll(m));
+    ok[i] = src.get(base + i * kSortThreads, m, &key[i], &pos[i]);
+    const uint64_t bm = hlr::ballot(ok[i]);
+    rank[i] = static_cast<uint32_t>(__popcll(bm & lt));
+    if (hlr::lane_id() == 0) wcnt[i][w] = static_cast<uint32_t>(__popcll(bm));
   }
   __syncthreads();
   uint32_t run = blk_off;
@@ -528,43 +553,61 @@ __global__ void __launch_bounds__(kSortThreads)
     }
     if (ok[i]) {
       const uint32_t dst = run + before_w + rank[i];
-      k[dst] = static_cast<uint32_t>(r[i]);
-      v[dst] = static_cast<uint32_t>(base + i * kSortThreads);
+      k[dst] = key[i];
+      v[dst] = pos[i];
     }
     run += chunk;
   }
 }
 
-// Groups positions by row: returns the buffer index holding (row, position)
-// sorted by row, positions ascending within a row, with the segment table
-// (seg_start, seg_end, nseg) built.
 // Index (0/1) of the buffer that holds the sorted result for a table of num_rows rows.
 inline int sorted_buffer(int64_t num_rows) {
   return make_plan(bit_width_u64(static_cast<uint64_t>(num_rows))).passes & 1;
 }
 
-template <int ITEMS>
-inline void compact_masked(SegWork<uint32_t> &w, const int64_t *rows, const uint8_t *mask, int64_t num_rows,
-                           hipStream_t s) {
-  mask_count_kernel<ITEMS><<<w.nblocks, kSortThreads, 0, s>>>(rows, mask, w.n, num_rows, w.bcount);
-  mask_compact_kernel<ITEMS><<<w.nblocks, kSortThreads, 0, s>>>(rows, mask, w.n, num_rows, w.bcount, w.nblocks,
-                                                                 w.k[0], w.v[0], w.ticket, w.nact);
+// Compacts the elements of src that take part into (k[buf], v[buf]), in order;
+// count in *nact.
+template <int ITEMS, typename Src>
+inline void compact_into(SegWork<uint32_t> &w, const Src &src, int buf, hipStream_t s) {
+  mask_count_kernel<ITEMS, Src><<<w.nblocks, kSortThreads, 0, s>>>(src, w.n, w.bcount);
+  mask_compact_kernel<ITEMS, Src><<<w.nblocks, kSortThreads, 0, s>>>(src, w.n, w.bcount, w.nblocks, w.k[buf],
+                                                                      w.v[buf], w.ticket, w.nact);
 }
 
+inline void small_tiles(SegWork<uint32_t> &w) {
+  // a masked grouping usually keeps a few percent of the batch, and tiles past the
+  // compacted count cost a launch slot only
+  w.items = 4;
+  w.nblocks = static_cast<int>((w.n + kSortThreads * 4 - 1) / (kSortThreads * 4));
+}
+
+// Groups positions by row: returns the buffer index holding (row, position)
+// sorted by row, positions ascending within a row, with the segment table
+// (seg_start, seg_end, nseg) built.
 inline int group_by_row(SegWork<uint32_t> &w, const int64_t *rows, const uint8_t *mask, int64_t num_rows,
                         hipStream_t s) {
   if (mask) {
-    // small tiles: a masked grouping usually keeps a few percent of the batch, and tiles past
-    // the compacted count cost a launch slot only
-    w.items = 4;
-    w.nblocks = static_cast<int>((w.n + kSortThreads * 4 - 1) / (kSortThreads * 4));
-    compact_masked<4>(w, rows, mask, num_rows, s);
+    small_tiles(w);
+    compact_into<4>(w, FromPositions{rows, mask, num_rows}, 0, s);
   } else {
     rowkey_init<<<hlr::grid_for(w.n, 256), 256, 0, s>>>(rows, mask, w.n, num_rows, w.k[0], w.v[0], w.ticket,
                                                        w.nact);
   }
   const int bits = bit_width_u64(static_cast<uint64_t>(num_rows));
   const int cur = radix_sort_pairs<uint32_t>(w, bits, s, w.nact);
+  segment_sorted<uint32_t>(w, cur, static_cast<uint32_t>(num_rows), true, w.seg_key, NoEmit{}, s, w.nact);
+  return cur;
+}
+
+// The grouping of a subset: the pairs of an existing grouping `src` (same n and
+// num_rows) whose position has mask set, cut out in order (stable, so positions
+// stay ascending within each row) and segmented.  Equals group_by_row over the
+// same rows with the two masks combined, without sorting.
+inline int subset_of_group(SegWork<uint32_t> &w, const SegWork<uint32_t> &src, const uint8_t *mask, int64_t num_rows,
+                           hipStream_t s) {
+  const int cur = sorted_buffer(num_rows);
+  small_tiles(w);
+  compact_into<4>(w, FromPlan{src.k[cur], src.v[cur], src.nact, static_cast<uint32_t>(num_rows), mask}, cur, s);
   segment_sorted<uint32_t>(w, cur, static_cast<uint32_t>(num_rows), true, w.seg_key, NoEmit{}, s, w.nact);
   return cur;
 }
@@ -779,7 +822,7 @@ __device__ __forceinline__ void rows_run(const float4 *__restrict__ src, const u
 // Registers a long segment (>= kHeavyMin occurrences, cut into runs of B) as
 // work for the slice kernels: one entry (segment, run) per run, and the
 // segment in the combine list when it has more than one run.  Called by one
-// lane; counters[0] / counters[1] count the two lists (zeroed by rowkey_init).
+// lane; counters[0] / counters[1] count the two lists (zeroed with the keys).
 // Capacity: runs <= n/kHeavyMin + n/B <= n/32 for B >= 64.
 __device__ __forceinline__ void push_heavy(int32_t k, int32_t len, int B, uint32_t *counters, int2 *hlist,
                                            int32_t *clist) {
@@ -790,5 +833,29 @@ __device__ __forceinline__ void push_heavy(int32_t k, int32_t len, int B, uint32
 }
 
 constexpr int kHeavyMin = 64;  // segments with at least this many occurrences go to the slice kernels
+constexpr int kBaseRun = 256;  // the plan lists heavy segments in runs of this many occurrences
+
+// The plan's heavy work list: every segment of at least kHeavyMin elements,
+// cut into runs of kBaseRun (push_heavy), so that an apply knows its heavy
+// work before it starts and can run it beside the light rows in one launch.
+// Heavy segments are few (at most n / kHeavyMin), so one atomic per segment.
+__global__ void __launch_bounds__(256)
+    heavy_units_kernel(const int32_t *__restrict__ seg_start, const int32_t *__restrict__ seg_end,
+                       const int64_t *__restrict__ nseg_p, uint32_t *ticket, int2 *hlist, int32_t *clist) {
+  const int64_t nseg = *nseg_p;
+  const int64_t stride = static_cast<int64_t>(gridDim.x) * 256;
+  for (int64_t k = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x; k < nseg; k += stride) {
+    const int32_t len = seg_end[k] - seg_start[k];
+    if (len >= kHeavyMin) push_heavy(static_cast<int32_t>(k), len, kBaseRun, ticket, hlist, clist);
+  }
+}
+
+// After group_by_row: lists the heavy runs in hlist (count ticket[0]) and the
+// segments of more than one run in clist (count ticket[1]).
+inline void list_heavy_units(SegWork<uint32_t> &w, hipStream_t s) {
+  int g = hlr::grid_for(w.n, 256);
+  if (g > 1024) g = 1024;
+  heavy_units_kernel<<<g, 256, 0, s>>>(w.seg_start, w.seg_end, w.nseg, w.ticket, w.hlist, w.clist);
+}
 
 }  // namespace

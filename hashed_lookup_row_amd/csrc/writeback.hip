@@ -15,13 +15,14 @@
 // SGD_SUM — per-row SGD with duplicate gradients summed and applied once (the
 // same sparse-table update pattern at a learning rate other than 1, as in the
 // hashed tables of "DLRMv4: MLPerf recommendation training goes sequential").
-// Positions are grouped by row with a stable radix sort (radix.hpp).  Rows with
-// few occurrences are summed by one wave each (sgd_light), which also lists the
-// runs of longer rows.  Every (run of 256 consecutive occurrences, 128-element
-// slice) of a longer row is summed in batch order by its own wave (sgd_heavy),
-// so a Zipf-hot row (tens of thousands of duplicates) spreads over the whole
-// GPU; sgd_combine then adds each row's run totals in batch order and writes
-// fl(M - fl(lr * s)).
+// Positions are grouped by row with a stable radix sort (radix.hpp), and the
+// plan lists the runs of 256 consecutive occurrences of every longer row.
+// Rows with few occurrences are summed by one wave each (light part).  Every
+// (run, 64-element slice) of a longer row is summed in batch order by its own
+// wave (heavy part), so a Zipf-hot row (tens of thousands of duplicates)
+// spreads over the whole GPU; both parts run in one launch (sgd_apply_kernel,
+// heavy blocks first).  sgd_combine then adds each row's run totals in batch
+// order and writes fl(M - fl(lr * s)).
 //
 // L2_ALIGN — the alternative to Writeback that the same Memory Layer section
 // compares: SGD on ||M[r] - sg(e_i)||^2, i.e. the gradient 2 (M[r] - e_i) per
@@ -220,19 +221,19 @@ __device__ __forceinline__ void sum_run(const float4 *__restrict__ g, const uint
 
 // Light rows (fewer than kHeavyMin occurrences, hence one run): one wave per
 // row; the row is read once, before its gradients, and written once:
-// fl(M - fl(lr * s)).  Longer rows are registered for the slice kernels.  A
-// wave walks rows k, k + waves, ...; the next row's (start, end, row) is
-// loaded while the current row is processed (wave-uniform, so scalar loads).
+// fl(M - fl(lr * s)).  Longer rows belong to the heavy part.  A wave walks
+// rows k, k + waves, ...; the next row's (start, end, row) is loaded while the
+// current row is processed (wave-uniform, so scalar loads).
 template <int NC, bool L2>
-__global__ void __launch_bounds__(kThreads)
-    sgd_light(float4 *table, const float4 *__restrict__ g, const uint32_t *__restrict__ seg_key,
-              const uint32_t *__restrict__ spos, const int32_t *__restrict__ seg_start,
-              const int32_t *__restrict__ seg_end, const int64_t *__restrict__ nseg_p, float lr, int64_t v4,
-              uint32_t *counters, int2 *hlist, int32_t *clist) {
+__device__ __forceinline__ void sgd_light(float4 *table, const float4 *__restrict__ g,
+                                          const uint32_t *__restrict__ seg_key, const uint32_t *__restrict__ spos,
+                                          const int32_t *__restrict__ seg_start, const int32_t *__restrict__ seg_end,
+                                          const int64_t *__restrict__ nseg_p, float lr, int64_t v4, int block,
+                                          int nblocks) {
   const int64_t nseg = *nseg_p;
-  const int64_t waves = static_cast<int64_t>(gridDim.x) * (kThreads / kWave);
+  const int64_t waves = static_cast<int64_t>(nblocks) * (kThreads / kWave);
   const int lane = lane_id();
-  int64_t k = __builtin_amdgcn_readfirstlane(static_cast<int>((blockIdx.x * kThreads + threadIdx.x) / kWave));
+  int64_t k = __builtin_amdgcn_readfirstlane(static_cast<int>((block * kThreads + threadIdx.x) / kWave));
   if (k >= nseg) return;
   int32_t s = seg_start[k], e = seg_end[k];
   int64_t r = seg_key[k];
@@ -241,9 +242,7 @@ __global__ void __launch_bounds__(kThreads)
     const int64_t kc = kn < nseg ? kn : nseg - 1;
     const int32_t sn = seg_start[kc], en = seg_end[kc];
     const int64_t rn = seg_key[kc];
-    if (e - s >= kHeavyMin) {
-      if (lane == 0) push_heavy(static_cast<int32_t>(k), e - s, kRun, counters, hlist, clist);
-    } else {
+    if (e - s < kHeavyMin) {
       float4 m[NC], run[NC];
 #pragma unroll
       for (int q = 0; q < NC; ++q) {
@@ -277,16 +276,18 @@ __device__ __forceinline__ void sgd_write1(float *table, int64_t r, float acc, f
 // row with one run is updated at once; otherwise the run total goes to
 // `partial` for sgd_combine.  No wave writes a multi-run row before the
 // combine, so the L2 gradients all see the row as it was before the batch.
+static_assert(kRun == kBaseRun, "the plan lists heavy runs of kRun occurrences");
+
 template <bool L2>
-__global__ void __launch_bounds__(kThreads)
-    sgd_heavy(float *table, const float *__restrict__ g, const uint32_t *__restrict__ skey,
-              const uint32_t *__restrict__ spos, const int32_t *__restrict__ seg_start,
-              const int32_t *__restrict__ seg_end, const uint32_t *__restrict__ counters,
-              const int2 *__restrict__ hlist, float lr, int64_t D, float *partial) {
+__device__ __forceinline__ void sgd_heavy(float *table, const float *__restrict__ g,
+                                          const uint32_t *__restrict__ skey, const uint32_t *__restrict__ spos,
+                                          const int32_t *__restrict__ seg_start, const int32_t *__restrict__ seg_end,
+                                          const uint32_t *__restrict__ counters, const int2 *__restrict__ hlist,
+                                          float lr, int64_t D, float *partial, int block, int nblocks) {
   const int64_t S = num_slices(D);
   const int64_t items = static_cast<int64_t>(counters[0]) * S;
-  const int64_t waves = static_cast<int64_t>(gridDim.x) * (kThreads / kWave);
-  for (int64_t it = (static_cast<int64_t>(blockIdx.x) * kThreads + threadIdx.x) / kWave; it < items; it += waves) {
+  const int64_t waves = static_cast<int64_t>(nblocks) * (kThreads / kWave);
+  for (int64_t it = (static_cast<int64_t>(block) * kThreads + threadIdx.x) / kWave; it < items; it += waves) {
     const int2 km = hlist[it / S];
     const int64_t e = (it % S) * kSliceElems + lane_id();
     const int32_t s = seg_start[km.x], end = seg_end[km.x];
@@ -305,6 +306,24 @@ __global__ void __launch_bounds__(kThreads)
       partial[run_slot(j0, km.y, kRun) * D + e] = acc;
     }
   }
+}
+
+// Both parts in one launch: blocks [0, heavy_blocks) take the heavy runs, the
+// others the light rows.  The parts touch disjoint rows.
+template <int NC, bool L2>
+__global__ void __launch_bounds__(kThreads)
+    sgd_apply_kernel(float *table, const float *__restrict__ g, const uint32_t *__restrict__ seg_key,
+                     const uint32_t *__restrict__ skey, const uint32_t *__restrict__ spos,
+                     const int32_t *__restrict__ seg_start, const int32_t *__restrict__ seg_end,
+                     const int64_t *__restrict__ nseg_p, const uint32_t *__restrict__ counters,
+                     const int2 *__restrict__ hlist, float lr, int64_t D, int heavy_blocks, float *partial) {
+  const int blk = static_cast<int>(blockIdx.x);
+  if (blk < heavy_blocks)
+    sgd_heavy<L2>(table, g, skey, spos, seg_start, seg_end, counters, hlist, lr, D, partial, blk, heavy_blocks);
+  else
+    sgd_light<NC, L2>(reinterpret_cast<float4 *>(table), reinterpret_cast<const float4 *>(g), seg_key, spos,
+                      seg_start, seg_end, nseg_p, lr, D / 4, blk - heavy_blocks,
+                      static_cast<int>(gridDim.x) - heavy_blocks);
 }
 
 // Rows with several runs: one wave per (row, slice) adds the run totals in
@@ -335,16 +354,12 @@ inline size_t sgd_partial_elems(int64_t n, int64_t dim) {
 template <int NC, bool L2>
 void sgd_launch(float *table, const float *g, SegWork<uint32_t> &w, int cur, float lr, int64_t dim, float *partial,
                 hipStream_t s) {
-  const int64_t v4 = dim / 4;
-  int grid = grid_for(w.n, 4 * 4);
-  if (grid > 4096) grid = 4096;
-  sgd_light<NC, L2><<<grid, kThreads, 0, s>>>(reinterpret_cast<float4 *>(table), reinterpret_cast<const float4 *>(g),
-                                              w.seg_key, w.v[cur], w.seg_start, w.seg_end, w.nseg, lr, v4, w.ticket,
-                                              w.hlist, w.clist);
+  int gl = grid_for(w.n, 4 * 4);
+  if (gl > 4096) gl = 4096;
   int gh = grid_for(w.n / 32 * num_slices(dim), 4);
   if (gh > 2048) gh = 2048;
-  sgd_heavy<L2><<<gh, kThreads, 0, s>>>(table, g, w.k[cur], w.v[cur], w.seg_start, w.seg_end, w.ticket, w.hlist, lr,
-                                        dim, partial);
+  sgd_apply_kernel<NC, L2><<<gh + gl, kThreads, 0, s>>>(table, g, w.seg_key, w.k[cur], w.v[cur], w.seg_start,
+                                                        w.seg_end, w.nseg, w.ticket, w.hlist, lr, dim, gh, partial);
   int gc = grid_for(w.n / 256 * num_slices(dim), 4);
   if (gc > 1024) gc = 1024;
   sgd_combine<<<gc, kThreads, 0, s>>>(table, w.k[cur], w.seg_start, w.seg_end, w.ticket, w.clist, lr, dim, partial);
@@ -405,6 +420,7 @@ void wb_plan(int64_t num_rows, const int64_t *rows, int64_t n, int32_t mode, voi
   SegWork<uint32_t> w;
   segwork_layout<uint32_t>(n, &w, ws);
   group_by_row(w, rows, nullptr, num_rows, stream);
+  list_heavy_units(w, stream);
 }
 
 // Apply: reads the plan left in the workspace by wb_plan.

@@ -35,7 +35,7 @@ import torch
 
 from ._hip import hip
 from . import (WB_LAST_WINS, WB_SGD_SUM, HLRError, _check, _dev, _own_ws, clear_marks, ema_update_apply,
-               ema_update_plan, ema_workspace_size, gather_rows, hashed_rows, load_library, mark_rows,
+               ema_update_plan, ema_update_plan_subset, ema_workspace_size, gather_rows, hashed_rows, load_library, mark_rows,
                mpzch_lookup_or_insert, mpzch_workspace_size, mpzch_zero_inserted, new_workspace, quantize_rows_int8,
                writeback_apply, writeback_plan, writeback_plan_rows, writeback_workspace_size)
 
@@ -303,20 +303,40 @@ class HashedTablesPipeline:
 class EMAPipeline:
     """EMA row updates of several tables per batch (CS3: CTS on positives, CMS on all).
 
-    lookup stream:  ema_update_plan for every update of the batch
-    compute stream: ema_update_apply for every update, in the order given
-    `updates` fixes, per update, the table and its row count; step() takes the
-    rows, masks and values of each update."""
+    lookup stream:  the plan of every update of the batch
+    compute stream: ema_update_apply for every update
+    `tables` fixes, per update, the table and its row count; step() takes the rows, masks and values
+    of each update.  A masked update whose rows tensor is also the rows of an unmasked update of a
+    table with as many rows (CTS beside CMS on the same user or item IDs) gets its plan cut out of
+    that update's plan (ema_update_plan_subset: no second sort), unless derive=False.  Plans are made
+    unmasked first; when every update has its own table the applies follow the plans' order (updates
+    of different tables are independent), else the order given."""
 
-    def __init__(self, tables, n, depth=2):
-        self.tables, self.n = tables, n
+    def __init__(self, tables, n, depth=2, derive=True):
+        self.tables, self.n, self.derive = tables, n, derive
         dev = tables[0].device
         self.ring = _Ring(dev, depth, points=len(tables))
         self._ws = [[new_workspace(dev, ema_workspace_size(t.shape[0], t.shape[1], n)) for t in tables]
                     for _ in range(depth)]
+        self._distinct = len({id(t) for t in tables}) == len(tables)
 
     def restart(self):
         self.ring.restart()
+
+    def _sources(self, rows, masks):
+        """For each update, the unmasked update its plan is cut from (or None), and the planning order."""
+        src = [None] * len(self.tables)
+        if self.derive:
+            for i, m in enumerate(masks):
+                if m is None:
+                    continue
+                for j, mj in enumerate(masks):
+                    if mj is None and rows[j] is rows[i] and self.tables[j].shape[0] == self.tables[i].shape[0]:
+                        src[i] = j
+                        break
+        order = [i for i in range(len(masks)) if masks[i] is None] + \
+                [i for i in range(len(masks)) if masks[i] is not None]
+        return src, order
 
     def step(self, rows, masks, vals, coeffs, mark=None):
         """rows[i], masks[i] (or None), vals[i], coeffs[i] = (a, b) for update i of tables[i].
@@ -324,12 +344,18 @@ class EMAPipeline:
         before and after each apply is enqueued."""
         mark = mark if mark is not None else (lambda tag: None)
         r = self.ring
+        src, order = self._sources(rows, masks)
         k = r.begin_lookup()
         _on(r.lookup, *rows, *masks)
-        for i, t in enumerate(self.tables):
-            ema_update_plan(t.shape[0], rows[i], masks[i], self._ws[k][i], stream=r.ls)
+        for i in order:
+            t = self.tables[i]
+            if src[i] is not None:
+                ema_update_plan_subset(t.shape[0], masks[i], self._ws[k][src[i]], self._ws[k][i], stream=r.ls)
+            else:
+                ema_update_plan(t.shape[0], rows[i], masks[i], self._ws[k][i], stream=r.ls)
             r.mark(k, i)
-        for i, t in enumerate(self.tables):
+        for i in (order if self._distinct else range(len(self.tables))):
+            t = self.tables[i]
             a, b = coeffs[i]
             r.wait(k, i)
             mark(("apply", i, 0))

@@ -198,8 +198,9 @@ hlr_status writeback_plan_rows(int64_t num_rows, int64_t n, const void *ws, size
 /* ------------------------------------------------------------------------
  * EMA row updates   [CS3] sec. 2 (CTS: c <- a*c + (1-a)*v on positive
  * interactions; CMS: s <- b*s + (1-b)*h on every interaction)
- *  For every position i in batch order with rows[i] >= 0 and mask[i] != 0
- *  (mask NULL = every position): T[r] = fl(fl(a*T[r]) + fl(b*vals[i])),
+ *  For every position i in batch order with 0 <= rows[i] < num_rows and
+ *  mask[i] != 0 (mask NULL = every position; other rows take no part):
+ *  T[r] = fl(fl(a*T[r]) + fl(b*vals[i])),
  *  element-wise; duplicates of a row are applied in batch order, so the
  *  result equals the sequential loop bit for bit.  a and b are passed
  *  separately (b is not recomputed as 1-a).
@@ -221,6 +222,21 @@ hlr_status ema_update_plan(int64_t num_rows, const int64_t *rows, const uint8_t 
                            size_t ws_bytes, hipStream_t stream);
 hlr_status ema_update_apply(float *table, int64_t num_rows, int64_t dim, const float *vals, int64_t n, float a,
                             float b, void *ws, size_t ws_bytes, hipStream_t stream);
+
+/* The plan of a subset of another plan's positions, without sorting again
+ * ([CS3] sec. 2: CTS updates on the positive interactions, a subset of the
+ * pairs CMS updates on, keyed by the same user and item IDs).
+ *  src_ws: a workspace holding an ema_update_plan (or ema_update_plan_subset)
+ *    result for rows[n] and num_rows; only read, so it can still be applied.
+ *  mask[n] uint8: the positions to keep.  ws receives the plan that
+ *    ema_update_plan(num_rows, rows, src_mask AND mask, n) would make, and
+ *    applying it gives the same result bit for bit.
+ *  Both workspaces are ema_update_rows_workspace_size(num_rows, dim, n)
+ *  bytes, distinct and not overlapping (HLR_INVALID_ARG otherwise); mask must
+ *  not be NULL (HLR_INVALID_ARG).  The src plan must be complete when this
+ *  runs (same stream, or ordered by an event). */
+hlr_status ema_update_plan_subset(int64_t num_rows, const uint8_t *mask, int64_t n, const void *src_ws,
+                                  size_t src_ws_bytes, void *ws, size_t ws_bytes, hipStream_t stream);
 
 /* ------------------------------------------------------------------------
  * Serving score: int8 row dequantisation fused with a dot product

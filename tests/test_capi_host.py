@@ -125,6 +125,23 @@ def test_split_entry_point_argument_errors(lib):
     assert lib.mpzch_zero_inserted(P_ODD, 64, 8, P16, P16, 10, s) == MISALIGNED
 
 
+def test_ema_plan_subset_argument_errors(lib):
+    s = None
+    need = lib.ema_update_rows_workspace_size(100, 4, 10)
+    other = ctypes.c_void_p(1 << 40)  # a second stand-in workspace, far from P16 (never dereferenced)
+    call = lambda mask=P16, n=10, src=P16, srcb=need, ws=other, wsb=need: lib.ema_update_plan_subset(
+        100, mask, n, src, srcb, ws, wsb, s)
+    assert call(mask=None) == INVALID
+    assert call(ws=P16) == INVALID                                   # the two plans overlap
+    assert call(ws=ctypes.c_void_p((1 << 20) + need - 256)) == INVALID
+    assert call(srcb=need - 1) == WS_SMALL
+    assert call(wsb=need - 1) == WS_SMALL
+    assert call(src=None, srcb=0) == WS_SMALL
+    assert call(src=ctypes.c_void_p((1 << 20) + 16)) == MISALIGNED
+    assert call(n=-1) == INVALID
+    assert call(n=0, src=None, srcb=0, ws=None, wsb=0) == OK        # nothing to plan
+
+
 def test_publishing_entry_point_argument_errors(lib):
     s = None
     assert lib.quantize_rows_int8(P16, 10, 6, P16, 5, None, 0, P16, P16, P16, s) == DIM

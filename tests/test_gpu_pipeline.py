@@ -83,6 +83,36 @@ def test_ema_plan_apply(dev, masked):
     assert bits_equal(to_np(t), table)
 
 
+@pytest.mark.parametrize("src_masked", [False, True])
+@pytest.mark.parametrize("num_rows,n,D,dense", [(300, 30_000, 128, 0.05), (5000, 20_000, 64, 0.7), (40, 777, 8, 0.3)])
+def test_ema_plan_subset(dev, src_masked, num_rows, n, D, dense):
+    """A plan cut out of another plan (positions with a second mask) applies like a plan made from the
+    rows with both masks; the source plan is left intact and still applies to its own result."""
+    g = np.random.default_rng(num_rows + n + src_masked)
+    rows = np.minimum(synth.zipf_ranks(g, num_rows, 1.1, n), num_rows - 1).astype(np.int64)
+    rows[g.random(n) < 0.02] = -1
+    rows[g.random(n) < 0.01] = num_rows + 3  # out of range: takes no part
+    vals = g.standard_normal((n, D)).astype(np.float32)
+    m1 = (g.random(n) < 0.8).astype(np.uint8) if src_masked else None
+    m2 = (g.random(n) < dense).astype(np.uint8)
+    table = g.standard_normal((num_rows, D)).astype(np.float32)
+    t_all, t_sub = (torch.from_numpy(table).to(dev) for _ in range(2))
+    r, v = torch.from_numpy(rows).to(dev), torch.from_numpy(vals).to(dev)
+    ws_src = hlr.new_workspace(dev, hlr.ema_workspace_size(num_rows, D, n))
+    ws_sub = hlr.new_workspace(dev, hlr.ema_workspace_size(num_rows, D, n))
+    hlr.ema_update_plan(num_rows, r, torch.from_numpy(m1).to(dev) if src_masked else None, ws_src)
+    hlr.ema_update_plan_subset(num_rows, torch.from_numpy(m2).to(dev), ws_src, ws_sub)
+    hlr.ema_update_apply(t_sub, v, 0.9, 0.1, ws_sub)
+    hlr.ema_update_apply(t_all, v, 0.95, 0.05, ws_src)
+    both = m2 if m1 is None else (m1 & m2)
+    want_sub, want_all = table.copy(), table.copy()
+    orows = np.where(rows < num_rows, rows, -1)  # the oracle takes -1 for "no row"
+    oracle.ema(want_sub, orows, vals, both, 0.9, 0.1)
+    oracle.ema(want_all, orows, vals, m1, 0.95, 0.05)
+    assert bits_equal(to_np(t_sub), want_sub)
+    assert bits_equal(to_np(t_all), want_all)
+
+
 def prefilled_pair(dev, cfg):
     C, P, D = cfg.capacity, cfg.probes, cfg.dim
     identity = torch.full((C,), -1, dtype=torch.int64, device=dev)
@@ -194,7 +224,8 @@ def test_hashed_tables_pipeline(dev):
         assert bits_equal(to_np(tables[i]), tables_np[i]), i
 
 
-def test_ema_pipeline(dev):
+@pytest.mark.parametrize("derive", [True, False])
+def test_ema_pipeline(dev, derive):
     cfg = synth.CS3
     users, items, D, n = 4096, 8192, 128, 20_000
     g = np.random.default_rng(5)
@@ -212,7 +243,7 @@ def test_ema_pipeline(dev):
     dev_b = [tuple(torch.from_numpy(x).to(dev) for x in (u, it, y)) + ([torch.from_numpy(x).to(dev) for x in v],)
              for (u, it, y, v) in batches]
     torch.cuda.synchronize()
-    pipe = pipeline.EMAPipeline(gpu, n)
+    pipe = pipeline.EMAPipeline(gpu, n, derive=derive)
     coeffs = [(cfg.cts_a, cfg.cts_b), (cfg.cts_a, cfg.cts_b), (cfg.cms_a, cfg.cms_b), (cfg.cms_a, cfg.cms_b)]
     for (ur, ir, yy, vv) in dev_b:
         pipe.step([ur, ir, ur, ir], [yy, yy, None, None], [vv[0], vv[1], vv[2], vv[2]], coeffs)
