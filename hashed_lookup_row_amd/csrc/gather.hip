@@ -10,6 +10,7 @@
 // output rows are streamed with non-temporal stores so the table's hot rows
 // stay in L2/MALL.  No LDS staging: the data has no reuse inside a block.
 #include "hlr_common.hpp"
+#include "step_parts.hpp"
 
 namespace {
 using namespace hlr;
@@ -17,10 +18,12 @@ using namespace hlr;
 constexpr int kThreads = 256;
 constexpr int kUnroll = 4;
 
+// fresh (nullable): positions with fresh[i] == 0 read the zero vector too (a
+// row inserted by this batch's lookup whose storage has not been cleared).
 template <int V4>
 __global__ void __launch_bounds__(kThreads)
-    gather_kernel(const float4 *__restrict__ table, int64_t num_rows, const int64_t *__restrict__ rows, int64_t n,
-                  float4 *__restrict__ out, int64_t v4_rt) {
+    gather_kernel(const float4 *__restrict__ table, int64_t num_rows, const int64_t *__restrict__ rows,
+                  const int8_t *__restrict__ fresh, int64_t n, float4 *__restrict__ out, int64_t v4_rt) {
   const int64_t v4 = V4 > 0 ? V4 : v4_rt;
   const int64_t total = n * v4;
   const int64_t base = static_cast<int64_t>(blockIdx.x) * (kThreads * kUnroll) + threadIdx.x;
@@ -33,7 +36,7 @@ __global__ void __launch_bounds__(kThreads)
     if (u < total) {
       const int64_t i = u / v4;
       const int64_t r = rows[i];
-      if (r >= 0 && r < num_rows) src[k] = r * v4 + (u - i * v4);
+      if (r >= 0 && r < num_rows && (fresh == nullptr || fresh[i] != 0)) src[k] = r * v4 + (u - i * v4);
     }
   }
 #pragma unroll
@@ -53,8 +56,10 @@ __global__ void __launch_bounds__(kThreads)
 
 }  // namespace
 
-extern "C" hlr_status gather_rows(const float *table, int64_t num_rows, int64_t dim, const int64_t *rows, int64_t n,
-                                  float *out, hipStream_t stream) {
+namespace {
+
+hlr_status gather_launch(const float *table, int64_t num_rows, int64_t dim, const int64_t *rows, const int8_t *fresh,
+                         int64_t n, float *out, hipStream_t stream) {
   if (n < 0 || n > kMaxN || num_rows < 0) return HLR_INVALID_ARG;
   if (dim <= 0 || dim % 4 != 0) return HLR_UNSUPPORTED_DIM;
   if (n == 0) return HLR_OK;
@@ -65,13 +70,26 @@ extern "C" hlr_status gather_rows(const float *table, int64_t num_rows, int64_t 
   const float4 *t4 = reinterpret_cast<const float4 *>(table);
   float4 *o4 = reinterpret_cast<float4 *>(out);
   switch (v4) {
-    case 16: gather_kernel<16><<<grid, kThreads, 0, stream>>>(t4, num_rows, rows, n, o4, v4); break;
-    case 32: gather_kernel<32><<<grid, kThreads, 0, stream>>>(t4, num_rows, rows, n, o4, v4); break;
-    case 64: gather_kernel<64><<<grid, kThreads, 0, stream>>>(t4, num_rows, rows, n, o4, v4); break;
-    case 128: gather_kernel<128><<<grid, kThreads, 0, stream>>>(t4, num_rows, rows, n, o4, v4); break;
-    default: gather_kernel<0><<<grid, kThreads, 0, stream>>>(t4, num_rows, rows, n, o4, v4); break;
+    case 16: gather_kernel<16><<<grid, kThreads, 0, stream>>>(t4, num_rows, rows, fresh, n, o4, v4); break;
+    case 32: gather_kernel<32><<<grid, kThreads, 0, stream>>>(t4, num_rows, rows, fresh, n, o4, v4); break;
+    case 64: gather_kernel<64><<<grid, kThreads, 0, stream>>>(t4, num_rows, rows, fresh, n, o4, v4); break;
+    case 128: gather_kernel<128><<<grid, kThreads, 0, stream>>>(t4, num_rows, rows, fresh, n, o4, v4); break;
+    default: gather_kernel<0><<<grid, kThreads, 0, stream>>>(t4, num_rows, rows, fresh, n, o4, v4); break;
   }
   return launch_status();
+}
+
+}  // namespace
+
+extern "C" hlr_status gather_rows(const float *table, int64_t num_rows, int64_t dim, const int64_t *rows, int64_t n,
+                                  float *out, hipStream_t stream) {
+  return gather_launch(table, num_rows, dim, rows, nullptr, n, out, stream);
+}
+
+hlr_status hlr::gather_rows_fresh(const float *table, int64_t num_rows, int64_t dim, const int64_t *rows,
+                                  const int8_t *hit, int64_t n, float *out, hipStream_t stream) {
+  if (n > 0 && !hit) return HLR_INVALID_ARG;
+  return gather_launch(table, num_rows, dim, rows, hit, n, out, stream);
 }
 
 extern "C" hlr_status hashed_rows(const int64_t *ids, int64_t n, int64_t num_rows, int64_t *out_rows,

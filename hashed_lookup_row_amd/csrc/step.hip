@@ -2,12 +2,13 @@
 // for Recommendation Models", sec. 2: MPZCH ID -> row, gather, Writeback with
 // lr = 1) enqueued by a single host call in the two-stream schedule: the
 // ID-side half (lookup/insert, the Writeback plan) on a lookup stream, the row
-// traffic (zero-fill of inserted rows, gather, Writeback apply) on a compute
-// stream, ordered by events.  The overlap is the dispatch/compute stream split
+// traffic (gather, Writeback apply) on a compute stream, ordered by events.  The overlap is the dispatch/compute stream split
 // of "MTGR: Industrial-Scale Generative Recommendation Framework in Meituan",
-// sec. 3.5.  The calls are the library's own entry points, so the batch gives
-// the same results as those calls made one after another on one stream; one
-// host call instead of seven keeps the host ahead of the GPU.  The two halves
+// sec. 3.5.  The calls are the library's own entry points (the gather and
+// the apply in the variants that take the lookup's hit mask in place of a
+// zero-fill of the inserted rows), so the batch gives the same results as
+// those calls made one after another on one stream; one host call instead of
+// seven keeps the host ahead of the GPU.  The two halves
 // can also be enqueued by separate calls, so that a caller enqueues the
 // ID-side half of batch t+1 before the row traffic of batch t (lookahead): the
 // lookup kernels then find the GPU ready while the previous batch's rows move.
@@ -15,6 +16,7 @@
 
 #include "hlr.h"
 #include "hlr_common.hpp"
+#include "step_parts.hpp"
 
 namespace {
 
@@ -60,13 +62,14 @@ extern "C" hlr_status memory_layer_step(int64_t *identity, int64_t *stamps, floa
   }
   if (!cp) return HLR_OK;
   // compute stream
+  // The rows the lookup inserted are not cleared by a kernel of their own: only positions that missed
+  // refer to them, so the gather reads zeros there and the apply takes them as zero (step_parts.hpp).
   if ((st = hip_ok(hipStreamWaitEvent(compute, looked_up, 0))) != HLR_OK) return st;
-  if ((st = mpzch_zero_inserted(values, capacity, dim, out_rows, out_hit, n, compute)) != HLR_OK) return st;
   if (gather_begin && (st = hip_ok(hipEventRecord(gather_begin, compute))) != HLR_OK) return st;
-  if ((st = gather_rows(values, capacity, dim, out_rows, n, out, compute)) != HLR_OK) return st;
+  if ((st = hlr::gather_rows_fresh(values, capacity, dim, out_rows, out_hit, n, out, compute)) != HLR_OK) return st;
   if (gather_end && (st = hip_ok(hipEventRecord(gather_end, compute))) != HLR_OK) return st;
   if ((st = hip_ok(hipStreamWaitEvent(compute, planned, 0))) != HLR_OK) return st;
-  if ((st = writeback_apply(values, capacity, dim, e, n, HLR_WB_LAST_WINS, 1.0f, wb_ws, wb_ws_bytes, compute)) !=
+  if ((st = hlr::writeback_apply_last_fresh(values, capacity, dim, e, n, out_hit, wb_ws, wb_ws_bytes, compute)) !=
       HLR_OK)
     return st;
   if (slot_done && (st = hip_ok(hipEventRecord(slot_done, compute))) != HLR_OK) return st;

@@ -29,6 +29,7 @@
 // occurrence at the row's value before the batch, summed and applied as in
 // SGD_SUM (same kernels, the gradient formed on the fly from M and e).
 #include "radix.hpp"
+#include "step_parts.hpp"
 
 namespace {
 using namespace hlr;
@@ -148,22 +149,29 @@ __global__ void __launch_bounds__(kThreads)
 }
 
 // One wave per winner row (two rows in flight per wave): g = fl(M - e), M' = fl(M - g).
+// fresh (nullable): a row whose last position has fresh[p] == 0 was inserted by
+// this batch's lookup and not cleared; it is taken as zero (M = 0) instead of
+// being read.
 template <int NC>
 __global__ void __launch_bounds__(kThreads)
-    lw_apply(float4 *table, const float4 *__restrict__ src, LWWork w, int64_t v4) {
+    lw_apply(float4 *table, const float4 *__restrict__ src, const int8_t *__restrict__ fresh, LWWork w, int64_t v4) {
   constexpr int RPW = 2;
   const uint32_t count = *w.count;
   const int lane = lane_id();
   const uint32_t waves = gridDim.x * (kThreads / kWave);
   for (uint32_t j0 = ((blockIdx.x * kThreads + threadIdx.x) / kWave) * RPW; j0 < count; j0 += waves * RPW) {
     int64_t mrow[RPW], erow[RPW];
+    bool zero[RPW];
 #pragma unroll
     for (int q = 0; q < RPW; ++q) {
       mrow[q] = -1;
+      zero[q] = false;
       if (j0 + q < count) {
         const int32_t s = w.list[j0 + q];
+        const int32_t p = w.hlast[s];
         mrow[q] = w.hkey[s] * v4;
-        erow[q] = static_cast<int64_t>(w.hlast[s]) * v4;
+        erow[q] = static_cast<int64_t>(p) * v4;
+        if (fresh) zero[q] = fresh[p] == 0;
       }
     }
     float4 m[RPW][NC], e[RPW][NC];
@@ -173,8 +181,8 @@ __global__ void __launch_bounds__(kThreads)
       for (int c = 0; c < NC; ++c) {
         const int64_t col = lane + c * kWave;
         if (mrow[q] >= 0 && col < v4) {
-          m[q][c] = table[mrow[q] + col];
           e[q][c] = src[erow[q] + col];
+          m[q][c] = zero[q] ? make_float4(0.f, 0.f, 0.f, 0.f) : table[mrow[q] + col];
         }
       }
 #pragma unroll
@@ -425,7 +433,7 @@ void wb_plan(int64_t num_rows, const int64_t *rows, int64_t n, int32_t mode, voi
 
 // Apply: reads the plan left in the workspace by wb_plan.
 void wb_apply(float *table, int64_t num_rows, int64_t dim, const float *src, int64_t n, int32_t mode, float lr,
-              void *ws, hipStream_t stream) {
+              void *ws, hipStream_t stream, const int8_t *fresh = nullptr) {
   const int64_t v4 = dim / 4;
   const int64_t nc = (v4 + kWave - 1) / kWave;
   if (mode == HLR_WB_LAST_WINS) {
@@ -435,9 +443,9 @@ void wb_apply(float *table, int64_t num_rows, int64_t dim, const float *src, int
     if (ga > 2048) ga = 2048;
     float4 *t4 = reinterpret_cast<float4 *>(table);
     const float4 *s4 = reinterpret_cast<const float4 *>(src);
-    if (nc == 1) lw_apply<1><<<ga, kThreads, 0, stream>>>(t4, s4, w, v4);
-    else if (nc == 2) lw_apply<2><<<ga, kThreads, 0, stream>>>(t4, s4, w, v4);
-    else lw_apply<4><<<ga, kThreads, 0, stream>>>(t4, s4, w, v4);
+    if (nc == 1) lw_apply<1><<<ga, kThreads, 0, stream>>>(t4, s4, fresh, w, v4);
+    else if (nc == 2) lw_apply<2><<<ga, kThreads, 0, stream>>>(t4, s4, fresh, w, v4);
+    else lw_apply<4><<<ga, kThreads, 0, stream>>>(t4, s4, fresh, w, v4);
     return;
   }
   SegWork<uint32_t> w;
@@ -490,6 +498,20 @@ extern "C" hlr_status writeback_apply(float *table, int64_t num_rows, int64_t di
   if (!aligned(table, 16) || !aligned(src, 16)) return HLR_MISALIGNED;
   if ((st = ws_check(ws, ws_bytes, writeback_rows_workspace_size(num_rows, dim, n, mode))) != HLR_OK) return st;
   wb_apply(table, num_rows, dim, src, n, mode, lr, ws, stream);
+  return launch_status();
+}
+
+hlr_status hlr::writeback_apply_last_fresh(float *table, int64_t num_rows, int64_t dim, const float *src, int64_t n,
+                                           const int8_t *hit, void *ws, size_t ws_bytes, hipStream_t stream) {
+  hlr_status st = wb_args(num_rows, n, HLR_WB_LAST_WINS);
+  if (st != HLR_OK) return st;
+  if (dim <= 0 || dim % 4 != 0 || dim > 1024) return HLR_UNSUPPORTED_DIM;
+  if (n == 0 || num_rows == 0) return HLR_OK;
+  if (!table || !src || !hit) return HLR_INVALID_ARG;
+  if (!aligned(table, 16) || !aligned(src, 16)) return HLR_MISALIGNED;
+  if ((st = ws_check(ws, ws_bytes, writeback_rows_workspace_size(num_rows, dim, n, HLR_WB_LAST_WINS))) != HLR_OK)
+    return st;
+  wb_apply(table, num_rows, dim, src, n, HLR_WB_LAST_WINS, 1.0f, ws, stream, hit);
   return launch_status();
 }
 

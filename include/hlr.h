@@ -342,11 +342,16 @@ hlr_status hashed_rows(const int64_t *ids, int64_t n, int64_t num_rows, int64_t 
  *                   record looked_up;
  *                   writeback_plan(LAST_WINS) over out_rows into wb_ws;
  *                   record planned.
- *   compute stream: wait looked_up; mpzch_zero_inserted;
+ *   compute stream: wait looked_up;
  *                   record gather_begin (if given); gather_rows into out;
  *                   record gather_end (if given); wait planned;
  *                   writeback_apply(LAST_WINS, lr = 1) with e;
  *                   record slot_done (if given).
+ *  The rows the lookup inserts are not zero-filled in memory first (no
+ *  mpzch_zero_inserted): every position that refers to such a row has
+ *  out_hit 0 (a row the batch uses is never evicted by it), so the gather
+ *  reads zeros for positions with out_hit 0 and the apply takes their rows as
+ *  zero, and every inserted row is then written by the apply.
  *  The results equal those calls made one after another on one stream:
  *  identity/stamps/values updated, out_rows/out_hit/out_evicted/out_stats as
  *  mpzch_lookup_or_insert, out[n*dim] the gathered rows (read before the
