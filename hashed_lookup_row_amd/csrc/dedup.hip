@@ -3,10 +3,12 @@
 // each row receives exactly one exact write).  The winner of a key is its last
 // occurrence; distinct keys come out in ascending signed order.
 //
-// Plan: keys are mapped to unsigned order (sign bit flipped) and sorted stably
-// with their positions (LSD radix, 11-bit digits); the segment pass then
-// writes, per distinct key, the key, its last position (stable sort keeps
-// positions ascending inside a key) and, per position, the inverse index.
+// Plan: keys are mapped to unsigned order (sign bit flipped) and sorted with
+// their positions as (key, position) pairs (msort.hpp: tile sort + merge
+// path), so positions are ascending inside a key; the segment pass then
+// writes, per distinct key, the key, its last position and, per position, the
+// inverse index.
+#include "msort.hpp"
 #include "radix.hpp"
 
 namespace {
@@ -64,7 +66,7 @@ extern "C" hlr_status dedup_ids(const int64_t *keys, int64_t n, int64_t *out_uni
   segwork_layout<uint64_t>(n, &w, ws);
   w.nseg = out_num_unique;
   dedup_init<<<grid_for(n, 256), 256, 0, stream>>>(keys, n, w.k[0], w.v[0], w.ticket);
-  const int cur = radix_sort_pairs<uint64_t>(w, 64, stream);
+  const int cur = merge_sort_pairs<uint64_t>(w.k, w.v, n, nullptr, stream);
   segment_sorted<uint64_t>(w, cur, 0ull, false, nullptr, DedupEmit{out_unique, out_last_pos, out_inverse}, stream);
   return launch_status();
 }

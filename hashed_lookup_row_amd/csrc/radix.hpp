@@ -2,6 +2,9 @@
 // sorted keys.  Used to group a batch's positions by key (dedup) or by row
 // (duplicate-summed SGD, EMA), positions ascending inside every group.
 //
+// Row keys (at most 31 bits) take 3-4 passes here; 64-bit ID keys (dedup)
+// are sorted by msort.hpp instead, where 8 radix passes would cost more.
+//
 // Per pass: hist_kernel (per-tile digit histograms) and scatter_kernel (each
 // tile derives its output offsets from all tiles' histograms, then stable
 // ranks inside the tile from wave ballots + per-wave LDS counters).  No kernel

@@ -194,7 +194,7 @@ def test_gather_ragged(dev, n, D):
     assert bits_equal(to_np(out), oracle.gather(table, rows))
 
 
-@pytest.mark.parametrize("n", [1, 2, 4095, 4096, 4097, 20_000, 70_001])
+@pytest.mark.parametrize("n", [1, 2, 4095, 4096, 4097, 8191, 8192, 8193, 16_385, 20_000, 70_001, 262_145])
 def test_dedup_matches_oracle(dev, n):
     g = np.random.default_rng(n)
     pool = np.concatenate([g.integers(-(1 << 62), 1 << 62, size=max(1, n // 3)), [0, -1, 1, -(1 << 63), (1 << 63) - 1]])
@@ -205,6 +205,20 @@ def test_dedup_matches_oracle(dev, n):
     assert u == ouq.size
     assert np.array_equal(to_np(uq)[:u], ouq)
     assert np.array_equal(to_np(lp)[:u], olp)
+    assert np.array_equal(to_np(inv), oinv)
+
+
+@pytest.mark.parametrize("n,distinct", [(30_000, 1), (30_000, 2), (50_000, 7)])
+def test_dedup_few_keys(dev, n, distinct):
+    """Long runs of equal keys: the sort orders them by position alone, across tiles and merge rounds."""
+    g = np.random.default_rng(n + distinct)
+    pool = g.integers(-(1 << 62), 1 << 62, size=distinct)
+    keys = pool[g.integers(0, distinct, size=n)].astype(np.int64)
+    uq, lp, inv, nu = hlr.dedup_ids(torch.from_numpy(keys).to(dev))
+    u = int(to_np(nu)[0])
+    ouq, olp, oinv = oracle.dedup(keys)
+    assert u == ouq.size
+    assert np.array_equal(to_np(uq)[:u], ouq) and np.array_equal(to_np(lp)[:u], olp)
     assert np.array_equal(to_np(inv), oinv)
 
 
