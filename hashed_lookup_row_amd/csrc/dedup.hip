@@ -27,16 +27,14 @@ struct DedupEmit {
   }
 };
 
-__global__ void __launch_bounds__(256)
-    dedup_init(const int64_t *__restrict__ keys, int64_t n, uint64_t *__restrict__ k, uint32_t *__restrict__ v,
-               uint32_t *ticket) {
-  const int64_t i = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;
-  if (i < n) {
-    k[i] = static_cast<uint64_t>(keys[i]) ^ kSign;
-    v[i] = static_cast<uint32_t>(i);
+// The sort's input: pair i is (keys[i] in unsigned order, i).
+struct DedupLoad {
+  const int64_t *keys;
+  __device__ __forceinline__ void operator()(int64_t i, uint64_t *key, uint32_t *pos) const {
+    *key = static_cast<uint64_t>(keys[i]) ^ kSign;
+    *pos = static_cast<uint32_t>(i);
   }
-  if (i < 4) ticket[i] = 0u;
-}
+};
 
 }  // namespace
 
@@ -65,8 +63,7 @@ extern "C" hlr_status dedup_ids(const int64_t *keys, int64_t n, int64_t *out_uni
   if (!aligned(ws, 256)) return HLR_MISALIGNED;
   segwork_layout<uint64_t>(n, &w, ws);
   w.nseg = out_num_unique;
-  dedup_init<<<grid_for(n, 256), 256, 0, stream>>>(keys, n, w.k[0], w.v[0], w.ticket);
-  const int cur = merge_sort_pairs<uint64_t>(w.k, w.v, n, nullptr, stream);
+  const int cur = merge_sort_pairs<uint64_t>(DedupLoad{keys}, w.k, w.v, n, nullptr, stream);
   segment_sorted<uint64_t>(w, cur, 0ull, false, nullptr, DedupEmit{out_unique, out_last_pos, out_inverse}, stream);
   return launch_status();
 }

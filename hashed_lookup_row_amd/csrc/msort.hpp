@@ -92,11 +92,22 @@ __device__ __forceinline__ int ms_lds(int i) { return i + (i >> 4); }
 // each thread sorts its 16 pairs in registers, then log2(NT) merge levels
 // double the sorted runs: the threads write their runs to LDS, and each thread
 // finds where its 16 outputs start in the two runs it merges (binary search,
-// the merge path) and merges them into its registers.  kin/kout may be the
-// same buffer (in place): each block reads its own tile whole before writing it.
-template <typename K, int NT>
+// the merge path) and merges them into its registers.  The input may be the
+// output buffer (in place): each block reads its own tile whole before writing it.
+// Reads pair g of the input: from a (keys, positions) buffer pair.
+template <typename K>
+struct PairsIn {
+  const K *k;
+  const uint32_t *v;
+  __device__ __forceinline__ void operator()(int64_t g, K *key, uint32_t *pos) const {
+    *key = k[g];
+    *pos = v[g];
+  }
+};
+
+template <typename K, int NT, typename Load>
 __global__ void __launch_bounds__(NT)
-    tile_sort_kernel(const K *kin, const uint32_t *vin, K *kout, uint32_t *vout, int64_t n, const uint32_t *nact) {
+    tile_sort_kernel(Load load, K *kout, uint32_t *vout, int64_t n, const uint32_t *nact) {
   constexpr int E = 16;
   constexpr int T = NT * E;
   __shared__ K sk[T + T / 16];
@@ -110,9 +121,9 @@ __global__ void __launch_bounds__(NT)
 #pragma unroll
   for (int e = 0; e < E; ++e) {
     const int64_t g = base + t * E + e;
-    const bool ok = g < m;
-    x[e] = ok ? kin[g] : ~K(0);  // padding sorts last and is never written out
-    y[e] = ok ? vin[g] : 0xffffffffu;
+    x[e] = ~K(0);  // padding sorts last and is never written out
+    y[e] = 0xffffffffu;
+    if (g < m) load(g, &x[e], &y[e]);
   }
   ms_sort16(x, y);
   for (int R = E; R < T; R <<= 1) {  // runs of R -> runs of 2R
@@ -268,16 +279,17 @@ __global__ void __launch_bounds__(kMsThreads)
     }
 }
 
-// Sorts the pairs in (k[0], v[0]) (the first *nact of n slots when nact is
-// given); the result is in buffer kMsResultBuffer.
-template <typename K>
-inline int merge_sort_pairs(K *const k[2], uint32_t *const v[2], int64_t n, const uint32_t *nact, hipStream_t s) {
+// Sorts the pairs that `load` reads (pair g for g below n, or below *nact when
+// given) into (k, v); the result is in buffer kMsResultBuffer.
+template <typename K, typename Load>
+inline int merge_sort_pairs(Load load, K *const k[2], uint32_t *const v[2], int64_t n, const uint32_t *nact,
+                            hipStream_t s) {
   constexpr int64_t tile = ms_tile<K>();
   const int rounds = merge_rounds(n, tile);
   int cur = (rounds % 2 == 0) ? kMsResultBuffer : kMsResultBuffer ^ 1;
   const int tiles = static_cast<int>((n + tile - 1) / tile);
-  tile_sort_kernel<K, ms_tile_threads<K>()><<<tiles, ms_tile_threads<K>(), 0, s>>>(k[0], v[0], k[cur], v[cur], n,
-                                                                                  nact);
+  tile_sort_kernel<K, ms_tile_threads<K>(), Load><<<tiles, ms_tile_threads<K>(), 0, s>>>(load, k[cur], v[cur], n,
+                                                                                        nact);
   const int blocks = static_cast<int>((n + kMsOut - 1) / kMsOut);
   int64_t L = tile;
   for (int r = 0; r < rounds; ++r, L <<= 1) {
