@@ -193,6 +193,9 @@ def main():
         if evs is not None:
             timer.record(evs[3], cur)
 
+    # the lookup state before the first batch, for an untimed replay of the same lookups after the timed
+    # regions (it gives each batch's insert count: rows the gather reads as zero instead of loading)
+    id_snap, st_snap = identity.clone(), stamps.clone()
     la = args.lookahead
     if la:
         pipe.prefetch(ids_dev[0], base_now + 1)
@@ -242,10 +245,20 @@ def main():
     # invalid IDs, both 0 on this workload: see stats_after)
     us = np.array([np.unique(stream[W + k]).size for k in range(K)], dtype=np.float64)
     dup = 1.0 - us.mean() / n
-    gather_bytes = n * R + us * R + n * 8  # write out, read distinct rows, read row indices
+    # rows the gather loads: distinct rows that were already stored (a row inserted by the batch reads as
+    # zero and is not loaded); insert and overflow counts from the replay of the same lookups
+    rstats = torch.zeros((W + K, 6), dtype=torch.int64, device=dev)
+    for t in range(W + K):
+        hlr.mpzch_lookup_or_insert(id_snap, st_snap, None, P, ids_dev[t], base_now + 1 + t, insert=True,
+                                   out_rows=rows_buf, out_hit=hit_buf, out_stats=rstats[t])
+    rst = rstats.cpu().numpy()[W:W + K].astype(np.float64)
+    u_read = us - rst[:, 1] - rst[:, 3]
+    del id_snap, st_snap
+    gather_bytes = n * R + u_read * R + n * 8 + n  # write out, read stored distinct rows, row indices, hit flags
     gather_gbs = float(gather_bytes[gather_steps].sum() / gather_s.sum() / 1e9)
-    wb_bytes = 3 * us * R + n * 8
-    step_bytes = n * R + 4 * us * R + 8 * n
+    # step: gather as above; Writeback apply reads e at each row's last position and the stored rows, and
+    # writes every distinct row
+    step_bytes = n * R + 2 * u_read * R + 2 * us * R + 9 * n
     ms_per_step = total_s / K * 1e3
     value = n * K / total_s
 
@@ -273,8 +286,9 @@ def main():
             "capacity": C, "dim": D, "probes": P, "ids_per_step": n, "universe": cfg.universe,
             "zipf_s": cfg.zipf_s, "fresh_frac": cfg.fresh_frac, "prefilled": True,
             "step": "mpzch_lookup_or_insert + gather_rows + writeback_rows(last_wins, lr=1)",
-            "schedule": ("two streams: lookup (MPZCH without values, Writeback plan) beside compute (zero-fill of "
-                         "new rows, gather, Writeback apply), one library call per half batch; "
+            "schedule": ("two streams: lookup (MPZCH without values, Writeback plan) beside compute (gather, "
+                         "Writeback apply; rows the lookup inserts read as zero through its hit mask), one library "
+                         "call per half batch; "
                          + (f"lookahead: batch t+1's lookup is enqueued before batch t's row traffic, ring depth "
                             f"{args.depth}" if la else f"batch t's lookup with its own row traffic, ring depth "
                                                        f"{args.depth}")),
@@ -297,6 +311,7 @@ def main():
                                    "gather": float(per_op[:, 1].mean() * 1e6),
                                    "writeback": float(per_op[:, 2].mean() * 1e6)} if args.op_events else None)},
         "distinct_rows_per_step": float(us.mean()),
+        "stored_rows_read_per_step": float(u_read.mean()),
         "dup_frac": float(dup),
         "hit_rate_after": None,
         "wall_s": wall,

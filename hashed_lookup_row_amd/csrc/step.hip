@@ -41,7 +41,6 @@ extern "C" hlr_status memory_layer_step(int64_t *identity, int64_t *stamps, floa
   if (!values || !out_rows || !out_hit || !looked_up || !planned) return HLR_INVALID_ARG;
   if (lk && (!identity || !stamps || (n > 0 && !ids))) return HLR_INVALID_ARG;
   if (cp && n > 0 && (!e || !out)) return HLR_INVALID_ARG;
-  if ((gather_begin == nullptr) != (gather_end == nullptr)) return HLR_INVALID_ARG;
   if (!hlr::aligned(values, 16) || (e && !hlr::aligned(e, 16)) || (out && !hlr::aligned(out, 16)) ||
       (identity && !hlr::aligned(identity, 8)) || (stamps && !hlr::aligned(stamps, 8)) ||
       (ids && !hlr::aligned(ids, 8)) || !hlr::aligned(out_rows, 8))

@@ -96,6 +96,8 @@ class MemoryLayerPipeline:
 
     lookup stream:  mpzch_lookup_or_insert(values=None) -> writeback_plan(LAST_WINS)
     compute stream: mpzch_zero_inserted -> gather_rows -> writeback_apply(LAST_WINS)
+                    (native: no zero-fill; the gather and the apply read the rows the lookup
+                    inserted as zero through its hit mask, with the same results)
     step() returns the gathered rows (on the compute stream) and leaves rows/hit of
     the batch in ring slot k (`rows(k)`, `hit(k)`).
 

@@ -358,8 +358,7 @@ hlr_status hashed_rows(const int64_t *ids, int64_t n, int64_t num_rows, int64_t 
  *  Writeback), values[r] <- fl(M - fl(M - e[last position of r])).
  *  Arguments as the calls above; capacity = the table's row count.  Events are
  *  the caller's (hipEventCreateWithFlags; timing needed only for the gather
- *  pair); looked_up and planned are required, the others nullable
- *  (gather_begin and gather_end together).  mz_ws / wb_ws: workspaces of
+ *  pair); looked_up and planned are required, the others nullable.  mz_ws / wb_ws: workspaces of
  *  mpzch_lookup_or_insert_workspace_size(n, 1) and
  *  writeback_rows_workspace_size(capacity, dim, n, HLR_WB_LAST_WINS) bytes;
  *  out_rows, out_hit and wb_ws stay in use until slot_done.
