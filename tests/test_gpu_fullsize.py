@@ -3,7 +3,9 @@
   * Memory-Layer cache: 4,194,304 x 512 fp32, 8 probes, prefilled with a 20M-ID
     universe, then 65,536-ID steps (Zipf 1.05 + 0.5% fresh): rows, hit,
     evicted, stats every step; identity and stamps in full; every touched row
-    bit for bit and the count of non-zero rows (no stray writes).
+    bit for bit and the count of non-zero rows (no stray writes); the same in
+    the benchmark's configuration (one call per half batch, two streams,
+    lookahead, ring depth 3), every batch's gathered rows bit for bit.
   * Serving read path: that prefilled identity, an int8 4Mi x 512 table,
     256 requests x 1024 candidates: lookup-only rows/hit bit-exact, scores
     within 1e-6 of sum_d |x_d u_d|.
@@ -107,6 +109,52 @@ def test_memory_layer_full_size(dev, prefilled):
     nonzero_gpu = int((values != 0).any(dim=1).sum().item())
     assert nonzero_gpu == int(np.count_nonzero(tab.values[idx].any(axis=1)))
     free(values, identity, stamps)
+
+
+def test_memory_layer_full_size_one_call_lookahead(dev, prefilled):
+    """The headline's launch configuration: memory_layer_step through MemoryLayerPipeline, two streams,
+    ring depth 3, batch t+1's lookup enqueued before batch t's row traffic, no synchronisation between
+    batches.  Every batch's gathered rows and stats, the ID table and every touched row bit-exact."""
+    from hashed_lookup_row_amd.pipeline import MemoryLayerPipeline
+    cfg, identity0, stamps0, tab0, base = prefilled
+    C, P, D, n = cfg.capacity, cfg.probes, cfg.dim, cfg.batch
+    identity, stamps = identity0.clone(), stamps0.clone()
+    values = torch.zeros((C, D), dtype=torch.float32, device=dev)
+    tab = oracle.MPZCHTable(C, P, D, with_values=False)
+    tab.identity, tab.stamps = tab0.identity.copy(), tab0.stamps.copy()
+    tab.values = np.zeros((C, D), np.float32)
+    steps, fc = 4, 0
+    ids_np = []
+    for t in range(1, steps + 1):
+        x, fc = synth.mpzch_step_ids(cfg, t, fc)
+        ids_np.append(x)
+    ids = [torch.from_numpy(x).to(dev) for x in ids_np]
+    es = [synth.normal_rows(n, D, cfg.e_std, cfg.config, t + 1, device=dev) for t in range(steps)]
+    outs = [torch.empty((n, D), dtype=torch.float32, device=dev) for _ in range(steps)]
+    stats = [torch.zeros(6, dtype=torch.int64, device=dev) for _ in range(steps)]
+    torch.cuda.synchronize()
+    pipe = MemoryLayerPipeline(identity, stamps, values, P, n, depth=3)
+    pipe.prefetch(ids[0], base + 1, stats=stats[0])
+    for t in range(steps):
+        if t + 1 < steps:
+            pipe.prefetch(ids[t + 1], base + t + 2, stats=stats[t + 1])
+        pipe.step(ids[t], base + t + 1, es[t], out=outs[t], stats=stats[t])
+    touched = set()
+    for t in range(steps):
+        orows, ohit, oev, ost = tab.step(ids_np[t], base + t + 1)
+        oout = tab.gather(orows)
+        tab.writeback(orows, to_np(es[t]))
+        assert bits_equal(to_np(outs[t]), oout), f"gather step {t}"
+        s = to_np(stats[t])
+        assert np.array_equal(s[:5], ost) and s[5] == 0, (t, s, ost)
+        touched.update(np.unique(orows[orows >= 0]).tolist())
+        print(f"step {t}: inserts {ost[1]}", flush=True)
+    assert np.array_equal(to_np(identity), tab.identity)
+    assert np.array_equal(to_np(stamps), tab.stamps)
+    idx = np.array(sorted(touched), dtype=np.int64)
+    assert bits_equal(to_np(values[torch.from_numpy(idx).to(dev)]), tab.values[idx])
+    assert int((values != 0).any(dim=1).sum().item()) == int(np.count_nonzero(tab.values[idx].any(axis=1)))
+    free(values, identity, stamps, *outs)
 
 
 def test_serving_score_full_size(dev, prefilled):
