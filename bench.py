@@ -78,6 +78,8 @@ def parse():
     ap.add_argument("--e-pool", type=int, default=16, help="distinct e batches cycled through")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="oracle time budget for the CPU baseline")
+    ap.add_argument("--ema-lookup-streams", type=int, default=2,
+                    help="cs3: lookup streams the EMA plans run on (independent plans side by side)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain 1 GiB device copy (reference for HBM counters)")
     ap.add_argument("--scale", type=float, default=1.0, help="shrink capacity/universe/batch (testing only)")
@@ -560,7 +562,7 @@ def run_cs3(args):
     # (table, rows index, values index, masked, a, b) per update, in the order applied
     calls = [("c_user", 0, 3, True, cfg.cts_a, cfg.cts_b), ("c_item", 1, 4, True, cfg.cts_a, cfg.cts_b),
              ("s_user", 0, 5, False, cfg.cms_a, cfg.cms_b), ("s_item", 1, 5, False, cfg.cms_a, cfg.cms_b)]
-    pipe = EMAPipeline([tabs[c[0]] for c in calls], n)
+    pipe = EMAPipeline([tabs[c[0]] for c in calls], n, lookup_streams=args.ema_lookup_streams)
 
     def piped_step(s, mark=None):
         x = inp[s % 2]
@@ -608,8 +610,9 @@ def run_cs3(args):
     worst = max(per, key=lambda k: per[k])
     _line("interaction pairs/s (CTS + CMS EMA row updates)", n / step_s, "pairs/s", K, W, step_s * 1e3,
           {"workload": cfg.name, "users": cfg.users, "items": cfg.items, "dim": D, "pairs": n,
-           "schedule": "two streams: the EMA plans on a lookup stream (CMS plans sorted, CTS plans cut out of "
-                       "them by the label mask) beside the four applies on the compute stream"},
+           "schedule": f"the EMA plans on {args.ema_lookup_streams} lookup stream(s) (user-keyed and item-keyed "
+                       "plans side by side; CMS plans sorted, CTS plans cut out of them by the label mask) beside "
+                       "the four applies on the compute stream"},
           _roof(f"ema_update_apply ({worst}: ema_apply_kernel + ema_combine)", nb[worst], per[worst]),
           {"dtype": "fp32", "step_hbm_gbs": tot_bytes / step_s / 1e9,
            "apply_us": {k: v * 1e6 for k, v in per.items()},

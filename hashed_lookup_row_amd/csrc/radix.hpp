@@ -180,17 +180,20 @@ __global__ void __launch_bounds__(kSortThreads)
   const uint32_t mask = static_cast<uint32_t>(bins - 1);
   const int w = threadIdx.x >> 6;
   // This tile's output offset of every digit: (keys with smaller digits) + (same digit, earlier tiles).
-  // Thread d reads digit d of every tile's histogram (rows of 256 counts, coalesced across the block).
+  // Thread d reads digit d of every tile's histogram (rows of 256 counts, coalesced across the block),
+  // 64 tiles per round of loads (a sort here runs about 64 tiles, so usually one round trip).
   nblocks = used_tiles(n, TILE, nblocks);
   {
+    constexpr int kRound = 64;
     const int d = threadIdx.x;
     uint32_t before = 0, total = 0;
-    for (int b0 = 0; b0 < nblocks; b0 += 16) {
-      uint32_t v[16];
+    for (int b0 = 0; b0 < nblocks; b0 += kRound) {
+      uint32_t v[kRound];
 #pragma unroll
-      for (int u = 0; u < 16; ++u) v[u] = b0 + u < nblocks ? counts[static_cast<int64_t>(b0 + u) * kMaxBins + d] : 0u;
+      for (int u = 0; u < kRound; ++u)
+        v[u] = b0 + u < nblocks ? counts[static_cast<int64_t>(b0 + u) * kMaxBins + d] : 0u;
 #pragma unroll
-      for (int u = 0; u < 16; ++u) {
+      for (int u = 0; u < kRound; ++u) {
         if (b0 + u < static_cast<int>(blockIdx.x)) before += v[u];
         total += v[u];
       }
@@ -714,6 +717,25 @@ struct Narrow {
   __host__ __device__ static constexpr int64_t slices(int64_t D) { return (D + kWidth - 1) / kWidth; }
 };
 
+// Group g's value (same lane within the group) in the lanes of group 0.  With
+// four groups of 16 lanes (one "row" each) this is gfx950's row swaps, plain
+// VALU operations: permlane16_swap moves row 1 onto row 0, permlane32_swap
+// row 2, the two together row 3 (lanes of the other rows receive values the
+// caller drops).  Other group counts use a lane permute through LDS.
+template <int G>
+__device__ __forceinline__ float from_group(float x, int g, int lane) {
+  if constexpr (G == 4) {
+    const uint32_t xi = __float_as_uint(x);
+    if (g == 1) return __uint_as_float(__builtin_amdgcn_permlane16_swap(xi, xi, false, false)[1]);
+    const uint32_t y = __builtin_amdgcn_permlane32_swap(xi, xi, false, false)[1];
+    if (g == 2) return __uint_as_float(y);
+    return __uint_as_float(__builtin_amdgcn_permlane16_swap(y, y, false, false)[1]);
+  } else {
+    constexpr int W = 64 / G;
+    return __shfl(x, g * W + (lane & (W - 1)));
+  }
+}
+
 template <int G, int P, typename F>
 __device__ __forceinline__ void slice_run_narrow(const float *__restrict__ src, const uint32_t *__restrict__ spos,
                                                  int32_t j0, int32_t j1, int64_t D, int64_t e, F f) {
@@ -750,13 +772,13 @@ __device__ __forceinline__ void slice_run_narrow(const float *__restrict__ src, 
 #pragma unroll
       for (int u = 0; u < P; ++u)
 #pragma unroll
-        for (int g = 0; g < G; ++g) f(j + G * u + g, g == 0 ? x[u] : __shfl(x[u], g * W + (lane & (W - 1))));
+        for (int g = 0; g < G; ++g) f(j + G * u + g, g == 0 ? x[u] : from_group<G>(x[u], g, lane));
     } else {
 #pragma unroll
       for (int u = 0; u < P; ++u)
 #pragma unroll
         for (int g = 0; g < G; ++g)
-          if (j + G * u + g < j1) f(j + G * u + g, g == 0 ? x[u] : __shfl(x[u], g * W + (lane & (W - 1))));
+          if (j + G * u + g < j1) f(j + G * u + g, g == 0 ? x[u] : from_group<G>(x[u], g, lane));
     }
   }
 }

@@ -305,25 +305,31 @@ class HashedTablesPipeline:
 class EMAPipeline:
     """EMA row updates of several tables per batch (CS3: CTS on positives, CMS on all).
 
-    lookup stream:  the plan of every update of the batch
+    lookup streams: the plan of every update of the batch
     compute stream: ema_update_apply for every update
     `tables` fixes, per update, the table and its row count; step() takes the rows, masks and values
     of each update.  A masked update whose rows tensor is also the rows of an unmasked update of a
     table with as many rows (CTS beside CMS on the same user or item IDs) gets its plan cut out of
     that update's plan (ema_update_plan_subset: no second sort), unless derive=False.  Plans are made
     unmasked first; when every update has its own table the applies follow the plans' order (updates
-    of different tables are independent), else the order given."""
+    of different tables are independent), else the order given.
 
-    def __init__(self, tables, n, depth=2, derive=True):
+    Updates keyed by different rows tensors have independent plans (CS3: the user-keyed ones and the
+    item-keyed ones); with lookup_streams = 2 they are planned on two lookup streams at once.  A plan
+    is a chain of short, latency-bound kernels, so two chains side by side take about as long as one."""
+
+    def __init__(self, tables, n, depth=2, derive=True, lookup_streams=2):
         self.tables, self.n, self.derive = tables, n, derive
         dev = tables[0].device
-        self.ring = _Ring(dev, depth, points=len(tables))
+        self.rings = [_Ring(dev, depth, points=len(tables)) for _ in range(max(1, int(lookup_streams)))]
+        self.ring = self.rings[0]
         self._ws = [[new_workspace(dev, ema_workspace_size(t.shape[0], t.shape[1], n)) for t in tables]
                     for _ in range(depth)]
         self._distinct = len({id(t) for t in tables}) == len(tables)
 
     def restart(self):
-        self.ring.restart()
+        for r in self.rings:
+            r.restart()
 
     def _sources(self, rows, masks):
         """For each update, the unmasked update its plan is cut from (or None), and the planning order."""
@@ -340,30 +346,41 @@ class EMAPipeline:
                 [i for i in range(len(masks)) if masks[i] is not None]
         return src, order
 
+    def _chains(self, rows):
+        """Lookup stream of each update: updates with the same rows tensor share one (a cut plan
+        reads its source plan), distinct rows tensors go round-robin over the lookup streams."""
+        keys = {}
+        return [keys.setdefault(id(r), len(keys)) % len(self.rings) for r in rows]
+
     def step(self, rows, masks, vals, coeffs, mark=None):
         """rows[i], masks[i] (or None), vals[i], coeffs[i] = (a, b) for update i of tables[i].
         mark: optional callable, called on the compute stream with ("apply", i, 0 | 1) just
         before and after each apply is enqueued."""
         mark = mark if mark is not None else (lambda tag: None)
-        r = self.ring
         src, order = self._sources(rows, masks)
-        k = r.begin_lookup()
-        _on(r.lookup, *rows, *masks)
+        chain = self._chains(rows)
+        used = sorted(set(chain))
+        ks = {c: self.rings[c].begin_lookup() for c in used}
+        k = ks[used[0]]
+        for c in used:
+            _on(self.rings[c].lookup, *rows, *masks)
         for i in order:
-            t = self.tables[i]
+            t, r = self.tables[i], self.rings[chain[i]]
             if src[i] is not None:
                 ema_update_plan_subset(t.shape[0], masks[i], self._ws[k][src[i]], self._ws[k][i], stream=r.ls)
             else:
                 ema_update_plan(t.shape[0], rows[i], masks[i], self._ws[k][i], stream=r.ls)
             r.mark(k, i)
+        cs = self.ring.cs
         for i in (order if self._distinct else range(len(self.tables))):
             t = self.tables[i]
             a, b = coeffs[i]
-            r.wait(k, i)
+            self.rings[chain[i]].wait(k, i)
             mark(("apply", i, 0))
-            ema_update_apply(t, vals[i], a, b, self._ws[k][i], stream=r.cs)
+            ema_update_apply(t, vals[i], a, b, self._ws[k][i], stream=cs)
             mark(("apply", i, 1))
-        r.end_compute(k)
+        for r in self.rings:  # every ring advances each step, so their slots stay in step
+            r.end_compute(k)
 
 
 class RESPublisher:

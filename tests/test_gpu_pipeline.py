@@ -224,8 +224,8 @@ def test_hashed_tables_pipeline(dev):
         assert bits_equal(to_np(tables[i]), tables_np[i]), i
 
 
-@pytest.mark.parametrize("derive", [True, False])
-def test_ema_pipeline(dev, derive):
+@pytest.mark.parametrize("derive,lookup_streams", [(True, 2), (True, 1), (False, 2)])
+def test_ema_pipeline(dev, derive, lookup_streams):
     cfg = synth.CS3
     users, items, D, n = 4096, 8192, 128, 20_000
     g = np.random.default_rng(5)
@@ -243,7 +243,7 @@ def test_ema_pipeline(dev, derive):
     dev_b = [tuple(torch.from_numpy(x).to(dev) for x in (u, it, y)) + ([torch.from_numpy(x).to(dev) for x in v],)
              for (u, it, y, v) in batches]
     torch.cuda.synchronize()
-    pipe = pipeline.EMAPipeline(gpu, n, derive=derive)
+    pipe = pipeline.EMAPipeline(gpu, n, derive=derive, lookup_streams=lookup_streams)
     coeffs = [(cfg.cts_a, cfg.cts_b), (cfg.cts_a, cfg.cts_b), (cfg.cms_a, cfg.cms_b), (cfg.cms_a, cfg.cms_b)]
     for (ur, ir, yy, vv) in dev_b:
         pipe.step([ur, ir, ur, ir], [yy, yy, None, None], [vv[0], vv[1], vv[2], vv[2]], coeffs)
