@@ -84,9 +84,12 @@ __device__ __forceinline__ float ema1(float t, float v, float a, float b) { retu
 // A heavy chunk is one dependent chain per element, so its speed is set by how
 // many of its positions are requested ahead: its waves walk 16-element slices,
 // four positions per load instruction, 56 instructions (224 positions) a batch.
-constexpr int kHeavyG = 4;
+// When chunks are long (L >= kWideChunk: a slowly decaying a, so a long
+// warm-up) the chains are few and long and their latency is the whole cost:
+// then 8-element slices, eight positions per instruction (448 a batch), at
+// the price of 32-byte accesses.
 constexpr int kHeavyP = 56;
-using HeavySlices = Narrow<kHeavyG>;
+constexpr int kWideChunk = 2048;
 
 // Heavy rows: one wave per (chunk of <= L occurrences, 16-element slice).  A
 // row with one chunk is applied exactly from its stored value.  For a longer
@@ -96,12 +99,14 @@ using HeavySlices = Narrow<kHeavyG>;
 // its first occurrence) and tau (the state after its last) for ema_combine.
 // The plan lists runs of kBaseRun; a chunk is L / kBaseRun of them, and the
 // wave of a run that does not start a chunk has nothing to do.
+template <int G>
 __device__ __forceinline__ void ema_heavy(float *table, const float *__restrict__ vals,
                                           const uint32_t *__restrict__ skey, const uint32_t *__restrict__ spos,
                                           const int32_t *__restrict__ seg_start, const int32_t *__restrict__ seg_end,
                                           const uint32_t *__restrict__ counters, const int2 *__restrict__ hlist,
                                           float a, float b, int64_t D, int L, int W, float *partial, int block,
                                           int nblocks) {
+  using HeavySlices = Narrow<G>;
   const int64_t S = HeavySlices::slices(D);
   const int64_t items = static_cast<int64_t>(counters[0]) * S;
   const int64_t waves = static_cast<int64_t>(nblocks) * (kThreads / kWave);
@@ -127,7 +132,7 @@ __device__ __forceinline__ void ema_heavy(float *table, const float *__restrict_
     int32_t w0 = whole ? s : from, w1 = whole ? end : j0;
     float sig = st;
     for (int k = 0; k < 2; ++k) {
-      slice_run_narrow<kHeavyG, kHeavyP>(vals, spos, w0, w1, D, e, [&](int32_t, float x) { st = ema1(st, x, a, b); });
+      slice_run_narrow<G, kHeavyP>(vals, spos, w0, w1, D, e, [&](int32_t, float x) { st = ema1(st, x, a, b); });
       if (k == 0) {
         sig = st;
         w0 = w1;
@@ -149,7 +154,7 @@ __device__ __forceinline__ void ema_heavy(float *table, const float *__restrict_
 // Both parts in one launch: blocks [0, heavy_blocks) take the heavy runs (so
 // their chains start first), the others the light rows.  The parts touch
 // disjoint rows.
-template <int NC>
+template <int NC, int G>
 __global__ void __launch_bounds__(kThreads)
     ema_apply_kernel(float *table, const float *__restrict__ vals, const uint32_t *__restrict__ seg_key,
                      const uint32_t *__restrict__ skey, const uint32_t *__restrict__ spos,
@@ -159,8 +164,8 @@ __global__ void __launch_bounds__(kThreads)
                      float *partial) {
   const int blk = static_cast<int>(blockIdx.x);
   if (blk < heavy_blocks)
-    ema_heavy(table, vals, skey, spos, seg_start, seg_end, counters, hlist, a, b, D, L, W, partial, blk,
-              heavy_blocks);
+    ema_heavy<G>(table, vals, skey, spos, seg_start, seg_end, counters, hlist, a, b, D, L, W, partial, blk,
+                 heavy_blocks);
   else
     ema_light<NC>(reinterpret_cast<float4 *>(table), reinterpret_cast<const float4 *>(vals), seg_key, spos,
                   seg_start, seg_end, nseg_p, a, b, D / 4, blk - heavy_blocks,
@@ -266,11 +271,17 @@ void ema_launch(float *table, const float *vals, SegWork<uint32_t> &w, int cur, 
   ema_plan(a, w.n, &L, &W);
   int gl = grid_for(w.n, 4 * 4);
   if (gl > 4096) gl = 4096;
-  int gh = grid_for(w.n / 32 * HeavySlices::slices(dim), 4);
+  const bool wide = L >= kWideChunk;
+  int gh = grid_for(w.n / 32 * (wide ? Narrow<8>::slices(dim) : Narrow<4>::slices(dim)), 4);
   if (gh > 2048) gh = 2048;
-  ema_apply_kernel<NC><<<gh + gl, kThreads, 0, s>>>(table, vals, w.seg_key, w.k[cur], w.v[cur], w.seg_start,
-                                                    w.seg_end, w.nseg, w.ticket, w.hlist, a, b, dim, L, W, gh,
-                                                    partial);
+  if (wide)
+    ema_apply_kernel<NC, 8><<<gh + gl, kThreads, 0, s>>>(table, vals, w.seg_key, w.k[cur], w.v[cur], w.seg_start,
+                                                         w.seg_end, w.nseg, w.ticket, w.hlist, a, b, dim, L, W, gh,
+                                                         partial);
+  else
+    ema_apply_kernel<NC, 4><<<gh + gl, kThreads, 0, s>>>(table, vals, w.seg_key, w.k[cur], w.v[cur], w.seg_start,
+                                                         w.seg_end, w.nseg, w.ticket, w.hlist, a, b, dim, L, W, gh,
+                                                         partial);
   int gc = grid_for(w.n / 256 * num_slices(dim), 4);
   if (gc > 1024) gc = 1024;
   ema_combine<<<gc, kThreads, 0, s>>>(table, vals, w.k[cur], w.v[cur], w.seg_start, w.seg_end, w.ticket, w.clist, a,

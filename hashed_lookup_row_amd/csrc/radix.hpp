@@ -717,19 +717,30 @@ struct Narrow {
   __host__ __device__ static constexpr int64_t slices(int64_t D) { return (D + kWidth - 1) / kWidth; }
 };
 
-// Group g's value (same lane within the group) in the lanes of group 0.  With
-// four groups of 16 lanes (one "row" each) this is gfx950's row swaps, plain
-// VALU operations: permlane16_swap moves row 1 onto row 0, permlane32_swap
-// row 2, the two together row 3 (lanes of the other rows receive values the
-// caller drops).  Other group counts use a lane permute through LDS.
+// Row r (16 lanes) of x in row 0, by gfx950's row swaps (plain VALU
+// operations): permlane16_swap moves row 1 onto row 0, permlane32_swap row 2,
+// the two together row 3; the other rows receive values the caller drops.
+__device__ __forceinline__ uint32_t row_to_row0(uint32_t x, int r) {
+  if (r == 0) return x;
+  if (r == 1) return __builtin_amdgcn_permlane16_swap(x, x, false, false)[1];
+  const uint32_t y = __builtin_amdgcn_permlane32_swap(x, x, false, false)[1];
+  if (r == 2) return y;
+  return __builtin_amdgcn_permlane16_swap(y, y, false, false)[1];
+}
+
+// Group g's value (same lane within the group) in the lanes of group 0.  Four
+// groups of 16 lanes are the four rows; eight groups of 8 lanes are the row
+// halves: the group's row is brought to row 0, then an odd group's half is
+// rotated onto lanes 0-7 (DPP row_ror:8).  Other group counts use a lane
+// permute through LDS.
 template <int G>
 __device__ __forceinline__ float from_group(float x, int g, int lane) {
   if constexpr (G == 4) {
-    const uint32_t xi = __float_as_uint(x);
-    if (g == 1) return __uint_as_float(__builtin_amdgcn_permlane16_swap(xi, xi, false, false)[1]);
-    const uint32_t y = __builtin_amdgcn_permlane32_swap(xi, xi, false, false)[1];
-    if (g == 2) return __uint_as_float(y);
-    return __uint_as_float(__builtin_amdgcn_permlane16_swap(y, y, false, false)[1]);
+    return __uint_as_float(row_to_row0(__float_as_uint(x), g));
+  } else if constexpr (G == 8) {
+    const uint32_t y = row_to_row0(__float_as_uint(x), g >> 1);
+    if ((g & 1) == 0) return __uint_as_float(y);
+    return __int_as_float(__builtin_amdgcn_mov_dpp(static_cast<int>(y), 0x128, 0xf, 0xf, false));
   } else {
     constexpr int W = 64 / G;
     return __shfl(x, g * W + (lane & (W - 1)));
