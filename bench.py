@@ -206,9 +206,8 @@ def main():
     torch.cuda.synchronize()
 
     # two-stream schedule (the headline): gather timed with HIP events on the compute stream on every
-    # `sample`-th step (events add a little time to a step)
-    sample = 4
-    evs = {k: [timer.event() for _ in range(2)] for k in range(0, K, sample)}
+    # EV_SAMPLE-th step (events add a little time to a step)
+    evs = {k: [timer.event() for _ in range(2)] for k in range(0, K, EV_SAMPLE)}
     start, stop = timer.event(), timer.event()
     torch.cuda.synchronize()
     wall0 = time.perf_counter()
@@ -440,6 +439,12 @@ def run_serving(args):
            "score_valu_ops_per_s": float(3 * n * D / np.median(t_score))})
 
 
+# Kernel times inside a timed region are taken with HIP events on every EV_SAMPLE-th step only: each event
+# is a packet on the compute stream between kernels, and events around every kernel of every step add to
+# the step they measure.
+EV_SAMPLE = 4
+
+
 class _EventPool:
     """Timing events created before the timed region: creating HIP events inside it has stalled the GPU
     for tens of milliseconds now and then (the runtime growing its signal pool)."""
@@ -506,7 +511,8 @@ def run_dlrm(args):
     pool = _EventPool(timer, K * 8 * 2 * 2)  # per step: 8 tables x (gather, apply) x 2 edges
     timer.record(a, cur)
     for s in range(K):
-        pipe.step(keys[s % 2], grads[s % 2], cfg.lr, outs, mark=_marker(timer, cur, ev, pool))
+        pipe.step(keys[s % 2], grads[s % 2], cfg.lr, outs,
+                  mark=_marker(timer, cur, ev, pool) if s % EV_SAMPLE == 0 else None)
     timer.record(b, cur)
     torch.cuda.synchronize()
     total = timer.elapsed_s(a, b)
@@ -586,7 +592,7 @@ def run_cs3(args):
     sev = [timer.event() for _ in range(K)]
     timer.record(a, cur)
     for s in range(K):
-        piped_step(W + s, _marker(timer, cur, ev, pool))
+        piped_step(W + s, _marker(timer, cur, ev, pool) if s % EV_SAMPLE == 0 else None)
         timer.record(sev[s], cur)
     timer.record(b, cur)
     torch.cuda.synchronize()
