@@ -66,6 +66,7 @@ def load_library():
             "ema_update_plan": (i32, [i64, p, p, i64, p, sz, p]),
             "ema_update_apply": (i32, [p, i64, i64, p, i64, f32, f32, p, sz, p]),
             "ema_update_plan_subset": (i32, [i64, p, i64, p, sz, p, sz, p]),
+            "ema_update_apply_batch": (i32, [i32, p, p]),
             "writeback_plan_rows": (i32, [i64, i64, p, sz, p, p, p]),
             "quantize_rows_int8": (i32, [p, i64, i64, p, i64, p, i32, p, p, p, p]),
             "mark_rows": (i32, [p, i64, p, i64, p, p, p, p]),
@@ -90,7 +91,7 @@ def exported_symbols():
             "writeback_rows", "ema_update_rows_workspace_size", "ema_update_rows", "gather_dequant_score",
             "hashed_rows", "mpzch_zero_inserted", "writeback_plan", "writeback_apply", "ema_update_plan",
             "ema_update_apply", "writeback_plan_rows", "quantize_rows_int8", "mark_rows", "clear_marks",
-            "dks_workspace_size", "dks_lookup_or_insert", "dks_rehash", "memory_layer_step", "ema_update_plan_subset"]
+            "dks_workspace_size", "dks_lookup_or_insert", "dks_rehash", "memory_layer_step", "ema_update_plan_subset", "ema_update_apply_batch"]
 
 
 def _check(rc: int, what: str):
@@ -339,6 +340,33 @@ def ema_update_plan_subset(num_rows, mask, src_ws, ws, stream=None):
     w, wb = _own_ws(ws, need)
     _check(lib.ema_update_plan_subset(int(num_rows), _ptr(mask), n, sw, swb, w, wb, _stream(mask.device, stream)),
            "ema_update_plan_subset")
+
+
+class _EmaApply(ctypes.Structure):
+    """hlr_ema_apply (include/hlr.h)."""
+    _fields_ = [("table", ctypes.c_void_p), ("num_rows", ctypes.c_int64), ("dim", ctypes.c_int64),
+                ("vals", ctypes.c_void_p), ("n", ctypes.c_int64), ("a", ctypes.c_float), ("b", ctypes.c_float),
+                ("ws", ctypes.c_void_p), ("ws_bytes", ctypes.c_size_t)]
+
+
+def ema_update_apply_batch(updates, stream=None):
+    """Applies up to four independent EMA updates, each (table, vals, a, b, ws) with its plan in ws,
+    in one launch; the results equal ema_update_apply for each in turn."""
+    lib = load_library()
+    arr = (_EmaApply * max(1, len(updates)))()
+    dev = None
+    for i, (table, vals, a, b, ws) in enumerate(updates):
+        _dev(table, "table", torch.float32)
+        _dev(vals, "vals", torch.float32)
+        dim = table.shape[1]
+        n = vals.numel() // dim
+        w, wb = _own_ws(ws, lib.ema_update_rows_workspace_size(table.shape[0], dim, n))
+        arr[i] = _EmaApply(table.data_ptr(), table.shape[0], dim, vals.data_ptr(), n, float(a), float(b), w.value, wb)
+        dev = table.device
+    if not updates:
+        return
+    _check(lib.ema_update_apply_batch(len(updates), ctypes.cast(arr, ctypes.c_void_p), _stream(dev, stream)),
+           "ema_update_apply_batch")
 
 
 def ema_update_apply(table, vals, a, b, ws, stream=None):

@@ -151,25 +151,53 @@ __device__ __forceinline__ void ema_heavy(float *table, const float *__restrict_
   }
 }
 
-// Both parts in one launch: blocks [0, heavy_blocks) take the heavy runs (so
-// their chains start first), the others the light rows.  The parts touch
-// disjoint rows.
-template <int NC, int G>
-__global__ void __launch_bounds__(kThreads)
-    ema_apply_kernel(float *table, const float *__restrict__ vals, const uint32_t *__restrict__ seg_key,
-                     const uint32_t *__restrict__ skey, const uint32_t *__restrict__ spos,
-                     const int32_t *__restrict__ seg_start, const int32_t *__restrict__ seg_end,
-                     const int64_t *__restrict__ nseg_p, const uint32_t *__restrict__ counters,
-                     const int2 *__restrict__ hlist, float a, float b, int64_t D, int L, int W, int heavy_blocks,
-                     float *partial) {
+// One update (table, values, plan) of a launch, and the blocks it owns.
+struct EmaJob {
+  float *table;
+  const float *vals;
+  const uint32_t *seg_key, *skey, *spos;
+  const int32_t *seg_start, *seg_end;
+  const int64_t *nseg;
+  const uint32_t *counters;
+  const int2 *hlist;
+  const int32_t *clist;
+  float *partial;
+  float a, b;
+  int L, W;
+  int wide;  // eight lane groups in the heavy walk (long chunks)
+  int heavy_begin, heavy_blocks, light_begin, light_blocks, comb_begin, comb_blocks;
+};
+
+// Independent updates (distinct tables) applied by one launch: a launch holds
+// the heavy blocks of every update first (so all the long chains start at
+// once), then the light blocks of every update, which stream beside them.
+constexpr int kMaxEmaJobs = 4;
+struct EmaJobs {
+  EmaJob job[kMaxEmaJobs];
+  int count;
+  int64_t D;
+};
+
+template <int NC>
+__global__ void __launch_bounds__(kThreads) ema_apply_kernel(EmaJobs js) {
   const int blk = static_cast<int>(blockIdx.x);
-  if (blk < heavy_blocks)
-    ema_heavy<G>(table, vals, skey, spos, seg_start, seg_end, counters, hlist, a, b, D, L, W, partial, blk,
-                 heavy_blocks);
-  else
-    ema_light<NC>(reinterpret_cast<float4 *>(table), reinterpret_cast<const float4 *>(vals), seg_key, spos,
-                  seg_start, seg_end, nseg_p, a, b, D / 4, blk - heavy_blocks,
-                  static_cast<int>(gridDim.x) - heavy_blocks);
+  for (int i = 0; i < js.count; ++i) {
+    const EmaJob &j = js.job[i];
+    if (blk >= j.heavy_begin && blk < j.heavy_begin + j.heavy_blocks) {
+      if (j.wide)
+        ema_heavy<8>(j.table, j.vals, j.skey, j.spos, j.seg_start, j.seg_end, j.counters, j.hlist, j.a, j.b, js.D,
+                     j.L, j.W, j.partial, blk - j.heavy_begin, j.heavy_blocks);
+      else
+        ema_heavy<4>(j.table, j.vals, j.skey, j.spos, j.seg_start, j.seg_end, j.counters, j.hlist, j.a, j.b, js.D,
+                     j.L, j.W, j.partial, blk - j.heavy_begin, j.heavy_blocks);
+      return;
+    }
+    if (blk >= j.light_begin && blk < j.light_begin + j.light_blocks) {
+      ema_light<NC>(reinterpret_cast<float4 *>(j.table), reinterpret_cast<const float4 *>(j.vals), j.seg_key, j.spos,
+                    j.seg_start, j.seg_end, j.nseg, j.a, j.b, js.D / 4, blk - j.light_begin, j.light_blocks);
+      return;
+    }
+  }
 }
 
 // Rows with several chunks: one wave per (row, slice) walks the chunks in
@@ -180,16 +208,17 @@ __global__ void __launch_bounds__(kThreads)
 // so they are loaded kCombineBatch chunks at a time ahead of it.
 constexpr int kCombineBatch = 16;
 
-__global__ void __launch_bounds__(kThreads)
-    ema_combine(float *table, const float *__restrict__ vals, const uint32_t *__restrict__ skey,
-                const uint32_t *__restrict__ spos, const int32_t *__restrict__ seg_start,
-                const int32_t *__restrict__ seg_end, const uint32_t *__restrict__ counters,
-                const int32_t *__restrict__ clist, float a, float b, int64_t D, int L,
-                const float *__restrict__ partial) {
+__device__ __forceinline__ void ema_combine(float *table, const float *__restrict__ vals,
+                                            const uint32_t *__restrict__ skey, const uint32_t *__restrict__ spos,
+                                            const int32_t *__restrict__ seg_start,
+                                            const int32_t *__restrict__ seg_end,
+                                            const uint32_t *__restrict__ counters,
+                                            const int32_t *__restrict__ clist, float a, float b, int64_t D, int L,
+                                            const float *__restrict__ partial, int block, int nblocks) {
   const int64_t S = num_slices(D);
   const int64_t items = static_cast<int64_t>(counters[1]) * S;
-  const int64_t waves = static_cast<int64_t>(gridDim.x) * (kThreads / kWave);
-  for (int64_t it = (static_cast<int64_t>(blockIdx.x) * kThreads + threadIdx.x) / kWave; it < items; it += waves) {
+  const int64_t waves = static_cast<int64_t>(nblocks) * (kThreads / kWave);
+  for (int64_t it = (static_cast<int64_t>(block) * kThreads + threadIdx.x) / kWave; it < items; it += waves) {
     const int32_t k = clist[it / S];
     const int32_t s = seg_start[k], end = seg_end[k];
     if (end - s <= L) continue;  // one chunk: walked whole by the heavy part
@@ -233,6 +262,18 @@ __global__ void __launch_bounds__(kThreads)
   }
 }
 
+__global__ void __launch_bounds__(kThreads) ema_combine_kernel(EmaJobs js) {
+  const int blk = static_cast<int>(blockIdx.x);
+  for (int i = 0; i < js.count; ++i) {
+    const EmaJob &j = js.job[i];
+    if (blk >= j.comb_begin && blk < j.comb_begin + j.comb_blocks) {
+      ema_combine(j.table, j.vals, j.skey, j.spos, j.seg_start, j.seg_end, j.counters, j.clist, j.a, j.b, js.D, j.L,
+                  j.partial, blk - j.comb_begin, j.comb_blocks);
+      return;
+    }
+  }
+}
+
 // Chunking: a warm-up of W = ceil(28 / -ln a) steps shrinks a start error by
 // e^-28, about 2^-40: far below fp32 resolution, with the remaining steps
 // spent while the two trajectories' roundings fall onto the same value (for
@@ -264,28 +305,62 @@ inline size_t ema_partial_elems(int64_t n, int64_t dim) {
   return static_cast<size_t>(2 * ((n + 255) / 256) + 2) * 2 * static_cast<size_t>(dim / 4);
 }
 
-template <int NC>
-void ema_launch(float *table, const float *vals, SegWork<uint32_t> &w, int cur, float a, float b, int64_t dim,
-                float *partial, hipStream_t s) {
-  int L, W;
-  ema_plan(a, w.n, &L, &W);
-  int gl = grid_for(w.n, 4 * 4);
-  if (gl > 4096) gl = 4096;
-  const bool wide = L >= kWideChunk;
-  int gh = grid_for(w.n / 32 * (wide ? Narrow<8>::slices(dim) : Narrow<4>::slices(dim)), 4);
-  if (gh > 2048) gh = 2048;
-  if (wide)
-    ema_apply_kernel<NC, 8><<<gh + gl, kThreads, 0, s>>>(table, vals, w.seg_key, w.k[cur], w.v[cur], w.seg_start,
-                                                         w.seg_end, w.nseg, w.ticket, w.hlist, a, b, dim, L, W, gh,
-                                                         partial);
-  else
-    ema_apply_kernel<NC, 4><<<gh + gl, kThreads, 0, s>>>(table, vals, w.seg_key, w.k[cur], w.v[cur], w.seg_start,
-                                                         w.seg_end, w.nseg, w.ticket, w.hlist, a, b, dim, L, W, gh,
-                                                         partial);
-  int gc = grid_for(w.n / 256 * num_slices(dim), 4);
-  if (gc > 1024) gc = 1024;
-  ema_combine<<<gc, kThreads, 0, s>>>(table, vals, w.k[cur], w.v[cur], w.seg_start, w.seg_end, w.ticket, w.clist, a,
-                                      b, dim, L, partial);
+// The job of one update: its plan's buffers in ws (grouped by group_by_row),
+// chunking for a, and its block counts.
+EmaJob ema_job(float *table, const float *vals, int64_t n, int64_t dim, float a, float b, void *ws,
+               int64_t num_rows) {
+  SegWork<uint32_t> w;
+  Carver c(ws);
+  c.off = segwork_layout<uint32_t>(n, &w, ws);
+  float *partial = reinterpret_cast<float *>(c.take<float4>(ema_partial_elems(n, dim)));
+  const int cur = sorted_buffer(num_rows);
+  EmaJob j{};
+  j.table = table;
+  j.vals = vals;
+  j.seg_key = w.seg_key;
+  j.skey = w.k[cur];
+  j.spos = w.v[cur];
+  j.seg_start = w.seg_start;
+  j.seg_end = w.seg_end;
+  j.nseg = w.nseg;
+  j.counters = w.ticket;
+  j.hlist = w.hlist;
+  j.clist = w.clist;
+  j.partial = partial;
+  j.a = a;
+  j.b = b;
+  ema_plan(a, n, &j.L, &j.W);
+  j.wide = j.L >= kWideChunk;
+  j.light_blocks = grid_for(n, 4 * 4) < 4096 ? grid_for(n, 4 * 4) : 4096;
+  const int64_t hs = j.wide ? Narrow<8>::slices(dim) : Narrow<4>::slices(dim);
+  j.heavy_blocks = grid_for(n / 32 * hs, 4) < 2048 ? grid_for(n / 32 * hs, 4) : 2048;
+  j.comb_blocks = grid_for(n / 256 * num_slices(dim), 4) < 1024 ? grid_for(n / 256 * num_slices(dim), 4) : 1024;
+  return j;
+}
+
+// Two launches for up to kMaxEmaJobs updates of one dim: heavy blocks of every
+// job, then light blocks of every job; then the combine of every job.
+void ema_launch(EmaJobs &js, hipStream_t s) {
+  int next = 0;
+  for (int i = 0; i < js.count; ++i) {
+    js.job[i].heavy_begin = next;
+    next += js.job[i].heavy_blocks;
+  }
+  for (int i = 0; i < js.count; ++i) {
+    js.job[i].light_begin = next;
+    next += js.job[i].light_blocks;
+  }
+  int comb = 0;
+  for (int i = 0; i < js.count; ++i) {
+    js.job[i].comb_begin = comb;
+    comb += js.job[i].comb_blocks;
+  }
+  if (next == 0) return;
+  const int64_t nc = (js.D / 4 + kWave - 1) / kWave;
+  if (nc == 1) ema_apply_kernel<1><<<next, kThreads, 0, s>>>(js);
+  else if (nc == 2) ema_apply_kernel<2><<<next, kThreads, 0, s>>>(js);
+  else ema_apply_kernel<4><<<next, kThreads, 0, s>>>(js);
+  if (comb > 0) ema_combine_kernel<<<comb, kThreads, 0, s>>>(js);
 }
 
 }  // namespace
@@ -316,15 +391,11 @@ hlr_status ema_ws(void *ws, size_t ws_bytes, size_t need) {
 
 void ema_apply(float *table, int64_t num_rows, int64_t dim, const float *vals, int64_t n, float a, float b, void *ws,
                hipStream_t stream) {
-  SegWork<uint32_t> w;
-  Carver c(ws);
-  c.off = segwork_layout<uint32_t>(n, &w, ws);
-  float *partial = reinterpret_cast<float *>(c.take<float4>(ema_partial_elems(n, dim)));
-  const int cur = sorted_buffer(num_rows);
-  const int64_t nc = (dim / 4 + kWave - 1) / kWave;
-  if (nc == 1) ema_launch<1>(table, vals, w, cur, a, b, dim, partial, stream);
-  else if (nc == 2) ema_launch<2>(table, vals, w, cur, a, b, dim, partial, stream);
-  else ema_launch<4>(table, vals, w, cur, a, b, dim, partial, stream);
+  EmaJobs js{};
+  js.count = 1;
+  js.D = dim;
+  js.job[0] = ema_job(table, vals, n, dim, a, b, ws, num_rows);
+  ema_launch(js, stream);
 }
 
 }  // namespace
@@ -359,6 +430,47 @@ extern "C" hlr_status ema_update_plan(int64_t num_rows, const int64_t *rows, con
   segwork_layout<uint32_t>(n, &w, ws);
   group_by_row(w, rows, mask, num_rows, stream);
   list_heavy_units(w, stream);
+  return launch_status();
+}
+
+namespace {
+
+bool ranges_overlap(const void *a, size_t an, const void *b, size_t bn) {
+  const char *x = static_cast<const char *>(a), *y = static_cast<const char *>(b);
+  return x < y + bn && y < x + an;
+}
+
+}  // namespace
+
+extern "C" hlr_status ema_update_apply_batch(int32_t count, const hlr_ema_apply *updates, hipStream_t stream) {
+  if (count < 0 || count > kMaxEmaJobs || (count > 0 && !updates)) return HLR_INVALID_ARG;
+  EmaJobs js{};
+  js.D = 0;
+  for (int32_t i = 0; i < count; ++i) {
+    const hlr_ema_apply &u = updates[i];
+    hlr_status st = ema_args(u.num_rows, u.n);
+    if (st != HLR_OK) return st;
+    if (u.dim <= 0 || u.dim % 4 != 0 || u.dim > 1024) return HLR_UNSUPPORTED_DIM;
+    if (u.n == 0 || u.num_rows == 0) continue;
+    if (!u.table || !u.vals) return HLR_INVALID_ARG;
+    if (!aligned(u.table, 16) || !aligned(u.vals, 16)) return HLR_MISALIGNED;
+    if ((st = ema_ws(u.ws, u.ws_bytes, ema_update_rows_workspace_size(u.num_rows, u.dim, u.n))) != HLR_OK) return st;
+    if (js.D != 0 && u.dim != js.D) return HLR_INVALID_ARG;  // one dim per launch
+    js.D = u.dim;
+    const size_t tb = static_cast<size_t>(u.num_rows) * static_cast<size_t>(u.dim) * sizeof(float);
+    const size_t wb = ema_update_rows_workspace_size(u.num_rows, u.dim, u.n);
+    for (int32_t k = 0; k < i; ++k) {  // the updates run at once: no shared table or workspace
+      const hlr_ema_apply &v = updates[k];
+      if (v.n == 0 || v.num_rows == 0) continue;
+      const size_t vb = static_cast<size_t>(v.num_rows) * static_cast<size_t>(v.dim) * sizeof(float);
+      if (ranges_overlap(u.table, tb, v.table, vb) ||
+          ranges_overlap(u.ws, wb, v.ws, ema_update_rows_workspace_size(v.num_rows, v.dim, v.n)))
+        return HLR_INVALID_ARG;
+    }
+    js.job[js.count++] = ema_job(u.table, u.vals, u.n, u.dim, u.a, u.b, u.ws, u.num_rows);
+  }
+  if (js.count == 0) return HLR_OK;
+  ema_launch(js, stream);
   return launch_status();
 }
 

@@ -35,7 +35,7 @@ import torch
 
 from ._hip import hip
 from . import (WB_LAST_WINS, WB_SGD_SUM, HLRError, _check, _dev, _own_ws, clear_marks, ema_update_apply,
-               ema_update_plan, ema_update_plan_subset, ema_workspace_size, gather_rows, hashed_rows, load_library, mark_rows,
+               ema_update_apply_batch, ema_update_plan, ema_update_plan_subset, ema_workspace_size, gather_rows, hashed_rows, load_library, mark_rows,
                mpzch_lookup_or_insert, mpzch_workspace_size, mpzch_zero_inserted, new_workspace, quantize_rows_int8,
                writeback_apply, writeback_plan, writeback_plan_rows, writeback_workspace_size)
 
@@ -316,9 +316,12 @@ class EMAPipeline:
 
     Updates keyed by different rows tensors have independent plans (CS3: the user-keyed ones and the
     item-keyed ones); with lookup_streams = 2 they are planned on two lookup streams at once.  A plan
-    is a chain of short, latency-bound kernels, so two chains side by side take about as long as one."""
+    is a chain of short, latency-bound kernels, so two chains side by side take about as long as one.
+    With batch=True (distinct tables of one dim, at most four) all the applies of a batch are one
+    ema_update_apply_batch call once every plan is ready: their long dependent chains then run side by
+    side instead of one update after another; mark is then called with ("apply", -1, 0 | 1)."""
 
-    def __init__(self, tables, n, depth=2, derive=True, lookup_streams=2):
+    def __init__(self, tables, n, depth=2, derive=True, lookup_streams=2, batch=True):
         self.tables, self.n, self.derive = tables, n, derive
         dev = tables[0].device
         self.rings = [_Ring(dev, depth, points=len(tables)) for _ in range(max(1, int(lookup_streams)))]
@@ -326,6 +329,8 @@ class EMAPipeline:
         self._ws = [[new_workspace(dev, ema_workspace_size(t.shape[0], t.shape[1], n)) for t in tables]
                     for _ in range(depth)]
         self._distinct = len({id(t) for t in tables}) == len(tables)
+        # one launch for all the applies of a batch (ema_update_apply_batch): distinct tables of one dim
+        self.batch = bool(batch) and self._distinct and len(tables) <= 4 and len({t.shape[1] for t in tables}) == 1
 
     def restart(self):
         for r in self.rings:
@@ -372,6 +377,16 @@ class EMAPipeline:
                 ema_update_plan(t.shape[0], rows[i], masks[i], self._ws[k][i], stream=r.ls)
             r.mark(k, i)
         cs = self.ring.cs
+        if self.batch:
+            for i in order:
+                self.rings[chain[i]].wait(k, i)
+            mark(("apply", -1, 0))
+            ema_update_apply_batch([(self.tables[i], vals[i], coeffs[i][0], coeffs[i][1], self._ws[k][i])
+                                    for i in order], stream=cs)
+            mark(("apply", -1, 1))
+            for r in self.rings:
+                r.end_compute(k)
+            return
         for i in (order if self._distinct else range(len(self.tables))):
             t = self.tables[i]
             a, b = coeffs[i]

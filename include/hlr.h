@@ -223,6 +223,30 @@ hlr_status ema_update_plan(int64_t num_rows, const int64_t *rows, const uint8_t 
 hlr_status ema_update_apply(float *table, int64_t num_rows, int64_t dim, const float *vals, int64_t n, float a,
                             float b, void *ws, size_t ws_bytes, hipStream_t stream);
 
+/* Several independent EMA updates applied by one launch ([CS3] sec. 2 keeps
+ * four caches per batch: CTS and CMS for users and for items).  Each update
+ * is ema_update_apply(table, num_rows, dim, vals, n, a, b, ws, ws_bytes) with
+ * its plan in ws; the results equal those calls made one after another.  The
+ * heavy rows of all updates start together and their light rows stream
+ * beside them (two kernel launches for the whole batch).
+ *  count in [0, 4]; updates[count] is a host array.  Every update must have
+ *  the same dim (HLR_INVALID_ARG otherwise); tables and workspaces must not
+ *  overlap between updates (HLR_INVALID_ARG).  Updates with n == 0 or
+ *  num_rows == 0 are skipped.  Other errors as ema_update_apply, checked
+ *  for every update before anything is enqueued. */
+typedef struct {
+  float *table;
+  int64_t num_rows;
+  int64_t dim;
+  const float *vals;
+  int64_t n;
+  float a;
+  float b;
+  void *ws;
+  size_t ws_bytes;
+} hlr_ema_apply;
+hlr_status ema_update_apply_batch(int32_t count, const hlr_ema_apply *updates, hipStream_t stream);
+
 /* The plan of a subset of another plan's positions, without sorting again
  * ([CS3] sec. 2: CTS updates on the positive interactions, a subset of the
  * pairs CMS updates on, keyed by the same user and item IDs).

@@ -125,6 +125,37 @@ def test_split_entry_point_argument_errors(lib):
     assert lib.mpzch_zero_inserted(P_ODD, 64, 8, P16, P16, 10, s) == MISALIGNED
 
 
+def test_ema_apply_batch_argument_errors(lib):
+    """Every host-checkable fault of the batched apply returns before anything is enqueued."""
+    class Up(ctypes.Structure):
+        _fields_ = [("table", ctypes.c_void_p), ("num_rows", ctypes.c_int64), ("dim", ctypes.c_int64),
+                    ("vals", ctypes.c_void_p), ("n", ctypes.c_int64), ("a", ctypes.c_float), ("b", ctypes.c_float),
+                    ("ws", ctypes.c_void_p), ("ws_bytes", ctypes.c_size_t)]
+    s = None
+    need = lib.ema_update_rows_workspace_size(100, 8, 10)
+    base = 1 << 30  # stand-in addresses, far apart (never dereferenced)
+
+    def up(k, dim=8, table=None, ws=None, wsb=need, n=10, num_rows=100):
+        return Up(table if table is not None else base + k * (1 << 24), num_rows, dim, base + (1 << 28) + k * (1 << 24),
+                  n, 0.9, 0.1, ws if ws is not None else base + (1 << 29) + k * (1 << 24), wsb)
+
+    def call(*ups, count=None):
+        arr = (Up * max(1, len(ups)))(*ups)
+        return lib.ema_update_apply_batch(len(ups) if count is None else count, ctypes.cast(arr, ctypes.c_void_p), s)
+    assert call(up(0), up(1), up(2), up(3), up(4)) == INVALID             # at most four
+    assert call(up(0), count=-1) == INVALID
+    assert lib.ema_update_apply_batch(2, None, s) == INVALID
+    assert call(up(0), up(1, dim=16, wsb=lib.ema_update_rows_workspace_size(100, 16, 10))) == INVALID  # one dim
+    assert call(up(0), up(1, table=base)) == INVALID                      # same table
+    assert call(up(0), up(1, ws=base + (1 << 29))) == INVALID             # same workspace
+    assert call(up(0), up(1, dim=6)) == DIM
+    assert call(up(0), up(1, wsb=need - 1)) == WS_SMALL
+    assert call(up(0, n=-1)) == INVALID
+    assert call(up(0, table=base + 4)) == MISALIGNED
+    assert call(up(0, n=0), up(1, num_rows=0)) == OK                      # nothing to do
+    assert lib.ema_update_apply_batch(0, None, s) == OK
+
+
 def test_ema_plan_subset_argument_errors(lib):
     s = None
     need = lib.ema_update_rows_workspace_size(100, 4, 10)

@@ -113,6 +113,32 @@ def test_ema_plan_subset(dev, src_masked, num_rows, n, D, dense):
     assert bits_equal(to_np(t_all), want_all)
 
 
+def test_ema_apply_batch(dev):
+    """Four updates of different tables in one launch (long and short chunks, masked and cut plans, a
+    row count that differs per table) equal the oracle applied to each in turn."""
+    g = np.random.default_rng(23)
+    D, n = 64, 40_000
+    specs = [(300, 1.1, 0.99, 0.01, 0.1), (5000, 1.05, 0.95, 0.05, None), (900, 1.2, 0.9, 0.1, 0.5),
+             (300, 1.1, 0.97, 0.03, None)]
+    ups, want = [], []
+    for num_rows, z, a, b, dense in specs:
+        rows = np.minimum(synth.zipf_ranks(g, num_rows, z, n), num_rows - 1).astype(np.int64)
+        rows[g.random(n) < 0.01] = -1
+        vals = g.standard_normal((n, D)).astype(np.float32)
+        mask = (g.random(n) < dense).astype(np.uint8) if dense is not None else None
+        table = g.standard_normal((num_rows, D)).astype(np.float32)
+        t = torch.from_numpy(table).to(dev)
+        ws = hlr.new_workspace(dev, hlr.ema_workspace_size(num_rows, D, n))
+        hlr.ema_update_plan(num_rows, torch.from_numpy(rows).to(dev),
+                            torch.from_numpy(mask).to(dev) if mask is not None else None, ws)
+        ups.append((t, torch.from_numpy(vals).to(dev), a, b, ws))
+        oracle.ema(table, rows, vals, mask, a, b)
+        want.append(table)
+    hlr.ema_update_apply_batch(ups)
+    for (t, *_), w in zip(ups, want):
+        assert bits_equal(to_np(t), w)
+
+
 def prefilled_pair(dev, cfg):
     C, P, D = cfg.capacity, cfg.probes, cfg.dim
     identity = torch.full((C,), -1, dtype=torch.int64, device=dev)
@@ -224,8 +250,9 @@ def test_hashed_tables_pipeline(dev):
         assert bits_equal(to_np(tables[i]), tables_np[i]), i
 
 
-@pytest.mark.parametrize("derive,lookup_streams", [(True, 2), (True, 1), (False, 2)])
-def test_ema_pipeline(dev, derive, lookup_streams):
+@pytest.mark.parametrize("derive,lookup_streams,batch", [(True, 2, True), (True, 2, False), (True, 1, True),
+                                                          (False, 2, True), (False, 1, False)])
+def test_ema_pipeline(dev, derive, lookup_streams, batch):
     cfg = synth.CS3
     users, items, D, n = 4096, 8192, 128, 20_000
     g = np.random.default_rng(5)
@@ -243,7 +270,7 @@ def test_ema_pipeline(dev, derive, lookup_streams):
     dev_b = [tuple(torch.from_numpy(x).to(dev) for x in (u, it, y)) + ([torch.from_numpy(x).to(dev) for x in v],)
              for (u, it, y, v) in batches]
     torch.cuda.synchronize()
-    pipe = pipeline.EMAPipeline(gpu, n, derive=derive, lookup_streams=lookup_streams)
+    pipe = pipeline.EMAPipeline(gpu, n, derive=derive, lookup_streams=lookup_streams, batch=batch)
     coeffs = [(cfg.cts_a, cfg.cts_b), (cfg.cts_a, cfg.cts_b), (cfg.cms_a, cfg.cms_b), (cfg.cms_a, cfg.cms_b)]
     for (ur, ir, yy, vv) in dev_b:
         pipe.step([ur, ir, ur, ir], [yy, yy, None, None], [vv[0], vv[1], vv[2], vv[2]], coeffs)
