@@ -594,10 +594,12 @@ def run_cs3(args):
     # effect, seen as an idle GPU in kernel traces, never with these events)
     sev = [timer.event() for _ in range(K)]
     timer.record(a, cur)
+    h0 = time.perf_counter()
     for s in range(K):
         piped_step(W + s, _marker(timer, cur, ev, pool) if s % EV_SAMPLE == 0 else None)
         timer.record(sev[s], cur)
     timer.record(b, cur)
+    enqueue_s = time.perf_counter() - h0
     torch.cuda.synchronize()
     total = timer.elapsed_s(a, b)
     step_ms = [timer.elapsed_s(a if s == 0 else sev[s - 1], sev[s]) * 1e3 for s in range(K)]
@@ -634,6 +636,7 @@ def run_cs3(args):
           {"dtype": "fp32", "step_hbm_gbs": tot_bytes / step_s / 1e9,
            "apply_us": {k: v * 1e6 for k, v in per.items()},
            "step_ms_median": float(np.median(step_ms)), "step_ms_max": float(np.max(step_ms)),
+           "host_enqueue_us_per_step": enqueue_s / K * 1e6,
            "one_stream": {"ms_per_step": serial / K * 1e3, "pairs_per_s": n * K / serial},
            "top_user_occurrences": int(np.bincount(ur).max())})
 

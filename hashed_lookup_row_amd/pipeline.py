@@ -29,13 +29,14 @@ lookup stream does not wait for the compute stream.
 """
 from __future__ import annotations
 
+import ctypes
 from collections import deque
 
 import torch
 
 from ._hip import hip
 from . import (WB_LAST_WINS, WB_SGD_SUM, HLRError, _check, _dev, _own_ws, clear_marks, ema_update_apply,
-               ema_update_apply_batch, ema_update_plan, ema_update_plan_subset, ema_workspace_size, gather_rows, hashed_rows, load_library, mark_rows,
+               ema_workspace_size, gather_rows, hashed_rows, load_library, mark_rows,
                mpzch_lookup_or_insert, mpzch_workspace_size, mpzch_zero_inserted, new_workspace, quantize_rows_int8,
                writeback_apply, writeback_plan, writeback_plan_rows, writeback_workspace_size)
 
@@ -331,6 +332,20 @@ class EMAPipeline:
         self._distinct = len({id(t) for t in tables}) == len(tables)
         # one launch for all the applies of a batch (ema_update_apply_batch): distinct tables of one dim
         self.batch = bool(batch) and self._distinct and len(tables) <= 4 and len({t.shape[1] for t in tables}) == 1
+        # the plan calls and the batch go straight to the library (a step is enqueued often enough that the
+        # binding's per-call checks and conversions show up in its host time): workspace pointers per slot
+        self._lib = load_library()
+        need = [self._lib.ema_update_rows_workspace_size(t.shape[0], t.shape[1], n) for t in tables]
+        self._wsp = [[_own_ws(w, need[i]) for i, w in enumerate(slot)] for slot in self._ws]
+        self._wsp = [[(p.value, b) for p, b in slot] for slot in self._wsp]
+        if self.batch:
+            from . import _EmaApply
+            self._arr = [(_EmaApply * len(tables))() for _ in range(depth)]
+            for k, arr in enumerate(self._arr):
+                for i, t in enumerate(tables):
+                    _dev(t, "table", torch.float32)
+                    arr[i].table, arr[i].num_rows, arr[i].dim = t.data_ptr(), t.shape[0], t.shape[1]
+                    arr[i].ws, arr[i].ws_bytes = self._wsp[k][i]
 
     def restart(self):
         for r in self.rings:
@@ -367,22 +382,43 @@ class EMAPipeline:
         used = sorted(set(chain))
         ks = {c: self.rings[c].begin_lookup() for c in used}
         k = ks[used[0]]
+        seen = {}
+        for i, (x, m) in enumerate(zip(rows, masks)):  # each distinct input tensor checked and registered once
+            if x.numel() > self.n:
+                raise HLRError(f"rows of update {i} has more than {self.n} elements")
+            for t, name, dt, cnt in ((x, "rows", torch.int64, x.numel()), (m, "mask", torch.uint8, x.numel())):
+                if t is not None and id(t) not in seen:
+                    seen[id(t)] = t
+                    if not (t.is_cuda and t.dtype == dt and t.is_contiguous() and t.numel() == cnt):
+                        raise HLRError(f"{name} of update {i} must be a contiguous GPU {dt} tensor of {cnt} elements")
         for c in used:
-            _on(self.rings[c].lookup, *rows, *masks)
+            _on(self.rings[c].lookup, *seen.values())
+        lib, wsp = self._lib, self._wsp[k]
         for i in order:
             t, r = self.tables[i], self.rings[chain[i]]
+            n = rows[i].numel()
             if src[i] is not None:
-                ema_update_plan_subset(t.shape[0], masks[i], self._ws[k][src[i]], self._ws[k][i], stream=r.ls)
+                rc = lib.ema_update_plan_subset(t.shape[0], masks[i].data_ptr(), n, wsp[src[i]][0], wsp[src[i]][1],
+                                                wsp[i][0], wsp[i][1], r.ls)
             else:
-                ema_update_plan(t.shape[0], rows[i], masks[i], self._ws[k][i], stream=r.ls)
+                rc = lib.ema_update_plan(t.shape[0], rows[i].data_ptr(), None if masks[i] is None else
+                                         masks[i].data_ptr(), n, wsp[i][0], wsp[i][1], r.ls)
+            _check(rc, "ema plan")
             r.mark(k, i)
         cs = self.ring.cs
         if self.batch:
             for i in order:
                 self.rings[chain[i]].wait(k, i)
+            arr = self._arr[k]
+            D = self.tables[0].shape[1]
+            for i in range(len(self.tables)):
+                v = vals[i]
+                if not (v.is_cuda and v.dtype == torch.float32 and v.is_contiguous() and v.numel() == rows[i].numel() * D):
+                    raise HLRError(f"vals of update {i} must be a contiguous GPU float32 tensor of n x {D} elements")
+                arr[i].vals, arr[i].n, arr[i].a, arr[i].b = v.data_ptr(), rows[i].numel(), coeffs[i][0], coeffs[i][1]
+            _on(self.ring.compute, *vals)
             mark(("apply", -1, 0))
-            ema_update_apply_batch([(self.tables[i], vals[i], coeffs[i][0], coeffs[i][1], self._ws[k][i])
-                                    for i in order], stream=cs)
+            _check(lib.ema_update_apply_batch(len(self.tables), ctypes.addressof(arr), cs), "ema_update_apply_batch")
             mark(("apply", -1, 1))
             for r in self.rings:
                 r.end_compute(k)
