@@ -143,11 +143,37 @@ __device__ __forceinline__ uint32_t block_exclusive_scan(uint32_t x, uint32_t *s
   return incl - x;
 }
 
-template <typename K, int ITEMS>
+// Where a pass reads its (key, position) pairs: the ping-pong buffers, or, in
+// the first pass of a grouping by row, the batch's rows themselves (key = the
+// row, or the sentinel num_rows for a row out of range; position = index),
+// which saves the kernel that would write them out first.
+template <typename K>
+struct BufPairs {
+  const K *k;
+  const uint32_t *v;
+  __device__ __forceinline__ K key(int64_t i) const { return k[i]; }
+  __device__ __forceinline__ uint32_t pos(int64_t i) const { return v[i]; }
+};
+
+struct RowPairs {
+  const int64_t *rows;
+  int64_t num_rows;
+  __device__ __forceinline__ uint32_t key(int64_t i) const {
+    const int64_t r = rows[i];
+    return static_cast<uint32_t>(r >= 0 && r < num_rows ? r : num_rows);
+  }
+  __device__ __forceinline__ uint32_t pos(int64_t i) const { return static_cast<uint32_t>(i); }
+};
+
+// init_ticket / init_nact (first pass over RowPairs only): block 0 also clears
+// the plan's counters and records that all n pairs take part.
+template <typename K, int ITEMS, typename Src>
 __global__ void __launch_bounds__(kSortThreads)
-    hist_kernel(const K *__restrict__ keys, int64_t n, const uint32_t *__restrict__ nact, int shift, int bits,
-                uint32_t *counts) {
+    hist_kernel(Src src, int64_t n, const uint32_t *__restrict__ nact, int shift, int bits, uint32_t *counts,
+                uint32_t *init_ticket, uint32_t *init_nact) {
   constexpr int TILE = kSortThreads * ITEMS;
+  if (blockIdx.x == 0 && init_ticket && threadIdx.x < 4) init_ticket[threadIdx.x] = 0u;
+  if (blockIdx.x == 0 && init_nact && threadIdx.x == 0) *init_nact = static_cast<uint32_t>(n);
   n = active_count(n, nact);
   if (static_cast<int64_t>(blockIdx.x) * TILE >= n) return;  // empty tiles are never read (see used_tiles)
   __shared__ uint32_t h[kMaxBins];
@@ -159,17 +185,17 @@ __global__ void __launch_bounds__(kSortThreads)
 #pragma unroll
   for (int k = 0; k < ITEMS; ++k) {
     const int64_t idx = base + k * kSortThreads + threadIdx.x;
-    if (idx < n) atomicAdd(&h[static_cast<uint32_t>(keys[idx] >> shift) & mask], 1u);
+    if (idx < n) atomicAdd(&h[static_cast<uint32_t>(src.key(idx) >> shift) & mask], 1u);
   }
   __syncthreads();
   counts[static_cast<int64_t>(blockIdx.x) * kMaxBins + threadIdx.x] = threadIdx.x < bins ? h[threadIdx.x] : 0u;
 }
 
-template <typename K, int ITEMS>
+template <typename K, int ITEMS, typename Src>
 __global__ void __launch_bounds__(kSortThreads)
-    scatter_kernel(const K *__restrict__ kin, const uint32_t *__restrict__ vin, K *__restrict__ kout,
-                   uint32_t *__restrict__ vout, int64_t n, const uint32_t *__restrict__ nact, int shift, int bits,
-                   const uint32_t *__restrict__ counts, int nblocks) {
+    scatter_kernel(Src src, K *__restrict__ kout, uint32_t *__restrict__ vout, int64_t n,
+                   const uint32_t *__restrict__ nact, int shift, int bits, const uint32_t *__restrict__ counts,
+                   int nblocks) {
   constexpr int TILE = kSortThreads * ITEMS;
   n = active_count(n, nact);
   if (static_cast<int64_t>(blockIdx.x) * TILE >= n) return;  // an empty tile writes nothing
@@ -212,7 +238,7 @@ __global__ void __launch_bounds__(kSortThreads)
   for (int r = 0; r < ITEMS; ++r) {
     const int64_t idx = base + r * hlr::kWave + hlr::lane_id();
     const bool valid = idx < n;
-    const K k = valid ? kin[idx] : K(0);
+    const K k = valid ? src.key(idx) : K(0);
     const uint32_t d = static_cast<uint32_t>(k >> shift) & mask;
     uint64_t peers = hlr::ballot(valid);
     for (int b = 0; b < bits; ++b) {
@@ -224,7 +250,7 @@ __global__ void __launch_bounds__(kSortThreads)
     const uint32_t prev = valid ? cnt[w][d] : 0u;
     if (valid && rin == 0) cnt[w][d] = prev + static_cast<uint32_t>(__popcll(peers));
     kk[r] = k;
-    vv[r] = valid ? vin[idx] : 0u;
+    vv[r] = valid ? src.pos(idx) : 0u;
     rk[r] = prev + rin;
   }
   __syncthreads();
@@ -385,16 +411,29 @@ struct NoEmit {
 };
 
 // Runs every radix pass; returns the index (0/1) of the buffer holding the result.
+// rows != NULL: the first pass reads the pairs from the batch's rows (RowPairs)
+// and sets up the plan's counters and active count on the way; then every
+// element takes part (nact is written, not read, by that pass).
 template <typename K, int ITEMS>
-inline int radix_sort_pairs_t(SegWork<K> &w, int total_bits, const uint32_t *nact, hipStream_t s) {
+inline int radix_sort_pairs_t(SegWork<K> &w, int total_bits, const uint32_t *nact, hipStream_t s,
+                              const int64_t *rows, int64_t num_rows) {
   const SortPlan plan = make_plan(total_bits);
   int cur = 0;
   for (int p = 0; p < plan.passes; ++p) {
-    hist_kernel<K, ITEMS><<<w.nblocks, kSortThreads, 0, s>>>(w.k[cur], w.n, nact, plan.shift[p], plan.bits[p],
-                                                              w.counts);
-    scatter_kernel<K, ITEMS><<<w.nblocks, kSortThreads, 0, s>>>(w.k[cur], w.v[cur], w.k[cur ^ 1], w.v[cur ^ 1],
-                                                                 w.n, nact, plan.shift[p], plan.bits[p], w.counts,
-                                                                 w.nblocks);
+    if (p == 0 && rows) {
+      const RowPairs src{rows, num_rows};
+      hist_kernel<K, ITEMS, RowPairs><<<w.nblocks, kSortThreads, 0, s>>>(src, w.n, nullptr, plan.shift[p],
+                                                                          plan.bits[p], w.counts, w.ticket, w.nact);
+      scatter_kernel<K, ITEMS, RowPairs><<<w.nblocks, kSortThreads, 0, s>>>(
+          src, w.k[cur ^ 1], w.v[cur ^ 1], w.n, nullptr, plan.shift[p], plan.bits[p], w.counts, w.nblocks);
+    } else {
+      const BufPairs<K> src{w.k[cur], w.v[cur]};
+      hist_kernel<K, ITEMS, BufPairs<K>><<<w.nblocks, kSortThreads, 0, s>>>(src, w.n, nact, plan.shift[p],
+                                                                             plan.bits[p], w.counts, nullptr,
+                                                                             nullptr);
+      scatter_kernel<K, ITEMS, BufPairs<K>><<<w.nblocks, kSortThreads, 0, s>>>(
+          src, w.k[cur ^ 1], w.v[cur ^ 1], w.n, nact, plan.shift[p], plan.bits[p], w.counts, w.nblocks);
+    }
     cur ^= 1;
   }
   return cur;
@@ -402,10 +441,11 @@ inline int radix_sort_pairs_t(SegWork<K> &w, int total_bits, const uint32_t *nac
 
 // nact: device count of the elements in use (the first *nact slots), or NULL for all n.
 template <typename K>
-inline int radix_sort_pairs(SegWork<K> &w, int total_bits, hipStream_t s, const uint32_t *nact = nullptr) {
-  if (w.items == 4) return radix_sort_pairs_t<K, 4>(w, total_bits, nact, s);
-  if (w.items == 8) return radix_sort_pairs_t<K, 8>(w, total_bits, nact, s);
-  return radix_sort_pairs_t<K, 16>(w, total_bits, nact, s);
+inline int radix_sort_pairs(SegWork<K> &w, int total_bits, hipStream_t s, const uint32_t *nact = nullptr,
+                            const int64_t *rows = nullptr, int64_t num_rows = 0) {
+  if (w.items == 4) return radix_sort_pairs_t<K, 4>(w, total_bits, nact, s, rows, num_rows);
+  if (w.items == 8) return radix_sort_pairs_t<K, 8>(w, total_bits, nact, s, rows, num_rows);
+  return radix_sort_pairs_t<K, 16>(w, total_bits, nact, s, rows, num_rows);
 }
 
 template <typename K, typename Emit, int ITEMS>
@@ -429,23 +469,6 @@ inline void segment_sorted(SegWork<K> &w, int cur, K excluded, bool use_excluded
 }  // namespace
 
 namespace {
-
-// Sort keys for grouping a batch by row: row r for positions that take part
-// (row in range, mask set), the sentinel num_rows (sorted last, excluded from
-// every segment) for the others.  All n positions are sorted (*nact = n).
-__global__ void __launch_bounds__(256)
-    rowkey_init(const int64_t *__restrict__ rows, const uint8_t *__restrict__ mask, int64_t n, int64_t num_rows,
-                uint32_t *__restrict__ k, uint32_t *__restrict__ v, uint32_t *ticket, uint32_t *nact) {
-  const int64_t i = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;
-  if (i < n) {
-    const int64_t r = rows[i];
-    const bool ok = r >= 0 && r < num_rows && (mask == nullptr || mask[i] != 0);
-    k[i] = ok ? static_cast<uint32_t>(r) : static_cast<uint32_t>(num_rows);
-    v[i] = static_cast<uint32_t>(i);
-  }
-  if (i < 4) ticket[i] = 0u;
-  if (i == 0) *nact = static_cast<uint32_t>(n);
-}
 
 // With a mask, only the positions that take part are sorted: they are first
 // compacted, in position order, into the first *nact slots (a masked update
@@ -592,15 +615,15 @@ inline void small_tiles(SegWork<uint32_t> &w) {
 // (seg_start, seg_end, nseg) built.
 inline int group_by_row(SegWork<uint32_t> &w, const int64_t *rows, const uint8_t *mask, int64_t num_rows,
                         hipStream_t s) {
+  const int bits = bit_width_u64(static_cast<uint64_t>(num_rows));
+  int cur;
   if (mask) {
     small_tiles(w);
     compact_into<4>(w, FromPositions{rows, mask, num_rows}, 0, s);
-  } else {
-    rowkey_init<<<hlr::grid_for(w.n, 256), 256, 0, s>>>(rows, mask, w.n, num_rows, w.k[0], w.v[0], w.ticket,
-                                                       w.nact);
+    cur = radix_sort_pairs<uint32_t>(w, bits, s, w.nact);
+  } else {  // the first pass reads the rows directly
+    cur = radix_sort_pairs<uint32_t>(w, bits, s, w.nact, rows, num_rows);
   }
-  const int bits = bit_width_u64(static_cast<uint64_t>(num_rows));
-  const int cur = radix_sort_pairs<uint32_t>(w, bits, s, w.nact);
   segment_sorted<uint32_t>(w, cur, static_cast<uint32_t>(num_rows), true, w.seg_key, NoEmit{}, s, w.nact);
   return cur;
 }
