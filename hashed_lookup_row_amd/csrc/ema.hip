@@ -6,12 +6,16 @@
 // Plan: positions that take part are grouped by row with a stable radix sort
 // (radix.hpp), so each row's positions come out in batch order.  A row's
 // positions are applied in order (T = fl(fl(a*T) + fl(b*v))): short rows by
-// one wave each (light part), long rows by one wave per (chunk, 16-element
-// slice), the chunks of a row running in parallel from speculative warmed-up
-// states (heavy part) that ema_combine verifies bit for bit.  The result equals
-// the sequential loop bit for bit.  The plan lists the long rows' runs, so one
-// launch (ema_apply_kernel) holds both parts: its first blocks start the long
-// dependent chains and the rest stream the short rows beside them.
+// one wave each (light part), long rows by one wave per (chunk, 16- or
+// 8-element slice), the chunks of a row running in parallel from speculative
+// warmed-up states (heavy part) that ema_combine verifies bit for bit.  The
+// result equals the sequential loop bit for bit.  The plan lists the long
+// rows' runs, so one launch (ema_apply_kernel) holds both parts, for up to
+// four independent updates at once: its first blocks start the long dependent
+// chains of every update and the rest stream the short rows beside them; one
+// more launch (ema_combine_kernel) finishes the rows cut into chunks.  A plan
+// for a subset of another plan's positions (ema_update_plan_subset) is cut out
+// of that plan's sorted pairs instead of being sorted again.
 #include <cmath>
 
 #include "radix.hpp"
