@@ -63,11 +63,15 @@ extern "C" hlr_status memory_layer_step(int64_t *identity, int64_t *stamps, floa
   // compute stream
   // The rows the lookup inserted are not cleared by a kernel of their own: only positions that missed
   // refer to them, so the gather reads zeros there and the apply takes them as zero (step_parts.hpp).
-  if ((st = hip_ok(hipStreamWaitEvent(compute, looked_up, 0))) != HLR_OK) return st;
+  // A compute half enqueued on its own (halves == 2) follows a lookup half enqueued earlier, so its plan is
+  // normally long finished: one wait on `planned` (recorded after `looked_up` on the lookup stream) covers
+  // both.  With both halves in one call the gather starts as soon as the lookup is done.
+  const bool one_wait = halves == 2;
+  if ((st = hip_ok(hipStreamWaitEvent(compute, one_wait ? planned : looked_up, 0))) != HLR_OK) return st;
   if (gather_begin && (st = hip_ok(hipEventRecord(gather_begin, compute))) != HLR_OK) return st;
   if ((st = hlr::gather_rows_fresh(values, capacity, dim, out_rows, out_hit, n, out, compute)) != HLR_OK) return st;
   if (gather_end && (st = hip_ok(hipEventRecord(gather_end, compute))) != HLR_OK) return st;
-  if ((st = hip_ok(hipStreamWaitEvent(compute, planned, 0))) != HLR_OK) return st;
+  if (!one_wait && (st = hip_ok(hipStreamWaitEvent(compute, planned, 0))) != HLR_OK) return st;
   if ((st = hlr::writeback_apply_last_fresh(values, capacity, dim, e, n, out_hit, wb_ws, wb_ws_bytes, compute)) !=
       HLR_OK)
     return st;

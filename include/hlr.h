@@ -371,6 +371,8 @@ hlr_status hashed_rows(const int64_t *ids, int64_t n, int64_t num_rows, int64_t 
  *                   record gather_end (if given); wait planned;
  *                   writeback_apply(LAST_WINS, lr = 1) with e;
  *                   record slot_done (if given).
+ *   (A compute half enqueued alone, halves = 2, waits once, on planned,
+ *   before the gather: planned follows looked_up on the lookup stream.)
  *  The rows the lookup inserts are not zero-filled in memory first (no
  *  mpzch_zero_inserted): every position that refers to such a row has
  *  out_hit 0 (a row the batch uses is never evicted by it), so the gather
