@@ -67,6 +67,7 @@ def load_library():
             "ema_update_apply": (i32, [p, i64, i64, p, i64, f32, f32, p, sz, p]),
             "ema_update_plan_subset": (i32, [i64, p, i64, p, sz, p, sz, p]),
             "ema_update_apply_batch": (i32, [i32, p, p]),
+            "writeback_apply_batch": (i32, [i32, p, i32, p]),
             "writeback_plan_rows": (i32, [i64, i64, p, sz, p, p, p]),
             "quantize_rows_int8": (i32, [p, i64, i64, p, i64, p, i32, p, p, p, p]),
             "mark_rows": (i32, [p, i64, p, i64, p, p, p, p]),
@@ -91,7 +92,8 @@ def exported_symbols():
             "writeback_rows", "ema_update_rows_workspace_size", "ema_update_rows", "gather_dequant_score",
             "hashed_rows", "mpzch_zero_inserted", "writeback_plan", "writeback_apply", "ema_update_plan",
             "ema_update_apply", "writeback_plan_rows", "quantize_rows_int8", "mark_rows", "clear_marks",
-            "dks_workspace_size", "dks_lookup_or_insert", "dks_rehash", "memory_layer_step", "ema_update_plan_subset", "ema_update_apply_batch"]
+            "dks_workspace_size", "dks_lookup_or_insert", "dks_rehash", "memory_layer_step", "ema_update_plan_subset", "ema_update_apply_batch",
+            "writeback_apply_batch"]
 
 
 def _check(rc: int, what: str):
@@ -317,6 +319,33 @@ def writeback_apply(table, src, ws, mode=WB_LAST_WINS, lr=1.0, stream=None):
     _check(lib.writeback_apply(_ptr(table), table.shape[0], dim, _ptr(src), n, int(mode), float(lr), w, wb,
                                _stream(table.device, stream)), "writeback_apply")
     return table
+
+
+class _WbApply(ctypes.Structure):
+    """hlr_wb_apply (include/hlr.h)."""
+    _fields_ = [("table", ctypes.c_void_p), ("num_rows", ctypes.c_int64), ("dim", ctypes.c_int64),
+                ("src", ctypes.c_void_p), ("n", ctypes.c_int64), ("lr", ctypes.c_float),
+                ("ws", ctypes.c_void_p), ("ws_bytes", ctypes.c_size_t)]
+
+
+def writeback_apply_batch(updates, mode=WB_SGD_SUM, stream=None):
+    """Applies up to eight independent SGD_SUM / L2_ALIGN updates, each (table, src, lr, ws) with its
+    plan in ws, in two launches; the results equal writeback_apply for each in turn."""
+    lib = load_library()
+    arr = (_WbApply * max(1, len(updates)))()
+    dev = None
+    for i, (table, src, lr, ws) in enumerate(updates):
+        _dev(table, "table", torch.float32)
+        _dev(src, "src", torch.float32)
+        dim = table.shape[1]
+        n = src.numel() // dim
+        w, wb = _own_ws(ws, lib.writeback_rows_workspace_size(table.shape[0], dim, n, int(mode)))
+        arr[i] = _WbApply(table.data_ptr(), table.shape[0], dim, src.data_ptr(), n, float(lr), w.value, wb)
+        dev = table.device
+    if not updates:
+        return
+    _check(lib.writeback_apply_batch(len(updates), ctypes.cast(arr, ctypes.c_void_p), int(mode),
+                                     _stream(dev, stream)), "writeback_apply_batch")
 
 
 def ema_update_plan(num_rows, rows, mask, ws, stream=None):

@@ -21,8 +21,10 @@
 // (run, 64-element slice) of a longer row is summed in batch order by its own
 // wave (heavy part), so a Zipf-hot row (tens of thousands of duplicates)
 // spreads over the whole GPU; both parts run in one launch (sgd_apply_kernel,
-// heavy blocks first).  sgd_combine then adds each row's run totals in batch
-// order and writes fl(M - fl(lr * s)).
+// heavy blocks first).  sgd_combine_kernel then adds each row's run totals in
+// batch order and writes fl(M - fl(lr * s)).  The two launches take up to
+// eight independent updates (distinct tables) at once: the heavy blocks of
+// all of them first, then the light blocks of all of them.
 //
 // L2_ALIGN — the alternative to Writeback that the same Memory Layer section
 // compares: SGD on ||M[r] - sg(e_i)||^2, i.e. the gradient 2 (M[r] - e_i) per
@@ -316,34 +318,62 @@ __device__ __forceinline__ void sgd_heavy(float *table, const float *__restrict_
   }
 }
 
-// Both parts in one launch: blocks [0, heavy_blocks) take the heavy runs, the
-// others the light rows.  The parts touch disjoint rows.
+// One update (table, gradients, plan) of a launch, and the blocks it owns.
+struct SgdJob {
+  float *table;
+  const float *g;
+  const uint32_t *seg_key, *skey, *spos;
+  const int32_t *seg_start, *seg_end;
+  const int64_t *nseg;
+  const uint32_t *counters;
+  const int2 *hlist;
+  const int32_t *clist;
+  float *partial;
+  float lr;
+  int heavy_begin, heavy_blocks, light_begin, light_blocks, comb_begin, comb_blocks;
+};
+
+// Independent updates (distinct tables) applied by one launch: the heavy
+// blocks of every update first (their runs start at once), then the light
+// blocks of every update.  The parts and the updates touch disjoint rows.
+constexpr int kMaxSgdJobs = 8;
+struct SgdJobs {
+  SgdJob job[kMaxSgdJobs];
+  int count;
+  int64_t D;
+};
+
 template <int NC, bool L2>
-__global__ void __launch_bounds__(kThreads)
-    sgd_apply_kernel(float *table, const float *__restrict__ g, const uint32_t *__restrict__ seg_key,
-                     const uint32_t *__restrict__ skey, const uint32_t *__restrict__ spos,
-                     const int32_t *__restrict__ seg_start, const int32_t *__restrict__ seg_end,
-                     const int64_t *__restrict__ nseg_p, const uint32_t *__restrict__ counters,
-                     const int2 *__restrict__ hlist, float lr, int64_t D, int heavy_blocks, float *partial) {
+__global__ void __launch_bounds__(kThreads) sgd_apply_kernel(SgdJobs js) {
   const int blk = static_cast<int>(blockIdx.x);
-  if (blk < heavy_blocks)
-    sgd_heavy<L2>(table, g, skey, spos, seg_start, seg_end, counters, hlist, lr, D, partial, blk, heavy_blocks);
-  else
-    sgd_light<NC, L2>(reinterpret_cast<float4 *>(table), reinterpret_cast<const float4 *>(g), seg_key, spos,
-                      seg_start, seg_end, nseg_p, lr, D / 4, blk - heavy_blocks,
-                      static_cast<int>(gridDim.x) - heavy_blocks);
+  for (int i = 0; i < js.count; ++i) {
+    const SgdJob &j = js.job[i];
+    if (blk >= j.heavy_begin && blk < j.heavy_begin + j.heavy_blocks) {
+      sgd_heavy<L2>(j.table, j.g, j.skey, j.spos, j.seg_start, j.seg_end, j.counters, j.hlist, j.lr, js.D,
+                    j.partial, blk - j.heavy_begin, j.heavy_blocks);
+      return;
+    }
+    if (blk >= j.light_begin && blk < j.light_begin + j.light_blocks) {
+      sgd_light<NC, L2>(reinterpret_cast<float4 *>(j.table), reinterpret_cast<const float4 *>(j.g), j.seg_key,
+                        j.spos, j.seg_start, j.seg_end, j.nseg, j.lr, js.D / 4, blk - j.light_begin,
+                        j.light_blocks);
+      return;
+    }
+  }
 }
 
 // Rows with several runs: one wave per (row, slice) adds the run totals in
 // batch order, then updates the row once.
-__global__ void __launch_bounds__(kThreads)
-    sgd_combine(float *table, const uint32_t *__restrict__ skey, const int32_t *__restrict__ seg_start,
-                const int32_t *__restrict__ seg_end, const uint32_t *__restrict__ counters,
-                const int32_t *__restrict__ clist, float lr, int64_t D, const float *__restrict__ partial) {
+__device__ __forceinline__ void sgd_combine(float *table, const uint32_t *__restrict__ skey,
+                                            const int32_t *__restrict__ seg_start,
+                                            const int32_t *__restrict__ seg_end,
+                                            const uint32_t *__restrict__ counters,
+                                            const int32_t *__restrict__ clist, float lr, int64_t D,
+                                            const float *__restrict__ partial, int block, int nblocks) {
   const int64_t S = num_slices(D);
   const int64_t items = static_cast<int64_t>(counters[1]) * S;
-  const int64_t waves = static_cast<int64_t>(gridDim.x) * (kThreads / kWave);
-  for (int64_t it = (static_cast<int64_t>(blockIdx.x) * kThreads + threadIdx.x) / kWave; it < items; it += waves) {
+  const int64_t waves = static_cast<int64_t>(nblocks) * (kThreads / kWave);
+  for (int64_t it = (static_cast<int64_t>(block) * kThreads + threadIdx.x) / kWave; it < items; it += waves) {
     const int32_t k = clist[it / S];
     const int64_t e = (it % S) * kSliceElems + lane_id();
     const int32_t s = seg_start[k], end = seg_end[k];
@@ -355,31 +385,75 @@ __global__ void __launch_bounds__(kThreads)
   }
 }
 
+__global__ void __launch_bounds__(kThreads) sgd_combine_kernel(SgdJobs js) {
+  const int blk = static_cast<int>(blockIdx.x);
+  for (int i = 0; i < js.count; ++i) {
+    const SgdJob &j = js.job[i];
+    if (blk >= j.comb_begin && blk < j.comb_begin + j.comb_blocks) {
+      sgd_combine(j.table, j.skey, j.seg_start, j.seg_end, j.counters, j.clist, j.lr, js.D, j.partial,
+                  blk - j.comb_begin, j.comb_blocks);
+      return;
+    }
+  }
+}
+
 inline size_t sgd_partial_elems(int64_t n, int64_t dim) {
   return static_cast<size_t>(2 * ((n + kRun - 1) / kRun) + 2) * static_cast<size_t>(dim / 4);
 }
 
-template <int NC, bool L2>
-void sgd_launch(float *table, const float *g, SegWork<uint32_t> &w, int cur, float lr, int64_t dim, float *partial,
-                hipStream_t s) {
-  int gl = grid_for(w.n, 4 * 4);
-  if (gl > 4096) gl = 4096;
-  int gh = grid_for(w.n / 32 * num_slices(dim), 4);
-  if (gh > 2048) gh = 2048;
-  sgd_apply_kernel<NC, L2><<<gh + gl, kThreads, 0, s>>>(table, g, w.seg_key, w.k[cur], w.v[cur], w.seg_start,
-                                                        w.seg_end, w.nseg, w.ticket, w.hlist, lr, dim, gh, partial);
-  int gc = grid_for(w.n / 256 * num_slices(dim), 4);
-  if (gc > 1024) gc = 1024;
-  sgd_combine<<<gc, kThreads, 0, s>>>(table, w.k[cur], w.seg_start, w.seg_end, w.ticket, w.clist, lr, dim, partial);
+// The job of one SGD_SUM / L2_ALIGN update: its plan's buffers in ws and its block counts.
+SgdJob sgd_job(float *table, const float *g, int64_t n, int64_t dim, float lr, void *ws, int64_t num_rows) {
+  SegWork<uint32_t> w;
+  Carver c(ws);
+  c.off = segwork_layout<uint32_t>(n, &w, ws);
+  float *partial = reinterpret_cast<float *>(c.take<float4>(sgd_partial_elems(n, dim)));
+  const int cur = sorted_buffer(num_rows);
+  SgdJob j{};
+  j.table = table;
+  j.g = g;
+  j.seg_key = w.seg_key;
+  j.skey = w.k[cur];
+  j.spos = w.v[cur];
+  j.seg_start = w.seg_start;
+  j.seg_end = w.seg_end;
+  j.nseg = w.nseg;
+  j.counters = w.ticket;
+  j.hlist = w.hlist;
+  j.clist = w.clist;
+  j.partial = partial;
+  j.lr = lr;
+  const int gl = grid_for(n, 4 * 4), gh = grid_for(n / 32 * num_slices(dim), 4);
+  const int gc = grid_for(n / 256 * num_slices(dim), 4);
+  j.light_blocks = gl < 4096 ? gl : 4096;
+  j.heavy_blocks = gh < 2048 ? gh : 2048;
+  j.comb_blocks = gc < 1024 ? gc : 1024;
+  return j;
 }
 
+// Two launches for up to kMaxSgdJobs updates of one dim and mode: heavy blocks
+// of every job, then light blocks of every job; then the combine of every job.
 template <bool L2>
-void sgd_dispatch(float *table, const float *g, SegWork<uint32_t> &w, int cur, float lr, int64_t dim, float *partial,
-                  hipStream_t s) {
-  const int64_t nc = (dim / 4 + kWave - 1) / kWave;
-  if (nc == 1) sgd_launch<1, L2>(table, g, w, cur, lr, dim, partial, s);
-  else if (nc == 2) sgd_launch<2, L2>(table, g, w, cur, lr, dim, partial, s);
-  else sgd_launch<4, L2>(table, g, w, cur, lr, dim, partial, s);
+void sgd_launch(SgdJobs &js, hipStream_t s) {
+  int next = 0;
+  for (int i = 0; i < js.count; ++i) {
+    js.job[i].heavy_begin = next;
+    next += js.job[i].heavy_blocks;
+  }
+  for (int i = 0; i < js.count; ++i) {
+    js.job[i].light_begin = next;
+    next += js.job[i].light_blocks;
+  }
+  int comb = 0;
+  for (int i = 0; i < js.count; ++i) {
+    js.job[i].comb_begin = comb;
+    comb += js.job[i].comb_blocks;
+  }
+  if (next == 0) return;
+  const int64_t nc = (js.D / 4 + kWave - 1) / kWave;
+  if (nc == 1) sgd_apply_kernel<1, L2><<<next, kThreads, 0, s>>>(js);
+  else if (nc == 2) sgd_apply_kernel<2, L2><<<next, kThreads, 0, s>>>(js);
+  else sgd_apply_kernel<4, L2><<<next, kThreads, 0, s>>>(js);
+  if (comb > 0) sgd_combine_kernel<<<comb, kThreads, 0, s>>>(js);
 }
 
 }  // namespace
@@ -448,13 +522,12 @@ void wb_apply(float *table, int64_t num_rows, int64_t dim, const float *src, int
     else lw_apply<4><<<ga, kThreads, 0, stream>>>(t4, s4, fresh, w, v4);
     return;
   }
-  SegWork<uint32_t> w;
-  Carver c(ws);
-  c.off = segwork_layout<uint32_t>(n, &w, ws);
-  float *partial = reinterpret_cast<float *>(c.take<float4>(sgd_partial_elems(n, dim)));
-  const int cur = sorted_buffer(num_rows);
-  if (mode == HLR_WB_L2_ALIGN) sgd_dispatch<true>(table, src, w, cur, lr, dim, partial, stream);
-  else sgd_dispatch<false>(table, src, w, cur, lr, dim, partial, stream);
+  SgdJobs js{};
+  js.count = 1;
+  js.D = dim;
+  js.job[0] = sgd_job(table, src, n, dim, lr, ws, num_rows);
+  if (mode == HLR_WB_L2_ALIGN) sgd_launch<true>(js, stream);
+  else sgd_launch<false>(js, stream);
 }
 
 }  // namespace
@@ -512,6 +585,42 @@ hlr_status hlr::writeback_apply_last_fresh(float *table, int64_t num_rows, int64
   if ((st = ws_check(ws, ws_bytes, writeback_rows_workspace_size(num_rows, dim, n, HLR_WB_LAST_WINS))) != HLR_OK)
     return st;
   wb_apply(table, num_rows, dim, src, n, HLR_WB_LAST_WINS, 1.0f, ws, stream, hit);
+  return launch_status();
+}
+
+extern "C" hlr_status writeback_apply_batch(int32_t count, const hlr_wb_apply *updates, int32_t mode,
+                                            hipStream_t stream) {
+  if (count < 0 || count > kMaxSgdJobs || (count > 0 && !updates)) return HLR_INVALID_ARG;
+  if (mode != HLR_WB_SGD_SUM && mode != HLR_WB_L2_ALIGN) return HLR_INVALID_ARG;
+  SgdJobs js{};
+  js.D = 0;
+  for (int32_t i = 0; i < count; ++i) {
+    const hlr_wb_apply &u = updates[i];
+    hlr_status st = wb_args(u.num_rows, u.n, mode);
+    if (st != HLR_OK) return st;
+    if (u.dim <= 0 || u.dim % 4 != 0 || u.dim > 1024) return HLR_UNSUPPORTED_DIM;
+    if (u.n == 0 || u.num_rows == 0) continue;
+    if (!u.table || !u.src) return HLR_INVALID_ARG;
+    if (!aligned(u.table, 16) || !aligned(u.src, 16)) return HLR_MISALIGNED;
+    const size_t wb = writeback_rows_workspace_size(u.num_rows, u.dim, u.n, mode);
+    if ((st = ws_check(u.ws, u.ws_bytes, wb)) != HLR_OK) return st;
+    if (js.D != 0 && u.dim != js.D) return HLR_INVALID_ARG;  // one dim per launch
+    js.D = u.dim;
+    const size_t tb = static_cast<size_t>(u.num_rows) * static_cast<size_t>(u.dim) * sizeof(float);
+    for (int32_t k = 0; k < i; ++k) {  // the updates run at once: no shared table or workspace
+      const hlr_wb_apply &v = updates[k];
+      if (v.n == 0 || v.num_rows == 0) continue;
+      const size_t vb = static_cast<size_t>(v.num_rows) * static_cast<size_t>(v.dim) * sizeof(float);
+      const char *ut = reinterpret_cast<const char *>(u.table), *vt = reinterpret_cast<const char *>(v.table);
+      const char *uw = static_cast<const char *>(u.ws), *vw = static_cast<const char *>(v.ws);
+      const size_t vwb = writeback_rows_workspace_size(v.num_rows, v.dim, v.n, mode);
+      if ((ut < vt + vb && vt < ut + tb) || (uw < vw + vwb && vw < uw + wb)) return HLR_INVALID_ARG;
+    }
+    js.job[js.count++] = sgd_job(u.table, u.src, u.n, u.dim, u.lr, u.ws, u.num_rows);
+  }
+  if (js.count == 0) return HLR_OK;
+  if (mode == HLR_WB_L2_ALIGN) sgd_launch<true>(js, stream);
+  else sgd_launch<false>(js, stream);
   return launch_status();
 }
 

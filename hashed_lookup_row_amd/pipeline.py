@@ -255,16 +255,42 @@ class HashedTablesPipeline:
 
     lookup stream:  hashed_rows -> writeback_plan(SGD_SUM), table by table
     compute stream: gather_rows -> writeback_apply(SGD_SUM, lr), table by table
-    One ring per table, so a table's next batch may plan while other tables apply."""
+    With batch=False there is one ring per table, so a table's next batch may plan while other
+    tables apply.  With batch=True (the default; distinct tables of one dim) the tables go in groups
+    of `group` (at most eight), one ring per group: the lookup stream makes the group's rows, then
+    its plans; the compute stream waits once for the rows, gathers table by table, waits once for
+    the plans and applies the whole group in one writeback_apply_batch call (two kernel launches per
+    group instead of two per table; the duplicate runs of the group's tables overlap).  mark is then
+    called with ("apply", -1 - group index, 0 | 1).  Groups of four suit the 8 tables of [DLRM]:
+    with all eight in one group the plan chains (many small kernels) wait behind the long gathers
+    and applies of the group before."""
 
-    def __init__(self, tables, n, depth=2):
+    def __init__(self, tables, n, depth=2, batch=True, group=4):
         self.tables, self.n = tables, n
         dev = tables[0].device
+        self.batch = (bool(batch) and len({id(t) for t in tables}) == len(tables) and
+                      len({t.shape[1] for t in tables}) == 1)
+        g = max(1, min(int(group), 8)) if self.batch else 1
+        self.groups = [list(range(i, min(i + g, len(tables)))) for i in range(0, len(tables), g)]
         first = _Ring(dev, depth, points=2)
-        self.rings = [first] + [_Ring(dev, depth, points=2, lookup=first.lookup) for _ in tables[1:]]
+        self.rings = [first] + [_Ring(dev, depth, points=2, lookup=first.lookup) for _ in
+                                range((len(self.groups) if self.batch else len(tables)) - 1)]
         self._rows = [[torch.empty(n, dtype=torch.int64, device=dev) for _ in range(depth)] for _ in tables]
         self._ws = [[new_workspace(dev, writeback_workspace_size(t.shape[0], t.shape[1], n, WB_SGD_SUM))
                      for _ in range(depth)] for t in tables]
+        if self.batch:
+            from . import _WbApply
+            self._lib = load_library()
+            self._arr = [[(_WbApply * len(grp))() for _ in range(depth)] for grp in self.groups]
+            for gi, grp in enumerate(self.groups):
+                for k, arr in enumerate(self._arr[gi]):
+                    for j, i in enumerate(grp):
+                        t = tables[i]
+                        _dev(t, "table", torch.float32)
+                        need = self._lib.writeback_rows_workspace_size(t.shape[0], t.shape[1], n, WB_SGD_SUM)
+                        w, wb = _own_ws(self._ws[i][k], need)
+                        arr[j].table, arr[j].num_rows, arr[j].dim = t.data_ptr(), t.shape[0], t.shape[1]
+                        arr[j].ws, arr[j].ws_bytes = w.value, wb
 
     def restart(self):
         for r in self.rings:
@@ -278,6 +304,8 @@ class HashedTablesPipeline:
         mark: optional callable, called on the compute stream with ("gather" | "apply", table, 0 | 1)
         just before (0) and after (1) each gather and apply is enqueued."""
         mark = mark if mark is not None else (lambda tag: None)
+        if self.batch:
+            return self._step_batch(keys, grads, lr, outs, mark)
         ks = []
         for i, t in enumerate(self.tables):
             r = self.rings[i]
@@ -299,6 +327,44 @@ class HashedTablesPipeline:
             mark(("apply", i, 0))
             writeback_apply(t, grads[i], self._ws[i][k], WB_SGD_SUM, lr, stream=r.cs)
             mark(("apply", i, 1))
+            r.end_compute(k)
+        return res
+
+    def _step_batch(self, keys, grads, lr, outs, mark):
+        ks = []
+        for gi, grp in enumerate(self.groups):
+            r = self.rings[gi]
+            k = r.begin_lookup()
+            for i in grp:
+                _on(r.lookup, keys[i])
+                hashed_rows(keys[i], self.tables[i].shape[0], out=self._rows[i][k], stream=r.ls)
+            r.mark(k, 0)
+            for i in grp:
+                writeback_plan(self.tables[i].shape[0], self._rows[i][k], self._ws[i][k], WB_SGD_SUM, stream=r.ls)
+            r.mark(k, 1)
+            ks.append(k)
+        res = []
+        for gi, grp in enumerate(self.groups):
+            r, k = self.rings[gi], ks[gi]
+            r.wait(k, 0)
+            for i in grp:
+                mark(("gather", i, 0))
+                res.append(gather_rows(self.tables[i], self._rows[i][k], None if outs is None else outs[i],
+                                       stream=r.cs))
+                mark(("gather", i, 1))
+            arr = self._arr[gi][k]
+            for j, i in enumerate(grp):
+                g = grads[i]
+                _dev(g, "grads", torch.float32)
+                if g.numel() != self.n * self.tables[i].shape[1]:
+                    raise ValueError(f"grads[{i}] must hold n x dim values")
+                arr[j].src, arr[j].n, arr[j].lr = g.data_ptr(), self.n, float(lr)
+            r.wait(k, 1)
+            mark(("apply", -1 - gi, 0))
+            rc = self._lib.writeback_apply_batch(len(grp), ctypes.cast(arr, ctypes.c_void_p), WB_SGD_SUM, r.cs)
+            if rc != 0:
+                _check(rc, "writeback_apply_batch")
+            mark(("apply", -1 - gi, 1))
             r.end_compute(k)
         return res
 

@@ -186,6 +186,30 @@ hlr_status writeback_plan(int64_t num_rows, const int64_t *rows, int64_t n, int3
 hlr_status writeback_apply(float *table, int64_t num_rows, int64_t dim, const float *src, int64_t n,
                            int32_t mode, float lr, void *ws, size_t ws_bytes, hipStream_t stream);
 
+/* Several independent SGD_SUM or L2_ALIGN updates applied by one launch (the
+ * hashed tables of [DLRM] take one update per table per step).  Each update
+ * is writeback_apply(table, num_rows, dim, src, n, mode, lr, ws, ws_bytes)
+ * with its plan in ws (writeback_plan with the same mode); the results equal
+ * those calls made one after another.  The duplicate runs of all updates
+ * start together and their other rows stream beside them (two kernel
+ * launches for the whole batch).
+ *  count in [0, 8]; updates[count] is a host array; mode HLR_WB_SGD_SUM or
+ *  HLR_WB_L2_ALIGN for all.  Every update must have the same dim; tables and
+ *  workspaces must not overlap between updates (HLR_INVALID_ARG).  Updates
+ *  with n == 0 or num_rows == 0 are skipped.  Other errors as
+ *  writeback_apply, checked for every update before anything is enqueued. */
+typedef struct {
+  float *table;
+  int64_t num_rows;
+  int64_t dim;
+  const float *src;
+  int64_t n;
+  float lr;
+  void *ws;
+  size_t ws_bytes;
+} hlr_wb_apply;
+hlr_status writeback_apply_batch(int32_t count, const hlr_wb_apply *updates, int32_t mode, hipStream_t stream);
+
 /* The distinct rows a LAST_WINS plan covers (the rows the batch writes), for
  * publishing them after the apply (Raw Embedding Streaming, [ML] sec. 2).
  *  ws: a workspace holding a writeback_plan(..., HLR_WB_LAST_WINS) for the

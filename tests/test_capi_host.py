@@ -156,6 +156,39 @@ def test_ema_apply_batch_argument_errors(lib):
     assert lib.ema_update_apply_batch(0, None, s) == OK
 
 
+def test_wb_apply_batch_argument_errors(lib):
+    """Every host-checkable fault of the batched SGD apply returns before anything is enqueued."""
+    class Up(ctypes.Structure):
+        _fields_ = [("table", ctypes.c_void_p), ("num_rows", ctypes.c_int64), ("dim", ctypes.c_int64),
+                    ("src", ctypes.c_void_p), ("n", ctypes.c_int64), ("lr", ctypes.c_float),
+                    ("ws", ctypes.c_void_p), ("ws_bytes", ctypes.c_size_t)]
+    s, SGD, L2 = None, 1, 2
+    need = lib.writeback_rows_workspace_size(100, 8, 10, SGD)
+    base = 1 << 30  # stand-in addresses, far apart (never dereferenced)
+
+    def up(k, dim=8, table=None, ws=None, wsb=need, n=10, num_rows=100):
+        return Up(table if table is not None else base + k * (1 << 24), num_rows, dim, base + (1 << 28) + k * (1 << 24),
+                  n, 0.5, ws if ws is not None else base + (1 << 29) + k * (1 << 24), wsb)
+
+    def call(*ups, count=None, mode=SGD):
+        arr = (Up * max(1, len(ups)))(*ups)
+        return lib.writeback_apply_batch(len(ups) if count is None else count, ctypes.cast(arr, ctypes.c_void_p),
+                                         mode, s)
+    assert call(*[up(k) for k in range(9)]) == INVALID                   # at most eight
+    assert call(up(0), count=-1) == INVALID
+    assert lib.writeback_apply_batch(2, None, SGD, s) == INVALID
+    assert call(up(0), mode=0) == INVALID                                 # LAST_WINS has no batch
+    assert call(up(0), up(1, dim=16, wsb=lib.writeback_rows_workspace_size(100, 16, 10, SGD))) == INVALID
+    assert call(up(0), up(1, table=base)) == INVALID                      # same table
+    assert call(up(0), up(1, ws=base + (1 << 29))) == INVALID             # same workspace
+    assert call(up(0), up(1, dim=6)) == DIM
+    assert call(up(0), up(1, wsb=need - 1)) == WS_SMALL
+    assert call(up(0, n=-1)) == INVALID
+    assert call(up(0, table=base + 4)) == MISALIGNED
+    assert call(up(0, n=0), up(1, num_rows=0), mode=L2) == OK             # nothing to do
+    assert lib.writeback_apply_batch(0, None, SGD, s) == OK
+
+
 def test_ema_plan_subset_argument_errors(lib):
     s = None
     need = lib.ema_update_rows_workspace_size(100, 4, 10)

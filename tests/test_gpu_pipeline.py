@@ -139,6 +139,34 @@ def test_ema_apply_batch(dev):
         assert bits_equal(to_np(t), w)
 
 
+@pytest.mark.parametrize("mode", ["sgd", "l2"])
+def test_wb_apply_batch(dev, mode):
+    """Eight SGD_SUM (or L2_ALIGN) updates of different tables in one batch (multi-run rows, a tiny
+    table, an empty update, different row counts and learning rates) equal the oracle applied to each
+    in turn."""
+    g = np.random.default_rng(29 if mode == "sgd" else 31)
+    D = 64
+    m = hlr.WB_SGD_SUM if mode == "sgd" else hlr.WB_L2_ALIGN
+    specs = [(300, 1.1, 30_000), (5000, 1.05, 20_000), (2, 1.0, 3000), (900, 1.2, 0), (60_000, 1.2, 50_000),
+             (40, 1.1, 777), (300, 1.3, 9000), (10_000, 1.15, 4096)]
+    ups, want = [], []
+    for k, (num_rows, z, n) in enumerate(specs):
+        rows = np.minimum(synth.zipf_ranks(g, num_rows, z, n), num_rows - 1).astype(np.int64)
+        rows[g.random(n) < 0.01] = -1
+        src = (g.standard_normal((n, D)) * (1e-3 if mode == "sgd" else 1.0)).astype(np.float32)
+        table = (g.standard_normal((num_rows, D)) * 0.01).astype(np.float32)
+        lr = 0.01 * (k + 1)
+        t = torch.from_numpy(table).to(dev)
+        ws = hlr.new_workspace(dev, hlr.writeback_workspace_size(num_rows, D, n, m))
+        hlr.writeback_plan(num_rows, torch.from_numpy(rows).to(dev), ws, m)
+        ups.append((t, torch.from_numpy(src).to(dev), lr, ws))
+        (oracle.sgd_sum if mode == "sgd" else oracle.l2_align)(table, rows, src, np.float32(lr))
+        want.append(table)
+    hlr.writeback_apply_batch(ups, mode=m)
+    for k, ((t, *_), w) in enumerate(zip(ups, want)):
+        assert bits_equal(to_np(t), w), k
+
+
 def prefilled_pair(dev, cfg):
     C, P, D = cfg.capacity, cfg.probes, cfg.dim
     identity = torch.full((C,), -1, dtype=torch.int64, device=dev)
@@ -228,7 +256,8 @@ def test_prefetch_limits(dev):
     assert int((identity >= 0).sum().item()) == 2 * n
 
 
-def test_hashed_tables_pipeline(dev):
+@pytest.mark.parametrize("batch,group", [(True, 8), (True, 2), (False, 8)])
+def test_hashed_tables_pipeline(dev, batch, group):
     g = np.random.default_rng(11)
     sizes, n, D, lr, steps = [5000, 700, 3000], 6000, 128, 0.01, 4
     tables_np = [(g.standard_normal((m, D)) * 0.01).astype(np.float32) for m in sizes]
@@ -239,7 +268,8 @@ def test_hashed_tables_pipeline(dev):
     keys = [[torch.from_numpy(k).to(dev) for k in ks] for ks in keys_np]
     grads = [[torch.from_numpy(x).to(dev) for x in gs] for gs in grads_np]
     torch.cuda.synchronize()
-    pipe = pipeline.HashedTablesPipeline(tables, n)
+    pipe = pipeline.HashedTablesPipeline(tables, n, batch=batch, group=group)
+    assert pipe.batch == batch
     outs = [pipe.step(keys[s], grads[s], lr) for s in range(steps)]
     for s in range(steps):
         for i, m in enumerate(sizes):
