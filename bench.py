@@ -548,7 +548,7 @@ def run_dlrm(args):
                                       "two streams: hashed rows + SGD plan (sort) on a lookup stream beside gather + "
                                       "SGD apply on the compute stream, table by table")},
           (_roof(f"writeback_apply_batch SGD_SUM, {len(pipe.groups[0])} tables per launch (sgd_apply_kernel + "
-                 "sgd_combine_kernel; achieved over all 8 tables)", s_bytes, s_time)
+                 "sgd_combine_kernel)", s_bytes / len(pipe.groups), s_time / len(pipe.groups))
            if pipe.batch else
            _roof("writeback_apply SGD_SUM (sgd_apply_kernel + sgd_combine_kernel)", s_bytes / 8, s_time / 8)),
           {"dtype": "fp32", "distinct_rows_per_table": us,
