@@ -139,13 +139,12 @@ def test_ema_apply_batch(dev):
         assert bits_equal(to_np(t), w)
 
 
-@pytest.mark.parametrize("mode", ["sgd", "l2"])
-def test_wb_apply_batch(dev, mode):
+@pytest.mark.parametrize("mode,D", [("sgd", 64), ("l2", 64), ("sgd", 512), ("l2", 1024), ("sgd", 4)])
+def test_wb_apply_batch(dev, mode, D):
     """Eight SGD_SUM (or L2_ALIGN) updates of different tables in one batch (multi-run rows, a tiny
     table, an empty update, different row counts and learning rates) equal the oracle applied to each
     in turn."""
-    g = np.random.default_rng(29 if mode == "sgd" else 31)
-    D = 64
+    g = np.random.default_rng((29 if mode == "sgd" else 31) + D)
     m = hlr.WB_SGD_SUM if mode == "sgd" else hlr.WB_L2_ALIGN
     specs = [(300, 1.1, 30_000), (5000, 1.05, 20_000), (2, 1.0, 3000), (900, 1.2, 0), (60_000, 1.2, 50_000),
              (40, 1.1, 777), (300, 1.3, 9000), (10_000, 1.15, 4096)]
