@@ -4,7 +4,7 @@
 // position is), so sorting by the pair itself gives exactly the stable order;
 // no pass has to preserve input order.
 //
-//   tile_sort_kernel    a block sorts a tile of 4096 or 16384 pairs (16 per
+//   tile_sort_kernel    a block sorts a tile of 2048 or 16384 pairs (16 per
 //                       thread in registers, then merge levels through LDS),
 //                       so runs of a tile are sorted;
 //   merge_round_kernel  runs of L are merged pairwise into runs of 2L.  A
@@ -15,7 +15,11 @@
 //                       search, each round one load per lane, so a run of
 //                       2^17 takes three dependent loads, not seventeen; the
 //                       block then stages both input pieces in LDS and each
-//                       thread merges kMsOut / 256 outputs.
+//                       thread merges kMsOut / 256 outputs.  Small output
+//                       blocks (256) put many blocks on the GPU per round:
+//                       a round is latency-bound (three dependent searches,
+//                       then the staging), so more, shorter blocks finish it
+//                       sooner.
 //
 // With a device count of active elements (a compacted input), only the first
 // *nact slots take part: tiles and output blocks past it exit at once, so a
@@ -29,15 +33,15 @@
 namespace {
 
 constexpr int kMsThreads = 256;  // merge rounds
-constexpr int kMsOut = 2048;     // outputs per block in a merge round (8 per thread)
+constexpr int kMsOut = 256;      // outputs per block in a merge round (one per thread)
 
 // Tile sort: 16 pairs per thread; 1024 threads (16384 pairs) for 32-bit keys,
-// 256 (4096 pairs) for 64-bit keys.  For a 65,536-ID dedup, 16 tiles and four
-// merge rounds take 81.8 us against 86.2 us with 8 tiles of 8192 and three
-// rounds (more blocks sort at once; each merge round costs about 10 us) and
-// 84.0 us with 32 tiles of 2048 and five rounds.
+// 128 (2048 pairs) for 64-bit keys.  A 65,536-ID dedup (32 tiles, five merge
+// rounds of 256-output blocks) takes 64.6 us; with tiles of 8192 pairs and
+// 2048-output blocks (three rounds of 32 blocks) it took 86.2 us, with tiles
+// of 4096 and 256-output blocks 65.4 us, 512-output blocks 67.2 us.
 template <typename K>
-constexpr int ms_tile_threads() { return sizeof(K) == 4 ? 1024 : 256; }
+constexpr int ms_tile_threads() { return sizeof(K) == 4 ? 1024 : 128; }
 template <typename K>
 constexpr int64_t ms_tile() { return static_cast<int64_t>(ms_tile_threads<K>()) * 16; }
 constexpr int kMsResultBuffer = 1;
