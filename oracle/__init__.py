@@ -27,7 +27,6 @@ _lock = threading.Lock()
 _lib = None
 
 OK, EINVAL, ENOMEM, ESTAMP = 0, 1, 2, 3
-SUM_RUN = 256  # run length of the duplicate-gradient sum (see oracle.c)
 
 
 def build(force: bool = True) -> str:
@@ -178,6 +177,7 @@ def writeback_last(table, rows, e):
 
 
 def sgd_sum(table, rows, g, lr):
+    """Per row: s = one fp32 running sum of its gradients in batch order; M <- fl(M - fl(lr*s))."""
     assert table.dtype == np.float32 and table.flags.c_contiguous
     rows = _c(rows, np.int64)
     g = _c(g, np.float32)

@@ -42,8 +42,8 @@
  *    occurrence of the ID that replaced them;
  *  - dedup keeps the last occurrence, unique keys ascending;
  *  - Writeback arithmetic is fp32: M' = fl(M - fl(M - e));
- *  - duplicate gradients are summed in batch order inside runs of 256
- *    consecutive occurrences, run totals added in batch order, then
+ *  - duplicate gradients of a row are summed as one fp32 running sum in
+ *    ascending batch position, starting from the first gradient, then
  *    M' = fl(M - fl(lr * s));
  *  - EMA arithmetic is fp32 per step: T' = fl(fl(a*T) + fl(b*v)), positions in
  *    batch order;
@@ -61,7 +61,6 @@
 #define ORC_ESTAMP 3
 
 #define ORC_EMPTY (-1)
-#define ORC_SUM_RUN 256
 
 /* [SM64] finaliser. */
 uint64_t orc_mix64(uint64_t z) {
@@ -252,9 +251,11 @@ int orc_writeback_last(float *table, int64_t num_rows, int64_t dim, const int64_
 
 /* --------------------------------------------- SGD with summed duplicates */
 /*
- * Duplicate gradients of a row are summed, then applied once:
- * s = (sum over the row's positions in batch order, in runs of 256 consecutive
- * occurrences; the run totals are added in batch order), M[r] = fl(M[r] - fl(lr*s)).
+ * Duplicate gradients of a row are summed, then applied once ([DLRM] hashed
+ * tables take a per-row SGD step; [ML] sec. 2 deduplicates a batch so a row is
+ * written once).  For each element the sum is one fp32 running sum over the
+ * row's positions in ascending batch order, starting from the first gradient
+ * (s = g[p1], then s = fl(s + g[pk])); then M[r] = fl(M[r] - fl(lr*s)).
  */
 int orc_sgd_sum(float *table, int64_t num_rows, int64_t dim, const int64_t *rows, const float *g, int64_t n,
                 float lr) {
@@ -268,13 +269,8 @@ int orc_sgd_sum(float *table, int64_t num_rows, int64_t dim, const int64_t *rows
         while (k1 < m && p[k1].key == p[k0].key) k1++;
         float *w = table + p[k0].key * dim;
         for (int64_t d = 0; d < dim; ++d) {
-            float s = 0.0f;
-            for (int64_t r0 = k0; r0 < k1; r0 += ORC_SUM_RUN) {
-                const int64_t r1 = r0 + ORC_SUM_RUN < k1 ? r0 + ORC_SUM_RUN : k1;
-                float run = g[p[r0].pos * dim + d];
-                for (int64_t k = r0 + 1; k < r1; ++k) run = run + g[p[k].pos * dim + d];
-                s = (r0 == k0) ? run : s + run;
-            }
+            float s = g[p[k0].pos * dim + d];
+            for (int64_t k = k0 + 1; k < k1; ++k) s = s + g[p[k].pos * dim + d];
             const float step = lr * s;
             w[d] = w[d] - step;
         }
@@ -362,9 +358,9 @@ int orc_dks_step(int64_t *keys, int64_t *krows, int64_t key_cap, int64_t *stamps
  * it: learn the cache row by SGD on the squared distance ||M[r] - sg(e_i)||^2.
  * Each occurrence i of row r contributes the gradient 2 (M[r] - e_i), taken at
  * the row's value before the batch: g_i = fl(2 * fl(M[r] - e_i)) (the doubling
- * is exact).  A row's gradients are summed as in orc_sgd_sum (runs of
- * ORC_SUM_RUN consecutive occurrences in batch order, run totals in order) and
- * applied once: M[r] = fl(M[r] - fl(lr * s)).
+ * is exact).  A row's gradients are summed as in orc_sgd_sum (one running sum
+ * in ascending batch order, from the first) and applied once:
+ * M[r] = fl(M[r] - fl(lr * s)).
  */
 int orc_l2_align(float *table, int64_t num_rows, int64_t dim, const int64_t *rows, const float *e, int64_t n,
                  float lr) {
@@ -379,16 +375,11 @@ int orc_l2_align(float *table, int64_t num_rows, int64_t dim, const int64_t *row
         float *w = table + p[k0].key * dim;
         for (int64_t d = 0; d < dim; ++d) {
             const float before = w[d];
-            float s = 0.0f;
-            for (int64_t r0 = k0; r0 < k1; r0 += ORC_SUM_RUN) {
-                const int64_t r1 = r0 + ORC_SUM_RUN < k1 ? r0 + ORC_SUM_RUN : k1;
-                float diff = before - e[p[r0].pos * dim + d];
-                float run = 2.0f * diff;
-                for (int64_t k = r0 + 1; k < r1; ++k) {
-                    diff = before - e[p[k].pos * dim + d];
-                    run = run + 2.0f * diff;
-                }
-                s = (r0 == k0) ? run : s + run;
+            float diff = before - e[p[k0].pos * dim + d];
+            float s = 2.0f * diff;
+            for (int64_t k = k0 + 1; k < k1; ++k) {
+                diff = before - e[p[k].pos * dim + d];
+                s = s + 2.0f * diff;
             }
             const float step = lr * s;
             w[d] = before - step;

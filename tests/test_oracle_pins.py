@@ -37,16 +37,33 @@ def test_mix64_matches_published_splitmix64_outputs():
     assert got == want
 
 
-def test_bucket_is_hash_mod_bucket_count_on_twos_complement_bits():
-    for x in [0, 1, -1, -2, 123456789, -(1 << 63), (1 << 63) - 1]:
-        for nb in [1, 7, 512, 524288]:
-            assert oracle.bucket(x, nb) == oracle.mix64(x & 0xFFFFFFFFFFFFFFFF) % nb
+def _golden_splitmix64():
+    """(state, output) pairs of the published SplitMix64 sequence for seed 0: state k = k * gamma mod 2^64."""
+    want = [int(l.split()[0], 16) for l in open(os.path.join(GOLDEN, "splitmix64_seed0.txt")) if l.startswith("0x")]
+    gamma = 0x9E3779B97F4A7C15
+    return [((k + 1) * gamma) & 0xFFFFFFFFFFFFFFFF for k in range(len(want))], want
 
 
-def test_hashed_rows_is_hash_mod_rows():
-    ids = np.array([0, 5, -7, 1 << 40, -(1 << 62)], np.int64)
-    rows = oracle.hashed_rows(ids, 25_165_824)
-    assert rows.tolist() == [oracle.mix64(int(x) & 0xFFFFFFFFFFFFFFFF) % 25_165_824 for x in ids]
+def _as_i64(u):
+    return u - (1 << 64) if u >= (1 << 63) else u
+
+
+def test_bucket_of_published_states_is_published_output_mod_bucket_count():
+    """bucket(x, nb) reduces the published hash of x's two's-complement bits: for the SplitMix64 states
+    (most of them negative as int64) the bucket is the published output mod nb, for power-of-two and
+    other bucket counts."""
+    states, outs = _golden_splitmix64()
+    for x, h in zip(states, outs):
+        for nb in [1, 2, 512, 1 << 19, 7, 524_287, 25_165_824 // 8]:
+            assert oracle.bucket(_as_i64(x), nb) == h % nb, (hex(x), nb)
+
+
+def test_hashed_rows_of_published_states_is_published_output_mod_rows():
+    states, outs = _golden_splitmix64()
+    ids = np.array([_as_i64(x) for x in states], np.int64)
+    for num_rows in [1, 4 << 20, 25_165_824, 5 << 20, 1_000_003]:
+        rows = oracle.hashed_rows(ids, num_rows)
+        assert rows.tolist() == [h % num_rows for h in outs], num_rows
 
 
 # ------------------------------------------------------------ textbook LRU
@@ -304,11 +321,16 @@ def _exact_update(w, gs, lr):
     return Fraction(float(w)) - Fraction(float(lr)) * sum(Fraction(float(x)) for x in gs)
 
 
-def test_sgd_sum_short_segments_equal_sequential_cumsum():
+def test_sgd_sum_every_segment_length_equals_sequential_cumsum():
+    """Each row's sum is numpy's float32 cumsum (np.add.accumulate: strictly sequential) over the row's
+    gradients in batch order, for segments of every length from 1 to a few thousand."""
     g = np.random.default_rng(9)
-    C, D, n = 50, 8, 3000
+    C, D = 60, 8
+    lens = np.concatenate([np.arange(1, 41), [63, 64, 65, 255, 256, 257, 511, 512, 513, 1000, 2049, 4100]])
+    rows = np.concatenate([np.full(k, r, np.int64) for r, k in enumerate(lens)] + [np.full(50, -1, np.int64)])
+    g.shuffle(rows)
+    n = rows.size
     table = g.standard_normal((C, D)).astype(np.float32)
-    rows = g.integers(-1, C, size=n)
     grads = (g.standard_normal((n, D)) * 1e-3).astype(np.float32)
     before = table.copy()
     oracle.sgd_sum(table, rows, grads, 0.01)
@@ -317,26 +339,39 @@ def test_sgd_sum_short_segments_equal_sequential_cumsum():
         if pos.size == 0:
             assert np.array_equal(table[r], before[r])
             continue
-        assert pos.size <= oracle.SUM_RUN
-        s = np.cumsum(grads[pos], axis=0, dtype=np.float32)[-1]  # numpy cumsum: strictly sequential
+        assert pos.size == lens[r]
+        s = np.cumsum(grads[pos], axis=0, dtype=np.float32)[-1]
         want = before[r] - (np.float32(0.01) * s).astype(np.float32)
-        assert np.array_equal(table[r], want.astype(np.float32))
+        assert np.array_equal(table[r], want.astype(np.float32)), r
 
 
-def test_sgd_sum_long_segment_runs_of_256_and_exact_bound():
+def test_sgd_sum_long_segment_within_exact_bound():
+    """The running sum of k terms is within (k-1) 2^-24 sum|g| of the exact rational sum, and the update
+    adds two more roundings."""
     g = np.random.default_rng(11)
-    D, k = 4, 1000
+    D, k = 4, 3000
     rows = np.zeros(k, np.int64)
     grads = (g.standard_normal((k, D)) * 1e-3).astype(np.float32)
     table = np.ones((1, D), np.float32)
     oracle.sgd_sum(table, rows, grads, 1.0)
-    runs = [np.cumsum(grads[i:i + 256], axis=0, dtype=np.float32)[-1] for i in range(0, k, 256)]
-    s = np.cumsum(np.stack(runs), axis=0, dtype=np.float32)[-1]
-    assert np.array_equal(table[0], (np.float32(1.0) - s).astype(np.float32))
     for d in range(D):
         exact = _exact_update(1.0, grads[:, d], 1.0)
         err_bound = Fraction(k + 2) * Fraction(U32) * (sum(abs(Fraction(float(x))) for x in grads[:, d]) + 1)
         assert abs(Fraction(float(table[0, d])) - exact) <= err_bound
+
+
+def test_sgd_sum_order_is_ascending_batch_position():
+    """Three gradients whose fp32 sum depends on the order: 1 + 2^-24 + 2^-24 rounds to 1 left to right
+    (each tiny term is lost) but to 1 + 2^-23 when the tiny terms come first.  The row's result tells the
+    order: batch order must give exactly M - 1."""
+    tiny = np.float32(2.0 ** -24)
+    grads = np.array([[1.0], [tiny], [tiny]], np.float32)
+    t = np.zeros((1, 1), np.float32)
+    oracle.sgd_sum(t, np.zeros(3, np.int64), grads, 1.0)
+    assert t[0, 0] == np.float32(-1.0)
+    t = np.zeros((1, 1), np.float32)
+    oracle.sgd_sum(t, np.zeros(3, np.int64), grads[::-1].copy(), 1.0)
+    assert t[0, 0] == -(np.float32(1.0) + np.float32(2.0 ** -23))
 
 
 def test_sgd_sum_integer_gradients_are_exact():
@@ -433,7 +468,7 @@ def test_l2_align_duplicates_exact_on_short_dyadics():
     g = np.random.default_rng(22)
     C, D, n = 6, 4, 900
     rows = g.integers(-1, C, size=n).astype(np.int64)
-    rows[:300] = 2  # one row with 300+ occurrences: more than one run of 256
+    rows[:300] = 2  # one row with 300+ occurrences
     e = (g.integers(-64, 65, size=(n, D)) / 16.0).astype(np.float32)
     table = (g.integers(-64, 65, size=(C, D)) / 16.0).astype(np.float32)
     before = table.copy()
