@@ -89,8 +89,12 @@ def parse():
                     help="only run a plain 1 GiB device copy (reference for HBM counters)")
     ap.add_argument("--scale", type=float, default=1.0, help="shrink capacity/universe/batch (testing only)")
     ap.add_argument("--workload", default="memory-layer",
-                    choices=["memory-layer", "serving", "dlrm", "cs3", "dedup", "res", "keystore"],
+                    choices=["memory-layer", "serving", "dlrm", "cs3", "dedup", "res", "keystore", "hbm-ceiling"],
                     help="memory-layer (default, the headline) or one of the other rows' workloads")
+    ap.add_argument("--ceiling-gib", default="1,2,4,8",
+                    help="hbm-ceiling: buffer sizes in GiB (comma-separated)")
+    ap.add_argument("--ceiling-kinds", default="read,write,copy,read-nt,write-nt,copy-nt",
+                    help="hbm-ceiling: which sweeps to time")
     ap.add_argument("--op-events", action="store_true",
                     help="also time lookup and writeback separately (events between every call)")
     return ap.parse_args()
@@ -129,7 +133,7 @@ def main():
     sys.path.insert(0, ROOT)
     if args.workload != "memory-layer":
         {"serving": run_serving, "dlrm": run_dlrm, "cs3": run_cs3, "dedup": run_dedup,
-         "res": run_res, "keystore": run_keystore}[args.workload](args)
+         "res": run_res, "keystore": run_keystore, "hbm-ceiling": run_hbm_ceiling}[args.workload](args)
         return
     import hashed_lookup_row_amd as hlr
     import synth
@@ -547,10 +551,10 @@ def run_dlrm(args):
                                       "group's gathers, then one batched SGD apply for the group" if pipe.batch else
                                       "two streams: hashed rows + SGD plan (sort) on a lookup stream beside gather + "
                                       "SGD apply on the compute stream, table by table")},
-          (_roof(f"writeback_apply_batch SGD_SUM, {len(pipe.groups[0])} tables per launch (sgd_apply_kernel + "
-                 "sgd_combine_kernel)", s_bytes / len(pipe.groups), s_time / len(pipe.groups))
+          (_roof(f"writeback_apply_batch SGD_SUM, {len(pipe.groups[0])} tables per launch (sgd_apply_kernel)",
+                 s_bytes / len(pipe.groups), s_time / len(pipe.groups))
            if pipe.batch else
-           _roof("writeback_apply SGD_SUM (sgd_apply_kernel + sgd_combine_kernel)", s_bytes / 8, s_time / 8)),
+           _roof("writeback_apply SGD_SUM (sgd_apply_kernel)", s_bytes / 8, s_time / 8)),
           {"dtype": "fp32", "distinct_rows_per_table": us,
            "gather_roofline": _roof("gather_kernel<128>", g_bytes / 8, g_time / 8),
            "step_hbm_gbs": (g_bytes + s_bytes) / step_s / 1e9,
@@ -810,6 +814,57 @@ def run_dedup(args):
           float(np.median(t)) * 1e3, {"workload": "memory-layer ID stream", "ids": n},
           _roof("dedup_ids (radix sort + segments, all kernels)", nbytes, float(np.median(t))),
           {"dtype": "int64", "distinct": u})
+
+
+def run_hbm_ceiling(args):
+    """Measured HBM ceiling: hand-written read-only, write-only and copy sweeps (ordinary and non-temporal
+    accesses) over buffers of 1-8 GiB, each launch timed with HIP events on the stream it runs on."""
+    import ctypes
+    import statistics
+    import torch
+
+    lib = ctypes.CDLL(os.path.join(ROOT, "hashed_lookup_row_amd", "libhlr_bwprobe.so"))
+    lib.hlr_bwprobe.restype = ctypes.c_int
+    lib.hlr_bwprobe.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int64,
+                                ctypes.c_void_p, ctypes.c_void_p]
+    lib.hlr_bwprobe_sink_words.restype = ctypes.c_int64
+    lib.hlr_bwprobe_sink_words.argtypes = [ctypes.c_int64]
+    dev = torch.device("cuda:0")
+    timer, cur = HipTimer(), torch.cuda.current_stream(dev).cuda_stream
+    sizes = [int(float(x) * (1 << 30)) for x in args.ceiling_gib.split(",")]
+    kinds = args.ceiling_kinds.split(",")
+    big = max(sizes)
+    src = torch.empty(big // 4, dtype=torch.float32, device=dev).uniform_()
+    dst = torch.empty(big // 4, dtype=torch.float32, device=dev)
+    sink = torch.empty(lib.hlr_bwprobe_sink_words(big), dtype=torch.int32, device=dev)
+    torch.cuda.synchronize()
+    code = {"read": 0, "write": 1, "copy": 2}
+    reps = max(3, args.steps if args.steps < 50 else 10)
+    out = []
+    for nbytes in sizes:
+        for kind in kinds:
+            base, nt = kind.split("-")[0], kind.endswith("-nt")
+            evs = [(timer.event(), timer.event()) for _ in range(reps)]
+            for w in range(2):  # untimed warm-up launches
+                rc = lib.hlr_bwprobe(code[base], int(nt), src.data_ptr(), dst.data_ptr(), nbytes, sink.data_ptr(), cur)
+                if rc:
+                    raise RuntimeError(f"hlr_bwprobe failed ({rc})")
+            for a, b in evs:
+                timer.record(a, cur)
+                lib.hlr_bwprobe(code[base], int(nt), src.data_ptr(), dst.data_ptr(), nbytes, sink.data_ptr(), cur)
+                timer.record(b, cur)
+            torch.cuda.synchronize()
+            ts = [timer.elapsed_s(a, b) for a, b in evs]
+            moved = 2 * nbytes if base == "copy" else nbytes
+            rec = {"kind": kind, "gib": nbytes / (1 << 30), "bytes_moved": moved,
+                   "us_median": statistics.median(ts) * 1e6, "us_min": min(ts) * 1e6,
+                   "gbs_median": moved / statistics.median(ts) / 1e9, "gbs_best": moved / min(ts) / 1e9}
+            out.append(rec)
+            print(json.dumps(rec), flush=True)
+    best = {k: max(r["gbs_median"] for r in out if r["kind"] == k) for k in kinds}
+    print(json.dumps({"metric": "HBM ceiling of hand-written streaming kernels (median over launches)",
+                      "unit": "GB/s", "per_kind_best_median": best, "peak": HBM_PEAK_GBS,
+                      "reps": reps}), flush=True)
 
 
 if __name__ == "__main__":

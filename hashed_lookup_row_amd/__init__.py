@@ -23,7 +23,6 @@ STATUS = {0: "ok", 1: "invalid argument", 2: "unsupported dim", 3: "misaligned p
 WB_LAST_WINS = 0
 WB_SGD_SUM = 1
 WB_L2_ALIGN = 2
-SGD_SUM_RUN = 256
 EMPTY_ID = -1
 
 _lib = None

@@ -13,6 +13,8 @@
 // ceil(bits/8) passes.
 #pragma once
 
+#include <utility>
+
 #include "hlr_common.hpp"
 
 namespace {
@@ -22,6 +24,22 @@ constexpr int kMaxSortItems = 16;                      // elements per thread, a
 constexpr int kMaxDigitBits = 8;
 constexpr int kPosPad = 128;  // slack after the position buffers: batched reads may run past n
 constexpr int kMaxBins = 1 << kMaxDigitBits;           // one digit per thread in the offset scan
+
+// Segments long enough for whole-segment chains (kChainMin or more
+// occurrences) listed by length: bucket b holds lengths in
+// [2^(9+b), 2^(10+b)) (the last bucket also everything longer), in a region of
+// (n >> (9+b)) + 1 entries, since at most n / 2^(9+b) segments of n positions
+// can be that long.
+constexpr int kLenBuckets = 16;
+constexpr int kLenShift = 9;  // log2 of the shortest chained segment
+constexpr int kChainMin = 1 << kLenShift;
+constexpr int kTickets = 4 + kLenBuckets;
+__host__ __device__ __forceinline__ int64_t len_bucket_cap(int64_t n, int b) { return (n >> (kLenShift + b)) + 1; }
+__host__ __device__ __forceinline__ int64_t len_bucket_off(int64_t n, int b) {
+  int64_t o = 0;
+  for (int i = 0; i < b; ++i) o += len_bucket_cap(n, i);
+  return o;
+}
 
 // Elements per thread: tiles of 1024..4096 so that a sort runs about 128 tiles
 // (the passes are latency-bound at these sizes: against about 64 tiles, a
@@ -69,7 +87,7 @@ struct SegWork {
   K *k[2];
   uint32_t *v[2];
   uint32_t *counts;  // [kMaxBins * nblocks]
-  uint32_t *ticket;  // [4]
+  uint32_t *ticket;  // [kTickets]: heavy-run and combine list counts, then the length-bucket counts
   uint32_t *bcount;  // [nblocks]
   int32_t *segidx;   // [n]   segment of each sorted element (-1: excluded)
   int32_t *seg_start;  // [n]
@@ -79,6 +97,7 @@ struct SegWork {
   uint32_t *nact;      // [1]   elements that take part (sorted first); the rest of the n slots are unused
   int2 *hlist;         // heavy work units (segment, run), listed by the plan (list_heavy_units)
   int32_t *clist;      // segments with more than one run (combined after the heavy kernel)
+  int32_t *slist;      // heavy segments by length bucket, longest bucket first (list_heavy_segments)
   int64_t n;
   int nblocks;
   int items;  // elements per thread (tile = 256 * items)
@@ -98,7 +117,7 @@ inline size_t segwork_layout(int64_t n, SegWork<K> *w, void *base) {
   // per-tile tables sized for the smallest tile (a masked grouping sorts with 4 items per thread)
   const int64_t nb_max = (n + kSortThreads * 4 - 1) / (kSortThreads * 4);
   w->counts = c.take<uint32_t>(static_cast<size_t>(kMaxBins) * (nb_max > 0 ? nb_max : 1));
-  w->ticket = c.take<uint32_t>(4);
+  w->ticket = c.take<uint32_t>(kTickets);
   w->bcount = c.take<uint32_t>(2 * static_cast<size_t>(nb_max > 0 ? nb_max : 1));
   w->segidx = c.take<int32_t>(nn);
   w->seg_start = c.take<int32_t>(nn);
@@ -108,6 +127,7 @@ inline size_t segwork_layout(int64_t n, SegWork<K> *w, void *base) {
   w->nact = c.take<uint32_t>(1);
   w->hlist = c.take<int2>(nn / 32 + 64);
   w->clist = c.take<int32_t>(nn / 256 + 64);
+  w->slist = c.take<int32_t>(static_cast<size_t>(len_bucket_off(static_cast<int64_t>(nn), kLenBuckets)));
   w->n = n;
   w->nblocks = nb;
   w->items = items;
@@ -176,7 +196,7 @@ __global__ void __launch_bounds__(kSortThreads)
     hist_kernel(Src src, int64_t n, const uint32_t *__restrict__ nact, int shift, int bits, uint32_t *counts,
                 uint32_t *init_ticket, uint32_t *init_nact) {
   constexpr int TILE = kSortThreads * ITEMS;
-  if (blockIdx.x == 0 && init_ticket && threadIdx.x < 4) init_ticket[threadIdx.x] = 0u;
+  if (blockIdx.x == 0 && init_ticket && threadIdx.x < kTickets) init_ticket[threadIdx.x] = 0u;
   if (blockIdx.x == 0 && init_nact && threadIdx.x == 0) *init_nact = static_cast<uint32_t>(n);
   n = active_count(n, nact);
   if (static_cast<int64_t>(blockIdx.x) * TILE >= n) return;  // empty tiles are never read (see used_tiles)
@@ -558,7 +578,7 @@ __global__ void __launch_bounds__(kSortThreads)
     uint32_t tall;
     block_exclusive_scan(total, sh, &tall);
     if (blockIdx.x == 0 && threadIdx.x == 0) *nact = tall;
-    if (blockIdx.x == 0 && threadIdx.x < 4) ticket[threadIdx.x] = 0u;
+    if (blockIdx.x == 0 && threadIdx.x < kTickets) ticket[threadIdx.x] = 0u;
   }
   const int64_t m = src.count(n);
   const int w = threadIdx.x / hlr::kWave;
@@ -919,6 +939,148 @@ inline void list_heavy_units(SegWork<uint32_t> &w, hipStream_t s) {
   int g = hlr::grid_for(w.n, 256);
   if (g > 1024) g = 1024;
   heavy_units_kernel<<<g, 256, 0, s>>>(w.seg_start, w.seg_end, w.nseg, w.ticket, w.hlist, w.clist);
+}
+
+// The plan's list of long segments for whole-segment chains (the SGD sum):
+// segment k of length len >= kChainMin goes to the region of its length
+// bucket; counts in ticket[4 + b].  Such segments are few, so one atomic each.
+__global__ void __launch_bounds__(256)
+    heavy_segments_kernel(const int32_t *__restrict__ seg_start, const int32_t *__restrict__ seg_end,
+                          const int64_t *__restrict__ nseg_p, int64_t n, uint32_t *ticket, int32_t *slist) {
+  const int64_t nseg = *nseg_p;
+  const int64_t stride = static_cast<int64_t>(gridDim.x) * 256;
+  for (int64_t k = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x; k < nseg; k += stride) {
+    const int32_t len = seg_end[k] - seg_start[k];
+    if (len < kChainMin) continue;
+    int b = 31 - __builtin_clz(static_cast<uint32_t>(len)) - kLenShift;
+    b = b < kLenBuckets - 1 ? b : kLenBuckets - 1;
+    const uint32_t slot = atomicAdd(&ticket[4 + b], 1u);
+    slist[len_bucket_off(n, b) + slot] = static_cast<int32_t>(k);
+  }
+}
+
+// After group_by_row: lists the heavy segments by length bucket (slist).
+inline void list_heavy_segments(SegWork<uint32_t> &w, hipStream_t s) {
+  int g = hlr::grid_for(w.n, 256);
+  if (g > 1024) g = 1024;
+  heavy_segments_kernel<<<g, 256, 0, s>>>(w.seg_start, w.seg_end, w.nseg, w.n, w.ticket, w.slist);
+}
+
+// Heavy-segment work item it of a plan (items = segments x S slices, the
+// longest length bucket first): the segment and the slice.  Returns false
+// past the last item.  cnt[b] = ticket[4 + b].
+__device__ __forceinline__ bool heavy_item(const uint32_t (&cnt)[kLenBuckets], const int32_t *__restrict__ slist,
+                                           int64_t n, int64_t S, int64_t it, int32_t *seg, int64_t *slice) {
+  int64_t off = len_bucket_off(n, kLenBuckets);
+#pragma unroll
+  for (int b = kLenBuckets - 1; b >= 0; --b) {
+    off -= len_bucket_cap(n, b);
+    const int64_t c = static_cast<int64_t>(cnt[b]) * S;
+    if (it < c) {
+      *seg = slist[off + it / S];
+      *slice = it % S;
+      return true;
+    }
+    it -= c;
+  }
+  return false;
+}
+
+// Long running sums (the SGD sum of a hot row, one dependent fp32 chain per
+// element): one element per 16-lane row of the wave (row r takes element
+// el_r), 16 positions per load instruction.  Lane l of a row reads position
+// j + 16u + l of instruction u; the chain runs in lane 0 of each row.  The 16
+// values of a row reach lane 0 through LDS: every lane writes its value to
+// the wave's slot, and each lane reads its row's 16 values back as four
+// 16-byte reads (a broadcast within the row), so the chain itself is 16 plain
+// dependent adds per instruction.  (Folding a DPP row shift into each add
+// instead makes every add wait for the cross-lane network: about 14 cycles
+// per dependent add on this GPU against about 6 for a plain add.)  The sum
+// starts from -0.0 and positions past j1 read -0.0: -0.0 is the identity of
+// IEEE addition (s + -0.0 == s for every s, signed zeros included), so the
+// result equals the running sum started from the first value, and every batch
+// is the same straight-line code.  Indices come in by vector loads of 64
+// positions and reach each row by a lane permute; P load instructions per
+// batch plus P / 4 index loads stay within the 63-load counter.  grad(x) turns
+// a loaded value into the term summed (the L2-alignment gradient).  lds: this
+// wave's kChainSlots * 64 floats.  Only lane 0 of each row returns a
+// meaningful sum.
+constexpr int kChainSlots = 4;
+
+// Instruction u of a batch through LDS: each lane writes its term (-0.0 past
+// j1) to the slot of u, then reads its row's 16 terms back.
+template <typename Grad>
+__device__ __forceinline__ void stage1(float *lds, int u, int32_t j, int32_t j1, int l, int lane, int r16, float x,
+                                       Grad grad, float4 (&out)[4]) {
+  float *sl = lds + (u % kChainSlots) * 64;
+  sl[lane] = j + 16 * u + l < j1 ? grad(x) : -0.0f;
+  __builtin_amdgcn_wave_barrier();
+  const float4 *q = reinterpret_cast<const float4 *>(sl + r16);
+#pragma unroll
+  for (int k = 0; k < 4; ++k) out[k] = q[k];
+  __builtin_amdgcn_wave_barrier();
+}
+
+template <int P, bool Off32, typename Grad>
+__device__ __forceinline__ float chain_sum16(const float *__restrict__ src, const uint32_t *__restrict__ spos,
+                                             int32_t j0, int32_t j1, int64_t D, int64_t el, float *lds, Grad grad) {
+  constexpr int NP = 16 * P;
+  constexpr int NI = NP / 64;
+  static_assert(P % 4 == 0 && P + NI <= 63, "counter limit");
+  const int lane = hlr::lane_id();
+  const int l = lane & 15;
+  const int r16 = lane & ~15;
+  const uint32_t ecol = static_cast<uint32_t>(el < D ? el : 0);
+  const uint32_t row_bytes = static_cast<uint32_t>(D * 4);
+  j0 = __builtin_amdgcn_readfirstlane(j0);
+  j1 = __builtin_amdgcn_readfirstlane(j1);
+  float s = -0.0f;
+  if (j0 >= j1) return s;
+  const __amdgpu_buffer_rsrc_t rs =
+      __builtin_amdgcn_make_buffer_rsrc(const_cast<float *>(src), 0, 0x7fffffff, 0x00020000);
+  uint32_t pv[NI];
+#pragma unroll
+  for (int i = 0; i < NI; ++i) {
+    const int32_t jj = j0 + 64 * i + lane;
+    pv[i] = spos[jj < j1 ? jj : j1 - 1];
+  }
+  for (int32_t j = j0; j < j1; j += NP) {
+    float x[P];
+#pragma unroll
+    for (int u = 0; u < P; ++u) {
+      const uint32_t p = static_cast<uint32_t>(__shfl(static_cast<int>(pv[u / 4]), 16 * (u % 4) + l));
+      if (Off32) {
+        x[u] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rs, p * row_bytes + ecol * 4, 0, 0));
+      } else {
+        x[u] = src[static_cast<int64_t>(p) * D + ecol];
+      }
+    }
+#pragma unroll
+    for (int i = 0; i < NI; ++i) {  // next batch's indices, behind this batch's rows
+      const int32_t jj = j + NP + 64 * i + lane;
+      pv[i] = spos[jj < j1 ? jj : j1 - 1];
+    }
+    __builtin_amdgcn_sched_barrier(0);
+    // The next instruction's terms are written and read back before the
+    // current one's adds, so the LDS round trip hides behind them.
+    float4 cur[4], nxt[4];
+    stage1(lds, 0, j, j1, l, lane, r16, x[0], grad, cur);
+#pragma unroll
+    for (int u = 0; u < P; ++u) {
+      if (u + 1 < P) stage1(lds, u + 1, j, j1, l, lane, r16, x[u + 1], grad, nxt);
+      __builtin_amdgcn_sched_barrier(0);  // keep the next stage's LDS traffic ahead of these adds
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        s = s + cur[q].x;
+        s = s + cur[q].y;
+        s = s + cur[q].z;
+        s = s + cur[q].w;
+      }
+#pragma unroll
+      for (int q = 0; q < 4; ++q) cur[q] = nxt[q];
+    }
+  }
+  return s;
 }
 
 }  // namespace

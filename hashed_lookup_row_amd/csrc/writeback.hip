@@ -15,16 +15,21 @@
 // SGD_SUM — per-row SGD with duplicate gradients summed and applied once (the
 // same sparse-table update pattern at a learning rate other than 1, as in the
 // hashed tables of "DLRMv4: MLPerf recommendation training goes sequential").
-// Positions are grouped by row with a stable radix sort (radix.hpp), and the
-// plan lists the runs of 256 consecutive occurrences of every longer row.
-// Rows with few occurrences are summed by one wave each (light part).  Every
-// (run, 64-element slice) of a longer row is summed in batch order by its own
-// wave (heavy part), so a Zipf-hot row (tens of thousands of duplicates)
-// spreads over the whole GPU; both parts run in one launch (sgd_apply_kernel,
-// heavy blocks first).  sgd_combine_kernel then adds each row's run totals in
-// batch order and writes fl(M - fl(lr * s)).  The two launches take up to
-// eight independent updates (distinct tables) at once: the heavy blocks of
-// all of them first, then the light blocks of all of them.
+// A row's sum is one fp32 running sum per element over its positions in batch
+// order.  Positions are grouped by row with a stable radix sort (radix.hpp),
+// and the plan lists the rows of kChainMin (512) or more occurrences by
+// length.  Rows with fewer occurrences are summed by one wave each (light
+// part: 8 positions per round trip, so such a row takes at most about 64 of
+// them).  A longer row is one dependent chain per element: every (row,
+// 16-element slice) is a block of four waves, one element per 16-lane row,
+// walking the row's positions in order with 16 positions per load
+// instruction (chain_sum16), so a Zipf-hot row (tens of thousands of
+// duplicates) spreads over many CUs while each element's sum keeps its order.
+// Both parts run in one launch (sgd_apply_kernel): a few heavy blocks per
+// update first, longest rows first, so the long chains start at once; the
+// light rows, which carry most of the bytes, stream beside them on the rest
+// of the GPU.  The launch takes up to eight independent updates (distinct
+// tables) at once.
 //
 // L2_ALIGN — the alternative to Writeback that the same Memory Layer section
 // compares: SGD on ||M[r] - sg(e_i)||^2, i.e. the gradient 2 (M[r] - e_i) per
@@ -205,8 +210,6 @@ __global__ void __launch_bounds__(kThreads)
 // L2 = true is the L2-alignment update: the source holds targets e_i and each
 // occurrence's gradient is fl(2 * fl(M - e_i)) with M the row before the batch
 // (the doubling is exact); everything else is as for SGD_SUM.
-constexpr int kRun = HLR_SGD_SUM_RUN;
-
 template <int NC>
 constexpr int light_batch() { return NC == 4 ? 4 : 8; }
 
@@ -229,9 +232,8 @@ __device__ __forceinline__ void sum_run(const float4 *__restrict__ g, const uint
   });
 }
 
-// Light rows (fewer than kHeavyMin occurrences, hence one run): one wave per
-// row; the row is read once, before its gradients, and written once:
-// fl(M - fl(lr * s)).  Longer rows belong to the heavy part.  A wave walks
+// Light rows (fewer than kChainMin occurrences): one wave per row; the row
+// is read once, before its gradients, and written once: fl(M - fl(lr * s)).  Longer rows belong to the heavy part.  A wave walks
 // rows k, k + waves, ...; the next row's (start, end, row) is loaded while the
 // current row is processed (wave-uniform, so scalar loads).
 template <int NC, bool L2>
@@ -252,7 +254,7 @@ __device__ __forceinline__ void sgd_light(float4 *table, const float4 *__restric
     const int64_t kc = kn < nseg ? kn : nseg - 1;
     const int32_t sn = seg_start[kc], en = seg_end[kc];
     const int64_t rn = seg_key[kc];
-    if (e - s < kHeavyMin) {
+    if (e - s < kChainMin) {
       float4 m[NC], run[NC];
 #pragma unroll
       for (int q = 0; q < NC; ++q) {
@@ -275,45 +277,42 @@ __device__ __forceinline__ void sgd_light(float4 *table, const float4 *__restric
   }
 }
 
-__device__ __forceinline__ void sgd_write1(float *table, int64_t r, float acc, float lr, int64_t D, int64_t e) {
-  if (e < D) {
-    const float st = lr * acc;
-    table[r * D + e] = table[r * D + e] - st;  // fl(M - fl(lr * s))
-  }
-}
-
-// Heavy rows: one wave per (run of <= 256 occurrences, 64-element slice).  A
-// row with one run is updated at once; otherwise the run total goes to
-// `partial` for sgd_combine.  No wave writes a multi-run row before the
-// combine, so the L2 gradients all see the row as it was before the batch.
-static_assert(kRun == kBaseRun, "the plan lists heavy runs of kRun occurrences");
-
-template <bool L2>
+// Heavy rows: one block of four waves per (row, 16-element slice); wave w
+// takes elements 16 * slice + 4w + r in its rows r = 0..3, each one chain over
+// all the row's positions in batch order (chain_sum16), then lane 0 of the row
+// writes fl(M - fl(lr * s)).  Blocks take items in the plan's order, longest
+// rows first.  L2: every gradient is taken at the row before the batch, which
+// no block writes before its own chain has read it (one block per element).
+template <bool L2, bool Off32>
 __device__ __forceinline__ void sgd_heavy(float *table, const float *__restrict__ g,
                                           const uint32_t *__restrict__ skey, const uint32_t *__restrict__ spos,
                                           const int32_t *__restrict__ seg_start, const int32_t *__restrict__ seg_end,
-                                          const uint32_t *__restrict__ counters, const int2 *__restrict__ hlist,
-                                          float lr, int64_t D, float *partial, int block, int nblocks) {
-  const int64_t S = num_slices(D);
-  const int64_t items = static_cast<int64_t>(counters[0]) * S;
-  const int64_t waves = static_cast<int64_t>(nblocks) * (kThreads / kWave);
-  for (int64_t it = (static_cast<int64_t>(block) * kThreads + threadIdx.x) / kWave; it < items; it += waves) {
-    const int2 km = hlist[it / S];
-    const int64_t e = (it % S) * kSliceElems + lane_id();
-    const int32_t s = seg_start[km.x], end = seg_end[km.x];
-    const int32_t j0 = s + km.y * kRun;
-    const int32_t j1 = j0 + kRun < end ? j0 + kRun : end;
-    float mv = 0.f;
-    if (L2) mv = table[static_cast<int64_t>(skey[s]) * D + (e < D ? e : 0)];
-    float acc = 0.f;
-    slice_run(g, spos, j0, j1, D, e, [&](int32_t j, float x) {
-      const float y = L2 ? l2_grad(mv, x) : x;
-      acc = j == j0 ? y : acc + y;
-    });
-    if (end - s <= kRun) {
-      sgd_write1(table, skey[s], acc, lr, D, e);
-    } else if (e < D) {
-      partial[run_slot(j0, km.y, kRun) * D + e] = acc;
+                                          const uint32_t *__restrict__ counters, const int32_t *__restrict__ slist,
+                                          int64_t n, float lr, int64_t D, int block, int nblocks) {
+  const int64_t S = (D + 15) / 16;
+  uint32_t cnt[kLenBuckets];
+  int64_t items = 0;
+#pragma unroll
+  for (int b = 0; b < kLenBuckets; ++b) {
+    cnt[b] = counters[4 + b];
+    items += static_cast<int64_t>(cnt[b]) * S;
+  }
+  const int wv = static_cast<int>(threadIdx.x) / kWave;
+  const int r = lane_id() / 16;
+  __shared__ __align__(16) float lds[kThreads / kWave][kChainSlots * 64];
+  for (int64_t it = block; it < items; it += nblocks) {
+    int32_t k;
+    int64_t slice;
+    heavy_item(cnt, slist, n, S, it, &k, &slice);
+    const int64_t el = slice * 16 + 4 * wv + r;
+    const int32_t s = seg_start[k], end = seg_end[k];
+    const int64_t at = static_cast<int64_t>(skey[s]) * D + (el < D ? el : 0);
+    const float mv = table[at];
+    const float acc =
+        chain_sum16<48, Off32>(g, spos, s, end, D, el, lds[wv], [&](float x) { return L2 ? l2_grad(mv, x) : x; });
+    if ((lane_id() & 15) == 0 && el < D) {
+      const float st = lr * acc;
+      table[at] = mv - st;  // fl(M - fl(lr * s))
     }
   }
 }
@@ -326,11 +325,10 @@ struct SgdJob {
   const int32_t *seg_start, *seg_end;
   const int64_t *nseg;
   const uint32_t *counters;
-  const int2 *hlist;
-  const int32_t *clist;
-  float *partial;
+  const int32_t *slist;
+  int64_t n;
   float lr;
-  int heavy_begin, heavy_blocks, light_begin, light_blocks, comb_begin, comb_blocks;
+  int heavy_begin, heavy_blocks, light_begin, light_blocks;
 };
 
 // Independent updates (distinct tables) applied by one launch: the heavy
@@ -343,14 +341,14 @@ struct SgdJobs {
   int64_t D;
 };
 
-template <int NC, bool L2>
+template <int NC, bool L2, bool Off32>
 __global__ void __launch_bounds__(kThreads) sgd_apply_kernel(SgdJobs js) {
   const int blk = static_cast<int>(blockIdx.x);
   for (int i = 0; i < js.count; ++i) {
     const SgdJob &j = js.job[i];
     if (blk >= j.heavy_begin && blk < j.heavy_begin + j.heavy_blocks) {
-      sgd_heavy<L2>(j.table, j.g, j.skey, j.spos, j.seg_start, j.seg_end, j.counters, j.hlist, j.lr, js.D,
-                    j.partial, blk - j.heavy_begin, j.heavy_blocks);
+      sgd_heavy<L2, Off32>(j.table, j.g, j.skey, j.spos, j.seg_start, j.seg_end, j.counters, j.slist, j.n, j.lr,
+                           js.D, blk - j.heavy_begin, j.heavy_blocks);
       return;
     }
     if (blk >= j.light_begin && blk < j.light_begin + j.light_blocks) {
@@ -362,51 +360,10 @@ __global__ void __launch_bounds__(kThreads) sgd_apply_kernel(SgdJobs js) {
   }
 }
 
-// Rows with several runs: one wave per (row, slice) adds the run totals in
-// batch order, then updates the row once.
-__device__ __forceinline__ void sgd_combine(float *table, const uint32_t *__restrict__ skey,
-                                            const int32_t *__restrict__ seg_start,
-                                            const int32_t *__restrict__ seg_end,
-                                            const uint32_t *__restrict__ counters,
-                                            const int32_t *__restrict__ clist, float lr, int64_t D,
-                                            const float *__restrict__ partial, int block, int nblocks) {
-  const int64_t S = num_slices(D);
-  const int64_t items = static_cast<int64_t>(counters[1]) * S;
-  const int64_t waves = static_cast<int64_t>(nblocks) * (kThreads / kWave);
-  for (int64_t it = (static_cast<int64_t>(block) * kThreads + threadIdx.x) / kWave; it < items; it += waves) {
-    const int32_t k = clist[it / S];
-    const int64_t e = (it % S) * kSliceElems + lane_id();
-    const int32_t s = seg_start[k], end = seg_end[k];
-    const int32_t nruns = (end - s + kRun - 1) / kRun;
-    float acc = 0.f;
-    slice_run_rows([&](int32_t m) { return partial + run_slot(s + m * kRun, m, kRun) * D; }, 0, nruns, D, e,
-                   [&](int32_t m, float x) { acc = m == 0 ? x : acc + x; });
-    sgd_write1(table, skey[s], acc, lr, D, e);
-  }
-}
-
-__global__ void __launch_bounds__(kThreads) sgd_combine_kernel(SgdJobs js) {
-  const int blk = static_cast<int>(blockIdx.x);
-  for (int i = 0; i < js.count; ++i) {
-    const SgdJob &j = js.job[i];
-    if (blk >= j.comb_begin && blk < j.comb_begin + j.comb_blocks) {
-      sgd_combine(j.table, j.skey, j.seg_start, j.seg_end, j.counters, j.clist, j.lr, js.D, j.partial,
-                  blk - j.comb_begin, j.comb_blocks);
-      return;
-    }
-  }
-}
-
-inline size_t sgd_partial_elems(int64_t n, int64_t dim) {
-  return static_cast<size_t>(2 * ((n + kRun - 1) / kRun) + 2) * static_cast<size_t>(dim / 4);
-}
-
 // The job of one SGD_SUM / L2_ALIGN update: its plan's buffers in ws and its block counts.
 SgdJob sgd_job(float *table, const float *g, int64_t n, int64_t dim, float lr, void *ws, int64_t num_rows) {
   SegWork<uint32_t> w;
-  Carver c(ws);
-  c.off = segwork_layout<uint32_t>(n, &w, ws);
-  float *partial = reinterpret_cast<float *>(c.take<float4>(sgd_partial_elems(n, dim)));
+  segwork_layout<uint32_t>(n, &w, ws);
   const int cur = sorted_buffer(num_rows);
   SgdJob j{};
   j.table = table;
@@ -418,42 +375,48 @@ SgdJob sgd_job(float *table, const float *g, int64_t n, int64_t dim, float lr, v
   j.seg_end = w.seg_end;
   j.nseg = w.nseg;
   j.counters = w.ticket;
-  j.hlist = w.hlist;
-  j.clist = w.clist;
-  j.partial = partial;
+  j.slist = w.slist;
+  j.n = n;
   j.lr = lr;
-  const int gl = grid_for(n, 4 * 4), gh = grid_for(n / 32 * num_slices(dim), 4);
-  const int gc = grid_for(n / 256 * num_slices(dim), 4);
+  // heavy blocks hold 4 waves of about 120 registers each; 64 per update
+  // leave most of the GPU to the light rows that stream beside them
+  const int gl = grid_for(n, 4 * 4), gh = grid_for(n, 2048);
   j.light_blocks = gl < 4096 ? gl : 4096;
-  j.heavy_blocks = gh < 2048 ? gh : 2048;
-  j.comb_blocks = gc < 1024 ? gc : 1024;
+  j.heavy_blocks = gh < 64 ? gh : 64;
   return j;
 }
 
-// Two launches for up to kMaxSgdJobs updates of one dim and mode: heavy blocks
-// of every job, then light blocks of every job; then the combine of every job.
+// A gradient array whose byte offsets fit the 31-bit range of a buffer resource.
+inline bool off32_ok(int64_t n, int64_t dim) { return n * dim * 4 < (int64_t(1) << 31); }
+
+// One launch for up to kMaxSgdJobs updates of one dim and mode: heavy blocks
+// of every job, then light blocks of every job.
 template <bool L2>
 void sgd_launch(SgdJobs &js, hipStream_t s) {
   int next = 0;
+  bool off32 = true;
   for (int i = 0; i < js.count; ++i) {
     js.job[i].heavy_begin = next;
     next += js.job[i].heavy_blocks;
+    off32 = off32 && off32_ok(js.job[i].n, js.D);
   }
   for (int i = 0; i < js.count; ++i) {
     js.job[i].light_begin = next;
     next += js.job[i].light_blocks;
   }
-  int comb = 0;
-  for (int i = 0; i < js.count; ++i) {
-    js.job[i].comb_begin = comb;
-    comb += js.job[i].comb_blocks;
-  }
   if (next == 0) return;
   const int64_t nc = (js.D / 4 + kWave - 1) / kWave;
-  if (nc == 1) sgd_apply_kernel<1, L2><<<next, kThreads, 0, s>>>(js);
-  else if (nc == 2) sgd_apply_kernel<2, L2><<<next, kThreads, 0, s>>>(js);
-  else sgd_apply_kernel<4, L2><<<next, kThreads, 0, s>>>(js);
-  if (comb > 0) sgd_combine_kernel<<<comb, kThreads, 0, s>>>(js);
+#define HLR_SGD_LAUNCH(NC, O32) sgd_apply_kernel<NC, L2, O32><<<next, kThreads, 0, s>>>(js)
+  if (off32) {
+    if (nc == 1) HLR_SGD_LAUNCH(1, true);
+    else if (nc == 2) HLR_SGD_LAUNCH(2, true);
+    else HLR_SGD_LAUNCH(4, true);
+  } else {
+    if (nc == 1) HLR_SGD_LAUNCH(1, false);
+    else if (nc == 2) HLR_SGD_LAUNCH(2, false);
+    else HLR_SGD_LAUNCH(4, false);
+  }
+#undef HLR_SGD_LAUNCH
 }
 
 }  // namespace
@@ -467,10 +430,7 @@ extern "C" size_t writeback_rows_workspace_size(int64_t num_rows, int64_t dim, i
     return lw_layout(n, &w, nullptr);
   }
   SegWork<uint32_t> w;
-  Carver c(nullptr);
-  c.off = segwork_layout<uint32_t>(n, &w, nullptr);
-  c.take<float4>(sgd_partial_elems(n, dim > 0 ? dim : 4));
-  return c.off;
+  return segwork_layout<uint32_t>(n, &w, nullptr);
 }
 
 namespace {
@@ -502,7 +462,7 @@ void wb_plan(int64_t num_rows, const int64_t *rows, int64_t n, int32_t mode, voi
   SegWork<uint32_t> w;
   segwork_layout<uint32_t>(n, &w, ws);
   group_by_row(w, rows, nullptr, num_rows, stream);
-  list_heavy_units(w, stream);
+  list_heavy_segments(w, stream);
 }
 
 // Apply: reads the plan left in the workspace by wb_plan.

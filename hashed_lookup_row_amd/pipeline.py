@@ -259,8 +259,8 @@ class HashedTablesPipeline:
     tables apply.  With batch=True (the default; distinct tables of one dim) the tables go in groups
     of `group` (at most eight), one ring per group: the lookup stream makes the group's rows, then
     its plans; the compute stream waits once for the rows, gathers table by table, waits once for
-    the plans and applies the whole group in one writeback_apply_batch call (two kernel launches per
-    group instead of two per table; the duplicate runs of the group's tables overlap).  mark is then
+    the plans and applies the whole group in one writeback_apply_batch call (one kernel launch per
+    group instead of one per table; the long duplicate chains of the group's tables overlap).  mark is then
     called with ("apply", -1 - group index, 0 | 1).  Groups of four suit the 8 tables of [DLRM]:
     with all eight in one group the plan chains (many small kernels) wait behind the long gathers
     and applies of the group before."""

@@ -148,8 +148,9 @@ hlr_status dedup_ids(const int64_t *keys, int64_t n, int64_t *out_unique, int64_
  *    g = fl(M[r] - e_p), M[r] = fl(M[r] - g)   (exact SGD at learning rate 1,
  *    so M[r] becomes e_p up to these two roundings).  lr must be 1.
  *  mode HLR_WB_SGD_SUM: src holds gradients g_i.  The gradients of each row
- *    are summed in batch order within runs of 256 consecutive occurrences,
- *    run totals added in batch order (s), then M[r] = fl(M[r] - fl(lr*s)).
+ *    are summed as one fp32 running sum per element in ascending batch
+ *    order, starting from the first (s = g_1, s = fl(s + g_k)), then
+ *    M[r] = fl(M[r] - fl(lr*s)).
  *  mode HLR_WB_L2_ALIGN: src holds targets e_i; the row is learned by SGD on
  *    ||M[r] - e_i||^2, the alternative to Writeback in [ML] sec. 2 and 3:
  *    each occurrence's gradient is fl(2*fl(M[r] - e_i)) with M[r] the row
@@ -160,7 +161,6 @@ hlr_status dedup_ids(const int64_t *keys, int64_t n, int64_t *out_unique, int64_
 #define HLR_WB_LAST_WINS 0
 #define HLR_WB_SGD_SUM 1
 #define HLR_WB_L2_ALIGN 2
-#define HLR_SGD_SUM_RUN 256
 size_t writeback_rows_workspace_size(int64_t num_rows, int64_t dim, int64_t n, int32_t mode);
 hlr_status writeback_rows(float *table, int64_t num_rows, int64_t dim, const int64_t *rows, const float *src,
                           int64_t n, int32_t mode, float lr, void *ws, size_t ws_bytes, hipStream_t stream);

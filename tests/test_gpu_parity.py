@@ -257,7 +257,7 @@ def test_sgd_sum_matches_oracle(dev, n, C, D, s):
                        lr=0.01)
     oracle.sgd_sum(table, rows, grads, 0.01)
     assert bits_equal(to_np(t), table)
-    assert np.bincount(rows[rows >= 0]).max() > 256 or n < 5000  # a multi-run segment is exercised
+    assert np.bincount(rows[rows >= 0]).max() >= 64 or n < 5000  # a heavy (chained) row is exercised
 
 
 @pytest.mark.parametrize("n,C,D,s,lr", [(20_000, 3000, 512, 1.2, 0.05), (3000, 2, 64, 1.0, 0.5),
@@ -394,8 +394,8 @@ def test_ema_speculation_fallback_is_exact(dev, spike_at):
     assert bits_equal(to_np(t), table)
 
 
-def test_sgd_sum_single_row_many_runs(dev):
-    """One row with 30,000 duplicate gradients: 118 runs summed in parallel, combined in order."""
+def test_sgd_sum_single_row_long_chain(dev):
+    """One row with about 24,000 duplicate gradients: one running sum per element, in batch order."""
     g = np.random.default_rng(30)
     n, D = 30_000, 512
     rows = np.where(g.random(n) < 0.8, 7, g.integers(0, 10, size=n)).astype(np.int64)
@@ -404,5 +404,52 @@ def test_sgd_sum_single_row_many_runs(dev):
     t = torch.from_numpy(table).to(dev)
     hlr.writeback_rows(t, torch.from_numpy(rows).to(dev), torch.from_numpy(grads).to(dev), mode=hlr.WB_SGD_SUM,
                        lr=0.01)
+    oracle.sgd_sum(table, rows, grads, 0.01)
+    assert bits_equal(to_np(t), table)
+
+
+@pytest.mark.parametrize("k", [63, 64, 65, 511, 512, 513, 1000, 4097, 20_000])
+@pytest.mark.parametrize("D", [4, 12, 512])
+def test_sgd_sum_order_revealing_rows(dev, k, D):
+    """Row 0's gradients in batch order are 1, then k - 1 copies of 2^-24 (negated in odd elements):
+    summed left to right each tiny term rounds away (ties to even) and the row moves by exactly lr;
+    any other order (tiny terms first, a split into partial sums, a permuted group of lanes) gives a
+    different fp32 result.  Row 1 interleaves random gradients; rows of k - 1, k and k + 1
+    occurrences cover the threshold between one wave per row and the per-element chains (512)."""
+    g = np.random.default_rng(k * 7 + D)
+    rows = np.concatenate([np.zeros(k, np.int64), np.ones(3 * k, np.int64), np.full(k - 1, 2), np.full(k + 1, 3)])
+    perm = np.sort(g.permutation(rows.size)[:k])  # row 0 at increasing positions, spread over the batch
+    rest = np.setdiff1d(np.arange(rows.size), perm)
+    order = np.empty(rows.size, np.int64)
+    order[perm] = 0
+    order[rest] = rows[k:]
+    rows = order
+    grads = (g.standard_normal((rows.size, D)) * 1e-3).astype(np.float32)
+    sign = np.where(np.arange(D) % 2 == 0, np.float32(1.0), np.float32(-1.0))
+    p0 = np.nonzero(rows == 0)[0]
+    grads[p0] = sign * np.float32(2.0 ** -24)
+    grads[p0[0]] = sign
+    table = np.zeros((4, D), np.float32)
+    t = torch.from_numpy(table).to(dev)
+    hlr.writeback_rows(t, torch.from_numpy(rows).to(dev), torch.from_numpy(grads).to(dev), mode=hlr.WB_SGD_SUM,
+                       lr=1.0)
+    oracle.sgd_sum(table, rows, grads, 1.0)
+    assert np.array_equal(table[0], -sign)  # the oracle itself: left to right, the tiny terms vanish
+    assert bits_equal(to_np(t), table)
+
+
+def test_sgd_sum_gradients_over_2gib(dev):
+    """Gradient array of 2 GiB (byte offsets past the 31-bit buffer range): 64-bit addressing path."""
+    g = np.random.default_rng(31)
+    n, D = 1 << 19, 1024
+    rows = np.minimum(synth.zipf_ranks(g, 40, 1.3, n), 39).astype(np.int64)
+    grads = np.empty((n, D), np.float32)
+    grads[:] = (g.standard_normal((1, D)) * 1e-3).astype(np.float32)
+    grads[:, ::7] = (g.standard_normal((n, 1)) * 1e-3).astype(np.float32)
+    table = (g.standard_normal((40, D)) * 0.01).astype(np.float32)
+    t = torch.from_numpy(table).to(dev)
+    gd = torch.from_numpy(grads).to(dev)
+    hlr.writeback_rows(t, torch.from_numpy(rows).to(dev), gd, mode=hlr.WB_SGD_SUM, lr=0.01)
+    del gd
     oracle.sgd_sum(table, rows, grads, 0.01)
     assert bits_equal(to_np(t), table)
