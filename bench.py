@@ -28,7 +28,7 @@ import time
 
 ROOT = os.path.dirname(os.path.abspath(__file__))
 HBM_PEAK_GBS = 8000.0
-PMC_FILE = os.path.join(ROOT, "profiles", "gather_memory_layer_pmc.json")
+PMC_FILE = os.path.join(ROOT, "profiles", "ml_fused_memory_layer_pmc.json")
 
 
 class HipTimer:
@@ -67,11 +67,21 @@ def src_sha(path):
     return hashlib.sha256(open(path, "rb").read()).hexdigest()[:16]
 
 
+def row_pass_sha():
+    """Source hash of the Memory-Layer row pass and the plan it reads (the kernel the counters describe)."""
+    h = hashlib.sha256()
+    for f in ("mlstep.hip", "mlwork.hpp"):
+        h.update(open(os.path.join(ROOT, "hashed_lookup_row_amd", "csrc", f), "rb").read())
+    return h.hexdigest()[:16]
+
+
 def parse():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--depth", type=int, default=3, help="ring depth of the two-stream schedule")
+    ap.add_argument("--eager", dest="graph", action="store_false",
+                    help="enqueue the timed Memory-Layer batches call by call instead of as one HIP graph")
     ap.add_argument("--no-lookahead", dest="lookahead", action="store_false",
                     help="enqueue each batch's lookup with its own row traffic instead of one batch ahead")
     ap.add_argument("--warmup", type=int, default=10)
@@ -137,7 +147,7 @@ def main():
         return
     import hashed_lookup_row_amd as hlr
     import synth
-    from hashed_lookup_row_amd.pipeline import MemoryLayerPipeline
+    from hashed_lookup_row_amd.pipeline import MemoryLayerPipeline, StepGraph
 
     hlr.load_library()
     dev = torch.device("cuda:0")
@@ -155,7 +165,7 @@ def main():
     t0 = time.time()
     prefill = synth.prefill_batches(cfg)
     stream, fc = [], 0
-    for t in range(1, W + 2 * K + 3):
+    for t in range(1, W + 3 * K + 3):
         ids, fc = synth.mpzch_step_ids(cfg, t, fc)
         stream.append(ids)
     print(f"[bench] generated inputs in {time.time() - t0:.1f}s", file=sys.stderr, flush=True)
@@ -180,6 +190,10 @@ def main():
           file=sys.stderr, flush=True)
 
     timer = HipTimer()
+    # a non-default compute stream (a HIP graph cannot be captured on the legacy default stream)
+    side = torch.cuda.Stream(dev)
+    side.wait_stream(torch.cuda.current_stream(dev))
+    torch.cuda.set_stream(side)
     cur = torch.cuda.current_stream(dev).cuda_stream
     pipe = MemoryLayerPipeline(identity, stamps, values, P, n, depth=args.depth)
 
@@ -208,33 +222,64 @@ def main():
     # regions (it gives each batch's insert count: rows the gather reads as zero instead of loading)
     id_snap, st_snap = identity.clone(), stamps.clone()
     la = args.lookahead
+    if args.graph and not la:
+        raise SystemExit("--graph needs the lookahead schedule")
+
+    def two_stream(first, timed_evs):
+        """Batches first .. first+K-1 in the two-stream schedule, timed on the compute stream; returns
+        (total seconds, host enqueue seconds, wall seconds)."""
+        start, stop = timer.event(), timer.event()
+        if args.graph:
+            batches = [(ids_dev[first + k], base_now + 1 + first + k, e_pool[(first + k) % npool], out)
+                       for k in range(K)]
+            graph = StepGraph(pipe, batches)  # captured, not run
+            torch.cuda.synchronize()
+            wall0 = time.perf_counter()
+            timer.record(start, cur)
+            graph.replay()
+            timer.record(stop, cur)
+        else:
+            torch.cuda.synchronize()
+            wall0 = time.perf_counter()
+            timer.record(start, cur)
+            if la:
+                pipe.prefetch(ids_dev[first], base_now + 1 + first)
+            for k in range(K):
+                piped_step(first + k, timed_evs.get(k) if timed_evs else None,
+                           ahead=first + k + 1 if la and k + 1 < K else None)
+            timer.record(stop, cur)
+        enqueue = time.perf_counter() - wall0
+        torch.cuda.synchronize()
+        wall = time.perf_counter() - wall0
+        return timer.elapsed_s(start, stop), enqueue, wall
+
+    # warm-up (eager), ending with no batch looked up ahead
     if la:
         pipe.prefetch(ids_dev[0], base_now + 1)
     for t in range(W):
-        piped_step(t, ahead=t + 1 if la else None)
+        piped_step(t, ahead=t + 1 if la and t + 1 < W else None)
     torch.cuda.synchronize()
 
-    # two-stream schedule (the headline): gather timed with HIP events on the compute stream on every
-    # EV_SAMPLE-th step (events add a little time to a step)
+    # the headline: batches W .. W+K-1 in the two-stream schedule with lookahead.  The row pass is timed with
+    # HIP events on the compute stream on every EV_SAMPLE-th batch of the call-by-call schedule (events
+    # inside a captured graph cannot be timed on this runtime): with --graph, over the next K batches, which
+    # are reported beside the headline (there too batch t+1's lookup runs beside batch t's row pass)
     evs = {k: [timer.event() for _ in range(2)] for k in range(0, K, EV_SAMPLE)}
-    start, stop = timer.event(), timer.event()
-    torch.cuda.synchronize()
-    wall0 = time.perf_counter()
-    timer.record(start, cur)
-    for k in range(K):  # with lookahead: K lookup halves (W+1 .. W+K) and K row halves (W .. W+K-1)
-        piped_step(W + k, evs.get(k), ahead=W + k + 1 if la else None)
-    timer.record(stop, cur)
-    enqueue = time.perf_counter() - wall0
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - wall0
-    total_s = timer.elapsed_s(start, stop)
+    eager = None
+    if args.graph:
+        total_s, enqueue, wall = two_stream(W, None)
+        args.graph = False
+        e_total, e_enqueue, _ = two_stream(W + K, evs)
+        args.graph = True
+        eager = {"ms_per_step": e_total / K * 1e3, "rows_per_s": n * K / e_total,
+                 "host_enqueue_us_per_step": e_enqueue / K * 1e6}
+        ev_first = W + K
+    else:
+        total_s, enqueue, wall = two_stream(W, evs)
+        ev_first = W
     gather_s = np.array([timer.elapsed_s(e[0], e[1]) for e in evs.values()])
     gather_steps = np.array(sorted(evs.keys()))
-
-    if la:  # the row half of the batch looked up last, outside the timed region
-        piped_step(W + K)
-        torch.cuda.synchronize()
-    off = 1 if la else 0
+    off = K if args.graph else 0
 
     # the same step as three calls on one stream, over the next K batches (reported beside the headline)
     sevs = {k: [timer.event() for _ in range(4)] for k in range(K)} if args.op_events else {}
@@ -253,29 +298,40 @@ def main():
     # distinct rows per timed step (for algorithmic bytes): MPZCH gives every distinct valid ID its own
     # row and no two IDs share one, so u = distinct IDs minus those without a row (overflows and
     # invalid IDs, both 0 on this workload: see stats_after)
-    us = np.array([np.unique(stream[W + k]).size for k in range(K)], dtype=np.float64)
+    nb = (ev_first - W) + K  # the headline batches, then (with --graph) the call-by-call batches timed by events
+    us_all = np.array([np.unique(stream[W + k]).size for k in range(nb)], dtype=np.float64)
+    us = us_all[:K]
     dup = 1.0 - us.mean() / n
     # rows the gather loads: distinct rows that were already stored (a row inserted by the batch reads as
     # zero and is not loaded); insert and overflow counts from the replay of the same lookups
-    rstats = torch.zeros((W + K, 6), dtype=torch.int64, device=dev)
-    for t in range(W + K):
+    rstats = torch.zeros((W + nb, 6), dtype=torch.int64, device=dev)
+    for t in range(W + nb):
         hlr.mpzch_lookup_or_insert(id_snap, st_snap, None, P, ids_dev[t], base_now + 1 + t, insert=True,
                                    out_rows=rows_buf, out_hit=hit_buf, out_stats=rstats[t])
-    rst = rstats.cpu().numpy()[W:W + K].astype(np.float64)
-    u_read = us - rst[:, 1] - rst[:, 3]
+    rst = rstats.cpu().numpy()[W:W + nb].astype(np.float64)
+    u_read_all = us_all - rst[:, 1] - rst[:, 3]
+    u_read = u_read_all[:K]
     del id_snap, st_snap
-    gather_bytes = n * R + u_read * R + n * 8 + n  # write out, read stored distinct rows, row indices, hit flags
-    gather_gbs = float(gather_bytes[gather_steps].sum() / gather_s.sum() / 1e9)
-    # step: gather as above; Writeback apply reads e at each row's last position and the stored rows, and
-    # writes every distinct row
-    step_bytes = n * R + 2 * u_read * R + 2 * us * R + 9 * n
+    # the row pass (gather + Writeback in one kernel), algorithmic bytes per batch as the method defines them:
+    # the gather writes every position's row and reads every distinct row, the Writeback reads the row and e
+    # at its last position and writes the row, plus the row index of every position: n*R + 4u*R + 8n
+    row_bytes_all = n * R + 4 * us_all * R + 8 * n
+    row_bytes = row_bytes_all[:K]
+    # what this one-pass design must move: each stored row read once (rows the batch inserted read as zero),
+    # e at the last position, every position's output and every distinct row written, and the plan it reads
+    # (a 16-byte descriptor and a 4-byte position per position at most)
+    design_bytes_all = n * R + u_read_all * R + 2 * us_all * R + 20 * n
+    timed = (ev_first - W) + gather_steps  # indices of the event-timed batches in the arrays above
+    row_gbs = float(row_bytes_all[timed].sum() / gather_s.sum() / 1e9)
+    design_gbs = float(design_bytes_all[timed].sum() / gather_s.sum() / 1e9)
+    step_bytes = row_bytes
     ms_per_step = total_s / K * 1e3
     value = n * K / total_s
 
     traffic = None
     if os.path.exists(PMC_FILE):
         pmc = json.load(open(PMC_FILE))
-        if pmc.get("gather_src_sha") == src_sha(os.path.join(ROOT, "hashed_lookup_row_amd", "csrc", "gather.hip")):
+        if pmc.get("src_sha") == row_pass_sha():
             traffic = pmc.get("traffic_bytes_per_launch")
 
     line = {
@@ -296,26 +352,32 @@ def main():
             "capacity": C, "dim": D, "probes": P, "ids_per_step": n, "universe": cfg.universe,
             "zipf_s": cfg.zipf_s, "fresh_frac": cfg.fresh_frac, "prefilled": True,
             "step": "mpzch_lookup_or_insert + gather_rows + writeback_rows(last_wins, lr=1)",
-            "schedule": ("two streams: lookup (MPZCH without values, Writeback plan) beside compute (gather, "
-                         "Writeback apply; rows the lookup inserts read as zero through its hit mask), one library "
-                         "call per half batch; "
+            "schedule": ("two streams: lookup (MPZCH without values, whose last kernel groups the batch's positions "
+                         "by row) beside compute (one pass over the batch's rows: gather and Writeback; rows the "
+                         "lookup inserts read as zero), one library call per half batch; "
                          + (f"lookahead: batch t+1's lookup is enqueued before batch t's row traffic, ring depth "
                             f"{args.depth}" if la else f"batch t's lookup with its own row traffic, ring depth "
-                                                       f"{args.depth}")),
+                                                       f"{args.depth}")
+                         + ("; the K timed batches captured (untimed) as one HIP graph of those calls and replayed "
+                            "once" if args.graph else "; enqueued call by call")),
         },
         "roofline": {
-            "bound": "hbm", "kernel": "gather_kernel<128>",
-            "achieved": gather_gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": gather_gbs / HBM_PEAK_GBS,
+            "bound": "hbm", "kernel": "ml_fused<2> (gather + Writeback, one pass over the batch's rows)",
+            "achieved": row_gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": row_gbs / HBM_PEAK_GBS,
             "traffic": traffic,
-            "algorithmic_bytes_per_launch": float(gather_bytes[gather_steps].mean()),
+            "algorithmic_bytes_per_launch": float(row_bytes_all[timed].mean()),
             "avg_launch_us": float(gather_s.mean() * 1e6),
             "timed_launches": int(len(gather_steps)),
+            "design_bytes_per_launch": float(design_bytes_all[timed].mean()),
+            "timed_in": "the call-by-call two-stream batches" if args.graph else "the headline batches",
+            "design_frac": design_gbs / HBM_PEAK_GBS,
         },
         "step_hbm": {
             "algorithmic_bytes_per_step": float(step_bytes.mean()),
             "achieved_gbs": float(step_bytes.sum() / total_s / 1e9),
             "frac": float(step_bytes.sum() / total_s / 1e9 / HBM_PEAK_GBS),
         },
+        "eager_two_stream": eager,
         "one_stream": {"ms_per_step": serial_s / K * 1e3, "rows_per_s": n * K / serial_s,
                        "ops_us": ({"lookup_or_insert": float(per_op[:, 0].mean() * 1e6),
                                    "gather": float(per_op[:, 1].mean() * 1e6),
@@ -337,8 +399,19 @@ def main():
     print(json.dumps(line), flush=True)
 
 
+def cpu_model():
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return None
+
+
 def cpu_baseline(cfg, prefill, stream, e_pool, npool, base_now, budget_s, W):
-    """Times the CPU oracle (single-threaded C) on the same steps: a bounded sample."""
+    """Times the CPU oracle (single-threaded C) on the same steps: a bounded sample, the process pinned to one
+    core of its CPU set for the duration (os.sched_setaffinity, no re-exec), mean and median per step."""
     import numpy as np
     import oracle
 
@@ -351,24 +424,36 @@ def cpu_baseline(cfg, prefill, stream, e_pool, npool, base_now, budget_s, W):
     tab.values.fill(0.0)  # touch every page before timing (inputs resident)
     setup = time.time() - t0
     e_host = {}
-    spent, steps = 0.0, 0
-    for t in range(W, len(stream)):
-        e = e_host.get(t % npool)
-        if e is None:
-            e = e_pool[t % npool].cpu().numpy()
-            e_host[t % npool] = e
-        a = time.perf_counter()
-        rows, hit, ev, st = tab.step(stream[t], base_now + 1 + t)
-        tab.gather(rows)
-        tab.writeback(rows, e)
-        spent += time.perf_counter() - a
-        steps += 1
-        if spent >= budget_s:
-            break
+    for t in range(W, len(stream)):  # host copies of e before timing
+        if t % npool not in e_host:
+            e_host[t % npool] = e_pool[t % npool].cpu().numpy()
+    allowed = sorted(os.sched_getaffinity(0)) if hasattr(os, "sched_getaffinity") else []
+    core = allowed[-1] if allowed else None
+    if core is not None:
+        os.sched_setaffinity(0, {core})
+    per_step = []
+    try:
+        for t in range(W, len(stream)):
+            e = e_host[t % npool]
+            a = time.perf_counter()
+            rows, hit, ev, st = tab.step(stream[t], base_now + 1 + t)
+            tab.gather(rows)
+            tab.writeback(rows, e)
+            per_step.append(time.perf_counter() - a)
+            if sum(per_step) >= budget_s:
+                break
+    finally:
+        if core is not None:
+            os.sched_setaffinity(0, set(allowed))
+    spent, steps = float(sum(per_step)), len(per_step)
     return {"value": steps * n / spent, "unit": "rows/s", "cores": 1, "kind": "oracle",
             "sample": f"{steps} steps (steps {W + 1}..{W + steps} of the same stream, {n} IDs each) after an "
                       f"untimed oracle prefill ({setup:.1f}s); single-threaded C oracle, lookup+gather+writeback",
-            "seconds": spent, "host_nproc": os.cpu_count()}
+            "seconds": spent, "step_ms_mean": spent / steps * 1e3,
+            "step_ms_median": float(np.median(per_step)) * 1e3,
+            "rows_per_s_median_step": n / float(np.median(per_step)),
+            "pinned_core": core, "cpu_model": cpu_model(), "host_nproc": os.cpu_count(),
+            "cpus_allowed": len(allowed) or None}
 
 
 # ----------------------------------------------------------------------------------------------

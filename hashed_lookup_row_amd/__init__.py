@@ -74,8 +74,10 @@ def load_library():
             "dks_workspace_size": (sz, [i64]),
             "dks_lookup_or_insert": (i32, [p, p, i64, p, p, i64, i64, p, p, i64, i64, i32, p, p, p, p, sz, p]),
             "dks_rehash": (i32, [p, p, i64, p, p, i64, p]),
-            "memory_layer_step": (i32, [p, p, p, i64, i32, i64, p, i64, i64, p, p, p, p, p, p, p, sz, p, sz,
+            "memory_layer_step": (i32, [p, p, p, i64, i32, i64, p, i64, i64, i64, p, p, p, p, p, p, p, sz, p, sz,
                                         p, p, p, p, p, p, p, p, i32]),
+            "memory_layer_step_workspace_size": (sz, [i64, i64]),
+            "memory_layer_step_workspace_init": (i32, [p, sz, p, sz, i64, i64, p]),
         }
         for name, (res, args) in sig.items():
             f = getattr(lib, name)
@@ -91,7 +93,8 @@ def exported_symbols():
             "writeback_rows", "ema_update_rows_workspace_size", "ema_update_rows", "gather_dequant_score",
             "hashed_rows", "mpzch_zero_inserted", "writeback_plan", "writeback_apply", "ema_update_plan",
             "ema_update_apply", "writeback_plan_rows", "quantize_rows_int8", "mark_rows", "clear_marks",
-            "dks_workspace_size", "dks_lookup_or_insert", "dks_rehash", "memory_layer_step", "ema_update_plan_subset", "ema_update_apply_batch",
+            "dks_workspace_size", "dks_lookup_or_insert", "dks_rehash", "memory_layer_step",
+            "memory_layer_step_workspace_size", "memory_layer_step_workspace_init", "ema_update_plan_subset", "ema_update_apply_batch",
             "writeback_apply_batch"]
 
 
@@ -283,6 +286,10 @@ def _own_ws(ws: torch.Tensor, need: int):
 
 def writeback_workspace_size(num_rows, dim, n, mode=WB_LAST_WINS) -> int:
     return int(load_library().writeback_rows_workspace_size(int(num_rows), int(dim), int(n), int(mode)))
+
+
+def memory_layer_step_workspace_size(n, capacity) -> int:
+    return int(load_library().memory_layer_step_workspace_size(int(n), int(capacity)))
 
 
 def ema_workspace_size(num_rows, dim, n) -> int:

@@ -21,6 +21,13 @@ class _Hip:
         self.lib.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p, ctypes.c_void_p]
         self.lib.hipEventDestroy.argtypes = [ctypes.c_void_p]
         self.lib.hipEventSynchronize.argtypes = [ctypes.c_void_p]
+        self.lib.hipStreamBeginCapture.argtypes = [ctypes.c_void_p, ctypes.c_int]
+        self.lib.hipStreamEndCapture.argtypes = [ctypes.c_void_p, ctypes.POINTER(ctypes.c_void_p)]
+        self.lib.hipGraphInstantiate.argtypes = [ctypes.POINTER(ctypes.c_void_p), ctypes.c_void_p, ctypes.c_void_p,
+                                                 ctypes.c_char_p, ctypes.c_size_t]
+        self.lib.hipGraphLaunch.argtypes = [ctypes.c_void_p, ctypes.c_void_p]
+        self.lib.hipGraphExecDestroy.argtypes = [ctypes.c_void_p]
+        self.lib.hipGraphDestroy.argtypes = [ctypes.c_void_p]
 
     def event(self, timing: bool = False) -> ctypes.c_void_p:
         e = ctypes.c_void_p()
@@ -39,6 +46,37 @@ class _Hip:
         rc = self.lib.hipStreamWaitEvent(ctypes.c_void_p(stream), e, 0)
         if rc != 0:
             raise RuntimeError(f"hipStreamWaitEvent failed ({rc})")
+
+    # Stream capture into a HIP graph (relaxed mode: other threads may keep using the runtime).
+    def begin_capture(self, stream: int):
+        rc = self.lib.hipStreamBeginCapture(ctypes.c_void_p(stream), 2)
+        if rc != 0:
+            raise RuntimeError(f"hipStreamBeginCapture failed ({rc})")
+
+    def end_capture(self, stream: int) -> ctypes.c_void_p:
+        g = ctypes.c_void_p()
+        rc = self.lib.hipStreamEndCapture(ctypes.c_void_p(stream), ctypes.byref(g))
+        if rc != 0:
+            raise RuntimeError(f"hipStreamEndCapture failed ({rc})")
+        return g
+
+    def instantiate(self, graph) -> ctypes.c_void_p:
+        x = ctypes.c_void_p()
+        rc = self.lib.hipGraphInstantiate(ctypes.byref(x), graph, None, None, 0)
+        if rc != 0:
+            raise RuntimeError(f"hipGraphInstantiate failed ({rc})")
+        return x
+
+    def launch_graph(self, graph_exec, stream: int):
+        rc = self.lib.hipGraphLaunch(graph_exec, ctypes.c_void_p(stream))
+        if rc != 0:
+            raise RuntimeError(f"hipGraphLaunch failed ({rc})")
+
+    def destroy_graph(self, graph, graph_exec):
+        if graph_exec:
+            self.lib.hipGraphExecDestroy(graph_exec)
+        if graph:
+            self.lib.hipGraphDestroy(graph)
 
     def synchronize(self, e):
         rc = self.lib.hipEventSynchronize(e)

@@ -26,7 +26,7 @@ LIB = os.path.join(HERE, "libhlr.so")
 PROBE_SOURCES = ["bwprobe.hip"]
 PROBE_LIB = os.path.join(HERE, "libhlr_bwprobe.so")
 
-SOURCES = ["capi.hip", "mpzch.hip", "gather.hip", "dedup.hip", "writeback.hip", "ema.hip", "score.hip", "quantize.hip", "publish.hip", "keystore.hip", "step.hip"]
+SOURCES = ["capi.hip", "mpzch.hip", "gather.hip", "dedup.hip", "writeback.hip", "ema.hip", "score.hip", "quantize.hip", "publish.hip", "keystore.hip", "mlstep.hip", "step.hip"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 FLAGS = [

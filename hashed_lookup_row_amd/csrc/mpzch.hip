@@ -30,6 +30,8 @@
 // Counts are kept per block and folded once, never with same-address global
 // atomics (those serialise at the memory side).
 #include "hlr_common.hpp"
+#include "mlwork.hpp"
+#include "step_parts.hpp"
 
 namespace {
 using namespace hlr;
@@ -293,6 +295,8 @@ __global__ void __launch_bounds__(kThreads)
       if (old != HLR_EMPTY_ID) ++evs;
     }
     ovf += L - cnt;
+    w.bkey[t] = -1;  // the bucket-table entry is spent: leave it free for the next batch
+    w.bhead[t] = -1;
   }
   }
   if (stats) {
@@ -311,33 +315,46 @@ __global__ void __launch_bounds__(kThreads)
   }
 }
 
+// The miss-table entry of an ID is spent once its positions know their row:
+// the ID's first occurrence frees it for the next batch (the other positions
+// of the ID read only mslot and mevict, and compare mfpos with their own
+// position, which a cleared mfpos never equals).  With mz_assign freeing its
+// bucket-table entries, a batch leaves both tables as mz_init makes them.
+__device__ __forceinline__ void clear_miss_entry(const MZWork &w, int32_t e) {
+  w.mkey[e] = -1;
+  w.mfpos[e] = 0x7fffffff;
+}
+
+// Final stats from the per-block partial counts of mz_probe and mz_assign (no
+// global atomics): the work of one extra block.
+__device__ __forceinline__ void fold_stats(const MZWork &w, unsigned long long *stats, uint32_t assign_blocks) {
+  if (!stats) return;
+  __shared__ unsigned long long acc[6];
+  if (threadIdx.x < 6) acc[threadIdx.x] = 0ull;
+  __syncthreads();
+  unsigned long long loc[6] = {0, 0, 0, 0, 0, 0};
+  for (uint32_t b = threadIdx.x; b < w.probe_blocks; b += kThreads) {
+    loc[0] += w.part[2 * b];
+    loc[4] += w.part[2 * b + 1];
+  }
+  for (uint32_t b = threadIdx.x; b < assign_blocks; b += kThreads) {
+    const uint32_t *p = w.part + 2 * w.probe_blocks + 4 * b;
+    loc[1] += p[0];
+    loc[2] += p[1];
+    loc[3] += p[2];
+    loc[5] += p[3];
+  }
+  for (int k = 0; k < 6; ++k)
+    if (loc[k]) atomicAdd(&acc[k], loc[k]);
+  __syncthreads();
+  if (threadIdx.x < 6) stats[threadIdx.x] = acc[threadIdx.x];
+}
+
 __global__ void __launch_bounds__(kThreads)
     mz_resolve(int64_t n, float *values, int64_t dim, MZWork w, int64_t *__restrict__ rows,
                int64_t *__restrict__ evicted, unsigned long long *stats, uint32_t assign_blocks) {
-  if (blockIdx.x == gridDim.x - 1) {
-    // The extra last block folds the per-block partial counts of mz_probe and
-    // mz_assign into the stats (no global atomics); it has no positions.
-    if (!stats) return;
-    // Final stats from the per-block partials of mz_probe and mz_assign (no global atomics).
-    __shared__ unsigned long long acc[6];
-    if (threadIdx.x < 6) acc[threadIdx.x] = 0ull;
-    __syncthreads();
-    unsigned long long loc[6] = {0, 0, 0, 0, 0, 0};
-    for (uint32_t b = threadIdx.x; b < w.probe_blocks; b += kThreads) {
-      loc[0] += w.part[2 * b];
-      loc[4] += w.part[2 * b + 1];
-    }
-    for (uint32_t b = threadIdx.x; b < assign_blocks; b += kThreads) {
-      const uint32_t *p = w.part + 2 * w.probe_blocks + 4 * b;
-      loc[1] += p[0];
-      loc[2] += p[1];
-      loc[3] += p[2];
-      loc[5] += p[3];
-    }
-    for (int k = 0; k < 6; ++k)
-      if (loc[k]) atomicAdd(&acc[k], loc[k]);
-    __syncthreads();
-    if (threadIdx.x < 6) stats[threadIdx.x] = acc[threadIdx.x];
+  if (blockIdx.x == gridDim.x - 1) {  // the extra last block: stats; it has no positions
+    fold_stats(w, stats, assign_blocks);
     return;
   }
   const int64_t i = static_cast<int64_t>(blockIdx.x) * kThreads + threadIdx.x;
@@ -352,6 +369,7 @@ __global__ void __launch_bounds__(kThreads)
       if (evicted) evicted[i] = w.mevict[e];
       zero_fill = values != nullptr;
     }
+    if (first) clear_miss_entry(w, e);
   }
   // The whole wave zero-fills each new row: 16-byte stores, lanes along the row.
   uint64_t m = ballot(zero_fill);
@@ -364,6 +382,51 @@ __global__ void __launch_bounds__(kThreads)
     float4 *dst = reinterpret_cast<float4 *>(values) + s * v4;
     for (int64_t c = lane_id(); c < v4; c += kWave) dst[c] = z;
   }
+}
+
+// mz_resolve for the one-call Memory-Layer step (no zero-fill: the rows it
+// inserts are read as zero by the row pass), fused with the grouping of the
+// batch's positions by row (mlwork.hpp): a block resolves a tile of
+// ml::kTile positions, then groups them.  A position's row is its hit row
+// (from mz_probe) or the slot its missed ID took here; a row taken by a missed
+// ID was inserted by this batch (fresh).
+__global__ void __launch_bounds__(kThreads)
+    mz_resolve_group(int64_t n, int64_t num_rows, MZWork w, int64_t *__restrict__ rows,
+                     int64_t *__restrict__ evicted, unsigned long long *stats, uint32_t assign_blocks, ml::Work g) {
+  if (blockIdx.x == gridDim.x - 1) {  // the extra last block: stats; it has no positions
+    fold_stats(w, stats, assign_blocks);
+    return;
+  }
+  __shared__ ml::Shared sh;
+  const int64_t base = static_cast<int64_t>(blockIdx.x) * ml::kTile;
+  int32_t ent[ml::kItems];
+  int64_t r[ml::kItems];
+#pragma unroll
+  for (int k = 0; k < ml::kItems; ++k) {  // every load first
+    const int64_t i = base + k * kThreads + threadIdx.x;
+    ent[k] = i < n ? w.pent[i] : -1;
+    r[k] = i < n ? rows[i] : -1;
+  }
+  int32_t key[ml::kItems], pos[ml::kItems];
+  bool fresh[ml::kItems];
+#pragma unroll
+  for (int k = 0; k < ml::kItems; ++k) {
+    const int64_t i = base + k * kThreads + threadIdx.x;
+    fresh[k] = false;
+    if (ent[k] >= 0) {
+      const int32_t e = ent[k];
+      const int64_t slot = w.mslot[e];
+      rows[i] = slot;
+      const bool first = w.mfpos[e] == static_cast<int32_t>(i);
+      if (slot >= 0 && evicted && first) evicted[i] = w.mevict[e];
+      if (first) clear_miss_entry(w, e);
+      r[k] = slot;
+      fresh[k] = slot >= 0;
+    }
+    key[k] = (r[k] >= 0 && r[k] < num_rows) ? static_cast<int32_t>(r[k]) : -1;
+    pos[k] = i < n ? static_cast<int32_t>(i) : -1;
+  }
+  ml::group_tile(sh, g, blockIdx.x, key, fresh, pos);
 }
 
 // Zero-fill of the rows a batch inserted (positions with hit 0 and a row),
@@ -392,15 +455,15 @@ __global__ void __launch_bounds__(kThreads)
 template <int P>
 void mz_launch(int64_t *identity, int64_t *stamps, float *values, int64_t capacity, int probes, int64_t dim,
                const int64_t *ids, int64_t n, int64_t now, int insert, int64_t *rows, int8_t *hit,
-               int64_t *evicted, unsigned long long *stats, MZWork &w, hipStream_t s) {
+               int64_t *evicted, unsigned long long *stats, MZWork &w, const ml::Work *group, hipStream_t s) {
   const uint64_t nb = static_cast<uint64_t>(capacity / probes);
   const bool pow2 = (nb & (nb - 1)) == 0;
   const int gpos = grid_for(n, kThreads);
-  if (insert) {
+  if (insert && !group) {  // the step (group) keeps its tables clear from batch to batch instead
     int gi = grid_for(w.cap, kThreads);
     if (gi > 4096) gi = 4096;
     mz_init<<<gi, kThreads, 0, s>>>(w);
-  } else if (stats) {
+  } else if (!insert && stats) {
     mz_zero_stats<<<1, 64, 0, s>>>(stats);
   }
   mz_probe<P><<<gpos, kThreads, 0, s>>>(ids, n, identity, stamps, nb, pow2, probes, now, insert, rows, hit, evicted,
@@ -409,7 +472,11 @@ void mz_launch(int64_t *identity, int64_t *stamps, float *values, int64_t capaci
   int ga = grid_for(w.cap, kThreads);
   if (ga > kAssignMaxBlocks) ga = kAssignMaxBlocks;
   mz_assign<P><<<ga, kThreads, 0, s>>>(identity, stamps, probes, now, w, stats);
-  mz_resolve<<<gpos + 1, kThreads, 0, s>>>(n, values, dim, w, rows, evicted, stats, static_cast<uint32_t>(ga));
+  if (group)
+    mz_resolve_group<<<grid_for(n, ml::kTile) + 1, kThreads, 0, s>>>(n, capacity, w, rows, evicted, stats,
+                                                                     static_cast<uint32_t>(ga), *group);
+  else
+    mz_resolve<<<gpos + 1, kThreads, 0, s>>>(n, values, dim, w, rows, evicted, stats, static_cast<uint32_t>(ga));
 }
 
 }  // namespace
@@ -420,11 +487,15 @@ extern "C" size_t mpzch_lookup_or_insert_workspace_size(int64_t n, int32_t inser
   return mz_layout(n, &w, nullptr);
 }
 
-extern "C" hlr_status mpzch_lookup_or_insert(int64_t *identity, int64_t *stamps, float *values, int64_t capacity,
-                                             int32_t probes, int64_t dim, const int64_t *ids, int64_t n,
-                                             int64_t now, int32_t insert, int64_t *out_rows, int8_t *out_hit,
-                                             int64_t *out_evicted, int64_t *out_stats, void *ws, size_t ws_bytes,
-                                             hipStream_t stream) {
+namespace {
+
+// layout_n: the batch size the workspace's tables are laid out for (n, or for
+// the step, whose tables stay clear from batch to batch, the largest batch
+// the workspace was prepared for: the layout must not move between batches).
+hlr_status mpzch_run(int64_t *identity, int64_t *stamps, float *values, int64_t capacity, int32_t probes,
+                     int64_t dim, const int64_t *ids, int64_t n, int64_t now, int32_t insert, int64_t *out_rows,
+                     int8_t *out_hit, int64_t *out_evicted, int64_t *out_stats, void *ws, size_t ws_bytes,
+                     int64_t layout_n, const ml::Work *group, hipStream_t stream) {
   if (n < 0 || n > kMaxN || capacity <= 0 || probes < 1 || probes > kMaxProbes || capacity % probes != 0)
     return HLR_INVALID_ARG;
   if (insert != 0 && insert != 1) return HLR_INVALID_ARG;
@@ -439,10 +510,12 @@ extern "C" hlr_status mpzch_lookup_or_insert(int64_t *identity, int64_t *stamps,
   if (probes == 8 && !aligned(identity, 16)) return HLR_MISALIGNED;
   MZWork w{};
   if (insert) {
-    const size_t need = mz_layout(n, &w, nullptr);
+    if (layout_n < n) return HLR_INVALID_ARG;
+    const size_t need = mz_layout(layout_n, &w, nullptr);
     if (!ws || ws_bytes < need) return HLR_WORKSPACE_TOO_SMALL;
     if (!aligned(ws, 256)) return HLR_MISALIGNED;
-    mz_layout(n, &w, ws);
+    mz_layout(layout_n, &w, ws);
+    w.probe_blocks = static_cast<uint32_t>((n + kThreads - 1) / kThreads);  // this batch's probe blocks
   }
   unsigned long long *stats = reinterpret_cast<unsigned long long *>(out_stats);
   if (n == 0) {
@@ -451,11 +524,61 @@ extern "C" hlr_status mpzch_lookup_or_insert(int64_t *identity, int64_t *stamps,
   }
   if (probes == 8)
     mz_launch<8>(identity, stamps, values, capacity, probes, dim, ids, n, now, insert, out_rows, out_hit, out_evicted,
-                 stats, w, stream);
+                 stats, w, group, stream);
   else
     mz_launch<0>(identity, stamps, values, capacity, probes, dim, ids, n, now, insert, out_rows, out_hit,
-                 out_evicted, stats, w, stream);
+                 out_evicted, stats, w, group, stream);
   return launch_status();
+}
+
+}  // namespace
+
+extern "C" hlr_status mpzch_lookup_or_insert(int64_t *identity, int64_t *stamps, float *values, int64_t capacity,
+                                             int32_t probes, int64_t dim, const int64_t *ids, int64_t n,
+                                             int64_t now, int32_t insert, int64_t *out_rows, int8_t *out_hit,
+                                             int64_t *out_evicted, int64_t *out_stats, void *ws, size_t ws_bytes,
+                                             hipStream_t stream) {
+  return mpzch_run(identity, stamps, values, capacity, probes, dim, ids, n, now, insert, out_rows, out_hit,
+                   out_evicted, out_stats, ws, ws_bytes, n, nullptr, stream);
+}
+
+extern "C" size_t memory_layer_step_workspace_size(int64_t n, int64_t capacity) {
+  if (n < 0 || capacity < 0) return 0;
+  ml::Work g;
+  return ml::layout(n, capacity, &g, nullptr);
+}
+
+extern "C" hlr_status memory_layer_step_workspace_init(void *mz_ws, size_t mz_ws_bytes, void *wb_ws, size_t wb_ws_bytes,
+                                                       int64_t n, int64_t capacity, hipStream_t stream) {
+  if (n < 0 || n > kMaxN || capacity <= 0) return HLR_INVALID_ARG;
+  if ((mz_ws && !aligned(mz_ws, 256)) || (wb_ws && !aligned(wb_ws, 256))) return HLR_MISALIGNED;
+  if (mz_ws) {
+    if (mz_ws_bytes < mpzch_lookup_or_insert_workspace_size(n, 1)) return HLR_WORKSPACE_TOO_SMALL;
+    MZWork w{};
+    mz_layout(n, &w, mz_ws);
+    int gi = grid_for(w.cap, kThreads);
+    if (gi > 4096) gi = 4096;
+    mz_init<<<gi, kThreads, 0, stream>>>(w);
+  }
+  if (wb_ws) {
+    if (wb_ws_bytes < memory_layer_step_workspace_size(n, capacity)) return HLR_WORKSPACE_TOO_SMALL;
+    ml::Work g;
+    ml::layout(n, capacity, &g, wb_ws);
+    hlr_fill(g.hcount, capacity, 0u, stream);
+    hlr_fill(g.hlast, capacity, 0u, stream);
+    hlr_fill(g.hdone, capacity, 0u, stream);
+  }
+  return launch_status();
+}
+
+hlr_status hlr::ml_plan(int64_t *identity, int64_t *stamps, int64_t capacity, int32_t probes, const int64_t *ids,
+                        int64_t n, int64_t n_max, int64_t now, int64_t *out_rows, int8_t *out_hit,
+                        int64_t *out_evicted, int64_t *out_stats, void *mz_ws, size_t mz_ws_bytes, void *ws,
+                        hipStream_t stream) {
+  ml::Work g;
+  ml::layout(n_max, capacity, &g, ws);
+  return mpzch_run(identity, stamps, nullptr, capacity, probes, 0, ids, n, now, 1, out_rows, out_hit, out_evicted,
+                   out_stats, mz_ws, mz_ws_bytes, n_max, &g, stream);
 }
 
 extern "C" hlr_status mpzch_zero_inserted(float *values, int64_t capacity, int64_t dim, const int64_t *rows,

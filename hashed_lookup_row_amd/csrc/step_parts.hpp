@@ -26,4 +26,23 @@ __attribute__((visibility("hidden"))) hlr_status writeback_apply_last_fresh(floa
                                                                             int64_t n, const int8_t *hit, void *ws,
                                                                             size_t ws_bytes, hipStream_t stream);
 
+// The one-call step's ID-side half: the MPZCH lookup/insert (values = NULL)
+// whose last kernel also groups the batch's positions by row into ws
+// (memory_layer_step_workspace_size(n_max, capacity) bytes, 256-byte
+// aligned).  Both workspaces are laid out for batches of up to n_max
+// positions and must be as memory_layer_step_workspace_init(..., n_max, ...)
+// leaves them; the batch's kernels leave them so again.
+__attribute__((visibility("hidden"))) hlr_status ml_plan(int64_t *identity, int64_t *stamps, int64_t capacity,
+                                                         int32_t probes, const int64_t *ids, int64_t n, int64_t n_max,
+                                                         int64_t now, int64_t *out_rows, int8_t *out_hit,
+                                                         int64_t *out_evicted, int64_t *out_stats, void *mz_ws,
+                                                         size_t mz_ws_bytes, void *ws, hipStream_t stream);
+
+// Its row half: the gather of every position into out and the Writeback
+// (last occurrence wins, lr = 1) of every distinct row, one pass over the rows
+// through the grouping in ws.
+__attribute__((visibility("hidden"))) hlr_status ml_apply(float *values, int64_t num_rows, int64_t dim,
+                                                          const float *e, int64_t n, int64_t n_max, float *out,
+                                                          void *ws, hipStream_t stream);
+
 }  // namespace hlr

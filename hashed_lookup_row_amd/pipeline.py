@@ -38,7 +38,8 @@ from ._hip import hip
 from . import (WB_LAST_WINS, WB_SGD_SUM, HLRError, _check, _dev, _own_ws, clear_marks, ema_update_apply,
                ema_workspace_size, gather_rows, hashed_rows, load_library, mark_rows,
                mpzch_lookup_or_insert, mpzch_workspace_size, mpzch_zero_inserted, new_workspace, quantize_rows_int8,
-               writeback_apply, writeback_plan, writeback_plan_rows, writeback_workspace_size)
+               writeback_apply, writeback_plan, writeback_plan_rows, writeback_workspace_size,
+               memory_layer_step_workspace_size)
 
 
 class _Ring:
@@ -121,7 +122,7 @@ class MemoryLayerPipeline:
         wsb = writeback_workspace_size(C, D, n, WB_LAST_WINS)
         self._rows = [torch.empty(n, dtype=torch.int64, device=dev) for _ in range(depth)]
         self._hit = [torch.empty(n, dtype=torch.int8, device=dev) for _ in range(depth)]
-        self._ws = [new_workspace(dev, wsb) for _ in range(depth)]
+        self._ws = [new_workspace(dev, wsb) for _ in range(depth)]  # the call-by-call Writeback plans
         self._mz_ws = new_workspace(dev, mpzch_workspace_size(n))
         self.native = native
         if native:
@@ -129,11 +130,27 @@ class MemoryLayerPipeline:
                                 (values, "values", torch.float32)):
                 _dev(t, name, dt)
             self._fn = load_library().memory_layer_step
-            self._mz = _own_ws(self._mz_ws, mpzch_workspace_size(n))
-            self._wb = [_own_ws(w, wsb) for w in self._ws]
+            # the one-call step's row groupings, apart from the call-by-call plans: the step keeps its
+            # tables clear from batch to batch, which a call-by-call plan written there would break
+            ssb = memory_layer_step_workspace_size(n, C)
+            self._sws = [new_workspace(dev, ssb) for _ in range(depth)]
+            self._smz_ws = new_workspace(dev, mpzch_workspace_size(n))  # the step's own, laid out for n
+            self._mz = _own_ws(self._smz_ws, mpzch_workspace_size(n))
+            self._wb = [_own_ws(w, ssb) for w in self._sws]
+            self._prepare()
             self._const = (identity.data_ptr(), stamps.data_ptr(), values.data_ptr(), C, int(probes), D)
         self._tl = 0              # lookup halves enqueued (the ring's t counts row halves)
         self._ahead = deque()     # (ids, now, slot, evicted, stats) looked up ahead of their step()
+
+    def _prepare(self):
+        """Clears the one-call step's workspaces (its tables stay clear from batch to batch after that);
+        on the compute stream, which the lookup stream waits for at its first batch (restart)."""
+        init = load_library().memory_layer_step_workspace_init
+        C = self.values.shape[0]
+        mz, mzb = self._mz
+        for wb, wbb in self._wb:
+            _check(init(mz, mzb, wb, wbb, self.n, C, self.ring.cs), "memory_layer_step_workspace_init")
+        self.ring.restart()
 
     def restart(self):
         if self._ahead:
@@ -217,7 +234,7 @@ class MemoryLayerPipeline:
         gb, ge = gather_events if gather_events is not None else (None, None)
         mz, mzb = self._mz
         wb, wbb = self._wb[k]
-        rc = self._fn(*self._const, ids.data_ptr(), ids.numel(), int(now), None if e is None else e.data_ptr(),
+        rc = self._fn(*self._const, ids.data_ptr(), ids.numel(), self.n, int(now), None if e is None else e.data_ptr(),
                       self._rows[k].data_ptr(), self._hit[k].data_ptr(),
                       None if evicted is None else evicted.data_ptr(), None if stats is None else stats.data_ptr(),
                       None if out is None else out.data_ptr(), mz, mzb, wb, wbb, r.ls, r.cs, slot_free,
@@ -248,6 +265,62 @@ class MemoryLayerPipeline:
             self._call(ids, now, e, out, evicted, stats, gather_events, k, 3)
         r.t += 1
         return out, k
+
+
+class StepGraph:
+    """A fixed sequence of Memory-Layer batches enqueued once, as one HIP graph, through a native
+    MemoryLayerPipeline: the same library calls in the same two-stream schedule with lookahead
+    (batch t+1's lookup half before batch t's row half), captured from the compute stream, the
+    lookup stream joining through the ring's fork event and rejoining at the end.  Replaying the
+    graph runs the whole sequence with one host call: the eager schedule spends about 20 us of host
+    time on every cross-stream wait, and two per batch make it host-bound.
+
+    batches: list of (ids, now, e, out) per batch, in order.  (HIP events recorded inside a capture
+    cannot be timed on this runtime, so the row pass is not timed inside a graph.)  Every `now` must
+    stay valid when the
+    graph runs: a graph is meant to be replayed once for the state it was captured for, or again only
+    after that state has been restored (the MPZCH stamps must stay below every `now`)."""
+
+    def __init__(self, pipe: MemoryLayerPipeline, batches):
+        if not pipe.native:
+            raise HLRError("StepGraph needs a native MemoryLayerPipeline")
+        if pipe._ahead:
+            raise HLRError("StepGraph: finish the batches looked up ahead first")
+        r = pipe.ring
+        if not r.cs:
+            raise HLRError("StepGraph: the legacy default stream cannot be captured; build the pipeline while a "
+                           "non-default torch stream is current")
+        h = r.hip
+        self.hip, self.stream, self.pipe = h, r.cs, pipe
+        self.graph = self.exec = None
+        h.begin_capture(r.cs)
+        try:
+            pipe.restart()
+            ids0, now0 = batches[0][0], batches[0][1]
+            pipe.prefetch(ids0, now0)
+            for k, (ids, now, e, out) in enumerate(batches):
+                if k + 1 < len(batches):
+                    pipe.prefetch(batches[k + 1][0], batches[k + 1][1])
+                pipe.step(ids, now, e, out=out)
+            join = h.event()
+            h.record(join, r.ls)
+            h.wait(r.cs, join)
+        finally:
+            self.graph = h.end_capture(r.cs)
+        self.exec = h.instantiate(self.graph)
+        pipe.restart()
+
+    def replay(self):
+        """Runs the sequence on the compute stream; the pipeline's lookup stream is then ordered after it
+        (and its ring restarted), so eager batches may follow."""
+        self.hip.launch_graph(self.exec, self.stream)
+        self.pipe.restart()
+
+    def __del__(self):
+        try:
+            self.hip.destroy_graph(self.graph, self.exec)
+        except Exception:
+            pass
 
 
 class HashedTablesPipeline:

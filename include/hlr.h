@@ -386,38 +386,45 @@ hlr_status hashed_rows(const int64_t *ids, int64_t n, int64_t num_rows, int64_t 
  * compute streams of [MTGR] sec. 3.5.
  *  Enqueues, in this order:
  *   lookup stream:  wait slot_free (if given);
- *                   mpzch_lookup_or_insert(values = NULL, insert = 1);
- *                   record looked_up;
- *                   writeback_plan(LAST_WINS) over out_rows into wb_ws;
- *                   record planned.
- *   compute stream: wait looked_up;
- *                   record gather_begin (if given); gather_rows into out;
- *                   record gather_end (if given); wait planned;
- *                   writeback_apply(LAST_WINS, lr = 1) with e;
- *                   record slot_done (if given).
- *   (A compute half enqueued alone, halves = 2, waits once, on planned,
- *   before the gather: planned follows looked_up on the lookup stream.)
- *  The rows the lookup inserts are not zero-filled in memory first (no
- *  mpzch_zero_inserted): every position that refers to such a row has
- *  out_hit 0 (a row the batch uses is never evicted by it), so the gather
- *  reads zeros for positions with out_hit 0 and the apply takes their rows as
- *  zero, and every inserted row is then written by the apply.
- *  The results equal those calls made one after another on one stream:
+ *                   MPZCH lookup/insert (as mpzch_lookup_or_insert with
+ *                   values = NULL, insert = 1), then the grouping of the
+ *                   batch's positions by row into wb_ws;
+ *                   record looked_up; record planned.
+ *   compute stream: wait planned;
+ *                   record gather_begin (if given);
+ *                   one pass over the batch's distinct rows: each row is read
+ *                   once, written to out at every position that holds it
+ *                   (the gather), then takes its Writeback from its last
+ *                   position;
+ *                   record gather_end (if given); record slot_done (if given).
+ *  The rows the lookup inserts are not zero-filled in memory first: a row the
+ *  batch inserted is read as the zero vector (a new ID never reads an evicted
+ *  ID's vector) and is then written by its Writeback.
+ *  The results equal mpzch_lookup_or_insert, gather_rows and
+ *  writeback_rows(LAST_WINS) made one after another on one stream:
  *  identity/stamps/values updated, out_rows/out_hit/out_evicted/out_stats as
  *  mpzch_lookup_or_insert, out[n*dim] the gathered rows (read before the
  *  Writeback), values[r] <- fl(M - fl(M - e[last position of r])).
- *  Arguments as the calls above; capacity = the table's row count.  Events are
- *  the caller's (hipEventCreateWithFlags; timing needed only for the gather
- *  pair); looked_up and planned are required, the others nullable.  mz_ws / wb_ws: workspaces of
- *  mpzch_lookup_or_insert_workspace_size(n, 1) and
- *  writeback_rows_workspace_size(capacity, dim, n, HLR_WB_LAST_WINS) bytes;
- *  out_rows, out_hit and wb_ws stay in use until slot_done.
+ *  Arguments as the calls above; capacity = the table's row count, below
+ *  2^31 - 1; dim <= 1024.  Events are the caller's (hipEventCreateWithFlags;
+ *  timing needed only for the gather pair); looked_up and planned are
+ *  required, the others nullable.  n_max >= n: the largest batch the
+ *  workspaces serve (the same for every batch that uses them).  mz_ws: a
+ *  workspace of mpzch_lookup_or_insert_workspace_size(n_max, 1) bytes; wb_ws:
+ *  one of memory_layer_step_workspace_size(n_max, capacity) bytes (both
+ *  256-byte aligned).  Unlike the other entry points' scratch, these two keep
+ *  their tables clear from batch to batch (no clearing kernel per batch):
+ *  prepare each with memory_layer_step_workspace_init(..., n_max, capacity,
+ *  ...) before its first batch; a batch whose two halves both ran leaves them
+ *  prepared.  out_rows, out_hit and wb_ws
+ *  stay in use until slot_done.
  *  halves: 1 = the lookup-stream half only, 2 = the compute-stream half
  *  only, 3 = both.  A batch's lookup half must be enqueued before its compute
- *  half (the compute half waits on looked_up and planned as recorded by the
- *  most recent lookup half); enqueueing the lookup half of batch t+1 before
- *  the compute half of batch t (lookahead) is allowed and gives the same
- *  results, since the compute stream keeps the row traffic in batch order.
+ *  half (the compute half waits on planned as recorded by the most recent
+ *  lookup half); enqueueing the lookup half of batch t+1 before the compute
+ *  half of batch t (lookahead) is allowed and gives the same results, since
+ *  the compute stream keeps the row traffic in batch order, provided each
+ *  batch in flight has its own out_rows, out_hit, wb_ws and events.
  *  Pointers a half does not use may be NULL there (the lookup half does not
  *  read e or out, the compute half does not read identity, stamps or ids);
  *  the buffers of a batch (out_rows, out_hit, wb_ws) and its events must be
@@ -425,8 +432,20 @@ hlr_status hashed_rows(const int64_t *ids, int64_t n, int64_t num_rows, int64_t 
  *  Host-checkable errors return before anything is enqueued; a HIP error
  *  from a later call returns HLR_HIP_ERROR with the batch partly enqueued.
  * --------------------------------------------------------------------- */
+size_t memory_layer_step_workspace_size(int64_t n, int64_t capacity);
+
+/* Puts a pair of workspaces for memory_layer_step into the state every batch
+ * expects on entry and leaves behind (its tables clear), laid out for batches
+ * of up to n positions (memory_layer_step's n_max): mz_ws of
+ * mpzch_lookup_or_insert_workspace_size(n, 1) bytes and wb_ws of
+ * memory_layer_step_workspace_size(n, capacity) bytes, either nullable.  Call
+ * it once for every workspace before its first batch, and again after a batch
+ * whose halves were not both enqueued or that returned an error.  Enqueued on
+ * stream. */
+hlr_status memory_layer_step_workspace_init(void *mz_ws, size_t mz_ws_bytes, void *wb_ws, size_t wb_ws_bytes,
+                                            int64_t n, int64_t capacity, hipStream_t stream);
 hlr_status memory_layer_step(int64_t *identity, int64_t *stamps, float *values, int64_t capacity, int32_t probes,
-                             int64_t dim, const int64_t *ids, int64_t n, int64_t now, const float *e,
+                             int64_t dim, const int64_t *ids, int64_t n, int64_t n_max, int64_t now, const float *e,
                              int64_t *out_rows, int8_t *out_hit, int64_t *out_evicted, int64_t *out_stats,
                              float *out, void *mz_ws, size_t mz_ws_bytes, void *wb_ws, size_t wb_ws_bytes,
                              hipStream_t lookup, hipStream_t compute, hipEvent_t slot_free, hipEvent_t looked_up,

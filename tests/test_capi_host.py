@@ -250,15 +250,16 @@ def test_memory_layer_step_argument_errors(lib):
     s = None
     n, C, D, P = 1000, 4096, 64, 8
     mzb = lib.mpzch_lookup_or_insert_workspace_size(n, 1)
-    wbb = lib.writeback_rows_workspace_size(C, D, n, 0)
+    wbb = lib.memory_layer_step_workspace_size(n, C)
 
-    def call(cap=C, probes=P, dim=D, n=n, values=P16, ids=P16, mzb=mzb, wbb=wbb, looked=P16, planned=P16,
+    def call(cap=C, probes=P, dim=D, n=n, n_max=n, values=P16, ids=P16, mzb=mzb, wbb=wbb, looked=P16, planned=P16,
              gb=None, ge=None, halves=3):
-        return lib.memory_layer_step(P16, P16, values, cap, probes, dim, ids, n, 5, P16, P16, P16, None, None,
-                                     P16, P16, mzb, P16, wbb, s, s, None, looked, planned, gb, ge, None, halves)
+        return lib.memory_layer_step(P16, P16, values, cap, probes, dim, ids, n, n_max, 5, P16, P16, P16, None,
+                                     None, P16, P16, mzb, P16, wbb, s, s, None, looked, planned, gb, ge, None, halves)
     assert call(cap=4095) == INVALID                 # capacity % probes
     assert call(probes=0) == INVALID
     assert call(n=-1) == INVALID
+    assert call(n=n + 1) == INVALID                  # a batch larger than the workspaces serve (n_max)
     assert call(dim=6) == DIM
     assert call(values=None) == INVALID
     assert call(ids=None) == INVALID

@@ -234,6 +234,105 @@ def test_memory_layer_pipeline(dev, depth, native, lookahead):
     assert bits_equal(to_np(values), o.values)
 
 
+@pytest.mark.parametrize("C,P,D,n,depth", [(64, 8, 4, 1, 2), (64, 8, 12, 1023, 2), (256, 4, 1024, 1025, 3),
+                                            (2048, 8, 512, 3000, 3), (96, 32, 64, 5000, 2)])
+def test_memory_layer_step_edge_cases(dev, C, P, D, n, depth):
+    """The one-call step (one pass over the batch's rows) against the oracle on edge cases: stale
+    rows (an insert must read as zero, not as the evicted ID's vector), invalid IDs (-1), buckets
+    overflowing (every slot pinned: row -1, zero vector, no Writeback), hot IDs spread over many
+    1024-position tiles, ragged batch sizes (1, 1023, 1025, ...) and dims of 1, 3 and 256 16-byte
+    units, with lookahead and batches of different sizes."""
+    g = np.random.default_rng(C + n + D)
+    steps = 6
+    values_np = g.standard_normal((C, D)).astype(np.float32)
+    identity = torch.full((C,), -1, dtype=torch.int64, device=dev)
+    stamps = torch.full((C,), -1, dtype=torch.int64, device=dev)
+    values = torch.from_numpy(values_np.copy()).to(dev)
+    o = oracle.MPZCHTable(C, P, D)
+    o.values = values_np.copy()
+    universe = g.choice(1 << 40, size=4 * C, replace=False).astype(np.int64)
+    sizes = [n if t % 2 == 0 else max(1, n // 2 + 1) for t in range(steps)]
+    ids_np = []
+    for t in range(steps):
+        r = np.minimum(synth.zipf_ranks(g, universe.size, 1.2, sizes[t]), universe.size - 1)
+        x = universe[r]
+        x[g.random(sizes[t]) < 0.02] = -1
+        ids_np.append(x.astype(np.int64))
+    ids = [torch.from_numpy(x).to(dev) for x in ids_np]
+    es = [torch.from_numpy(g.standard_normal((sz, D)).astype(np.float32)).to(dev) for sz in sizes]
+    outs = [torch.empty((sz, D), dtype=torch.float32, device=dev) for sz in sizes]
+    evs = [torch.empty(sz, dtype=torch.int64, device=dev) for sz in sizes]
+    sts = [torch.zeros(6, dtype=torch.int64, device=dev) for _ in sizes]
+    pipe = pipeline.MemoryLayerPipeline(identity, stamps, values, P, n, depth=depth)
+    pipe.prefetch(ids[0], 1, evicted=evs[0], stats=sts[0])
+    for t in range(steps):
+        if t + 1 < steps:
+            pipe.prefetch(ids[t + 1], t + 2, evicted=evs[t + 1], stats=sts[t + 1])
+        pipe.step(ids[t], t + 1, es[t], out=outs[t], evicted=evs[t], stats=sts[t])
+    overflows = 0
+    for t in range(steps):
+        orows, ohit, oev, ost = o.step(ids_np[t], t + 1)
+        assert bits_equal(to_np(outs[t]), o.gather(orows)), f"gather step {t}"
+        o.writeback(orows, to_np(es[t]))
+        assert np.array_equal(to_np(evs[t]), oev), f"evicted step {t}"
+        assert np.array_equal(to_np(sts[t])[:5], ost), f"stats step {t}"
+        overflows += int(ost[3])
+    assert np.array_equal(to_np(identity), o.identity)
+    assert np.array_equal(to_np(stamps), o.stamps)
+    assert bits_equal(to_np(values), o.values)
+    if C <= 256 and n > 100:
+        assert overflows > 0  # the overflow path is exercised
+
+
+def test_step_graph_replays_match_oracle(dev):
+    """A sequence of batches captured as one HIP graph (StepGraph) and replayed three times, each
+    time from the same restored state with eager work and synchronisation in between: every replay's
+    gathered rows, evicted IDs, stats and final state equal the oracle's sequential result bit for bit.
+    Eager batches then continue after the last replay."""
+    cfg = synth.scaled_memory_layer(capacity=16_384, universe=120_000, batch=8_192, steps=6)
+    C, P, D, n = cfg.capacity, cfg.probes, cfg.dim, cfg.batch
+    identity, stamps, o, base = prefilled_pair(dev, cfg)
+    values = torch.zeros((C, D), dtype=torch.float32, device=dev)
+    ids_np = synth.mpzch_stream(cfg, cfg.steps + 1)
+    e_np = [synth.normal_rows_np(n, D, cfg.e_std, 2, t) for t in range(1, cfg.steps + 2)]
+    ids = [torch.from_numpy(x).to(dev) for x in ids_np]
+    es = [torch.from_numpy(x).to(dev) for x in e_np]
+    steps = cfg.steps
+    expect = []
+    for t in range(steps):
+        orows, ohit, oev, ost = o.step(ids_np[t], base + t + 1)
+        expect.append(o.gather(orows))
+        o.writeback(orows, e_np[t])
+    side = torch.cuda.Stream(dev)
+    side.wait_stream(torch.cuda.current_stream(dev))
+    with torch.cuda.stream(side):
+        snap = (identity.clone(), stamps.clone(), values.clone())
+        outs = [torch.empty((n, D), dtype=torch.float32, device=dev) for _ in range(steps)]
+        pipe = pipeline.MemoryLayerPipeline(identity, stamps, values, P, n, depth=3)
+        graph = pipeline.StepGraph(pipe, [(ids[t], base + t + 1, es[t], outs[t]) for t in range(steps)])
+        for rep in range(3):
+            identity.copy_(snap[0])
+            stamps.copy_(snap[1])
+            values.copy_(snap[2])
+            for x in outs:
+                x.fill_(float("nan"))
+            torch.cuda.synchronize()
+            graph.replay()
+            torch.cuda.synchronize()
+            for t in range(steps):
+                assert bits_equal(to_np(outs[t]), expect[t]), f"replay {rep} gather step {t}"
+            assert np.array_equal(to_np(identity), o.identity), f"replay {rep} identity"
+            assert np.array_equal(to_np(stamps), o.stamps), f"replay {rep} stamps"
+            assert bits_equal(to_np(values), o.values), f"replay {rep} values"
+        # an eager batch after the last replay
+        out = pipe.step(ids[steps], base + steps + 1, es[steps])[0]
+        torch.cuda.synchronize()
+    orows, _, _, _ = o.step(ids_np[steps], base + steps + 1)
+    assert bits_equal(to_np(out), o.gather(orows))
+    o.writeback(orows, e_np[steps])
+    assert bits_equal(to_np(values), o.values)
+
+
 def test_prefetch_limits(dev):
     """Lookahead is bounded by the ring depth and must be consumed in order (host-side errors)."""
     C, P, D, n = 1024, 8, 16, 64
