@@ -77,6 +77,8 @@ def load_library():
             "memory_layer_step": (i32, [p, p, p, i64, i32, i64, p, i64, i64, i64, p, p, p, p, p, p, p, sz, p, sz,
                                         p, p, p, p, p, p, p, p, i32]),
             "memory_layer_step_workspace_size": (sz, [i64, i64]),
+            "mpzch_lookup_or_insert_static_max_n": (i64, []),
+            "mpzch_lookup_or_insert_static": (i32, [p, p, p, i64, i32, i64, p, i64, i64, i32, p, p, p, p, p]),
             "memory_layer_step_workspace_init": (i32, [p, sz, p, sz, i64, i64, p]),
         }
         for name, (res, args) in sig.items():
@@ -94,7 +96,8 @@ def exported_symbols():
             "hashed_rows", "mpzch_zero_inserted", "writeback_plan", "writeback_apply", "ema_update_plan",
             "ema_update_apply", "writeback_plan_rows", "quantize_rows_int8", "mark_rows", "clear_marks",
             "dks_workspace_size", "dks_lookup_or_insert", "dks_rehash", "memory_layer_step",
-            "memory_layer_step_workspace_size", "memory_layer_step_workspace_init", "ema_update_plan_subset", "ema_update_apply_batch",
+            "memory_layer_step_workspace_size", "memory_layer_step_workspace_init",
+            "mpzch_lookup_or_insert_static_max_n", "mpzch_lookup_or_insert_static", "ema_update_plan_subset", "ema_update_apply_batch",
             "writeback_apply_batch"]
 
 

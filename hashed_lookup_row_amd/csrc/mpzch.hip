@@ -29,6 +29,8 @@
 //              per-block partial counts of probe and assign into the stats
 // Counts are kept per block and folded once, never with same-address global
 // atomics (those serialise at the memory side).
+#include <mutex>
+
 #include "hlr_common.hpp"
 #include "mlwork.hpp"
 #include "step_parts.hpp"
@@ -540,6 +542,59 @@ extern "C" hlr_status mpzch_lookup_or_insert(int64_t *identity, int64_t *stamps,
                                              hipStream_t stream) {
   return mpzch_run(identity, stamps, values, capacity, probes, dim, ids, n, now, insert, out_rows, out_hit,
                    out_evicted, out_stats, ws, ws_bytes, n, nullptr, stream);
+}
+
+// ---------------------------------------------------------------------------
+// The same call without a caller workspace, for callers that cannot allocate
+// device memory (code under graph capture, serving loops, harnesses that
+// forbid allocation): the scratch is this file-scope device array, one per
+// GPU for the life of the process.  Host code must not pass `scratch` itself
+// to a kernel (in host code it names a host-side stand-in): its device address
+// comes from hipGetSymbolAddress, once per device, with that device current.
+namespace {
+
+constexpr int64_t kStaticMaxN = 262144;         // largest batch of the allocation-free call
+constexpr size_t kStaticBytes = size_t(24) << 20;  // >= mpzch_lookup_or_insert_workspace_size(kStaticMaxN, 1)
+constexpr int kStaticMaxDevices = 64;
+
+static __device__ __align__(256) char scratch[kStaticBytes];
+
+std::mutex g_scratch_mu;
+void *g_scratch_ptr[kStaticMaxDevices];
+
+// This device's address of `scratch` (nullptr on a HIP error).
+void *scratch_on_current_device() {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kStaticMaxDevices) return nullptr;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void *p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) return nullptr;
+    g_scratch_ptr[dev] = p;
+  }
+  return g_scratch_ptr[dev];
+}
+
+}  // namespace
+
+extern "C" int64_t mpzch_lookup_or_insert_static_max_n(void) { return kStaticMaxN; }
+
+extern "C" hlr_status mpzch_lookup_or_insert_static(int64_t *identity, int64_t *stamps, float *values,
+                                                    int64_t capacity, int32_t probes, int64_t dim,
+                                                    const int64_t *ids, int64_t n, int64_t now, int32_t insert,
+                                                    int64_t *out_rows, int8_t *out_hit, int64_t *out_evicted,
+                                                    int64_t *out_stats, hipStream_t stream) {
+  if (n < 0 || n > kStaticMaxN) return HLR_INVALID_ARG;  // beyond the array's batch size
+  const size_t need = mpzch_lookup_or_insert_workspace_size(n, insert);
+  if (need > kStaticBytes) return HLR_WORKSPACE_TOO_SMALL;
+  void *ws = nullptr;
+  if (need > 0) {
+    ws = scratch_on_current_device();
+    if (!ws) return HLR_HIP_ERROR;
+  }
+  // mz_init clears every table the batch uses first, so the last call's contents do not matter
+  return mpzch_run(identity, stamps, values, capacity, probes, dim, ids, n, now, insert, out_rows, out_hit,
+                   out_evicted, out_stats, ws, need > 0 ? kStaticBytes : 0, n, nullptr, stream);
 }
 
 extern "C" size_t memory_layer_step_workspace_size(int64_t n, int64_t capacity) {

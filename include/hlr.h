@@ -106,6 +106,23 @@ hlr_status mpzch_lookup_or_insert(int64_t *identity, int64_t *stamps, float *val
                                   int32_t insert, int64_t *out_rows, int8_t *out_hit, int64_t *out_evicted,
                                   int64_t *out_stats, void *ws, size_t ws_bytes, hipStream_t stream);
 
+/* mpzch_lookup_or_insert without a workspace argument, for callers that
+ * cannot allocate device memory (code under HIP graph capture, tight serving
+ * loops, harnesses that forbid allocation).  Same arguments, semantics and
+ * errors as mpzch_lookup_or_insert; the scratch is a device array inside the
+ * library (24 MiB per GPU it runs on, held until the process ends), so the call
+ * allocates nothing.  n must be at most mpzch_lookup_or_insert_static_max_n()
+ * (262,144): larger batches return HLR_INVALID_ARG before anything is
+ * enqueued.  Every call on one GPU shares that GPU's array: calls that may
+ * overlap on one GPU (different streams, or different host threads) race and
+ * must be ordered by the caller.  A HIP error while locating the array returns
+ * HLR_HIP_ERROR. */
+int64_t mpzch_lookup_or_insert_static_max_n(void);
+hlr_status mpzch_lookup_or_insert_static(int64_t *identity, int64_t *stamps, float *values, int64_t capacity,
+                                         int32_t probes, int64_t dim, const int64_t *ids, int64_t n, int64_t now,
+                                         int32_t insert, int64_t *out_rows, int8_t *out_hit, int64_t *out_evicted,
+                                         int64_t *out_stats, hipStream_t stream);
+
 /* Zero-fill of the rows a batch inserted, split from the lookup: a lookup
  * run with values == NULL (for instance on its own stream, so it can overlap
  * the previous batch's row traffic) leaves the new rows as they were; this

@@ -270,6 +270,17 @@ def test_memory_layer_step_argument_errors(lib):
     assert call(halves=0) == INVALID and call(halves=4) == INVALID
 
 
+def test_static_mpzch_rejects_batches_beyond_its_array(lib):
+    """The allocation-free MPZCH call refuses a batch larger than its device array serves, before
+    anything is enqueued (no device is touched here)."""
+    m = lib.mpzch_lookup_or_insert_static_max_n()
+    assert m == 262144
+    args = (P16, P16, None, 4096, 8, 64, P16)
+    tail = (7, 1, P16, P16, None, None, None)
+    assert lib.mpzch_lookup_or_insert_static(*args, m + 1, *tail) == INVALID
+    assert lib.mpzch_lookup_or_insert_static(*args, -1, *tail) == INVALID
+
+
 def test_score_dedup_hashed_argument_errors(lib):
     s = None
     assert lib.gather_dequant_score(P16, P16, P16, 10, 520, P16, 2, 3, P16, P16, s) == DIM
