@@ -21,6 +21,8 @@ class _Hip:
         self.lib.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p, ctypes.c_void_p]
         self.lib.hipEventDestroy.argtypes = [ctypes.c_void_p]
         self.lib.hipEventSynchronize.argtypes = [ctypes.c_void_p]
+        self.lib.hipMemcpyAsync.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_size_t, ctypes.c_int,
+                                            ctypes.c_void_p]
         self.lib.hipStreamBeginCapture.argtypes = [ctypes.c_void_p, ctypes.c_int]
         self.lib.hipStreamEndCapture.argtypes = [ctypes.c_void_p, ctypes.POINTER(ctypes.c_void_p)]
         self.lib.hipGraphInstantiate.argtypes = [ctypes.POINTER(ctypes.c_void_p), ctypes.c_void_p, ctypes.c_void_p,
@@ -46,6 +48,11 @@ class _Hip:
         rc = self.lib.hipStreamWaitEvent(ctypes.c_void_p(stream), e, 0)
         if rc != 0:
             raise RuntimeError(f"hipStreamWaitEvent failed ({rc})")
+
+    def copy_d2d(self, dst: int, src: int, nbytes: int, stream: int):
+        rc = self.lib.hipMemcpyAsync(ctypes.c_void_p(dst), ctypes.c_void_p(src), nbytes, 3, ctypes.c_void_p(stream))
+        if rc != 0:
+            raise RuntimeError(f"hipMemcpyAsync failed ({rc})")
 
     # Stream capture into a HIP graph (relaxed mode: other threads may keep using the runtime).
     def begin_capture(self, stream: int):

@@ -165,7 +165,8 @@ class MemoryLayerPipeline:
         return self._hit[k]
 
     def prefetch(self, ids, now, evicted=None, stats=None):
-        """Enqueues the ID-side half (lookup/insert, Writeback plan) of a later batch now."""
+        """Enqueues the ID-side half (lookup/insert, grouping by row) of a later batch now; returns its ring
+        slot (rows(k), hit(k) hold the batch's rows and hit mask until its row half is done)."""
         if not self.native:
             raise HLRError("prefetch() needs native=True")
         r = self.ring
@@ -175,6 +176,7 @@ class MemoryLayerPipeline:
         k = self._tl % r.depth
         self._call(ids, now, None, None, evicted, stats, None, k, 1)
         self._ahead.append((ids, int(now), k, evicted, stats))
+        return k
 
     def step(self, ids, now, e, out=None, evicted=None, stats=None, mark=None, publisher=None, gather_events=None):
         """mark: optional callable, called with 0 just before and 1 just after the gather is
@@ -275,9 +277,12 @@ class StepGraph:
     graph runs the whole sequence with one host call: the eager schedule spends about 20 us of host
     time on every cross-stream wait, and two per batch make it host-bound.
 
-    batches: list of (ids, now, e, out) per batch, in order.  (HIP events recorded inside a capture
-    cannot be timed on this runtime, so the row pass is not timed inside a graph.)  Every `now` must
-    stay valid when the
+    batches: list of (ids, now, e, out) per batch, in order, optionally followed by (evicted, stats,
+    rows, hit): int64[n] evicted IDs and int64[6] stats written by the lookup as in
+    mpzch_lookup_or_insert, and int64[n] rows / int8[n] hit buffers that receive copies of the batch's
+    rows and hit mask (copied on the lookup stream while the ring slot still holds them).  (HIP events
+    recorded inside a capture cannot be timed on this runtime, so the row pass is not timed inside a
+    graph.)  Every `now` must stay valid when the
     graph runs: a graph is meant to be replayed once for the state it was captured for, or again only
     after that state has been restored (the MPZCH stamps must stay below every `now`)."""
 
@@ -296,12 +301,22 @@ class StepGraph:
         h.begin_capture(r.cs)
         try:
             pipe.restart()
-            ids0, now0 = batches[0][0], batches[0][1]
-            pipe.prefetch(ids0, now0)
-            for k, (ids, now, e, out) in enumerate(batches):
-                if k + 1 < len(batches):
-                    pipe.prefetch(batches[k + 1][0], batches[k + 1][1])
-                pipe.step(ids, now, e, out=out)
+            bs = [tuple(b) + (None,) * (8 - len(b)) for b in batches]
+
+            def look(b):
+                ids, now, _, _, ev, st, rows_out, hit_out = b
+                k = pipe.prefetch(ids, now, evicted=ev, stats=st)
+                n = ids.numel()
+                if rows_out is not None:
+                    h.copy_d2d(rows_out.data_ptr(), pipe.rows(k).data_ptr(), 8 * n, r.ls)
+                if hit_out is not None:
+                    h.copy_d2d(hit_out.data_ptr(), pipe.hit(k).data_ptr(), n, r.ls)
+
+            look(bs[0])
+            for k, (ids, now, e, out, ev, st, _, _) in enumerate(bs):
+                if k + 1 < len(bs):
+                    look(bs[k + 1])
+                pipe.step(ids, now, e, out=out, evicted=ev, stats=st)
             join = h.event()
             h.record(join, r.ls)
             h.wait(r.cs, join)
