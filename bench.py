@@ -79,11 +79,17 @@ def parse():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=200)
-    ap.add_argument("--depth", type=int, default=3, help="ring depth of the two-stream schedule")
-    ap.add_argument("--eager", dest="graph", action="store_false",
-                    help="enqueue the timed Memory-Layer batches call by call instead of as one HIP graph")
+    ap.add_argument("--depth", type=int, default=3,
+                    help="ring depth of the two-stream schedule (grouped: at least (ahead + 2) * group)")
+    ap.add_argument("--schedule", default="graph", choices=["grouped", "graph", "eager"],
+                    help="Memory Layer: grouped = the lookup halves of a group of batches back to back, one "
+                         "cross-stream wait per stream per group (MemoryLayerPipeline.run); graph = batch by "
+                         "batch with lookahead, captured as one HIP graph and replayed; eager = batch by batch "
+                         "with lookahead, call by call")
+    ap.add_argument("--group", type=int, default=4, help="grouped schedule: batches per group")
+    ap.add_argument("--ahead", type=int, default=1, help="grouped schedule: groups the lookups run ahead")
     ap.add_argument("--no-lookahead", dest="lookahead", action="store_false",
-                    help="enqueue each batch's lookup with its own row traffic instead of one batch ahead")
+                    help="eager: enqueue each batch's lookup with its own row traffic instead of one batch ahead")
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--e-pool", type=int, default=16, help="distinct e batches cycled through")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -161,7 +167,8 @@ def main():
     R = D * 4
 
     # ---------------------------------------------------------------- inputs
-    # step t uses stream[t]: W warm-up steps, K timed two-stream steps, K timed one-stream steps, one stats step
+    # step t uses stream[t]: W warm-up steps, K timed headline steps, K steps timed by events (roofline),
+    # K one-stream steps, one stats step
     t0 = time.time()
     prefill = synth.prefill_batches(cfg)
     stream, fc = [], 0
@@ -195,7 +202,12 @@ def main():
     side.wait_stream(torch.cuda.current_stream(dev))
     torch.cuda.set_stream(side)
     cur = torch.cuda.current_stream(dev).cuda_stream
-    pipe = MemoryLayerPipeline(identity, stamps, values, P, n, depth=args.depth)
+    G, A = args.group, args.ahead
+    depth = args.depth
+    if args.schedule == "grouped":  # a multiple of the group, at least (ahead + 2) groups
+        depth = max(depth, (A + 2) * G)
+        depth = (depth + G - 1) // G * G
+    pipe = MemoryLayerPipeline(identity, stamps, values, P, n, depth=depth)
 
     def piped_step(t, evs=None, ahead=None):
         # one library call per half batch (memory_layer_step): the lookup half of batch `ahead` (the next
@@ -221,22 +233,27 @@ def main():
     # the lookup state before the first batch, for an untimed replay of the same lookups after the timed
     # regions (it gives each batch's insert count: rows the gather reads as zero instead of loading)
     id_snap, st_snap = identity.clone(), stamps.clone()
-    la = args.lookahead
-    if args.graph and not la:
-        raise SystemExit("--graph needs the lookahead schedule")
+    la = args.lookahead or args.schedule != "eager"
 
-    def two_stream(first, timed_evs):
-        """Batches first .. first+K-1 in the two-stream schedule, timed on the compute stream; returns
+    def two_stream(first, timed_evs, mode):
+        """Batches first .. first+K-1 in the two-stream schedule `mode`, timed on the compute stream; returns
         (total seconds, host enqueue seconds, wall seconds)."""
         start, stop = timer.event(), timer.event()
-        if args.graph:
-            batches = [(ids_dev[first + k], base_now + 1 + first + k, e_pool[(first + k) % npool], out)
-                       for k in range(K)]
+        batches = [(ids_dev[first + k], base_now + 1 + first + k, e_pool[(first + k) % npool], out)
+                   for k in range(K)]
+        if mode == "graph":
             graph = StepGraph(pipe, batches)  # captured, not run
             torch.cuda.synchronize()
             wall0 = time.perf_counter()
             timer.record(start, cur)
             graph.replay()
+            timer.record(stop, cur)
+        elif mode == "grouped":
+            gevs = [timed_evs.get(k) for k in range(K)] if timed_evs else None
+            torch.cuda.synchronize()
+            wall0 = time.perf_counter()
+            timer.record(start, cur)
+            pipe.run(batches, group=G, ahead=A, gather_events=gevs)
             timer.record(stop, cur)
         else:
             torch.cuda.synchronize()
@@ -260,26 +277,20 @@ def main():
         piped_step(t, ahead=t + 1 if la and t + 1 < W else None)
     torch.cuda.synchronize()
 
-    # the headline: batches W .. W+K-1 in the two-stream schedule with lookahead.  The row pass is timed with
-    # HIP events on the compute stream on every EV_SAMPLE-th batch of the call-by-call schedule (events
-    # inside a captured graph cannot be timed on this runtime): with --graph, over the next K batches, which
-    # are reported beside the headline (there too batch t+1's lookup runs beside batch t's row pass)
-    evs = {k: [timer.event() for _ in range(2)] for k in range(0, K, EV_SAMPLE)}
-    eager = None
-    if args.graph:
-        total_s, enqueue, wall = two_stream(W, None)
-        args.graph = False
-        e_total, e_enqueue, _ = two_stream(W + K, evs)
-        args.graph = True
-        eager = {"ms_per_step": e_total / K * 1e3, "rows_per_s": n * K / e_total,
+    # the headline: batches W .. W+K-1 in the chosen two-stream schedule, no events inside.  The row pass is
+    # then timed with HIP events on the compute stream around every EV_SAMPLE-th batch of the next K batches,
+    # in the same schedule (grouped, eager) or, for the graph (events inside a captured graph cannot be timed
+    # on this runtime), call by call; that leg is reported beside the headline
+    evs = {k: [timer.event() for _ in range(2)] for k in range(0, K, EV_SAMPLE_ML)}
+    total_s, enqueue, wall = two_stream(W, None, args.schedule)
+    ev_mode = "eager" if args.schedule == "graph" else args.schedule
+    e_total, e_enqueue, _ = two_stream(W + K, evs, ev_mode)
+    timed_leg = {"schedule": ev_mode, "ms_per_step": e_total / K * 1e3, "rows_per_s": n * K / e_total,
                  "host_enqueue_us_per_step": e_enqueue / K * 1e6}
-        ev_first = W + K
-    else:
-        total_s, enqueue, wall = two_stream(W, evs)
-        ev_first = W
+    ev_first = W + K
     gather_s = np.array([timer.elapsed_s(e[0], e[1]) for e in evs.values()])
     gather_steps = np.array(sorted(evs.keys()))
-    off = K if args.graph else 0
+    off = K
 
     # the same step as three calls on one stream, over the next K batches (reported beside the headline)
     sevs = {k: [timer.event() for _ in range(4)] for k in range(K)} if args.op_events else {}
@@ -355,11 +366,14 @@ def main():
             "schedule": ("two streams: lookup (MPZCH without values, whose last kernel groups the batch's positions "
                          "by row) beside compute (one pass over the batch's rows: gather and Writeback; rows the "
                          "lookup inserts read as zero), one library call per half batch; "
-                         + (f"lookahead: batch t+1's lookup is enqueued before batch t's row traffic, ring depth "
-                            f"{args.depth}" if la else f"batch t's lookup with its own row traffic, ring depth "
-                                                       f"{args.depth}")
-                         + ("; the K timed batches captured (untimed) as one HIP graph of those calls and replayed "
-                            "once" if args.graph else "; enqueued call by call")),
+                         + (f"grouped: the lookup halves of {G} batches back to back on the lookup stream, one "
+                            f"event after them; the compute stream waits once per group, then runs the group's "
+                            f"row passes back to back; lookups {A} group(s) ahead, ring depth {depth}; enqueued "
+                            f"call by call (MemoryLayerPipeline.run)" if args.schedule == "grouped" else
+                            (f"lookahead: batch t+1's lookup is enqueued before batch t's row traffic, ring depth "
+                             f"{depth}" if la else f"batch t's lookup with its own row traffic, ring depth {depth}")
+                            + ("; the K timed batches captured (untimed) as one HIP graph of those calls and "
+                               "replayed once" if args.schedule == "graph" else "; enqueued call by call"))),
         },
         "roofline": {
             "bound": "hbm", "kernel": "ml_fused<2> (gather + Writeback, one pass over the batch's rows)",
@@ -369,7 +383,8 @@ def main():
             "avg_launch_us": float(gather_s.mean() * 1e6),
             "timed_launches": int(len(gather_steps)),
             "design_bytes_per_launch": float(design_bytes_all[timed].mean()),
-            "timed_in": "the call-by-call two-stream batches" if args.graph else "the headline batches",
+            "timed_in": f"the next {K} batches in the {ev_mode} schedule, events around every "
+                        f"{EV_SAMPLE_ML}rd row pass",
             "design_frac": design_gbs / HBM_PEAK_GBS,
         },
         "step_hbm": {
@@ -377,7 +392,7 @@ def main():
             "achieved_gbs": float(step_bytes.sum() / total_s / 1e9),
             "frac": float(step_bytes.sum() / total_s / 1e9 / HBM_PEAK_GBS),
         },
-        "eager_two_stream": eager,
+        "event_timed_leg": timed_leg,
         "one_stream": {"ms_per_step": serial_s / K * 1e3, "rows_per_s": n * K / serial_s,
                        "ops_us": ({"lookup_or_insert": float(per_op[:, 0].mean() * 1e6),
                                    "gather": float(per_op[:, 1].mean() * 1e6),
@@ -537,6 +552,7 @@ def run_serving(args):
 # is a packet on the compute stream between kernels, and events around every kernel of every step add to
 # the step they measure.
 EV_SAMPLE = 4
+EV_SAMPLE_ML = 3  # Memory Layer: coprime with the default group of 4, so the sampled row passes sit anywhere in a group
 
 
 class _EventPool:

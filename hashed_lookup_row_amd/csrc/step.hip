@@ -41,7 +41,7 @@ extern "C" hlr_status memory_layer_step(int64_t *identity, int64_t *stamps, floa
   if (dim <= 0 || dim % 4 != 0 || dim > 1024) return HLR_UNSUPPORTED_DIM;
   if (halves < 1 || halves > 3) return HLR_INVALID_ARG;
   const bool lk = halves & 1, cp = halves & 2;
-  if (!values || !out_rows || !out_hit || !looked_up || !planned) return HLR_INVALID_ARG;
+  if (!values || !out_rows || !out_hit) return HLR_INVALID_ARG;
   if (lk && (!identity || !stamps || (n > 0 && !ids))) return HLR_INVALID_ARG;
   if (cp && n > 0 && (!e || !out)) return HLR_INVALID_ARG;
   if (!hlr::aligned(values, 16) || (e && !hlr::aligned(e, 16)) || (out && !hlr::aligned(out, 16)) ||
@@ -60,12 +60,12 @@ extern "C" hlr_status memory_layer_step(int64_t *identity, int64_t *stamps, floa
     if ((st = hlr::ml_plan(identity, stamps, capacity, probes, ids, n, n_max, now, out_rows, out_hit, out_evicted,
                            out_stats, mz_ws, mz_ws_bytes, wb_ws, lookup)) != HLR_OK)
       return st;
-    if ((st = hip_ok(hipEventRecord(looked_up, lookup))) != HLR_OK) return st;
-    if ((st = hip_ok(hipEventRecord(planned, lookup))) != HLR_OK) return st;
+    if (looked_up && (st = hip_ok(hipEventRecord(looked_up, lookup))) != HLR_OK) return st;
+    if (planned && (st = hip_ok(hipEventRecord(planned, lookup))) != HLR_OK) return st;
   }
   if (!cp) return HLR_OK;
   // compute stream: one pass over the batch's rows (gather + Writeback)
-  if ((st = hip_ok(hipStreamWaitEvent(compute, planned, 0))) != HLR_OK) return st;
+  if (planned && (st = hip_ok(hipStreamWaitEvent(compute, planned, 0))) != HLR_OK) return st;
   if (gather_begin && (st = hip_ok(hipEventRecord(gather_begin, compute))) != HLR_OK) return st;
   if ((st = hlr::ml_apply(values, capacity, dim, e, n, n_max, out, wb_ws, compute)) != HLR_OK) return st;
   if (gather_end && (st = hip_ok(hipEventRecord(gather_end, compute))) != HLR_OK) return st;

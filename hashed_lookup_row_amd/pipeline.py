@@ -269,6 +269,99 @@ class MemoryLayerPipeline:
         return out, k
 
 
+    def run(self, batches, group=4, ahead=1, gather_events=None):
+        """Enqueues a known sequence of batches (eager, no graph) with one cross-stream wait per stream per
+        group of `group` batches: the lookup stream enqueues the lookup halves of a group back to back and
+        records one event after the last; the compute stream waits once for that event, then runs the
+        group's row halves back to back and records one event after the last.  The lookup halves run
+        `ahead` groups ahead of the row halves.
+
+        A queue that reaches a wait for another stream's event before the event completes resumes about
+        10 us after it completes; a wait whose event has completed costs nothing.  With the lookups a
+        group ahead, each stream's waits have normally completed when reached, and the host enqueues two
+        waits per group instead of two per batch.  Ring slots: batch b uses slot b mod depth, so a
+        group's lookups reuse the slots of the group depth / group groups back, and wait for that
+        group's row halves: depth must be a multiple of `group`, at least (ahead + 2) * group.
+
+        batches: as StepGraph's, (ids, now, e, out) per batch, optionally followed by (evicted, stats,
+        rows, hit).  gather_events: optional list of (begin, end) HIP event pairs, one per batch (or
+        None), recorded on the compute stream around each batch's row pass.  Returns after enqueueing;
+        the lookup stream is then ordered after everything enqueued so far (restart())."""
+        if not self.native:
+            raise HLRError("run() needs native=True")
+        if self._ahead:
+            raise HLRError("run(): finish the batches looked up ahead first")
+        r = self.ring
+        G, A, D = int(group), int(ahead), r.depth
+        if G < 1 or A < 1 or D % G != 0 or D < (A + 2) * G:
+            raise HLRError(f"run(): need group >= 1, ahead >= 1 and depth a multiple of group, at least "
+                           f"(ahead + 2) * group (depth {D}, group {G}, ahead {A})")
+        bs = [tuple(b) + (None,) * (8 - len(b)) for b in batches]
+        nD = self._const[5]
+        for b in bs:
+            ids, _, e, out, ev, st, ro, ho = b
+            self._check_ids(ids, ev, st)
+            n = ids.numel()
+            for t, name in ((e, "e"), (out, "out")):
+                if not (t is not None and t.is_cuda and t.dtype == torch.float32 and t.is_contiguous() and
+                        t.numel() == n * nD):
+                    raise HLRError(f"{name} must be a contiguous GPU float32 tensor of {n} x {nD} elements")
+            if ro is not None and not (ro.is_cuda and ro.dtype == torch.int64 and ro.numel() >= n):
+                raise HLRError("rows copy must be a GPU int64 tensor of at least n elements")
+            if ho is not None and not (ho.is_cuda and ho.dtype == torch.int8 and ho.numel() >= n):
+                raise HLRError("hit copy must be a GPU int8 tensor of at least n elements")
+        self.restart()
+        h, fn, mz = r.hip, self._fn, self._mz
+        ngroups = (len(bs) + G - 1) // G
+
+        def last(gi):  # slot of the group's last batch: its events are the group's
+            return (min(len(bs), gi * G + G) - 1) % D
+
+        def lookup_group(gi):
+            b0, b1 = gi * G, min(len(bs), gi * G + G)
+            kl = last(gi)
+            for b in range(b0, b1):
+                ids, now, _, _, ev, st, ro, ho = bs[b]
+                k = b % D
+                wb, wbb = self._wb[k]
+                _on(r.lookup, ids, ev, st)
+                rc = fn(*self._const, ids.data_ptr(), ids.numel(), self.n, int(now), None,
+                        self._rows[k].data_ptr(), self._hit[k].data_ptr(), None if ev is None else ev.data_ptr(),
+                        None if st is None else st.data_ptr(), None, mz[0], mz[1], wb, wbb, r.ls, r.cs,
+                        r.done[kl] if (b == b0 and b >= D) else None, None, r.marks[kl][1] if b == b1 - 1 else None,
+                        None, None, None, 1)
+                _check(rc, "memory_layer_step")
+                n = ids.numel()
+                if ro is not None:
+                    h.copy_d2d(ro.data_ptr(), self._rows[k].data_ptr(), 8 * n, r.ls)
+                if ho is not None:
+                    h.copy_d2d(ho.data_ptr(), self._hit[k].data_ptr(), n, r.ls)
+
+        def compute_group(gi):
+            b0, b1 = gi * G, min(len(bs), gi * G + G)
+            kl = last(gi)
+            for b in range(b0, b1):
+                ids, now, e, out, ev, st, _, _ = bs[b]
+                k = b % D
+                wb, wbb = self._wb[k]
+                _on(r.compute, e, out)
+                gb, ge = gather_events[b] if gather_events is not None and gather_events[b] is not None \
+                    else (None, None)
+                rc = fn(*self._const, None, ids.numel(), self.n, int(now), e.data_ptr(),
+                        self._rows[k].data_ptr(), self._hit[k].data_ptr(), None, None, out.data_ptr(),
+                        mz[0], mz[1], wb, wbb, r.ls, r.cs, None, None, r.marks[kl][1] if b == b0 else None,
+                        gb, ge, r.done[kl] if b == b1 - 1 else None, 2)
+                _check(rc, "memory_layer_step")
+
+        for gi in range(min(A, ngroups)):
+            lookup_group(gi)
+        for gi in range(ngroups):
+            if gi + A < ngroups:
+                lookup_group(gi + A)
+            compute_group(gi)
+        self.restart()
+
+
 class StepGraph:
     """A fixed sequence of Memory-Layer batches enqueued once, as one HIP graph, through a native
     MemoryLayerPipeline: the same library calls in the same two-stream schedule with lookahead
@@ -280,18 +373,25 @@ class StepGraph:
     batches: list of (ids, now, e, out) per batch, in order, optionally followed by (evicted, stats,
     rows, hit): int64[n] evicted IDs and int64[6] stats written by the lookup as in
     mpzch_lookup_or_insert, and int64[n] rows / int8[n] hit buffers that receive copies of the batch's
-    rows and hit mask (copied on the lookup stream while the ring slot still holds them).  (HIP events
+    rows and hit mask (copied on the lookup stream while the ring slot still holds them).
+    ahead: how many batches the lookup half runs ahead of the row half (at most depth - 1).  A wait on
+    another stream's event takes about 10 us to resolve when the event completes after the waiting
+    queue reached it; with the lookup two batches ahead, the event the row half of batch t waits for
+    completed a whole row pass earlier.  (HIP events
     recorded inside a capture cannot be timed on this runtime, so the row pass is not timed inside a
     graph.)  Every `now` must stay valid when the
     graph runs: a graph is meant to be replayed once for the state it was captured for, or again only
     after that state has been restored (the MPZCH stamps must stay below every `now`)."""
 
-    def __init__(self, pipe: MemoryLayerPipeline, batches):
+    def __init__(self, pipe: MemoryLayerPipeline, batches, ahead=1):
         if not pipe.native:
             raise HLRError("StepGraph needs a native MemoryLayerPipeline")
         if pipe._ahead:
             raise HLRError("StepGraph: finish the batches looked up ahead first")
         r = pipe.ring
+        ahead = int(ahead)
+        if not 1 <= ahead < r.depth:
+            raise HLRError(f"StepGraph: ahead must be in [1, depth - 1] = [1, {r.depth - 1}]")
         if not r.cs:
             raise HLRError("StepGraph: the legacy default stream cannot be captured; build the pipeline while a "
                            "non-default torch stream is current")
@@ -312,10 +412,11 @@ class StepGraph:
                 if hit_out is not None:
                     h.copy_d2d(hit_out.data_ptr(), pipe.hit(k).data_ptr(), n, r.ls)
 
-            look(bs[0])
+            for b in bs[:ahead]:
+                look(b)
             for k, (ids, now, e, out, ev, st, _, _) in enumerate(bs):
-                if k + 1 < len(bs):
-                    look(bs[k + 1])
+                if k + ahead < len(bs):
+                    look(bs[k + ahead])
                 pipe.step(ids, now, e, out=out, evicted=ev, stats=st)
             join = h.event()
             h.record(join, r.ls)

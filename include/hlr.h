@@ -406,8 +406,8 @@ hlr_status hashed_rows(const int64_t *ids, int64_t n, int64_t num_rows, int64_t 
  *                   MPZCH lookup/insert (as mpzch_lookup_or_insert with
  *                   values = NULL, insert = 1), then the grouping of the
  *                   batch's positions by row into wb_ws;
- *                   record looked_up; record planned.
- *   compute stream: wait planned;
+ *                   record looked_up (if given); record planned (if given).
+ *   compute stream: wait planned (if given);
  *                   record gather_begin (if given);
  *                   one pass over the batch's distinct rows: each row is read
  *                   once, written to out at every position that holds it
@@ -424,8 +424,12 @@ hlr_status hashed_rows(const int64_t *ids, int64_t n, int64_t num_rows, int64_t 
  *  Writeback), values[r] <- fl(M - fl(M - e[last position of r])).
  *  Arguments as the calls above; capacity = the table's row count, below
  *  2^31 - 1; dim <= 1024.  Events are the caller's (hipEventCreateWithFlags;
- *  timing needed only for the gather pair); looked_up and planned are
- *  required, the others nullable.  n_max >= n: the largest batch the
+ *  timing needed only for the gather pair), each nullable.  A compute half
+ *  without planned does not wait for its lookup half: give NULL only when the
+ *  caller orders the two halves itself (the same stream for both, or a wait
+ *  the caller enqueued on the compute stream for an event recorded after this
+ *  batch's lookup half, e.g. once for a group of batches).  n_max >= n: the
+ *  largest batch the
  *  workspaces serve (the same for every batch that uses them).  mz_ws: a
  *  workspace of mpzch_lookup_or_insert_workspace_size(n_max, 1) bytes; wb_ws:
  *  one of memory_layer_step_workspace_size(n_max, capacity) bytes (both
@@ -437,8 +441,8 @@ hlr_status hashed_rows(const int64_t *ids, int64_t n, int64_t num_rows, int64_t 
  *  stay in use until slot_done.
  *  halves: 1 = the lookup-stream half only, 2 = the compute-stream half
  *  only, 3 = both.  A batch's lookup half must be enqueued before its compute
- *  half (the compute half waits on planned as recorded by the most recent
- *  lookup half); enqueueing the lookup half of batch t+1 before the compute
+ *  half (the compute half waits on planned, if given, as recorded by the most
+ *  recent lookup half); enqueueing the lookup half of batch t+1 before the compute
  *  half of batch t (lookahead) is allowed and gives the same results, since
  *  the compute stream keeps the row traffic in batch order, provided each
  *  batch in flight has its own out_rows, out_hit, wb_ws and events.

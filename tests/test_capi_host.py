@@ -263,7 +263,6 @@ def test_memory_layer_step_argument_errors(lib):
     assert call(dim=6) == DIM
     assert call(values=None) == INVALID
     assert call(ids=None) == INVALID
-    assert call(looked=None) == INVALID              # ordering events are required
     assert call(values=P_ODD) == MISALIGNED
     assert call(mzb=mzb - 1) == WS_SMALL
     assert call(wbb=wbb - 1) == WS_SMALL

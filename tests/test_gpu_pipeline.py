@@ -333,6 +333,74 @@ def test_step_graph_replays_match_oracle(dev):
     assert bits_equal(to_np(values), o.values)
 
 
+@pytest.mark.parametrize("group,ahead,steps", [(4, 1, 11), (2, 2, 9), (1, 1, 5), (3, 1, 3)])
+def test_grouped_run_matches_oracle(dev, group, ahead, steps):
+    """MemoryLayerPipeline.run: the lookup halves of a group of batches back to back, one cross-stream
+    wait per stream per group, lookups `ahead` groups ahead, batches of varying size and a ragged last
+    group.  Every batch's rows, hit mask, evicted IDs, stats and gathered rows, and the final state,
+    equal the oracle's sequential result bit for bit; an eager batch then follows."""
+    cfg = synth.scaled_memory_layer(capacity=16_384, universe=120_000, batch=8_192, steps=steps)
+    C, P, D, n = cfg.capacity, cfg.probes, cfg.dim, cfg.batch
+    identity, stamps, o, base = prefilled_pair(dev, cfg)
+    values = torch.zeros((C, D), dtype=torch.float32, device=dev)
+    ids_np = synth.mpzch_stream(cfg, steps + 1)
+    ids_np = [x if t % 3 != 1 else x[: n - 777 * t] for t, x in enumerate(ids_np)]  # some smaller batches
+    e_np = [synth.normal_rows_np(x.size, D, cfg.e_std, 2, t) for t, x in enumerate(ids_np, start=1)]
+    ids = [torch.from_numpy(x).to(dev) for x in ids_np]
+    es = [torch.from_numpy(x).to(dev) for x in e_np]
+    side = torch.cuda.Stream(dev)
+    side.wait_stream(torch.cuda.current_stream(dev))
+    with torch.cuda.stream(side):
+        outs = [torch.full((x.size, D), float("nan"), dtype=torch.float32, device=dev) for x in ids_np[:steps]]
+        evs = [torch.empty(x.size, dtype=torch.int64, device=dev) for x in ids_np[:steps]]
+        sts = [torch.zeros(6, dtype=torch.int64, device=dev) for _ in range(steps)]
+        rws = [torch.empty(x.size, dtype=torch.int64, device=dev) for x in ids_np[:steps]]
+        hts = [torch.empty(x.size, dtype=torch.int8, device=dev) for x in ids_np[:steps]]
+        pipe = pipeline.MemoryLayerPipeline(identity, stamps, values, P, n, depth=(ahead + 2) * group)
+        pipe.run([(ids[t], base + t + 1, es[t], outs[t], evs[t], sts[t], rws[t], hts[t]) for t in range(steps)],
+                 group=group, ahead=ahead)
+        out = pipe.step(ids[steps], base + steps + 1, es[steps])[0]
+        torch.cuda.synchronize()
+    for t in range(steps):
+        orows, ohit, oev, ost = o.step(ids_np[t], base + t + 1)
+        assert np.array_equal(to_np(rws[t]), orows), f"rows batch {t}"
+        assert np.array_equal(to_np(hts[t]), ohit), f"hit batch {t}"
+        assert np.array_equal(to_np(evs[t]), oev), f"evicted batch {t}"
+        s_ = to_np(sts[t])
+        assert np.array_equal(s_[:5], ost) and s_[5] == 0, (t, s_, ost)
+        assert bits_equal(to_np(outs[t]), o.gather(orows)), f"gather batch {t}"
+        o.writeback(orows, e_np[t])
+    orows, _, _, _ = o.step(ids_np[steps], base + steps + 1)  # the eager batch after run()
+    assert bits_equal(to_np(out), o.gather(orows))
+    o.writeback(orows, e_np[steps])
+    assert np.array_equal(to_np(identity), o.identity)
+    assert np.array_equal(to_np(stamps), o.stamps)
+    assert bits_equal(to_np(values), o.values)
+
+
+def test_grouped_run_argument_errors(dev):
+    """run() refuses a ring depth that cannot hold (ahead + 2) groups, and lookahead left pending."""
+    C, P, D, n = 1024, 8, 16, 64
+    identity = torch.full((C,), -1, dtype=torch.int64, device=dev)
+    stamps = torch.full((C,), -1, dtype=torch.int64, device=dev)
+    values = torch.zeros((C, D), dtype=torch.float32, device=dev)
+    pipe = pipeline.MemoryLayerPipeline(identity, stamps, values, P, n, depth=6)
+    ids = torch.arange(n, dtype=torch.int64, device=dev)
+    e = torch.zeros((n, D), dtype=torch.float32, device=dev)
+    out = torch.empty((n, D), dtype=torch.float32, device=dev)
+    with pytest.raises(hlr.HLRError):
+        pipe.run([(ids, 1, e, out)], group=4)           # depth 6 < 3 groups of 4
+    with pytest.raises(hlr.HLRError):
+        pipe.run([(ids, 1, e, out)], group=2, ahead=2)  # depth 6 < 4 groups of 2
+    pipe.prefetch(ids, 1)
+    with pytest.raises(hlr.HLRError):
+        pipe.run([(ids, 2, e, out)], group=2)
+    pipe.step(ids, 1, e)
+    pipe.run([(ids, 2, e, out)], group=2)
+    torch.cuda.synchronize()
+    assert int((identity >= 0).sum().item()) == n
+
+
 def test_prefetch_limits(dev):
     """Lookahead is bounded by the ring depth and must be consumed in order (host-side errors)."""
     C, P, D, n = 1024, 8, 16, 64
