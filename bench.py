@@ -204,7 +204,7 @@ def main():
     cur = torch.cuda.current_stream(dev).cuda_stream
     G, A = args.group, args.ahead
     depth = args.depth
-    if args.schedule == "grouped":  # a multiple of the group, at least (ahead + 2) groups
+    if args.schedule != "eager":  # the grouped leg: a multiple of the group, at least (ahead + 2) groups
         depth = max(depth, (A + 2) * G)
         depth = (depth + G - 1) // G * G
     pipe = MemoryLayerPipeline(identity, stamps, values, P, n, depth=depth)
@@ -249,7 +249,15 @@ def main():
             graph.replay()
             timer.record(stop, cur)
         elif mode == "grouped":
-            gevs = [timed_evs.get(k) for k in range(K)] if timed_evs else None
+            # timed_evs: group -> (begin, end), recorded before the group's first and after its last row pass
+            gevs = None
+            if timed_evs:
+                gevs = [None] * K
+                for g, (eb, ee) in timed_evs.items():
+                    b0, b1 = g * G, min(K, g * G + G) - 1
+                    gevs[b0] = (eb, ee if b1 == b0 else None)
+                    if b1 != b0:
+                        gevs[b1] = (None, ee)
             torch.cuda.synchronize()
             wall0 = time.perf_counter()
             timer.record(start, cur)
@@ -278,18 +286,29 @@ def main():
     torch.cuda.synchronize()
 
     # the headline: batches W .. W+K-1 in the chosen two-stream schedule, no events inside.  The row pass is
-    # then timed with HIP events on the compute stream around every EV_SAMPLE-th batch of the next K batches,
-    # in the same schedule (grouped, eager) or, for the graph (events inside a captured graph cannot be timed
-    # on this runtime), call by call; that leg is reported beside the headline
-    evs = {k: [timer.event() for _ in range(2)] for k in range(0, K, EV_SAMPLE_ML)}
+    # then timed with HIP events on the compute stream over the next K batches (events inside a captured
+    # graph cannot be timed on this runtime): with the grouped schedule (unless the headline is the eager
+    # one), one event pair around each group's back-to-back row passes, whose span / group size is the mean
+    # launch duration (markers around every single launch would add their own few us to each); eager:
+    # around every EV_SAMPLE_ML-th row pass.  That leg is reported beside the headline
     total_s, enqueue, wall = two_stream(W, None, args.schedule)
-    ev_mode = "eager" if args.schedule == "graph" else args.schedule
+    ev_mode = "eager" if args.schedule == "eager" else "grouped"
+    if ev_mode == "grouped":
+        evs = {g: [timer.event() for _ in range(2)] for g in range((K + G - 1) // G)}
+        ev_count = {g: min(K, g * G + G) - g * G for g in evs}
+        ev_batches = {g: list(range(g * G, g * G + ev_count[g])) for g in evs}
+    else:
+        evs = {k: [timer.event() for _ in range(2)] for k in range(0, K, EV_SAMPLE_ML)}
+        ev_count = {k: 1 for k in evs}
+        ev_batches = {k: [k] for k in evs}
     e_total, e_enqueue, _ = two_stream(W + K, evs, ev_mode)
     timed_leg = {"schedule": ev_mode, "ms_per_step": e_total / K * 1e3, "rows_per_s": n * K / e_total,
                  "host_enqueue_us_per_step": e_enqueue / K * 1e6}
     ev_first = W + K
-    gather_s = np.array([timer.elapsed_s(e[0], e[1]) for e in evs.values()])
-    gather_steps = np.array(sorted(evs.keys()))
+    span_s = np.array([timer.elapsed_s(evs[g][0], evs[g][1]) for g in sorted(evs)])
+    launches = np.array([ev_count[g] for g in sorted(evs)])
+    gather_s = span_s / launches  # mean launch duration in each timed span
+    gather_steps = np.array([b for g in sorted(evs) for b in ev_batches[g]])
     off = K
 
     # the same step as three calls on one stream, over the next K batches (reported beside the headline)
@@ -333,8 +352,8 @@ def main():
     # (a 16-byte descriptor and a 4-byte position per position at most)
     design_bytes_all = n * R + u_read_all * R + 2 * us_all * R + 20 * n
     timed = (ev_first - W) + gather_steps  # indices of the event-timed batches in the arrays above
-    row_gbs = float(row_bytes_all[timed].sum() / gather_s.sum() / 1e9)
-    design_gbs = float(design_bytes_all[timed].sum() / gather_s.sum() / 1e9)
+    row_gbs = float(row_bytes_all[timed].sum() / span_s.sum() / 1e9)
+    design_gbs = float(design_bytes_all[timed].sum() / span_s.sum() / 1e9)
     step_bytes = row_bytes
     ms_per_step = total_s / K * 1e3
     value = n * K / total_s
@@ -380,11 +399,12 @@ def main():
             "achieved": row_gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": row_gbs / HBM_PEAK_GBS,
             "traffic": traffic,
             "algorithmic_bytes_per_launch": float(row_bytes_all[timed].mean()),
-            "avg_launch_us": float(gather_s.mean() * 1e6),
-            "timed_launches": int(len(gather_steps)),
+            "avg_launch_us": float(span_s.sum() / launches.sum() * 1e6),
+            "timed_launches": int(launches.sum()),
             "design_bytes_per_launch": float(design_bytes_all[timed].mean()),
-            "timed_in": f"the next {K} batches in the {ev_mode} schedule, events around every "
-                        f"{EV_SAMPLE_ML}rd row pass",
+            "timed_in": (f"the next {K} batches in the grouped schedule (groups of {G}), one HIP event pair "
+                         f"around each group's back-to-back row passes" if ev_mode == "grouped" else
+                         f"the next {K} batches call by call, events around every {EV_SAMPLE_ML}rd row pass"),
             "design_frac": design_gbs / HBM_PEAK_GBS,
         },
         "step_hbm": {

@@ -58,8 +58,9 @@ __global__ void __launch_bounds__(ml::kThreads)
   float4 m[NC];
 #pragma unroll
   for (int c = 0; c < NC; ++c) m[c] = table[rb + col[c]];
-  const uint32_t total = norow ? cnt : w.hcount[row];
-  const uint32_t last1 = norow ? 1u : w.hlast[row];  // last position + 1
+  const uint2 hc = norow ? make_uint2(cnt, 1u) : *reinterpret_cast<const uint2 *>(&w.hrow[row]);
+  const uint32_t total = hc.x;
+  const uint32_t last1 = hc.y;  // last position + 1
   const int32_t pv = w.gpos[d.z + (static_cast<uint32_t>(lane) < cnt ? lane : 0)];
   const bool whole = !norow && total == cnt;
   float4 e[NC];
@@ -97,18 +98,14 @@ __global__ void __launch_bounds__(ml::kThreads)
     // has read the row's entries by then.
     __atomic_signal_fence(__ATOMIC_SEQ_CST);
     uint32_t prev = 0;
-    if (lane == 0) prev = atomicAdd(&w.hdone[row], cnt);
+    if (lane == 0) prev = atomicAdd(&w.hrow[row].z, cnt);
     prev = __builtin_amdgcn_readfirstlane(prev);
     if (prev + cnt != total) return;
     const int64_t lb = static_cast<int64_t>(last1 - 1) * v4;
 #pragma unroll
     for (int c = 0; c < NC; ++c) e[c] = src[lb + col[c]];
   }
-  if (lane == 0) {  // the row's entries back to zero for the next batch
-    w.hcount[row] = 0u;
-    w.hlast[row] = 0u;
-    if (!whole) w.hdone[row] = 0u;
-  }
+  if (lane == 0) w.hrow[row] = make_uint4(0u, 0u, 0u, 0u);  // the row's entry back to zero for the next batch
   const int64_t wb = static_cast<int64_t>(row) * v4;
 #pragma unroll
   for (int c = 0; c < NC; ++c)

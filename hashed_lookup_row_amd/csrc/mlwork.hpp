@@ -7,9 +7,10 @@
 //
 // A tile of kTile consecutive positions is grouped by row in LDS: a group is
 // (tile, row) with its positions listed contiguously in gpos and one
-// descriptor in gdesc.  Across tiles a row's groups meet in tables indexed by
-// the row itself (position count, last position + 1, positions done), added
-// to with one global atomic per group and no return value.  A group that
+// descriptor in gdesc.  Across tiles a row's groups meet in one 16-byte entry
+// per row, indexed by the row itself (position count, last position + 1,
+// positions done: one cache line per row touched, not one per field), added
+// to with global atomics that return nothing.  A group that
 // holds all positions of its row ("whole") applies the Writeback on its own;
 // the groups of a row spread over several tiles count their positions into
 // the row's done counter, and the one that completes it applies the
@@ -38,9 +39,9 @@ constexpr uint32_t kNoRow = 1u << 30;   // positions without a row: zero vector,
 constexpr uint32_t kCountMask = (1u << 28) - 1;
 
 struct Work {
-  uint32_t *hcount;  // [rows] positions of the row in the batch         } zero between batches
-  uint32_t *hlast;   // [rows] last position of the row + 1 (0: none)    }
-  uint32_t *hdone;   // [rows] positions whose read of the row is done   }
+  uint4 *hrow;       // [rows] x: positions of the row in the batch,      } zero between batches
+                     //        y: last position of the row + 1 (0: none), }
+                     //        z: positions whose read of the row is done }
   uint32_t *ntile;   // [tiles] groups of each tile
   uint4 *gdesc;      // [tiles * kTile] group j of tile t at t * kTile + j: row, -, first index in gpos,
                      //                 count | flags
@@ -51,9 +52,7 @@ struct Work {
 inline size_t layout(int64_t n, int64_t rows, Work *w, void *base) {
   hlr::Carver c(base);
   const size_t nr = static_cast<size_t>(rows > 0 ? rows : 1);
-  w->hcount = c.take<uint32_t>(nr);
-  w->hlast = c.take<uint32_t>(nr);
-  w->hdone = c.take<uint32_t>(nr);
+  w->hrow = c.take<uint4>(nr);
   w->tiles = (n + kTile - 1) / kTile;
   const size_t nt = static_cast<size_t>(w->tiles > 0 ? w->tiles : 1);
   w->ntile = c.take<uint32_t>(nt);
@@ -149,8 +148,8 @@ __device__ __forceinline__ void group_tile(Shared &sh, Work &w, int64_t tile, co
     if (key < 0) {
       d.w |= kNoRow;
     } else {
-      atomicAdd(&w.hcount[key], cnt);
-      atomicMax(&w.hlast[key], static_cast<uint32_t>(sh.last[e]) + 1u);
+      atomicAdd(&w.hrow[key].x, cnt);
+      atomicMax(&w.hrow[key].y, static_cast<uint32_t>(sh.last[e]) + 1u);
       if (sh.fresh[e]) d.w |= kFresh;
     }
     w.gdesc[base + sh.gid[e]] = d;

@@ -619,9 +619,7 @@ extern "C" hlr_status memory_layer_step_workspace_init(void *mz_ws, size_t mz_ws
     if (wb_ws_bytes < memory_layer_step_workspace_size(n, capacity)) return HLR_WORKSPACE_TOO_SMALL;
     ml::Work g;
     ml::layout(n, capacity, &g, wb_ws);
-    hlr_fill(g.hcount, capacity, 0u, stream);
-    hlr_fill(g.hlast, capacity, 0u, stream);
-    hlr_fill(g.hdone, capacity, 0u, stream);
+    hlr_fill(reinterpret_cast<uint32_t *>(g.hrow), 4 * capacity, 0u, stream);
   }
   return launch_status();
 }
