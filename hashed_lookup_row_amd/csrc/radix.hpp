@@ -87,7 +87,8 @@ struct SegWork {
   K *k[2];
   uint32_t *v[2];
   uint32_t *counts;  // [kMaxBins * nblocks]
-  uint32_t *ticket;  // [kTickets]: heavy-run and combine list counts, then the length-bucket counts
+  uint32_t *ticket;  // [kTickets]: heavy-run and combine list counts, the SGD apply's item and
+                     // finished-block counters, then the length-bucket counts
   uint32_t *bcount;  // [nblocks]
   int32_t *segidx;   // [n]   segment of each sorted element (-1: excluded)
   int32_t *seg_start;  // [n]
@@ -1001,7 +1002,11 @@ __device__ __forceinline__ bool heavy_item(const uint32_t (&cnt)[kLenBuckets], c
 // result equals the running sum started from the first value, and every batch
 // is the same straight-line code.  Indices come in by vector loads of 64
 // positions and reach each row by a lane permute; P load instructions per
-// batch plus P / 4 index loads stay within the 63-load counter.  grad(x) turns
+// batch plus P / 4 index loads stay within the 63-load counter.  (Double
+// buffering two batches of half the size measured slower on the hashed-tables
+// step: while other blocks stream at full bandwidth a batch's memory latency is
+// several times its adds, and the positions in flight per wave are what
+// count.)  grad(x) turns
 // a loaded value into the term summed (the L2-alignment gradient).  lds: this
 // wave's kChainSlots * 64 floats.  Only lane 0 of each row returns a
 // meaningful sum.

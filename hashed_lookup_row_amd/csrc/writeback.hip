@@ -287,8 +287,8 @@ template <bool L2, bool Off32>
 __device__ __forceinline__ void sgd_heavy(float *table, const float *__restrict__ g,
                                           const uint32_t *__restrict__ skey, const uint32_t *__restrict__ spos,
                                           const int32_t *__restrict__ seg_start, const int32_t *__restrict__ seg_end,
-                                          const uint32_t *__restrict__ counters, const int32_t *__restrict__ slist,
-                                          int64_t n, float lr, int64_t D, int block, int nblocks) {
+                                          uint32_t *counters, const int32_t *__restrict__ slist,
+                                          int64_t n, float lr, int64_t D, int nblocks) {
   const int64_t S = (D + 15) / 16;
   uint32_t cnt[kLenBuckets];
   int64_t items = 0;
@@ -300,7 +300,17 @@ __device__ __forceinline__ void sgd_heavy(float *table, const float *__restrict_
   const int wv = static_cast<int>(threadIdx.x) / kWave;
   const int r = lane_id() / 16;
   __shared__ __align__(16) float lds[kThreads / kWave][kChainSlots * 64];
-  for (int64_t it = block; it < items; it += nblocks) {
+  __shared__ uint32_t sh_it;
+  // Items (segment, slice), longest segments first, go to the blocks as they
+  // come free (counters[2]), so a block that drew a short chain takes the
+  // next one while the longest runs: the apply ends with the longest chain,
+  // not with the block that drew the most work.
+  for (;;) {
+    if (threadIdx.x == 0) sh_it = atomicAdd(&counters[2], 1u);
+    __syncthreads();
+    const int64_t it = sh_it;
+    __syncthreads();
+    if (it >= items) break;
     int32_t k;
     int64_t slice;
     heavy_item(cnt, slist, n, S, it, &k, &slice);
@@ -315,6 +325,13 @@ __device__ __forceinline__ void sgd_heavy(float *table, const float *__restrict_
       table[at] = mv - st;  // fl(M - fl(lr * s))
     }
   }
+  // The last heavy block of the update to finish drawing returns both
+  // counters to zero (counters[3] counts the blocks done), so the plan can be
+  // applied again.
+  if (threadIdx.x == 0 && atomicAdd(&counters[3], 1u) == static_cast<uint32_t>(nblocks - 1)) {
+    counters[2] = 0u;
+    counters[3] = 0u;
+  }
 }
 
 // One update (table, gradients, plan) of a launch, and the blocks it owns.
@@ -324,7 +341,7 @@ struct SgdJob {
   const uint32_t *seg_key, *skey, *spos;
   const int32_t *seg_start, *seg_end;
   const int64_t *nseg;
-  const uint32_t *counters;
+  uint32_t *counters;
   const int32_t *slist;
   int64_t n;
   float lr;
@@ -348,7 +365,7 @@ __global__ void __launch_bounds__(kThreads) sgd_apply_kernel(SgdJobs js) {
     const SgdJob &j = js.job[i];
     if (blk >= j.heavy_begin && blk < j.heavy_begin + j.heavy_blocks) {
       sgd_heavy<L2, Off32>(j.table, j.g, j.skey, j.spos, j.seg_start, j.seg_end, j.counters, j.slist, j.n, j.lr,
-                           js.D, blk - j.heavy_begin, j.heavy_blocks);
+                           js.D, j.heavy_blocks);
       return;
     }
     if (blk >= j.light_begin && blk < j.light_begin + j.light_blocks) {
@@ -378,11 +395,11 @@ SgdJob sgd_job(float *table, const float *g, int64_t n, int64_t dim, float lr, v
   j.slist = w.slist;
   j.n = n;
   j.lr = lr;
-  // heavy blocks hold 4 waves of about 120 registers each; 64 per update
+  // heavy blocks hold 4 waves of about 120 registers each; 128 per update
   // leave most of the GPU to the light rows that stream beside them
-  const int gl = grid_for(n, 4 * 4), gh = grid_for(n, 2048);
+  const int gl = grid_for(n, 4 * 4), gh = grid_for(n, 1024);
   j.light_blocks = gl < 4096 ? gl : 4096;
-  j.heavy_blocks = gh < 64 ? gh : 64;
+  j.heavy_blocks = gh < 128 ? gh : 128;
   return j;
 }
 

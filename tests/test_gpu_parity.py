@@ -416,6 +416,25 @@ def test_sgd_sum_single_row_long_chain(dev):
     assert bits_equal(to_np(t), table)
 
 
+def test_sgd_sum_plan_applied_twice(dev):
+    """One SGD_SUM plan applied twice (the heavy rows' work items are drawn from a counter in the plan,
+    which the last heavy block returns to zero): the table equals two sequential oracle updates."""
+    g = np.random.default_rng(31)
+    n, D, C = 40_000, 64, 300
+    rows = np.where(g.random(n) < 0.5, g.integers(0, 4, size=n), g.integers(0, C, size=n)).astype(np.int64)
+    grads = (g.standard_normal((n, D)) * 1e-3).astype(np.float32)
+    table = (g.standard_normal((C, D)) * 0.01).astype(np.float32)
+    t = torch.from_numpy(table).to(dev)
+    r, gr = torch.from_numpy(rows).to(dev), torch.from_numpy(grads).to(dev)
+    ws = hlr.new_workspace(dev, hlr.writeback_workspace_size(C, D, n, hlr.WB_SGD_SUM))
+    hlr.writeback_plan(C, r, ws, hlr.WB_SGD_SUM)
+    hlr.writeback_apply(t, gr, ws, hlr.WB_SGD_SUM, 0.01)
+    hlr.writeback_apply(t, gr, ws, hlr.WB_SGD_SUM, 0.01)
+    oracle.sgd_sum(table, rows, grads, 0.01)
+    oracle.sgd_sum(table, rows, grads, 0.01)
+    assert bits_equal(to_np(t), table)
+
+
 @pytest.mark.parametrize("k", [63, 64, 65, 511, 512, 513, 1000, 4097, 20_000])
 @pytest.mark.parametrize("D", [4, 12, 512])
 def test_sgd_sum_order_revealing_rows(dev, k, D):
