@@ -16,14 +16,24 @@ from . import dks_lookup_or_insert, dks_rehash, dks_workspace_size, new_workspac
 
 
 class DynamicKeyStore:
+    """stream: the torch stream the store's kernels run on (None: the current stream at each call).  The
+    tables are filled on the current stream at construction; a given stream is ordered after that fill, and
+    the tables a rehash replaces are kept alive for the allocator until the stream is done with them."""
+
     def __init__(self, values, max_rows, key_cap=1 << 16, stream=None, max_load=0.5):
         dev = values.device
+        if stream is not None and not isinstance(stream, torch.cuda.Stream):
+            raise TypeError("stream must be a torch.cuda.Stream (or None for the current stream)")
         self.values, self.max_rows, self.max_load = values, int(max_rows), float(max_load)
         self.keys = torch.full((key_cap,), -1, dtype=torch.int64, device=dev)
         self.krows = torch.full((key_cap,), -1, dtype=torch.int64, device=dev)
         self.stamps = torch.full((self.max_rows,), -1, dtype=torch.int64, device=dev)
         self.next_row = torch.zeros(1, dtype=torch.int64, device=dev)
         self.stream = stream
+        if stream is not None:  # the fills above ran on the current stream
+            stream.wait_stream(torch.cuda.current_stream(dev))
+            for t in (self.keys, self.krows, self.stamps, self.next_row, values):
+                t.record_stream(stream)
         # pinned copies of next_row, each with its event (created here: creating events per batch can
         # stall the GPU now and then while the runtime grows its signal pool)
         self._pinned = deque((torch.zeros(1, dtype=torch.int64, pin_memory=True), torch.cuda.Event())
@@ -54,7 +64,13 @@ class DynamicKeyStore:
         while need > self.max_load * cap:
             cap *= 2
         if cap != self.keys.numel():
+            old = (self.keys, self.krows)
             self.keys, self.krows = dks_rehash(self.keys, self.krows, cap, stream=self.stream)
+            if self.stream is not None:
+                # the rehash reads the old tables and fills the new ones on self.stream: tell the caching
+                # allocator, so it neither reuses the old blocks nor hands out the new ones elsewhere early
+                for t in old + (self.keys, self.krows):
+                    t.record_stream(self.stream)
             self.rehashes += 1
 
     def step(self, ids, now, out_rows=None, out_hit=None, out_stats=None):

@@ -133,14 +133,17 @@ def test_rehash_keeps_the_map(dev):
         assert dict(zip(kk[sel].tolist(), rr[sel].tolist())) == m
 
 
-def test_dynamic_key_store_grows_without_waiting(dev):
+@pytest.mark.parametrize("side", [False, True])
+def test_dynamic_key_store_grows_without_waiting(dev, side):
     """DynamicKeyStore: batches enqueued back to back (no synchronisation), growth decided from
-    completed copies of the row count; every batch's rows equal the oracle's."""
+    completed copies of the row count; every batch's rows equal the oracle's.  With side=True the store
+    runs on a stream of its own: its first batch must follow the tables' fill on the current stream, and
+    the tables each rehash replaces must stay allocated until that stream is done with them."""
     from hashed_lookup_row_amd.keystore import DynamicKeyStore
     g = np.random.default_rng(12)
     dim, max_rows, n = 32, 60_000, 3000
     values = torch.zeros((max_rows, dim), dtype=torch.float32, device=dev)
-    store = DynamicKeyStore(values, max_rows, key_cap=1024)
+    store = DynamicKeyStore(values, max_rows, key_cap=1024, stream=torch.cuda.Stream(dev) if side else None)
     ora = oracle.KeyStore(1 << 18, max_rows, dim)
     batches = [zipf_keys(g, n, 1.1, 500_000) for _ in range(15)]
     dev_b = [torch.from_numpy(b).to(dev) for b in batches]
