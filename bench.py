@@ -854,7 +854,8 @@ def run_res(args):
 def run_keystore(args):
     """The Memory-Layer ID stream (65,536 IDs per batch, Zipf(1.05) over 20M keys + 0.5% fresh) through
     the decoupled key store: key store from 2^20 slots, grown by rehash (keys only) whenever it could
-    pass half full; value store of 4Mi rows x 512 fp32 (new rows zero-filled), as in the Memory Layer."""
+    pass half full; value store of up to 4Mi rows x 512 fp32 in chunks of 65,536 rows, 2Mi rows at the
+    start and grown a chunk at a time as rows fill (new rows zero-filled, stamped and counted)."""
     import numpy as np
     import torch
     import hashed_lookup_row_amd as hlr
@@ -869,8 +870,7 @@ def run_keystore(args):
         ids, fc = synth.mpzch_step_ids(cfg, t, fc)
         stream.append(ids)
     ids_dev = [torch.from_numpy(x).to(dev) for x in stream]
-    values = torch.zeros((C, D), dtype=torch.float32, device=dev)
-    store = DynamicKeyStore(values, C, key_cap=1 << 20)
+    store = DynamicKeyStore(D, C, dev, key_cap=1 << 20, chunk_shift=16, initial_rows=C // 2)
     rows = torch.empty(n, dtype=torch.int64, device=dev)
     hit = torch.empty(n, dtype=torch.int8, device=dev)
     stats = torch.zeros(4, dtype=torch.int64, device=dev)
@@ -907,7 +907,9 @@ def run_keystore(args):
            "last_step_stats": {"hits": int(st[0]), "inserts": int(st[1]), "overflows": int(st[2]),
                                "invalid": int(st[3])},
            "rehash": {"from_slots": cap, "to_slots": 2 * cap, "us": rehash_s * 1e6,
-                      "bytes_moved": cap * 16 + 2 * cap * 16}})
+                      "bytes_moved": cap * 16 + 2 * cap * 16},
+           "value_store": {"chunks": len(store.values.chunks), "rows_held": store.values.capacity,
+                           "chunk_rows": store.values.rows_per_chunk}})
 
 
 def run_dedup(args):

@@ -72,7 +72,10 @@ def load_library():
             "mark_rows": (i32, [p, i64, p, i64, p, p, p, p]),
             "clear_marks": (i32, [p, p, i64, p, p]),
             "dks_workspace_size": (sz, [i64]),
-            "dks_lookup_or_insert": (i32, [p, p, i64, p, p, i64, i64, p, p, i64, i64, i32, p, p, p, p, sz, p]),
+            "dks_lookup_or_insert": (i32, [p, p, i64, p, i32, i64, i64, p, p, i64, i64, i32, p, p, p, p, sz, p]),
+            "dks_chunk_bytes": (i64, [i32, i64]),
+            "dks_chunk_init": (i32, [p, i32, i64, p]),
+            "dks_gather_rows": (i32, [p, i32, i64, i64, p, i64, p, p]),
             "dks_rehash": (i32, [p, p, i64, p, p, i64, p]),
             "memory_layer_step": (i32, [p, p, p, i64, i32, i64, p, i64, i64, i64, p, p, p, p, p, p, p, sz, p, sz,
                                         p, p, p, p, p, p, p, p, i32]),
@@ -95,7 +98,8 @@ def exported_symbols():
             "writeback_rows", "ema_update_rows_workspace_size", "ema_update_rows", "gather_dequant_score",
             "hashed_rows", "mpzch_zero_inserted", "writeback_plan", "writeback_apply", "ema_update_plan",
             "ema_update_apply", "writeback_plan_rows", "quantize_rows_int8", "mark_rows", "clear_marks",
-            "dks_workspace_size", "dks_lookup_or_insert", "dks_rehash", "memory_layer_step",
+            "dks_workspace_size", "dks_lookup_or_insert", "dks_rehash", "dks_chunk_bytes", "dks_chunk_init",
+            "dks_gather_rows", "memory_layer_step",
             "memory_layer_step_workspace_size", "memory_layer_step_workspace_init",
             "mpzch_lookup_or_insert_static_max_n", "mpzch_lookup_or_insert_static", "ema_update_plan_subset", "ema_update_apply_batch",
             "writeback_apply_batch"]
@@ -477,21 +481,35 @@ def dks_workspace_size(n) -> int:
     return int(load_library().dks_workspace_size(int(n)))
 
 
-def dks_lookup_or_insert(keys, krows, stamps, values, max_rows, next_row, ids, now, insert=True, out_rows=None,
-                         out_hit=None, out_stats=None, ws=None, stream=None):
-    """Decoupled key store lookup (insert=False) or lookup-or-insert.  Returns (rows, hit, stats or None)."""
+def dks_chunk_bytes(chunk_shift, dim) -> int:
+    """Bytes of one value-store chunk of 2^chunk_shift rows (0 for an invalid shift or dim)."""
+    return int(load_library().dks_chunk_bytes(int(chunk_shift), int(dim)))
+
+
+def dks_chunk_init(chunk, chunk_shift, dim, stream=None):
+    """Clears a value-store chunk (a uint8 GPU tensor of dks_chunk_bytes bytes) before it joins the store."""
+    lib = load_library()
+    _dev(chunk, "chunk", torch.uint8)
+    if chunk.numel() < lib.dks_chunk_bytes(int(chunk_shift), int(dim)):
+        raise HLRError("chunk smaller than dks_chunk_bytes(chunk_shift, dim)")
+    _check(lib.dks_chunk_init(_ptr(chunk), int(chunk_shift), int(dim), _stream(chunk.device, stream)),
+           "dks_chunk_init")
+
+
+def dks_lookup_or_insert(keys, krows, chunks, chunk_shift, num_chunks, dim, next_row, ids, now, insert=True,
+                         out_rows=None, out_hit=None, out_stats=None, ws=None, stream=None):
+    """Decoupled key store lookup (insert=False) or lookup-or-insert.  chunks: int64 GPU tensor of the value
+    store's chunk addresses (its first num_chunks entries are used).  Returns (rows, hit, stats or None)."""
     lib = load_library()
     _dev(keys, "keys", torch.int64)
     _dev(krows, "krows", torch.int64)
     _dev(ids, "ids", torch.int64)
-    if stamps is not None:
-        _dev(stamps, "stamps", torch.int64)
-    if values is not None:
-        _dev(values, "values", torch.float32)
+    _dev(chunks, "chunks", torch.int64)
+    if chunks.numel() < int(num_chunks):
+        raise HLRError("chunks holds fewer addresses than num_chunks")
     if next_row is not None:
         _dev(next_row, "next_row", torch.int64)
     dev, n = keys.device, ids.numel()
-    dim = values.shape[1] if values is not None else 0
     rows = out_rows if out_rows is not None else torch.empty(n, dtype=torch.int64, device=dev)
     hit = out_hit if out_hit is not None else torch.empty(n, dtype=torch.int8, device=dev)
     need = lib.dks_workspace_size(n) if insert else 0
@@ -499,11 +517,29 @@ def dks_lookup_or_insert(keys, krows, stamps, values, max_rows, next_row, ids, n
         w, wb = _own_ws(ws, need)
     else:
         w, wb = _ws_args(dev, need)
-    _check(lib.dks_lookup_or_insert(_ptr(keys), _ptr(krows), keys.numel(), _ptr(stamps), _ptr(values), dim,
-                                    int(max_rows), _ptr(next_row), _ptr(ids), n, int(now), 1 if insert else 0,
-                                    _ptr(rows), _ptr(hit), _ptr(out_stats), w, wb, _stream(dev, stream)),
-           "dks_lookup_or_insert")
+    _check(lib.dks_lookup_or_insert(_ptr(keys), _ptr(krows), keys.numel(), _ptr(chunks), int(chunk_shift),
+                                    int(num_chunks), int(dim), _ptr(next_row), _ptr(ids), n, int(now),
+                                    1 if insert else 0, _ptr(rows), _ptr(hit), _ptr(out_stats), w, wb,
+                                    _stream(dev, stream)), "dks_lookup_or_insert")
     return rows, hit, out_stats
+
+
+def dks_gather_rows(chunks, chunk_shift, num_chunks, dim, rows, out=None, stream=None):
+    """out[n][dim] = the value-store vectors of rows (zeros for rows < 0 or beyond the rows held)."""
+    lib = load_library()
+    _dev(chunks, "chunks", torch.int64)
+    _dev(rows, "rows", torch.int64)
+    if chunks.numel() < int(num_chunks):
+        raise HLRError("chunks holds fewer addresses than num_chunks")
+    n = rows.numel()
+    if out is None:
+        out = torch.empty((n, int(dim)), dtype=torch.float32, device=rows.device)
+    _dev(out, "out", torch.float32)
+    if out.numel() != n * int(dim):
+        raise HLRError("out must hold n x dim values")
+    _check(lib.dks_gather_rows(_ptr(chunks), int(chunk_shift), int(num_chunks), int(dim), _ptr(rows), n, _ptr(out),
+                               _stream(rows.device, stream)), "dks_gather_rows")
+    return out
 
 
 def dks_rehash(keys, krows, new_cap, stream=None):

@@ -360,33 +360,52 @@ hlr_status clear_marks(const int64_t *list, int64_t *list_count, int64_t num_row
 
 /* ------------------------------------------------------------------------
  * Decoupled, growable key store   "MTGR: Industrial-Scale Generative
- * Recommendation Framework in Meituan", sec. 3.2 (key store maps a key to a
- * row of a separate value store holding the rows and their eviction
- * metadata; growing copies the light key store only)
+ * Recommendation Framework in Meituan", sec. 3.2 (a light key store maps a key
+ * to a row of a separate value store, which holds the embedding with counters
+ * and timestamps for eviction; growing copies the light key store only)
  *  keys[key_cap], krows[key_cap] int64: the key store, open addressing with
  *    linear probing from SplitMix64-finaliser(key) mod key_cap; key_cap a
  *    power of two; key -1 = empty slot.  Keep at least n empty slots before a
  *    batch (grow with dks_rehash); otherwise results are unspecified.
- *  Value store: values[max_rows*dim] fp32 (nullable: new rows are then not
- *    zero-filled), stamps[max_rows] int64 (last batch that touched the row),
+ *  Value store: chunks of 2^chunk_shift rows (4 <= chunk_shift <= 24), each
+ *    one device allocation of dks_chunk_bytes(chunk_shift, dim) bytes (16-byte
+ *    aligned) laid out as the rows' vectors fp32[2^chunk_shift][dim], then
+ *    their stamps int64[2^chunk_shift] (last batch that touched the row; -1
+ *    never), then their counts uint32[2^chunk_shift] (lookups that reached the
+ *    row); chunks[num_chunks] is a device array of the chunks' addresses, and
+ *    row r lives at row r mod 2^chunk_shift of chunks[r >> chunk_shift].  The
+ *    store holds num_chunks << chunk_shift rows and grows by appending chunks
+ *    (prepared with dks_chunk_init); no row ever moves.  dim % 4 == 0.
  *    next_row: device int64, rows in use (in/out).
- *  Semantics (insert 1): keys already stored are hits (row, stamps[row] =
+ *  Semantics (insert 1): keys already stored are hits (row; the row's stamp =
  *    now); then the distinct missed keys, in order of first occurrence in ids,
- *    take rows next_row, next_row + 1, ... (zero-filled, stamped) while rows
- *    remain; later ones overflow (row -1, not stored).  insert 0 only looks
- *    up and changes nothing.  ids of -1 are invalid (row -1, counted).
+ *    take rows next_row, next_row + 1, ... (vector zero-filled, stamped) while
+ *    the store holds rows; later ones overflow (row -1, not stored).  Every
+ *    position whose key has a row after the batch adds one to that row's
+ *    count (a hit, or any occurrence of a key the batch inserted).  insert 0
+ *    only looks up and changes nothing.  ids of -1 are invalid (row -1,
+ *    counted).
  *  out_rows[n], out_hit[n] int8; out_stats[4] nullable, device int64:
  *    {hit positions, inserted keys, overflowed keys, invalid positions}.
  *  Workspace: dks_workspace_size(n) bytes (insert mode only).
+ * dks_chunk_bytes: bytes of one chunk (0 for an invalid shift or dim).
+ * dks_chunk_init: clears a chunk before it joins the store (vectors and
+ *  counts 0, stamps -1); enqueued on stream.
+ * dks_gather_rows: out[n][dim] fp32 = the vector of row rows[i], or zeros for
+ *  rows[i] < 0 or beyond the rows the store holds.
  * dks_rehash: copies every stored key with its row into an empty key store of
- *  new_cap >= key_cap slots (filled with -1 by the call); rows and values are
+ *  new_cap >= key_cap slots (filled with -1 by the call); the value store is
  *  not touched.
  * --------------------------------------------------------------------- */
 size_t dks_workspace_size(int64_t n);
-hlr_status dks_lookup_or_insert(int64_t *keys, int64_t *krows, int64_t key_cap, int64_t *stamps, float *values,
-                                int64_t dim, int64_t max_rows, int64_t *next_row, const int64_t *ids, int64_t n,
-                                int64_t now, int32_t insert, int64_t *out_rows, int8_t *out_hit,
-                                int64_t *out_stats, void *ws, size_t ws_bytes, hipStream_t stream);
+int64_t dks_chunk_bytes(int32_t chunk_shift, int64_t dim);
+hlr_status dks_chunk_init(void *chunk, int32_t chunk_shift, int64_t dim, hipStream_t stream);
+hlr_status dks_lookup_or_insert(int64_t *keys, int64_t *krows, int64_t key_cap, const uint64_t *chunks,
+                                int32_t chunk_shift, int64_t num_chunks, int64_t dim, int64_t *next_row,
+                                const int64_t *ids, int64_t n, int64_t now, int32_t insert, int64_t *out_rows,
+                                int8_t *out_hit, int64_t *out_stats, void *ws, size_t ws_bytes, hipStream_t stream);
+hlr_status dks_gather_rows(const uint64_t *chunks, int32_t chunk_shift, int64_t num_chunks, int64_t dim,
+                           const int64_t *rows, int64_t n, float *out, hipStream_t stream);
 hlr_status dks_rehash(const int64_t *keys, const int64_t *krows, int64_t key_cap, int64_t *new_keys,
                       int64_t *new_krows, int64_t new_cap, hipStream_t stream);
 

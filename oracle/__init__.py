@@ -61,7 +61,7 @@ def _load():
             lib.orc_sgd_sum.restype = ctypes.c_int
             lib.orc_sgd_sum.argtypes = [p, i64, i64, p, p, i64, ctypes.c_float]
             lib.orc_dks_step.restype = ctypes.c_int
-            lib.orc_dks_step.argtypes = [p, p, i64, p, p, i64, i64, p, p, i64, i64, i32, p, p, p]
+            lib.orc_dks_step.argtypes = [p, p, i64, p, p, p, i64, i64, p, p, i64, i64, i32, p, p, p]
             lib.orc_l2_align.restype = ctypes.c_int
             lib.orc_l2_align.argtypes = [p, i64, i64, p, p, i64, ctypes.c_float]
             lib.orc_quantize_rows.restype = ctypes.c_int
@@ -186,30 +186,37 @@ def sgd_sum(table, rows, g, lr):
 
 
 class KeyStore:
-    """Decoupled key store (open addressing, linear probing) + value store (rows handed out in order)."""
+    """Decoupled key store (open addressing, linear probing) + value store (rows handed out in order, each
+    with its last-touch stamp and lookup count).  max_rows: the arrays' size; step(capacity=...) gives the
+    rows the store holds during that batch (the caller's growth)."""
 
     def __init__(self, key_cap: int, max_rows: int, dim: int, with_values: bool = True):
         self.key_cap, self.max_rows, self.dim = int(key_cap), int(max_rows), int(dim)
         self.keys = np.full(self.key_cap, -1, np.int64)
         self.krows = np.full(self.key_cap, -1, np.int64)
         self.stamps = np.full(self.max_rows, -1, np.int64)
+        self.counts = np.zeros(self.max_rows, np.uint32)
         self.values = np.zeros((self.max_rows, self.dim), np.float32) if with_values else None
         self.next_row = np.zeros(1, np.int64)
 
-    def step(self, ids, now: int, insert: bool = True):
+    def step(self, ids, now: int, insert: bool = True, capacity=None):
         ids = _c(ids, np.int64)
         n = ids.size
+        cap = self.max_rows if capacity is None else int(capacity)
+        if not 0 <= cap <= self.max_rows:
+            raise ValueError("capacity beyond the oracle's arrays")
         rows = np.empty(n, np.int64)
         hit = np.empty(n, np.int8)
         stats = np.zeros(4, np.int64)
         _check(_load().orc_dks_step(_ptr(self.keys), _ptr(self.krows), self.key_cap, _ptr(self.stamps),
-                                    _ptr(self.values), self.dim, self.max_rows, _ptr(self.next_row), _ptr(ids), n,
-                                    int(now), 1 if insert else 0, _ptr(rows), _ptr(hit), _ptr(stats)), "dks_step")
+                                    _ptr(self.counts), _ptr(self.values), self.dim, cap, _ptr(self.next_row),
+                                    _ptr(ids), n, int(now), 1 if insert else 0, _ptr(rows), _ptr(hit), _ptr(stats)),
+               "dks_step")
         return rows, hit, stats
 
     def mapping(self):
-        """{key: row} of the stored keys."""
-        m = self.keys >= 0
+        """{key: row} of the stored keys (every key but -1, the empty marker, is a valid key)."""
+        m = self.keys != -1
         return dict(zip(self.keys[m].tolist(), self.krows[m].tolist()))
 
 

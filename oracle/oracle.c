@@ -283,18 +283,21 @@ int orc_sgd_sum(float *table, int64_t num_rows, int64_t dim, const int64_t *rows
 /* ------------------------------ decoupled, growable key store [MTGR] sec. 3.2 */
 /*
  * Key store and value store are separate ([MTGR] sec. 3.2): the key store maps
- * a raw key to a row of the value store; the value store holds the rows and
- * their metadata (here the last batch that touched the row); growing the key
- * store copies keys only.  Readings: the key store is an open-addressing table
- * of `key_cap` slots (keys[], krows[]; key -1 = empty), linear probing from
- * mix(key) mod key_cap; the value store hands out rows in order (next_row, at
- * most max_rows).  One batch, two phases as for MPZCH: keys already stored are
- * hits (row, stamp = now); then the distinct missed keys, in order of first
- * occurrence, take rows next_row, next_row + 1, ... (zero-filled when values
- * is given, stamp = now) until max_rows, after which they overflow (row -1,
- * nothing stored).  insert == 0 only looks up.  The table must keep at least
- * one empty slot.  stats: {hit positions, inserted keys, overflowed keys,
- * invalid positions}.
+ * a raw key to a row of the value store; the value store holds the rows with
+ * the metadata an eviction policy uses (counters and timestamps: here the last
+ * batch that touched the row and the number of lookups that reached it);
+ * growing the key store copies keys only.  Readings: the key store is an
+ * open-addressing table of `key_cap` slots (keys[], krows[]; key -1 = empty),
+ * linear probing from mix(key) mod key_cap; the value store hands out rows in
+ * order (next_row, below max_rows = the rows the store holds during this
+ * batch; the caller grows it between batches).  One batch, two phases as for
+ * MPZCH: keys already stored are hits (row, stamp = now); then the distinct
+ * missed keys, in order of first occurrence, take rows next_row, next_row + 1,
+ * ... (zero-filled when values is given, stamp = now) until max_rows, after
+ * which they overflow (row -1, nothing stored).  Every position whose key has
+ * a row after the batch adds one to that row's count (counts nullable).
+ * insert == 0 only looks up.  The table must keep at least one empty slot.
+ * stats: {hit positions, inserted keys, overflowed keys, invalid positions}.
  */
 static int64_t orc_dks_find(const int64_t *keys, int64_t key_cap, int64_t key, int64_t *slot) {
     int64_t s = (int64_t)(orc_mix64((uint64_t)key) % (uint64_t)key_cap);
@@ -307,9 +310,9 @@ static int64_t orc_dks_find(const int64_t *keys, int64_t key_cap, int64_t key, i
     return 0;
 }
 
-int orc_dks_step(int64_t *keys, int64_t *krows, int64_t key_cap, int64_t *stamps, float *values, int64_t dim,
-                 int64_t max_rows, int64_t *next_row, const int64_t *ids, int64_t n, int64_t now, int32_t insert,
-                 int64_t *rows, int8_t *hit, int64_t *stats) {
+int orc_dks_step(int64_t *keys, int64_t *krows, int64_t key_cap, int64_t *stamps, uint32_t *counts, float *values,
+                 int64_t dim, int64_t max_rows, int64_t *next_row, const int64_t *ids, int64_t n, int64_t now,
+                 int32_t insert, int64_t *rows, int8_t *hit, int64_t *stats) {
     if (key_cap <= 0 || n < 0 || max_rows < 0 || *next_row < 0 || *next_row > max_rows) return ORC_EINVAL;
     int64_t st[4] = {0, 0, 0, 0};
     /* Phase 1: keys already stored. */
@@ -347,6 +350,9 @@ int orc_dks_step(int64_t *keys, int64_t *krows, int64_t key_cap, int64_t *stamps
             rows[i] = r;
             st[1]++;
         }
+        if (counts)  /* one lookup per position that reached a row */
+            for (int64_t i = 0; i < n; ++i)
+                if (rows[i] >= 0) counts[rows[i]]++;
     }
     for (int k = 0; k < 4; ++k) stats[k] = st[k];
     return ORC_OK;

@@ -229,17 +229,26 @@ def test_publishing_entry_point_argument_errors(lib):
 def test_key_store_argument_errors(lib):
     s = None
     need = lib.dks_workspace_size(10)
-    call = lambda cap, ins, ws, wsb, dim=0, values=None, n=10: lib.dks_lookup_or_insert(
-        P16, P16, cap, P16, values, dim, 100, P16, P16, n, 3, ins, P16, P16, None, ws, wsb, s)
+    call = lambda cap, ins, ws, wsb, dim=8, shift=6, nch=2, chunks=P16, nxt=P16, n=10: lib.dks_lookup_or_insert(
+        P16, P16, cap, chunks, shift, nch, dim, nxt, P16, n, 3, ins, P16, P16, None, ws, wsb, s)
     assert call(1000, 1, P16, need) == INVALID      # key capacity not a power of two
     assert call(1024, 2, P16, need) == INVALID      # insert flag
     assert call(1024, 1, None, 0) == WS_SMALL
     assert call(1024, 1, P16, need - 1) == WS_SMALL
     assert call(1024, 1, ctypes.c_void_p((1 << 20) + 16), need) == MISALIGNED
-    assert call(1024, 1, P16, need, dim=6, values=P16) == DIM
+    assert call(1024, 1, P16, need, dim=6) == DIM
     assert call(1024, 1, P16, need, n=-1) == INVALID
-    assert lib.dks_lookup_or_insert(P16, P16, 1024, None, None, 0, 100, None, P16, 10, 3, 1, P16, P16, None, P16,
-                                    need, s) == INVALID  # insert needs stamps and next_row
+    assert call(1024, 1, P16, need, shift=3) == INVALID and call(1024, 1, P16, need, shift=25) == INVALID
+    assert call(1024, 1, P16, need, chunks=None) == INVALID   # chunks in use but no chunk table
+    assert call(1024, 1, P16, need, chunks=P_ODD) == MISALIGNED
+    assert call(1024, 1, P16, need, nxt=None) == INVALID      # insert needs next_row
+    assert lib.dks_chunk_bytes(6, 8) == (4 * 8 + 8 + 4) * 64
+    assert lib.dks_chunk_bytes(3, 8) == 0 and lib.dks_chunk_bytes(6, 6) == 0
+    assert lib.dks_chunk_init(None, 6, 8, s) == INVALID
+    assert lib.dks_chunk_init(P_ODD, 6, 8, s) == MISALIGNED
+    assert lib.dks_gather_rows(P16, 6, 2, 8, P16, -1, P16, s) == INVALID
+    assert lib.dks_gather_rows(P16, 6, 2, 6, P16, 10, P16, s) == DIM
+    assert lib.dks_gather_rows(P16, 6, 2, 8, P16, 10, P_ODD, s) == MISALIGNED
     assert lib.dks_rehash(P16, P16, 1024, P16, P16, 512, s) == INVALID  # smaller table
     assert lib.dks_rehash(P16, P16, 1024, P16, P16, 3000, s) == INVALID
     assert lib.dks_rehash(P_ODD, P16, 1024, P16, P16, 2048, s) == MISALIGNED

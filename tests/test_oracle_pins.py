@@ -386,9 +386,11 @@ def test_sgd_sum_integer_gradients_are_exact():
 
 # ------------------------------------------------ decoupled key store (MTGR)
 def _dict_store(stream, max_rows):
-    """Reference key -> row map: a Python dict, rows handed out in order of first appearance."""
+    """Reference key -> row map: a Python dict, rows handed out in order of first appearance.
+    max_rows: the rows the store holds, one number or one per batch (a growing value store)."""
     d, out = {}, []
-    for ids in stream:
+    caps = max_rows if isinstance(max_rows, (list, tuple)) else [max_rows] * len(stream)
+    for ids, max_rows in zip(stream, caps):
         rows, hit = [], []
         pending = {}
         for k in ids.tolist():
@@ -423,7 +425,7 @@ def test_key_store_matches_dict_reference_and_table_invariants():
             assert np.array_equal(rows, ref[t][0]) and np.array_equal(hit, ref[t][1]), (key_cap, t)
             assert st[3] == np.count_nonzero(ids == -1) and st[0] == hit.sum()
         assert ks.mapping() == d and ks.next_row[0] == len(d)
-        used = ks.keys >= 0
+        used = ks.keys != -1
         for s in np.nonzero(used)[0]:  # every key reachable from its home slot without crossing an empty slot
             home = oracle.mix64(int(ks.keys[s])) % key_cap
             j = home
@@ -432,6 +434,35 @@ def test_key_store_matches_dict_reference_and_table_invariants():
                 j = (j + 1) % key_cap
         new_rows = np.arange(len(d))
         assert np.all(ks.values[new_rows] == 0) and np.all(ks.values[len(d):] == 1)  # only new rows zeroed
+
+
+def test_key_store_counts_and_growing_value_store_match_dict_reference():
+    """The value store grows between batches (the rows it holds per batch rise in steps, and stay below
+    the keys offered for a while, so keys overflow and later batches insert them): rows, hits and the
+    key -> row map equal the dict reference, and each row's count is the number of positions, over all
+    batches, whose key had that row (a Counter over the reference's rows), never counting overflowed
+    or invalid positions."""
+    g = np.random.default_rng(43)
+    stream = [np.where(g.random(400) < 0.02, -1, g.zipf(1.2, size=400) * 104729 - 7).astype(np.int64)
+              for _ in range(14)]
+    caps = [16, 16, 48, 48, 48, 112, 112, 240, 240, 240, 496, 496, 496, 1008]
+    ks = oracle.KeyStore(2048, 1008, 4)
+    d, ref = _dict_store(stream, caps)
+    want = np.zeros(1008, np.int64)
+    for t, ids in enumerate(stream):
+        rows, hit, st = ks.step(ids, t + 1, capacity=caps[t])
+        assert np.array_equal(rows, ref[t][0]) and np.array_equal(hit, ref[t][1]), t
+        assert ks.next_row[0] <= caps[t]
+        for r in ref[t][0].tolist():
+            if r >= 0:
+                want[r] += 1
+    assert ks.mapping() == d
+    assert np.array_equal(ks.counts.astype(np.int64), want)
+    assert want[:ks.next_row[0]].min() >= 1 and not want[ks.next_row[0]:].any()
+    # a lookup-only batch counts nothing
+    before = ks.counts.copy()
+    ks.step(stream[0], 99, insert=False, capacity=caps[-1])
+    assert np.array_equal(ks.counts, before)
 
 
 def test_key_store_lookup_only_changes_nothing_and_stamps():
