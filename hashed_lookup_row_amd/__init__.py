@@ -58,6 +58,7 @@ def load_library():
             "ema_update_rows_workspace_size": (sz, [i64, i64, i64]),
             "ema_update_rows": (i32, [p, i64, i64, p, p, p, i64, f32, f32, p, sz, p]),
             "gather_dequant_score": (i32, [p, p, p, i64, i64, p, i64, i64, p, p, p]),
+            "mpzch_score": (i32, [p, i64, i32, p, p, p, p, i64, i64, i64, p, p, p, p, p]),
             "hashed_rows": (i32, [p, i64, i64, p, p]),
             "mpzch_zero_inserted": (i32, [p, i64, i64, p, p, i64, p]),
             "writeback_plan": (i32, [i64, p, i64, i32, p, sz, p]),
@@ -95,7 +96,7 @@ def load_library():
 def exported_symbols():
     return ["hlr_status_string", "hlr_version", "mpzch_lookup_or_insert_workspace_size", "mpzch_lookup_or_insert",
             "gather_rows", "dedup_ids_workspace_size", "dedup_ids", "writeback_rows_workspace_size",
-            "writeback_rows", "ema_update_rows_workspace_size", "ema_update_rows", "gather_dequant_score",
+            "writeback_rows", "ema_update_rows_workspace_size", "ema_update_rows", "gather_dequant_score", "mpzch_score",
             "hashed_rows", "mpzch_zero_inserted", "writeback_plan", "writeback_apply", "ema_update_plan",
             "ema_update_apply", "writeback_plan_rows", "quantize_rows_int8", "mark_rows", "clear_marks",
             "dks_workspace_size", "dks_lookup_or_insert", "dks_rehash", "dks_chunk_bytes", "dks_chunk_init",
@@ -264,6 +265,34 @@ def gather_dequant_score(qtable, scale, bias, rows, user, cands, out=None, strea
     _check(lib.gather_dequant_score(_ptr(qtable), _ptr(scale), _ptr(bias), qtable.shape[0], dim, _ptr(rows), nreq,
                                     int(cands), _ptr(user), _ptr(out), _stream(qtable.device, stream)),
            "gather_dequant_score")
+    return out
+
+
+def mpzch_score(identity, probes, ids, qtable, scale, bias, user, cands, out=None, out_rows=None, out_hit=None,
+                stream=None):
+    """Lookup-only MPZCH of ids and the int8 dequant-score of the rows found, in one launch (qtable holds
+    one row per identity slot).  Returns the scores [requests, cands]."""
+    lib = load_library()
+    _dev(identity, "identity", torch.int64)
+    _dev(ids, "ids", torch.int64)
+    _dev(qtable, "qtable", torch.int8)
+    _dev(scale, "scale", torch.float32)
+    _dev(bias, "bias", torch.float32)
+    _dev(user, "user", torch.float32)
+    if qtable.shape[0] != identity.numel():
+        raise HLRError("qtable must hold one row per identity slot")
+    nreq, dim = user.shape[0], qtable.shape[1]
+    if ids.numel() != nreq * int(cands):
+        raise HLRError("ids must hold requests x cands IDs")
+    for t, name, dt in ((out_rows, "out_rows", torch.int64), (out_hit, "out_hit", torch.int8)):
+        if t is not None:
+            _dev(t, name, dt)
+            if t.numel() < ids.numel():
+                raise HLRError(f"{name} must hold one entry per ID")
+    out = out if out is not None else torch.empty((nreq, cands), dtype=torch.float32, device=qtable.device)
+    _check(lib.mpzch_score(_ptr(identity), identity.numel(), int(probes), _ptr(ids), _ptr(qtable), _ptr(scale),
+                           _ptr(bias), dim, nreq, int(cands), _ptr(user), _ptr(out), _ptr(out_rows), _ptr(out_hit),
+                           _stream(qtable.device, stream)), "mpzch_score")
     return out
 
 

@@ -15,6 +15,13 @@
 // then all their row loads are issued before any is used, and each batch of
 // four partial sums is combined across the 16 lanes by halving, which leaves
 // every candidate's total in the lane that loaded its scale and bias.
+//
+// Where a candidate's row comes from is a template parameter: a row array
+// (gather_dequant_score, after a lookup-only MPZCH call), or the MPZCH probe
+// itself (mpzch_score: the lane that owns a candidate reads the ID's bucket of
+// the identity tensor and takes the slot holding the ID, the lookup-only rule
+// of mpzch_lookup_or_insert), which saves the lookup's own launch and its
+// row array's round trip through memory.
 #include "hlr_common.hpp"
 
 namespace {
@@ -22,6 +29,51 @@ using namespace hlr;
 
 constexpr int kThreads = 256;
 constexpr int kCandsPerBlock = 64;
+
+// Candidate rows from a row array.
+struct RowsIn {
+  const int64_t *rows;
+  __device__ __forceinline__ int64_t row(int64_t i, bool) const { return rows[i]; }
+};
+
+// Candidate rows from the identity tensor (lookup only): bucket mix64(id) mod
+// nb, slots bucket * probes + j; the slot holding the ID, or -1.  An ID of -1
+// (the empty marker) never has a row.  The owning lane may record the row and
+// the hit flag.
+struct ProbeIn {
+  const int64_t *ids;
+  const int64_t *identity;
+  uint64_t nb;
+  bool pow2;
+  int probes;
+  int64_t *out_rows;
+  int8_t *out_hit;
+  __device__ __forceinline__ int64_t row(int64_t i, bool own) const {
+    const int64_t id = ids[i];
+    const uint64_t h = mix64(static_cast<uint64_t>(id));
+    const uint64_t b = pow2 ? (h & (nb - 1)) : (h % nb);
+    const int64_t base = static_cast<int64_t>(b) * probes;
+    int64_t r = -1;
+    if (probes == 8) {  // the bucket as four 16-byte loads (identity 16-byte aligned)
+      const longlong2 *q = reinterpret_cast<const longlong2 *>(identity + base);
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const longlong2 v = q[j];
+        if (v.x == id) r = base + 2 * j;
+        if (v.y == id) r = base + 2 * j + 1;
+      }
+    } else {
+      for (int j = 0; j < probes; ++j)
+        if (identity[base + j] == id) r = base + j;
+    }
+    if (id == HLR_EMPTY_ID) r = -1;
+    if (own) {
+      if (out_rows) out_rows[i] = r;
+      if (out_hit) out_hit[i] = r >= 0 ? 1 : 0;
+    }
+    return r;
+  }
+};
 
 __device__ __forceinline__ double dot16(const int4 v, const double *u, double s, double b, double acc) {
   const int w[4] = {v.x, v.y, v.z, v.w};
@@ -81,11 +133,11 @@ __device__ __forceinline__ double group16_scatter4(double a0, double a1, double 
 // candidate 4*(sub & 3) + (sub >> 2) of the group: it loads that candidate's
 // row index, scale and bias, and is the lane that holds the candidate's full
 // sum after the halving reduction of batch sub & 3.
-template <int CPL, int NB>
+template <int CPL, int NB, typename Src>
 __global__ void __launch_bounds__(kThreads)
     score_kernel(const int8_t *__restrict__ q, const float *__restrict__ scale, const float *__restrict__ bias,
-                 int64_t num_rows, int64_t dim, const int64_t *__restrict__ rows, int64_t cands,
-                 const float *__restrict__ user, float *__restrict__ out) {
+                 int64_t num_rows, int64_t dim, Src src, int64_t cands, const float *__restrict__ user,
+                 float *__restrict__ out) {
   constexpr int J = 4 * NB;
   const int64_t req = blockIdx.y;
   const int grp = threadIdx.x >> 4;
@@ -94,7 +146,7 @@ __global__ void __launch_bounds__(kThreads)
   const int kb = sub & 3, kt = sub >> 2;
   const int64_t c = c0 + 4 * kb + kt;
   const bool own = kb < NB && c < cands;
-  const int64_t r = rows[req * cands + (c < cands ? c : cands - 1)];
+  const int64_t r = src.row(req * cands + (c < cands ? c : cands - 1), own);
   const bool ok = own && r >= 0 && r < num_rows;
   const int64_t myrow = ok ? r : 0;
   const double sc = static_cast<double>(scale[myrow]);
@@ -136,10 +188,11 @@ __global__ void __launch_bounds__(kThreads)
 }
 
 // Any dim % 16 == 0: chunks walked in a loop, dequantise-then-dot.
+template <typename Src>
 __global__ void __launch_bounds__(kThreads)
     score_kernel_any(const int8_t *__restrict__ q, const float *__restrict__ scale, const float *__restrict__ bias,
-                     int64_t num_rows, int64_t dim, const int64_t *__restrict__ rows, int64_t cands,
-                     const float *__restrict__ user, float *__restrict__ out) {
+                     int64_t num_rows, int64_t dim, Src src, int64_t cands, const float *__restrict__ user,
+                     float *__restrict__ out) {
   const int64_t req = blockIdx.y;
   const int grp = threadIdx.x >> 4;
   const int sub = threadIdx.x & 15;
@@ -148,7 +201,7 @@ __global__ void __launch_bounds__(kThreads)
   const int64_t c0 = static_cast<int64_t>(blockIdx.x) * kCandsPerBlock;
   const int64_t c1 = c0 + kCandsPerBlock < cands ? c0 + kCandsPerBlock : cands;
   for (int64_t c = c0 + grp; c < c1; c += kGroups) {
-    const int64_t row = rows[req * cands + c];
+    const int64_t row = src.row(req * cands + c, sub == 0);
     const bool ok = row >= 0 && row < num_rows;
     double acc = 0.0;
     if (ok) {
@@ -168,34 +221,70 @@ __global__ void __launch_bounds__(kThreads)
   }
 }
 
+// Checks and launches shared by both entry points: src gives each candidate's row.
+template <typename Src>
+hlr_status score_launch(const int8_t *qtable, const float *scale, const float *bias, int64_t num_rows, int64_t dim,
+                        Src src, int64_t num_requests, int64_t cands_per_request, const float *user_vecs,
+                        float *out_scores, hipStream_t stream) {
+  auto launch = [&](auto kern, int per_block) {
+    dim3 grid(static_cast<unsigned>((cands_per_request + per_block - 1) / per_block),
+              static_cast<unsigned>(num_requests));
+    kern<<<grid, kThreads, 0, stream>>>(qtable, scale, bias, num_rows, dim, src, cands_per_request, user_vecs,
+                                        out_scores);
+  };
+  // Two batches of four candidates per group: enough loads in flight to
+  // cover the row fetches, registers for four waves per SIMD.
+  if (dim == 256) launch(score_kernel<1, 2, Src>, kGroups * 8);
+  else if (dim == 512) launch(score_kernel<2, 2, Src>, kGroups * 8);
+  else launch(score_kernel_any<Src>, kCandsPerBlock);
+  return launch_status();
+}
+
+hlr_status score_args(const int8_t *qtable, const float *scale, const float *bias, int64_t num_rows, int64_t dim,
+                      int64_t num_requests, int64_t cands_per_request, const float *user_vecs, float *out_scores) {
+  if (num_rows < 0 || num_requests < 0 || cands_per_request < 0 || num_requests > 65535) return HLR_INVALID_ARG;
+  if (num_requests * cands_per_request > kMaxN) return HLR_INVALID_ARG;
+  if (dim <= 0 || dim % 16 != 0) return HLR_UNSUPPORTED_DIM;
+  if (num_requests == 0 || cands_per_request == 0) return HLR_OK;
+  if (!user_vecs || !out_scores || (num_rows > 0 && (!qtable || !scale || !bias))) return HLR_INVALID_ARG;
+  if ((qtable && !aligned(qtable, 16)) || !aligned(user_vecs, 4) || !aligned(out_scores, 4) ||
+      (scale && !aligned(scale, 4)) || (bias && !aligned(bias, 4)))
+    return HLR_MISALIGNED;
+  return HLR_OK;
+}
+
 }  // namespace
 
 extern "C" hlr_status gather_dequant_score(const int8_t *qtable, const float *scale, const float *bias,
                                            int64_t num_rows, int64_t dim, const int64_t *rows, int64_t num_requests,
                                            int64_t cands_per_request, const float *user_vecs, float *out_scores,
                                            hipStream_t stream) {
-  if (num_rows < 0 || num_requests < 0 || cands_per_request < 0 || num_requests > 65535) return HLR_INVALID_ARG;
-  if (num_requests * cands_per_request > kMaxN) return HLR_INVALID_ARG;
-  if (dim <= 0 || dim % 16 != 0) return HLR_UNSUPPORTED_DIM;
-  if (num_requests == 0 || cands_per_request == 0) return HLR_OK;
-  if (!rows || !user_vecs || !out_scores || (num_rows > 0 && (!qtable || !scale || !bias))) return HLR_INVALID_ARG;
-  if ((qtable && !aligned(qtable, 16)) || !aligned(rows, 8) || !aligned(user_vecs, 4) || !aligned(out_scores, 4) ||
-      (scale && !aligned(scale, 4)) || (bias && !aligned(bias, 4)))
-    return HLR_MISALIGNED;
+  hlr_status st = score_args(qtable, scale, bias, num_rows, dim, num_requests, cands_per_request, user_vecs,
+                             out_scores);
+  if (st != HLR_OK || num_requests == 0 || cands_per_request == 0) return st;
+  if (!rows) return HLR_INVALID_ARG;
+  if (!aligned(rows, 8)) return HLR_MISALIGNED;
   if (num_rows == 0) {  // every candidate misses (and the kernels' clamped loads would have no row 0)
     hlr_fill(out_scores, num_requests * cands_per_request, 0.0f, stream);
     return launch_status();
   }
-  auto launch = [&](auto kern, int per_block) {
-    dim3 grid(static_cast<unsigned>((cands_per_request + per_block - 1) / per_block),
-              static_cast<unsigned>(num_requests));
-    kern<<<grid, kThreads, 0, stream>>>(qtable, scale, bias, num_rows, dim, rows, cands_per_request, user_vecs,
-                                        out_scores);
-  };
-  // Two batches of four candidates per group: enough loads in flight to
-  // cover the row fetches, registers for four waves per SIMD.
-  if (dim == 256) launch(score_kernel<1, 2>, kGroups * 8);
-  else if (dim == 512) launch(score_kernel<2, 2>, kGroups * 8);
-  else launch(score_kernel_any, kCandsPerBlock);
-  return launch_status();
+  return score_launch(qtable, scale, bias, num_rows, dim, RowsIn{rows}, num_requests, cands_per_request, user_vecs,
+                      out_scores, stream);
+}
+
+extern "C" hlr_status mpzch_score(const int64_t *identity, int64_t capacity, int32_t probes, const int64_t *ids,
+                                  const int8_t *qtable, const float *scale, const float *bias, int64_t dim,
+                                  int64_t num_requests, int64_t cands_per_request, const float *user_vecs,
+                                  float *out_scores, int64_t *out_rows, int8_t *out_hit, hipStream_t stream) {
+  if (capacity <= 0 || probes < 1 || probes > 32 || capacity % probes != 0) return HLR_INVALID_ARG;
+  hlr_status st = score_args(qtable, scale, bias, capacity, dim, num_requests, cands_per_request, user_vecs,
+                             out_scores);
+  if (st != HLR_OK || num_requests == 0 || cands_per_request == 0) return st;
+  if (!identity || !ids || !qtable) return HLR_INVALID_ARG;
+  if (!aligned(identity, probes == 8 ? 16 : 8) || !aligned(ids, 8) || (out_rows && !aligned(out_rows, 8)))
+    return HLR_MISALIGNED;
+  const uint64_t nb = static_cast<uint64_t>(capacity / probes);
+  const ProbeIn src{ids, identity, nb, (nb & (nb - 1)) == 0, probes, out_rows, out_hit};
+  return score_launch(qtable, scale, bias, capacity, dim, src, num_requests, cands_per_request, user_vecs,
+                      out_scores, stream);
 }

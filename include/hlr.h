@@ -322,6 +322,23 @@ hlr_status gather_dequant_score(const int8_t *qtable, const float *scale, const 
                                 hipStream_t stream);
 
 /* ------------------------------------------------------------------------
+ * Serving lookup and score in one launch   [ML] sec. 2 (MPZCH identity
+ *   tensor) and sec. 1, 5 (candidates scored against int8 rows)
+ *  The lookup-only MPZCH rule of mpzch_lookup_or_insert (insert 0: the slot
+ *  of bucket(id) holding the ID, else -1; an ID of -1 never has a row;
+ *  nothing changes) followed by gather_dequant_score, in one launch:
+ *  identity[capacity] (16-byte aligned when probes == 8), probes,
+ *  ids[num_requests*cands_per_request]; qtable/scale/bias hold one row per
+ *  identity slot (num_rows = capacity); other arguments and out_scores as
+ *  gather_dequant_score.  out_rows (int64) and out_hit (int8), nullable,
+ *  receive the lookup's rows and hit mask.
+ * --------------------------------------------------------------------- */
+hlr_status mpzch_score(const int64_t *identity, int64_t capacity, int32_t probes, const int64_t *ids,
+                       const int8_t *qtable, const float *scale, const float *bias, int64_t dim,
+                       int64_t num_requests, int64_t cands_per_request, const float *user_vecs, float *out_scores,
+                       int64_t *out_rows, int8_t *out_hit, hipStream_t stream);
+
+/* ------------------------------------------------------------------------
  * int8 row quantisation for publishing   [ML] sec. 2 (Raw Embedding
  * Streaming quantises the rows a step touched before pushing them to
  * serving) and sec. 5 (serving reads int8 rows)

@@ -232,7 +232,13 @@ def test_serving_score_full_size(dev, prefilled):
         float((err / np.maximum(np.abs(ref.astype(np.float64)), 1e-30)).max())
     assert np.all(got[sel < 0] == 0.0)
     print(f"serving: hit rate {ohit.mean():.4f}, max err/cond {float((err / np.maximum(cond, 1e-300)).max()):.3e}")
-    free(q, scale, bias, user, rows, scores)
+    # the same lookup and score in one launch (the serving bench's step): the same rows, hit mask and scores
+    rows2 = torch.empty_like(rows)
+    hit2 = torch.empty_like(hit)
+    fused = hlr.mpzch_score(identity, cfg.probes, ids, q, scale, bias, user, sv.cands, out_rows=rows2, out_hit=hit2)
+    assert np.array_equal(to_np(rows2), orows) and np.array_equal(to_np(hit2), ohit)
+    assert bits_equal(to_np(fused), got)
+    free(q, scale, bias, user, rows, scores, fused, rows2, hit2)
 
 
 @pytest.mark.timeout(900)

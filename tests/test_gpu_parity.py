@@ -319,6 +319,48 @@ def test_dequant_score(dev, R, K, D):
     assert np.all(got[rows.reshape(R, K) < 0] == 0.0)
 
 
+@pytest.mark.parametrize("P,D", [(8, 512), (8, 256), (4, 48), (8, 48), (16, 512)])
+def test_mpzch_score_matches_lookup_then_score(dev, P, D):
+    """mpzch_score (lookup-only MPZCH and the int8 dequant-score in one launch): rows and hit mask equal
+    the oracle's lookup-only MPZCH (stored IDs, fresh IDs, invalid IDs), and the scores the oracle's
+    dequant-score of those rows (1e-6 relative, absolute floor 1e-12 of sum |x u|); the identity tensor
+    is not changed."""
+    g = np.random.default_rng(P * 1000 + D)
+    C = 4096
+    ids_all = g.integers(0, 1 << 40, size=6000).astype(np.int64)
+    identity = torch.full((C,), -1, dtype=torch.int64, device=dev)
+    stamps = torch.full((C,), -1, dtype=torch.int64, device=dev)
+    tab = oracle.MPZCHTable(C, P, 4, with_values=False)
+    for k in range(3):
+        b = ids_all[k * 2000:(k + 1) * 2000]
+        hlr.mpzch_lookup_or_insert(identity, stamps, None, P, torch.from_numpy(b).to(dev), k + 1)
+        tab.step(b, k + 1, zero_fill=False)
+    R, K = 3, 700
+    cands = np.where(g.random(R * K) < 0.8, g.choice(ids_all, R * K), g.integers(1 << 41, 1 << 42, R * K))
+    cands[::97] = -1  # invalid IDs
+    cands = cands.astype(np.int64)
+    q = np.clip(np.rint(g.standard_normal((C, D)) * 42), -128, 127).astype(np.int8)
+    scale = (g.random(C).astype(np.float32) * 0.004 + 0.001).astype(np.float32)
+    bias = (g.standard_normal(C) * 0.005).astype(np.float32)
+    user = g.standard_normal((R, D)).astype(np.float32)
+    ident_before = to_np(identity).copy()
+    rows_out = torch.empty(R * K, dtype=torch.int64, device=dev)
+    hit_out = torch.empty(R * K, dtype=torch.int8, device=dev)
+    out = hlr.mpzch_score(identity, P, torch.from_numpy(cands).to(dev),
+                          *(torch.from_numpy(x).to(dev) for x in (q, scale, bias, user)), K,
+                          out_rows=rows_out, out_hit=hit_out)
+    orows, ohit, _, _ = tab.step(cands, 0, insert=False)
+    assert np.array_equal(to_np(rows_out), orows) and np.array_equal(to_np(hit_out), ohit)
+    assert 0 < ohit.mean() < 1
+    assert np.array_equal(to_np(identity), ident_before)
+    ref = oracle.dequant_score(q, scale, bias, orows, user, K)
+    x = q.astype(np.float64) * scale[:, None] + bias[:, None]
+    cond = np.einsum("rkd,rd->rk", np.abs(x[np.maximum(orows, 0)].reshape(R, K, D)), np.abs(user.astype(np.float64)))
+    got = to_np(out)
+    assert score_close(got, ref, cond)
+    assert np.all(got[orows.reshape(R, K) < 0] == 0.0)
+
+
 def test_dequant_score_edge_cases(dev):
     """An empty table scores every candidate 0; a ragged last block of candidates (K % 64 != 0)
     and rows at both ends of the table match the oracle."""
