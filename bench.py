@@ -85,7 +85,8 @@ def parse():
                     help="Memory Layer: grouped = the lookup halves of a group of batches back to back, one "
                          "cross-stream wait per stream per group (MemoryLayerPipeline.run); graph = batch by "
                          "batch with lookahead, captured as one HIP graph and replayed; eager = batch by batch "
-                         "with lookahead, call by call")
+                         "with lookahead, call by call.  CS3: eager = step by step; otherwise grouped "
+                         "(EMAPipeline.run, plans a group ahead)")
     ap.add_argument("--group", type=int, default=4, help="grouped schedule: batches per group")
     ap.add_argument("--ahead", type=int, default=1, help="grouped schedule: groups the lookups run ahead")
     ap.add_argument("--no-lookahead", dest="lookahead", action="store_false",
@@ -719,39 +720,66 @@ def run_cs3(args):
     # (table, rows index, values index, masked, a, b) per update, in the order applied
     calls = [("c_user", 0, 3, True, cfg.cts_a, cfg.cts_b), ("c_item", 1, 4, True, cfg.cts_a, cfg.cts_b),
              ("s_user", 0, 5, False, cfg.cms_a, cfg.cms_b), ("s_item", 1, 5, False, cfg.cms_a, cfg.cms_b)]
-    pipe = EMAPipeline([tabs[c[0]] for c in calls], n, lookup_streams=args.ema_lookup_streams,
-                       batch=args.ema_batch)
+    grouped = args.schedule != "eager" and args.ema_batch
+    G, A = args.group, args.ahead
+    pipe = EMAPipeline([tabs[c[0]] for c in calls], n, depth=(A + 2) * G if grouped else 2,
+                       lookup_streams=args.ema_lookup_streams, batch=args.ema_batch)
+
+    def step_args(s):
+        x = inp[s % 2]
+        return ([x[c[1]] for c in calls], [x[2] if c[3] else None for c in calls], [x[c[2]] for c in calls],
+                [(c[4], c[5]) for c in calls])
 
     def piped_step(s, mark=None):
-        x = inp[s % 2]
-        pipe.step([x[c[1]] for c in calls], [x[2] if c[3] else None for c in calls], [x[c[2]] for c in calls],
-                  [(c[4], c[5]) for c in calls], mark=mark)
+        pipe.step(*step_args(s), mark=mark)
 
     def serial_step(s):
         x = inp[s % 2]
         for name, ri, vi, masked, a, b in calls:
             hlr.ema_update_rows(tabs[name], x[ri], x[vi], x[2] if masked else None, a, b)
 
-    for s in range(W):
-        piped_step(s)
-    torch.cuda.synchronize()
     ev = {}
     a, b = timer.event(), timer.event()
-    pool = _EventPool(timer, K * 4 * 2)  # per step: 4 applies x 2 edges
-    # an event on the compute stream after every step: per-step times (median reported), and without them
-    # this schedule has stalled for about 40 ms at the start of the timed region on some runs (a runtime
-    # effect, seen as an idle GPU in kernel traces, never with these events)
-    sev = [timer.event() for _ in range(K)]
-    timer.record(a, cur)
-    h0 = time.perf_counter()
-    for s in range(K):
-        piped_step(W + s, _marker(timer, cur, ev, pool) if s % EV_SAMPLE == 0 else None)
-        timer.record(sev[s], cur)
-    timer.record(b, cur)
-    enqueue_s = time.perf_counter() - h0
-    torch.cuda.synchronize()
-    total = timer.elapsed_s(a, b)
-    step_ms = [timer.elapsed_s(a if s == 0 else sev[s - 1], sev[s]) * 1e3 for s in range(K)]
+    if grouped:
+        # the plans of a group run a group ahead of its applies; one event pair per group on the compute
+        # stream around its back-to-back applies (apply time = span / batches in the group), the ends
+        # giving per-group step times
+        if W:
+            pipe.run([step_args(s) for s in range(W)], group=G, ahead=A)
+        torch.cuda.synchronize()
+        ngroups = (K + G - 1) // G
+        gev = [(timer.event(), timer.event()) for _ in range(ngroups)]
+        todo = [step_args(W + s) for s in range(K)]
+        timer.record(a, cur)
+        h0 = time.perf_counter()
+        pipe.run(todo, group=G, ahead=A, apply_events=gev)
+        timer.record(b, cur)
+        enqueue_s = time.perf_counter() - h0
+        torch.cuda.synchronize()
+        total = timer.elapsed_s(a, b)
+        sizes = [min(G, K - g * G) for g in range(ngroups)]
+        apply_s = [timer.elapsed_s(x, y) / sizes[g] for g, (x, y) in enumerate(gev)]
+        step_ms = [timer.elapsed_s(gev[g - 1][1], gev[g][1]) / sizes[g] * 1e3 for g in range(1, ngroups)] or \
+            [total / K * 1e3]
+    else:
+        for s in range(W):
+            piped_step(s)
+        torch.cuda.synchronize()
+        pool = _EventPool(timer, K * 4 * 2)  # per step: 4 applies x 2 edges
+        # an event on the compute stream after every step: per-step times (median reported), and without them
+        # this schedule has stalled for about 40 ms at the start of the timed region on some runs (a runtime
+        # effect, seen as an idle GPU in kernel traces, never with these events)
+        sev = [timer.event() for _ in range(K)]
+        timer.record(a, cur)
+        h0 = time.perf_counter()
+        for s in range(K):
+            piped_step(W + s, _marker(timer, cur, ev, pool) if s % EV_SAMPLE == 0 else None)
+            timer.record(sev[s], cur)
+        timer.record(b, cur)
+        enqueue_s = time.perf_counter() - h0
+        torch.cuda.synchronize()
+        total = timer.elapsed_s(a, b)
+        step_ms = [timer.elapsed_s(a if s == 0 else sev[s - 1], sev[s]) * 1e3 for s in range(K)]
     c, d = timer.event(), timer.event()
     timer.record(c, cur)
     for s in range(K):
@@ -759,8 +787,11 @@ def run_cs3(args):
     timer.record(d, cur)
     torch.cuda.synchronize()
     serial = timer.elapsed_s(c, d)
-    per = ({"batch": _mean_s(timer, ev, ("apply", -1))} if pipe.batch else
-           {calls[i][0]: _mean_s(timer, ev, ("apply", i)) for i in range(4)})
+    if grouped:
+        per = {"batch": float(np.mean(apply_s))}
+    else:
+        per = ({"batch": _mean_s(timer, ev, ("apply", -1))} if pipe.batch else
+               {calls[i][0]: _mean_s(timer, ev, ("apply", i)) for i in range(4)})
     x = inp[0]
     ur, ir, y = (t.cpu().numpy() for t in x[:3])
     m = int(y.sum())
@@ -780,7 +811,10 @@ def run_cs3(args):
           {"workload": cfg.name, "users": cfg.users, "items": cfg.items, "dim": D, "pairs": n,
            "schedule": f"the EMA plans on {args.ema_lookup_streams} lookup stream(s) (user-keyed and item-keyed "
                        "plans side by side; CMS plans sorted, CTS plans cut out of them by the label mask) beside "
-                       f"{applies} on the compute stream"},
+                       f"{applies} on the compute stream" +
+                       (f"; grouped: plans of {G} steps back to back, {A} group(s) ahead of the applies, one "
+                        "cross-stream wait per stream per group (EMAPipeline.run)" if grouped else
+                        "; step by step, plans one step ahead")},
           roof,
           {"dtype": "fp32", "step_hbm_gbs": tot_bytes / step_s / 1e9,
            "apply_us": {k: v * 1e6 for k, v in per.items()},

@@ -627,6 +627,37 @@ class EMAPipeline:
         keys = {}
         return [keys.setdefault(id(r), len(keys)) % len(self.rings) for r in rows]
 
+    def _check_ids(self, rows, masks, seen):
+        """Checks rows and masks; each distinct tensor once (seen: id -> tensor, filled in)."""
+        if len(rows) != len(self.tables) or len(masks) != len(self.tables):
+            raise HLRError(f"expected rows and masks of {len(self.tables)} updates")
+        for i, (x, m) in enumerate(zip(rows, masks)):
+            if x.numel() > self.n:
+                raise HLRError(f"rows of update {i} has more than {self.n} elements")
+            for t, name, dt, cnt in ((x, "rows", torch.int64, x.numel()), (m, "mask", torch.uint8, x.numel())):
+                if t is not None and id(t) not in seen:
+                    seen[id(t)] = t
+                    if not (t.is_cuda and t.dtype == dt and t.is_contiguous() and t.numel() == cnt):
+                        raise HLRError(f"{name} of update {i} must be a contiguous GPU {dt} tensor of {cnt} elements")
+
+    def _check_vals(self, rows, vals):
+        D = self.tables[0].shape[1]
+        for i, v in enumerate(vals):
+            if not (v.is_cuda and v.dtype == torch.float32 and v.is_contiguous() and v.numel() == rows[i].numel() * D):
+                raise HLRError(f"vals of update {i} must be a contiguous GPU float32 tensor of n x {D} elements")
+
+    def _plan(self, i, rows, masks, src, k, ls):
+        """Enqueues the plan of update i of a batch into slot k on lookup stream ls."""
+        t, lib, wsp = self.tables[i], self._lib, self._wsp[k]
+        n = rows[i].numel()
+        if src[i] is not None:
+            rc = lib.ema_update_plan_subset(t.shape[0], masks[i].data_ptr(), n, wsp[src[i]][0], wsp[src[i]][1],
+                                            wsp[i][0], wsp[i][1], ls)
+        else:
+            rc = lib.ema_update_plan(t.shape[0], rows[i].data_ptr(), None if masks[i] is None else
+                                     masks[i].data_ptr(), n, wsp[i][0], wsp[i][1], ls)
+        _check(rc, "ema plan")
+
     def step(self, rows, masks, vals, coeffs, mark=None):
         """rows[i], masks[i] (or None), vals[i], coeffs[i] = (a, b) for update i of tables[i].
         mark: optional callable, called on the compute stream with ("apply", i, 0 | 1) just
@@ -638,39 +669,22 @@ class EMAPipeline:
         ks = {c: self.rings[c].begin_lookup() for c in used}
         k = ks[used[0]]
         seen = {}
-        for i, (x, m) in enumerate(zip(rows, masks)):  # each distinct input tensor checked and registered once
-            if x.numel() > self.n:
-                raise HLRError(f"rows of update {i} has more than {self.n} elements")
-            for t, name, dt, cnt in ((x, "rows", torch.int64, x.numel()), (m, "mask", torch.uint8, x.numel())):
-                if t is not None and id(t) not in seen:
-                    seen[id(t)] = t
-                    if not (t.is_cuda and t.dtype == dt and t.is_contiguous() and t.numel() == cnt):
-                        raise HLRError(f"{name} of update {i} must be a contiguous GPU {dt} tensor of {cnt} elements")
+        self._check_ids(rows, masks, seen)
         for c in used:
             _on(self.rings[c].lookup, *seen.values())
-        lib, wsp = self._lib, self._wsp[k]
+        lib = self._lib
         for i in order:
-            t, r = self.tables[i], self.rings[chain[i]]
-            n = rows[i].numel()
-            if src[i] is not None:
-                rc = lib.ema_update_plan_subset(t.shape[0], masks[i].data_ptr(), n, wsp[src[i]][0], wsp[src[i]][1],
-                                                wsp[i][0], wsp[i][1], r.ls)
-            else:
-                rc = lib.ema_update_plan(t.shape[0], rows[i].data_ptr(), None if masks[i] is None else
-                                         masks[i].data_ptr(), n, wsp[i][0], wsp[i][1], r.ls)
-            _check(rc, "ema plan")
+            r = self.rings[chain[i]]
+            self._plan(i, rows, masks, src, k, r.ls)
             r.mark(k, i)
         cs = self.ring.cs
         if self.batch:
             for i in order:
                 self.rings[chain[i]].wait(k, i)
             arr = self._arr[k]
-            D = self.tables[0].shape[1]
+            self._check_vals(rows, vals)
             for i in range(len(self.tables)):
-                v = vals[i]
-                if not (v.is_cuda and v.dtype == torch.float32 and v.is_contiguous() and v.numel() == rows[i].numel() * D):
-                    raise HLRError(f"vals of update {i} must be a contiguous GPU float32 tensor of n x {D} elements")
-                arr[i].vals, arr[i].n, arr[i].a, arr[i].b = v.data_ptr(), rows[i].numel(), coeffs[i][0], coeffs[i][1]
+                arr[i].vals, arr[i].n, arr[i].a, arr[i].b = vals[i].data_ptr(), rows[i].numel(), coeffs[i][0], coeffs[i][1]
             _on(self.ring.compute, *vals)
             mark(("apply", -1, 0))
             _check(lib.ema_update_apply_batch(len(self.tables), ctypes.addressof(arr), cs), "ema_update_apply_batch")
@@ -687,6 +701,99 @@ class EMAPipeline:
             mark(("apply", i, 1))
         for r in self.rings:  # every ring advances each step, so their slots stay in step
             r.end_compute(k)
+
+    def run(self, batches, group=4, ahead=1, apply_events=None):
+        """Enqueues a known sequence of batches with one cross-stream wait per stream per group of `group`
+        batches (the schedule of MemoryLayerPipeline.run): each lookup stream enqueues its plans of a group
+        back to back and records one event after the last; the compute stream waits once for each such
+        event, runs the group's batched applies back to back and records one event after the last.  The
+        plans run `ahead` groups ahead of the applies, so a stream normally reaches a wait whose event has
+        completed (free), and the host enqueues two waits per lookup stream and group instead of two per
+        stream and batch (a wait plus the launch after it costs the host about 20 us, more than a launch).
+
+        Needs batch=True (one apply launch per batch).  Ring slots: batch b uses slot b mod depth, so a
+        group's plans reuse the slots of the group depth / group groups back and wait for that group's
+        applies: depth must be a multiple of `group`, at least (ahead + 2) * group.  batches:
+        (rows, masks, vals, coeffs) per batch, as step() takes them.  apply_events: optional list of
+        (begin, end) HIP event pairs, one per group (or None), recorded on the compute stream around the
+        group's applies.  Returns after enqueueing; the lookup streams are then ordered after everything
+        enqueued so far (restart())."""
+        if not self.batch:
+            raise HLRError("run() needs batch=True (distinct tables of one dim, at most four)")
+        G, A, D = int(group), int(ahead), self.ring.depth
+        if G < 1 or A < 1 or D % G != 0 or D < (A + 2) * G:
+            raise HLRError(f"run(): need group >= 1, ahead >= 1 and depth a multiple of group, at least "
+                           f"(ahead + 2) * group (depth {D}, group {G}, ahead {A})")
+        seen, plans = {}, []
+        for b, x in enumerate(batches):
+            if len(x) != 4:
+                raise HLRError(f"batch {b}: expected (rows, masks, vals, coeffs)")
+            rows, masks, vals, coeffs = x
+            self._check_ids(rows, masks, seen)
+            if len(vals) != len(self.tables) or len(coeffs) != len(self.tables):
+                raise HLRError(f"batch {b}: expected vals and coeffs of {len(self.tables)} updates")
+            self._check_vals(rows, vals)
+            for v in vals:
+                seen[id(v)] = v
+            src, order = self._sources(rows, masks)
+            plans.append((src, order, self._chains(rows)))
+        if apply_events is not None and len(apply_events) < (len(batches) + G - 1) // G:
+            raise HLRError("apply_events needs one entry per group")
+        self.restart()
+        r0, h, lib = self.ring, self.ring.hip, self._lib
+        for c, r in enumerate(self.rings):  # the caller's tensors, registered once with each stream using them
+            _on(r.lookup, *(t for t in seen.values() if t.dtype != torch.float32))
+        _on(r0.compute, *(t for t in seen.values() if t.dtype == torch.float32))
+        ngroups = (len(batches) + G - 1) // G
+
+        def last(gi):  # slot of the group's last batch: its events are the group's
+            return (min(len(batches), gi * G + G) - 1) % D
+
+        def streams(gi):
+            return sorted({c for b in range(gi * G, min(len(batches), gi * G + G)) for c in plans[b][2]})
+
+        def lookup_group(gi):
+            b0, b1 = gi * G, min(len(batches), gi * G + G)
+            kl = last(gi)
+            used = streams(gi)
+            if b0 >= D:
+                for c in used:
+                    h.wait(self.rings[c].ls, r0.done[kl])
+            for b in range(b0, b1):
+                rows, masks, _, _ = batches[b]
+                src, order, chain = plans[b]
+                for i in order:
+                    self._plan(i, rows, masks, src, b % D, self.rings[chain[i]].ls)
+            for c in used:
+                self.rings[c].mark(kl, 0)
+
+        def compute_group(gi):
+            b0, b1 = gi * G, min(len(batches), gi * G + G)
+            kl = last(gi)
+            for c in streams(gi):
+                self.rings[c].wait(kl, 0)
+            ev = apply_events[gi] if apply_events is not None else None
+            if ev is not None:
+                h.record(ev[0], r0.cs)
+            for b in range(b0, b1):
+                rows, _, vals, coeffs = batches[b]
+                arr = self._arr[b % D]
+                for i in range(len(self.tables)):
+                    arr[i].vals, arr[i].n = vals[i].data_ptr(), rows[i].numel()
+                    arr[i].a, arr[i].b = coeffs[i][0], coeffs[i][1]
+                _check(lib.ema_update_apply_batch(len(self.tables), ctypes.addressof(arr), r0.cs),
+                       "ema_update_apply_batch")
+            if ev is not None:
+                h.record(ev[1], r0.cs)
+            h.record(r0.done[kl], r0.cs)
+
+        for gi in range(min(A, ngroups)):
+            lookup_group(gi)
+        for gi in range(ngroups):
+            if gi + A < ngroups:
+                lookup_group(gi + A)
+            compute_group(gi)
+        self.restart()
 
 
 class RESPublisher:

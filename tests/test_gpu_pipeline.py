@@ -477,3 +477,66 @@ def test_ema_pipeline(dev, derive, lookup_streams, batch):
         oracle.ema(cpu[3], it, v[2], None, cfg.cms_a, cfg.cms_b)
     for k, name in enumerate(names):
         assert bits_equal(to_np(gpu[k]), cpu[k]), name
+
+
+@pytest.mark.parametrize("group,ahead,lookup_streams,derive", [(4, 1, 2, True), (2, 2, 2, True), (3, 1, 1, False),
+                                                               (1, 1, 2, True)])
+def test_ema_grouped_run_matches_oracle(dev, group, ahead, lookup_streams, derive):
+    """EMAPipeline.run() (plans a group ahead, one wait per stream and group) between step() calls: every
+    table bit-equal to the oracle's batch-order EMA after all batches (CS3 page, sec. 2), with a last
+    group shorter than the others and batches of different sizes."""
+    cfg = synth.CS3
+    users, items, D, n = 4096, 8192, 128, 12_000
+    g = np.random.default_rng(17 + group)
+    shapes = [users, items, users, items]
+    cpu = [np.zeros((m, D), np.float32) for m in shapes]
+    gpu = [torch.zeros((m, D), dtype=torch.float32, device=dev) for m in shapes]
+    batches = []
+    for s in range(12):
+        m = n - 1000 * (s % 3)
+        u = np.minimum(synth.zipf_ranks(g, users, 1.1, m), users - 1).astype(np.int64)
+        it = np.minimum(synth.zipf_ranks(g, items, 1.05, m), items - 1).astype(np.int64)
+        y = (g.random(m) < 0.05).astype(np.uint8)
+        v = [g.standard_normal((m, D)).astype(np.float32) for _ in range(3)]
+        batches.append((u, it, y, v))
+    dev_b = [tuple(torch.from_numpy(x).to(dev) for x in (u, it, y)) + ([torch.from_numpy(x).to(dev) for x in v],)
+             for (u, it, y, v) in batches]
+    torch.cuda.synchronize()
+    depth = (ahead + 2) * group
+    pipe = pipeline.EMAPipeline(gpu, n, depth=depth, derive=derive, lookup_streams=lookup_streams)
+    coeffs = [(cfg.cts_a, cfg.cts_b), (cfg.cts_a, cfg.cts_b), (cfg.cms_a, cfg.cms_b), (cfg.cms_a, cfg.cms_b)]
+
+    def args(b):
+        ur, ir, yy, vv = b
+        return [ur, ir, ur, ir], [yy, yy, None, None], [vv[0], vv[1], vv[2], vv[2]], coeffs
+
+    pipe.step(*args(dev_b[0]))
+    pipe.step(*args(dev_b[1]))
+    pipe.run([args(b) for b in dev_b[2:11]], group=group, ahead=ahead)
+    pipe.step(*args(dev_b[11]))
+    for (u, it, y, v) in batches:
+        oracle.ema(cpu[0], u, v[0], y, cfg.cts_a, cfg.cts_b)
+        oracle.ema(cpu[1], it, v[1], y, cfg.cts_a, cfg.cts_b)
+        oracle.ema(cpu[2], u, v[2], None, cfg.cms_a, cfg.cms_b)
+        oracle.ema(cpu[3], it, v[2], None, cfg.cms_a, cfg.cms_b)
+    for k in range(4):
+        assert bits_equal(to_np(gpu[k]), cpu[k]), k
+
+
+def test_ema_grouped_run_argument_errors(dev):
+    """run() needs the batched apply and a ring that holds (ahead + 2) groups (host-side errors)."""
+    D, n = 16, 64
+    tabs = [torch.zeros((256, D), dtype=torch.float32, device=dev) for _ in range(2)]
+    rows = torch.arange(n, dtype=torch.int64, device=dev)
+    vals = torch.zeros((n, D), dtype=torch.float32, device=dev)
+    b = ([rows, rows], [None, None], [vals, vals], [(0.5, 0.5), (0.5, 0.5)])
+    with pytest.raises(hlr.HLRError):
+        pipeline.EMAPipeline(tabs, n, depth=6).run([b], group=4)
+    with pytest.raises(hlr.HLRError):
+        pipeline.EMAPipeline(tabs, n, depth=12, batch=False).run([b], group=4)
+    with pytest.raises(hlr.HLRError):
+        pipeline.EMAPipeline(tabs, n, depth=12).run([([rows], [None], [vals], [(0.5, 0.5)])], group=4)
+    pipe = pipeline.EMAPipeline(tabs, n, depth=12)
+    pipe.run([b, b], group=4)
+    torch.cuda.synchronize()
+    assert bool((tabs[0][:n] == 0).all().item())
