@@ -6,8 +6,8 @@
 // Plan: positions that take part are grouped by row with a stable radix sort
 // (radix.hpp), so each row's positions come out in batch order.  A row's
 // positions are applied in order (T = fl(fl(a*T) + fl(b*v))): short rows by
-// one wave each (light part), long rows by one wave per (chunk, 16- or
-// 8-element slice), the chunks of a row running in parallel from speculative
+// one wave each (light part), long rows by one wave per (chunk, 32-element
+// slice), the chunks of a row running in parallel from speculative
 // warmed-up states (heavy part) that ema_combine verifies bit for bit.  The
 // result equals the sequential loop bit for bit.  The plan lists the long
 // rows' runs, so one launch (ema_apply_kernel) holds both parts, for up to
@@ -30,7 +30,7 @@ __device__ __forceinline__ float4 ema_step(float4 t, float4 v, float a, float b)
 }
 
 // Row loads in flight per wave in the light part.  The launch's register
-// budget is set by the heavy part's narrow walk (about 136 registers, three
+// budget is set by the heavy part's slice walk (about 117 registers, four
 // waves per SIMD), so the light rows at dim <= 256 keep 16 rows in flight per
 // wave to make up for the lower occupancy.
 template <int NC>
@@ -86,16 +86,20 @@ __device__ __forceinline__ void ema_light(float4 *table, const float4 *__restric
 __device__ __forceinline__ float ema1(float t, float v, float a, float b) { return a * t + b * v; }
 
 // A heavy chunk is one dependent chain per element, so its speed is set by how
-// many of its positions are requested ahead: its waves walk 16-element slices,
-// four positions per load instruction, 56 instructions (224 positions) a batch.
-// When chunks are long (L >= kWideChunk: a slowly decaying a, so a long
-// warm-up) the chains are few and long and their latency is the whole cost:
-// then 8-element slices, eight positions per instruction (448 a batch), at
-// the price of 32-byte accesses.
-constexpr int kHeavyP = 56;
-constexpr int kWideChunk = 2048;
+// many of its positions are requested ahead, and by how well its scattered
+// value reads use the lines they fetch: its waves walk 32-element slices (one
+// 128-byte line of a position's value row), two positions per load
+// instruction, 48 instructions (96 positions) a batch, which keeps the launch
+// at 117 registers and four waves per SIMD (56 instructions: 125-133
+// registers, three waves per SIMD, 183 us).  Measured on the CS3 step's
+// batched apply (four updates, dim 128): 164 us, against 183 us with
+// 16-element slices (four positions per instruction, each fetching half a
+// line that another wave fetches again) and 8-element slices for the longest
+// chunks, and 200 us with 64-element slices (one position per instruction).
+constexpr int kHeavyG = 2;  // lane groups (positions per load instruction)
+constexpr int kHeavyP = 48;
 
-// Heavy rows: one wave per (chunk of <= L occurrences, 16-element slice).  A
+// Heavy rows: one wave per (chunk of <= L occurrences, 32-element slice).  A
 // row with one chunk is applied exactly from its stored value.  For a longer
 // row, chunk 0 runs exactly; chunk m > 0 starts W occurrences early from a zero
 // state (the recurrence contracts by a per step, so after W steps the state no
@@ -103,7 +107,7 @@ constexpr int kWideChunk = 2048;
 // its first occurrence) and tau (the state after its last) for ema_combine.
 // The plan lists runs of kBaseRun; a chunk is L / kBaseRun of them, and the
 // wave of a run that does not start a chunk has nothing to do.
-template <int G>
+template <int G, bool Off32>
 __device__ __forceinline__ void ema_heavy(float *table, const float *__restrict__ vals,
                                           const uint32_t *__restrict__ skey, const uint32_t *__restrict__ spos,
                                           const int32_t *__restrict__ seg_start, const int32_t *__restrict__ seg_end,
@@ -136,7 +140,7 @@ __device__ __forceinline__ void ema_heavy(float *table, const float *__restrict_
     int32_t w0 = whole ? s : from, w1 = whole ? end : j0;
     float sig = st;
     for (int k = 0; k < 2; ++k) {
-      slice_run_narrow<G, kHeavyP>(vals, spos, w0, w1, D, e, [&](int32_t, float x) { st = ema1(st, x, a, b); });
+      slice_run_narrow<G, kHeavyP, Off32>(vals, spos, w0, w1, D, e, [&](int32_t, float x) { st = ema1(st, x, a, b); });
       if (k == 0) {
         sig = st;
         w0 = w1;
@@ -166,9 +170,9 @@ struct EmaJob {
   const int2 *hlist;
   const int32_t *clist;
   float *partial;
+  int64_t n;  // positions (rows of vals)
   float a, b;
   int L, W;
-  int wide;  // eight lane groups in the heavy walk (long chunks)
   int heavy_begin, heavy_blocks, light_begin, light_blocks, comb_begin, comb_blocks;
 };
 
@@ -182,18 +186,15 @@ struct EmaJobs {
   int64_t D;
 };
 
-template <int NC>
+// Off32: every update's values are under 2 GiB (32-bit offsets in the heavy walk).
+template <int NC, bool Off32>
 __global__ void __launch_bounds__(kThreads) ema_apply_kernel(EmaJobs js) {
   const int blk = static_cast<int>(blockIdx.x);
   for (int i = 0; i < js.count; ++i) {
     const EmaJob &j = js.job[i];
     if (blk >= j.heavy_begin && blk < j.heavy_begin + j.heavy_blocks) {
-      if (j.wide)
-        ema_heavy<8>(j.table, j.vals, j.skey, j.spos, j.seg_start, j.seg_end, j.counters, j.hlist, j.a, j.b, js.D,
-                     j.L, j.W, j.partial, blk - j.heavy_begin, j.heavy_blocks);
-      else
-        ema_heavy<4>(j.table, j.vals, j.skey, j.spos, j.seg_start, j.seg_end, j.counters, j.hlist, j.a, j.b, js.D,
-                     j.L, j.W, j.partial, blk - j.heavy_begin, j.heavy_blocks);
+      ema_heavy<kHeavyG, Off32>(j.table, j.vals, j.skey, j.spos, j.seg_start, j.seg_end, j.counters, j.hlist, j.a,
+                                j.b, js.D, j.L, j.W, j.partial, blk - j.heavy_begin, j.heavy_blocks);
       return;
     }
     if (blk >= j.light_begin && blk < j.light_begin + j.light_blocks) {
@@ -284,16 +285,17 @@ __global__ void __launch_bounds__(kThreads) ema_combine_kernel(EmaJobs js) {
 // a = 0.95 and 0.99 about one 128-element slice in a thousand still differs
 // after W steps; a slice that differs is recomputed by ema_combine).  A chunk's
 // wave walks W + L positions and reads a value row for each, so L >= max(256,
-// 2W) keeps the redundant warm-up reads at most half of a chunk's; L is a
-// whole number of the plan's runs (kBaseRun), and a row of at most L
-// occurrences runs whole, as one exact chain.  Without contraction (a outside
-// (0, 1)) rows run whole.
+// 3W) keeps the redundant warm-up reads at most a third of a chunk's (against
+// 2W: a third fewer redundant reads for chains a third longer, 1% faster on
+// the CS3 step); L is a whole number of the plan's runs
+// (kBaseRun), and a row of at most L occurrences runs whole, as one exact
+// chain.  Without contraction (a outside (0, 1)) rows run whole.
 inline void ema_plan(float a, int64_t n, int *L, int *W) {
   int64_t len;
   if (a > 0.f && a < 1.f) {
     const double w = std::ceil(28.0 / -std::log(static_cast<double>(a)));
     *W = static_cast<int>(w < 1048576.0 ? w : 1048576.0);
-    len = 2 * static_cast<int64_t>(*W);
+    len = 3 * static_cast<int64_t>(*W);
   } else {
     *W = 0;
     len = n;
@@ -321,6 +323,7 @@ EmaJob ema_job(float *table, const float *vals, int64_t n, int64_t dim, float a,
   EmaJob j{};
   j.table = table;
   j.vals = vals;
+  j.n = n;
   j.seg_key = w.seg_key;
   j.skey = w.k[cur];
   j.spos = w.v[cur];
@@ -334,9 +337,8 @@ EmaJob ema_job(float *table, const float *vals, int64_t n, int64_t dim, float a,
   j.a = a;
   j.b = b;
   ema_plan(a, n, &j.L, &j.W);
-  j.wide = j.L >= kWideChunk;
   j.light_blocks = grid_for(n, 4 * 4) < 4096 ? grid_for(n, 4 * 4) : 4096;
-  const int64_t hs = j.wide ? Narrow<8>::slices(dim) : Narrow<4>::slices(dim);
+  const int64_t hs = Narrow<kHeavyG>::slices(dim);
   j.heavy_blocks = grid_for(n / 32 * hs, 4) < 2048 ? grid_for(n / 32 * hs, 4) : 2048;
   j.comb_blocks = grid_for(n / 256 * num_slices(dim), 4) < 1024 ? grid_for(n / 256 * num_slices(dim), 4) : 1024;
   return j;
@@ -361,9 +363,17 @@ void ema_launch(EmaJobs &js, hipStream_t s) {
   }
   if (next == 0) return;
   const int64_t nc = (js.D / 4 + kWave - 1) / kWave;
-  if (nc == 1) ema_apply_kernel<1><<<next, kThreads, 0, s>>>(js);
-  else if (nc == 2) ema_apply_kernel<2><<<next, kThreads, 0, s>>>(js);
-  else ema_apply_kernel<4><<<next, kThreads, 0, s>>>(js);
+  bool off32 = true;
+  for (int i = 0; i < js.count; ++i) off32 = off32 && js.job[i].n * js.D * 4 < (int64_t(1) << 31);
+  if (off32) {
+    if (nc == 1) ema_apply_kernel<1, true><<<next, kThreads, 0, s>>>(js);
+    else if (nc == 2) ema_apply_kernel<2, true><<<next, kThreads, 0, s>>>(js);
+    else ema_apply_kernel<4, true><<<next, kThreads, 0, s>>>(js);
+  } else {
+    if (nc == 1) ema_apply_kernel<1, false><<<next, kThreads, 0, s>>>(js);
+    else if (nc == 2) ema_apply_kernel<2, false><<<next, kThreads, 0, s>>>(js);
+    else ema_apply_kernel<4, false><<<next, kThreads, 0, s>>>(js);
+  }
   if (comb > 0) ema_combine_kernel<<<comb, kThreads, 0, s>>>(js);
 }
 

@@ -783,7 +783,9 @@ __device__ __forceinline__ uint32_t row_to_row0(uint32_t x, int r) {
 // permute through LDS.
 template <int G>
 __device__ __forceinline__ float from_group(float x, int g, int lane) {
-  if constexpr (G == 4) {
+  if constexpr (G == 2) {  // two groups of 32 lanes: rows 2-3 onto rows 0-1
+    return g == 0 ? x : __uint_as_float(row_to_row0(__float_as_uint(x), 2 * g));
+  } else if constexpr (G == 4) {
     return __uint_as_float(row_to_row0(__float_as_uint(x), g));
   } else if constexpr (G == 8) {
     const uint32_t y = row_to_row0(__float_as_uint(x), g >> 1);
@@ -795,7 +797,11 @@ __device__ __forceinline__ float from_group(float x, int g, int lane) {
   }
 }
 
-template <int G, int P, typename F>
+// Off32: src holds less than 2 GiB, so a position's element is addressed by a
+// 32-bit byte offset from src through a buffer load (one register per load
+// address instead of two: with 56 loads in flight that decides the walk's
+// register count, hence the occupancy).
+template <int G, int P, bool Off32, typename F>
 __device__ __forceinline__ void slice_run_narrow(const float *__restrict__ src, const uint32_t *__restrict__ spos,
                                                  int32_t j0, int32_t j1, int64_t D, int64_t e, F f) {
   constexpr int W = 64 / G;
@@ -805,9 +811,13 @@ __device__ __forceinline__ void slice_run_narrow(const float *__restrict__ src, 
   const int lane = hlr::lane_id();
   const int h = lane / W;
   const int64_t ec = e < D ? e : 0;
+  const uint32_t row_bytes = static_cast<uint32_t>(D * 4);
+  const uint32_t ecol4 = static_cast<uint32_t>(ec) * 4u;
   j0 = __builtin_amdgcn_readfirstlane(j0);
   j1 = __builtin_amdgcn_readfirstlane(j1);
   if (j0 >= j1) return;
+  const __amdgpu_buffer_rsrc_t rs =
+      __builtin_amdgcn_make_buffer_rsrc(const_cast<float *>(src), 0, 0x7fffffff, 0x00020000);
   uint32_t pv[NI];
 #pragma unroll
   for (int i = 0; i < NI; ++i) {
@@ -818,8 +828,21 @@ __device__ __forceinline__ void slice_run_narrow(const float *__restrict__ src, 
     SliceV x[P];
 #pragma unroll
     for (int u = 0; u < P; ++u) {
-      const uint32_t p = static_cast<uint32_t>(__shfl(static_cast<int>(pv[(G * u) / 64]), (G * u) % 64 + h));
-      x[u] = src[static_cast<int64_t>(p) * D + ec];
+      if constexpr (G == 2 && Off32) {
+        // the two positions by readlane, their byte offsets in scalar registers, one select per lane: no
+        // lane permute (one address register per distinct source lane, 32 of them here, all live)
+        const int q = (2 * u) % 64;
+        const uint32_t o0 = static_cast<uint32_t>(__builtin_amdgcn_readlane(static_cast<int>(pv[(2 * u) / 64]), q));
+        const uint32_t o1 = static_cast<uint32_t>(__builtin_amdgcn_readlane(static_cast<int>(pv[(2 * u) / 64]), q + 1));
+        const uint32_t off = (h ? o1 * row_bytes : o0 * row_bytes) + ecol4;
+        x[u] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rs, off, 0, 0));
+      } else {
+        const uint32_t p = static_cast<uint32_t>(__shfl(static_cast<int>(pv[(G * u) / 64]), (G * u) % 64 + h));
+        if (Off32)
+          x[u] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rs, p * row_bytes + ecol4, 0, 0));
+        else
+          x[u] = src[static_cast<int64_t>(p) * D + ec];
+      }
     }
 #pragma unroll
     for (int i = 0; i < NI; ++i) {  // next batch's indices, behind this batch's rows

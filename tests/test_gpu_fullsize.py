@@ -294,13 +294,14 @@ def test_dlrm_hashed_tables_full_size(dev):
 
 def test_cs3_ema_full_size(dev):
     """The bench's launch configuration: EMAPipeline (user-keyed and item-keyed plans on two lookup
-    streams, CTS plans cut out of the CMS plans, the four applies as one batched launch), ten steps of
-    262,144 pairs without synchronising in between; all four tables bit for bit after every step's
-    sequential oracle."""
+    streams, CTS plans cut out of the CMS plans, the four applies as one batched launch) in the grouped
+    schedule (run(): plans of four steps back to back, a group ahead of the applies) for ten steps of
+    262,144 pairs, after two step() calls, without synchronising in between; all four tables bit for bit
+    against the sequential oracle over the twelve steps."""
     from hashed_lookup_row_amd.pipeline import EMAPipeline
     cfg = synth.CS3
     D, n = cfg.dim, cfg.batch
-    steps = 10
+    steps = 12
     shapes = {"c_user": cfg.users, "s_user": cfg.users, "c_item": cfg.items, "s_item": cfg.items}
     gpu = {k: torch.zeros((m, D), dtype=torch.float32, device=dev) for k, m in shapes.items()}
     cpu = {k: np.zeros((m, D), np.float32) for k, m in shapes.items()}
@@ -311,10 +312,12 @@ def test_cs3_ema_full_size(dev):
         inp.append(((urows, irows, y), [torch.from_numpy(x).to(dev) for x in (urows, irows, y)], dvals))
     calls = [("c_user", 0, 0, True, cfg.cts_a, cfg.cts_b), ("c_item", 1, 1, True, cfg.cts_a, cfg.cts_b),
              ("s_user", 0, 2, False, cfg.cms_a, cfg.cms_b), ("s_item", 1, 2, False, cfg.cms_a, cfg.cms_b)]
-    pipe = EMAPipeline([gpu[c[0]] for c in calls], n, lookup_streams=2, batch=True)
-    for _, x, v in inp:
-        pipe.step([x[c[1]] for c in calls], [x[2] if c[3] else None for c in calls], [v[c[2]] for c in calls],
-                  [(c[4], c[5]) for c in calls])
+    pipe = EMAPipeline([gpu[c[0]] for c in calls], n, depth=12, lookup_streams=2, batch=True)
+    args = [([x[c[1]] for c in calls], [x[2] if c[3] else None for c in calls], [v[c[2]] for c in calls],
+             [(c[4], c[5]) for c in calls]) for _, x, v in inp]
+    pipe.step(*args[0])
+    pipe.step(*args[1])
+    pipe.run(args[2:], group=4, ahead=1)
     torch.cuda.synchronize()
     for step, ((urows, irows, y), _, v) in enumerate(inp, start=1):
         vn = [to_np(x) for x in v]
@@ -324,3 +327,21 @@ def test_cs3_ema_full_size(dev):
     for k in shapes:
         assert bits_equal(to_np(gpu[k]), cpu[k]), k
     free(*gpu.values())
+
+
+def test_ema_values_over_2gib(dev):
+    """EMA update with a values array of 2 GiB (n = 524,288 positions of 1024 floats): the heavy walk
+    then addresses values with 64-bit offsets instead of 32-bit buffer offsets.  Few rows, so every
+    row is long and cut into chunks; bit for bit against the oracle's batch-order loop (CS3 page, sec. 2)."""
+    cfg = synth.CS3
+    n, D, R = 524_288, 1024, 97
+    g = np.random.default_rng(23)
+    rows = np.minimum(synth.zipf_ranks(g, R, 1.1, n), R - 1).astype(np.int64)
+    vals = g.standard_normal((n, D), dtype=np.float32)
+    table = g.standard_normal((R, D), dtype=np.float32)
+    assert vals.nbytes >= 1 << 31
+    t = torch.from_numpy(table).to(dev)
+    hlr.ema_update_rows(t, torch.from_numpy(rows).to(dev), torch.from_numpy(vals).to(dev), None, cfg.cms_a, cfg.cms_b)
+    torch.cuda.synchronize()
+    oracle.ema(table, rows, vals, None, cfg.cms_a, cfg.cms_b)
+    assert bits_equal(to_np(t), table)
