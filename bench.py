@@ -628,10 +628,13 @@ def run_dlrm(args):
     D, n = cfg.dim, cfg.per_table
     R = D * 4
     tables = []
+    t0 = time.time()
     for t, nr in enumerate(cfg.table_rows):
         x = torch.empty((nr, D), dtype=torch.float32, device=dev)
         synth.dlrm_fill_table(t, nr, D, x)
         tables.append(x)
+        torch.cuda.synchronize()
+        print(f"[bench] table {t} ({nr} x {D}) filled, {time.time() - t0:.1f}s", file=sys.stderr, flush=True)
     K, W = args.steps, args.warmup
     keys = [[torch.from_numpy(synth.dlrm_keys(cfg, t, s + 1)).to(dev) for t in range(8)] for s in range(2)]
     grads = [[synth.normal_rows(n, D, cfg.g_std, 4, 100 * s + t, device=dev) for t in range(8)] for s in range(2)]
@@ -659,6 +662,8 @@ def run_dlrm(args):
     timer.record(b, cur)
     torch.cuda.synchronize()
     total = timer.elapsed_s(a, b)
+    print(f"[bench] {K} pipelined steps: {total / K * 1e3:.3f} ms per step; one-stream leg next", file=sys.stderr,
+          flush=True)
     c, d = timer.event(), timer.event()
     timer.record(c, cur)
     for s in range(K):
