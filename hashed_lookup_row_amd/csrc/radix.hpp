@@ -776,11 +776,12 @@ __device__ __forceinline__ uint32_t row_to_row0(uint32_t x, int r) {
   return __builtin_amdgcn_permlane16_swap(y, y, false, false)[1];
 }
 
-// Group g's value (same lane within the group) in the lanes of group 0.  Four
-// groups of 16 lanes are the four rows; eight groups of 8 lanes are the row
-// halves: the group's row is brought to row 0, then an odd group's half is
-// rotated onto lanes 0-7 (DPP row_ror:8).  Other group counts use a lane
-// permute through LDS.
+// Group g's value (same lane within the group) in the lanes of group 0.  Two
+// groups of 32 lanes are the wave's halves (one permlane32_swap: the walk the
+// EMA uses); four groups of 16 lanes are the four rows; eight groups of 8
+// lanes are the row halves: the group's row is brought to row 0, then an odd
+// group's half is rotated onto lanes 0-7 (DPP row_ror:8).  Other group counts
+// use a lane permute through LDS.
 template <int G>
 __device__ __forceinline__ float from_group(float x, int g, int lane) {
   if constexpr (G == 2) {  // two groups of 32 lanes: rows 2-3 onto rows 0-1
@@ -798,9 +799,10 @@ __device__ __forceinline__ float from_group(float x, int g, int lane) {
 }
 
 // Off32: src holds less than 2 GiB, so a position's element is addressed by a
-// 32-bit byte offset from src through a buffer load (one register per load
-// address instead of two: with 56 loads in flight that decides the walk's
-// register count, hence the occupancy).
+// 32-bit byte offset from src through a buffer load.  With two lane groups the
+// offsets are formed without a lane permute (below): a permute per position
+// kept one address register live per distinct source lane, which with dozens
+// of loads in flight set the walk's register count, hence the occupancy.
 template <int G, int P, bool Off32, typename F>
 __device__ __forceinline__ void slice_run_narrow(const float *__restrict__ src, const uint32_t *__restrict__ spos,
                                                  int32_t j0, int32_t j1, int64_t D, int64_t e, F f) {
