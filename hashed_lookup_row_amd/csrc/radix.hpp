@@ -1029,9 +1029,8 @@ __device__ __forceinline__ bool heavy_item(const uint32_t (&cnt)[kLenBuckets], c
 // positions and reach each row by a lane permute; P load instructions per
 // batch plus P / 4 index loads stay within the 63-load counter.  (Double
 // buffering two batches of half the size measured slower on the hashed-tables
-// step: while other blocks stream at full bandwidth a batch's memory latency is
-// several times its adds, and the positions in flight per wave are what
-// count.)  grad(x) turns
+// step; the caller's batch size is measured too: more positions in flight per
+// batch is not faster here.)  grad(x) turns
 // a loaded value into the term summed (the L2-alignment gradient).  lds: this
 // wave's kChainSlots * 64 floats.  Only lane 0 of each row returns a
 // meaningful sum.

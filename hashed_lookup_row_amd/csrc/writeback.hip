@@ -280,9 +280,16 @@ __device__ __forceinline__ void sgd_light(float4 *table, const float4 *__restric
 // Heavy rows: one block of four waves per (row, 16-element slice); wave w
 // takes elements 16 * slice + 4w + r in its rows r = 0..3, each one chain over
 // all the row's positions in batch order (chain_sum16), then lane 0 of the row
-// writes fl(M - fl(lr * s)).  Blocks take items in the plan's order, longest
+// writes fl(M - fl(lr * s)).  24 load instructions (384 positions) a batch:
+// one hot row of 24,576 occurrences at dim 512 alone took 19.8 ns per position
+// with 48 and 14.8 with 24 (12-16: no faster), and the hashed-tables apply
+// 531-553 us against 561-574 (with the light rows beside them the heavy part is
+// bound by its random 64-byte reads, not by the chain: with the light rows
+// skipped it still takes about 510 us).  Blocks take items in the plan's order, longest
 // rows first.  L2: every gradient is taken at the row before the batch, which
 // no block writes before its own chain has read it (one block per element).
+constexpr int kHeavyBatch = 24;  // load instructions per batch of the heavy walk
+
 template <bool L2, bool Off32>
 __device__ __forceinline__ void sgd_heavy(float *table, const float *__restrict__ g,
                                           const uint32_t *__restrict__ skey, const uint32_t *__restrict__ spos,
@@ -319,7 +326,7 @@ __device__ __forceinline__ void sgd_heavy(float *table, const float *__restrict_
     const int64_t at = static_cast<int64_t>(skey[s]) * D + (el < D ? el : 0);
     const float mv = table[at];
     const float acc =
-        chain_sum16<48, Off32>(g, spos, s, end, D, el, lds[wv], [&](float x) { return L2 ? l2_grad(mv, x) : x; });
+        chain_sum16<kHeavyBatch, Off32>(g, spos, s, end, D, el, lds[wv], [&](float x) { return L2 ? l2_grad(mv, x) : x; });
     if ((lane_id() & 15) == 0 && el < D) {
       const float st = lr * acc;
       table[at] = mv - st;  // fl(M - fl(lr * s))
