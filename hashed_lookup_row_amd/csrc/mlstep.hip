@@ -62,11 +62,19 @@ __global__ void __launch_bounds__(ml::kThreads)
   const uint32_t total = hc.x;
   const uint32_t last1 = hc.y;  // last position + 1
   const int32_t pv = w.gpos[d.z + (static_cast<uint32_t>(lane) < cnt ? lane : 0)];
-  const bool whole = !norow && total == cnt;
+  // whole is the same in every lane (one descriptor, one record): a scalar
+  // branch, so a group that does not apply the Writeback now loads no e (an
+  // e read from row 0 and dropped cost about 1 us per batch in L2 traffic)
+  const bool whole = __builtin_amdgcn_readfirstlane(static_cast<int>(!norow && total == cnt)) != 0;
   float4 e[NC];
-  const int64_t eb = whole ? static_cast<int64_t>(last1 - 1) * v4 : 0;
+  if (whole) {
+    const int64_t eb = static_cast<int64_t>(last1 - 1) * v4;
 #pragma unroll
-  for (int c = 0; c < NC; ++c) e[c] = src[eb + col[c]];
+    for (int c = 0; c < NC; ++c) e[c] = src[eb + col[c]];
+  } else {
+#pragma unroll
+    for (int c = 0; c < NC; ++c) e[c] = make_float4(0.f, 0.f, 0.f, 0.f);
+  }
   if (!read) {
 #pragma unroll
     for (int c = 0; c < NC; ++c) m[c] = make_float4(0.f, 0.f, 0.f, 0.f);
