@@ -100,6 +100,12 @@ def parse():
     ap.add_argument("--no-dlrm-batch", dest="dlrm_batch", action="store_false",
                     help="DLRM: one ring and one SGD apply launch per table instead of one batched apply")
     ap.add_argument("--dlrm-group", type=int, default=4, help="DLRM: tables per batched SGD apply")
+    ap.add_argument("--ema-derive", default="auto", choices=["auto", "yes", "no"],
+                    help="CS3: cut the CTS plans out of the CMS plans (yes) or sort them on their own (no); auto: "
+                         "no with pairs (the two pair plans then run on two lookup streams), yes without")
+    ap.add_argument("--no-ema-pairs", dest="ema_pairs", action="store_false",
+                    help="CS3: plan each of the four updates on its own instead of the user- and item-keyed update "
+                         "of each rule by one sort (EMAPipeline pairs)")
     ap.add_argument("--no-ema-batch", dest="ema_batch", action="store_false",
                     help="cs3: one apply launch per update instead of ema_update_apply_batch")
     ap.add_argument("--copy-calibration", action="store_true",
@@ -726,9 +732,11 @@ def run_cs3(args):
     calls = [("c_user", 0, 3, True, cfg.cts_a, cfg.cts_b), ("c_item", 1, 4, True, cfg.cts_a, cfg.cts_b),
              ("s_user", 0, 5, False, cfg.cms_a, cfg.cms_b), ("s_item", 1, 5, False, cfg.cms_a, cfg.cms_b)]
     grouped = args.schedule != "eager" and args.ema_batch
+    derive = {"yes": True, "no": False}.get(args.ema_derive, not args.ema_pairs)
     G, A = args.group, args.ahead
     pipe = EMAPipeline([tabs[c[0]] for c in calls], n, depth=(A + 2) * G if grouped else 2,
-                       lookup_streams=args.ema_lookup_streams, batch=args.ema_batch)
+                       lookup_streams=args.ema_lookup_streams, batch=args.ema_batch, pairs=args.ema_pairs,
+                       derive=derive)
 
     def step_args(s):
         x = inp[s % 2]
@@ -805,8 +813,8 @@ def run_cs3(args):
     tot_bytes = sum(nb.values()) + 4 * 9 * n
     step_s = total / K
     if pipe.batch:
-        roof = _roof("ema_update_apply_batch (the four updates: ema_apply_kernel + ema_combine_kernel)",
-                     sum(nb.values()), per["batch"])
+        roof = _roof(("ema_update_apply_pairs" if args.ema_pairs else "ema_update_apply_batch") +
+                     " (the four updates: ema_apply_kernel + ema_combine_kernel)", sum(nb.values()), per["batch"])
         applies = "the four applies as one ema_update_apply_batch call"
     else:
         worst = max(per, key=lambda k: per[k])
@@ -814,9 +822,14 @@ def run_cs3(args):
         applies = "the four applies"
     _line("interaction pairs/s (CTS + CMS EMA row updates)", n / step_s, "pairs/s", K, W, step_s * 1e3,
           {"workload": cfg.name, "users": cfg.users, "items": cfg.items, "dim": D, "pairs": n,
-           "schedule": f"the EMA plans on {args.ema_lookup_streams} lookup stream(s) (user-keyed and item-keyed "
-                       "plans side by side; CMS plans sorted, CTS plans cut out of them by the label mask) beside "
-                       f"{applies} on the compute stream" +
+           "schedule": (f"each rule's user- and item-keyed updates planned by one sort (CMS and CTS pair plans"
+                        + (", CTS cut out of CMS by the label mask" if derive else ", each sorted on its own") +
+                        f") on {args.ema_lookup_streams} lookup stream(s), beside the four applies as one "
+                        "ema_update_apply_pairs call on the compute stream" if args.ema_pairs else
+                        f"the EMA plans on {args.ema_lookup_streams} lookup stream(s) (user-keyed and item-keyed "
+                        "plans side by side; CMS plans sorted, CTS plans "
+                        + ("cut out of them by the label mask" if derive else "sorted on their own") +
+                        f") beside {applies} on the compute stream") +
                        (f"; grouped: plans of {G} steps back to back, {A} group(s) ahead of the applies, one "
                         "cross-stream wait per stream per group (EMAPipeline.run)" if grouped else
                         "; step by step, plans one step ahead")},

@@ -67,6 +67,9 @@ def load_library():
             "ema_update_apply": (i32, [p, i64, i64, p, i64, f32, f32, p, sz, p]),
             "ema_update_plan_subset": (i32, [i64, p, i64, p, sz, p, sz, p]),
             "ema_update_apply_batch": (i32, [i32, p, p]),
+            "ema_update_pair_workspace_size": (sz, [i64, i64, i64, i64]),
+            "ema_update_plan_pair": (i32, [i64, p, i64, p, p, i64, p, sz, p]),
+            "ema_update_apply_pairs": (i32, [i32, p, p]),
             "writeback_apply_batch": (i32, [i32, p, i32, p]),
             "writeback_plan_rows": (i32, [i64, i64, p, sz, p, p, p]),
             "quantize_rows_int8": (i32, [p, i64, i64, p, i64, p, i32, p, p, p, p]),
@@ -103,7 +106,7 @@ def exported_symbols():
             "dks_gather_rows", "memory_layer_step",
             "memory_layer_step_workspace_size", "memory_layer_step_workspace_init",
             "mpzch_lookup_or_insert_static_max_n", "mpzch_lookup_or_insert_static", "ema_update_plan_subset", "ema_update_apply_batch",
-            "writeback_apply_batch"]
+            "writeback_apply_batch", "ema_update_pair_workspace_size", "ema_update_plan_pair", "ema_update_apply_pairs"]
 
 
 def _check(rc: int, what: str):
@@ -438,6 +441,75 @@ def ema_update_apply_batch(updates, stream=None):
         return
     _check(lib.ema_update_apply_batch(len(updates), ctypes.cast(arr, ctypes.c_void_p), _stream(dev, stream)),
            "ema_update_apply_batch")
+
+
+def ema_pair_workspace_size(num_rows0, num_rows1, dim, n) -> int:
+    """Bytes of a pair plan's workspace (0 for sizes out of range)."""
+    return int(load_library().ema_update_pair_workspace_size(int(num_rows0), int(num_rows1), int(dim), int(n)))
+
+
+def ema_update_plan_pair(num_rows0, rows0, num_rows1, rows1, mask, ws, stream=None):
+    """One plan for two updates keyed by rows0 (a table of num_rows0 rows) and rows1 (num_rows1 rows), with the
+    same mask (or None); its subsets come from ema_update_plan_subset(num_rows0 + num_rows1, mask2, ...)
+    with a mask of n elements and a workspace of ema_pair_workspace_size."""
+    lib = load_library()
+    _dev(rows0, "rows0", torch.int64)
+    _dev(rows1, "rows1", torch.int64)
+    n = rows0.numel()
+    if rows1.numel() != n:
+        raise HLRError("rows0 and rows1 must have the same number of positions")
+    if mask is not None:
+        _dev(mask, "mask", torch.uint8)
+        if mask.numel() != n:
+            raise HLRError("mask must have one entry per position")
+    w, wb = _own_ws(ws, lib.ema_update_pair_workspace_size(int(num_rows0), int(num_rows1), 4, n))
+    _check(lib.ema_update_plan_pair(int(num_rows0), _ptr(rows0), int(num_rows1), _ptr(rows1), _ptr(mask), n, w, wb,
+                                    _stream(rows0.device, stream)), "ema_update_plan_pair")
+
+
+def ema_update_plan_pair_subset(num_rows0, num_rows1, mask, src_ws, ws, stream=None):
+    """The pair plan of the positions of the pair plan in src_ws whose mask (n elements) is set."""
+    lib = load_library()
+    _dev(mask, "mask", torch.uint8)
+    n = mask.numel()
+    need = lib.ema_update_pair_workspace_size(int(num_rows0), int(num_rows1), 4, n)
+    sw, swb = _own_ws(src_ws, need)
+    w, wb = _own_ws(ws, need)
+    _check(lib.ema_update_plan_subset(int(num_rows0) + int(num_rows1), _ptr(mask), 2 * n, sw, swb, w, wb,
+                                      _stream(mask.device, stream)), "ema_update_plan_subset")
+
+
+class _EmaApplyPair(ctypes.Structure):
+    """hlr_ema_apply_pair (include/hlr.h)."""
+    _fields_ = [("table0", ctypes.c_void_p), ("num_rows0", ctypes.c_int64), ("vals0", ctypes.c_void_p),
+                ("table1", ctypes.c_void_p), ("num_rows1", ctypes.c_int64), ("vals1", ctypes.c_void_p),
+                ("dim", ctypes.c_int64), ("n", ctypes.c_int64), ("a", ctypes.c_float), ("b", ctypes.c_float),
+                ("ws", ctypes.c_void_p), ("ws_bytes", ctypes.c_size_t)]
+
+
+def ema_update_apply_pairs(pairs, stream=None):
+    """Applies up to four pair plans in one launch; each pair is (table0, vals0, table1, vals1, a, b, ws) with its
+    plan in ws.  The results equal ema_update_apply on each table in turn."""
+    lib = load_library()
+    arr = (_EmaApplyPair * max(1, len(pairs)))()
+    dev = None
+    for i, (t0, v0, t1, v1, a, b, ws) in enumerate(pairs):
+        for t, name in ((t0, "table0"), (v0, "vals0"), (t1, "table1"), (v1, "vals1")):
+            _dev(t, name, torch.float32)
+        dim = t0.shape[1]
+        if t1.shape[1] != dim:
+            raise HLRError("both tables of a pair must have the same dim")
+        n = v0.numel() // dim
+        if v1.numel() != n * dim:
+            raise HLRError("vals0 and vals1 must both hold n x dim values")
+        w, wb = _own_ws(ws, lib.ema_update_pair_workspace_size(t0.shape[0], t1.shape[0], dim, n))
+        arr[i] = _EmaApplyPair(t0.data_ptr(), t0.shape[0], v0.data_ptr(), t1.data_ptr(), t1.shape[0], v1.data_ptr(),
+                               dim, n, float(a), float(b), w.value, wb)
+        dev = t0.device
+    if not pairs:
+        return
+    _check(lib.ema_update_apply_pairs(len(pairs), ctypes.cast(arr, ctypes.c_void_p), _stream(dev, stream)),
+           "ema_update_apply_pairs")
 
 
 def ema_update_apply(table, vals, a, b, ws, stream=None):

@@ -41,7 +41,8 @@ constexpr int light_batch() { return NC == 4 ? 4 : (NC == 2 ? 8 : 16); }
 // while the current row is processed (wave-uniform, so scalar loads).  Longer
 // rows belong to the heavy part.
 template <int NC>
-__device__ __forceinline__ void ema_light(float4 *table, const float4 *__restrict__ vals,
+__device__ __forceinline__ void ema_light(float4 *table0, const float4 *__restrict__ vals0, float4 *table1,
+                                          const float4 *__restrict__ vals1, uint32_t split,
                                           const uint32_t *__restrict__ seg_key, const uint32_t *__restrict__ spos,
                                           const int32_t *__restrict__ seg_start, const int32_t *__restrict__ seg_end,
                                           const int64_t *__restrict__ nseg_p, float a, float b, int64_t v4,
@@ -59,6 +60,11 @@ __device__ __forceinline__ void ema_light(float4 *table, const float4 *__restric
     const int32_t sn = seg_start[kc], en = seg_end[kc];
     const int64_t rn = seg_key[kc];
     if (e - s < kHeavyMin) {
+      // a pair plan's keys from split on are rows of the second table
+      const bool second = r >= split;
+      float4 *table = second ? table1 : table0;
+      const float4 *vals = second ? vals1 : vals0;
+      if (second) r -= split;
       float4 st[NC];
 #pragma unroll
       for (int q = 0; q < NC; ++q) {
@@ -108,7 +114,8 @@ constexpr int kHeavyP = 48;
 // The plan lists runs of kBaseRun; a chunk is L / kBaseRun of them, and the
 // wave of a run that does not start a chunk has nothing to do.
 template <int G, bool Off32>
-__device__ __forceinline__ void ema_heavy(float *table, const float *__restrict__ vals,
+__device__ __forceinline__ void ema_heavy(float *table0, const float *__restrict__ vals0, float *table1,
+                                          const float *__restrict__ vals1, uint32_t split,
                                           const uint32_t *__restrict__ skey, const uint32_t *__restrict__ spos,
                                           const int32_t *__restrict__ seg_start, const int32_t *__restrict__ seg_end,
                                           const uint32_t *__restrict__ counters, const int2 *__restrict__ hlist,
@@ -127,7 +134,11 @@ __device__ __forceinline__ void ema_heavy(float *table, const float *__restrict_
     const int64_t e = (it % S) * HeavySlices::kWidth + (lane % HeavySlices::kWidth);
     const bool act = lane < HeavySlices::kWidth && e < D;  // lane group 0 holds the chain
     const int32_t s = seg_start[km.x], end = seg_end[km.x];
-    const int64_t r = skey[s];
+    const uint32_t key = skey[s];
+    const bool second = key >= split;  // a pair plan's row of the second table
+    float *table = second ? table1 : table0;
+    const float *vals = second ? vals1 : vals0;
+    const int64_t r = second ? key - split : key;
     const int32_t j0 = s + m * L;
     const int32_t j1 = static_cast<int64_t>(j0) + L < end ? j0 + L : end;
     const bool exact_start = m == 0 || j0 - W <= s;
@@ -163,6 +174,9 @@ __device__ __forceinline__ void ema_heavy(float *table, const float *__restrict_
 struct EmaJob {
   float *table;
   const float *vals;
+  float *table1;        // a pair plan: keys from split on are rows of table1, valued by vals1
+  const float *vals1;
+  uint32_t split;       // 0xffffffff: one table
   const uint32_t *seg_key, *skey, *spos;
   const int32_t *seg_start, *seg_end;
   const int64_t *nseg;
@@ -193,12 +207,14 @@ __global__ void __launch_bounds__(kThreads) ema_apply_kernel(EmaJobs js) {
   for (int i = 0; i < js.count; ++i) {
     const EmaJob &j = js.job[i];
     if (blk >= j.heavy_begin && blk < j.heavy_begin + j.heavy_blocks) {
-      ema_heavy<kHeavyG, Off32>(j.table, j.vals, j.skey, j.spos, j.seg_start, j.seg_end, j.counters, j.hlist, j.a,
+      ema_heavy<kHeavyG, Off32>(j.table, j.vals, j.table1, j.vals1, j.split, j.skey, j.spos, j.seg_start, j.seg_end, j.counters, j.hlist, j.a,
                                 j.b, js.D, j.L, j.W, j.partial, blk - j.heavy_begin, j.heavy_blocks);
       return;
     }
     if (blk >= j.light_begin && blk < j.light_begin + j.light_blocks) {
-      ema_light<NC>(reinterpret_cast<float4 *>(j.table), reinterpret_cast<const float4 *>(j.vals), j.seg_key, j.spos,
+      ema_light<NC>(reinterpret_cast<float4 *>(j.table), reinterpret_cast<const float4 *>(j.vals),
+                    reinterpret_cast<float4 *>(j.table1), reinterpret_cast<const float4 *>(j.vals1), j.split,
+                    j.seg_key, j.spos,
                     j.seg_start, j.seg_end, j.nseg, j.a, j.b, js.D / 4, blk - j.light_begin, j.light_blocks);
       return;
     }
@@ -213,7 +229,8 @@ __global__ void __launch_bounds__(kThreads) ema_apply_kernel(EmaJobs js) {
 // so they are loaded kCombineBatch chunks at a time ahead of it.
 constexpr int kCombineBatch = 16;
 
-__device__ __forceinline__ void ema_combine(float *table, const float *__restrict__ vals,
+__device__ __forceinline__ void ema_combine(float *table0, const float *__restrict__ vals0, float *table1,
+                                            const float *__restrict__ vals1, uint32_t split,
                                             const uint32_t *__restrict__ skey, const uint32_t *__restrict__ spos,
                                             const int32_t *__restrict__ seg_start,
                                             const int32_t *__restrict__ seg_end,
@@ -227,6 +244,11 @@ __device__ __forceinline__ void ema_combine(float *table, const float *__restric
     const int32_t k = clist[it / S];
     const int32_t s = seg_start[k], end = seg_end[k];
     if (end - s <= L) continue;  // one chunk: walked whole by the heavy part
+    const uint32_t key = skey[s];
+    const bool second = key >= split;  // a pair plan's row of the second table
+    float *table = second ? table1 : table0;
+    const float *vals = second ? vals1 : vals0;
+    const int64_t row = second ? key - split : key;
     const int64_t e = (it % S) * kSliceElems + lane_id();
     const bool act = e < D;
     const int64_t ec = act ? e : 0;
@@ -263,7 +285,7 @@ __device__ __forceinline__ void ema_combine(float *table, const float *__restric
       slice_run(vals, spos, c0, c1, D, e, [&](int32_t, float x) { cur = ema1(cur, x, a, b); });
       m += bad + 1;
     }
-    if (act) table[skey[s] * D + e] = cur;
+    if (act) table[row * D + e] = cur;
   }
 }
 
@@ -272,8 +294,8 @@ __global__ void __launch_bounds__(kThreads) ema_combine_kernel(EmaJobs js) {
   for (int i = 0; i < js.count; ++i) {
     const EmaJob &j = js.job[i];
     if (blk >= j.comb_begin && blk < j.comb_begin + j.comb_blocks) {
-      ema_combine(j.table, j.vals, j.skey, j.spos, j.seg_start, j.seg_end, j.counters, j.clist, j.a, j.b, js.D, j.L,
-                  j.partial, blk - j.comb_begin, j.comb_blocks);
+      ema_combine(j.table, j.vals, j.table1, j.vals1, j.split, j.skey, j.spos, j.seg_start, j.seg_end, j.counters,
+                  j.clist, j.a, j.b, js.D, j.L, j.partial, blk - j.comb_begin, j.comb_blocks);
       return;
     }
   }
@@ -313,8 +335,11 @@ inline size_t ema_partial_elems(int64_t n, int64_t dim) {
 
 // The job of one update: its plan's buffers in ws (grouped by group_by_row),
 // chunking for a, and its block counts.
+// A pair plan (table1 != NULL): n counts both updates' pairs, num_rows both
+// tables' rows, and keys from split (the first table's rows) on belong to table1.
 EmaJob ema_job(float *table, const float *vals, int64_t n, int64_t dim, float a, float b, void *ws,
-               int64_t num_rows) {
+               int64_t num_rows, float *table1 = nullptr, const float *vals1 = nullptr,
+               uint32_t split = 0xffffffffu) {
   SegWork<uint32_t> w;
   Carver c(ws);
   c.off = segwork_layout<uint32_t>(n, &w, ws);
@@ -323,6 +348,9 @@ EmaJob ema_job(float *table, const float *vals, int64_t n, int64_t dim, float a,
   EmaJob j{};
   j.table = table;
   j.vals = vals;
+  j.table1 = table1;
+  j.vals1 = vals1;
+  j.split = table1 ? split : 0xffffffffu;
   j.n = n;
   j.seg_key = w.seg_key;
   j.skey = w.k[cur];
@@ -482,6 +510,81 @@ extern "C" hlr_status ema_update_apply_batch(int32_t count, const hlr_ema_apply 
         return HLR_INVALID_ARG;
     }
     js.job[js.count++] = ema_job(u.table, u.vals, u.n, u.dim, u.a, u.b, u.ws, u.num_rows);
+  }
+  if (js.count == 0) return HLR_OK;
+  ema_launch(js, stream);
+  return launch_status();
+}
+
+namespace {
+
+// A pair plan's sizes: both tables' rows below the 32-bit key range (the
+// sentinel num_rows0 + num_rows1 is a key too), both updates' pairs within
+// the batch limit.
+hlr_status pair_args(int64_t num_rows0, int64_t num_rows1, int64_t n) {
+  if (num_rows0 < 0 || num_rows1 < 0 || n < 0 || n > kMaxN / 2) return HLR_INVALID_ARG;
+  return ema_args(num_rows0 + num_rows1, 2 * n);
+}
+
+}  // namespace
+
+extern "C" size_t ema_update_pair_workspace_size(int64_t num_rows0, int64_t num_rows1, int64_t dim, int64_t n) {
+  if (pair_args(num_rows0, num_rows1, n) != HLR_OK) return 0;
+  return ema_update_rows_workspace_size(num_rows0 + num_rows1, dim, 2 * n);
+}
+
+extern "C" hlr_status ema_update_plan_pair(int64_t num_rows0, const int64_t *rows0, int64_t num_rows1,
+                                           const int64_t *rows1, const uint8_t *mask, int64_t n, void *ws,
+                                           size_t ws_bytes, hipStream_t stream) {
+  hlr_status st = pair_args(num_rows0, num_rows1, n);
+  if (st != HLR_OK) return st;
+  if (n == 0 || num_rows0 + num_rows1 == 0) return HLR_OK;
+  if (!rows0 || !rows1) return HLR_INVALID_ARG;
+  if (!aligned(rows0, 8) || !aligned(rows1, 8)) return HLR_MISALIGNED;
+  if ((st = ema_ws(ws, ws_bytes, ema_update_pair_workspace_size(num_rows0, num_rows1, 4, n))) != HLR_OK) return st;
+  SegWork<uint32_t> w;
+  segwork_layout<uint32_t>(2 * n, &w, ws);
+  group_by_row_pair(w, rows0, num_rows0, rows1, num_rows1, mask, stream);
+  list_heavy_units(w, stream);
+  return launch_status();
+}
+
+extern "C" hlr_status ema_update_apply_pairs(int32_t count, const hlr_ema_apply_pair *pairs, hipStream_t stream) {
+  if (count < 0 || count > kMaxEmaJobs || (count > 0 && !pairs)) return HLR_INVALID_ARG;
+  EmaJobs js{};
+  js.D = 0;
+  for (int32_t i = 0; i < count; ++i) {
+    const hlr_ema_apply_pair &u = pairs[i];
+    hlr_status st = pair_args(u.num_rows0, u.num_rows1, u.n);
+    if (st != HLR_OK) return st;
+    if (u.dim <= 0 || u.dim % 4 != 0 || u.dim > 1024) return HLR_UNSUPPORTED_DIM;
+    if (u.n == 0 || u.num_rows0 + u.num_rows1 == 0) continue;
+    if ((u.num_rows0 > 0 && (!u.table0 || !u.vals0)) || (u.num_rows1 > 0 && (!u.table1 || !u.vals1)))
+      return HLR_INVALID_ARG;
+    if ((u.table0 && !aligned(u.table0, 16)) || (u.vals0 && !aligned(u.vals0, 16)) ||
+        (u.table1 && !aligned(u.table1, 16)) || (u.vals1 && !aligned(u.vals1, 16)))
+      return HLR_MISALIGNED;
+    const size_t wb = ema_update_pair_workspace_size(u.num_rows0, u.num_rows1, u.dim, u.n);
+    if ((st = ema_ws(u.ws, u.ws_bytes, wb)) != HLR_OK) return st;
+    if (js.D != 0 && u.dim != js.D) return HLR_INVALID_ARG;  // one dim per launch
+    js.D = u.dim;
+    const size_t tb0 = static_cast<size_t>(u.num_rows0) * static_cast<size_t>(u.dim) * sizeof(float);
+    const size_t tb1 = static_cast<size_t>(u.num_rows1) * static_cast<size_t>(u.dim) * sizeof(float);
+    if (u.num_rows0 > 0 && u.num_rows1 > 0 && ranges_overlap(u.table0, tb0, u.table1, tb1)) return HLR_INVALID_ARG;
+    for (int32_t k = 0; k < i; ++k) {  // the updates run at once: no shared table or workspace
+      const hlr_ema_apply_pair &v = pairs[k];
+      if (v.n == 0 || v.num_rows0 + v.num_rows1 == 0) continue;
+      const size_t vb0 = static_cast<size_t>(v.num_rows0) * static_cast<size_t>(v.dim) * sizeof(float);
+      const size_t vb1 = static_cast<size_t>(v.num_rows1) * static_cast<size_t>(v.dim) * sizeof(float);
+      if ((tb0 && vb0 && ranges_overlap(u.table0, tb0, v.table0, vb0)) ||
+          (tb0 && vb1 && ranges_overlap(u.table0, tb0, v.table1, vb1)) ||
+          (tb1 && vb0 && ranges_overlap(u.table1, tb1, v.table0, vb0)) ||
+          (tb1 && vb1 && ranges_overlap(u.table1, tb1, v.table1, vb1)) ||
+          ranges_overlap(u.ws, wb, v.ws, ema_update_pair_workspace_size(v.num_rows0, v.num_rows1, v.dim, v.n)))
+        return HLR_INVALID_ARG;
+    }
+    js.job[js.count++] = ema_job(u.table0, u.vals0, 2 * u.n, u.dim, u.a, u.b, u.ws, u.num_rows0 + u.num_rows1,
+                                 u.table1, u.vals1, static_cast<uint32_t>(u.num_rows0));
   }
   if (js.count == 0) return HLR_OK;
   ema_launch(js, stream);

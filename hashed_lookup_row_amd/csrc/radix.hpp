@@ -190,6 +190,22 @@ struct RowPairs {
   __device__ __forceinline__ uint32_t pos(int64_t i) const { return static_cast<uint32_t>(i); }
 };
 
+// The rows of two tables as one key space (a pair plan: two updates keyed by
+// different rows, planned by one sort).  Pair i < n is position i of rows0
+// with its row; pair n + i is position i of rows1 with num_rows0 + its row.
+// A row out of range takes the sentinel num_rows0 + num_rows1.
+struct PairRowPairs {
+  const int64_t *rows0, *rows1;
+  int64_t n, num_rows0, num_rows1;
+  __device__ __forceinline__ uint32_t key(int64_t i) const {
+    const bool second = i >= n;
+    const int64_t r = second ? rows1[i - n] : rows0[i];
+    const int64_t lim = second ? num_rows1 : num_rows0;
+    return static_cast<uint32_t>(r >= 0 && r < lim ? (second ? num_rows0 + r : r) : num_rows0 + num_rows1);
+  }
+  __device__ __forceinline__ uint32_t pos(int64_t i) const { return static_cast<uint32_t>(i >= n ? i - n : i); }
+};
+
 // init_ticket / init_nact (first pass over RowPairs only): block 0 also clears
 // the plan's counters and records that all n pairs take part.
 template <typename K, int ITEMS, typename Src>
@@ -436,21 +452,19 @@ struct NoEmit {
 };
 
 // Runs every radix pass; returns the index (0/1) of the buffer holding the result.
-// rows != NULL: the first pass reads the pairs from the batch's rows (RowPairs)
-// and sets up the plan's counters and active count on the way; then every
-// element takes part (nact is written, not read, by that pass).
-template <typename K, int ITEMS>
-inline int radix_sort_pairs_t(SegWork<K> &w, int total_bits, const uint32_t *nact, hipStream_t s,
-                              const int64_t *rows, int64_t num_rows) {
+// first != NULL: the first pass reads the pairs from the batch's rows (RowPairs
+// or PairRowPairs) and sets up the plan's counters and active count on the
+// way; then every element takes part (nact is written, not read, by that pass).
+template <typename K, int ITEMS, typename First>
+inline int radix_sort_pairs_t(SegWork<K> &w, int total_bits, const uint32_t *nact, hipStream_t s, const First *first) {
   const SortPlan plan = make_plan(total_bits);
   int cur = 0;
   for (int p = 0; p < plan.passes; ++p) {
-    if (p == 0 && rows) {
-      const RowPairs src{rows, num_rows};
-      hist_kernel<K, ITEMS, RowPairs><<<w.nblocks, kSortThreads, 0, s>>>(src, w.n, nullptr, plan.shift[p],
-                                                                          plan.bits[p], w.counts, w.ticket, w.nact);
-      scatter_kernel<K, ITEMS, RowPairs><<<w.nblocks, kSortThreads, 0, s>>>(
-          src, w.k[cur ^ 1], w.v[cur ^ 1], w.n, nullptr, plan.shift[p], plan.bits[p], w.counts, w.nblocks);
+    if (p == 0 && first) {
+      hist_kernel<K, ITEMS, First><<<w.nblocks, kSortThreads, 0, s>>>(*first, w.n, nullptr, plan.shift[p],
+                                                                       plan.bits[p], w.counts, w.ticket, w.nact);
+      scatter_kernel<K, ITEMS, First><<<w.nblocks, kSortThreads, 0, s>>>(
+          *first, w.k[cur ^ 1], w.v[cur ^ 1], w.n, nullptr, plan.shift[p], plan.bits[p], w.counts, w.nblocks);
     } else {
       const BufPairs<K> src{w.k[cur], w.v[cur]};
       hist_kernel<K, ITEMS, BufPairs<K>><<<w.nblocks, kSortThreads, 0, s>>>(src, w.n, nact, plan.shift[p],
@@ -465,12 +479,12 @@ inline int radix_sort_pairs_t(SegWork<K> &w, int total_bits, const uint32_t *nac
 }
 
 // nact: device count of the elements in use (the first *nact slots), or NULL for all n.
-template <typename K>
+template <typename K, typename First = RowPairs>
 inline int radix_sort_pairs(SegWork<K> &w, int total_bits, hipStream_t s, const uint32_t *nact = nullptr,
-                            const int64_t *rows = nullptr, int64_t num_rows = 0) {
-  if (w.items == 4) return radix_sort_pairs_t<K, 4>(w, total_bits, nact, s, rows, num_rows);
-  if (w.items == 8) return radix_sort_pairs_t<K, 8>(w, total_bits, nact, s, rows, num_rows);
-  return radix_sort_pairs_t<K, 16>(w, total_bits, nact, s, rows, num_rows);
+                            const First *first = nullptr) {
+  if (w.items == 4) return radix_sort_pairs_t<K, 4, First>(w, total_bits, nact, s, first);
+  if (w.items == 8) return radix_sort_pairs_t<K, 8, First>(w, total_bits, nact, s, first);
+  return radix_sort_pairs_t<K, 16, First>(w, total_bits, nact, s, first);
 }
 
 template <typename K, typename Emit, int ITEMS>
@@ -522,6 +536,25 @@ struct FromPositions {
 
 // Element i of a plan's sorted (row, position) pairs: kept if it belongs to a
 // row (not the sentinel) and the mask is set at its position.
+// Pair i of a pair plan's 2n pairs (see PairRowPairs), kept if its row is in
+// range and the mask is set at its position.
+struct FromPositionsPair {
+  const int64_t *rows0, *rows1;
+  const uint8_t *mask;
+  int64_t n, num_rows0, num_rows1;
+  __device__ __forceinline__ int64_t count(int64_t m) const { return m; }
+  __device__ __forceinline__ bool get(int64_t i, int64_t m, uint32_t *key, uint32_t *pos) const {
+    if (i >= m) return false;
+    const bool second = i >= n;
+    const int64_t p = second ? i - n : i;
+    const int64_t r = second ? rows1[p] : rows0[p];
+    const int64_t lim = second ? num_rows1 : num_rows0;
+    *key = static_cast<uint32_t>(second ? num_rows0 + r : r);
+    *pos = static_cast<uint32_t>(p);
+    return r >= 0 && r < lim && mask[p] != 0;
+  }
+};
+
 struct FromPlan {
   const uint32_t *keys;
   const uint32_t *spos;
@@ -647,9 +680,32 @@ inline int group_by_row(SegWork<uint32_t> &w, const int64_t *rows, const uint8_t
     compact_into<4>(w, FromPositions{rows, mask, num_rows}, 0, s);
     cur = radix_sort_pairs<uint32_t>(w, bits, s, w.nact);
   } else {  // the first pass reads the rows directly
-    cur = radix_sort_pairs<uint32_t>(w, bits, s, w.nact, rows, num_rows);
+    const RowPairs first{rows, num_rows};
+    cur = radix_sort_pairs<uint32_t>(w, bits, s, w.nact, &first);
   }
   segment_sorted<uint32_t>(w, cur, static_cast<uint32_t>(num_rows), true, w.seg_key, NoEmit{}, s, w.nact);
+  return cur;
+}
+
+// Groups the positions of two updates by row in one sort (a pair plan over
+// w.n = 2n pairs, keys as in PairRowPairs): returns the buffer index holding
+// the sorted pairs, with the segment table built.  Each segment belongs to one
+// table (keys below num_rows0: rows0's table), its positions ascending.
+inline int group_by_row_pair(SegWork<uint32_t> &w, const int64_t *rows0, int64_t num_rows0, const int64_t *rows1,
+                             int64_t num_rows1, const uint8_t *mask, hipStream_t s) {
+  const int64_t n = w.n / 2;
+  const int64_t sentinel = num_rows0 + num_rows1;
+  const int bits = bit_width_u64(static_cast<uint64_t>(sentinel));
+  int cur;
+  if (mask) {
+    small_tiles(w);
+    compact_into<4>(w, FromPositionsPair{rows0, rows1, mask, n, num_rows0, num_rows1}, 0, s);
+    cur = radix_sort_pairs<uint32_t>(w, bits, s, w.nact);
+  } else {
+    const PairRowPairs first{rows0, rows1, n, num_rows0, num_rows1};
+    cur = radix_sort_pairs<uint32_t>(w, bits, s, w.nact, &first);
+  }
+  segment_sorted<uint32_t>(w, cur, static_cast<uint32_t>(sentinel), true, w.seg_key, NoEmit{}, s, w.nact);
   return cur;
 }
 

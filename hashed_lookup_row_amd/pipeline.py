@@ -575,11 +575,24 @@ class EMAPipeline:
     is a chain of short, latency-bound kernels, so two chains side by side take about as long as one.
     With batch=True (distinct tables of one dim, at most four) all the applies of a batch are one
     ema_update_apply_batch call once every plan is ready: their long dependent chains then run side by
-    side instead of one update after another; mark is then called with ("apply", -1, 0 | 1)."""
+    side instead of one update after another; mark is then called with ("apply", -1, 0 | 1).
 
-    def __init__(self, tables, n, depth=2, derive=True, lookup_streams=2, batch=True):
+    With pairs=True the tables come in pairs (tables[2k], tables[2k + 1]: a user-keyed and an item-keyed
+    cache with the same rule, as CS3's CTS and CMS pairs), at most four pairs of one dim; updates 2k and
+    2k + 1 of every batch take the same mask tensor (or None) and the same (a, b).  Each pair is planned by
+    one sort of both updates' positions (ema_update_plan_pair; with derive, a masked pair whose rows tensors
+    are those of an unmasked pair of the same tables' sizes is cut out of that pair's plan, on that pair's
+    lookup stream; other pairs go round-robin over the lookup streams), and all pairs are applied by one
+    ema_update_apply_pairs launch: half the plan launches of the unpaired schedule."""
+
+    def __init__(self, tables, n, depth=2, derive=True, lookup_streams=2, batch=True, pairs=False):
         self.tables, self.n, self.derive = tables, n, derive
         dev = tables[0].device
+        self.pairs = bool(pairs)
+        self._lookup_streams = lookup_streams
+        if self.pairs:
+            self._init_pairs(tables, n, depth, dev)
+            return
         self.rings = [_Ring(dev, depth, points=len(tables)) for _ in range(max(1, int(lookup_streams)))]
         self.ring = self.rings[0]
         self._ws = [[new_workspace(dev, ema_workspace_size(t.shape[0], t.shape[1], n)) for t in tables]
@@ -601,6 +614,117 @@ class EMAPipeline:
                     _dev(t, "table", torch.float32)
                     arr[i].table, arr[i].num_rows, arr[i].dim = t.data_ptr(), t.shape[0], t.shape[1]
                     arr[i].ws, arr[i].ws_bytes = self._wsp[k][i]
+
+    def _init_pairs(self, tables, n, depth, dev):
+        from . import _EmaApplyPair
+        P = len(tables) // 2
+        if len(tables) % 2 or not 1 <= P <= 4:
+            raise HLRError("pairs=True needs an even number of tables, at most eight")
+        if len({id(t) for t in tables}) != len(tables) or len({t.shape[1] for t in tables}) != 1:
+            raise HLRError("pairs=True needs distinct tables of one dim")
+        for t in tables:
+            _dev(t, "table", torch.float32)
+        self._distinct, self.batch, self._np = True, True, P
+        self.rings = [_Ring(dev, depth, points=1) for _ in range(max(1, int(self._lookup_streams)))]
+        self.ring = self.rings[0]
+        self._lib = load_library()
+        D = tables[0].shape[1]
+        need = [self._lib.ema_update_pair_workspace_size(tables[2 * k].shape[0], tables[2 * k + 1].shape[0], D, n)
+                for k in range(P)]
+        if min(need) == 0:
+            raise HLRError("pair sizes out of range (rows of a pair below 2^31 - 1, 2n within the batch limit)")
+        self._ws = [[new_workspace(dev, need[k]) for k in range(P)] for _ in range(depth)]
+        self._wsp = [[_own_ws(w, need[k]) for k, w in enumerate(slot)] for slot in self._ws]
+        self._wsp = [[(p.value, b) for p, b in slot] for slot in self._wsp]
+        self._arr = [(_EmaApplyPair * P)() for _ in range(depth)]
+        for k, arr in enumerate(self._arr):
+            for j in range(P):
+                t0, t1 = tables[2 * j], tables[2 * j + 1]
+                arr[j].table0, arr[j].num_rows0 = t0.data_ptr(), t0.shape[0]
+                arr[j].table1, arr[j].num_rows1 = t1.data_ptr(), t1.shape[0]
+                arr[j].dim = D
+                arr[j].ws, arr[j].ws_bytes = self._wsp[k][j]
+
+    def _pair_sources(self, rows, masks, coeffs):
+        """Per pair, the unmasked pair its plan is cut from (or None), and the planning order."""
+        P, T = self._np, self.tables
+        for k in range(P):
+            if masks[2 * k] is not masks[2 * k + 1]:
+                raise HLRError(f"updates {2 * k} and {2 * k + 1} form a pair and take the same mask")
+            if tuple(coeffs[2 * k]) != tuple(coeffs[2 * k + 1]):
+                raise HLRError(f"updates {2 * k} and {2 * k + 1} form a pair and take the same (a, b)")
+            if rows[2 * k].numel() != rows[2 * k + 1].numel():
+                raise HLRError(f"updates {2 * k} and {2 * k + 1} form a pair and take as many positions")
+        src = [None] * P
+        if self.derive:
+            for k in range(P):
+                if masks[2 * k] is None:
+                    continue
+                for j in range(P):
+                    if (masks[2 * j] is None and rows[2 * j] is rows[2 * k] and rows[2 * j + 1] is rows[2 * k + 1]
+                            and T[2 * j].shape[0] == T[2 * k].shape[0] and T[2 * j + 1].shape[0] == T[2 * k + 1].shape[0]):
+                        src[k] = j
+                        break
+        order = [k for k in range(P) if masks[2 * k] is None] + [k for k in range(P) if masks[2 * k] is not None]
+        return src, order
+
+    def _pair_chains(self, src):
+        """Lookup stream of each pair: pairs with a plan of their own round-robin over the lookup streams, a
+        pair cut out of another pair's plan on that pair's stream (it reads that plan)."""
+        chain, nxt = [0] * self._np, 0
+        for k in range(self._np):
+            if src[k] is None:
+                chain[k] = nxt % len(self.rings)
+                nxt += 1
+        for k in range(self._np):
+            if src[k] is not None:
+                chain[k] = chain[src[k]]
+        return chain
+
+    def _pair_plan(self, k, rows, masks, src, slot, ls):
+        T, lib, wsp = self.tables, self._lib, self._wsp[slot]
+        U, I = T[2 * k].shape[0], T[2 * k + 1].shape[0]
+        n = rows[2 * k].numel()
+        if src[k] is not None:
+            rc = lib.ema_update_plan_subset(U + I, masks[2 * k].data_ptr(), 2 * n, wsp[src[k]][0], wsp[src[k]][1],
+                                            wsp[k][0], wsp[k][1], ls)
+        else:
+            m = masks[2 * k]
+            rc = lib.ema_update_plan_pair(U, rows[2 * k].data_ptr(), I, rows[2 * k + 1].data_ptr(),
+                                          None if m is None else m.data_ptr(), n, wsp[k][0], wsp[k][1], ls)
+        _check(rc, "ema pair plan")
+
+    def _pair_apply(self, rows, vals, coeffs, slot, cs):
+        arr = self._arr[slot]
+        for k in range(self._np):
+            arr[k].vals0, arr[k].vals1 = vals[2 * k].data_ptr(), vals[2 * k + 1].data_ptr()
+            arr[k].n = rows[2 * k].numel()
+            arr[k].a, arr[k].b = coeffs[2 * k][0], coeffs[2 * k][1]
+        _check(self._lib.ema_update_apply_pairs(self._np, ctypes.addressof(arr), cs), "ema_update_apply_pairs")
+
+    def _pair_step(self, rows, masks, vals, coeffs, mark):
+        src, order = self._pair_sources(rows, masks, coeffs)
+        chain = self._pair_chains(src)
+        used = sorted(set(chain))
+        seen = {}
+        self._check_ids(rows, masks, seen)
+        self._check_vals(rows, vals)
+        ks = {c: self.rings[c].begin_lookup() for c in used}
+        k = ks[used[0]]
+        for c in used:
+            _on(self.rings[c].lookup, *seen.values())
+        for j in order:
+            self._pair_plan(j, rows, masks, src, k, self.rings[chain[j]].ls)
+        for c in used:
+            self.rings[c].mark(k, 0)
+        for c in used:
+            self.rings[c].wait(k, 0)
+        _on(self.ring.compute, *vals)
+        mark(("apply", -1, 0))
+        self._pair_apply(rows, vals, coeffs, k, self.ring.cs)
+        mark(("apply", -1, 1))
+        for r in self.rings:  # every ring advances each step, so their slots stay in step
+            r.end_compute(k)
 
     def restart(self):
         for r in self.rings:
@@ -663,6 +787,9 @@ class EMAPipeline:
         mark: optional callable, called on the compute stream with ("apply", i, 0 | 1) just
         before and after each apply is enqueued."""
         mark = mark if mark is not None else (lambda tag: None)
+        if self.pairs:
+            self._pair_step(rows, masks, vals, coeffs, mark)
+            return
         src, order = self._sources(rows, masks)
         chain = self._chains(rows)
         used = sorted(set(chain))
@@ -735,8 +862,12 @@ class EMAPipeline:
             self._check_vals(rows, vals)
             for v in vals:
                 seen[id(v)] = v
-            src, order = self._sources(rows, masks)
-            plans.append((src, order, self._chains(rows)))
+            if self.pairs:
+                src, order = self._pair_sources(rows, masks, coeffs)
+                plans.append((src, order, self._pair_chains(src)))
+            else:
+                src, order = self._sources(rows, masks)
+                plans.append((src, order, self._chains(rows)))
         if apply_events is not None and len(apply_events) < (len(batches) + G - 1) // G:
             raise HLRError("apply_events needs one entry per group")
         self.restart()
@@ -762,6 +893,10 @@ class EMAPipeline:
             for b in range(b0, b1):
                 rows, masks, _, _ = batches[b]
                 src, order, chain = plans[b]
+                if self.pairs:
+                    for i in order:
+                        self._pair_plan(i, rows, masks, src, b % D, self.rings[chain[i]].ls)
+                    continue
                 for i in order:
                     self._plan(i, rows, masks, src, b % D, self.rings[chain[i]].ls)
             for c in used:
@@ -777,6 +912,9 @@ class EMAPipeline:
                 h.record(ev[0], r0.cs)
             for b in range(b0, b1):
                 rows, _, vals, coeffs = batches[b]
+                if self.pairs:
+                    self._pair_apply(rows, vals, coeffs, b % D, r0.cs)
+                    continue
                 arr = self._arr[b % D]
                 for i in range(len(self.tables)):
                     arr[i].vals, arr[i].n = vals[i].data_ptr(), rows[i].numel()

@@ -288,6 +288,43 @@ typedef struct {
 } hlr_ema_apply;
 hlr_status ema_update_apply_batch(int32_t count, const hlr_ema_apply *updates, hipStream_t stream);
 
+/* Two EMA updates keyed by different rows, planned by one sort and applied as
+ * one ([CS3] sec. 2: each batch updates a user-keyed and an item-keyed cache
+ * with the same rule, CTS on the positives and CMS on every pair).
+ *  Update 0: table0[num_rows0*dim] with rows0[n], values vals0[n*dim];
+ *  update 1: table1[num_rows1*dim] with rows1[n], values vals1[n*dim];
+ *  both with the same mask[n] (NULL = every position) and the same (a, b).
+ *  The result equals ema_update_rows on each table, bit for bit (the two
+ *  tables are independent).  ema_update_plan_pair groups the 2n pairs by
+ *  (table, row) into ws; ema_update_apply_pairs applies up to four such pairs
+ *  in one launch, under the rules of ema_update_apply_batch (one dim; no
+ *  table or workspace shared between or within pairs).  The plan of a subset
+ *  of a pair plan's positions comes from ema_update_plan_subset given
+ *  num_rows0 + num_rows1 as num_rows and 2n as n (its mask is still mask[n]).
+ *  ws: ema_update_pair_workspace_size(num_rows0, num_rows1, dim, n) bytes
+ *  (0 for sizes out of range: num_rows0 + num_rows1 must stay below 2^31 - 1
+ *  and 2n within the batch limit).  Errors: HLR_INVALID_ARG for sizes out of
+ *  range, NULL pointers or overlaps, HLR_MISALIGNED, HLR_UNSUPPORTED_DIM,
+ *  HLR_WORKSPACE_TOO_SMALL; nothing is enqueued then. */
+size_t ema_update_pair_workspace_size(int64_t num_rows0, int64_t num_rows1, int64_t dim, int64_t n);
+hlr_status ema_update_plan_pair(int64_t num_rows0, const int64_t *rows0, int64_t num_rows1, const int64_t *rows1,
+                                const uint8_t *mask, int64_t n, void *ws, size_t ws_bytes, hipStream_t stream);
+typedef struct {
+  float *table0;
+  int64_t num_rows0;
+  const float *vals0;
+  float *table1;
+  int64_t num_rows1;
+  const float *vals1;
+  int64_t dim;
+  int64_t n;
+  float a;
+  float b;
+  void *ws;
+  size_t ws_bytes;
+} hlr_ema_apply_pair;
+hlr_status ema_update_apply_pairs(int32_t count, const hlr_ema_apply_pair *pairs, hipStream_t stream);
+
 /* The plan of a subset of another plan's positions, without sorting again
  * ([CS3] sec. 2: CTS updates on the positive interactions, a subset of the
  * pairs CMS updates on, keyed by the same user and item IDs).

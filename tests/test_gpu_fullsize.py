@@ -292,9 +292,11 @@ def test_dlrm_hashed_tables_full_size(dev):
     free(*tables)
 
 
-def test_cs3_ema_full_size(dev):
-    """The bench's launch configuration: EMAPipeline (user-keyed and item-keyed plans on two lookup
-    streams, CTS plans cut out of the CMS plans, the four applies as one batched launch) in the grouped
+@pytest.mark.parametrize("pairs,derive", [(True, False), (False, True)])
+def test_cs3_ema_full_size(dev, pairs, derive):
+    """The bench's launch configuration: EMAPipeline with pair plans (each rule's user- and item-keyed
+    updates planned by one sort, the CMS and the CTS pair on two lookup streams, all four applies as one
+    launch), and the unpaired one (four plans, CTS cut out of CMS, on two lookup streams), in the grouped
     schedule (run(): plans of four steps back to back, a group ahead of the applies) for ten steps of
     262,144 pairs, after two step() calls, without synchronising in between; all four tables bit for bit
     against the sequential oracle over the twelve steps."""
@@ -312,7 +314,8 @@ def test_cs3_ema_full_size(dev):
         inp.append(((urows, irows, y), [torch.from_numpy(x).to(dev) for x in (urows, irows, y)], dvals))
     calls = [("c_user", 0, 0, True, cfg.cts_a, cfg.cts_b), ("c_item", 1, 1, True, cfg.cts_a, cfg.cts_b),
              ("s_user", 0, 2, False, cfg.cms_a, cfg.cms_b), ("s_item", 1, 2, False, cfg.cms_a, cfg.cms_b)]
-    pipe = EMAPipeline([gpu[c[0]] for c in calls], n, depth=12, lookup_streams=2, batch=True)
+    pipe = EMAPipeline([gpu[c[0]] for c in calls], n, depth=12, lookup_streams=2, batch=True, pairs=pairs,
+                       derive=derive)
     args = [([x[c[1]] for c in calls], [x[2] if c[3] else None for c in calls], [v[c[2]] for c in calls],
              [(c[4], c[5]) for c in calls]) for _, x, v in inp]
     pipe.step(*args[0])

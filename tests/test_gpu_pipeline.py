@@ -113,6 +113,61 @@ def test_ema_plan_subset(dev, src_masked, num_rows, n, D, dense):
     assert bits_equal(to_np(t_all), want_all)
 
 
+@pytest.mark.parametrize("src_masked", [False, True])
+@pytest.mark.parametrize("U,I,n,D", [(4096, 8192, 30_000, 128), (300, 7, 20_000, 64), (1, 3000, 5000, 48),
+                                     (2000, 2000, 777, 8)])
+def test_ema_pair_plan(dev, src_masked, U, I, n, D):
+    """A pair plan (the positions of a user-keyed and an item-keyed update grouped by one sort) applied with
+    ema_update_apply_pairs equals the oracle's batch-order EMA on each table (CS3 page, sec. 2), with rows out
+    of range in both halves, hot rows long enough to be cut into chunks, a table of a single row; a subset cut
+    out of the pair plan applies like the two updates with both masks, and the source plan still applies."""
+    g = np.random.default_rng(U + I + n + src_masked)
+    r0 = np.minimum(synth.zipf_ranks(g, U, 1.1, n), U - 1).astype(np.int64)
+    r1 = np.minimum(synth.zipf_ranks(g, I, 1.05, n), I - 1).astype(np.int64)
+    r0[g.random(n) < 0.02] = -1
+    r1[g.random(n) < 0.01] = I + 5
+    v0 = g.standard_normal((n, D)).astype(np.float32)
+    v1 = g.standard_normal((n, D)).astype(np.float32)
+    m1 = (g.random(n) < 0.8).astype(np.uint8) if src_masked else None
+    m2 = (g.random(n) < 0.3).astype(np.uint8)
+    t0 = g.standard_normal((U, D)).astype(np.float32)
+    t1 = g.standard_normal((I, D)).astype(np.float32)
+    d = lambda x: torch.from_numpy(x).to(dev)
+    a0, a1, s0, s1 = d(t0), d(t1), d(t0), d(t1)
+    r0d, r1d, v0d, v1d = d(r0), d(r1), d(v0), d(v1)
+    need = hlr.ema_pair_workspace_size(U, I, D, n)
+    ws_src, ws_sub = hlr.new_workspace(dev, need), hlr.new_workspace(dev, need)
+    hlr.ema_update_plan_pair(U, r0d, I, r1d, d(m1) if src_masked else None, ws_src)
+    hlr.ema_update_plan_pair_subset(U, I, d(m2), ws_src, ws_sub)
+    hlr.ema_update_apply_pairs([(s0, v0d, s1, v1d, 0.9, 0.1, ws_sub)])
+    hlr.ema_update_apply_pairs([(a0, v0d, a1, v1d, 0.95, 0.05, ws_src)])
+    both = m2 if m1 is None else (m1 & m2)
+    o0 = np.where(r0 < U, r0, -1)
+    o1 = np.where(r1 < I, r1, -1)  # the oracle takes -1 for "no row"
+    w = {k: x.copy() for k, x in (("a0", t0), ("a1", t1), ("s0", t0), ("s1", t1))}
+    oracle.ema(w["a0"], o0, v0, m1, 0.95, 0.05)
+    oracle.ema(w["a1"], o1, v1, m1, 0.95, 0.05)
+    oracle.ema(w["s0"], o0, v0, both, 0.9, 0.1)
+    oracle.ema(w["s1"], o1, v1, both, 0.9, 0.1)
+    for k, x in (("a0", a0), ("a1", a1), ("s0", s0), ("s1", s1)):
+        assert bits_equal(to_np(x), w[k]), k
+
+
+def test_ema_pair_argument_errors(dev):
+    """Pair plans refuse sizes past the key range, shared tables and mismatched inputs (host-side errors)."""
+    assert hlr.ema_pair_workspace_size(1 << 30, 1 << 30, 4, 10) == 0
+    assert hlr.ema_pair_workspace_size(5, 5, 4, 10) > 0
+    t = torch.zeros((64, 8), dtype=torch.float32, device=dev)
+    v = torch.zeros((16, 8), dtype=torch.float32, device=dev)
+    rows = torch.zeros(16, dtype=torch.int64, device=dev)
+    ws = hlr.new_workspace(dev, hlr.ema_pair_workspace_size(64, 64, 8, 16))
+    hlr.ema_update_plan_pair(64, rows, 64, rows, None, ws)
+    with pytest.raises(hlr.HLRError):
+        hlr.ema_update_apply_pairs([(t, v, t, v, 0.5, 0.5, ws)])  # one table twice
+    with pytest.raises(hlr.HLRError):
+        hlr.ema_update_plan_pair(64, rows, 64, rows[:8], None, ws)
+
+
 def test_ema_apply_batch(dev):
     """Four updates of different tables in one launch (long and short chunks, masked and cut plans, a
     row count that differs per table) equal the oracle applied to each in turn."""
@@ -540,3 +595,47 @@ def test_ema_grouped_run_argument_errors(dev):
     pipe.run([b, b], group=4)
     torch.cuda.synchronize()
     assert bool((tabs[0][:n] == 0).all().item())
+
+
+@pytest.mark.parametrize("derive,group", [(True, 4), (False, 2), (True, 1)])
+def test_ema_pairs_pipeline_matches_oracle(dev, derive, group):
+    """EMAPipeline(pairs=True): the user- and item-keyed updates of each rule planned by one sort (the CTS
+    pair cut out of the CMS pair's plan when derive), all pairs applied by one launch, through step() and
+    the grouped run(); every table bit-equal to the oracle's batch-order EMA (CS3 page, sec. 2)."""
+    cfg = synth.CS3
+    users, items, D, n = 4096, 8192, 128, 12_000
+    g = np.random.default_rng(29 + group)
+    shapes = [users, items, users, items]
+    cpu = [np.zeros((m, D), np.float32) for m in shapes]
+    gpu = [torch.zeros((m, D), dtype=torch.float32, device=dev) for m in shapes]
+    batches = []
+    for s in range(10):
+        m = n - 700 * (s % 3)
+        u = np.minimum(synth.zipf_ranks(g, users, 1.1, m), users - 1).astype(np.int64)
+        it = np.minimum(synth.zipf_ranks(g, items, 1.05, m), items - 1).astype(np.int64)
+        y = (g.random(m) < 0.05).astype(np.uint8)
+        v = [g.standard_normal((m, D)).astype(np.float32) for _ in range(3)]
+        batches.append((u, it, y, v))
+    dev_b = [tuple(torch.from_numpy(x).to(dev) for x in (u, it, y)) + ([torch.from_numpy(x).to(dev) for x in v],)
+             for (u, it, y, v) in batches]
+    torch.cuda.synchronize()
+    pipe = pipeline.EMAPipeline(gpu, n, depth=3 * group, derive=derive, pairs=True)
+    coeffs = [(cfg.cts_a, cfg.cts_b), (cfg.cts_a, cfg.cts_b), (cfg.cms_a, cfg.cms_b), (cfg.cms_a, cfg.cms_b)]
+
+    def args(b):
+        ur, ir, yy, vv = b
+        return [ur, ir, ur, ir], [yy, yy, None, None], [vv[0], vv[1], vv[2], vv[2]], coeffs
+
+    pipe.step(*args(dev_b[0]))
+    pipe.run([args(b) for b in dev_b[1:9]], group=group, ahead=1)
+    pipe.step(*args(dev_b[9]))
+    for (u, it, y, v) in batches:
+        oracle.ema(cpu[0], u, v[0], y, cfg.cts_a, cfg.cts_b)
+        oracle.ema(cpu[1], it, v[1], y, cfg.cts_a, cfg.cts_b)
+        oracle.ema(cpu[2], u, v[2], None, cfg.cms_a, cfg.cms_b)
+        oracle.ema(cpu[3], it, v[2], None, cfg.cms_a, cfg.cms_b)
+    for k in range(4):
+        assert bits_equal(to_np(gpu[k]), cpu[k]), k
+    with pytest.raises(hlr.HLRError):  # the two updates of a pair share their mask
+        ur, ir, yy, vv = dev_b[0]
+        pipe.step([ur, ir, ur, ir], [yy, None, None, None], [vv[0], vv[1], vv[2], vv[2]], coeffs)
