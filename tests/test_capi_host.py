@@ -156,6 +156,54 @@ def test_ema_apply_batch_argument_errors(lib):
     assert lib.ema_update_apply_batch(0, None, s) == OK
 
 
+def test_ema_pair_argument_errors(lib):
+    """Every host-checkable fault of the EMA pair plans returns before anything is enqueued."""
+    class Pair(ctypes.Structure):
+        _fields_ = [("table0", ctypes.c_void_p), ("num_rows0", ctypes.c_int64), ("vals0", ctypes.c_void_p),
+                    ("table1", ctypes.c_void_p), ("num_rows1", ctypes.c_int64), ("vals1", ctypes.c_void_p),
+                    ("dim", ctypes.c_int64), ("n", ctypes.c_int64), ("a", ctypes.c_float), ("b", ctypes.c_float),
+                    ("ws", ctypes.c_void_p), ("ws_bytes", ctypes.c_size_t)]
+    s = None
+    P16 = ctypes.c_void_p(1 << 20)
+    P_ODD = ctypes.c_void_p((1 << 20) + 4)
+    # sizes: the joint key range must leave room for the sentinel, 2n must fit the batch limit
+    assert lib.ema_update_pair_workspace_size(100, 50, 8, 10) == lib.ema_update_rows_workspace_size(150, 8, 20)
+    assert lib.ema_update_pair_workspace_size(1 << 30, 1 << 30, 8, 10) == 0
+    assert lib.ema_update_pair_workspace_size(-1, 5, 8, 10) == 0
+    need = lib.ema_update_pair_workspace_size(100, 50, 4, 10)
+    plan = lambda r0=P16, r1=P16, n=10, ws=P16, wsb=need, nr0=100, nr1=50: lib.ema_update_plan_pair(
+        nr0, r0, nr1, r1, None, n, ws, wsb, s)
+    assert plan(r1=None) == INVALID
+    assert plan(r0=P_ODD) == MISALIGNED
+    assert plan(ws=ctypes.c_void_p((1 << 20) + 16)) == MISALIGNED
+    assert plan(wsb=need - 1) == WS_SMALL
+    assert plan(n=-1) == INVALID
+    assert plan(nr0=1 << 30, nr1=1 << 30) == INVALID
+    assert plan(n=0) == OK                                               # nothing to do
+    base = 1 << 30
+    wneed = lib.ema_update_pair_workspace_size(100, 50, 8, 10)
+
+    def pr(k, dim=8, t0=None, t1=None, ws=None, wsb=wneed):
+        return Pair(t0 if t0 is not None else base + k * (1 << 24), 100, base + (1 << 27) + k * (1 << 24),
+                    t1 if t1 is not None else base + (1 << 26) + k * (1 << 24), 50,
+                    base + (1 << 27) + (1 << 26) + k * (1 << 24), dim, 10, 0.9, 0.1,
+                    ws if ws is not None else base + (1 << 29) + k * (1 << 24), wsb)
+
+    def call(*ps, count=None):
+        arr = (Pair * max(1, len(ps)))(*ps)
+        return lib.ema_update_apply_pairs(len(ps) if count is None else count, ctypes.cast(arr, ctypes.c_void_p), s)
+    assert call(*(pr(k) for k in range(5))) == INVALID                  # at most four
+    assert lib.ema_update_apply_pairs(1, None, s) == INVALID
+    assert call(pr(0, t1=base)) == INVALID                               # one table twice in a pair
+    assert call(pr(0), pr(1, t0=base + (1 << 26))) == INVALID            # a table shared between pairs
+    assert call(pr(0), pr(1, ws=base + (1 << 29))) == INVALID            # a workspace shared between pairs
+    assert call(pr(0, dim=6)) == DIM
+    assert call(pr(0), pr(1, dim=16, wsb=lib.ema_update_pair_workspace_size(100, 50, 16, 10))) == INVALID
+    assert call(pr(0, wsb=wneed - 1)) == WS_SMALL
+    assert call(pr(0, t1=base + (1 << 26) + 8)) == MISALIGNED
+    assert lib.ema_update_apply_pairs(0, None, s) == OK
+
+
 def test_wb_apply_batch_argument_errors(lib):
     """Every host-checkable fault of the batched SGD apply returns before anything is enqueued."""
     class Up(ctypes.Structure):
