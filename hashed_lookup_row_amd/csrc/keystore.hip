@@ -59,7 +59,7 @@ inline int64_t chunk_bytes(int shift, int64_t dim) { return (int64_t(4) * dim + 
 // Every lane finds its count's address first (its chunk's address is a load),
 // so the loop over the wave's distinct rows touches no memory but the atomics.
 // Called by the whole wave.
-__device__ __forceinline__ void count_rows(const VStore &v, int64_t row) {
+__device__ __forceinline__ void count_rows_wave(const VStore &v, int64_t row) {
   const int64_t addr = row >= 0 ? static_cast<int64_t>(reinterpret_cast<uintptr_t>(v.count(row))) : 0;
   uint64_t left = ballot(row >= 0);
   while (left) {
@@ -70,6 +70,45 @@ __device__ __forceinline__ void count_rows(const VStore &v, int64_t row) {
                                   static_cast<uint32_t>(__popcll(same)));
     left &= ~same;
   }
+}
+
+// The same for the whole block: the block's lookups are first summed per row
+// in an LDS table, then each distinct row of the block takes one atomic.
+// Same-address atomics are executed one after another at the memory side, so
+// a Zipf-hot row's count costs one atomic per block instead of one per wave
+// (the hottest key is several percent of a batch).  Rows that do not find a
+// free LDS entry within a few probes are counted by the wave loop instead.
+// Called by the whole block; the counts are integers, so the result does not
+// depend on the order of the additions.
+constexpr int kCountSlots = 512;
+constexpr int kCountProbes = 8;
+
+__device__ __forceinline__ void count_rows(const VStore &v, int64_t row) {
+  __shared__ unsigned long long sh_row[kCountSlots];
+  __shared__ uint32_t sh_cnt[kCountSlots];
+  for (int e = threadIdx.x; e < kCountSlots; e += blockDim.x) {
+    sh_row[e] = ~0ull;
+    sh_cnt[e] = 0u;
+  }
+  __syncthreads();
+  int64_t left = -1;  // a row that found no LDS entry
+  if (row >= 0) {
+    uint32_t e = static_cast<uint32_t>(mix64(static_cast<uint64_t>(row))) & (kCountSlots - 1);
+    bool done = false;
+    for (int p = 0; p < kCountProbes && !done; ++p) {
+      const unsigned long long prev = atomicCAS(&sh_row[e], ~0ull, static_cast<unsigned long long>(row));
+      if (prev == ~0ull || prev == static_cast<unsigned long long>(row)) {
+        atomicAdd(&sh_cnt[e], 1u);
+        done = true;
+      }
+      e = (e + 1) & (kCountSlots - 1);
+    }
+    if (!done) left = row;
+  }
+  __syncthreads();
+  for (int e = threadIdx.x; e < kCountSlots; e += blockDim.x)
+    if (sh_cnt[e] != 0u) atomicAdd(v.count(static_cast<int64_t>(sh_row[e])), sh_cnt[e]);
+  count_rows_wave(v, left);
 }
 
 struct KSWork {
