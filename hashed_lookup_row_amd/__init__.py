@@ -87,6 +87,7 @@ def load_library():
             "mpzch_lookup_or_insert_static_max_n": (i64, []),
             "mpzch_lookup_or_insert_static": (i32, [p, p, p, i64, i32, i64, p, i64, i64, i32, p, p, p, p, p]),
             "memory_layer_step_workspace_init": (i32, [p, sz, p, sz, i64, i64, p]),
+            "memory_layer_step_mark_written": (i32, [p, sz, i64, i64, i64, p, p, p, p]),
         }
         for name, (res, args) in sig.items():
             f = getattr(lib, name)
@@ -104,7 +105,7 @@ def exported_symbols():
             "ema_update_apply", "writeback_plan_rows", "quantize_rows_int8", "mark_rows", "clear_marks",
             "dks_workspace_size", "dks_lookup_or_insert", "dks_rehash", "dks_chunk_bytes", "dks_chunk_init",
             "dks_gather_rows", "memory_layer_step",
-            "memory_layer_step_workspace_size", "memory_layer_step_workspace_init",
+            "memory_layer_step_workspace_size", "memory_layer_step_workspace_init", "memory_layer_step_mark_written",
             "mpzch_lookup_or_insert_static_max_n", "mpzch_lookup_or_insert_static", "ema_update_plan_subset", "ema_update_apply_batch",
             "writeback_apply_batch", "ema_update_pair_workspace_size", "ema_update_plan_pair", "ema_update_apply_pairs"]
 

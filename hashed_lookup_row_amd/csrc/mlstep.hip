@@ -125,7 +125,50 @@ __global__ void __launch_bounds__(ml::kThreads)
     if (on[c]) store_nt(table + wb + col[c], f4_sub(m[c], f4_sub(m[c], e[c])));
 }
 
+// The rows a batch's row pass wrote, added to a written-row set (RES
+// publishing): one thread per descriptor slot; a group with a row sets the
+// row's flag, and the lanes that found it clear append the row to the list
+// (one list atomic per wave).  A row in several tiles is several groups; its
+// flag is set once, so it is listed once.
+__global__ void __launch_bounds__(ml::kThreads)
+    ml_mark_written(ml::Work w, int64_t num_rows, uint32_t *flags, int64_t *list, unsigned long long *list_count) {
+  const int64_t g = static_cast<int64_t>(blockIdx.x) * ml::kThreads + threadIdx.x;
+  const int64_t tile = g / ml::kTile;
+  bool fresh = false;
+  int64_t r = -1;
+  if (tile < w.tiles && static_cast<uint32_t>(g % ml::kTile) < w.ntile[tile]) {
+    const uint4 d = w.gdesc[g];
+    if (!(d.w & ml::kNoRow) && static_cast<int64_t>(d.x) < num_rows) {
+      r = d.x;
+      fresh = atomicOr(&flags[r], 1u) == 0u;
+    }
+  }
+  const uint64_t bal = ballot(fresh);
+  if (bal == 0) return;
+  const int leader = __builtin_ctzll(bal);
+  unsigned long long base = 0;
+  if (lane_id() == leader) base = atomicAdd(list_count, static_cast<unsigned long long>(__popcll(bal)));
+  base = __shfl(base, leader);
+  if (fresh) list[base + static_cast<unsigned long long>(__popcll(bal & lanemask_lt()))] = r;
+}
+
 }  // namespace
+
+extern "C" hlr_status memory_layer_step_mark_written(const void *wb_ws, size_t wb_ws_bytes, int64_t n, int64_t n_max,
+                                                     int64_t capacity, uint32_t *flags, int64_t *list,
+                                                     int64_t *list_count, hipStream_t stream) {
+  if (n < 0 || n > n_max || n_max > kMaxN || capacity <= 0) return HLR_INVALID_ARG;
+  if (n == 0) return HLR_OK;
+  if (!wb_ws || !flags || !list || !list_count) return HLR_INVALID_ARG;
+  if (!aligned(wb_ws, 256) || !aligned(flags, 4) || !aligned(list, 8) || !aligned(list_count, 8))
+    return HLR_MISALIGNED;
+  ml::Work w;
+  if (wb_ws_bytes < ml::layout(n_max, capacity, &w, const_cast<void *>(wb_ws))) return HLR_WORKSPACE_TOO_SMALL;
+  w.tiles = (n + ml::kTile - 1) / ml::kTile;  // this batch's tiles
+  ml_mark_written<<<grid_for(w.tiles * ml::kTile, ml::kThreads), ml::kThreads, 0, stream>>>(
+      w, capacity, flags, list, reinterpret_cast<unsigned long long *>(list_count));
+  return launch_status();
+}
 
 hlr_status hlr::ml_apply(float *values, int64_t num_rows, int64_t dim, const float *e, int64_t n, int64_t n_max,
                          float *out, void *ws, hipStream_t stream) {

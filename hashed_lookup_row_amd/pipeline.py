@@ -188,6 +188,8 @@ class MemoryLayerPipeline:
             return self._native_step(ids, now, e, out, evicted, stats, gather_events)
         if self._ahead:
             raise HLRError("a step with mark or publisher cannot follow prefetch()")
+        if self.native and mark is None:
+            return self._native_published_step(ids, now, e, out, evicted, stats, gather_events, publisher)
         if gather_events is not None:
             if mark is not None:
                 raise ValueError("give mark or gather_events, not both")
@@ -226,7 +228,30 @@ class MemoryLayerPipeline:
             if t is not None and not (t.is_cuda and t.dtype == torch.int64 and t.is_contiguous() and t.numel() >= m):
                 raise HLRError(f"{name} must be a contiguous GPU int64 tensor of at least {m} elements")
 
-    def _call(self, ids, now, e, out, evicted, stats, gather_events, k, halves):
+    def _native_published_step(self, ids, now, e, out, evicted, stats, gather_events, publisher):
+        """The one-call step in two halves around the publisher: the lookup half, the publisher's snapshot on
+        the lookup stream at this batch boundary, the compute half, then the rows it wrote added to the
+        publisher's set (memory_layer_step_mark_written, from this slot's grouping) before the slot is
+        released."""
+        r = self.ring
+        D = self._const[5]
+        n = ids.numel()
+        if not (e.is_cuda and e.dtype == torch.float32 and e.is_contiguous() and e.numel() == n * D):
+            raise HLRError(f"e must be a contiguous GPU float32 tensor of {n} x {D} elements")
+        if out is None:
+            out = torch.empty((n, D), dtype=torch.float32, device=self.values.device)
+        elif not (out.is_cuda and out.dtype == torch.float32 and out.is_contiguous() and out.numel() == n * D):
+            raise HLRError(f"out must be a contiguous GPU float32 tensor of {n} x {D} elements")
+        self._check_ids(ids, evicted, stats)
+        k = self._tl % r.depth
+        self._call(ids, now, e, out, evicted, stats, gather_events, k, 1)
+        publisher.after_lookup(self)
+        self._call(ids, now, e, out, evicted, stats, gather_events, k, 2, done=False)
+        publisher.after_native_apply(self, k, n)
+        r.end_compute(k)
+        return out, k
+
+    def _call(self, ids, now, e, out, evicted, stats, gather_events, k, halves, done=True):
         r = self.ring
         if halves & 1:
             _on(r.lookup, ids, evicted, stats)
@@ -240,7 +265,7 @@ class MemoryLayerPipeline:
                       self._rows[k].data_ptr(), self._hit[k].data_ptr(),
                       None if evicted is None else evicted.data_ptr(), None if stats is None else stats.data_ptr(),
                       None if out is None else out.data_ptr(), mz, mzb, wb, wbb, r.ls, r.cs, slot_free,
-                      r.marks[k][0], r.marks[k][1], gb, ge, r.done[k], halves)
+                      r.marks[k][0], r.marks[k][1], gb, ge, r.done[k] if done else None, halves)
         _check(rc, "memory_layer_step")
         if halves & 1:
             self._tl += 1
@@ -940,7 +965,9 @@ class RESPublisher:
     quantised and pushed to serving together with the ID map and its metadata at intervals.
 
     Per batch (compute stream, after the Writeback apply): the rows the batch wrote are added once
-    each to a written-row set (writeback_plan_rows + mark_rows).  Every `every` batches a publish:
+    each to a written-row set (writeback_plan_rows + mark_rows; with a native pipeline the batch runs
+    as the one-call step's two halves and memory_layer_step_mark_written reads the rows from the
+    step's row grouping).  Every `every` batches a publish:
       compute stream: quantise the set's rows to int8 (quantize_rows_int8, per-row min-max) into a
                       device staging slot, keep the row list and count beside it, clear the set;
       lookup stream:  at that batch's boundary (after its MPZCH step, before the next one) copy
@@ -965,6 +992,7 @@ class RESPublisher:
         self.copy = torch.cuda.Stream(dev)
         self.cps = self.copy.cuda_stream
         self.hip = hip()
+        self._lib = load_library()
         i64 = dict(dtype=torch.int64, device=dev)
         self.flags = torch.zeros(C, dtype=torch.int32, device=dev)
         self.lst = torch.empty(C, **i64)
@@ -1030,6 +1058,18 @@ class RESPublisher:
         cs = pipe.ring.cs
         writeback_plan_rows(self.C, pipe.n, plan_ws, out_rows=self.plan_rows, out_count=self.plan_count, stream=cs)
         mark_rows(self.plan_rows, self.C, self.flags, self.lst, self.lst_count, count=self.plan_count, stream=cs)
+        if self._publishing():
+            self._publish(pipe)
+        self.t += 1
+
+    def after_native_apply(self, pipe, k, n):
+        """Compute stream, after the compute half of a one-call step in ring slot k (n positions): the rows
+        its row pass wrote join the set, read from the slot's row grouping."""
+        cs = pipe.ring.cs
+        wb, wbb = pipe._wb[k]
+        _check(self._lib.memory_layer_step_mark_written(wb, wbb, int(n), pipe.n, self.C, self.flags.data_ptr(),
+                                                        self.lst.data_ptr(), self.lst_count.data_ptr(), cs),
+               "memory_layer_step_mark_written")
         if self._publishing():
             self._publish(pipe)
         self.t += 1

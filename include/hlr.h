@@ -538,6 +538,22 @@ size_t memory_layer_step_workspace_size(int64_t n, int64_t capacity);
  * stream. */
 hlr_status memory_layer_step_workspace_init(void *mz_ws, size_t mz_ws_bytes, void *wb_ws, size_t wb_ws_bytes,
                                             int64_t n, int64_t capacity, hipStream_t stream);
+/* The rows a memory_layer_step batch wrote, added to a written-row set for
+ * RES publishing ([ML] sec. 2, Raw Embedding Streaming: the rows training
+ * updated since the last push): every row the batch's compute half applied
+ * a Writeback to sets flags[row] (flags[capacity] uint32) and, if the flag was
+ * clear, is appended to list (int64) at *list_count (int64, advanced), as
+ * mark_rows does; a row already in the set is not listed again.  Reads the
+ * batch's row grouping from wb_ws (memory_layer_step_workspace_size(n_max,
+ * capacity) bytes, 256-byte aligned), so enqueue it on the compute stream
+ * after the batch's compute half and before a later batch's lookup half
+ * reuses wb_ws (record the slot's done event after this call).  n: the
+ * batch's positions.  Errors: HLR_INVALID_ARG (n out of [0, n_max], NULL
+ * pointers), HLR_MISALIGNED, HLR_WORKSPACE_TOO_SMALL; nothing is enqueued
+ * then. */
+hlr_status memory_layer_step_mark_written(const void *wb_ws, size_t wb_ws_bytes, int64_t n, int64_t n_max,
+                                          int64_t capacity, uint32_t *flags, int64_t *list, int64_t *list_count,
+                                          hipStream_t stream);
 hlr_status memory_layer_step(int64_t *identity, int64_t *stamps, float *values, int64_t capacity, int32_t probes,
                              int64_t dim, const int64_t *ids, int64_t n, int64_t n_max, int64_t now, const float *e,
                              int64_t *out_rows, int8_t *out_hit, int64_t *out_evicted, int64_t *out_stats,

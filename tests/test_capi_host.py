@@ -156,6 +156,24 @@ def test_ema_apply_batch_argument_errors(lib):
     assert lib.ema_update_apply_batch(0, None, s) == OK
 
 
+def test_mark_written_argument_errors(lib):
+    """memory_layer_step_mark_written checks its sizes and pointers before enqueueing anything."""
+    s = None
+    need = lib.memory_layer_step_workspace_size(1000, 4096)
+    ws, f, l, c = (ctypes.c_void_p(1 << 20), ctypes.c_void_p(1 << 24), ctypes.c_void_p(1 << 25),
+                   ctypes.c_void_p(1 << 26))
+    call = lambda n=100, n_max=1000, ws=ws, wsb=need, cap=4096, f=f, l=l, c=c: \
+        lib.memory_layer_step_mark_written(ws, wsb, n, n_max, cap, f, l, c, s)
+    assert call(n=1001) == INVALID
+    assert call(n=-1) == INVALID
+    assert call(cap=0) == INVALID
+    assert call(f=None) == INVALID
+    assert call(ws=ctypes.c_void_p((1 << 20) + 64)) == MISALIGNED
+    assert call(c=ctypes.c_void_p((1 << 26) + 4)) == MISALIGNED
+    assert call(wsb=need - 1) == WS_SMALL
+    assert call(n=0) == OK
+
+
 def test_ema_pair_argument_errors(lib):
     """Every host-checkable fault of the EMA pair plans returns before anything is enqueued."""
     class Pair(ctypes.Structure):

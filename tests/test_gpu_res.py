@@ -96,10 +96,13 @@ def test_writeback_plan_rows(dev):
     assert c == want.size and np.array_equal(np.sort(got), want)
 
 
-def test_res_publisher_schedule(dev):
+@pytest.mark.parametrize("native", [True, False])
+def test_res_publisher_schedule(dev, native):
     """Memory-Layer batches through the two-stream pipeline with a publish every 3 batches: each
     publish carries exactly the rows written since the previous one, quantised from the table as it
-    is after that batch, and identity/stamps as they are after that batch's lookup."""
+    is after that batch, and identity/stamps as they are after that batch's lookup.  native: the batch
+    runs as the one-call step's two halves and its written rows come from the step's row grouping
+    (memory_layer_step_mark_written); else call by call, the rows from the Writeback plan."""
     cfg = synth.scaled_memory_layer(capacity=8_192, universe=60_000, batch=4_096, steps=10, dim=64)
     C, P, D, n = cfg.capacity, cfg.probes, cfg.dim, cfg.batch
     identity = torch.full((C,), -1, dtype=torch.int64, device=dev)
@@ -117,7 +120,7 @@ def test_res_publisher_schedule(dev):
     es = [torch.from_numpy(x).to(dev) for x in e_np]
     torch.cuda.synchronize()
     packets = []
-    pipe = pipeline.MemoryLayerPipeline(identity, stamps, values, P, n)
+    pipe = pipeline.MemoryLayerPipeline(identity, stamps, values, P, n, native=native)
     pub = pipeline.RESPublisher(pipe, every=3, on_publish=packets.append)
     for t in range(cfg.steps):
         pipe.step(ids[t], base + t + 1, es[t], publisher=pub)
