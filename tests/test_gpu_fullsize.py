@@ -114,6 +114,52 @@ def test_memory_layer_full_size(dev, prefilled):
     free(values, identity, stamps)
 
 
+@pytest.mark.timeout(600)
+def test_res_publisher_full_size(dev, prefilled):
+    """The RES bench's configuration at full size: MemoryLayerPipeline steps with a publisher (the one-call
+    step's two halves, each batch's written rows marked from its row grouping), 20 batches, then one publish
+    at the batch boundary (Memory Layer page, sec. 2, Raw Embedding Streaming; sec. 5, int8 rows): the packet
+    lists exactly the rows the oracle wrote, each once, their int8 rows and scales equal the oracle's
+    quantisation of its table, and the identity and stamps snapshot equals the oracle's after the last batch."""
+    from hashed_lookup_row_amd.pipeline import MemoryLayerPipeline, RESPublisher
+    cfg, identity0, stamps0, tab0, base = prefilled
+    C, P, D, n = cfg.capacity, cfg.probes, cfg.dim, cfg.batch
+    identity, stamps = identity0.clone(), stamps0.clone()
+    values = torch.zeros((C, D), dtype=torch.float32, device=dev)
+    tab = oracle.MPZCHTable(C, P, D, with_values=False)
+    tab.identity, tab.stamps = tab0.identity.copy(), tab0.stamps.copy()
+    tab.values = np.zeros((C, D), np.float32)
+    steps, fc = 20, 0
+    stream = []
+    for t in range(1, steps + 1):
+        ids_np, fc = synth.mpzch_step_ids(cfg, t, fc)
+        stream.append(ids_np)
+    e_pool = [synth.normal_rows(n, D, cfg.e_std, cfg.config, t + 1, device=dev) for t in range(4)]
+    ids = [torch.from_numpy(x).to(dev) for x in stream]
+    torch.cuda.synchronize()
+    packets = []
+    pipe = MemoryLayerPipeline(identity, stamps, values, P, n)
+    pub = RESPublisher(pipe, 0, on_publish=packets.append, max_rows=1 << 20)
+    for t in range(steps):
+        pipe.step(ids[t], base + 1 + t, e_pool[t % 4], publisher=pub)
+    pub.publish_now(pipe)
+    pub.flush()
+    torch.cuda.synchronize()
+    written = set()
+    for t in range(steps):
+        orows, _, _, _ = tab.step(stream[t], base + 1 + t)
+        tab.writeback(orows, to_np(e_pool[t % 4]))
+        written |= set(np.unique(orows[orows >= 0]).tolist())
+    assert len(packets) == 1
+    p = packets[0]
+    assert len(p["rows"]) == len(written) and set(p["rows"].tolist()) == written
+    oq, osc, obi = oracle.quantize_rows(tab.values, p["rows"])
+    assert np.array_equal(p["q"], oq) and bits_equal(p["scale"], osc) and bits_equal(p["bias"], obi)
+    assert np.array_equal(p["identity"], tab.identity) and np.array_equal(p["stamps"], tab.stamps)
+    print(f"published {len(written)} rows written by {steps} batches", flush=True)
+    free(values, identity, stamps)
+
+
 @pytest.mark.timeout(900)
 def test_memory_layer_200_steps_benched_schedule_then_serving(dev, prefilled):
     """The headline's launch configuration over the workload's whole 200-step stream: memory_layer_step
