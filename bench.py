@@ -13,9 +13,13 @@ One step = mpzch_lookup_or_insert (lookup, pin, insert, LRU evict, zero-fill)
 lr = 1, in-batch dedup inside).  Inputs are resident in HBM before timing.
 
 Prints one JSON line.  `value` is positions (rows) per second of the whole
-step; `roofline` is the gather kernel's algorithmic bytes per launch over its
-HIP-event duration against 8 TB/s; `cpu_baseline` is the CPU oracle doing the
-same steps on the host (bounded sample).
+step; `roofline` is the row pass ml_fused (gather and Writeback in one pass over
+the batch's rows): its algorithmic bytes per launch over its mean launch time,
+taken with HIP events on the compute stream, against 8 TB/s; `step_hbm` is the
+whole step's algorithmic bytes over the step time; `cpu_baseline` is the CPU
+oracle doing the same steps on one host core (bounded sample).  Other
+workloads (--workload serving | dlrm | cs3 | dedup | res | keystore |
+hbm-ceiling) print their own line of the same shape.
 """
 from __future__ import annotations
 

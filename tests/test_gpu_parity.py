@@ -301,8 +301,11 @@ def score_close(got, ref, cond):
     return bool(np.all(err <= 1e-6 * np.abs(ref.astype(np.float64)) + 1e-12 * cond))
 
 
-@pytest.mark.parametrize("R,K,D", [(3, 1000, 512), (4, 70, 256), (2, 33, 48)])
+@pytest.mark.parametrize("R,K,D", [(3, 1000, 512), (4, 70, 256), (2, 33, 48), (2, 2500, 512), (3, 600, 256),
+                                   (1, 512, 512)])
 def test_dequant_score(dev, R, K, D):
+    """Requests of 33 to 2,500 candidates (ragged last blocks of a request), dims with and without
+    the register-resident user slice."""
     g = np.random.default_rng(R * K + D)
     C = 5000
     q = np.clip(np.rint(g.standard_normal((C, D)) * 42), -128, 127).astype(np.int8)
@@ -317,6 +320,37 @@ def test_dequant_score(dev, R, K, D):
     cond = np.einsum("rkd,rd->rk", np.abs(x[np.maximum(rows, 0)].reshape(R, K, D)), np.abs(user.astype(np.float64)))
     assert score_close(got, ref, cond)
     assert np.all(got[rows.reshape(R, K) < 0] == 0.0)
+
+
+@pytest.mark.parametrize("D", [512, 256])
+def test_dequant_score_repeated_rows(dev, D):
+    """Candidates that repeat rows within a request: one request of a single row 1,500 times, one of a
+    few rows with misses and out-of-range rows among them, one Zipf-skewed; scores equal the oracle's as
+    in test_dequant_score, and every copy of a row in a request has the same score bit for bit (a
+    candidate's score does not depend on the lane or block that computes it)."""
+    g = np.random.default_rng(D + 11)
+    C, R, K = 3000, 3, 1500
+    q = np.clip(np.rint(g.standard_normal((C, D)) * 42), -128, 127).astype(np.int8)
+    scale = (g.random(C).astype(np.float32) * 0.004 + 0.001).astype(np.float32)
+    bias = (g.standard_normal(C) * 0.005).astype(np.float32)
+    rows = np.empty((R, K), np.int64)
+    rows[0] = 17
+    rows[1] = g.choice(np.array([0, 5, C - 1, -1, C, -7]), K)
+    rows[2] = np.minimum(g.zipf(1.3, K) - 1, C - 1)
+    rows = rows.reshape(-1)
+    user = g.standard_normal((R, D)).astype(np.float32)
+    out = hlr.gather_dequant_score(*(torch.from_numpy(x).to(dev) for x in (q, scale, bias, rows, user)), K)
+    valid = np.where((rows >= 0) & (rows < C), rows, -1)
+    ref = oracle.dequant_score(q, scale, bias, valid, user, K)
+    x = q.astype(np.float64) * scale[:, None] + bias[:, None]
+    cond = np.einsum("rkd,rd->rk", np.abs(x[np.maximum(valid, 0)].reshape(R, K, D)), np.abs(user.astype(np.float64)))
+    got = to_np(out)
+    assert score_close(got, ref, cond)
+    assert np.all(got.reshape(-1)[valid < 0] == 0.0)
+    for r in range(R):
+        rr, gg = rows.reshape(R, K)[r], got.reshape(R, K)[r]
+        for v in np.unique(rr):
+            assert np.unique(gg[rr == v].view(np.uint32)).size == 1
 
 
 @pytest.mark.parametrize("P,D", [(8, 512), (8, 256), (4, 48), (8, 48), (16, 512)])
@@ -335,9 +369,11 @@ def test_mpzch_score_matches_lookup_then_score(dev, P, D):
         b = ids_all[k * 2000:(k + 1) * 2000]
         hlr.mpzch_lookup_or_insert(identity, stamps, None, P, torch.from_numpy(b).to(dev), k + 1)
         tab.step(b, k + 1, zero_fill=False)
-    R, K = 3, 700
+    R, K = (3, 700) if D != 512 else (2, 1300)
     cands = np.where(g.random(R * K) < 0.8, g.choice(ids_all, R * K), g.integers(1 << 41, 1 << 42, R * K))
     cands[::97] = -1  # invalid IDs
+    cands[5::7] = ids_all[3]  # a stored ID named many times by every request
+    cands[6::11] = 1 << 43  # a fresh ID named many times
     cands = cands.astype(np.int64)
     q = np.clip(np.rint(g.standard_normal((C, D)) * 42), -128, 127).astype(np.int8)
     scale = (g.random(C).astype(np.float32) * 0.004 + 0.001).astype(np.float32)
