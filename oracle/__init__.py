@@ -43,8 +43,12 @@ def _load():
     global _lib
     with _lock:
         if _lib is None:
-            build(force=False)
-            lib = ctypes.CDLL(_LIB)
+            # HLR_ORACLE_LIBRARY names another build of oracle.c to load instead (the mutation tests run the
+            # pins against copies of the oracle with a planted mistake)
+            alt = os.environ.get("HLR_ORACLE_LIBRARY")
+            if not alt:
+                build(force=False)
+            lib = ctypes.CDLL(alt or _LIB)
             i64, i32, p = ctypes.c_int64, ctypes.c_int32, ctypes.c_void_p
             lib.orc_mix64.restype = ctypes.c_uint64
             lib.orc_mix64.argtypes = [ctypes.c_uint64]

@@ -374,6 +374,26 @@ def test_sgd_sum_order_is_ascending_batch_position():
     assert t[0, 0] == -(np.float32(1.0) + np.float32(2.0 ** -23))
 
 
+def test_sgd_sum_learning_rate_scales_the_row_sum_once():
+    """lr multiplies the row's finished sum once (R11: M' = fl(M - fl(lr s))), not every gradient: with
+    gradients 1 and 2^-24 and lr = 3, the batch-order sum is fl(1 + 2^-24) = 1 (a tie, to even), so a zero
+    row becomes -3 exactly, while scaling each term first would give 3 + 3 2^-24, which rounds to
+    3 + 2^-22.  On zero rows (where the final subtraction loses nothing) random rows also equal
+    -fl(lr * s) with s the sequential float32 sum."""
+    t = np.zeros((1, 1), np.float32)
+    oracle.sgd_sum(t, np.zeros(2, np.int64), np.array([[1.0], [2.0 ** -24]], np.float32), 3.0)
+    assert t[0, 0] == np.float32(-3.0)
+    g = np.random.default_rng(21)
+    C, D, n = 8, 16, 400
+    rows = g.integers(0, C, size=n)
+    grads = (g.standard_normal((n, D)) * 1e-3).astype(np.float32)
+    t = np.zeros((C, D), np.float32)
+    oracle.sgd_sum(t, rows, grads, 0.01)
+    for r in range(C):
+        s = np.cumsum(grads[rows == r], axis=0, dtype=np.float32)[-1]
+        assert np.array_equal(t[r], -(np.float32(0.01) * s).astype(np.float32))
+
+
 def test_sgd_sum_integer_gradients_are_exact():
     g = np.random.default_rng(3)
     rows = g.integers(0, 5, size=2000)
@@ -408,7 +428,8 @@ def _dict_store(stream, max_rows):
         for k, r in pending.items():
             if r >= 0:
                 d[k] = r
-        out.append((np.array(rows), np.array(hit, np.int8)))
+        inserted = sum(1 for r in pending.values() if r >= 0)
+        out.append((np.array(rows), np.array(hit, np.int8), inserted, len(pending) - inserted))
     return d, out
 
 
@@ -424,6 +445,7 @@ def test_key_store_matches_dict_reference_and_table_invariants():
             rows, hit, st = ks.step(ids, t + 1)
             assert np.array_equal(rows, ref[t][0]) and np.array_equal(hit, ref[t][1]), (key_cap, t)
             assert st[3] == np.count_nonzero(ids == -1) and st[0] == hit.sum()
+            assert (st[1], st[2]) == (ref[t][2], ref[t][3]), (key_cap, t)  # inserted and overflowed keys
         assert ks.mapping() == d and ks.next_row[0] == len(d)
         used = ks.keys != -1
         for s in np.nonzero(used)[0]:  # every key reachable from its home slot without crossing an empty slot
@@ -452,6 +474,7 @@ def test_key_store_counts_and_growing_value_store_match_dict_reference():
     for t, ids in enumerate(stream):
         rows, hit, st = ks.step(ids, t + 1, capacity=caps[t])
         assert np.array_equal(rows, ref[t][0]) and np.array_equal(hit, ref[t][1]), t
+        assert (st[1], st[2]) == (ref[t][2], ref[t][3]), t
         assert ks.next_row[0] <= caps[t]
         for r in ref[t][0].tolist():
             if r >= 0:
@@ -592,6 +615,36 @@ def test_ema_special_cases():
     t = t0.copy()
     oracle.ema(t, rows, vals, np.zeros(n, np.uint8), 0.99, 0.01)
     assert np.array_equal(t, t0)
+
+
+def test_ema_rounds_each_product_before_the_sum():
+    """R15: T' = fl(fl(a T) + fl(b v)).  Each float32 product is exact in float64 (24 + 24 bits) and the sum
+    of two float32 values is exact in float64 here, so rounding those float64 values to float32 gives the
+    IEEE float32 result of each operation.  The cases are the seeded ones where that differs from rounding
+    the exact a T + b v once; the oracle must give the per-operation result."""
+    g = np.random.default_rng(31)
+    a, b = np.float32(0.95), np.float32(0.05)
+    T = g.standard_normal(20000).astype(np.float32)
+    v = g.standard_normal(20000).astype(np.float32)
+    x = np.float32(np.float64(a) * np.float64(T))
+    y = np.float32(np.float64(b) * np.float64(v))
+    per_op = np.float32(np.float64(x) + np.float64(y))
+    exact = [Fraction(float(a)) * Fraction(float(t)) + Fraction(float(b)) * Fraction(float(w)) for t, w in zip(T, v)]
+    once = np.array([np.float32(float(e)) for e in exact], np.float32)
+    pick = np.nonzero(per_op != once)[0][:200]
+    assert pick.size >= 20  # the readings differ often enough to tell them apart
+    t = T[pick].reshape(-1, 1).copy()
+    oracle.ema(t, np.arange(pick.size), v[pick].reshape(-1, 1), None, float(a), float(b))
+    assert np.array_equal(t[:, 0], per_op[pick])
+
+
+def test_ema_rejects_rows_outside_the_table():
+    t = np.zeros((4, 2), np.float32)
+    vals = np.ones((2, 2), np.float32)
+    for bad in ([0, 4], [-2, 1]):
+        with pytest.raises(ValueError):
+            oracle.ema(t, np.array(bad, np.int64), vals, None, 0.5, 0.5)
+    assert not t.any()
 
 
 def test_ema_dyadic_values_are_exact_rationals():
