@@ -581,12 +581,12 @@ def run_serving(args):
     _line("candidate scores/s (lookup-only MPZCH + int8 dequant + dot)", n / step_s, "scores/s", K, W,
           step_s * 1e3, {"workload": sv.name, "requests": sv.requests, "cands": sv.cands, "dim": D, "capacity": C,
                          "step": "mpzch_score: lookup-only MPZCH and the int8 dequant-score in one launch"},
-          _roof("score_kernel<2,2,ProbeIn> (mpzch_score)", fused_bytes, step_s),
+          _roof("score_kernel<2,2,2,ProbeIn8> (mpzch_score)", fused_bytes, step_s),
           {"dtype": "int8->fp64", "distinct_rows": int(u), "hit_rate": float((r >= 0).mean()),
            "ops_us": {"fused": step_s * 1e6, "lookup_only": float(np.median(t_look) * 1e6),
                       "score": float(np.median(t_score) * 1e6)},
            "two_calls": {"ms_per_step": float(np.median(t_look) + np.median(t_score)) * 1e3,
-                         "score_roofline": _roof("score_kernel<2,2>", score_bytes, float(np.median(t_score))),
+                         "score_roofline": _roof("score_kernel<2,2,2,RowsIn>", score_bytes, float(np.median(t_score))),
                          "lookup_roofline": _roof("mz_probe<8>", look_bytes, float(np.median(t_look)))},
            "score_valu_ops_per_s": float(3 * n * D / step_s)})
 

@@ -22,6 +22,14 @@
 // the identity tensor and takes the slot holding the ID, the lookup-only rule
 // of mpzch_lookup_or_insert), which saves the lookup's own launch and its
 // row array's round trip through memory.
+//
+// A block scores PASSES groups of candidates one after another, with every
+// pass's row found first: each candidate is a chain of dependent memory trips
+// (ID, bucket, row), and the later passes' ID and bucket trips run while the
+// first pass's rows are fetched and scored.  For 8-slot buckets and a
+// power-of-two bucket count the probe is branch-free (ProbeIn8), so the
+// passes' probes are in flight together (with a branch per probe the
+// compiler waits for each one before the next).
 #include "hlr_common.hpp"
 
 namespace {
@@ -34,6 +42,7 @@ constexpr int kCandsPerBlock = 64;
 struct RowsIn {
   const int64_t *rows;
   __device__ __forceinline__ int64_t row(int64_t i, bool) const { return rows[i]; }
+  __device__ __forceinline__ void record(int64_t, int64_t) const {}
 };
 
 // Candidate rows from the identity tensor (lookup only): bucket mix64(id) mod
@@ -67,11 +76,44 @@ struct ProbeIn {
         if (identity[base + j] == id) r = base + j;
     }
     if (id == HLR_EMPTY_ID) r = -1;
-    if (own) {
-      if (out_rows) out_rows[i] = r;
-      if (out_hit) out_hit[i] = r >= 0 ? 1 : 0;
-    }
+    if (own) record(i, r);
     return r;
+  }
+  __device__ __forceinline__ void record(int64_t i, int64_t r) const {
+    if (out_rows) out_rows[i] = r;
+    if (out_hit) out_hit[i] = r >= 0 ? 1 : 0;
+  }
+};
+
+// The same lookup for 8-slot buckets and a power-of-two bucket count, branch
+// free (the slot found by selects), so the probes of several passes can be in
+// flight together.
+struct ProbeIn8 {
+  const int64_t *ids;
+  const int64_t *identity;
+  uint64_t nb;
+  int64_t *out_rows;
+  int8_t *out_hit;
+  __device__ __forceinline__ int64_t row(int64_t i, bool own) const {
+    const int64_t id = ids[i];
+    const int64_t base = static_cast<int64_t>(mix64(static_cast<uint64_t>(id)) & (nb - 1)) * 8;
+    const longlong2 *q = reinterpret_cast<const longlong2 *>(identity + base);
+    longlong2 v[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) v[j] = q[j];
+    int64_t r = -1;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      r = v[j].x == id ? base + 2 * j : r;
+      r = v[j].y == id ? base + 2 * j + 1 : r;
+    }
+    r = id == HLR_EMPTY_ID ? -1 : r;
+    if (own) record(i, r);
+    return r;
+  }
+  __device__ __forceinline__ void record(int64_t i, int64_t r) const {
+    if (out_rows) out_rows[i] = r;
+    if (out_hit) out_hit[i] = r >= 0 ? 1 : 0;
   }
 };
 
@@ -133,8 +175,8 @@ __device__ __forceinline__ double group16_scatter4(double a0, double a1, double 
 // candidate 4*(sub & 3) + (sub >> 2) of the group: it loads that candidate's
 // row index, scale and bias, and is the lane that holds the candidate's full
 // sum after the halving reduction of batch sub & 3.
-template <int CPL, int NB, typename Src>
-__global__ void __launch_bounds__(kThreads)
+template <int CPL, int NB, int PASSES, typename Src>
+__global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4)))
     score_kernel(const int8_t *__restrict__ q, const float *__restrict__ scale, const float *__restrict__ bias,
                  int64_t num_rows, int64_t dim, Src src, int64_t cands, const float *__restrict__ user,
                  float *__restrict__ out) {
@@ -142,15 +184,22 @@ __global__ void __launch_bounds__(kThreads)
   const int64_t req = blockIdx.y;
   const int grp = threadIdx.x >> 4;
   const int sub = threadIdx.x & 15;
-  const int64_t c0 = static_cast<int64_t>(blockIdx.x) * (kGroups * J) + grp * J;
   const int kb = sub & 3, kt = sub >> 2;
-  const int64_t c = c0 + 4 * kb + kt;
-  const bool own = kb < NB && c < cands;
-  const int64_t r = src.row(req * cands + (c < cands ? c : cands - 1), own);
-  const bool ok = own && r >= 0 && r < num_rows;
-  const int64_t myrow = ok ? r : 0;
-  const double sc = static_cast<double>(scale[myrow]);
-  const double bi = static_cast<double>(bias[myrow]);
+  // Every pass's row first: the ID and bucket trips of the later passes run
+  // while the earlier passes' rows are fetched and scored.
+  int64_t cp[PASSES], rp[PASSES];
+  bool ownp[PASSES];
+#pragma unroll
+  for (int p = 0; p < PASSES; ++p) {
+    cp[p] = (static_cast<int64_t>(blockIdx.x) * PASSES + p) * (kGroups * J) + grp * J + 4 * kb + kt;
+    ownp[p] = kb < NB && cp[p] < cands;
+    rp[p] = src.row(req * cands + (cp[p] < cands ? cp[p] : cands - 1), false);
+  }
+  // the lookup's outputs after every probe (a store here would hold the next
+  // pass's loads behind it: the outputs may alias the inputs)
+#pragma unroll
+  for (int p = 0; p < PASSES; ++p)
+    if (ownp[p]) src.record(req * cands + cp[p], rp[p]);
   const float *u = user + req * dim;
   double ud[CPL][16];
   double usum = 0.0;
@@ -162,29 +211,40 @@ __global__ void __launch_bounds__(kThreads)
       usum += ud[m][e];
     }
   const double U = group16_sum(usum);
-  int4 v[NB][4][CPL];
 #pragma unroll
-  for (int k = 0; k < NB; ++k)
+  for (int p = 0; p < PASSES; ++p) {
+    const int64_t c = cp[p];
+    const bool own = ownp[p];
+    const int64_t r = rp[p];
+    const bool ok = own && r >= 0 && r < num_rows;
+    const int64_t myrow = ok ? r : 0;
+    const double sc = static_cast<double>(scale[myrow]);
+    const double bi = static_cast<double>(bias[myrow]);
+    int4 v[NB][4][CPL];
 #pragma unroll
-    for (int t = 0; t < 4; ++t) {
-      const int64_t rr = __shfl(myrow, 4 * t + k, 16);
+    for (int k = 0; k < NB; ++k)
 #pragma unroll
-      for (int m = 0; m < CPL; ++m) v[k][t][m] = *reinterpret_cast<const int4 *>(q + rr * dim + (sub + 16 * m) * 16);
+      for (int t = 0; t < 4; ++t) {
+        const int64_t rr = __shfl(myrow, 4 * t + k, 16);
+#pragma unroll
+        for (int m = 0; m < CPL; ++m)
+          v[k][t][m] = *reinterpret_cast<const int4 *>(q + rr * dim + (sub + 16 * m) * 16);
+      }
+    double res = 0.0;
+#pragma unroll
+    for (int k = 0; k < NB; ++k) {
+      double a[4];
+#pragma unroll
+      for (int t = 0; t < 4; ++t) {
+        a[t] = 0.0;
+#pragma unroll
+        for (int m = 0; m < CPL; ++m) a[t] = qdot16(v[k][t][m], ud[m], a[t]);
+      }
+      const double A = group16_scatter4(a[0], a[1], a[2], a[3], sub);
+      if (kb == k) res = __fma_rn(sc, A, bi * U);
     }
-  double res = 0.0;
-#pragma unroll
-  for (int k = 0; k < NB; ++k) {
-    double a[4];
-#pragma unroll
-    for (int t = 0; t < 4; ++t) {
-      a[t] = 0.0;
-#pragma unroll
-      for (int m = 0; m < CPL; ++m) a[t] = qdot16(v[k][t][m], ud[m], a[t]);
-    }
-    const double A = group16_scatter4(a[0], a[1], a[2], a[3], sub);
-    if (kb == k) res = __fma_rn(sc, A, bi * U);
+    if (own) out[req * cands + c] = ok ? static_cast<float>(res) : 0.0f;
   }
-  if (own) out[req * cands + c] = ok ? static_cast<float>(res) : 0.0f;
 }
 
 // Any dim % 16 == 0: chunks walked in a loop, dequantise-then-dot.
@@ -234,8 +294,8 @@ hlr_status score_launch(const int8_t *qtable, const float *scale, const float *b
   };
   // Two batches of four candidates per group: enough loads in flight to
   // cover the row fetches, registers for four waves per SIMD.
-  if (dim == 256) launch(score_kernel<1, 2, Src>, kGroups * 8);
-  else if (dim == 512) launch(score_kernel<2, 2, Src>, kGroups * 8);
+  if (dim == 256) launch(score_kernel<1, 2, 2, Src>, kGroups * 8 * 2);
+  else if (dim == 512) launch(score_kernel<2, 2, 2, Src>, kGroups * 8 * 2);
   else launch(score_kernel_any<Src>, kCandsPerBlock);
   return launch_status();
 }
@@ -284,7 +344,11 @@ extern "C" hlr_status mpzch_score(const int64_t *identity, int64_t capacity, int
   if (!aligned(identity, probes == 8 ? 16 : 8) || !aligned(ids, 8) || (out_rows && !aligned(out_rows, 8)))
     return HLR_MISALIGNED;
   const uint64_t nb = static_cast<uint64_t>(capacity / probes);
-  const ProbeIn src{ids, identity, nb, (nb & (nb - 1)) == 0, probes, out_rows, out_hit};
+  const bool pow2 = (nb & (nb - 1)) == 0;
+  if (probes == 8 && pow2)
+    return score_launch(qtable, scale, bias, capacity, dim, ProbeIn8{ids, identity, nb, out_rows, out_hit},
+                        num_requests, cands_per_request, user_vecs, out_scores, stream);
+  const ProbeIn src{ids, identity, nb, pow2, probes, out_rows, out_hit};
   return score_launch(qtable, scale, bias, capacity, dim, src, num_requests, cands_per_request, user_vecs,
                       out_scores, stream);
 }
