@@ -32,9 +32,11 @@ import time
 
 ROOT = os.path.dirname(os.path.abspath(__file__))
 HBM_PEAK_GBS = 8000.0
-# Batches the captured graph's lookups run ahead of the row passes (75.5-75.9 us per batch with 2 or 3,
-# 76.3 with 1, same box)
-GRAPH_AHEAD = 3
+# The captured graph runs the grouped schedule: the lookups of GRAPH_GROUP batches back to back, GRAPH_AHEAD
+# groups ahead of the row passes (73.3-73.4 us per batch; groups of 4 one ahead 73.7-73.9, of 8 73.5-73.8;
+# one cross-stream dependency per batch, lookups 1 batch ahead 76.0-76.1; same box)
+GRAPH_GROUP = 4
+GRAPH_AHEAD = 2
 PMC_FILE = os.path.join(ROOT, "profiles", "ml_fused_memory_layer_pmc.json")
 
 
@@ -218,9 +220,11 @@ def main():
     cur = torch.cuda.current_stream(dev).cuda_stream
     G, A = args.group, args.ahead
     depth = args.depth
-    if args.schedule != "eager":  # the grouped leg: a multiple of the group, at least (ahead + 2) groups
-        depth = max(depth, (A + 2) * G)
+    if args.schedule != "eager":  # grouped (and the graph's): a multiple of the group, at least (ahead + 2) groups
+        depth = max(depth, (A + 2) * G, (GRAPH_AHEAD + 2) * GRAPH_GROUP if args.schedule == "graph" else 0)
         depth = (depth + G - 1) // G * G
+        if args.schedule == "graph":
+            depth = (depth + GRAPH_GROUP - 1) // GRAPH_GROUP * GRAPH_GROUP
     pipe = MemoryLayerPipeline(identity, stamps, values, P, n, depth=depth)
 
     def piped_step(t, evs=None, ahead=None):
@@ -256,7 +260,7 @@ def main():
         batches = [(ids_dev[first + k], base_now + 1 + first + k, e_pool[(first + k) % npool], out)
                    for k in range(K)]
         if mode == "graph":
-            graph = StepGraph(pipe, batches, ahead=GRAPH_AHEAD)  # captured, not run
+            graph = StepGraph(pipe, batches, ahead=GRAPH_AHEAD, group=GRAPH_GROUP)  # captured, not run
             torch.cuda.synchronize()
             wall0 = time.perf_counter()
             timer.record(start, cur)
@@ -378,6 +382,7 @@ def main():
         if pmc.get("src_sha") == row_pass_sha():
             traffic = pmc.get("traffic_bytes_per_launch")
 
+    GG, AA = (GRAPH_GROUP, GRAPH_AHEAD) if args.schedule == "graph" else (G, A)
     line = {
         "metric": "rows/s and achieved HBM GB/s (% of peak), 512-d fp32 lookup+writeback",
         "value": value,
@@ -399,15 +404,16 @@ def main():
             "schedule": ("two streams: lookup (MPZCH without values, whose last kernel groups the batch's positions "
                          "by row) beside compute (one pass over the batch's rows: gather and Writeback; rows the "
                          "lookup inserts read as zero), one library call per half batch; "
-                         + (f"grouped: the lookup halves of {G} batches back to back on the lookup stream, one "
+                         + (f"grouped: the lookup halves of {GG} batches back to back on the lookup stream, one "
                             f"event after them; the compute stream waits once per group, then runs the group's "
-                            f"row passes back to back; lookups {A} group(s) ahead, ring depth {depth}; enqueued "
-                            f"call by call (MemoryLayerPipeline.run)" if args.schedule == "grouped" else
-                            (f"lookahead: batch t+{GRAPH_AHEAD if args.schedule == 'graph' else 1}'s lookup is "
-                             f"enqueued before batch t's row traffic, ring depth {depth}" if la else
-                             f"batch t's lookup with its own row traffic, ring depth {depth}")
-                            + ("; the K timed batches captured (untimed) as one HIP graph of those calls and "
-                               "replayed once" if args.schedule == "graph" else "; enqueued call by call"))),
+                            f"row passes back to back; lookups {AA} group(s) ahead, ring depth {depth}" +
+                            ("; the K timed batches captured (untimed) as one HIP graph of those calls "
+                             "(MemoryLayerPipeline.run inside StepGraph) and replayed once" if args.schedule == "graph"
+                             else "; enqueued call by call (MemoryLayerPipeline.run)")
+                            if args.schedule != "eager" else
+                            (f"lookahead: batch t+1's lookup is enqueued before batch t's row traffic, ring depth "
+                             f"{depth}" if la else f"batch t's lookup with its own row traffic, ring depth {depth}")
+                            + "; enqueued call by call")),
         },
         "roofline": {
             "bound": "hbm", "kernel": "ml_fused<2> (gather + Writeback, one pass over the batch's rows)",

@@ -402,21 +402,30 @@ class StepGraph:
     ahead: how many batches the lookup half runs ahead of the row half (at most depth - 1).  A wait on
     another stream's event takes about 10 us to resolve when the event completes after the waiting
     queue reached it; with the lookup two batches ahead, the event the row half of batch t waits for
-    completed a whole row pass earlier.  (HIP events
+    completed a whole row pass earlier.
+    group: when given, the graph captures the grouped schedule of MemoryLayerPipeline.run(batches,
+    group, ahead) instead (ahead then counts groups): one cross-stream dependency per stream and group
+    of batches rather than one per batch, which the graph's queues resolve faster (73.3-73.9 against
+    75.5-76.1 us per batch for groups of 4).  (HIP events
     recorded inside a capture cannot be timed on this runtime, so the row pass is not timed inside a
     graph.)  Every `now` must stay valid when the
     graph runs: a graph is meant to be replayed once for the state it was captured for, or again only
     after that state has been restored (the MPZCH stamps must stay below every `now`)."""
 
-    def __init__(self, pipe: MemoryLayerPipeline, batches, ahead=1):
+    def __init__(self, pipe: MemoryLayerPipeline, batches, ahead=1, group=None):
         if not pipe.native:
             raise HLRError("StepGraph needs a native MemoryLayerPipeline")
         if pipe._ahead:
             raise HLRError("StepGraph: finish the batches looked up ahead first")
         r = pipe.ring
         ahead = int(ahead)
-        if not 1 <= ahead < r.depth:
+        if group is None and not 1 <= ahead < r.depth:
             raise HLRError(f"StepGraph: ahead must be in [1, depth - 1] = [1, {r.depth - 1}]")
+        if group is not None:
+            G = int(group)
+            if G < 1 or ahead < 1 or r.depth % G != 0 or r.depth < (ahead + 2) * G:
+                raise HLRError(f"StepGraph: need group >= 1, ahead >= 1 and depth a multiple of group, at least "
+                               f"(ahead + 2) * group (depth {r.depth}, group {G}, ahead {ahead})")
         if not r.cs:
             raise HLRError("StepGraph: the legacy default stream cannot be captured; build the pipeline while a "
                            "non-default torch stream is current")
@@ -425,24 +434,27 @@ class StepGraph:
         self.graph = self.exec = None
         h.begin_capture(r.cs)
         try:
-            pipe.restart()
-            bs = [tuple(b) + (None,) * (8 - len(b)) for b in batches]
+            if group is not None:
+                pipe.run(batches, group=group, ahead=ahead)  # begins by ordering the lookup stream after cs
+            else:
+                pipe.restart()
+                bs = [tuple(b) + (None,) * (8 - len(b)) for b in batches]
 
-            def look(b):
-                ids, now, _, _, ev, st, rows_out, hit_out = b
-                k = pipe.prefetch(ids, now, evicted=ev, stats=st)
-                n = ids.numel()
-                if rows_out is not None:
-                    h.copy_d2d(rows_out.data_ptr(), pipe.rows(k).data_ptr(), 8 * n, r.ls)
-                if hit_out is not None:
-                    h.copy_d2d(hit_out.data_ptr(), pipe.hit(k).data_ptr(), n, r.ls)
+                def look(b):
+                    ids, now, _, _, ev, st, rows_out, hit_out = b
+                    k = pipe.prefetch(ids, now, evicted=ev, stats=st)
+                    n = ids.numel()
+                    if rows_out is not None:
+                        h.copy_d2d(rows_out.data_ptr(), pipe.rows(k).data_ptr(), 8 * n, r.ls)
+                    if hit_out is not None:
+                        h.copy_d2d(hit_out.data_ptr(), pipe.hit(k).data_ptr(), n, r.ls)
 
-            for b in bs[:ahead]:
-                look(b)
-            for k, (ids, now, e, out, ev, st, _, _) in enumerate(bs):
-                if k + ahead < len(bs):
-                    look(bs[k + ahead])
-                pipe.step(ids, now, e, out=out, evicted=ev, stats=st)
+                for b in bs[:ahead]:
+                    look(b)
+                for k, (ids, now, e, out, ev, st, _, _) in enumerate(bs):
+                    if k + ahead < len(bs):
+                        look(bs[k + ahead])
+                    pipe.step(ids, now, e, out=out, evicted=ev, stats=st)
             join = h.event()
             h.record(join, r.ls)
             h.wait(r.cs, join)

@@ -163,8 +163,9 @@ def test_res_publisher_full_size(dev, prefilled):
 @pytest.mark.timeout(900)
 def test_memory_layer_200_steps_benched_schedule_then_serving(dev, prefilled):
     """The headline's launch configuration over the workload's whole 200-step stream: memory_layer_step
-    through MemoryLayerPipeline (two streams, ring depth 12, batch t+3's lookup before batch t's row pass),
-    the 200 batches captured as one HIP graph and replayed, as bench.py times them.  Every step's rows,
+    through MemoryLayerPipeline in the grouped two-stream schedule (the lookups of 4 batches back to back,
+    two groups ahead of the row passes, ring depth 16), the 200 batches captured as one HIP graph and
+    replayed, as bench.py times them.  Every step's rows,
     hit mask, evicted IDs, stats and gathered rows bit for bit, then the ID table and the whole 8 GiB
     table.  Then the serving table is that trained table row-quantised to int8 (quantize_rows_int8 over
     every row, bit for bit against the oracle's quantiser), and 256 x 1024 candidates are looked up
@@ -191,9 +192,10 @@ def test_memory_layer_200_steps_benched_schedule_then_serving(dev, prefilled):
         sts = [torch.zeros(6, dtype=torch.int64, device=dev) for _ in range(steps)]
         rws = [torch.empty(n, dtype=torch.int64, device=dev) for _ in range(steps)]
         hts = [torch.empty(n, dtype=torch.int8, device=dev) for _ in range(steps)]
-        pipe = MemoryLayerPipeline(identity, stamps, values, P, n, depth=12)  # as bench.py: ring of 12, 3 ahead
+        # as bench.py: the grouped schedule captured, groups of 4 batches, lookups 2 groups ahead, ring of 16
+        pipe = MemoryLayerPipeline(identity, stamps, values, P, n, depth=16)
         graph = StepGraph(pipe, [(ids[t], base + t + 1, es[t % npool], outs[t], evs[t], sts[t], rws[t], hts[t])
-                                 for t in range(steps)], ahead=3)
+                                 for t in range(steps)], ahead=2, group=4)
         graph.replay()
         torch.cuda.synchronize()
     e_np = [to_np(x) for x in es]

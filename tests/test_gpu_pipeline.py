@@ -339,7 +339,8 @@ def test_memory_layer_step_edge_cases(dev, C, P, D, n, depth):
         assert overflows > 0  # the overflow path is exercised
 
 
-def test_step_graph_replays_match_oracle(dev):
+@pytest.mark.parametrize("group,ahead,depth", [(None, 1, 3), (2, 1, 6), (4, 2, 16)])
+def test_step_graph_replays_match_oracle(dev, group, ahead, depth):
     """A sequence of batches captured as one HIP graph (StepGraph) and replayed three times, each
     time from the same restored state with eager work and synchronisation in between: every replay's
     gathered rows, evicted IDs, stats and final state equal the oracle's sequential result bit for bit.
@@ -363,8 +364,9 @@ def test_step_graph_replays_match_oracle(dev):
     with torch.cuda.stream(side):
         snap = (identity.clone(), stamps.clone(), values.clone())
         outs = [torch.empty((n, D), dtype=torch.float32, device=dev) for _ in range(steps)]
-        pipe = pipeline.MemoryLayerPipeline(identity, stamps, values, P, n, depth=3)
-        graph = pipeline.StepGraph(pipe, [(ids[t], base + t + 1, es[t], outs[t]) for t in range(steps)])
+        pipe = pipeline.MemoryLayerPipeline(identity, stamps, values, P, n, depth=depth)
+        graph = pipeline.StepGraph(pipe, [(ids[t], base + t + 1, es[t], outs[t]) for t in range(steps)],
+                                   ahead=ahead, group=group)
         for rep in range(3):
             identity.copy_(snap[0])
             stamps.copy_(snap[1])
