@@ -345,6 +345,9 @@ class MemoryLayerPipeline:
         def lookup_group(gi):
             b0, b1 = gi * G, min(len(bs), gi * G + G)
             kl = last(gi)
+            # the group's slots were last used by the full group depth / group groups back, which released
+            # them all with the done event of its last slot (not this group's last slot when it is ragged)
+            kfree = (b0 + G - 1) % D
             for b in range(b0, b1):
                 ids, now, _, _, ev, st, ro, ho = bs[b]
                 k = b % D
@@ -353,7 +356,7 @@ class MemoryLayerPipeline:
                 rc = fn(*self._const, ids.data_ptr(), ids.numel(), self.n, int(now), None,
                         self._rows[k].data_ptr(), self._hit[k].data_ptr(), None if ev is None else ev.data_ptr(),
                         None if st is None else st.data_ptr(), None, mz[0], mz[1], wb, wbb, r.ls, r.cs,
-                        r.done[kl] if (b == b0 and b >= D) else None, None, r.marks[kl][1] if b == b1 - 1 else None,
+                        r.done[kfree] if (b == b0 and b >= D) else None, None, r.marks[kl][1] if b == b1 - 1 else None,
                         None, None, None, 1)
                 _check(rc, "memory_layer_step")
                 n = ids.numel()
@@ -924,9 +927,9 @@ class EMAPipeline:
             b0, b1 = gi * G, min(len(batches), gi * G + G)
             kl = last(gi)
             used = streams(gi)
-            if b0 >= D:
+            if b0 >= D:  # released by the full group depth / group groups back (its last slot's done event)
                 for c in used:
-                    h.wait(self.rings[c].ls, r0.done[kl])
+                    h.wait(self.rings[c].ls, r0.done[(b0 + G - 1) % D])
             for b in range(b0, b1):
                 rows, masks, _, _ = batches[b]
                 src, order, chain = plans[b]

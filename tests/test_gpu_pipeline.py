@@ -339,21 +339,22 @@ def test_memory_layer_step_edge_cases(dev, C, P, D, n, depth):
         assert overflows > 0  # the overflow path is exercised
 
 
-@pytest.mark.parametrize("group,ahead,depth", [(None, 1, 3), (2, 1, 6), (4, 2, 16)])
-def test_step_graph_replays_match_oracle(dev, group, ahead, depth):
-    """A sequence of batches captured as one HIP graph (StepGraph) and replayed three times, each
+@pytest.mark.parametrize("group,ahead,depth,steps", [(None, 1, 3, 6), (2, 1, 6, 6), (4, 2, 16, 6), (2, 2, 8, 9),
+                                                     (4, 1, 12, 14)])
+def test_step_graph_replays_match_oracle(dev, group, ahead, depth, steps):
+    """A sequence of batches captured as one HIP graph (StepGraph: per-batch lookahead, or the grouped
+    schedule, including ragged last groups whose slots were used before) and replayed three times, each
     time from the same restored state with eager work and synchronisation in between: every replay's
     gathered rows, evicted IDs, stats and final state equal the oracle's sequential result bit for bit.
     Eager batches then continue after the last replay."""
-    cfg = synth.scaled_memory_layer(capacity=16_384, universe=120_000, batch=8_192, steps=6)
+    cfg = synth.scaled_memory_layer(capacity=16_384, universe=120_000, batch=8_192, steps=steps)
     C, P, D, n = cfg.capacity, cfg.probes, cfg.dim, cfg.batch
     identity, stamps, o, base = prefilled_pair(dev, cfg)
     values = torch.zeros((C, D), dtype=torch.float32, device=dev)
-    ids_np = synth.mpzch_stream(cfg, cfg.steps + 1)
-    e_np = [synth.normal_rows_np(n, D, cfg.e_std, 2, t) for t in range(1, cfg.steps + 2)]
+    ids_np = synth.mpzch_stream(cfg, steps + 1)
+    e_np = [synth.normal_rows_np(n, D, cfg.e_std, 2, t) for t in range(1, steps + 2)]
     ids = [torch.from_numpy(x).to(dev) for x in ids_np]
     es = [torch.from_numpy(x).to(dev) for x in e_np]
-    steps = cfg.steps
     expect = []
     for t in range(steps):
         orows, ohit, oev, ost = o.step(ids_np[t], base + t + 1)
