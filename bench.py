@@ -727,7 +727,7 @@ def run_cs3(args):
     import torch
     import hashed_lookup_row_amd as hlr
     import synth
-    from hashed_lookup_row_amd.pipeline import EMAPipeline
+    from hashed_lookup_row_amd.pipeline import EMAPipeline, RunGraph
     dev = torch.device("cuda:0")
     cfg = synth.CS3
     D, n = cfg.dim, cfg.batch
@@ -741,6 +741,10 @@ def run_cs3(args):
         ur, ir, y = synth.cs3_step(cfg, s + 1)
         inp.append([torch.from_numpy(x).to(dev) for x in (ur, ir, y)] +
                    [synth.normal_rows(n, D, 1.0, 5, s + 1, stream=k, device=dev) for k in (1, 2, 3)])
+    # a non-default compute stream (a HIP graph cannot be captured on the legacy default stream)
+    side = torch.cuda.Stream(dev)
+    side.wait_stream(torch.cuda.current_stream(dev))
+    torch.cuda.set_stream(side)
     timer, cur = HipTimer(), torch.cuda.current_stream(dev).cuda_stream
     # (table, rows index, values index, masked, a, b) per update, in the order applied
     calls = [("c_user", 0, 3, True, cfg.cts_a, cfg.cts_b), ("c_item", 1, 4, True, cfg.cts_a, cfg.cts_b),
@@ -788,6 +792,20 @@ def run_cs3(args):
         apply_s = [timer.elapsed_s(x, y) / sizes[g] for g, (x, y) in enumerate(gev)]
         step_ms = [timer.elapsed_s(gev[g - 1][1], gev[g][1]) / sizes[g] * 1e3 for g in range(1, ngroups)] or \
             [total / K * 1e3]
+        if args.schedule == "graph":
+            # the same schedule captured (untimed) as one HIP graph and replayed: the step time; the apply
+            # times above come from the eagerly enqueued run (events inside a graph cannot be timed)
+            event_leg_ms = total / K * 1e3
+            graph = RunGraph(pipe, todo, group=G, ahead=A)
+            torch.cuda.synchronize()
+            ga, gb = timer.event(), timer.event()
+            timer.record(ga, cur)
+            h0 = time.perf_counter()
+            graph.replay()
+            timer.record(gb, cur)
+            enqueue_s = time.perf_counter() - h0
+            torch.cuda.synchronize()
+            total = timer.elapsed_s(ga, gb)
     else:
         for s in range(W):
             piped_step(s)
@@ -846,12 +864,16 @@ def run_cs3(args):
                         f") beside {applies} on the compute stream") +
                        (f"; grouped: plans of {G} steps back to back, {A} group(s) ahead of the applies, one "
                         "cross-stream wait per stream per group (EMAPipeline.run)" if grouped else
-                        "; step by step, plans one step ahead")},
+                        "; step by step, plans one step ahead") +
+                       ("; the K timed steps captured (untimed) as one HIP graph and replayed once (RunGraph); "
+                        "apply times from the same schedule enqueued call by call" if grouped and
+                        args.schedule == "graph" else "")},
           roof,
           {"dtype": "fp32", "step_hbm_gbs": tot_bytes / step_s / 1e9,
            "apply_us": {k: v * 1e6 for k, v in per.items()},
            "step_ms_median": float(np.median(step_ms)), "step_ms_max": float(np.max(step_ms)),
            "host_enqueue_us_per_step": enqueue_s / K * 1e6,
+           "eager_grouped_ms_per_step": event_leg_ms if grouped and args.schedule == "graph" else None,
            "one_stream": {"ms_per_step": serial / K * 1e3, "pairs_per_s": n * K / serial},
            "top_user_occurrences": int(np.bincount(ur).max())})
 

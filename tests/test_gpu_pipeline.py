@@ -543,6 +543,17 @@ def test_ema_grouped_run_matches_oracle(dev, group, ahead, lookup_streams, deriv
     """EMAPipeline.run() (plans a group ahead, one wait per stream and group) between step() calls: every
     table bit-equal to the oracle's batch-order EMA after all batches (CS3 page, sec. 2), with a last
     group shorter than the others and batches of different sizes."""
+    _ema_grouped(dev, group, ahead, lookup_streams, derive, graph=False)
+
+
+@pytest.mark.parametrize("group,ahead,lookup_streams,derive", [(2, 2, 2, True), (4, 1, 2, False)])
+def test_ema_run_graph_matches_oracle(dev, group, ahead, lookup_streams, derive):
+    """The same grouped schedule captured as one HIP graph (RunGraph, every lookup stream joined back) and
+    replayed once between step() calls: every table bit-equal to the oracle's batch-order EMA."""
+    _ema_grouped(dev, group, ahead, lookup_streams, derive, graph=True)
+
+
+def _ema_grouped(dev, group, ahead, lookup_streams, derive, graph):
     cfg = synth.CS3
     users, items, D, n = 4096, 8192, 128, 12_000
     g = np.random.default_rng(17 + group)
@@ -561,17 +572,25 @@ def test_ema_grouped_run_matches_oracle(dev, group, ahead, lookup_streams, deriv
              for (u, it, y, v) in batches]
     torch.cuda.synchronize()
     depth = (ahead + 2) * group
-    pipe = pipeline.EMAPipeline(gpu, n, depth=depth, derive=derive, lookup_streams=lookup_streams)
     coeffs = [(cfg.cts_a, cfg.cts_b), (cfg.cts_a, cfg.cts_b), (cfg.cms_a, cfg.cms_b), (cfg.cms_a, cfg.cms_b)]
 
     def args(b):
         ur, ir, yy, vv = b
         return [ur, ir, ur, ir], [yy, yy, None, None], [vv[0], vv[1], vv[2], vv[2]], coeffs
 
-    pipe.step(*args(dev_b[0]))
-    pipe.step(*args(dev_b[1]))
-    pipe.run([args(b) for b in dev_b[2:11]], group=group, ahead=ahead)
-    pipe.step(*args(dev_b[11]))
+    side = torch.cuda.Stream(dev)  # a graph cannot be captured on the legacy default stream
+    side.wait_stream(torch.cuda.current_stream(dev))
+    with torch.cuda.stream(side):
+        pipe = pipeline.EMAPipeline(gpu, n, depth=depth, derive=derive, lookup_streams=lookup_streams)
+        pipe.step(*args(dev_b[0]))
+        pipe.step(*args(dev_b[1]))
+        if graph:
+            g = pipeline.RunGraph(pipe, [args(b) for b in dev_b[2:11]], group=group, ahead=ahead)
+            g.replay()
+        else:
+            pipe.run([args(b) for b in dev_b[2:11]], group=group, ahead=ahead)
+        pipe.step(*args(dev_b[11]))
+        torch.cuda.synchronize()
     for (u, it, y, v) in batches:
         oracle.ema(cpu[0], u, v[0], y, cfg.cts_a, cfg.cts_b)
         oracle.ema(cpu[1], it, v[1], y, cfg.cts_a, cfg.cts_b)
